@@ -1,0 +1,351 @@
+/*
+ * oracle.c - plain, slow CPU reference for int4 KV-cache quantisation and
+ * decode attention computed on the quantised cache.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * bench's CPU-baseline leg use it.  It shares no code, header, table or
+ * constant with the GPU library.
+ *
+ * What it computes, and where that comes from:
+ *
+ *  - "Open-TQ-Metal: Fused Compressed-Domain Attention for Long-Context LLM
+ *    Inference on Apple Silicon" (arXiv 2604.16957, abstract): the KV cache
+ *    is quantised to int4 as it is produced, and attention is evaluated on
+ *    the compressed form with no dequantised intermediate.  Skipping the
+ *    intermediate does not change the mathematics, so the oracle simply
+ *    dequantises (exactly, in fp64) and runs textbook softmax attention.
+ *
+ *  - "SRFT + int4 KV-cache" (agents-report page, section on the core method):
+ *    every group gets its own abs-max, then symmetric int4 quantisation and
+ *    nibble packing; rotation happens before quantisation, all in one pass.
+ *
+ *  - "AdapTQ" (zingnex page, section on Fast Hadamard Rotation): an
+ *    O(d log d) in-place Hadamard rotation applied before quantisation to
+ *    spread outliers.  The sign-randomised form (SRHT) is named on the
+ *    agents-report page as the reference rotation.
+ *
+ * Readings where the pages are silent (each one listed in the design notes):
+ * group = 32 contiguous channels; scale = abs-max / 7 in IEEE fp32;
+ * code = round-half-to-even(x / scale) clamped to [-8, 7]; scale == 0 gives
+ * all-zero codes; byte j holds element 2j in its low nibble and element
+ * 2j+1 in its high nibble; rotation y = c * H_D * (s (.) x) with H_D the
+ * Sylvester Hadamard matrix, butterflies in ascending stride order, and the
+ * normalisation c applied last as one fp32 multiply; no fused multiply-add
+ * anywhere in the fp32 quantiser (this file is built with
+ * -ffp-contract=off).
+ *
+ * Parity pins for every function here live in the CPU test suite.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_GROUP 32
+
+/* ---------------------------------------------------------------- widening */
+
+/* IEEE binary16 -> binary32, from the format's definition:
+ * normal  (e in 1..30): (1024 + m) * 2^(e - 25)
+ * subnormal (e == 0)  :  m * 2^-24
+ * e == 31             :  inf / nan                                       */
+float oracle_f16_to_f32(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);
+    return (float)(sign ? -v : v);
+}
+
+/* bfloat16 is the upper half of a binary32 word. */
+float oracle_bf16_to_f32(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+static float widen(uint16_t bits, int dtype)
+{
+    return dtype == 0 ? oracle_f16_to_f32(bits) : oracle_bf16_to_f32(bits);
+}
+
+/* ---------------------------------------------------------------- rotation */
+
+/* y <- c * H_D * (s (.) y) in fp32, H_D Sylvester-ordered (H_1 = [1],
+ * H_2n = [[H_n, H_n], [H_n, -H_n]]).  Stage h pairs element j with j + h
+ * inside each block of 2h and replaces them with (a + b, a - b). */
+void oracle_srht_f32(float *y, const float *signs, int D, float c)
+{
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * signs[i];
+    for (int h = 1; h < D; h *= 2)
+        for (int blk = 0; blk < D; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                float a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* The same rotation in fp64, used on the query so that q'.k' = q.k. */
+void oracle_srht_f64(double *y, const float *signs, int D, double c)
+{
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * (double)signs[i];
+    for (int h = 1; h < D; h *= 2)
+        for (int blk = 0; blk < D; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                double a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* ---------------------------------------------------------------- quantise */
+
+/* One vector x[D] (already widened to fp32, already rotated if rotation is
+ * on) -> codes[D/2] packed nibbles and scales[D/32]. */
+void oracle_quantize_vector(const float *x, int D, uint8_t *codes, float *scales)
+{
+    int8_t c[1024];
+    for (int g = 0; g < D / ORACLE_GROUP; ++g) {
+        const float *xg = x + g * ORACLE_GROUP;
+        float a = 0.0f;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            float v = fabsf(xg[i]);
+            if (v > a)
+                a = v;
+        }
+        float s = a / 7.0f;
+        scales[g] = s;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            int8_t code = 0;
+            if (s != 0.0f) {
+                float r = rintf(xg[i] / s); /* default rounding: half to even */
+                if (r != r)
+                    r = 0.0f; /* non-finite input: unspecified, kept defined */
+                if (r > 7.0f)
+                    r = 7.0f;
+                if (r < -8.0f)
+                    r = -8.0f;
+                code = (int8_t)r;
+            }
+            c[g * ORACLE_GROUP + i] = code;
+        }
+    }
+    for (int j = 0; j < D / 2; ++j)
+        codes[j] = (uint8_t)((c[2 * j] & 0xF) | ((c[2 * j + 1] & 0xF) << 4));
+}
+
+/* Signed value of nibble i of a packed row. */
+static int nibble(const uint8_t *row, int i)
+{
+    int u = (row[i >> 1] >> ((i & 1) * 4)) & 0xF;
+    return u >= 8 ? u - 16 : u;
+}
+
+struct qrows_job {
+    const uint16_t *src;
+    int dtype;
+    long n0, n1;
+    int D;
+    const float *signs;
+    float rot_norm;
+    uint8_t *codes;
+    float *scales;
+};
+
+static void *qrows_worker(void *arg)
+{
+    struct qrows_job *j = (struct qrows_job *)arg;
+    float x[1024];
+    for (long n = j->n0; n < j->n1; ++n) {
+        for (int i = 0; i < j->D; ++i)
+            x[i] = widen(j->src[n * j->D + i], j->dtype);
+        if (j->signs)
+            oracle_srht_f32(x, j->signs, j->D, j->rot_norm);
+        oracle_quantize_vector(x, j->D, j->codes + n * (j->D / 2),
+                               j->scales + n * (j->D / ORACLE_GROUP));
+    }
+    return NULL;
+}
+
+/* N rows of D 16-bit values (dtype 0 = fp16, 1 = bf16) -> N rows of codes
+ * and scales.  signs == NULL means no rotation.  Rows are independent, so
+ * spreading them over threads does not change any result. */
+int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
+                         const float *signs, float rot_norm, uint8_t *codes,
+                         float *scales, int nthreads)
+{
+    if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1)
+        return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    struct qrows_job jobs[256];
+    long per = (N + nthreads - 1) / nthreads;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        long n0 = t * per, n1 = n0 + per > N ? N : n0 + per;
+        if (n0 >= n1)
+            break;
+        jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, codes, scales};
+        if (nthreads == 1) {
+            qrows_worker(&jobs[t]);
+        } else {
+            pthread_create(&th[t], NULL, qrows_worker, &jobs[t]);
+            ++started;
+        }
+    }
+    for (int t = 0; t < started; ++t)
+        pthread_join(th[t], NULL);
+    return 0;
+}
+
+/* ---------------------------------------------------------------- attend */
+
+/* One query row against one head's cache rows t < T:
+ *   K^[t][i] = code * scale  (exact in fp64)
+ *   S_t      = scale_attn * sum_i q'_i K^[t][i]
+ *   w_t      = exp(S_t - max_u S_u)
+ *   out      = sum_t w_t V^[t] / sum_t w_t
+ * T == 0 gives out = 0.  q' is q rotated in fp64 when signs != NULL.
+ * work must hold T doubles. */
+void oracle_attend_row(const uint16_t *q, int dtype, int D,
+                       const uint8_t *kc, const float *ks,
+                       const uint8_t *vc, const float *vs, long T,
+                       double scale, const float *signs, float rot_norm,
+                       double *work, double *out)
+{
+    double qd[1024], kd[1024];
+    int ng = D / ORACLE_GROUP;
+    for (int i = 0; i < D; ++i)
+        qd[i] = (double)widen(q[i], dtype);
+    if (signs)
+        oracle_srht_f64(qd, signs, D, (double)rot_norm);
+    for (int i = 0; i < D; ++i)
+        out[i] = 0.0;
+    if (T <= 0)
+        return;
+
+    double m = -INFINITY;
+    for (long t = 0; t < T; ++t) {
+        const uint8_t *row = kc + t * (D / 2);
+        const float *srow = ks + t * ng;
+        for (int i = 0; i < D; ++i)
+            kd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
+        double dot = 0.0;
+        for (int i = 0; i < D; ++i)
+            dot += qd[i] * kd[i];
+        work[t] = scale * dot;
+        if (work[t] > m)
+            m = work[t];
+    }
+    double l = 0.0;
+    for (long t = 0; t < T; ++t) {
+        double w = exp(work[t] - m);
+        l += w;
+        const uint8_t *row = vc + t * (D / 2);
+        const float *srow = vs + t * ng;
+        for (int i = 0; i < D; ++i)
+            out[i] += w * ((double)nibble(row, i) * (double)srow[i / ORACLE_GROUP]);
+    }
+    for (int i = 0; i < D; ++i)
+        out[i] /= l;
+}
+
+struct attn_job {
+    const uint16_t *q;
+    int dtype, B, Hq, Hkv, D;
+    long cap;
+    const uint8_t *kc, *vc;
+    const float *ks, *vs;
+    const int32_t *lens;
+    double scale;
+    const float *signs;
+    float rot_norm;
+    double *out;
+    const int32_t *rows;
+    long r0, r1;
+};
+
+static void *attn_worker(void *arg)
+{
+    struct attn_job *j = (struct attn_job *)arg;
+    double *work = (double *)malloc(sizeof(double) * (size_t)(j->cap > 0 ? j->cap : 1));
+    if (!work)
+        return NULL;
+    int G = j->Hq / j->Hkv;
+    for (long r = j->r0; r < j->r1; ++r) {
+        long row = j->rows ? j->rows[r] : r; /* row = b * Hq + h */
+        int b = (int)(row / j->Hq), h = (int)(row % j->Hq), hk = h / G;
+        long T = j->lens[b];
+        if (T > j->cap)
+            T = j->cap;
+        size_t head = (size_t)b * j->Hkv + hk;
+        oracle_attend_row(j->q + (size_t)row * j->D, j->dtype, j->D,
+                          j->kc + head * j->cap * (j->D / 2), j->ks + head * j->cap * (j->D / ORACLE_GROUP),
+                          j->vc + head * j->cap * (j->D / 2), j->vs + head * j->cap * (j->D / ORACLE_GROUP),
+                          T, j->scale, j->signs, j->rot_norm, work,
+                          j->out + (size_t)r * j->D);
+    }
+    free(work);
+    return NULL;
+}
+
+/* Decode attention for a batch.  q: [B][Hq][D] 16-bit; cache in the plain
+ * layout codes [B][Hkv][cap][D/2], scales [B][Hkv][cap][D/32]; lens [B].
+ * Query head h reads KV head h / (Hq / Hkv).  If rows != NULL only the
+ * listed rows (b * Hq + h) are computed and out is [nrows][D]; otherwise
+ * out is [B * Hq][D].  Threads split rows; results do not depend on them. */
+int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, long cap,
+                const uint8_t *kc, const float *ks, const uint8_t *vc, const float *vs,
+                const int32_t *lens, double scale, const float *signs, float rot_norm,
+                const int32_t *rows, long nrows, double *out, int nthreads)
+{
+    if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
+        D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1)
+        return -1;
+    long R = rows ? nrows : (long)B * Hq;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    struct attn_job jobs[256];
+    long per = (R + nthreads - 1) / nthreads;
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        long r0 = t * per, r1 = r0 + per > R ? R : r0 + per;
+        if (r0 >= r1)
+            break;
+        jobs[t] = (struct attn_job){q, dtype, B, Hq, Hkv, D, cap, kc, vc, ks, vs, lens,
+                                    scale, signs, rot_norm, out, rows, r0, r1};
+        if (nthreads == 1) {
+            attn_worker(&jobs[t]);
+        } else {
+            pthread_create(&th[t], NULL, attn_worker, &jobs[t]);
+            ++started;
+        }
+    }
+    for (int t = 0; t < started; ++t)
+        pthread_join(th[t], NULL);
+    return 0;
+}

@@ -1,0 +1,208 @@
+/*
+ * otq.h - int4 KV-cache quantisation and decode attention computed directly
+ * on the packed int4 cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method: new K/V vectors are quantised to int4 as they are produced and
+ * attention is evaluated on the compressed representation, with no
+ * dequantised fp16 K/V ever written to memory ("Open-TQ-Metal: Fused
+ * Compressed-Domain Attention for Long-Context LLM Inference on Apple
+ * Silicon", arXiv 2604.16957, abstract; zingnex Open-TQ-Metal page, sections
+ * on on-the-fly quantisation, compressed-domain attention and eliminating
+ * intermediate matrices).  The quantiser is symmetric group abs-max with
+ * nibble packing, optionally after a sign-randomised Hadamard rotation
+ * ("SRFT + int4 KV-cache", agents-report page, core-method section; AdapTQ,
+ * zingnex page, section on Fast Hadamard Rotation).  The call shape follows
+ * AdapTQ's engine API (section on the native Python API): a fixed-capacity
+ * cache, an append of new K/V, and an attention call over the cache.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing and keeps no state between calls.
+ *  - Descriptor structs (otq_cache, otq_plan) live in HOST memory and are
+ *    read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously; the return value reports only what the host can check
+ *    (arguments) and launch failures.
+ *  - No entry point throws; all return an otq_status (0 = OTQ_OK).
+ *  - Argument errors are detected on the host before any HIP call is made.
+ */
+#ifndef OTQ_H
+#define OTQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define OTQ_ABI_VERSION 1
+
+/* Elements per quantisation group (one fp32 scale each), along head_dim. */
+#define OTQ_GROUP 32
+/* Tokens per tile of the V code layout; capacity must be a multiple. */
+#define OTQ_TILE 32
+
+typedef enum otq_status {
+    OTQ_OK = 0,
+    OTQ_EINVAL = -1,       /* null pointer, bad count, Hq % Hkv != 0, ...      */
+    OTQ_ECAPACITY = -2,    /* max_len or n_new larger than the cache capacity */
+    OTQ_EUNSUPPORTED = -3, /* head_dim not in {64,128,256}, bad dtype, G > 16  */
+    OTQ_EWORKSPACE = -4,   /* workspace null or smaller than required          */
+    OTQ_EDEVICE = -5       /* a HIP launch failed                              */
+} otq_status;
+
+typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
+
+/*
+ * A quantised KV cache for one attention layer: caller-owned device arrays,
+ * described by a host struct.
+ *
+ * Quantisation (per vector x of head_dim elements, per group g of 32
+ * consecutive elements, all in IEEE fp32 with round-half-to-even):
+ *     s_g  = max_i |x_i| / 7
+ *     c_i  = 0 if s_g == 0, else clamp(rint(x_i / s_g), -8, 7)
+ * K only, when k_rot_signs != NULL, x is first replaced by
+ *     y = rot_norm * H (k_rot_signs (.) x)
+ * with H the Sylvester-ordered Walsh-Hadamard matrix, evaluated as in-place
+ * butterflies (a + b, a - b) in ascending stride order, then one multiply by
+ * rot_norm (pass fp32(1/sqrt(head_dim))).  The query is rotated the same way
+ * inside otq_sdpa_int4_decode, so scores are unchanged by the rotation.
+ *
+ * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
+ *  k_codes  uint8 [B][H][C][D/2]: byte j of a token's row holds element 2j in
+ *           its low nibble and element 2j+1 in its high nibble; nibbles are
+ *           two's-complement int4.
+ *  k_scales float [B][H][C][D/32], v_scales likewise: s_g per token, group.
+ *  v_codes  uint8 [B][H][C/32][16*D]: the same nibbles as K's layout would
+ *           hold, regrouped per tile of 32 tokens so that each 32-bit word
+ *           holds 8 tokens of one channel.  For tile-relative token u
+ *           (0..31) let quarter r = (u % 16) / 4 and slot j = 4*(u / 16) +
+ *           (u % 4).  Channel c with cb = c / 16, n = c % 16, a = cb / 4,
+ *           b = cb % 4 owns word ((a*4 + r)*16 + n)*4 + b of the tile, and
+ *           slot j sits in byte j/2 of that word, low nibble for even j.
+ *           Tokens 2m and 2m+1 always share a byte.
+ *
+ * Bytes per array: codes B*H*C*D/2, scales B*H*C*(D/32)*4.
+ */
+typedef struct otq_cache {
+    int32_t batch;
+    int32_t num_kv_heads;
+    int32_t head_dim;      /* 64, 128 or 256 */
+    int32_t capacity;      /* tokens per sequence, multiple of OTQ_TILE, >= 32 */
+    uint8_t *k_codes;
+    float *k_scales;
+    uint8_t *v_codes;
+    float *v_scales;
+    const float *k_rot_signs; /* device [D] of +1.0f / -1.0f, or NULL */
+    float rot_norm;           /* used only when k_rot_signs != NULL */
+} otq_cache;
+
+/* Human-readable name of a status code (static string). */
+const char *otq_status_str(int status);
+
+/* OTQ_ABI_VERSION of the loaded library. */
+int otq_abi_version(void);
+
+/*
+ * Byte sizes of one codes array and one scales array of a cache with these
+ * dimensions (K and V have the same sizes).  Returns OTQ_OK, or
+ * OTQ_EINVAL / OTQ_EUNSUPPORTED for dimensions the cache does not support.
+ * Pure host arithmetic.
+ */
+int otq_cache_array_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t capacity, size_t *codes_bytes, size_t *scales_bytes);
+
+/* Total bytes of the four arrays (0 for unsupported dimensions). */
+size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
+                       int32_t capacity);
+
+/*
+ * Quantise n_new new K and V vectors per (sequence, KV head) and store them
+ * into the cache at token positions pos[b] + t, t = 0..n_new-1 (Open-TQ-Metal
+ * abstract: the cache is quantised to int4 on the fly).
+ *
+ *  k, v   device [B][H][n_new][D] fp16 or bf16 (dtype), contiguous.
+ *  pos    device int32 [B].  Contract: 0 <= pos[b] and
+ *         pos[b] + n_new <= capacity.  Tokens that fall outside
+ *         [0, capacity) are skipped (never written out of bounds).
+ *  Codes and scales of every token not in the range are left untouched,
+ *  including the neighbour that shares a V byte with a new token.
+ *  Host errors: OTQ_EINVAL (null pointer, n_new < 1, bad dtype),
+ *  OTQ_EUNSUPPORTED (head_dim), OTQ_ECAPACITY (n_new > capacity).
+ */
+int otq_quantize_append(const void *k, const void *v, int32_t dtype, int32_t n_new,
+                        const otq_cache *cache, const int32_t *pos, void *stream);
+
+/* Kernel variants of the split pass. */
+typedef enum otq_variant {
+    OTQ_VARIANT_AUTO = 0,
+    OTQ_VARIANT_VECTOR = 1, /* fp32 vector FMA; chosen for G <= 2            */
+    OTQ_VARIANT_MFMA = 2    /* fp16 MFMA 16x16x32 for the GQA contraction, G >= 4 */
+} otq_variant;
+
+/*
+ * Work split of one decode call (flash-decoding style): the token axis of
+ * every (sequence, KV head) is cut into chunks of `chunk` tokens; each chunk
+ * is one workgroup producing an unnormalised partial (m, l, o), and a second
+ * kernel merges the partials of each (sequence, query head).
+ */
+typedef struct otq_plan {
+    int32_t chunk;       /* tokens per split, multiple of 128 */
+    int32_t num_splits;  /* ceil(max_len / chunk), >= 1 */
+    int32_t variant;     /* OTQ_VARIANT_VECTOR or OTQ_VARIANT_MFMA */
+    int32_t reserved;
+    size_t workspace_bytes;
+} otq_plan;
+
+/*
+ * Choose the plan for a decode call.  chunk_override = 0 and
+ * variant_override = OTQ_VARIANT_AUTO pick defaults from the shape; nonzero
+ * values force them (chunk must be a positive multiple of 128).  Any valid
+ * plan gives the same result up to fp32 rounding.  Pure host arithmetic.
+ */
+int otq_sdpa_plan(int32_t num_q_heads, const otq_cache *cache, int32_t max_len,
+                  int32_t chunk_override, int32_t variant_override, otq_plan *plan);
+
+/* Workspace bytes otq_sdpa_int4_decode needs for the default plan (0 on error). */
+size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache *cache, int32_t max_len);
+
+/*
+ * Decode attention on the packed cache (Open-TQ-Metal abstract: attention
+ * computed directly on the compressed representation; zingnex page, section
+ * on compressed-domain attention):
+ *
+ *   out[b,h] = sum_t w_t V^[b,kv(h),t] / sum_t w_t,  t < lens[b]
+ *   w_t      = exp(S_t - max_u S_u),  S_t = scale * q'[b,h] . K^[b,kv(h),t]
+ *
+ * with K^ = code * s (V^ likewise), kv(h) = h / (num_q_heads / H), q' = q
+ * rotated as K was when cache->k_rot_signs != NULL.  lens[b] == 0 gives 0.
+ *
+ *  q        device [B][Hq][D] fp16/bf16 (dtype).
+ *  lens     device int32 [B]; values are clamped to [0, max_len].
+ *  max_len  host bound on lens, 1..capacity; sizes the split grid.
+ *  out      device fp32 [B][Hq][D].
+ *  workspace device scratch of at least otq_sdpa_workspace_bytes(...) bytes
+ *           (or plan->workspace_bytes); contents need no initialisation.
+ * Host errors: OTQ_EINVAL, OTQ_EUNSUPPORTED (head_dim, dtype, G > 16, or a
+ * forced variant that does not support G), OTQ_ECAPACITY (max_len >
+ * capacity), OTQ_EWORKSPACE.
+ */
+int otq_sdpa_int4_decode(const void *q, int32_t dtype, int32_t num_q_heads,
+                         const otq_cache *cache, const int32_t *lens, int32_t max_len,
+                         float scale, float *out, void *workspace, size_t workspace_bytes,
+                         void *stream);
+
+/* The same call with an explicit plan from otq_sdpa_plan (for tuning and
+ * split-invariance checks). */
+int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_heads,
+                                 const otq_cache *cache, const int32_t *lens,
+                                 int32_t max_len, float scale, float *out,
+                                 void *workspace, size_t workspace_bytes,
+                                 const otq_plan *plan, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* OTQ_H */

@@ -1,0 +1,226 @@
+"""Python binding of libotq: int4 KV-cache quantisation and decode attention
+on the packed cache, for AMD MI355X (gfx950).
+
+This module only marshals arguments: every step of the path runs in the HIP
+kernels of libotq.so (built in-tree by ``build.py``).  PyTorch is used for
+device memory and streams.  If the library is missing, importing the native
+entry points raises: there is no CPU or PyTorch fallback.
+
+The names mirror the C ABI in include/otq.h:
+``otq_quantize_append``, ``otq_sdpa_int4_decode``, ``otq_sdpa_plan``, ...
+``Int4KVCache`` is a convenience owner of the four cache arrays.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libotq.so")
+
+OTQ_OK, OTQ_EINVAL, OTQ_ECAPACITY, OTQ_EUNSUPPORTED, OTQ_EWORKSPACE, OTQ_EDEVICE = 0, -1, -2, -3, -4, -5
+OTQ_F16, OTQ_BF16 = 0, 1
+OTQ_VARIANT_AUTO, OTQ_VARIANT_VECTOR, OTQ_VARIANT_MFMA = 0, 1, 2
+OTQ_GROUP, OTQ_TILE = 32, 32
+
+EXPORTED = [
+    "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
+    "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
+    "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned",
+]
+
+
+class OtqError(RuntimeError):
+    def __init__(self, status, what=""):
+        self.status = status
+        super().__init__(f"{what}: {status_str(status)} ({status})")
+
+
+class otq_cache(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("capacity", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
+        ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
+        ("k_rot_signs", ctypes.c_void_p), ("rot_norm", ctypes.c_float),
+    ]
+
+
+class otq_plan(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("num_splits", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libotq.so; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"libotq.so not built at {LIB_PATH}: run int4_kv_cache_quant_amd/build.py "
+                          "(or __graft_entry__.build()); there is no fallback path")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, S = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    CP = ctypes.POINTER(otq_cache)
+    L.otq_status_str.argtypes = [ctypes.c_int]
+    L.otq_status_str.restype = ctypes.c_char_p
+    L.otq_abi_version.argtypes = []
+    L.otq_abi_version.restype = ctypes.c_int
+    L.otq_cache_array_bytes.argtypes = [I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(S)]
+    L.otq_cache_array_bytes.restype = ctypes.c_int
+    L.otq_cache_bytes.argtypes = [I, I, I, I]
+    L.otq_cache_bytes.restype = S
+    L.otq_quantize_append.argtypes = [P, P, I, I, CP, P, P]
+    L.otq_quantize_append.restype = ctypes.c_int
+    L.otq_sdpa_plan.argtypes = [I, CP, I, I, I, ctypes.POINTER(otq_plan)]
+    L.otq_sdpa_plan.restype = ctypes.c_int
+    L.otq_sdpa_workspace_bytes.argtypes = [I, CP, I]
+    L.otq_sdpa_workspace_bytes.restype = S
+    L.otq_sdpa_int4_decode.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, P, S, P]
+    L.otq_sdpa_int4_decode.restype = ctypes.c_int
+    L.otq_sdpa_int4_decode_planned.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, P, S,
+                                               ctypes.POINTER(otq_plan), P]
+    L.otq_sdpa_int4_decode_planned.restype = ctypes.c_int
+    _lib = L
+    return L
+
+
+def status_str(status):
+    return lib().otq_status_str(int(status)).decode()
+
+
+def _check(rc, what):
+    if rc != OTQ_OK:
+        raise OtqError(rc, what)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def dtype_code(dt):
+    if dt == torch.float16:
+        return OTQ_F16
+    if dt == torch.bfloat16:
+        return OTQ_BF16
+    raise TypeError(f"unsupported dtype {dt}: fp16 or bf16 only")
+
+
+# ---------------------------------------------------------------- raw ABI
+def otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity):
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity,
+                                       ctypes.byref(cb), ctypes.byref(sb)), "otq_cache_array_bytes")
+    return cb.value, sb.value
+
+
+def otq_cache_bytes(batch, num_kv_heads, head_dim, capacity):
+    return lib().otq_cache_bytes(batch, num_kv_heads, head_dim, capacity)
+
+
+def otq_quantize_append(k, v, cache_desc, pos, n_new=None, dtype=None, stream=None, check=True):
+    """k, v: device [B, Hkv, n_new, D] fp16/bf16; pos: device int32 [B]."""
+    n_new = k.shape[2] if n_new is None else n_new
+    dtype = dtype_code(k.dtype) if dtype is None else dtype
+    rc = lib().otq_quantize_append(_ptr(k), _ptr(v), dtype, n_new, ctypes.byref(cache_desc),
+                                   _ptr(pos), _stream(stream))
+    if check:
+        _check(rc, "otq_quantize_append")
+    return rc
+
+
+def otq_sdpa_plan(num_q_heads, cache_desc, max_len, chunk=0, variant=OTQ_VARIANT_AUTO, check=True):
+    p = otq_plan()
+    rc = lib().otq_sdpa_plan(num_q_heads, ctypes.byref(cache_desc), max_len, chunk, variant,
+                             ctypes.byref(p))
+    if check:
+        _check(rc, "otq_sdpa_plan")
+        return p
+    return rc, p
+
+
+def otq_sdpa_workspace_bytes(num_q_heads, cache_desc, max_len):
+    return lib().otq_sdpa_workspace_bytes(num_q_heads, ctypes.byref(cache_desc), max_len)
+
+
+def otq_sdpa_int4_decode(q, cache_desc, lens, max_len, scale, out, workspace, plan=None,
+                         num_q_heads=None, dtype=None, workspace_bytes=None, stream=None,
+                         check=True):
+    """q: device [B, Hq, D]; lens: device int32 [B]; out: device fp32 [B, Hq, D]."""
+    Hq = q.shape[1] if num_q_heads is None else num_q_heads
+    dtype = dtype_code(q.dtype) if dtype is None else dtype
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    if plan is None:
+        rc = lib().otq_sdpa_int4_decode(_ptr(q), dtype, Hq, ctypes.byref(cache_desc), _ptr(lens),
+                                        max_len, float(scale), _ptr(out), _ptr(workspace), wsb,
+                                        _stream(stream))
+    else:
+        rc = lib().otq_sdpa_int4_decode_planned(_ptr(q), dtype, Hq, ctypes.byref(cache_desc),
+                                                _ptr(lens), max_len, float(scale), _ptr(out),
+                                                _ptr(workspace), wsb, ctypes.byref(plan),
+                                                _stream(stream))
+    if check:
+        _check(rc, "otq_sdpa_int4_decode")
+    return rc
+
+
+# ---------------------------------------------------------------- owner
+class Int4KVCache:
+    """Owns the four device arrays of one layer's cache and its descriptor.
+
+    ``rot_signs`` (device float32 [D] of +-1) turns on the K rotation; the
+    normalisation is fp32(1/sqrt(D)).
+    """
+
+    def __init__(self, batch, num_kv_heads, head_dim, capacity, device="cuda", rot_signs=None):
+        cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity)
+        self.shape = (batch, num_kv_heads, head_dim, capacity)
+        g = head_dim // OTQ_GROUP
+        self.k_codes = torch.zeros((batch, num_kv_heads, capacity, head_dim // 2), dtype=torch.uint8, device=device)
+        self.k_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
+        self.v_codes = torch.zeros((batch, num_kv_heads, capacity // OTQ_TILE, 16 * head_dim), dtype=torch.uint8, device=device)
+        self.v_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
+        assert self.k_codes.numel() == cb and self.k_scales.numel() * 4 == sb
+        self.rot_signs = None if rot_signs is None else rot_signs.to(device=device, dtype=torch.float32).contiguous()
+        self.rot_norm = float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+        self.desc = otq_cache(batch, num_kv_heads, head_dim, capacity,
+                              self.k_codes.data_ptr(), self.k_scales.data_ptr(),
+                              self.v_codes.data_ptr(), self.v_scales.data_ptr(),
+                              None if self.rot_signs is None else self.rot_signs.data_ptr(),
+                              self.rot_norm)
+
+    @property
+    def nbytes(self):
+        return sum(t.numel() * t.element_size() for t in (self.k_codes, self.k_scales, self.v_codes, self.v_scales))
+
+    def append(self, k, v, pos, stream=None):
+        return otq_quantize_append(k, v, self.desc, pos, stream=stream)
+
+    def plan(self, num_q_heads, max_len, chunk=0, variant=OTQ_VARIANT_AUTO):
+        return otq_sdpa_plan(num_q_heads, self.desc, max_len, chunk, variant)
+
+    def workspace(self, num_q_heads, max_len, plan=None):
+        n = (plan.workspace_bytes if plan is not None
+             else otq_sdpa_workspace_bytes(num_q_heads, self.desc, max_len))
+        if n == 0:
+            raise OtqError(OTQ_EINVAL, "workspace size")
+        return torch.empty(n, dtype=torch.uint8, device=self.k_codes.device)
+
+    def decode(self, q, lens, max_len, scale, out=None, workspace=None, plan=None, stream=None):
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(q.shape[1], max_len, plan)
+        otq_sdpa_int4_decode(q, self.desc, lens, max_len, scale, out, workspace, plan=plan, stream=stream)
+        return out

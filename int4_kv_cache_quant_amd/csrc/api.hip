@@ -1,0 +1,216 @@
+// api.hip - the C ABI of libotq: host-side validation, planning and launch.
+//
+// Every argument the host can see is checked before the first HIP call, so a
+// bad call returns a status and touches no device state.  Nothing here
+// allocates: buffers, descriptors and the workspace belong to the caller
+// (the AdapTQ page, section on zero heap allocation, keeps its hot path free
+// of allocation for the same reason: predictable latency).
+#include <limits.h>
+#include <stdint.h>
+
+#include "../../include/otq.h"
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
+constexpr int kMaxChunk = 2048;
+constexpr int kTargetGroups = 512;  // split workgroups aimed for (2 per CU)
+
+bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
+
+int check_dims(int32_t B, int32_t H, int32_t D, int32_t cap)
+{
+    if (B < 1 || H < 1 || cap < OTQ_TILE || cap % OTQ_TILE != 0) return OTQ_EINVAL;
+    if (!supported_dim(D)) return OTQ_EUNSUPPORTED;
+    // element offsets are formed in 64-bit; keep each array below 2^62 bytes
+    const unsigned __int128 n = (unsigned __int128)B * H * cap * D;
+    if (n > ((unsigned __int128)1 << 62)) return OTQ_EINVAL;
+    return OTQ_OK;
+}
+
+int check_cache(const otq_cache* c)
+{
+    if (!c) return OTQ_EINVAL;
+    const int rc = check_dims(c->batch, c->num_kv_heads, c->head_dim, c->capacity);
+    if (rc != OTQ_OK) return rc;
+    if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) return OTQ_EINVAL;
+    return OTQ_OK;
+}
+
+int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
+              int32_t variant_ov, otq_plan* p)
+{
+    int rc = check_cache(c);
+    if (rc != OTQ_OK) return rc;
+    if (!p || Hq < 1 || Hq % c->num_kv_heads != 0 || max_len < 1) return OTQ_EINVAL;
+    if (max_len > c->capacity) return OTQ_ECAPACITY;
+    const int G = Hq / c->num_kv_heads;
+    const int D = c->head_dim;
+    if (G > 16) return OTQ_EUNSUPPORTED;
+
+    int variant = variant_ov;
+    if (variant == OTQ_VARIANT_AUTO) {
+        variant = (G >= 4 && otq::split_mfma_supports(D, G)) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
+    }
+    if (variant == OTQ_VARIANT_VECTOR) {
+        if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;
+    } else if (variant == OTQ_VARIANT_MFMA) {
+        if (!otq::split_mfma_supports(D, G)) return OTQ_EUNSUPPORTED;
+    } else {
+        return OTQ_EINVAL;
+    }
+
+    int chunk = chunk_ov;
+    if (chunk == 0) {
+        const long long units = (long long)c->batch * c->num_kv_heads;
+        long long want = ((long long)max_len * units + kTargetGroups - 1) / kTargetGroups;
+        want = (want + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        if (want < kChunkAlign) want = kChunkAlign;
+        if (want > kMaxChunk) want = kMaxChunk;
+        chunk = (int)want;
+    } else if (chunk < 0 || chunk % kChunkAlign != 0) {
+        return OTQ_EINVAL;
+    }
+    const long long S = ((long long)max_len + chunk - 1) / chunk;
+    const unsigned __int128 rows = (unsigned __int128)c->batch * Hq * S;
+    const unsigned __int128 o_bytes = rows * D * sizeof(float);
+    const unsigned __int128 o_aligned = (o_bytes + 255) / 256 * 256;
+    const unsigned __int128 total = o_aligned + rows * 2 * sizeof(float);
+    if (total > ((unsigned __int128)1 << 62)) return OTQ_EINVAL;
+    p->chunk = chunk;
+    p->num_splits = (int32_t)S;
+    p->variant = variant;
+    p->reserved = 0;
+    p->workspace_bytes = (size_t)total;
+    return OTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* otq_status_str(int status)
+{
+    switch (status) {
+    case OTQ_OK: return "OTQ_OK";
+    case OTQ_EINVAL: return "OTQ_EINVAL: invalid argument";
+    case OTQ_ECAPACITY: return "OTQ_ECAPACITY: length exceeds cache capacity";
+    case OTQ_EUNSUPPORTED: return "OTQ_EUNSUPPORTED: unsupported head_dim, dtype or head grouping";
+    case OTQ_EWORKSPACE: return "OTQ_EWORKSPACE: workspace missing or too small";
+    case OTQ_EDEVICE: return "OTQ_EDEVICE: HIP launch failed";
+    default: return "unknown otq status";
+    }
+}
+
+int otq_abi_version(void) { return OTQ_ABI_VERSION; }
+
+int otq_cache_array_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, size_t* codes_bytes,
+                          size_t* scales_bytes)
+{
+    const int rc = check_dims(B, H, D, cap);
+    if (rc != OTQ_OK) return rc;
+    const size_t n = (size_t)B * H * cap;
+    if (codes_bytes) *codes_bytes = n * (size_t)(D / 2);
+    if (scales_bytes) *scales_bytes = n * (size_t)(D / OTQ_GROUP) * sizeof(float);
+    return OTQ_OK;
+}
+
+size_t otq_cache_bytes(int32_t B, int32_t H, int32_t D, int32_t cap)
+{
+    size_t cb = 0, sb = 0;
+    if (otq_cache_array_bytes(B, H, D, cap, &cb, &sb) != OTQ_OK) return 0;
+    return 2 * (cb + sb);
+}
+
+int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_new,
+                        const otq_cache* cache, const int32_t* pos, void* stream)
+{
+    const int rc = check_cache(cache);
+    if (rc != OTQ_OK) return rc;
+    if (!k || !v || !pos || n_new < 1) return OTQ_EINVAL;
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (n_new > cache->capacity) return OTQ_ECAPACITY;
+    const hipError_t e = otq::launch_quantize_append(
+        k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
+        cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
+        cache->rot_norm, pos, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+}
+
+int otq_sdpa_plan(int32_t num_q_heads, const otq_cache* cache, int32_t max_len,
+                  int32_t chunk_override, int32_t variant_override, otq_plan* plan)
+{
+    return make_plan(num_q_heads, cache, max_len, chunk_override, variant_override, plan);
+}
+
+size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache* cache, int32_t max_len)
+{
+    otq_plan p;
+    if (make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &p) != OTQ_OK) return 0;
+    return p.workspace_bytes;
+}
+
+int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_heads,
+                                 const otq_cache* cache, const int32_t* lens, int32_t max_len,
+                                 float scale, float* out, void* workspace, size_t workspace_bytes,
+                                 const otq_plan* plan, void* stream)
+{
+    if (!plan) return OTQ_EINVAL;
+    otq_plan chk;
+    int rc = make_plan(num_q_heads, cache, max_len, plan->chunk, plan->variant, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (!q || !lens || !out) return OTQ_EINVAL;
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
+        return OTQ_EINVAL;
+    if (!workspace || workspace_bytes < chk.workspace_bytes) return OTQ_EWORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return OTQ_EWORKSPACE;
+
+    const int D = cache->head_dim;
+    const size_t rows = (size_t)cache->batch * num_q_heads * chk.num_splits;
+    const size_t o_aligned = (rows * D * sizeof(float) + 255) / 256 * 256;
+    otq::SplitArgs a;
+    a.q = q;
+    a.dtype = dtype;
+    a.B = cache->batch;
+    a.Hq = num_q_heads;
+    a.H = cache->num_kv_heads;
+    a.D = D;
+    a.cap = cache->capacity;
+    a.kc = cache->k_codes;
+    a.ks = cache->k_scales;
+    a.vc = cache->v_codes;
+    a.vs = cache->v_scales;
+    a.signs = cache->k_rot_signs;
+    a.rot_norm = cache->rot_norm;
+    a.lens = lens;
+    a.max_len = max_len;
+    a.qscale = scale * otq::kLog2eHost;
+    a.chunk = chk.chunk;
+    a.num_splits = chk.num_splits;
+    a.part_o = static_cast<float*>(workspace);
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_aligned);
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
+                                                   : otq::launch_split_vector(a, s);
+    if (e != hipSuccess) return OTQ_EDEVICE;
+    e = otq::launch_lse_combine(a.part_o, a.part_ml, lens, max_len, chk.chunk, chk.num_splits,
+                                a.B, num_q_heads, D, out, s);
+    return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+}
+
+int otq_sdpa_int4_decode(const void* q, int32_t dtype, int32_t num_q_heads,
+                         const otq_cache* cache, const int32_t* lens, int32_t max_len,
+                         float scale, float* out, void* workspace, size_t workspace_bytes,
+                         void* stream)
+{
+    otq_plan p;
+    const int rc = make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &p);
+    if (rc != OTQ_OK) return rc;
+    return otq_sdpa_int4_decode_planned(q, dtype, num_q_heads, cache, lens, max_len, scale, out,
+                                        workspace, workspace_bytes, &p, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,46 @@
+// kernels.hpp - internal launchers of the gfx950 kernels (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace otq {
+
+constexpr float kLog2eHost = 1.4426950408889634f;
+
+hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
+                                  int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
+                                  const float* signs, float rot_norm, const int32_t* pos,
+                                  hipStream_t stream);
+
+// Split pass arguments shared by both variants.
+struct SplitArgs {
+    const void* q;
+    int dtype;
+    int B, Hq, H, D, cap;
+    const uint8_t* kc;
+    const float* ks;
+    const uint8_t* vc;
+    const float* vs;
+    const float* signs;
+    float rot_norm;
+    const int32_t* lens;
+    int max_len;
+    float qscale;  // softmax scale * log2(e): scores are kept in the log2 domain
+    int chunk;
+    int num_splits;
+    float* part_o;   // [B][Hq][S][D]
+    float2* part_ml; // [B][Hq][S] (m, l)
+};
+
+// Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
+hipError_t launch_split_vector(const SplitArgs& a, hipStream_t stream);
+hipError_t launch_split_mfma(const SplitArgs& a, hipStream_t stream);
+bool split_vector_supports(int D, int G);
+bool split_mfma_supports(int D, int G);
+
+hipError_t launch_lse_combine(const float* part_o, const float2* part_ml, const int32_t* lens,
+                              int max_len, int chunk, int num_splits, int B, int Hq, int D,
+                              float* out, hipStream_t stream);
+
+}  // namespace otq

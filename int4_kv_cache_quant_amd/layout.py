@@ -1,0 +1,57 @@
+"""Index maps between the V-code tile layout of the cache and the plain
+token-major layout (pure permutations of nibbles; no arithmetic).
+
+Plain layout: codes[..., token, D/2], byte j = element 2j (low nibble) and
+2j+1 (high nibble).  Tile layout (include/otq.h): per tile of 32 tokens,
+16*D bytes; tile-relative token u has quarter r = (u % 16) // 4 and slot
+j = 4 * (u // 16) + u % 4; channel c = 16 * (4a + b) + n owns word
+((a*4 + r)*16 + n)*4 + b; slot j is nibble j % 2 of byte j // 2 of that word.
+"""
+import functools
+
+import numpy as np
+
+
+@functools.lru_cache(maxsize=None)
+def _tile_maps(D):
+    o = np.arange(16 * D)
+    word, byte = o // 4, o % 4
+    b = word % 4
+    n = (word // 4) % 16
+    r = (word // 64) % 4
+    a = word // 256
+    c = 16 * (4 * a + b) + n
+    # nibble x of tile byte o holds slot j = 2 * byte + x
+    us, cs = [], []
+    for x in (0, 1):
+        j = 2 * byte + x
+        us.append(16 * (j // 4) + 4 * r + (j % 4))
+        cs.append(c)
+    return np.stack(us, -1), np.stack(cs, -1)   # [16D, 2] token, channel
+
+
+def _nibbles(packed):
+    p = np.asarray(packed, np.uint8)
+    return np.stack([p & 0xF, p >> 4], -1)
+
+
+def v_tiled_to_plain(tiled, D):
+    """[..., C/32, 16*D] tile layout -> [..., C, D/2] plain layout."""
+    tiled = np.asarray(tiled, np.uint8)
+    lead, ntile = tiled.shape[:-2], tiled.shape[-2]
+    u, c = _tile_maps(D)
+    nib = _nibbles(tiled)                                    # [..., ntile, 16D, 2]
+    plain = np.zeros(lead + (ntile, 32, D), np.uint8)
+    plain[..., u, c] = nib
+    plain = plain.reshape(lead + (ntile * 32, D // 2, 2))
+    return (plain[..., 0] | (plain[..., 1] << 4)).astype(np.uint8)
+
+
+def v_plain_to_tiled(plain, D):
+    """[..., C, D/2] plain layout -> [..., C/32, 16*D] tile layout."""
+    plain = np.asarray(plain, np.uint8)
+    lead, C = plain.shape[:-2], plain.shape[-2]
+    nib = _nibbles(plain).reshape(lead + (C // 32, 32, D))
+    u, c = _tile_maps(D)
+    t = nib[..., u, c]                                       # [..., C/32, 16D, 2]
+    return (t[..., 0] | (t[..., 1] << 4)).astype(np.uint8)

@@ -1,0 +1,145 @@
+"""CPU tests of libotq's C ABI: it loads, exports every declared symbol, and
+rejects bad arguments on the host (no GPU is touched by these calls)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import int4_kv_cache_quant_amd as otq
+from int4_kv_cache_quant_amd import layout
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "otq.h")
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+FAKE = 0x10000  # never dereferenced: every call below fails host validation first
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(otq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = otq.lib()
+    names = _declared_functions()
+    assert set(names) == set(otq.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.otq_abi_version() == 1
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5):
+        assert otq.status_str(s).startswith("OTQ_")
+    assert "unknown" in otq.status_str(7)
+
+
+def _desc(B=1, H=2, D=128, cap=64, signs=None):
+    return otq.otq_cache(B, H, D, cap, FAKE, FAKE, FAKE, FAKE, signs, 0.0883883)
+
+
+def test_cache_bytes_closed_form_llama70b_128k():
+    g = json.load(open(os.path.join(GOLDEN, "storage_closed_forms.json")))["llama31_70b_128k"]
+    per_layer = otq.otq_cache_bytes(1, g["kv_heads"], g["head_dim"], g["tokens"])
+    assert per_layer * g["layers"] == g["int4_bytes"]
+    fp16 = g["layers"] * g["kv_heads"] * g["head_dim"] * g["tokens"] * 2 * 2
+    assert fp16 / (per_layer * g["layers"]) == g["ratio"]
+    cb, sb = otq.otq_cache_array_bytes(1, 8, 128, 131072)
+    assert 2 * cb == 134217728 and 2 * sb == 33554432   # K + V codes, K + V scales
+
+
+def test_cache_bytes_rejects_bad_dims():
+    lib = otq.lib()
+    c, s = ctypes.c_size_t(), ctypes.c_size_t()
+    assert lib.otq_cache_array_bytes(1, 1, 96, 64, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EUNSUPPORTED
+    assert lib.otq_cache_array_bytes(1, 1, 128, 48, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
+    assert lib.otq_cache_array_bytes(0, 1, 128, 64, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
+    assert lib.otq_cache_bytes(1, 1, 100, 64) == 0
+
+
+def test_quantize_append_host_errors():
+    lib = otq.lib()
+    d = _desc()
+    P = ctypes.c_void_p
+    call = lambda k, v, dt, n, desc, pos: lib.otq_quantize_append(P(k), P(v), dt, n, ctypes.byref(desc), P(pos), None)
+    assert call(0, FAKE, 1, 1, d, FAKE) == otq.OTQ_EINVAL
+    assert call(FAKE, FAKE, 1, 1, d, 0) == otq.OTQ_EINVAL
+    assert call(FAKE, FAKE, 1, 0, d, FAKE) == otq.OTQ_EINVAL
+    assert call(FAKE, FAKE, 2, 1, d, FAKE) == otq.OTQ_EUNSUPPORTED
+    assert call(FAKE, FAKE, 1, 65, d, FAKE) == otq.OTQ_ECAPACITY
+    assert call(FAKE, FAKE, 1, 1, _desc(D=96), FAKE) == otq.OTQ_EUNSUPPORTED
+    assert call(FAKE, FAKE, 1, 1, _desc(cap=40), FAKE) == otq.OTQ_EINVAL
+    bad = _desc()
+    bad.v_scales = None
+    assert call(FAKE, FAKE, 1, 1, bad, FAKE) == otq.OTQ_EINVAL
+    assert lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, None, P(FAKE), None) == otq.OTQ_EINVAL
+
+
+def test_plan_defaults_and_errors():
+    d = _desc(B=1, H=8, D=128, cap=131072)
+    p = otq.otq_sdpa_plan(16, d, 131072)
+    assert p.chunk % 128 == 0 and p.num_splits == -(-131072 // p.chunk)
+    rows = 16 * p.num_splits
+    assert p.workspace_bytes == -(-rows * 128 * 4 // 256) * 256 + rows * 8
+    assert otq.otq_sdpa_workspace_bytes(16, d, 131072) == p.workspace_bytes
+    p = otq.otq_sdpa_plan(8, d, 1000, chunk=256, variant=otq.OTQ_VARIANT_VECTOR, check=False)[1]
+    assert (p.chunk, p.num_splits, p.variant) == (256, 4, otq.OTQ_VARIANT_VECTOR)
+    rc = lambda *a, **k: otq.otq_sdpa_plan(*a, check=False, **k)[0]
+    assert rc(60, d, 100) == otq.OTQ_EINVAL              # Hq % Hkv
+    assert rc(8 * 17, d, 100) == otq.OTQ_EUNSUPPORTED    # G > 16
+    assert rc(16, d, 131073) == otq.OTQ_ECAPACITY
+    assert rc(16, d, 0) == otq.OTQ_EINVAL
+    assert rc(16, d, 100, chunk=100) == otq.OTQ_EINVAL
+    assert rc(16, d, 100, variant=7) == otq.OTQ_EINVAL
+    assert otq.otq_sdpa_workspace_bytes(60, d, 100) == 0
+
+
+def test_decode_host_errors():
+    lib = otq.lib()
+    d = _desc(B=2, H=2, D=128, cap=256)
+    p = otq.otq_sdpa_plan(4, d, 256)
+    P = ctypes.c_void_p
+
+    def call(q=FAKE, dt=1, Hq=4, desc=d, lens=FAKE, max_len=256, scale=0.1, out=FAKE, ws=4096,
+             wsb=None):
+        wsb = p.workspace_bytes if wsb is None else wsb
+        return lib.otq_sdpa_int4_decode(P(q), dt, Hq, ctypes.byref(desc), P(lens), max_len, scale,
+                                        P(out), P(ws), wsb, None)
+    assert call(q=0) == otq.OTQ_EINVAL
+    assert call(lens=0) == otq.OTQ_EINVAL
+    assert call(out=0) == otq.OTQ_EINVAL
+    assert call(dt=3) == otq.OTQ_EUNSUPPORTED
+    assert call(max_len=257) == otq.OTQ_ECAPACITY
+    assert call(Hq=3) == otq.OTQ_EINVAL
+    assert call(scale=float("nan")) == otq.OTQ_EINVAL
+    assert call(ws=0) == otq.OTQ_EWORKSPACE
+    assert call(wsb=p.workspace_bytes - 1) == otq.OTQ_EWORKSPACE
+    assert call(ws=4096 + 4) == otq.OTQ_EWORKSPACE       # workspace must be 256-byte aligned
+    assert lib.otq_sdpa_int4_decode_planned(P(FAKE), 1, 4, ctypes.byref(d), P(FAKE), 256, 0.1,
+                                            P(FAKE), P(4096), p.workspace_bytes, None, None) == otq.OTQ_EINVAL
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_v_layout_roundtrip_and_fixed_points(D):
+    rng = np.random.default_rng(0)
+    plain = rng.integers(0, 256, (2, 3, 64, D // 2), dtype=np.uint8)
+    tiled = layout.v_plain_to_tiled(plain, D)
+    assert tiled.shape == (2, 3, 2, 16 * D)
+    assert np.array_equal(layout.v_tiled_to_plain(tiled, D), plain)
+    # hand-worked positions: token u=0, channel 0 -> word 0 byte 0 low nibble;
+    # u=1 -> same byte, high nibble; u=16 (slot 4) -> byte 2; u=4 (quarter 1)
+    # -> word (1*16 + 0)*4 = 64; channel 17 (cb 1, n 1) -> word 1*4 + 1 = 5.
+    p = np.zeros((32, D // 2), np.uint8)
+    p[0, 0] = 0x03          # token 0: ch0 = 3, ch1 = 0
+    p[1, 0] = 0x05          # token 1: ch0 = 5
+    p[16, 0] = 0x07         # token 16: ch0 = 7
+    p[4, 0] = 0x01          # token 4: ch0 = 1
+    p[0, 8] = 0x20          # token 0: ch17 = 2
+    t = layout.v_plain_to_tiled(p, D)[0]
+    assert t[0] == 0x53 and t[2] == 0x07 and t[64 * 4] == 0x01 and t[5 * 4] == 0x02
+    assert np.count_nonzero(t) == 4

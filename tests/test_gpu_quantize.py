@@ -1,0 +1,124 @@
+"""GPU parity of otq_quantize_append: codes and scales bit-exact against the
+CPU oracle (the oracle sees the same 16-bit inputs; nothing it uses comes
+from the GPU path)."""
+import numpy as np
+import pytest
+import torch
+
+import int4_kv_cache_quant_amd as otq
+from int4_kv_cache_quant_amd import synth
+
+from gpu_common import (build_cache, compare_codes, host_cache, oracle_cache, rot_norm32, say,
+                        to_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _rand_kv(B, H, T, D, dtype, seed, sigma=1.0, outliers=(3,)):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((2, B, H, T, D), generator=g) * sigma
+    for c in outliers:
+        x[..., c] *= 10
+    x = x.to(dtype)
+    return x[0].to(DEV), x[1].to(DEV)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantize_bit_exact(D, dtype, rotate):
+    B, H, T, cap = 2, 3, 77, 96
+    say(f"quantize D={D} dtype={dtype} rotate={rotate}")
+    k, v = _rand_kv(B, H, T, D, dtype, seed=D + 7 * rotate)
+    signs = None
+    if rotate:
+        s = torch.where(torch.rand(D, generator=torch.Generator().manual_seed(D)) < 0.5, -1.0, 1.0)
+        signs = s.to(DEV)
+    cache = build_cache(k, v, cap, signs=signs, prefill_chunk=19)
+    torch.cuda.synchronize()
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    ref = oracle_cache(k.cpu(), v.cpu(), name, None if signs is None else signs.cpu().numpy(),
+                       rot_norm32(D))
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
+def test_quantize_adversarial_values():
+    """Ties at every half-step, zero groups, subnormal groups, -0.0, abs-max
+    in every lane position, fp16 inputs."""
+    D, B, H = 128, 1, 1
+    rows = []
+    for pos in range(32):                       # abs-max at each position of the group
+        x = np.zeros(D, np.float32)
+        x[:32] = (np.arange(32) % 15 - 7) / 2.0  # k/2 ties
+        x[pos] = 7.0
+        x[32:64] = np.float32(-0.0)             # -0 group -> zero scale
+        x[64:96] = np.float32(1e-6) * (np.arange(32) - 16)   # fp16 subnormals
+        x[96:128] = 3.5 * ((-1.0) ** np.arange(32))            # all ties at abs-max/2
+        rows.append(x)
+    x = torch.tensor(np.stack(rows), dtype=torch.float16)[None, None]   # [1,1,32,D]
+    T = x.shape[2]
+    k = x.to(DEV)
+    v = (-x).to(DEV)
+    say("quantize adversarial")
+    cache = build_cache(k, v, 32, prefill_chunk=5)
+    torch.cuda.synchronize()
+    ref = oracle_cache(x, -x, "fp16")
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
+def test_append_preserves_neighbours_and_skips_out_of_range():
+    """Single-token appends at odd and even positions keep the other nibble of
+    each shared V byte; positions outside [0, capacity) are not written."""
+    D, B, H, cap = 128, 3, 2, 64
+    k, v = _rand_kv(B, H, cap, D, torch.bfloat16, seed=5)
+    cache = otq.Int4KVCache(B, H, D, cap, device=DEV)
+    order = np.random.default_rng(0).permutation(cap)      # scattered single appends
+    for t in order:
+        pos = torch.full((B,), int(t), dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t:t + 1].contiguous(), v[:, :, t:t + 1].contiguous(), pos)
+    torch.cuda.synchronize()
+    ref = oracle_cache(k.cpu(), v.cpu(), "bf16")
+    assert compare_codes(host_cache(cache), ref, cap) == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    before = [t.clone() for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales)]
+    # straddling the end: 4 tokens at pos cap-2 -> only cap-2, cap-1 are written
+    pos = torch.tensor([cap - 2, -3, cap], dtype=torch.int32, device=DEV)
+    k2, v2 = _rand_kv(B, H, 4, D, torch.bfloat16, seed=6)
+    cache.append(k2, v2, pos)
+    torch.cuda.synchronize()
+    after = [t for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales)]
+    # sequence 1 (pos -3: tokens -3..0) writes only token 0; sequence 2 writes nothing
+    assert torch.equal(before[0][2], after[0][2]) and torch.equal(before[2][2], after[2][2])
+    assert torch.equal(before[0][1, :, 1:], after[0][1, :, 1:])
+    assert torch.equal(before[1][0, :, :cap - 2], after[1][0, :, :cap - 2])
+    kk = torch.cat([k[:, :, :cap - 2].cpu(), k2[:, :, :2].cpu()], 2)[0:1]
+    vv = torch.cat([v[:, :, :cap - 2].cpu(), v2[:, :, :2].cpu()], 2)[0:1]
+    ref0 = oracle_cache(kk, vv, "bf16")
+    got = tuple(a[0:1] for a in host_cache(cache))
+    assert compare_codes(got, ref0, cap) == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    k1 = k[1:2, :, :].cpu().clone()
+    v1 = v[1:2, :, :].cpu().clone()
+    k1[:, :, 0] = k2[1:2, :, 3].cpu()
+    v1[:, :, 0] = v2[1:2, :, 3].cpu()
+    ref1 = oracle_cache(k1, v1, "bf16")
+    got = tuple(a[1:2] for a in host_cache(cache))
+    assert compare_codes(got, ref1, cap) == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+
+
+@pytest.mark.parametrize("cfg", [1, 4, 5])
+def test_quantize_full_size_workloads(cfg):
+    """Every token of one layer of the workload, at its full size."""
+    w = synth.WORKLOADS[cfg]
+    say(f"quantize full workload {cfg} {w.name}")
+    k = synth.kv(w, 0, "k", device=DEV)
+    v = synth.kv(w, 0, "v", device=DEV)
+    signs = torch.from_numpy(synth.rot_signs(w, 0)).to(DEV) if w.rotate else None
+    cache = build_cache(k, v, w.capacity, signs=signs, prefill_chunk=8192)
+    torch.cuda.synchronize()
+    ref = oracle_cache(k.cpu(), v.cpu(), w.dtype,
+                       None if signs is None else signs.cpu().numpy(), rot_norm32(w.D), threads=16)
+    bad = compare_codes(host_cache(cache), ref, w.T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad

@@ -1,0 +1,171 @@
+"""GPU parity of otq_sdpa_int4_decode against the fp64 CPU oracle.
+
+Tolerance (fp32 outputs vs the fp64 oracle): max-abs <= 2e-3 and relative
+L2 <= 1e-3 per checked set of rows.  The oracle reads a cache it quantised
+itself from the same 16-bit inputs (after the quantiser's bit-exactness is
+checked), so no oracle input comes from the GPU path."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int4_kv_cache_quant_amd as otq
+import oracle
+from int4_kv_cache_quant_amd import synth
+
+from gpu_common import (MAX_ABS, REL_L2, build_cache, compare_codes, errors, host_cache,
+                        oracle_cache, rot_norm32, say, to_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((2, B, Hkv, cap, D), generator=g) * sigma
+    oc = torch.randperm(D, generator=g)[:n_out]
+    x[..., oc] *= 10
+    x = x.to(dtype)
+    q = torch.randn((B, Hq, D), generator=g).to(dtype)
+    signs = None
+    if rotate:
+        signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
+    return x[0], x[1], q, signs
+
+
+def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
+         rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None):
+    k, v, q, signs = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    cache = build_cache(k.to(DEV), v.to(DEV), cap, signs=None if signs is None else signs.to(DEV),
+                        prefill_chunk=max(1, cap // 3))
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    max_len = max(1, int(max(lens)))
+    plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
+    say(f"sdpa B={B} Hq={Hq} Hkv={Hkv} D={D} cap={cap} chunk={plan.chunk} "
+        f"splits={plan.num_splits} variant={plan.variant} rotate={rotate}")
+    out = cache.decode(q.to(DEV), lens_t, max_len, scale, plan=plan)
+    torch.cuda.synchronize()
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D))
+    assert compare_codes(host_cache(cache), ref_cache, cap) == {
+        "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    kc, ks, vc, vs = ref_cache
+    ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(lens, np.int32), scale,
+                      signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
+                      rows=rows, threads=8)
+    got = out.cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got = got.reshape(-1, D)[rows]
+    return got, ref, plan
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_sdpa_small_parity(D, G):
+    if D == 256 and G == 4:
+        pytest.skip("vector variant does not build G=4 at D=256")
+    Hkv = 2
+    got, ref, _ = _run(2, G * Hkv, Hkv, D, 320, [300, 77], seed=D + G,
+                       variant=otq.OTQ_VARIANT_VECTOR, chunk=128)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("lens", [[0, 5], [1, 1], [31, 32], [33, 160], [160, 0]])
+def test_sdpa_edge_lengths(lens):
+    got, ref, _ = _run(2, 4, 2, 128, 160, lens, seed=sum(lens), variant=otq.OTQ_VARIANT_VECTOR,
+                       chunk=128)
+    ma, rel = errors(got, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert np.all(got[b] == 0.0)
+
+
+@pytest.mark.parametrize("chunk", [128, 256, 384, 1024])
+def test_sdpa_split_invariance(chunk):
+    got, ref, plan = _run(1, 2, 1, 128, 1024, [1000], seed=11, chunk=chunk,
+                          variant=otq.OTQ_VARIANT_VECTOR)
+    ma, rel = errors(got, ref)
+    assert plan.num_splits == -(-1000 // chunk)
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_sdpa_fp16_rotated_and_scale_one():
+    got, ref, _ = _run(3, 4, 2, 128, 256, [256, 200, 9], dtype=torch.float16, seed=3, rotate=True)
+    ma, rel = errors(got, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2
+    got, ref, _ = _run(1, 4, 2, 256, 512, [500], seed=4, scale=1.0, sigma=0.5)
+    ma, rel = errors(got, ref)
+    say(f"  scale=1 max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_sdpa_deterministic():
+    k, v, q, _ = _case(1, 2, 1, 128, 512, torch.bfloat16, 9)
+    cache = build_cache(k.to(DEV), v.to(DEV), 512)
+    lens = torch.tensor([512], dtype=torch.int32, device=DEV)
+    a = cache.decode(q.to(DEV), lens, 512, 0.1)
+    b = cache.decode(q.to(DEV), lens, 512, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+# -------------------------------------------------------------- full workloads
+
+def _full(cfg, rows_per_seq=None, layer=0):
+    w = synth.WORKLOADS[cfg]
+    say(f"sdpa full workload {cfg} {w.name}")
+    k = synth.kv(w, layer, "k", device=DEV)
+    v = synth.kv(w, layer, "v", device=DEV)
+    q = synth.query(w, layer, device=DEV)
+    lens = synth.lens(w, layer)
+    signs = torch.from_numpy(synth.rot_signs(w, layer)).to(DEV) if w.rotate else None
+    cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs)
+    # prefill lens-1 tokens per sequence, then append token lens-1 (ragged-aware)
+    for t0 in range(0, w.T, 8192):
+        t1 = min(w.T, t0 + 8192)
+        pos = torch.full((w.B,), t0, dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t0:t1].contiguous(), v[:, :, t0:t1].contiguous(), pos)
+    lens_t = torch.from_numpy(lens).to(DEV)
+    idx = (lens_t.long() - 1).clamp(min=0)
+    kn = k[torch.arange(w.B, device=DEV), :, idx][:, :, None].contiguous()
+    vn = v[torch.arange(w.B, device=DEV), :, idx][:, :, None].contiguous()
+    cache.append(kn, vn, (lens_t - 1).clamp(min=0))
+    out = cache.decode(q, lens_t, int(lens.max()), w.scale)
+    torch.cuda.synchronize()
+    ref_cache = oracle_cache(k.cpu(), v.cpu(), w.dtype,
+                             None if signs is None else signs.cpu().numpy(), rot_norm32(w.D),
+                             threads=16)
+    assert compare_codes(host_cache(cache), ref_cache, w.T) == {
+        "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    rng = np.random.default_rng(cfg)
+    if rows_per_seq is None:
+        rows = np.arange(w.B * w.Hq, dtype=np.int32)
+    else:
+        rows = np.sort(np.concatenate([b * w.Hq + rng.choice(w.Hq, rows_per_seq, replace=False)
+                                       for b in range(w.B)])).astype(np.int32)
+    kc, ks, vc, vs = ref_cache
+    ref = oracle.sdpa(to_bits(q), w.dtype, kc, ks, vc, vs, lens, w.scale,
+                      signs=None if signs is None else signs.cpu().numpy(),
+                      rot_norm=rot_norm32(w.D), rows=rows, threads=16)
+    got = out.cpu().numpy().reshape(-1, w.D)[rows].astype(np.float64)
+    ma, rel = errors(got, ref)
+    say(f"  rows={len(rows)} max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_full_workload_1_tiny():
+    _full(1)
+
+
+def test_full_workload_4_gemma_scale1():
+    _full(4, rows_per_seq=8)
+
+
+def test_full_workload_5_ragged_rotated():
+    _full(5, rows_per_seq=2)

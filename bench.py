@@ -1,0 +1,289 @@
+#!/usr/bin/env python3
+"""Decode benchmark of the int4 KV-cache attention path on one MI355X.
+
+Metric: sdpa_int4 decode microseconds per layer-step and the achieved HBM
+bandwidth of the split kernel, on the Llama-3.1-70B-shaped layer at 128K
+context (64 query heads / 8 KV heads, head_dim 128, bf16 inputs), cycling
+over 80 distinct caches (12.5 GiB, far larger than the 256 MB last-level
+cache, so every step streams from HBM).
+
+A step is one pass of the whole hot path over every layer: quantise-append
+the new token into the layer's cache, split pass, LSE combine.  The step is
+captured once in a HIP graph and replayed.  Inputs are synthetic and seeded
+(int4_kv_cache_quant_amd.synth); they are resident in HBM before timing.
+
+Prints one JSON line.  The CPU oracle is timed on the host on one full
+layer-step (all query heads of layer 0), which doubles as a parity check of
+the GPU outputs of that layer.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sdpa_int4 decode µs/layer-step + achieved HBM GB/s (% peak) at 128K ctx"
+HBM_PEAK_GBPS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    2: ["int4_kv_cache_quant_amd/csrc/sdpa_mfma.hip", "int4_kv_cache_quant_amd/csrc/common.hpp"],
+    1: ["int4_kv_cache_quant_amd/csrc/sdpa_vec.hip", "int4_kv_cache_quant_amd/csrc/common.hpp"],
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(variant):
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[variant]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(variant, workload_name):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None
+    when the kernel source changed since they were taken."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{'split_mfma' if variant == 2 else 'split_vec'}_{workload_name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha") != source_sha(variant):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, help="workload number (3 = 70B layer at 128K)")
+    ap.add_argument("--layers", type=int, default=None, help="distinct caches (default: the workload's)")
+    ap.add_argument("--chunk", type=int, default=0, help="force the split chunk (0 = planner default)")
+    ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-threads", type=int, default=None)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures a single GPU: --gpus {args.gpus} / WORLD_SIZE {world} is not "
+              "supported (the decode path has no multi-GPU component; see the sharding notes "
+              "in the design document).", file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import int4_kv_cache_quant_amd as otq
+    from int4_kv_cache_quant_amd import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    otq.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = synth.WORKLOADS[args.workload]
+    L = w.layers if args.layers is None else args.layers
+    log(f"bench: workload {args.workload} {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+        f"T={w.T} layers={L}")
+
+    # ---------------------------------------------------------------- setup
+    t_setup = time.time()
+    caches, k_new, v_new, qs, lens_l, pos_l = [], [], [], [], [], []
+    host_kv0 = None
+    for l in range(L):
+        signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if w.rotate else None
+        cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs)
+        k = synth.kv(w, l, "k", device=dev)
+        v = synth.kv(w, l, "v", device=dev)
+        lens = synth.lens(w, l)
+        lens_t = torch.from_numpy(lens).to(dev)
+        for t0 in range(0, w.T, 16384):
+            t1 = min(w.T, t0 + 16384)
+            pos = torch.full((w.B,), t0, dtype=torch.int32, device=dev)
+            cache.append(k[:, :, t0:t1].contiguous(), v[:, :, t0:t1].contiguous(), pos)
+        idx = (lens_t.long() - 1).clamp(min=0)
+        ar = torch.arange(w.B, device=dev)
+        k_new.append(k[ar, :, idx][:, :, None].contiguous())
+        v_new.append(v[ar, :, idx][:, :, None].contiguous())
+        if l == 0 and not args.no_cpu:
+            host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy())
+        del k, v
+        caches.append(cache)
+        qs.append(synth.query(w, l, device=dev))
+        lens_l.append(lens_t)
+        pos_l.append((lens_t - 1).clamp(min=0).to(torch.int32))
+        if l % 10 == 9 or l == L - 1:
+            torch.cuda.synchronize()
+            log(f"bench: built {l + 1}/{L} caches ({time.time() - t_setup:.1f}s)")
+    max_len = int(max(int(x.max()) for x in lens_l))
+    plan = caches[0].plan(w.Hq, max_len, chunk=args.chunk)
+    ws = caches[0].workspace(w.Hq, max_len, plan)
+    outs = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
+    torch.cuda.synchronize()
+    cache_bytes = sum(c.nbytes for c in caches)
+    log(f"bench: setup {time.time() - t_setup:.1f}s, cache {cache_bytes / 2**30:.2f} GiB, "
+        f"plan chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
+
+    def append(l):
+        otq.otq_quantize_append(k_new[l], v_new[l], caches[l].desc, pos_l[l])
+
+    def split(l):
+        otq.otq_sdpa_int4_split(qs[l], caches[l].desc, lens_l[l], max_len, w.scale, ws, plan)
+
+    def combine(l):
+        otq.otq_sdpa_lse_combine(w.Hq, caches[l].desc, lens_l[l], max_len, ws, plan, outs[l])
+
+    def step():
+        for l in range(L):
+            append(l)
+            split(l)
+            combine(l)
+
+    # ---------------------------------------------------------------- timed steps
+    graph = None
+    if not args.no_graph:
+        step()  # warm the launch path once before capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    run = graph.replay if graph is not None else step
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    us_layer_step = ms_per_step * 1000.0 / L
+    log(f"bench: {args.steps} steps, {ms_per_step:.3f} ms/step (events), {wall * 1e3 / args.steps:.3f} "
+        f"ms/step (wall), {us_layer_step:.2f} us/layer-step")
+
+    # ---------------------------------------------------------------- per-kernel durations
+    def kernel_avg_us(fn, passes=3):
+        evs = []
+        for _ in range(passes):
+            for l in range(L):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                fn(l)
+                b.record()
+                evs.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1000.0
+
+    split_us = kernel_avg_us(split)
+    combine_us = kernel_avg_us(combine)
+    append_us = kernel_avg_us(append)
+    torch.cuda.synchronize()
+    sdpa_graph_us = None
+    if graph is not None:
+        g2 = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g2):
+            for l in range(L):
+                split(l)
+                combine(l)
+        for _ in range(2):
+            g2.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g2.replay()
+        b.record()
+        torch.cuda.synchronize()
+        sdpa_graph_us = a.elapsed_time(b) * 1000.0 / (args.steps * L)
+    log(f"bench: split {split_us:.2f} us, combine {combine_us:.2f} us, append {append_us:.2f} us, "
+        f"sdpa (split+combine, graph) {sdpa_graph_us} us per layer")
+
+    # algorithmic bytes: packed codes + fp32 scales of every attended token, q read; out write
+    lens_sum = [int(x.long().sum()) for x in lens_l]
+    unit = w.Hkv * 2 * (w.D // 2 + 4 * (w.D // 32))            # bytes per attended token (K+V)
+    split_bytes = float(np.mean([s * unit for s in lens_sum])) + w.B * w.Hq * w.D * 2
+    layer_bytes = split_bytes + w.B * w.Hq * w.D * 4
+    achieved = split_bytes / (split_us * 1e-6) / 1e9
+    traffic = traffic_from_profile(plan.variant, w.name)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    check = None
+    if host_kv0 is not None:
+        import oracle
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        kb, vb, sg = host_kv0
+        t = time.time()
+        kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads)
+        vc, vs = oracle.quantize(vb, w.dtype, threads=threads)
+        log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
+        lens0 = synth.lens(w, 0)
+        q0 = synth.bits(qs[0])
+        t = time.perf_counter()
+        ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
+                          rot_norm=caches[0].rot_norm, threads=threads)
+        cpu_s = time.perf_counter() - t
+        got = outs[0].cpu().numpy().astype(np.float64)
+        err = got - ref
+        check = {"layer": 0, "rows": int(w.B * w.Hq), "max_abs": float(np.abs(err).max()),
+                 "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref)),
+                 "codes_note": "outputs of the last timed step vs the fp64 oracle"}
+        cpu = {"value": cpu_s * 1e6, "unit": "us/layer-step", "cores": threads, "kind": "oracle",
+               "sample": f"one full layer-step of layer 0 (all {w.B * w.Hq} query rows, "
+                         f"{sum(lens0)} tokens per KV head row set), fp64 attention in plain C"}
+        log(f"bench: oracle layer-step {cpu_s:.2f}s on {threads} threads; GPU vs oracle "
+            f"max_abs={check['max_abs']:.2e} rel_l2={check['rel_l2']:.2e}")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(us_layer_step, 3),
+        "unit": "us/layer-step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32 accumulate, f16 MFMA operands, int4 cache",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+            "head_dim": w.D, "context": w.T, "layers": L, "input_dtype": w.dtype,
+            "cache_gib": round(cache_bytes / 2**30, 3), "chunk": plan.chunk,
+            "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
+            "graph": graph is not None,
+            "step": "per layer: quantize_append(1 token) + split + lse_combine",
+        },
+        "kernels_us": {"split": round(split_us, 3), "combine": round(combine_us, 3),
+                       "append": round(append_us, 3),
+                       "sdpa_per_layer_graph": None if sdpa_graph_us is None else round(sdpa_graph_us, 3)},
+        "sdpa_GBps": round(layer_bytes / ((sdpa_graph_us or (split_us + combine_us)) * 1e-6) / 1e9, 1),
+        "roofline": {"bound": "hbm", "kernel": "split_mfma" if plan.variant == 2 else "split_vec",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "algorithmic_bytes_per_launch": int(split_bytes)},
+        "cpu_baseline": cpu,
+        "check": check,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -201,6 +201,32 @@ int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_hea
                                  void *workspace, size_t workspace_bytes,
                                  const otq_plan *plan, void *stream);
 
+/*
+ * The two phases of otq_sdpa_int4_decode as separate calls, for callers
+ * that time them apart or merge partials computed elsewhere (each split of
+ * the token axis is independent until the combine).
+ *
+ * otq_sdpa_int4_split writes the partials of every non-empty split into the
+ * workspace, laid out as
+ *   part_o  fp32 [B][Hq][num_splits][D]      at byte offset 0
+ *   part_ml fp32 [B][Hq][num_splits][2]      at byte offset
+ *           round_up(B*Hq*num_splits*D*4, 256)
+ * where split s covers tokens [s*chunk, min((s+1)*chunk, lens[b])), m is the
+ * split's max score in log2 units (score * log2(e)), l = sum 2^(S*log2e - m)
+ * and o = sum 2^(S*log2e - m) V^.  Splits with s*chunk >= lens[b] are not
+ * written.  otq_sdpa_lse_combine merges the first ceil(lens[b]/chunk)
+ * partials of each row into out.  Arguments and errors as for
+ * otq_sdpa_int4_decode_planned.
+ */
+int otq_sdpa_int4_split(const void *q, int32_t dtype, int32_t num_q_heads,
+                        const otq_cache *cache, const int32_t *lens, int32_t max_len,
+                        float scale, void *workspace, size_t workspace_bytes,
+                        const otq_plan *plan, void *stream);
+
+int otq_sdpa_lse_combine(int32_t num_q_heads, const otq_cache *cache, const int32_t *lens,
+                         int32_t max_len, const void *workspace, size_t workspace_bytes,
+                         const otq_plan *plan, float *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -28,6 +28,7 @@ EXPORTED = [
     "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
     "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
     "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned",
+    "otq_sdpa_int4_split", "otq_sdpa_lse_combine",
 ]
 
 
@@ -86,6 +87,11 @@ def lib():
     L.otq_sdpa_int4_decode_planned.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, P, S,
                                                ctypes.POINTER(otq_plan), P]
     L.otq_sdpa_int4_decode_planned.restype = ctypes.c_int
+    L.otq_sdpa_int4_split.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, S,
+                                      ctypes.POINTER(otq_plan), P]
+    L.otq_sdpa_int4_split.restype = ctypes.c_int
+    L.otq_sdpa_lse_combine.argtypes = [I, CP, P, I, P, S, ctypes.POINTER(otq_plan), P, P]
+    L.otq_sdpa_lse_combine.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -172,6 +178,32 @@ def otq_sdpa_int4_decode(q, cache_desc, lens, max_len, scale, out, workspace, pl
                                                 _stream(stream))
     if check:
         _check(rc, "otq_sdpa_int4_decode")
+    return rc
+
+
+def otq_sdpa_int4_split(q, cache_desc, lens, max_len, scale, workspace, plan, num_q_heads=None,
+                        dtype=None, workspace_bytes=None, stream=None, check=True):
+    """Split pass only: partials into the workspace (layout in include/otq.h)."""
+    Hq = q.shape[1] if num_q_heads is None else num_q_heads
+    dtype = dtype_code(q.dtype) if dtype is None else dtype
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    rc = lib().otq_sdpa_int4_split(_ptr(q), dtype, Hq, ctypes.byref(cache_desc), _ptr(lens),
+                                   max_len, float(scale), _ptr(workspace), wsb,
+                                   ctypes.byref(plan), _stream(stream))
+    if check:
+        _check(rc, "otq_sdpa_int4_split")
+    return rc
+
+
+def otq_sdpa_lse_combine(num_q_heads, cache_desc, lens, max_len, workspace, plan, out,
+                         workspace_bytes=None, stream=None, check=True):
+    """Combine pass only: merge the partials in the workspace into out."""
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    rc = lib().otq_sdpa_lse_combine(num_q_heads, ctypes.byref(cache_desc), _ptr(lens), max_len,
+                                    _ptr(workspace), wsb, ctypes.byref(plan), _ptr(out),
+                                    _stream(stream))
+    if check:
+        _check(rc, "otq_sdpa_lse_combine")
     return rc
 
 

@@ -151,25 +151,36 @@ size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache* cache, int
     return p.workspace_bytes;
 }
 
-int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_heads,
-                                 const otq_cache* cache, const int32_t* lens, int32_t max_len,
-                                 float scale, float* out, void* workspace, size_t workspace_bytes,
-                                 const otq_plan* plan, void* stream)
+}  // extern "C"
+
+namespace {
+
+int check_workspace(const void* workspace, size_t workspace_bytes, const otq_plan& p)
+{
+    if (!workspace || workspace_bytes < p.workspace_bytes) return OTQ_EWORKSPACE;
+    if (((uintptr_t)workspace & 255) != 0) return OTQ_EWORKSPACE;
+    return OTQ_OK;
+}
+
+size_t ml_offset(const otq_cache* c, int32_t Hq, const otq_plan& p)
+{
+    const size_t rows = (size_t)c->batch * Hq * p.num_splits;
+    return (rows * c->head_dim * sizeof(float) + 255) / 256 * 256;
+}
+
+// Validates a caller plan against the shape; on success *chk is the plan.
+int check_plan(int32_t Hq, const otq_cache* c, int32_t max_len, const otq_plan* plan,
+               otq_plan* chk)
 {
     if (!plan) return OTQ_EINVAL;
-    otq_plan chk;
-    int rc = make_plan(num_q_heads, cache, max_len, plan->chunk, plan->variant, &chk);
-    if (rc != OTQ_OK) return rc;
-    if (!q || !lens || !out) return OTQ_EINVAL;
-    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
-    if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
-        return OTQ_EINVAL;
-    if (!workspace || workspace_bytes < chk.workspace_bytes) return OTQ_EWORKSPACE;
-    if (((uintptr_t)workspace & 255) != 0) return OTQ_EWORKSPACE;
+    return make_plan(Hq, c, max_len, plan->chunk, plan->variant, chk);
+}
 
+int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache* cache,
+              const int32_t* lens, int32_t max_len, float scale, void* workspace,
+              const otq_plan& chk, hipStream_t s)
+{
     const int D = cache->head_dim;
-    const size_t rows = (size_t)cache->batch * num_q_heads * chk.num_splits;
-    const size_t o_aligned = (rows * D * sizeof(float) + 255) / 256 * 256;
     otq::SplitArgs a;
     a.q = q;
     a.dtype = dtype;
@@ -190,15 +201,76 @@ int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_hea
     a.chunk = chk.chunk;
     a.num_splits = chk.num_splits;
     a.part_o = static_cast<float*>(workspace);
-    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) + o_aligned);
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
-                                                   : otq::launch_split_vector(a, s);
-    if (e != hipSuccess) return OTQ_EDEVICE;
-    e = otq::launch_lse_combine(a.part_o, a.part_ml, lens, max_len, chk.chunk, chk.num_splits,
-                                a.B, num_q_heads, D, out, s);
+    a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
+                                          ml_offset(cache, num_q_heads, chk));
+    const hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
+                                                         : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+}
+
+int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens,
+                int32_t max_len, const void* workspace, const otq_plan& chk, float* out,
+                hipStream_t s)
+{
+    const float* part_o = static_cast<const float*>(workspace);
+    const float2* part_ml = reinterpret_cast<const float2*>(
+        static_cast<const char*>(workspace) + ml_offset(cache, num_q_heads, chk));
+    const hipError_t e = otq::launch_lse_combine(part_o, part_ml, lens, max_len, chk.chunk,
+                                                 chk.num_splits, cache->batch, num_q_heads,
+                                                 cache->head_dim, out, s);
+    return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+}
+
+bool finite(float x) { return x == x && x != __builtin_huge_valf() && x != -__builtin_huge_valf(); }
+
+}  // namespace
+
+extern "C" {
+
+int otq_sdpa_int4_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache* cache,
+                        const int32_t* lens, int32_t max_len, float scale, void* workspace,
+                        size_t workspace_bytes, const otq_plan* plan, void* stream)
+{
+    otq_plan chk;
+    int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (!q || !lens) return OTQ_EINVAL;
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (!finite(scale)) return OTQ_EINVAL;
+    if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
+    return run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk,
+                     static_cast<hipStream_t>(stream));
+}
+
+int otq_sdpa_lse_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens,
+                         int32_t max_len, const void* workspace, size_t workspace_bytes,
+                         const otq_plan* plan, float* out, void* stream)
+{
+    otq_plan chk;
+    int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (!lens || !out) return OTQ_EINVAL;
+    if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
+    return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out,
+                       static_cast<hipStream_t>(stream));
+}
+
+int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_heads,
+                                 const otq_cache* cache, const int32_t* lens, int32_t max_len,
+                                 float scale, float* out, void* workspace, size_t workspace_bytes,
+                                 const otq_plan* plan, void* stream)
+{
+    otq_plan chk;
+    int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (!q || !lens || !out) return OTQ_EINVAL;
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (!finite(scale)) return OTQ_EINVAL;
+    if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s);
+    if (rc != OTQ_OK) return rc;
+    return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s);
 }
 
 int otq_sdpa_int4_decode(const void* q, int32_t dtype, int32_t num_q_heads,

@@ -82,11 +82,15 @@ def test_quantize_append_host_errors():
 
 def test_plan_defaults_and_errors():
     d = _desc(B=1, H=8, D=128, cap=131072)
-    p = otq.otq_sdpa_plan(16, d, 131072)
+    p = otq.otq_sdpa_plan(64, d, 131072)
+    assert p.variant == otq.OTQ_VARIANT_MFMA
+    assert otq.otq_sdpa_plan(16, d, 131072).variant == otq.OTQ_VARIANT_VECTOR
     assert p.chunk % 128 == 0 and p.num_splits == -(-131072 // p.chunk)
-    rows = 16 * p.num_splits
+    rows = 64 * p.num_splits
     assert p.workspace_bytes == -(-rows * 128 * 4 // 256) * 256 + rows * 8
-    assert otq.otq_sdpa_workspace_bytes(16, d, 131072) == p.workspace_bytes
+    assert otq.otq_sdpa_workspace_bytes(64, d, 131072) == p.workspace_bytes
+    assert otq.otq_sdpa_plan(64, d, 100, variant=otq.OTQ_VARIANT_VECTOR, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    assert otq.otq_sdpa_plan(8, d, 100, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
     p = otq.otq_sdpa_plan(8, d, 1000, chunk=256, variant=otq.OTQ_VARIANT_VECTOR, check=False)[1]
     assert (p.chunk, p.num_splits, p.variant) == (256, 4, otq.OTQ_VARIANT_VECTOR)
     rc = lambda *a, **k: otq.otq_sdpa_plan(*a, check=False, **k)[0]
@@ -122,6 +126,17 @@ def test_decode_host_errors():
     assert call(ws=4096 + 4) == otq.OTQ_EWORKSPACE       # workspace must be 256-byte aligned
     assert lib.otq_sdpa_int4_decode_planned(P(FAKE), 1, 4, ctypes.byref(d), P(FAKE), 256, 0.1,
                                             P(FAKE), P(4096), p.workspace_bytes, None, None) == otq.OTQ_EINVAL
+    sp = lambda q=FAKE, lens=FAKE, ws=4096, wsb=p.workspace_bytes, plan=p, scale=0.1: lib.otq_sdpa_int4_split(
+        P(q), 1, 4, ctypes.byref(d), P(lens), 256, scale, P(ws), wsb,
+        None if plan is None else ctypes.byref(plan), None)
+    assert sp(q=0) == otq.OTQ_EINVAL and sp(lens=0) == otq.OTQ_EINVAL and sp(plan=None) == otq.OTQ_EINVAL
+    assert sp(wsb=16) == otq.OTQ_EWORKSPACE and sp(scale=float("inf")) == otq.OTQ_EINVAL
+    cb = lambda out=FAKE, lens=FAKE, ws=4096, wsb=p.workspace_bytes: lib.otq_sdpa_lse_combine(
+        4, ctypes.byref(d), P(lens), 256, P(ws), wsb, ctypes.byref(p), P(out), None)
+    assert cb(out=0) == otq.OTQ_EINVAL and cb(lens=0) == otq.OTQ_EINVAL and cb(ws=0) == otq.OTQ_EWORKSPACE
+    bad = otq.otq_plan(100, 3, 1, 0, 0)            # chunk not a multiple of 128
+    assert lib.otq_sdpa_lse_combine(4, ctypes.byref(d), P(FAKE), 256, P(4096), 1 << 20,
+                                    ctypes.byref(bad), P(FAKE), None) == otq.OTQ_EINVAL
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])

@@ -62,23 +62,37 @@ def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sig
     return got, ref, plan
 
 
+VEC, MF = otq.OTQ_VARIANT_VECTOR, otq.OTQ_VARIANT_MFMA
+
+
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G", [1, 2, 4])
-def test_sdpa_small_parity(D, G):
+def test_sdpa_small_parity_vector(D, G):
     if D == 256 and G == 4:
-        pytest.skip("vector variant does not build G=4 at D=256")
+        pytest.skip("vector variant does not build G=4 at D=256 (register file)")
     Hkv = 2
-    got, ref, _ = _run(2, G * Hkv, Hkv, D, 320, [300, 77], seed=D + G,
-                       variant=otq.OTQ_VARIANT_VECTOR, chunk=128)
+    got, ref, _ = _run(2, G * Hkv, Hkv, D, 320, [300, 77], seed=D + G, variant=VEC, chunk=128)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [4, 8, 16])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_sdpa_small_parity_mfma(D, G, rotate):
+    Hkv = 2
+    got, ref, _ = _run(2, G * Hkv, Hkv, D, 352, [350, 45], seed=3 * D + G + rotate, variant=MF,
+                       chunk=128, rotate=rotate)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("variant,Hq", [(VEC, 4), (MF, 16)])
 @pytest.mark.parametrize("lens", [[0, 5], [1, 1], [31, 32], [33, 160], [160, 0]])
-def test_sdpa_edge_lengths(lens):
-    got, ref, _ = _run(2, 4, 2, 128, 160, lens, seed=sum(lens), variant=otq.OTQ_VARIANT_VECTOR,
-                       chunk=128)
+def test_sdpa_edge_lengths(lens, variant, Hq):
+    got, ref, _ = _run(2, Hq, 2, 128, 160, lens, seed=sum(lens), variant=variant, chunk=128)
     ma, rel = errors(got, ref)
     assert ma <= MAX_ABS and rel <= REL_L2
     for b, n in enumerate(lens):
@@ -86,10 +100,10 @@ def test_sdpa_edge_lengths(lens):
             assert np.all(got[b] == 0.0)
 
 
+@pytest.mark.parametrize("variant,Hq", [(VEC, 2), (MF, 8)])
 @pytest.mark.parametrize("chunk", [128, 256, 384, 1024])
-def test_sdpa_split_invariance(chunk):
-    got, ref, plan = _run(1, 2, 1, 128, 1024, [1000], seed=11, chunk=chunk,
-                          variant=otq.OTQ_VARIANT_VECTOR)
+def test_sdpa_split_invariance(chunk, variant, Hq):
+    got, ref, plan = _run(1, Hq, 1, 128, 1024, [1000], seed=11, chunk=chunk, variant=variant)
     ma, rel = errors(got, ref)
     assert plan.num_splits == -(-1000 // chunk)
     assert ma <= MAX_ABS and rel <= REL_L2
@@ -111,6 +125,11 @@ def test_sdpa_deterministic():
     lens = torch.tensor([512], dtype=torch.int32, device=DEV)
     a = cache.decode(q.to(DEV), lens, 512, 0.1)
     b = cache.decode(q.to(DEV), lens, 512, 0.1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    q8 = torch.randn((1, 8, 128), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16).to(DEV)
+    a = cache.decode(q8, lens, 512, 0.1)
+    b = cache.decode(q8, lens, 512, 0.1)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 
@@ -157,6 +176,14 @@ def _full(cfg, rows_per_seq=None, layer=0):
     ma, rel = errors(got, ref)
     say(f"  rows={len(rows)} max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_full_workload_2_llama70b_32k():
+    _full(2, rows_per_seq=16)
+
+
+def test_full_workload_3_llama70b_128k():
+    _full(3, rows_per_seq=8)
 
 
 def test_full_workload_1_tiny():

@@ -20,8 +20,10 @@
 //  * the per-token, per-group K scale is applied in fp32 after the MFMA,
 //    since one MFMA of K = 32 covers exactly one scale group;
 //  * for P.V the V scale depends on the contracted token, so it is folded
-//    into the probability operand: A = fp16(p * s_v).  That rounding
-//    (relative 2^-11 per term) is the one approximation on this path.
+//    into the probability operand, x = p * s_v in fp32, and x enters as two
+//    fp16 MFMA operands hi = fp16(x), lo = fp16(x - hi) (~22 significant
+//    bits); fp16(x) alone (2^-11 relative) is too coarse when a handful of
+//    tokens carry the softmax and a channel is an outlier.
 //
 // Wave layout per 32-token tile (sub-tiles s = 0, 1 of 16 tokens), lane
 // l = 16 r + n:
@@ -214,8 +216,11 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
         mt = fmaxf(mt, shfl_xor(mt, 16));
         mt = fmaxf(mt, shfl_xor(mt, 32));
         const float m_new = fmaxf(m_run, mt);  // finite: the tile has a valid token
-        if (m_new != m_run) {                  // rescale rows of O whose head's max moved
-            const float alpha = exp2_approx(m_run - m_new);  // 0 on the first tile
+        // alpha is computed by every lane (1 where the max did not move, 0 on
+        // the first tile); the rescale runs only when some head's max moved,
+        // decided for the whole wave so that the shuffles see every lane.
+        const float alpha = exp2_approx(m_run - m_new);
+        if (__any(m_new != m_run)) {
             l_lane *= alpha;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -223,8 +228,8 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 #pragma unroll
                 for (int cb = 0; cb < NCB; ++cb) acc[cb][i] *= ai;
             }
-            m_run = m_new;
         }
+        m_run = m_new;
         float p[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -234,15 +239,18 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
                 l_lane += p[s][i];
             }
 
-        // ---- values: A_g = fp16(p * s_v[token][g]) per group, B = V codes
-        half8_t pa[NG];
+        // ---- values: A_g = p * s_v[token][g] as fp16 hi + lo, B = V codes
+        half8_t pa[NG], pl[NG];
         static_for<NG>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
             static_for<8>([&](auto eI) {
                 constexpr int e = decltype(eI)::value;
                 constexpr int j = kSlot[e], s = j / 4, i = j % 4;
                 const float scl = row_bcast<Geo::src_lane(i, g)>(sv[s][Geo::src_reg(i, g)]);
-                pa[g][e] = (_Float16)(p[s][i] * scl);
+                const float x = p[s][i] * scl;
+                const _Float16 hi = (_Float16)x;
+                pa[g][e] = hi;
+                pl[g][e] = (_Float16)(x - (float)hi);
             });
         });
         static_for<NCB>([&](auto cI) {
@@ -251,6 +259,7 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             const uint32_t word = bv == 0 ? vw[av].x : bv == 1 ? vw[av].y : bv == 2 ? vw[av].z : vw[av].w;
             const half8_t B = unpack_codes(word);
             acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[cb / 2], B, acc[cb], 0, 0, 0);
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[cb / 2], B, acc[cb], 0, 0, 0);
         });
     }
 

@@ -72,6 +72,9 @@ def main():
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-threads", type=int, default=None)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (5 times), "
+                         "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -97,6 +100,16 @@ def main():
     L = w.layers if args.layers is None else args.layers
     log(f"bench: workload {args.workload} {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
         f"T={w.T} layers={L}")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib * 2**20 // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration {args.copy_calibration_mib} MiB x 5 done")
+        del src, dst
 
     # ---------------------------------------------------------------- setup
     t_setup = time.time()

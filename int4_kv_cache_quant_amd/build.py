@@ -8,6 +8,9 @@ Flags:
                                   IEEE fp32 division and denormals, which the
                                   bit-exact quantiser relies on.
   -ffp-contract=off (quantiser)   one rounding per fp32 operation.
+  -mllvm -amdgpu-mfma-vgpr-form (MFMA split kernel)
+                                  accumulators stay in VGPRs instead of being
+                                  copied to and from AGPRs around every rescale.
 """
 import os
 import shutil
@@ -25,7 +28,9 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
-PER_FILE = {"quantize.hip": ["-ffp-contract=off"]}
+PER_FILE = {"quantize.hip": ["-ffp-contract=off"],
+            # keep MFMA accumulators in VGPRs: they are rescaled by VALU ops
+            "sdpa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():

@@ -16,6 +16,7 @@ namespace {
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
 constexpr int kMaxChunk = 2048;
 constexpr int kTargetGroups = 512;  // split workgroups aimed for (2 per CU)
+constexpr int kMaxSplits = 16384;
 
 bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
 
@@ -73,6 +74,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         return OTQ_EINVAL;
     }
     const long long S = ((long long)max_len + chunk - 1) / chunk;
+    if (S > kMaxSplits) return OTQ_EINVAL;  // the combine keeps one weight per split in LDS
     const unsigned __int128 rows = (unsigned __int128)c->batch * Hq * S;
     const unsigned __int128 o_bytes = rows * D * sizeof(float);
     const unsigned __int128 o_aligned = (o_bytes + 255) / 256 * 256;

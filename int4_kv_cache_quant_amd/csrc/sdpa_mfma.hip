@@ -12,8 +12,12 @@
 // page, section on numerical stability).
 //
 // Exactness of the products:
-//  * codes are integers in [-8, 7], exact in fp16 (built with the 1024 + n
-//    magic constant and one packed fp16 subtraction);
+//  * V codes are integers in [-8, 7], exact in fp16 (built with the 1024 + n
+//    magic constant and one packed fp16 subtraction); K codes enter as the
+//    fp16 subnormals n * 2^-24 of their offset-binary value n = c + 8 (one
+//    byte permute per pair, no arithmetic), the MFMA accumulator starts at
+//    -8 * 2^-24 * sum(q) so that it ends at 2^-24 * q.c, and 2^24 is folded
+//    into the softmax scale (the matrix cores keep fp16 subnormals);
 //  * q is converted to fp16 (bf16 values convert exactly in fp16's normal
 //    range); a rotated q is split into fp16 hi + lo parts and both are
 //    multiplied, so the score keeps ~22 bits of q;
@@ -78,6 +82,36 @@ __device__ __forceinline__ half8_t unpack_codes(uint32_t w)
     return out;
 }
 
+// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^-24, same operand order.
+__device__ __forceinline__ half8_t unpack_codes_offset(uint32_t w)
+{
+    const uint32_t x = w ^ 0x88888888u;
+    const uint32_t lo = x & 0x0F0F0F0Fu;
+    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
+    uint32_t r[4];
+    r[0] = __builtin_amdgcn_perm(0u, lo, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(0u, lo, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(0u, hi, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(0u, hi, 0x04030402u);
+    half8_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const half2_t p = __builtin_bit_cast(half2_t, r[m]);
+        out[2 * m] = p[0];
+        out[2 * m + 1] = p[1];
+    }
+    return out;
+}
+
+template <int D>
+struct TileLoads {
+    static constexpr int NG = D / kGroup;
+    static constexpr int SPL = NG >= 4 ? NG / 4 : 1;
+    uint32_t kw[2][NG];
+    float sk[2][SPL], sv[2][SPL];
+    uint4 vw[D / 64];
+};
+
 template <int D>
 struct MfmaGeom {
     static constexpr int NG = D / kGroup;           // scale groups per vector
@@ -89,8 +123,14 @@ struct MfmaGeom {
     static constexpr int src_reg(int i, int g) { return (NG * i + g) % SPL; }
 };
 
+// Waves per SIMD the register allocation must allow (occupancy floor).
+#ifndef OTQ_MFMA_WAVES_PER_EU
+#define OTQ_MFMA_WAVES_PER_EU 2
+#endif
+
 template <int D, bool ROT>
-__global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OTQ_MFMA_WAVES_PER_EU)))
+void split_mfma_kernel(SplitArgs a)
 {
     using Geo = MfmaGeom<D>;
     constexpr int NG = Geo::NG, NA = Geo::NA, NCB = Geo::NCB, SPL = Geo::SPL;
@@ -144,7 +184,23 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             if (ROT) qb_lo[g][e] = (_Float16)(x - (float)h16);
         }
     }
-    const float qmul = ROT ? a.qscale * a.rot_norm : a.qscale;
+    // accumulator start of the score MFMAs: -8 * 2^-24 * sum of the fp16 q
+    // values of head n16 in group g (summed over the whole group by lanes
+    // of the four quarters)
+    float qinit[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float t = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            t += (float)qb[g][e];
+            if (ROT) t += (float)qb_lo[g][e];
+        }
+        t += shfl_xor(t, 16);
+        t += shfl_xor(t, 32);
+        qinit[g] = -8.0f * 0x1p-24f * t;
+    }
+    const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
     __syncthreads();  // q_lds is reused for the final merge
 
     const size_t head = (size_t)b * a.H + hk;
@@ -159,30 +215,29 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    for (int it = wave; it < ntiles; it += kWaves) {
+    auto load_tile = [&](TileLoads<D>& t, int it) {
         const int tok0 = start + it * kTile;
-        // ---- loads: K words, K/V scales, V words
-        uint32_t kw[2][NG];
-        float sk[2][SPL], sv[2][SPL];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const uint8_t* krow = kbase + (size_t)(tok0 + 16 * s + n16) * (D / 2) + 4 * r;
 #pragma unroll
-            for (int g = 0; g < NG; ++g) kw[s][g] = *reinterpret_cast<const uint32_t*>(krow + 16 * g);
+            for (int g = 0; g < NG; ++g) t.kw[s][g] = *reinterpret_cast<const uint32_t*>(krow + 16 * g);
             const size_t sbase = (size_t)(tok0 + 16 * s) * NG + 4 * r * NG;
 #pragma unroll
             for (int e = 0; e < SPL; ++e) {
                 const int off = (n16 * SPL + e) % (4 * NG);
-                sk[s][e] = ksb[sbase + off];
-                sv[s][e] = vsb[sbase + off];
+                t.sk[s][e] = ksb[sbase + off];
+                t.sv[s][e] = vsb[sbase + off];
             }
         }
         const uint8_t* vt = vbase + (size_t)(tok0 / kTile) * (16 * D);
-        uint4 vw[NA];
 #pragma unroll
         for (int av = 0; av < NA; ++av)
-            vw[av] = *reinterpret_cast<const uint4*>(vt + ((av * 4 + r) * 16 + n16) * 16);
+            t.vw[av] = *reinterpret_cast<const uint4*>(vt + ((av * 4 + r) * 16 + n16) * 16);
+    };
 
+    auto compute_tile = [&](const TileLoads<D>& t, int it) {
+        const int tok0 = start + it * kTile;
         // ---- scores
         float S[2][4];
 #pragma unroll
@@ -190,20 +245,20 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
             static_for<NG>([&](auto gI) {
                 constexpr int g = decltype(gI)::value;
-                const half8_t A = unpack_codes(kw[s][g]);
-                floatx4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+                const half8_t A = unpack_codes_offset(t.kw[s][g]);
+                floatx4_t d = {qinit[g], qinit[g], qinit[g], qinit[g]};
                 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[g], d, 0, 0, 0);
                 if constexpr (ROT) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[g], d, 0, 0, 0);
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
-                    const float scl = row_bcast<Geo::src_lane(i, g)>(sk[s][Geo::src_reg(i, g)]);
+                    const float scl = row_bcast<Geo::src_lane(i, g)>(t.sk[s][Geo::src_reg(i, g)]);
                     tot[i] += scl * d[i];
                 });
             });
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int t = tok0 + 16 * s + 4 * r + i;
-                S[s][i] = (t < end) ? tot[i] * qmul : kNegInf;
+                const int tk = tok0 + 16 * s + 4 * r + i;
+                S[s][i] = (tk < end) ? tot[i] * qmul : kNegInf;
             }
         }
 
@@ -239,28 +294,45 @@ __global__ __launch_bounds__(256) void split_mfma_kernel(SplitArgs a)
                 l_lane += p[s][i];
             }
 
-        // ---- values: A_g = p * s_v[token][g] as fp16 hi + lo, B = V codes
-        half8_t pa[NG], pl[NG];
+        // ---- values, one scale group (two 16-channel blocks) at a time:
+        //      A_g = p * s_v[token][g] as fp16 hi + lo, B = V codes
         static_for<NG>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
+            half8_t pa, pl;
             static_for<8>([&](auto eI) {
                 constexpr int e = decltype(eI)::value;
                 constexpr int j = kSlot[e], s = j / 4, i = j % 4;
-                const float scl = row_bcast<Geo::src_lane(i, g)>(sv[s][Geo::src_reg(i, g)]);
+                const float scl = row_bcast<Geo::src_lane(i, g)>(t.sv[s][Geo::src_reg(i, g)]);
                 const float x = p[s][i] * scl;
                 const _Float16 hi = (_Float16)x;
-                pa[g][e] = hi;
-                pl[g][e] = (_Float16)(x - (float)hi);
+                pa[e] = hi;
+                pl[e] = (_Float16)(x - (float)hi);
+            });
+            static_for<2>([&](auto hI) {
+                constexpr int cb = 2 * g + decltype(hI)::value;
+                constexpr int av = cb / 4, bv = cb % 4;
+                const uint32_t word = bv == 0 ? t.vw[av].x : bv == 1 ? t.vw[av].y
+                                    : bv == 2 ? t.vw[av].z : t.vw[av].w;
+                const half8_t B = unpack_codes(word);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
             });
         });
-        static_for<NCB>([&](auto cI) {
-            constexpr int cb = decltype(cI)::value;
-            constexpr int av = cb / 4, bv = cb % 4;
-            const uint32_t word = bv == 0 ? vw[av].x : bv == 1 ? vw[av].y : bv == 2 ? vw[av].z : vw[av].w;
-            const half8_t B = unpack_codes(word);
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[cb / 2], B, acc[cb], 0, 0, 0);
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[cb / 2], B, acc[cb], 0, 0, 0);
-        });
+    };
+
+    // two register sets: the next tile's loads are in flight while the
+    // current one is computed
+    TileLoads<D> bufA, bufB;
+    int it = wave;
+    if (it < ntiles) load_tile(bufA, it);
+    while (it < ntiles) {
+        if (it + kWaves < ntiles) load_tile(bufB, it + kWaves);
+        compute_tile(bufA, it);
+        it += kWaves;
+        if (it >= ntiles) break;
+        if (it + kWaves < ntiles) load_tile(bufA, it + kWaves);
+        compute_tile(bufB, it);
+        it += kWaves;
     }
 
     // ---- merge the 4 rows (l only: m and O are already wave-wide), then waves

@@ -70,13 +70,16 @@ typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
  * inside otq_sdpa_int4_decode, so scores are unchanged by the rotation.
  *
  * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
- *  k_codes  uint8 [B][H][C][D/2]: byte j of a token's row holds element 2j in
- *           its low nibble and element 2j+1 in its high nibble; nibbles are
- *           two's-complement int4.
+ *  Codes are two's-complement int4 nibbles; a byte holds an even channel in
+ *  its low nibble and the next channel in its high nibble.
+ *  k_codes  uint8 [B][H][C][D/2]: a token's row is D/8 32-bit words; with
+ *           NG = D/32 groups, word (r*NG + g), r = 0..3, holds channels
+ *           32g + 8r .. 32g + 8r + 7, channel 32g + 8r + k in nibble k
+ *           (byte k/2, low nibble for even k).  So row quarter r (bytes
+ *           [r*D/8, (r+1)*D/8)) carries 8 channels of every group.
  *  k_scales float [B][H][C][D/32], v_scales likewise: s_g per token, group.
- *  v_codes  uint8 [B][H][C/32][16*D]: the same nibbles as K's layout would
- *           hold, regrouped per tile of 32 tokens so that each 32-bit word
- *           holds 8 tokens of one channel.  For tile-relative token u
+ *  v_codes  uint8 [B][H][C/32][16*D]: regrouped per tile of 32 tokens so
+ *           that each 32-bit word holds 8 tokens of one channel.  For tile-relative token u
  *           (0..31) let quarter r = (u % 16) / 4 and slot j = 4*(u / 16) +
  *           (u % 4).  Channel c with cb = c / 16, n = c % 16, a = cb / 4,
  *           b = cb % 4 owns word ((a*4 + r)*16 + n)*4 + b of the tile, and

@@ -64,7 +64,8 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
 
     int chunk = chunk_ov;
     if (chunk == 0) {
-        const long long units = (long long)c->batch * c->num_kv_heads;
+        long long units = (long long)c->batch * c->num_kv_heads;
+        if (variant == OTQ_VARIANT_MFMA) units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
         long long want = ((long long)max_len * units + kTargetGroups - 1) / kTargetGroups;
         want = (want + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
         if (want < kChunkAlign) want = kChunkAlign;

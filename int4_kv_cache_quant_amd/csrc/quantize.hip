@@ -78,6 +78,16 @@ __device__ __forceinline__ void rotate_lane(float (&y)[D / 64], const float* __r
     for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
 }
 
+// Byte offset, inside one K row, of the byte holding even channel c and
+// channel c + 1: word (r * NG + g) holds channels 32 g + 8 r + 0..7.
+template <int D>
+__device__ __forceinline__ int k_row_byte(int c)
+{
+    constexpr int NG = D / kGroup;
+    const int g = c >> 5, r = (c >> 3) & 3, k = c & 7;
+    return (r * NG + g) * 4 + (k >> 1);
+}
+
 // Byte offset, inside one V tile, of the byte holding (channel c, token pair
 // starting at even tile-relative token u).
 template <int D>
@@ -129,11 +139,12 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
         uint8_t* krow = kc + row * (D / 2);
         if constexpr (E == 1) {
             const int other = __shfl_xor(c[0], 1, 64);
-            if ((lane & 1) == 0) krow[lane >> 1] = (uint8_t)((c[0] & 0xF) | ((other & 0xF) << 4));
+            if ((lane & 1) == 0)
+                krow[k_row_byte<D>(lane)] = (uint8_t)((c[0] & 0xF) | ((other & 0xF) << 4));
         } else {
 #pragma unroll
             for (int e = 0; e < E; e += 2)
-                krow[(lane * E + e) >> 1] = (uint8_t)((c[e] & 0xF) | ((c[e + 1] & 0xF) << 4));
+                krow[k_row_byte<D>(lane * E + e)] = (uint8_t)((c[e] & 0xF) | ((c[e + 1] & 0xF) << 4));
         }
         if (lane % (kGroup / E) == 0) ks[row * NG + (lane * E) / kGroup] = sk;
 

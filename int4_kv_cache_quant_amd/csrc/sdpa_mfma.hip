@@ -29,16 +29,24 @@
 //    bits); fp16(x) alone (2^-11 relative) is too coarse when a handful of
 //    tokens carry the softmax and a channel is an outlier.
 //
-// Wave layout per 32-token tile (sub-tiles s = 0, 1 of 16 tokens), lane
-// l = 16 r + n:
-//  scores  A = K codes (row = token 16 s + n, k = 8 channels of quarter r of
-//          the group), B = q (column = head n), C = S[token 16 s + 4 r + i][head n]
-//  values  A = p * s_v (row = head n, k = the 8 tokens 4 r + i of both
+// One wave serves P = 16 / G KV heads at once (P = 2 for G = 8): MFMA column
+// n is query head n of the block, which belongs to KV head n / G, so no
+// column of the 16-wide products is padding.  Per 32-token tile (sub-tiles
+// s = 0, 1 of 16 tokens), lane l = 16 r + n:
+//  scores  for each KV head j: A = K_j codes (row = token 16 s + n, k = 8
+//          channels of quarter r of the group, all groups in one 16-byte load
+//          thanks to the quarter-interleaved K row), B = q masked to the columns
+//          of head j; all P products accumulate into one C = S[token
+//          16 s + 4 r + i][column n] since the other heads' B columns are 0
+//  values  A = p * s_v (row = column n, k = the 8 tokens 4 r + i of both
 //          sub-tiles, exactly the tokens whose scores this lane holds),
-//          B = V codes (column = channel, k = the same 8 tokens, one 32-bit
-//          word of the V tile layout), C = O[head 4 r + i][channel]
-//  scales  each lane loads one (or two) of the sub-tile's fp32 scales and
-//          the row of 16 lanes shares them by DPP row broadcast.
+//          B = V_j codes (column = channel, k = the same 8 tokens, one 32-bit
+//          word of the V tile layout), C_j = O[column 4 r + i][channel]; one
+//          accumulator set per KV head, of which only the rows of head j
+//          are kept
+//  scales  lane k of each quad loads the fp32 scales of token 4 r + k of its
+//          head and DPP quad broadcasts hand them to the quad (every quad
+//          lies inside one head, as G >= 4).
 #include <math.h>
 
 #include "common.hpp"
@@ -103,56 +111,73 @@ __device__ __forceinline__ half8_t unpack_codes_offset(uint32_t w)
     return out;
 }
 
-template <int D>
+// Lane K (0..3) of each quad of lanes, broadcast to the quad (DPP quad_perm).
+template <int K>
+__device__ __forceinline__ float quad_bcast(float v)
+{
+    static_assert(K >= 0 && K < 4, "quad lane");
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, false));
+}
+
+template <int NG>
+__device__ __forceinline__ void load_scales(float (&dst)[NG], const float* __restrict__ src)
+{
+    if constexpr (NG == 2) {
+        const float2 v = *reinterpret_cast<const float2*>(src);
+        dst[0] = v.x; dst[1] = v.y;
+    } else {
+#pragma unroll
+        for (int q = 0; q < NG / 4; ++q) {
+            const float4 v = reinterpret_cast<const float4*>(src)[q];
+            dst[4 * q + 0] = v.x; dst[4 * q + 1] = v.y;
+            dst[4 * q + 2] = v.z; dst[4 * q + 3] = v.w;
+        }
+    }
+}
+
+// One tile's loads for the P KV heads of the block.
+template <int D, int P>
 struct TileLoads {
     static constexpr int NG = D / kGroup;
-    static constexpr int SPL = NG >= 4 ? NG / 4 : 1;
-    uint32_t kw[2][NG];
-    float sk[2][SPL], sv[2][SPL];
-    uint4 vw[D / 64];
+    uint32_t kw[P][2][NG];   // K code words: head, sub-tile, group
+    uint4 vw[P][D / 64];     // V tile words: head, 128-bit load
+    float sk[2][NG];         // K scales of token 4 r + (lane % 4) of the lane's head
+    float sv[2][NG];         // V scales, same token
 };
 
+// Waves per SIMD the register allocation must allow: 2 (up to 256 VGPRs)
+// except at head_dim 256, whose accumulators alone take 64 VGPRs per head.
 template <int D>
-struct MfmaGeom {
-    static constexpr int NG = D / kGroup;           // scale groups per vector
-    static constexpr int NA = D / 64;               // 128-bit V loads per lane per tile
-    static constexpr int NCB = D / 16;              // 16-channel output blocks
-    static constexpr int SPL = NG >= 4 ? NG / 4 : 1;  // scale floats per lane per sub-tile
-    // lane (within the row) and register holding scale (token i of the row, group g)
-    static constexpr int src_lane(int i, int g) { return (NG * i + g) / SPL; }
-    static constexpr int src_reg(int i, int g) { return (NG * i + g) % SPL; }
-};
+constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 
-// Waves per SIMD the register allocation must allow (occupancy floor).
-#ifndef OTQ_MFMA_WAVES_PER_EU
-#define OTQ_MFMA_WAVES_PER_EU 2
-#endif
-
-template <int D, bool ROT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(OTQ_MFMA_WAVES_PER_EU)))
+template <int D, int P, bool ROT, bool PF>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
 void split_mfma_kernel(SplitArgs a)
 {
-    using Geo = MfmaGeom<D>;
-    constexpr int NG = Geo::NG, NA = Geo::NA, NCB = Geo::NCB, SPL = Geo::SPL;
-    extern __shared__ float lds[];  // q: [16][D]; later merge: [4][G][D] + ml [4][G]
+    constexpr int NG = D / kGroup, NA = D / 64, NCB = D / 16;
+    extern __shared__ float lds[];  // q: [16][D]; later merge: [4][P*G][D] + ml [4][P*G]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    const int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
     const int G = a.Hq / a.H;
+    const int PG = P * G;  // query heads served by the block (<= 16)
     const int len = min(max(a.lens[b], 0), a.max_len);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform
     const int end = min(start + a.chunk, len);
     const int ntiles = (end - start + kTile - 1) / kTile;
-    const int n16 = lane & 15, r = lane >> 4;
+    const int n16 = lane & 15, r = lane >> 4, slot = lane & 3;
+    const bool col_valid = n16 < PG;
+    const int jl = col_valid ? n16 / G : P - 1;  // KV head of this lane's column
 
     // ---- query prologue: fp32 in LDS, rotated like K when the cache is
     float* q_lds = lds;
-    const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
+    const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G) * D;
     for (int i = tid; i < 16 * D; i += 256) {
         const int h = i / D, c = i % D;
         float x = 0.0f;
-        if (h < G) {
+        if (h < PG) {
             x = widen(qsrc[h * D + c], a.dtype);
             if (ROT) x *= a.signs[c];
         }
@@ -171,31 +196,36 @@ void split_mfma_kernel(SplitArgs a)
             __syncthreads();
         }
     }
-    // B operands of the score MFMAs: column = head n16, k slot e = channel
-    // 32 g + 8 r + kSlot[e]
-    half8_t qb[NG], qb_lo[ROT ? NG : 1];
+    // B operands of the score MFMAs, one per KV head: column n16 holds q of
+    // query head n16 in the set of head jl and zeros in the others; k slot e
+    // = channel 32 g + 8 r + kSlot[e].
+    half8_t qb[P][NG], qb_lo[ROT ? P : 1][ROT ? NG : 1];
+    float qinit[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
+        half8_t hv, lv;
+        float t = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = q_lds[n16 * D + 32 * g + 8 * r + kSlot[e]];
             const _Float16 h16 = (_Float16)x;
-            qb[g][e] = h16;
-            if (ROT) qb_lo[g][e] = (_Float16)(x - (float)h16);
+            hv[e] = h16;
+            t += (float)h16;
+            if (ROT) {
+                lv[e] = (_Float16)(x - (float)h16);
+                t += (float)lv[e];
+            }
         }
-    }
-    // accumulator start of the score MFMAs: -8 * 2^-24 * sum of the fp16 q
-    // values of head n16 in group g (summed over the whole group by lanes
-    // of the four quarters)
-    float qinit[NG];
 #pragma unroll
-    for (int g = 0; g < NG; ++g) {
-        float t = 0.0f;
+        for (int j = 0; j < P; ++j) {
+            const bool mine = col_valid && j == jl;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            t += (float)qb[g][e];
-            if (ROT) t += (float)qb_lo[g][e];
+            for (int e = 0; e < 8; ++e) {
+                qb[j][g][e] = mine ? hv[e] : (_Float16)0.0f;
+                if (ROT) qb_lo[j][g][e] = mine ? lv[e] : (_Float16)0.0f;
+            }
         }
+        // the score accumulator starts at -8 * 2^-24 * sum(q over the group)
         t += shfl_xor(t, 16);
         t += shfl_xor(t, 32);
         qinit[g] = -8.0f * 0x1p-24f * t;
@@ -203,40 +233,59 @@ void split_mfma_kernel(SplitArgs a)
     const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
     __syncthreads();  // q_lds is reused for the final merge
 
-    const size_t head = (size_t)b * a.H + hk;
-    const uint8_t* kbase = a.kc + head * a.cap * (D / 2);
-    const float* ksb = a.ks + head * a.cap * NG;
-    const uint8_t* vbase = a.vc + head * (a.cap / kTile) * (16 * D);
-    const float* vsb = a.vs + head * a.cap * NG;
-
-    float m_run = kNegInf;  // running max of head n16 (log2 domain), same in all rows
-    float l_lane = 0.0f;    // sum of this lane's probabilities (head n16)
-    floatx4_t acc[NCB];
+    const uint8_t* kbase[P];
+    const uint8_t* vbase[P];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < P; ++j) {
+        const size_t head = (size_t)b * a.H + hk0 + j;
+        kbase[j] = a.kc + head * a.cap * (D / 2) + r * (D / 8);  // row quarter r
+        vbase[j] = a.vc + head * (a.cap / kTile) * (16 * D) + ((size_t)r * 16 + n16) * 16;
+    }
+    const size_t head_l = (size_t)b * a.H + hk0 + jl;
+    const float* ks_l = a.ks + head_l * a.cap * NG;
+    const float* vs_l = a.vs + head_l * a.cap * NG;
 
-    auto load_tile = [&](TileLoads<D>& t, int it) {
+    float m_run = kNegInf;  // running max of column n16 (log2 domain)
+    float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
+    floatx4_t acc[P][NCB];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    auto load_tile = [&](TileLoads<D, P>& t, int it) {
         const int tok0 = start + it * kTile;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint8_t* krow = kbase + (size_t)(tok0 + 16 * s + n16) * (D / 2) + 4 * r;
+        for (int j = 0; j < P; ++j) {
 #pragma unroll
-            for (int g = 0; g < NG; ++g) t.kw[s][g] = *reinterpret_cast<const uint32_t*>(krow + 16 * g);
-            const size_t sbase = (size_t)(tok0 + 16 * s) * NG + 4 * r * NG;
+            for (int s = 0; s < 2; ++s) {
+                // quarter r of the row: word g = channels 32 g + 8 r + 0..7
+                const uint8_t* krow = kbase[j] + (size_t)(tok0 + 16 * s + n16) * (D / 2);
+                if constexpr (NG == 2) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(krow);
+                    t.kw[j][s][0] = w.x; t.kw[j][s][1] = w.y;
+                } else {
 #pragma unroll
-            for (int e = 0; e < SPL; ++e) {
-                const int off = (n16 * SPL + e) % (4 * NG);
-                t.sk[s][e] = ksb[sbase + off];
-                t.sv[s][e] = vsb[sbase + off];
+                    for (int q = 0; q < NG / 4; ++q) {
+                        const uint4 w = reinterpret_cast<const uint4*>(krow)[q];
+                        t.kw[j][s][4 * q + 0] = w.x; t.kw[j][s][4 * q + 1] = w.y;
+                        t.kw[j][s][4 * q + 2] = w.z; t.kw[j][s][4 * q + 3] = w.w;
+                    }
+                }
             }
-        }
-        const uint8_t* vt = vbase + (size_t)(tok0 / kTile) * (16 * D);
+            const uint8_t* vt = vbase[j] + (size_t)(tok0 / kTile) * (16 * D);
 #pragma unroll
-        for (int av = 0; av < NA; ++av)
-            t.vw[av] = *reinterpret_cast<const uint4*>(vt + ((av * 4 + r) * 16 + n16) * 16);
+            for (int av = 0; av < NA; ++av) t.vw[j][av] = *reinterpret_cast<const uint4*>(vt + av * 1024);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const size_t tok = (size_t)(tok0 + 16 * s + 4 * r + slot) * NG;
+            load_scales<NG>(t.sk[s], ks_l + tok);
+            load_scales<NG>(t.sv[s], vs_l + tok);
+        }
     };
 
-    auto compute_tile = [&](const TileLoads<D>& t, int it) {
+    auto compute_tile = [&](const TileLoads<D, P>& t, int it) {
         const int tok0 = start + it * kTile;
         // ---- scores
         float S[2][4];
@@ -245,24 +294,27 @@ void split_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
             static_for<NG>([&](auto gI) {
                 constexpr int g = decltype(gI)::value;
-                const half8_t A = unpack_codes_offset(t.kw[s][g]);
                 floatx4_t d = {qinit[g], qinit[g], qinit[g], qinit[g]};
-                d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[g], d, 0, 0, 0);
-                if constexpr (ROT) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[g], d, 0, 0, 0);
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const half8_t A = unpack_codes_offset(t.kw[j][s][g]);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[j][g], d, 0, 0, 0);
+                    if constexpr (ROT) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
+                }
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
-                    const float scl = row_bcast<Geo::src_lane(i, g)>(t.sk[s][Geo::src_reg(i, g)]);
-                    tot[i] += scl * d[i];
+                    tot[i] += quad_bcast<i>(t.sk[s][g]) * d[i];
                 });
             });
+            const bool full = tok0 + 16 * s + 16 <= end;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int tk = tok0 + 16 * s + 4 * r + i;
-                S[s][i] = (tk < end) ? tot[i] * qmul : kNegInf;
+                S[s][i] = (full || tk < end) ? tot[i] * qmul : kNegInf;
             }
         }
 
-        // ---- online softmax for head n16 over the tile's 32 tokens
+        // ---- online softmax for column n16 over the tile's 32 tokens
         float mt = kNegInf;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -272,16 +324,18 @@ void split_mfma_kernel(SplitArgs a)
         mt = fmaxf(mt, shfl_xor(mt, 32));
         const float m_new = fmaxf(m_run, mt);  // finite: the tile has a valid token
         // alpha is computed by every lane (1 where the max did not move, 0 on
-        // the first tile); the rescale runs only when some head's max moved,
-        // decided for the whole wave so that the shuffles see every lane.
+        // the first tile); the rescale runs only when some column's max
+        // moved, decided for the whole wave so that the shuffles see every lane.
         const float alpha = exp2_approx(m_run - m_new);
         if (__any(m_new != m_run)) {
             l_lane *= alpha;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 20 * r + i, 64);  // alpha of head 4 r + i
+                const float ai = __shfl(alpha, 20 * r + i, 64);  // alpha of column 4 r + i
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb][i] *= ai;
+                for (int j = 0; j < P; ++j)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[j][cb][i] *= ai;
             }
         }
         m_run = m_new;
@@ -295,100 +349,132 @@ void split_mfma_kernel(SplitArgs a)
             }
 
         // ---- values, one scale group (two 16-channel blocks) at a time:
-        //      A_g = p * s_v[token][g] as fp16 hi + lo, B = V codes
+        //      A_g = p * s_v[token][g] as fp16 hi + lo, B = V_j codes
         static_for<NG>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
             half8_t pa, pl;
             static_for<8>([&](auto eI) {
                 constexpr int e = decltype(eI)::value;
-                constexpr int j = kSlot[e], s = j / 4, i = j % 4;
-                const float scl = row_bcast<Geo::src_lane(i, g)>(t.sv[s][Geo::src_reg(i, g)]);
-                const float x = p[s][i] * scl;
+                constexpr int js = kSlot[e], s = js / 4, i = js % 4;
+                const float x = p[s][i] * quad_bcast<i>(t.sv[s][g]);
                 const _Float16 hi = (_Float16)x;
                 pa[e] = hi;
                 pl[e] = (_Float16)(x - (float)hi);
             });
-            static_for<2>([&](auto hI) {
-                constexpr int cb = 2 * g + decltype(hI)::value;
-                constexpr int av = cb / 4, bv = cb % 4;
-                const uint32_t word = bv == 0 ? t.vw[av].x : bv == 1 ? t.vw[av].y
-                                    : bv == 2 ? t.vw[av].z : t.vw[av].w;
-                const half8_t B = unpack_codes(word);
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
-            });
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                static_for<2>([&](auto hI) {
+                    constexpr int cb = 2 * g + decltype(hI)::value;
+                    constexpr int av = cb / 4, bv = cb % 4;
+                    const uint32_t word = bv == 0 ? t.vw[j][av].x : bv == 1 ? t.vw[j][av].y
+                                        : bv == 2 ? t.vw[j][av].z : t.vw[j][av].w;
+                    const half8_t B = unpack_codes(word);
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[j][cb], 0, 0, 0);
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[j][cb], 0, 0, 0);
+                });
+            }
         });
     };
 
-    // two register sets: the next tile's loads are in flight while the
-    // current one is computed
-    TileLoads<D> bufA, bufB;
-    int it = wave;
-    if (it < ntiles) load_tile(bufA, it);
-    while (it < ntiles) {
-        if (it + kWaves < ntiles) load_tile(bufB, it + kWaves);
-        compute_tile(bufA, it);
-        it += kWaves;
-        if (it >= ntiles) break;
-        if (it + kWaves < ntiles) load_tile(bufA, it + kWaves);
-        compute_tile(bufB, it);
-        it += kWaves;
+    if constexpr (PF) {
+        // two register sets: the next tile's loads are in flight while the
+        // current one is computed
+        TileLoads<D, P> bufA, bufB;
+        int it = wave;
+        if (it < ntiles) load_tile(bufA, it);
+        while (it < ntiles) {
+            if (it + kWaves < ntiles) load_tile(bufB, it + kWaves);
+            compute_tile(bufA, it);
+            it += kWaves;
+            if (it >= ntiles) break;
+            if (it + kWaves < ntiles) load_tile(bufA, it + kWaves);
+            compute_tile(bufB, it);
+            it += kWaves;
+        }
+    } else {
+        for (int it = wave; it < ntiles; it += kWaves) {
+            TileLoads<D, P> buf;
+            load_tile(buf, it);
+            compute_tile(buf, it);
+        }
     }
 
     // ---- merge the 4 rows (l only: m and O are already wave-wide), then waves
     float L = l_lane;
     L += shfl_xor(L, 16);
     L += shfl_xor(L, 32);
-    float* merge_o = lds;                       // [4][G][D]
-    float2* merge_ml = reinterpret_cast<float2*>(lds + kWaves * G * D);  // [4][G]
-    if (lane < 16 && lane < G) merge_ml[wave * G + lane] = make_float2(m_run, L);
+    float* merge_o = lds;                                                  // [4][PG][D]
+    float2* merge_ml = reinterpret_cast<float2*>(lds + kWaves * PG * D);  // [4][PG]
+    if (lane < PG) merge_ml[wave * PG + lane] = make_float2(m_run, L);
+    // rows 4 r .. 4 r + 3 of O lie in one KV head (G >= 4): keep that head's set
+    const int jr = min(4 * r / G, P - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
-        if (h < G) {
+        if (h < PG) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) merge_o[(wave * G + h) * D + 16 * cb + n16] = acc[cb][i];
+            for (int cb = 0; cb < NCB; ++cb) {
+                float v = acc[0][cb][i];
+#pragma unroll
+                for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
+                merge_o[(wave * PG + h) * D + 16 * cb + n16] = v;
+            }
         }
     }
     __syncthreads();
-    for (int i = tid; i < G * D; i += 256) {
+    for (int i = tid; i < PG * D; i += 256) {
         const int h = i / D, c = i % D;
         float Mb = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) Mb = fmaxf(Mb, merge_ml[w * G + h].x);
+        for (int w = 0; w < kWaves; ++w) Mb = fmaxf(Mb, merge_ml[w * PG + h].x);
         float o = 0.0f, Ls = 0.0f;
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) {
-            const float mw = merge_ml[w * G + h].x;
+            const float mw = merge_ml[w * PG + h].x;
             const float f = (mw == kNegInf) ? 0.0f : exp2_approx(mw - Mb);
-            o += f * merge_o[(w * G + h) * D + c];
-            Ls += f * merge_ml[w * G + h].y;
+            o += f * merge_o[(w * PG + h) * D + c];
+            Ls += f * merge_ml[w * PG + h].y;
         }
-        const size_t prow = ((size_t)b * a.Hq + hk * G + h) * a.num_splits + split;
+        const size_t prow = ((size_t)b * a.Hq + hk0 * G + h) * a.num_splits + split;
         a.part_o[prow * D + c] = o;
         if (c == 0) a.part_ml[prow] = make_float2(Mb, Ls);
     }
 }
 
-template <int D, bool ROT>
+
+// Prefetching the next tile needs a second register set; it is used only
+// where that set still fits without spilling.
+template <int D, int P>
+constexpr bool kPrefetch = (D == 64) || (D == 128 && P == 1);
+
+template <int D, int P, bool ROT>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)
 {
     const int G = a.Hq / a.H;
     const size_t q_bytes = 16 * D * sizeof(float);
-    const size_t merge_bytes = kWaves * G * (D * sizeof(float) + sizeof(float2));
+    const size_t merge_bytes = (size_t)kWaves * P * G * (D * sizeof(float) + sizeof(float2));
     const size_t lds = q_bytes > merge_bytes ? q_bytes : merge_bytes;
-    dim3 grid(a.num_splits, a.H, a.B), block(256);
-    split_mfma_kernel<D, ROT><<<grid, block, lds, stream>>>(a);
+    dim3 grid(a.num_splits, a.H / P, a.B), block(256);
+    split_mfma_kernel<D, P, ROT, kPrefetch<D, P>><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int D>
-hipError_t dispatch_rot(const SplitArgs& a, hipStream_t stream)
+hipError_t dispatch(const SplitArgs& a, hipStream_t stream)
 {
-    return a.signs ? launch<D, true>(a, stream) : launch<D, false>(a, stream);
+    const int P = split_mfma_heads_per_wave(a.D, a.Hq / a.H, a.H);
+    if (P == 2) return a.signs ? launch<D, 2, true>(a, stream) : launch<D, 2, false>(a, stream);
+    return a.signs ? launch<D, 1, true>(a, stream) : launch<D, 1, false>(a, stream);
 }
 
 }  // namespace
+
+// KV heads per wave: two (filling 16 MFMA columns at G = 8) when the head
+// count allows it and the registers suffice, else one.
+int split_mfma_heads_per_wave(int D, int G, int H)
+{
+    return (D != 256 && G <= 8 && H % 2 == 0) ? 2 : 1;
+}
 
 bool split_mfma_supports(int D, int G)
 {
@@ -398,9 +484,9 @@ bool split_mfma_supports(int D, int G)
 hipError_t launch_split_mfma(const SplitArgs& a, hipStream_t stream)
 {
     switch (a.D) {
-    case 64: return dispatch_rot<64>(a, stream);
-    case 128: return dispatch_rot<128>(a, stream);
-    case 256: return dispatch_rot<256>(a, stream);
+    case 64: return dispatch<64>(a, stream);
+    case 128: return dispatch<128>(a, stream);
+    case 256: return dispatch<256>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -14,8 +14,9 @@
 //
 // Wave layout per 32-token tile (two sub-tiles of 16 tokens):
 //  * score role: lane = 4 * t + q, t = token of the sub-tile, q = quarter of
-//    head_dim.  One 128-bit load gives the lane D/4 channels of one token;
-//    it multiplies them by q in fp32, applies its group scale(s) and the
+//    the K row.  One 128-bit load gives the lane 8 channels of every scale
+//    group of one token (the K row layout interleaves quarters of groups);
+//    it multiplies them by q in fp32, applies each group's scale and the
 //    4 lanes of a token sum with two xor shuffles.
 //  * value role: lane = 16 * r + n.  One 128-bit load of the V tile gives
 //    4 channels x 8 tokens; the 8 tokens are those whose scores live in the
@@ -40,8 +41,8 @@ template <int D>
 struct VecGeom {
     static constexpr int NG = D / kGroup;
     static constexpr int QC = D / 4;             // channels per score lane
-    static constexpr int NW = QC / 8;            // 32-bit code words per score lane
-    static constexpr int PG = (D >= 128) ? D / 128 : 1;  // groups per score lane
+    static constexpr int NW = QC / 8;            // 32-bit code words per score lane (one per group)
+    static constexpr int PG = (D >= 128) ? D / 128 : 1;  // groups whose p * s_v a score lane supplies
     static constexpr int NA = D / 64;            // 128-bit V loads per lane per tile
     static constexpr int src_lane(int i, int g)
     {
@@ -93,7 +94,7 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-        for (int i = 0; i < QC; ++i) qr[hh][i] = q_lds[hh][q4 * QC + i] * qmul;
+        for (int i = 0; i < QC; ++i) qr[hh][i] = q_lds[hh][32 * (i / 8) + 8 * q4 + i % 8] * qmul;
 
     const size_t head = (size_t)b * a.H + hk;
     const uint8_t* kbase = a.kc + head * a.cap * (D / 2) + q4 * (D / 8);
@@ -137,30 +138,26 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
                     kw[4 * w4 + 2] = t.z; kw[4 * w4 + 3] = t.w;
                 }
             }
-            float skr[PG];
+            float skr[NG];
 #pragma unroll
-            for (int gi = 0; gi < PG; ++gi) {
-                skr[gi] = ksb[(size_t)rowc * NG + g_first + gi];
-                svr[s][gi] = vsb[(size_t)rowc * NG + g_first + gi];
-            }
+            for (int g = 0; g < NG; ++g) skr[g] = ksb[(size_t)rowc * NG + g];
+#pragma unroll
+            for (int gi = 0; gi < PG; ++gi) svr[s][gi] = vsb[(size_t)rowc * NG + g_first + gi];
             float part[G];
 #pragma unroll
             for (int hh = 0; hh < G; ++hh) {
                 float tot = 0.0f;
-#pragma unroll
-                for (int gi = 0; gi < PG; ++gi) {
+                // word g holds channels 32 g + 8 q4 + 0..7
+                static_for<NG>([&](auto gI) {
+                    constexpr int g = decltype(gI)::value;
+                    const uint32_t word = kw[g];
                     float dot = 0.0f;
-                    constexpr int WPG = NW / PG;  // words per group held by the lane
-                    static_for<WPG>([&](auto wI) {
-                        constexpr int w = decltype(wI)::value;
-                        const uint32_t word = kw[gi * WPG + w];
-                        static_for<8>([&](auto kI) {
-                            constexpr int kb = decltype(kI)::value;
-                            dot += qr[hh][(gi * WPG + w) * 8 + kb] * nib_f32<kb>(word);
-                        });
+                    static_for<8>([&](auto kI) {
+                        constexpr int kb = decltype(kI)::value;
+                        dot += qr[hh][g * 8 + kb] * nib_f32<kb>(word);
                     });
-                    tot += skr[gi] * dot;
-                }
+                    tot += skr[g] * dot;
+                });
                 part[hh] = tot;
             }
 #pragma unroll

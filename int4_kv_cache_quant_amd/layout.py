@@ -1,8 +1,9 @@
-"""Index maps between the V-code tile layout of the cache and the plain
-token-major layout (pure permutations of nibbles; no arithmetic).
+"""Index maps between the cache's code layouts and the plain token-major
+layout (pure permutations of nibbles; no arithmetic).
 
 Plain layout: codes[..., token, D/2], byte j = element 2j (low nibble) and
-2j+1 (high nibble).  Tile layout (include/otq.h): per tile of 32 tokens,
+2j+1 (high nibble).  K row layout (include/otq.h): 32-bit word r * NG + g of
+a row holds channels 32 g + 8 r + 0..7.  V tile layout: per tile of 32 tokens,
 16*D bytes; tile-relative token u has quarter r = (u % 16) // 4 and slot
 j = 4 * (u // 16) + u % 4; channel c = 16 * (4a + b) + n owns word
 ((a*4 + r)*16 + n)*4 + b; slot j is nibble j % 2 of byte j // 2 of that word.
@@ -55,3 +56,27 @@ def v_plain_to_tiled(plain, D):
     u, c = _tile_maps(D)
     t = nib[..., u, c]                                       # [..., C/32, 16D, 2]
     return (t[..., 0] | (t[..., 1] << 4)).astype(np.uint8)
+
+
+@functools.lru_cache(maxsize=None)
+def _k_row_map(D):
+    """plain byte index held by each K-row byte (same nibble order)."""
+    NG = D // 32
+    idx = np.zeros(D // 2, np.int64)
+    for c in range(0, D, 2):
+        g, r, k = c // 32, (c // 8) % 4, c % 8
+        idx[(r * NG + g) * 4 + k // 2] = c // 2
+    return idx
+
+
+def k_rows_to_plain(rows, D):
+    """[..., T, D/2] K row layout -> [..., T, D/2] plain layout."""
+    rows = np.asarray(rows, np.uint8)
+    out = np.empty_like(rows)
+    out[..., _k_row_map(D)] = rows
+    return out
+
+
+def k_plain_to_rows(plain, D):
+    """[..., T, D/2] plain layout -> [..., T, D/2] K row layout."""
+    return np.asarray(plain, np.uint8)[..., _k_row_map(D)]

@@ -42,7 +42,7 @@ def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True
 def host_cache(cache):
     """(k_codes, k_scales, v_codes_plain, v_scales) as numpy arrays."""
     D = cache.shape[2]
-    return (cache.k_codes.cpu().numpy(), cache.k_scales.cpu().numpy(),
+    return (layout.k_rows_to_plain(cache.k_codes.cpu().numpy(), D), cache.k_scales.cpu().numpy(),
             layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D), cache.v_scales.cpu().numpy())
 
 

@@ -158,3 +158,19 @@ def test_v_layout_roundtrip_and_fixed_points(D):
     t = layout.v_plain_to_tiled(p, D)[0]
     assert t[0] == 0x53 and t[2] == 0x07 and t[64 * 4] == 0x01 and t[5 * 4] == 0x02
     assert np.count_nonzero(t) == 4
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_k_row_layout_roundtrip_and_fixed_points(D):
+    rng = np.random.default_rng(1)
+    plain = rng.integers(0, 256, (3, 5, D // 2), dtype=np.uint8)
+    rows = layout.k_plain_to_rows(plain, D)
+    assert np.array_equal(layout.k_rows_to_plain(rows, D), plain)
+    NG = D // 32
+    # hand-worked: channel 8 (group 0, quarter 1, k 0) -> word NG -> byte 4*NG;
+    # channel 33 (group 1, quarter 0, k 1) -> word 1, byte 4, high nibble.
+    p = np.zeros((1, D // 2), np.uint8)
+    p[0, 4] = 0x05            # channel 8 = 5
+    p[0, 16] = 0x30           # channel 33 = 3
+    r = layout.k_plain_to_rows(p, D)[0]
+    assert r[4 * NG] == 0x05 and r[4] == 0x30 and np.count_nonzero(r) == 2

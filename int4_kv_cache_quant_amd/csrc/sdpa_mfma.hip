@@ -12,12 +12,15 @@
 // page, section on numerical stability).
 //
 // Exactness of the products:
-//  * V codes are integers in [-8, 7], exact in fp16 (built with the 1024 + n
-//    magic constant and one packed fp16 subtraction); K codes enter as the
-//    fp16 subnormals n * 2^-24 of their offset-binary value n = c + 8 (one
-//    byte permute per pair, no arithmetic), the MFMA accumulator starts at
-//    -8 * 2^-24 * sum(q) so that it ends at 2^-24 * q.c, and 2^24 is folded
-//    into the softmax scale (the matrix cores keep fp16 subnormals);
+//  * codes enter the MFMAs as fp16 subnormals of their offset-binary value
+//    n = c + 8: a nibble left at bit 0 (or bit 4) of a 16-bit half reads as
+//    n * 2^-24 (or n * 2^-20), so one shift and four masks give all eight
+//    operands of a 32-bit word; the 2^4 of the bit-4 nibbles is cancelled
+//    exactly by a power-of-two factor on the other operand, and the +8 is
+//    removed by starting the score accumulator at -8 * 2^-24 * sum(q) and,
+//    for values, by a correction product against a constant operand (the
+//    matrix cores keep fp16 subnormals); 2^24 is folded into the softmax
+//    scale and the final merge;
 //  * q is converted to fp16 (bf16 values convert exactly in fp16's normal
 //    range); a rotated q is split into fp16 hi + lo parts and both are
 //    multiplied, so the score keeps ~22 bits of q;
@@ -63,44 +66,21 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr int kWaves = 4;
 
-// MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the word:
-// registers are (0,2), (4,6), (1,3), (5,7) so that each is one byte permute.
-constexpr int kSlot[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+// MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
+// word, scaled by 2^(kShift[e] - 24): registers are (0,4), (1,5), (2,6),
+// (3,7), each one mask of the word or of the word shifted by 8 bits.
+constexpr int kSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+constexpr int kShift[8] = {0, 0, 4, 4, 0, 0, 4, 4};
 
-// 8 signed nibbles -> 8 exact fp16 integers in MFMA operand order.
+// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^(kShift[e] - 24).
 __device__ __forceinline__ half8_t unpack_codes(uint32_t w)
 {
-    const uint32_t x = w ^ 0x88888888u;          // offset binary: n = c + 8
-    const uint32_t lo = x & 0x0F0F0F0Fu;         // elements 0,2,4,6
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;  // elements 1,3,5,7
-    const uint32_t K = 0x64646464u;              // fp16 0x64nn = 1024 + nn
+    const uint32_t w8 = w >> 8;
     uint32_t r[4];
-    r[0] = __builtin_amdgcn_perm(K, lo, 0x04010400u);
-    r[1] = __builtin_amdgcn_perm(K, lo, 0x04030402u);
-    r[2] = __builtin_amdgcn_perm(K, hi, 0x04010400u);
-    r[3] = __builtin_amdgcn_perm(K, hi, 0x04030402u);
-    const half2_t bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-    half8_t out;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        half2_t p = __builtin_bit_cast(half2_t, r[m]) + bias;  // exact: 1024 + n - 1032
-        out[2 * m] = p[0];
-        out[2 * m + 1] = p[1];
-    }
-    return out;
-}
-
-// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^-24, same operand order.
-__device__ __forceinline__ half8_t unpack_codes_offset(uint32_t w)
-{
-    const uint32_t x = w ^ 0x88888888u;
-    const uint32_t lo = x & 0x0F0F0F0Fu;
-    const uint32_t hi = (x >> 4) & 0x0F0F0F0Fu;
-    uint32_t r[4];
-    r[0] = __builtin_amdgcn_perm(0u, lo, 0x04010400u);
-    r[1] = __builtin_amdgcn_perm(0u, lo, 0x04030402u);
-    r[2] = __builtin_amdgcn_perm(0u, hi, 0x04010400u);
-    r[3] = __builtin_amdgcn_perm(0u, hi, 0x04030402u);
+    r[0] = (w ^ 0x88888888u) & 0x000F000Fu;   // elements 0, 4 at bit 0
+    r[1] = (w ^ 0x88888888u) & 0x00F000F0u;   // elements 1, 5 at bit 4
+    r[2] = (w8 ^ 0x00888888u) & 0x000F000Fu;  // elements 2, 6 at bit 0
+    r[3] = (w8 ^ 0x00888888u) & 0x00F000F0u;  // elements 3, 7 at bit 4
     half8_t out;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
@@ -118,6 +98,86 @@ __device__ __forceinline__ float quad_bcast(float v)
     static_assert(K >= 0 && K < 4, "quad lane");
     return __builtin_bit_cast(
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, false));
+}
+
+// Cross-row reductions without LDS: v_permlane16_swap pairs rows (0,1) and
+// (2,3), v_permlane32_swap pairs the two halves; each lane receives its own
+// value and its partner's in the two results.
+__device__ __forceinline__ float max_xor16(float v)
+{
+    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
+                                                    __builtin_bit_cast(unsigned, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                    __builtin_bit_cast(unsigned, v), false, false);
+    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+}
+
+// Value of lane 4 r + I of the lane's own row (r = lane / 16), by DPP row
+// broadcasts: the source differs per row, so the four candidates are selected.
+template <int I>
+__device__ __forceinline__ float row_quad_gather(float v, int r)
+{
+    const float v0 = row_bcast<I>(v), v1 = row_bcast<4 + I>(v);
+    const float v2 = row_bcast<8 + I>(v), v3 = row_bcast<12 + I>(v);
+    return r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3;
+}
+
+// s_waitcnt lgkmcnt(0) with the vector-memory and export counters left
+// unconstrained (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4],
+// lgkmcnt [11:8]).
+constexpr int kWaitLgkm0 = 0xC07F;
+
+// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 l (lds_base wave-uniform).
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+__device__ __forceinline__ void dma16(const void* src, void* lds_base)
+{
+    __builtin_amdgcn_global_load_lds((glb_void_t*)const_cast<void*>(src), (lds_void_t*)lds_base, 16, 0, 0);
+}
+
+// One tile of the P KV heads, staged in LDS:
+//  [K_0 .. K_{P-1}][V_0 .. V_{P-1}][scales]
+// K_j: 32 rows x D/2 bytes as 16-byte chunks, chunk c of row t at slot
+//      k_slot(t, c) (a rotation within the row that spreads the 16 lanes
+//      reading one quarter over distinct banks);
+// V_j: the V tile as stored in memory;
+// scales: [K, V][head][32 tokens][D/32] fp32.
+template <int D, int P>
+struct Stage {
+    static constexpr int KB = 16 * D;             // K or V bytes per head per tile
+    static constexpr int SB_RAW = 2 * P * 4 * D;  // scale bytes (K and V, all heads)
+    static constexpr int SB = SB_RAW < 1024 ? 1024 : SB_RAW;
+    static constexpr int BYTES = 2 * P * KB + SB;
+    static constexpr int koff(int j) { return j * KB; }
+    static constexpr int voff(int j) { return (P + j) * KB; }
+    static constexpr int SOFF = 2 * P * KB;
+};
+
+template <int D>
+__device__ __forceinline__ int k_slot(int t, int c)
+{
+    if constexpr (D == 128) return 4 * t + ((c + (t >> 2)) & 3);
+    else if constexpr (D == 256) return 8 * t + (c ^ (((t >> 1) & 3) << 1));
+    else return 2 * t + c;
+}
+template <int D>
+__device__ __forceinline__ void k_unslot(int slot, int& t, int& c)
+{
+    if constexpr (D == 128) {
+        t = slot >> 2;
+        c = ((slot & 3) - (t >> 2)) & 3;
+    } else if constexpr (D == 256) {
+        t = slot >> 3;
+        c = (slot & 7) ^ (((t >> 1) & 3) << 1);
+    } else {
+        t = slot >> 1;
+        c = slot & 1;
+    }
 }
 
 template <int NG>
@@ -151,14 +211,15 @@ struct TileLoads {
 template <int D>
 constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 
-template <int D, int P, bool ROT, bool PF>
+template <int D, int P, bool ROT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
 void split_mfma_kernel(SplitArgs a)
 {
     constexpr int NG = D / kGroup, NA = D / 64, NCB = D / 16;
-    extern __shared__ float lds[];  // q: [16][D]; later merge: [4][P*G][D] + ml [4][P*G]
+    extern __shared__ float lds[];  // q: [16][D]; then per-wave tile stages; then the merge
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
     const int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
     const int G = a.Hq / a.H;
     const int PG = P * G;  // query heads served by the block (<= 16)
@@ -209,11 +270,15 @@ void split_mfma_kernel(SplitArgs a)
         for (int e = 0; e < 8; ++e) {
             const float x = q_lds[n16 * D + 32 * g + 8 * r + kSlot[e]];
             const _Float16 h16 = (_Float16)x;
-            hv[e] = h16;
-            t += (float)h16;
+            const _Float16 l16 = (_Float16)(x - (float)h16);
+            // cancel the code's 2^kShift (a power of two); the offset sum
+            // below uses the operands exactly as the MFMA sees them
+            const float down = kShift[e] ? 0.0625f : 1.0f, up = kShift[e] ? 16.0f : 1.0f;
+            hv[e] = (_Float16)((float)h16 * down);
+            t += (float)hv[e] * up;
             if (ROT) {
-                lv[e] = (_Float16)(x - (float)h16);
-                t += (float)lv[e];
+                lv[e] = (_Float16)((float)l16 * down);
+                t += (float)lv[e] * up;
             }
         }
 #pragma unroll
@@ -233,55 +298,81 @@ void split_mfma_kernel(SplitArgs a)
     const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
     __syncthreads();  // q_lds is reused for the final merge
 
-    const uint8_t* kbase[P];
-    const uint8_t* vbase[P];
-#pragma unroll
-    for (int j = 0; j < P; ++j) {
-        const size_t head = (size_t)b * a.H + hk0 + j;
-        kbase[j] = a.kc + head * a.cap * (D / 2) + r * (D / 8);  // row quarter r
-        vbase[j] = a.vc + head * (a.cap / kTile) * (16 * D) + ((size_t)r * 16 + n16) * 16;
-    }
-    const size_t head_l = (size_t)b * a.H + hk0 + jl;
-    const float* ks_l = a.ks + head_l * a.cap * NG;
-    const float* vs_l = a.vs + head_l * a.cap * NG;
+    using St = Stage<D, P>;
+    const size_t head0 = (size_t)b * a.H + hk0;
+    char* stage = reinterpret_cast<char*>(lds) + wave * St::BYTES;
 
     float m_run = kNegInf;  // running max of column n16 (log2 domain)
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
-    floatx4_t acc[P][NCB];
+    // acc[j]: 2^-24 * sum p s_v (c + 8) V rows of KV head j; corr: 2^-24 * 8 *
+    // sum p s_v per scale group (shared by the heads: it depends on p only)
+    floatx4_t acc[P][NCB], corr[NG];
 #pragma unroll
     for (int j = 0; j < P; ++j)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int g = 0; g < NG; ++g) corr[g] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    // B operand of the correction product: 8 * 2^(kShift[e] - 24) in every column
+    half8_t bcorr;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) bcorr[e] = (_Float16)(kShift[e] ? 0x1p-17f : 0x1p-21f);
 
-    auto load_tile = [&](TileLoads<D, P>& t, int it) {
+    // issue the direct-to-LDS copies of one tile (no registers held)
+    auto dma_tile = [&](int it) {
         const int tok0 = start + it * kTile;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const uint8_t* kt = a.kc + ((head0 + j) * a.cap + tok0) * (D / 2);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) {
+                int t, c;
+                k_unslot<D>(64 * i + lane, t, c);
+                dma16(kt + t * (D / 2) + 16 * c, stage + St::koff(j) + 1024 * i);
+            }
+            const uint8_t* vt = a.vc + ((head0 + j) * (a.cap / kTile) + tok0 / kTile) * (16 * D);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) dma16(vt + 1024 * i + 16 * lane, stage + St::voff(j) + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < St::SB / 1024; ++i) {
+            const int o = (1024 * i + 16 * lane) % St::SB_RAW;
+            const int kv = o / (P * 4 * D), j = (o / (4 * D)) % P, within = o % (4 * D);
+            const float* base = (kv ? a.vs : a.ks) + ((head0 + j) * a.cap + tok0) * NG;
+            dma16(reinterpret_cast<const char*>(base) + within, stage + St::SOFF + 1024 * i);
+        }
+    };
+
+    // this lane's operands of the staged tile, into registers
+    auto read_stage = [&](TileLoads<D, P>& t) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                // quarter r of the row: word g = channels 32 g + 8 r + 0..7
-                const uint8_t* krow = kbase[j] + (size_t)(tok0 + 16 * s + n16) * (D / 2);
-                if constexpr (NG == 2) {
-                    const uint2 w = *reinterpret_cast<const uint2*>(krow);
+                const int tr = 16 * s + n16;  // quarter r of row tr: word g = channels 32 g + 8 r + 0..7
+                if constexpr (D == 64) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(
+                        stage + St::koff(j) + 16 * k_slot<D>(tr, r >> 1) + 8 * (r & 1));
                     t.kw[j][s][0] = w.x; t.kw[j][s][1] = w.y;
                 } else {
 #pragma unroll
                     for (int q = 0; q < NG / 4; ++q) {
-                        const uint4 w = reinterpret_cast<const uint4*>(krow)[q];
+                        const uint4 w = *reinterpret_cast<const uint4*>(
+                            stage + St::koff(j) + 16 * k_slot<D>(tr, (NG / 4) * r + q));
                         t.kw[j][s][4 * q + 0] = w.x; t.kw[j][s][4 * q + 1] = w.y;
                         t.kw[j][s][4 * q + 2] = w.z; t.kw[j][s][4 * q + 3] = w.w;
                     }
                 }
             }
-            const uint8_t* vt = vbase[j] + (size_t)(tok0 / kTile) * (16 * D);
 #pragma unroll
-            for (int av = 0; av < NA; ++av) t.vw[j][av] = *reinterpret_cast<const uint4*>(vt + av * 1024);
+            for (int av = 0; av < NA; ++av)
+                t.vw[j][av] = *reinterpret_cast<const uint4*>(stage + St::voff(j) + 1024 * av + 16 * lane);
         }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const size_t tok = (size_t)(tok0 + 16 * s + 4 * r + slot) * NG;
-            load_scales<NG>(t.sk[s], ks_l + tok);
-            load_scales<NG>(t.sv[s], vs_l + tok);
+            const int tt = 16 * s + 4 * r + slot;
+            load_scales<NG>(t.sk[s], reinterpret_cast<const float*>(stage + St::SOFF) + (jl * 32 + tt) * NG);
+            load_scales<NG>(t.sv[s], reinterpret_cast<const float*>(stage + St::SOFF) + ((P + jl) * 32 + tt) * NG);
         }
     };
 
@@ -297,7 +388,7 @@ void split_mfma_kernel(SplitArgs a)
                 floatx4_t d = {qinit[g], qinit[g], qinit[g], qinit[g]};
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    const half8_t A = unpack_codes_offset(t.kw[j][s][g]);
+                    const half8_t A = unpack_codes(t.kw[j][s][g]);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[j][g], d, 0, 0, 0);
                     if constexpr (ROT) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
                 }
@@ -320,23 +411,25 @@ void split_mfma_kernel(SplitArgs a)
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, S[s][i]);
-        mt = fmaxf(mt, shfl_xor(mt, 16));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
+        mt = max_xor32(max_xor16(mt));
         const float m_new = fmaxf(m_run, mt);  // finite: the tile has a valid token
         // alpha is computed by every lane (1 where the max did not move, 0 on
         // the first tile); the rescale runs only when some column's max
-        // moved, decided for the whole wave so that the shuffles see every lane.
+        // moved, decided for the whole wave so that the cross-lane moves see
+        // every lane.
         const float alpha = exp2_approx(m_run - m_new);
         if (__any(m_new != m_run)) {
             l_lane *= alpha;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 20 * r + i, 64);  // alpha of column 4 r + i
+            static_for<4>([&](auto iI) {
+                constexpr int i = decltype(iI)::value;
+                const float ai = row_quad_gather<i>(alpha, r);  // alpha of column 4 r + i
 #pragma unroll
                 for (int j = 0; j < P; ++j)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) acc[j][cb][i] *= ai;
-            }
+#pragma unroll
+                for (int g = 0; g < NG; ++g) corr[g][i] *= ai;
+            });
         }
         m_run = m_new;
         float p[2][4];
@@ -349,18 +442,25 @@ void split_mfma_kernel(SplitArgs a)
             }
 
         // ---- values, one scale group (two 16-channel blocks) at a time:
-        //      A_g = p * s_v[token][g] as fp16 hi + lo, B = V_j codes
+        //      A_g = p * s_v[token][g] * 2^-kShift as fp16 hi + lo, B = V_j
+        //      codes.  Token slot j = kSlot[e] is token 4 r + j % 4 of sub-tile
+        //      j / 4; the odd slots are the bit-4 nibbles, so the quad lanes
+        //      holding odd tokens hand out s_v / 16.
+        const float vdown = (slot & 1) ? 0.0625f : 1.0f;
         static_for<NG>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
+            const float sv0 = t.sv[0][g] * vdown, sv1 = t.sv[1][g] * vdown;
             half8_t pa, pl;
             static_for<8>([&](auto eI) {
                 constexpr int e = decltype(eI)::value;
                 constexpr int js = kSlot[e], s = js / 4, i = js % 4;
-                const float x = p[s][i] * quad_bcast<i>(t.sv[s][g]);
+                const float x = p[s][i] * quad_bcast<i>(s == 0 ? sv0 : sv1);
                 const _Float16 hi = (_Float16)x;
                 pa[e] = hi;
                 pl[e] = (_Float16)(x - (float)hi);
             });
+            corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bcorr, corr[g], 0, 0, 0);
+            corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bcorr, corr[g], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 static_for<2>([&](auto hI) {
@@ -376,28 +476,22 @@ void split_mfma_kernel(SplitArgs a)
         });
     };
 
-    if constexpr (PF) {
-        // two register sets: the next tile's loads are in flight while the
-        // current one is computed
-        TileLoads<D, P> bufA, bufB;
-        int it = wave;
-        if (it < ntiles) load_tile(bufA, it);
-        while (it < ntiles) {
-            if (it + kWaves < ntiles) load_tile(bufB, it + kWaves);
-            compute_tile(bufA, it);
-            it += kWaves;
-            if (it >= ntiles) break;
-            if (it + kWaves < ntiles) load_tile(bufA, it + kWaves);
-            compute_tile(bufB, it);
-            it += kWaves;
+    // one LDS stage per wave: the next tile's copies are issued right after
+    // the current tile has been read into registers, and stream in while it
+    // is computed (the compute phase touches no LDS)
+    int it = wave;
+    if (it < ntiles) dma_tile(it);
+    for (; it < ntiles; it += kWaves) {
+        TileLoads<D, P> t;
+        read_stage(t);
+        if (it + kWaves < ntiles) {
+            // the copies overwrite the stage just read: let the reads finish
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            dma_tile(it + kWaves);
         }
-    } else {
-        for (int it = wave; it < ntiles; it += kWaves) {
-            TileLoads<D, P> buf;
-            load_tile(buf, it);
-            compute_tile(buf, it);
-        }
+        compute_tile(t, it);
     }
+    __syncthreads();  // every wave is done with its stage before the merge reuses LDS
 
     // ---- merge the 4 rows (l only: m and O are already wave-wide), then waves
     float L = l_lane;
@@ -417,7 +511,7 @@ void split_mfma_kernel(SplitArgs a)
                 float v = acc[0][cb][i];
 #pragma unroll
                 for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
-                merge_o[(wave * PG + h) * D + 16 * cb + n16] = v;
+                merge_o[(wave * PG + h) * D + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
             }
         }
     }
@@ -442,20 +536,17 @@ void split_mfma_kernel(SplitArgs a)
 }
 
 
-// Prefetching the next tile needs a second register set; it is used only
-// where that set still fits without spilling.
-template <int D, int P>
-constexpr bool kPrefetch = (D == 64) || (D == 128 && P == 1);
-
 template <int D, int P, bool ROT>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)
 {
     const int G = a.Hq / a.H;
     const size_t q_bytes = 16 * D * sizeof(float);
     const size_t merge_bytes = (size_t)kWaves * P * G * (D * sizeof(float) + sizeof(float2));
-    const size_t lds = q_bytes > merge_bytes ? q_bytes : merge_bytes;
+    const size_t stage_bytes = (size_t)kWaves * Stage<D, P>::BYTES;
+    size_t lds = q_bytes > merge_bytes ? q_bytes : merge_bytes;
+    if (stage_bytes > lds) lds = stage_bytes;
     dim3 grid(a.num_splits, a.H / P, a.B), block(256);
-    split_mfma_kernel<D, P, ROT, kPrefetch<D, P>><<<grid, block, lds, stream>>>(a);
+    split_mfma_kernel<D, P, ROT><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -60,7 +60,8 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
     __shared__ float2 merge_ml[4][G];
     __shared__ float merge_o[4][G][D];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
     const int len = min(max(a.lens[b], 0), a.max_len);
     const int start = split * a.chunk;

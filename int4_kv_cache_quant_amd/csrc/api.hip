@@ -58,6 +58,8 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_MFMA) {
         if (!otq::split_mfma_supports(D, G)) return OTQ_EUNSUPPORTED;
+        // the MFMA variant addresses two heads of codes with 32-bit buffer offsets
+        if ((long long)2 * c->capacity * (D / 2) >= ((long long)1 << 31)) return OTQ_EUNSUPPORTED;
     } else {
         return OTQ_EINVAL;
     }

@@ -41,13 +41,14 @@ __device__ __forceinline__ float widen(uint16_t b, int dtype)
 
 // ------------------------------------------------------------ cross-lane
 // Broadcast lane K (0..15) of each row of 16 lanes to the whole row (DPP
-// row_newbcast, gfx90a and later).
+// row_newbcast, gfx90a and later).  bound_ctrl is set (every source lane is
+// valid anyway) so that the move can fold into a consuming v_mul / v_add.
 template <int K>
 __device__ __forceinline__ float row_bcast(float v)
 {
     static_assert(K >= 0 && K < 16, "row lane");
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, false));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + K, 0xF, 0xF, true));
 }
 
 __device__ __forceinline__ float shfl_xor(float v, int m)

@@ -97,7 +97,7 @@ __device__ __forceinline__ float quad_bcast(float v)
 {
     static_assert(K >= 0 && K < 4, "quad lane");
     return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, false));
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, true));
 }
 
 // Cross-row reductions without LDS: v_permlane16_swap pairs rows (0,1) and
@@ -130,14 +130,22 @@ __device__ __forceinline__ float row_quad_gather(float v, int r)
 // unconstrained (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4],
 // lgkmcnt [11:8]).
 constexpr int kWaitLgkm0 = 0xC07F;
+// s_waitcnt vmcnt(0) with the other counters unconstrained.
+constexpr int kWaitVm0 = 0x0F70;
 
-// Direct global -> LDS copy of 16 bytes per lane: lane l's bytes land at
-// lds_base + 16 l (lds_base wave-uniform).
+// Direct buffer -> LDS copy of 16 bytes per lane: lane l reads the resource
+// at voffset + soffset and its bytes land at lds_base + 16 l (lds_base and
+// soffset wave-uniform).  Reads past the resource's record count return 0.
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-__device__ __forceinline__ void dma16(const void* src, void* lds_base)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
+                                      void* lds_base)
 {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)const_cast<void*>(src), (lds_void_t*)lds_base, 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voffset, soffset, 0, 0);
+}
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
 
 // One tile of the P KV heads, staged in LDS:
@@ -149,13 +157,14 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_base)
 // scales: [K, V][head][32 tokens][D/32] fp32.
 template <int D, int P>
 struct Stage {
-    static constexpr int KB = 16 * D;             // K or V bytes per head per tile
-    static constexpr int SB_RAW = 2 * P * 4 * D;  // scale bytes (K and V, all heads)
-    static constexpr int SB = SB_RAW < 1024 ? 1024 : SB_RAW;
-    static constexpr int BYTES = 2 * P * KB + SB;
+    static constexpr int KB = 16 * D;               // K or V bytes per head per tile
+    static constexpr int SRAW = P * 4 * D;          // K (or V) scale bytes, all heads
+    static constexpr int SPAD = SRAW < 1024 ? 1024 : SRAW;
+    static constexpr int BYTES = 2 * P * KB + 2 * SPAD;
     static constexpr int koff(int j) { return j * KB; }
     static constexpr int voff(int j) { return (P + j) * KB; }
-    static constexpr int SOFF = 2 * P * KB;
+    static constexpr int KSOFF = 2 * P * KB;        // K scales [head][32 tokens][D/32]
+    static constexpr int VSOFF = KSOFF + SPAD;      // V scales, same layout
 };
 
 template <int D>
@@ -223,17 +232,72 @@ void split_mfma_kernel(SplitArgs a)
     const int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
     const int G = a.Hq / a.H;
     const int PG = P * G;  // query heads served by the block (<= 16)
-    const int len = min(max(a.lens[b], 0), a.max_len);
     const int start = split * a.chunk;
-    if (start >= len) return;  // block-uniform
-    const int end = min(start + a.chunk, len);
-    const int ntiles = (end - start + kTile - 1) / kTile;
     const int n16 = lane & 15, r = lane >> 4, slot = lane & 3;
     const bool col_valid = n16 < PG;
     const int jl = col_valid ? n16 / G : P - 1;  // KV head of this lane's column
 
-    // ---- query prologue: fp32 in LDS, rotated like K when the cache is
-    float* q_lds = lds;
+    using St = Stage<D, P>;
+    const size_t head0 = (size_t)b * a.H + hk0;
+    char* stage = reinterpret_cast<char*>(lds) + wave * St::BYTES;
+
+    // Buffer resources of the block's P heads (K codes, V tiles, K and V
+    // scales); each spans exactly those heads, so no copy can leave them.
+    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(a.kc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
+    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(a.vc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
+    const __amdgpu_buffer_rsrc_t rs_ks = make_rsrc(a.ks + head0 * a.cap * NG, P * a.cap * NG * 4);
+    const __amdgpu_buffer_rsrc_t rs_vs = make_rsrc(a.vs + head0 * a.cap * NG, P * a.cap * NG * 4);
+    // per-lane byte offsets of each copy instruction (tile-independent; the
+    // tile enters as the scalar offset tok0 * D/2, or tok0 * D/8 for scales)
+    int vo_k[P][D / 64], vo_v[P][D / 64], vo_s;
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int i = 0; i < D / 64; ++i) {
+            int t, c;
+            k_unslot<D>(64 * i + lane, t, c);
+            vo_k[j][i] = j * a.cap * (D / 2) + t * (D / 2) + 16 * c;
+            vo_v[j][i] = j * a.cap * (D / 2) + 1024 * i + 16 * lane;
+        }
+    {
+        const int o = (16 * lane) % St::SRAW;  // lanes past the scale bytes repeat them
+        vo_s = (o / (4 * D)) * a.cap * NG * 4 + o % (4 * D);
+    }
+
+    // issue the direct-to-LDS copies of one tile (no registers held)
+    auto dma_tile = [&](int it) {
+        const int tok0 = start + it * kTile;
+        const int so_code = tok0 * (D / 2), so_scale = tok0 * NG * 4;
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) dma16(rs_k, vo_k[j][i], so_code, stage + St::koff(j) + 1024 * i);
+#pragma unroll
+            for (int i = 0; i < D / 64; ++i) dma16(rs_v, vo_v[j][i], so_code, stage + St::voff(j) + 1024 * i);
+        }
+#pragma unroll
+        for (int i = 0; i < St::SPAD / 1024; ++i) {
+            dma16(rs_ks, vo_s + 1024 * i, so_scale, stage + St::KSOFF + 1024 * i);
+            dma16(rs_vs, vo_s + 1024 * i, so_scale, stage + St::VSOFF + 1024 * i);
+        }
+    };
+
+    // The first tile of every wave streams in before lens[b] is even known,
+    // if it lies inside the cache (capacity is a multiple of 32, so a tile
+    // starting below it is whole); tokens past lens[b] are masked later, or
+    // the block leaves.
+    if (start + wave * kTile < a.cap) dma_tile(wave);
+    const int len = min(max(a.lens[b], 0), a.max_len);
+    if (start >= len) {  // block-uniform: no partial for an empty chunk
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy may land after the block is gone
+        return;
+    }
+    const int end = min(start + a.chunk, len);
+    const int ntiles = (end - start + kTile - 1) / kTile;
+
+    // ---- query prologue: fp32 in LDS (past the tile stages), rotated like K
+    //      when the cache is
+    float* q_lds = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kWaves * St::BYTES);
     const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G) * D;
     for (int i = tid; i < 16 * D; i += 256) {
         const int h = i / D, c = i % D;
@@ -295,12 +359,12 @@ void split_mfma_kernel(SplitArgs a)
         t += shfl_xor(t, 32);
         qinit[g] = -8.0f * 0x1p-24f * t;
     }
+    floatx4_t qinit4[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) qinit4[g] = floatx4_t{qinit[g], qinit[g], qinit[g], qinit[g]};
     const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
-    __syncthreads();  // q_lds is reused for the final merge
+    __syncthreads();  // q_lds is reused by the final merge
 
-    using St = Stage<D, P>;
-    const size_t head0 = (size_t)b * a.H + hk0;
-    char* stage = reinterpret_cast<char*>(lds) + wave * St::BYTES;
 
     float m_run = kNegInf;  // running max of column n16 (log2 domain)
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
@@ -317,31 +381,6 @@ void split_mfma_kernel(SplitArgs a)
     half8_t bcorr;
 #pragma unroll
     for (int e = 0; e < 8; ++e) bcorr[e] = (_Float16)(kShift[e] ? 0x1p-17f : 0x1p-21f);
-
-    // issue the direct-to-LDS copies of one tile (no registers held)
-    auto dma_tile = [&](int it) {
-        const int tok0 = start + it * kTile;
-#pragma unroll
-        for (int j = 0; j < P; ++j) {
-            const uint8_t* kt = a.kc + ((head0 + j) * a.cap + tok0) * (D / 2);
-#pragma unroll
-            for (int i = 0; i < D / 64; ++i) {
-                int t, c;
-                k_unslot<D>(64 * i + lane, t, c);
-                dma16(kt + t * (D / 2) + 16 * c, stage + St::koff(j) + 1024 * i);
-            }
-            const uint8_t* vt = a.vc + ((head0 + j) * (a.cap / kTile) + tok0 / kTile) * (16 * D);
-#pragma unroll
-            for (int i = 0; i < D / 64; ++i) dma16(vt + 1024 * i + 16 * lane, stage + St::voff(j) + 1024 * i);
-        }
-#pragma unroll
-        for (int i = 0; i < St::SB / 1024; ++i) {
-            const int o = (1024 * i + 16 * lane) % St::SB_RAW;
-            const int kv = o / (P * 4 * D), j = (o / (4 * D)) % P, within = o % (4 * D);
-            const float* base = (kv ? a.vs : a.ks) + ((head0 + j) * a.cap + tok0) * NG;
-            dma16(reinterpret_cast<const char*>(base) + within, stage + St::SOFF + 1024 * i);
-        }
-    };
 
     // this lane's operands of the staged tile, into registers
     auto read_stage = [&](TileLoads<D, P>& t) {
@@ -371,8 +410,8 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int tt = 16 * s + 4 * r + slot;
-            load_scales<NG>(t.sk[s], reinterpret_cast<const float*>(stage + St::SOFF) + (jl * 32 + tt) * NG);
-            load_scales<NG>(t.sv[s], reinterpret_cast<const float*>(stage + St::SOFF) + ((P + jl) * 32 + tt) * NG);
+            load_scales<NG>(t.sk[s], reinterpret_cast<const float*>(stage + St::KSOFF) + (jl * 32 + tt) * NG);
+            load_scales<NG>(t.sv[s], reinterpret_cast<const float*>(stage + St::VSOFF) + (jl * 32 + tt) * NG);
         }
     };
 
@@ -385,7 +424,7 @@ void split_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
             static_for<NG>([&](auto gI) {
                 constexpr int g = decltype(gI)::value;
-                floatx4_t d = {qinit[g], qinit[g], qinit[g], qinit[g]};
+                floatx4_t d = qinit4[g];
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
                     const half8_t A = unpack_codes(t.kw[j][s][g]);
@@ -394,7 +433,8 @@ void split_mfma_kernel(SplitArgs a)
                 }
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
-                    tot[i] += quad_bcast<i>(t.sk[s][g]) * d[i];
+                    const float term = quad_bcast<i>(t.sk[s][g]) * d[i];  // folds into v_mul_f32_dpp
+                    tot[i] = (g == 0) ? term : tot[i] + term;
                 });
             });
             const bool full = tok0 + 16 * s + 16 <= end;
@@ -452,6 +492,9 @@ void split_mfma_kernel(SplitArgs a)
             const float sv0 = t.sv[0][g] * vdown, sv1 = t.sv[1][g] * vdown;
             half8_t pa, pl;
             static_for<8>([&](auto eI) {
+                // one product x, consumed by both conversions, so the quad
+                // broadcast folds into v_mul_f32_dpp
+#pragma clang fp contract(off)
                 constexpr int e = decltype(eI)::value;
                 constexpr int js = kSlot[e], s = js / 4, i = js % 4;
                 const float x = p[s][i] * quad_bcast<i>(s == 0 ? sv0 : sv1);
@@ -479,9 +522,8 @@ void split_mfma_kernel(SplitArgs a)
     // one LDS stage per wave: the next tile's copies are issued right after
     // the current tile has been read into registers, and stream in while it
     // is computed (the compute phase touches no LDS)
-    int it = wave;
-    if (it < ntiles) dma_tile(it);
-    for (; it < ntiles; it += kWaves) {
+    if (wave >= ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // its tile is unused
+    for (int it = wave; it < ntiles; it += kWaves) {
         TileLoads<D, P> t;
         read_stage(t);
         if (it + kWaves < ntiles) {
@@ -542,9 +584,8 @@ hipError_t launch(const SplitArgs& a, hipStream_t stream)
     const int G = a.Hq / a.H;
     const size_t q_bytes = 16 * D * sizeof(float);
     const size_t merge_bytes = (size_t)kWaves * P * G * (D * sizeof(float) + sizeof(float2));
-    const size_t stage_bytes = (size_t)kWaves * Stage<D, P>::BYTES;
-    size_t lds = q_bytes > merge_bytes ? q_bytes : merge_bytes;
-    if (stage_bytes > lds) lds = stage_bytes;
+    const size_t stage_bytes = (size_t)kWaves * Stage<D, P>::BYTES + q_bytes;  // stages, then q
+    const size_t lds = stage_bytes > merge_bytes ? stage_bytes : merge_bytes;
     dim3 grid(a.num_splits, a.H / P, a.B), block(256);
     split_mfma_kernel<D, P, ROT><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();

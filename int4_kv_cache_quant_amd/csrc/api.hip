@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
 constexpr int kMaxChunk = 2048;
-constexpr int kTargetGroups = 512;  // split workgroups aimed for (2 per CU)
+constexpr int kTargetWaves = 2048;  // split waves aimed for (2 per SIMD)
 constexpr int kMaxSplits = 16384;
 
 bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
@@ -67,9 +67,15 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     int chunk = chunk_ov;
     if (chunk == 0) {
         long long units = (long long)c->batch * c->num_kv_heads;
-        if (variant == OTQ_VARIANT_MFMA) units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
-        long long want = ((long long)max_len * units + kTargetGroups - 1) / kTargetGroups;
-        want = (want + kChunkAlign - 1) / kChunkAlign * kChunkAlign;
+        int waves = 4, align = kChunkAlign;
+        if (variant == OTQ_VARIANT_MFMA) {
+            units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
+            waves = otq::split_mfma_block_waves(D);
+            align = waves * OTQ_TILE;  // one tile per wave and round
+        }
+        const long long groups = kTargetWaves / waves;
+        long long want = ((long long)max_len * units + groups - 1) / groups;
+        want = (want + align - 1) / align * align;
         if (want < kChunkAlign) want = kChunkAlign;
         if (want > kMaxChunk) want = kMaxChunk;
         chunk = (int)want;
@@ -77,7 +83,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         return OTQ_EINVAL;
     }
     const long long S = ((long long)max_len + chunk - 1) / chunk;
-    if (S > kMaxSplits) return OTQ_EINVAL;  // the combine keeps one weight per split in LDS
+    if (S > kMaxSplits) return OTQ_EINVAL;  // bounds the partials' workspace
     const unsigned __int128 rows = (unsigned __int128)c->batch * Hq * S;
     const unsigned __int128 o_bytes = rows * D * sizeof(float);
     const unsigned __int128 o_aligned = (o_bytes + 255) / 256 * 256;

@@ -40,6 +40,8 @@ bool split_vector_supports(int D, int G);
 bool split_mfma_supports(int D, int G);
 // KV heads one MFMA-variant workgroup serves (its grid has H / that blocks in y).
 int split_mfma_heads_per_wave(int D, int G, int H);
+// Waves per workgroup of the MFMA split kernel.
+int split_mfma_block_waves(int D);
 
 hipError_t launch_lse_combine(const float* part_o, const float2* part_ml, const int32_t* lens,
                               int max_len, int chunk, int num_splits, int B, int Hq, int D,

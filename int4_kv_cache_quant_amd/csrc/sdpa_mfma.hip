@@ -64,7 +64,9 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
-constexpr int kWaves = 4;
+// Headroom (base-2 exponent) the softmax reference keeps above the largest
+// score seen when it has to move.
+constexpr float kHeadroom = 2.0f;
 
 // MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
 // word, scaled by 2^(kShift[e] - 24): registers are (0,4), (1,5), (2,6),
@@ -100,20 +102,66 @@ __device__ __forceinline__ float quad_bcast(float v)
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, true));
 }
 
-// Cross-row reductions without LDS: v_permlane16_swap pairs rows (0,1) and
-// (2,3), v_permlane32_swap pairs the two halves; each lane receives its own
-// value and its partner's in the two results.
+// Cross-row exchanges without LDS: v_permlane16_swap pairs rows (0,1) and
+// (2,3) of the wave, v_permlane32_swap its two halves; applied to two copies
+// of a value, each lane ends up with its own value and its partner's, one in
+// each register.  Written as inline asm (a register move, no memory access):
+// the compiler builtin's two results are treated as equal when both inputs
+// are one value, which would drop the partner's.  The s_nop covers the wait
+// states between a VALU write and the swap reading it.
+__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows32(unsigned& a, unsigned& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+template <bool XOR16>
+__device__ __forceinline__ void pair_values(float v, float& x, float& y)
+{
+    unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+    if constexpr (XOR16) swap_rows16(a, b);
+    else swap_rows32(a, b);
+    x = __builtin_bit_cast(float, a);
+    y = __builtin_bit_cast(float, b);
+}
 __device__ __forceinline__ float max_xor16(float v)
 {
-    const auto r = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, v),
-                                                    __builtin_bit_cast(unsigned, v), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    float x, y;
+    pair_values<true>(v, x, y);
+    return fmaxf(x, y);
 }
 __device__ __forceinline__ float max_xor32(float v)
 {
-    const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
-                                                    __builtin_bit_cast(unsigned, v), false, false);
-    return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
+    float x, y;
+    pair_values<false>(v, x, y);
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float sum_xor16(float v)
+{
+    float x, y;
+    pair_values<true>(v, x, y);
+    return x + y;
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    float x, y;
+    pair_values<false>(v, x, y);
+    return x + y;
+}
+
+// Butterfly across lane bit 4 (XOR16) or bit 5 (XOR32 = false): the lane with
+// that bit clear gets lo + hi, its partner lo - hi.  first_lo says whether the
+// swap's first register holds the value of the lane with the bit clear (told
+// by swapping the lane's own row index once).
+template <bool XOR16>
+__device__ __forceinline__ float butterfly_lanes(float v, bool first_lo, bool upper)
+{
+    float x, y;
+    pair_values<XOR16>(v, x, y);
+    const float lo = first_lo ? x : y, hi = first_lo ? y : x;
+    return upper ? lo - hi : lo + hi;
 }
 
 // Value of lane 4 r + I of the lane's own row (r = lane / 16), by DPP row
@@ -130,22 +178,43 @@ __device__ __forceinline__ float row_quad_gather(float v, int r)
 // unconstrained (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4],
 // lgkmcnt [11:8]).
 constexpr int kWaitLgkm0 = 0xC07F;
-// s_waitcnt vmcnt(0) with the other counters unconstrained.
-constexpr int kWaitVm0 = 0x0F70;
+// s_waitcnt vmcnt(N) with the other counters unconstrained.
+constexpr int wait_vm(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitVm0 = wait_vm(0);
+
+// Buffer resource (4 SGPRs): base, no stride, size in bytes, 32-bit data
+// format; reads past the size return 0.
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ v4i_t make_rsrc(const void* base, uint32_t bytes)
+{
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return v4i_t{(int)(uint32_t)p, (int)((p >> 32) & 0xFFFF), (int)bytes, 0x00020000};
+}
 
 // Direct buffer -> LDS copy of 16 bytes per lane: lane l reads the resource
-// at voffset + soffset and its bytes land at lds_base + 16 l (lds_base and
-// soffset wave-uniform).  Reads past the resource's record count return 0.
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, int voffset, int soffset,
-                                      void* lds_base)
+// at voffset + soffset and its bytes land at LDS address lds_addr + 16 l
+// (every operand but voffset wave-uniform).  Issued as inline asm (M0, the
+// LDS base, saved and restored around it) so that the compiler does not
+// follow it with a wait for every copy in flight before each later LDS read;
+// the kernel waits on the vector-memory counter itself, one tile at a time,
+// which lets a second tile stream in while the first is consumed.
+typedef __attribute__((address_space(3))) char lds_char_t;
+__device__ __forceinline__ uint32_t lds_address(void* p)
 {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void_t*)lds_base, 16, voffset, soffset, 0, 0);
+    return (uint32_t)(uintptr_t)(lds_char_t*)p;
 }
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes)
+__device__ __forceinline__ void dma16(const v4i_t& rsrc, int voffset, int soffset, uint32_t lds_addr)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                             0x00020000);
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %4\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_addr)
+        : "memory");
 }
 
 // One tile of the P KV heads, staged in LDS:
@@ -165,6 +234,8 @@ struct Stage {
     static constexpr int voff(int j) { return (P + j) * KB; }
     static constexpr int KSOFF = 2 * P * KB;        // K scales [head][32 tokens][D/32]
     static constexpr int VSOFF = KSOFF + SPAD;      // V scales, same layout
+    // copy instructions per tile (one per 1 KB)
+    static constexpr int COPIES = 2 * P * (D / 64) + 2 * (SPAD / 1024);
 };
 
 template <int D>
@@ -220,12 +291,17 @@ struct TileLoads {
 template <int D>
 constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 
-template <int D, int P, bool ROT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
+// LDS stages per wave: two where the copies a block keeps in flight stay
+// within 80 KB, else one (measured: deeper queues per CU slow the stream).
+template <int D, int P, int W>
+constexpr int kStages = 2 * W * Stage<D, P>::BYTES <= 80 * 1024 ? 2 : 1;
+
+template <int D, int P, bool ROT, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
 void split_mfma_kernel(SplitArgs a)
 {
     constexpr int NG = D / kGroup, NA = D / 64, NCB = D / 16;
-    extern __shared__ float lds[];  // q: [16][D]; then per-wave tile stages; then the merge
+    extern __shared__ float lds[];  // per-wave tile stages; then the merge
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
@@ -238,15 +314,39 @@ void split_mfma_kernel(SplitArgs a)
     const int jl = col_valid ? n16 / G : P - 1;  // KV head of this lane's column
 
     using St = Stage<D, P>;
+    constexpr int NST = kStages<D, P, W>;
     const size_t head0 = (size_t)b * a.H + hk0;
-    char* stage = reinterpret_cast<char*>(lds) + wave * St::BYTES;
+    // the wave's LDS stages: stage s of wave w at (s W + w) * BYTES
+    auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (st * W + wave) * St::BYTES; };
+
+    // sequence length first, as a scalar load: nothing has been written yet
+    const int len = min(max(a.lens[b], 0), a.max_len);
+
+    // ---- q straight into registers, before any tile copy is queued: lane
+    //      (n16, r) needs, per scale group g, channels 32 g + 8 r + 0..7 of
+    //      query head n16 (one 16-byte load), and the same signs when rotated;
+    //      lanes of unused columns load head 0 of the block and drop it
+    uint4 qraw[NG];
+    float4 sgn[ROT ? NG : 1][2];
+    {
+        const uint16_t* qsrc =
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G + (col_valid ? n16 : 0)) * D;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            qraw[g] = *reinterpret_cast<const uint4*>(qsrc + 32 * g + 8 * r);
+            if constexpr (ROT) {
+                sgn[g][0] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r);
+                sgn[g][1] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r + 4);
+            }
+        }
+    }
 
     // Buffer resources of the block's P heads (K codes, V tiles, K and V
     // scales); each spans exactly those heads, so no copy can leave them.
-    const __amdgpu_buffer_rsrc_t rs_k = make_rsrc(a.kc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
-    const __amdgpu_buffer_rsrc_t rs_v = make_rsrc(a.vc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
-    const __amdgpu_buffer_rsrc_t rs_ks = make_rsrc(a.ks + head0 * a.cap * NG, P * a.cap * NG * 4);
-    const __amdgpu_buffer_rsrc_t rs_vs = make_rsrc(a.vs + head0 * a.cap * NG, P * a.cap * NG * 4);
+    const v4i_t rs_k = make_rsrc(a.kc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
+    const v4i_t rs_v = make_rsrc(a.vc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
+    const v4i_t rs_ks = make_rsrc(a.ks + head0 * a.cap * NG, P * a.cap * NG * 4);
+    const v4i_t rs_vs = make_rsrc(a.vs + head0 * a.cap * NG, P * a.cap * NG * 4);
     // per-lane byte offsets of each copy instruction (tile-independent; the
     // tile enters as the scalar offset tok0 * D/2, or tok0 * D/8 for scales)
     int vo_k[P][D / 64], vo_v[P][D / 64], vo_s;
@@ -264,30 +364,31 @@ void split_mfma_kernel(SplitArgs a)
         vo_s = (o / (4 * D)) * a.cap * NG * 4 + o % (4 * D);
     }
 
-    // issue the direct-to-LDS copies of one tile (no registers held)
-    auto dma_tile = [&](int it) {
+    // issue the St::COPIES direct-to-LDS copies of tile it into stage st
+    // (no registers held)
+    auto dma_tile = [&](int it, int st) {
         const int tok0 = start + it * kTile;
         const int so_code = tok0 * (D / 2), so_scale = tok0 * NG * 4;
+        const uint32_t base = lds_address(stage_of(st));
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
-            for (int i = 0; i < D / 64; ++i) dma16(rs_k, vo_k[j][i], so_code, stage + St::koff(j) + 1024 * i);
+            for (int i = 0; i < D / 64; ++i) dma16(rs_k, vo_k[j][i], so_code, base + St::koff(j) + 1024 * i);
 #pragma unroll
-            for (int i = 0; i < D / 64; ++i) dma16(rs_v, vo_v[j][i], so_code, stage + St::voff(j) + 1024 * i);
+            for (int i = 0; i < D / 64; ++i) dma16(rs_v, vo_v[j][i], so_code, base + St::voff(j) + 1024 * i);
         }
 #pragma unroll
         for (int i = 0; i < St::SPAD / 1024; ++i) {
-            dma16(rs_ks, vo_s + 1024 * i, so_scale, stage + St::KSOFF + 1024 * i);
-            dma16(rs_vs, vo_s + 1024 * i, so_scale, stage + St::VSOFF + 1024 * i);
+            dma16(rs_ks, vo_s + 1024 * i, so_scale, base + St::KSOFF + 1024 * i);
+            dma16(rs_vs, vo_s + 1024 * i, so_scale, base + St::VSOFF + 1024 * i);
         }
     };
 
-    // The first tile of every wave streams in before lens[b] is even known,
-    // if it lies inside the cache (capacity is a multiple of 32, so a tile
-    // starting below it is whole); tokens past lens[b] are masked later, or
-    // the block leaves.
-    if (start + wave * kTile < a.cap) dma_tile(wave);
-    const int len = min(max(a.lens[b], 0), a.max_len);
+    // The first tile of every wave streams in without waiting for lens[b] to
+    // arrive, if it lies inside the cache (capacity is a multiple of 32, so a
+    // tile starting below it is whole); tokens past lens[b] are masked later,
+    // or the block leaves.
+    if (start + wave * kTile < a.cap) dma_tile(wave, 0);
     if (start >= len) {  // block-uniform: no partial for an empty chunk
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy may land after the block is gone
         return;
@@ -295,44 +396,74 @@ void split_mfma_kernel(SplitArgs a)
     const int end = min(start + a.chunk, len);
     const int ntiles = (end - start + kTile - 1) / kTile;
 
-    // ---- query prologue: fp32 in LDS (past the tile stages), rotated like K
-    //      when the cache is
-    float* q_lds = reinterpret_cast<float*>(reinterpret_cast<char*>(lds) + kWaves * St::BYTES);
-    const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G) * D;
-    for (int i = tid; i < 16 * D; i += 256) {
-        const int h = i / D, c = i % D;
-        float x = 0.0f;
-        if (h < PG) {
-            x = widen(qsrc[h * D + c], a.dtype);
-            if (ROT) x *= a.signs[c];
+    // ---- q prologue, registers only: widen, and rotate like K when the
+    //      cache is (channel c = 32 g + 8 r + e: the butterflies over bits
+    //      0-2 and 5.. stay in the lane, bits 3 and 4 pair lanes 16 and 32
+    //      apart; the stages of a Walsh-Hadamard transform commute)
+    float qx[NG][8];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        const uint32_t w4[4] = {qraw[g].x, qraw[g].y, qraw[g].z, qraw[g].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint16_t h16 = (uint16_t)(w4[e / 2] >> (16 * (e % 2)));
+            qx[g][e] = col_valid ? widen(h16, a.dtype) : 0.0f;
         }
-        q_lds[i] = x;
     }
-    __syncthreads();
-    if (ROT) {
-        for (int h = 1; h < D; h <<= 1) {
-            for (int i = tid; i < 16 * D / 2; i += 256) {
-                const int hh = i / (D / 2), kk = i % (D / 2);
-                const int j = hh * D + (kk / h) * 2 * h + (kk % h);
-                const float lo = q_lds[j], hi = q_lds[j + h];
-                q_lds[j] = lo + hi;
-                q_lds[j + h] = lo - hi;
-            }
-            __syncthreads();
+    if constexpr (ROT) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float sg[8] = {sgn[g][0].x, sgn[g][0].y, sgn[g][0].z, sgn[g][0].w,
+                                 sgn[g][1].x, sgn[g][1].y, sgn[g][1].z, sgn[g][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[g][e] *= sg[e];
+#pragma unroll
+            for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if ((e & h) == 0) {
+                        const float lo = qx[g][e], hi = qx[g][e + h];
+                        qx[g][e] = lo + hi;
+                        qx[g][e + h] = lo - hi;
+                    }
         }
+        unsigned ra = (unsigned)r, rb = ra;
+        swap_rows16(ra, rb);
+        const bool lo16 = (ra & 1u) == 0;
+        ra = (unsigned)r; rb = ra;
+        swap_rows32(ra, rb);
+        const bool lo32 = (ra & 2u) == 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qx[g][e] = butterfly_lanes<true>(qx[g][e], lo16, (r & 1) != 0);
+                qx[g][e] = butterfly_lanes<false>(qx[g][e], lo32, (r & 2) != 0);
+            }
+#pragma unroll
+        for (int h = 1; h < NG; h <<= 1)
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+                if ((g & h) == 0)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const float lo = qx[g][e], hi = qx[g + h][e];
+                        qx[g][e] = lo + hi;
+                        qx[g + h][e] = lo - hi;
+                    }
     }
     // B operands of the score MFMAs, one per KV head: column n16 holds q of
     // query head n16 in the set of head jl and zeros in the others; k slot e
     // = channel 32 g + 8 r + kSlot[e].
     half8_t qb[P][NG], qb_lo[ROT ? P : 1][ROT ? NG : 1];
-    float qinit[NG];
+    floatx4_t qinit4[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         half8_t hv, lv;
         float t = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float x = q_lds[n16 * D + 32 * g + 8 * r + kSlot[e]];
+            const float x = qx[g][kSlot[e]];
             const _Float16 h16 = (_Float16)x;
             const _Float16 l16 = (_Float16)(x - (float)h16);
             // cancel the code's 2^kShift (a power of two); the offset sum
@@ -355,18 +486,12 @@ void split_mfma_kernel(SplitArgs a)
             }
         }
         // the score accumulator starts at -8 * 2^-24 * sum(q over the group)
-        t += shfl_xor(t, 16);
-        t += shfl_xor(t, 32);
-        qinit[g] = -8.0f * 0x1p-24f * t;
+        const float qi = -8.0f * 0x1p-24f * sum_xor32(sum_xor16(t));
+        qinit4[g] = floatx4_t{qi, qi, qi, qi};
     }
-    floatx4_t qinit4[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) qinit4[g] = floatx4_t{qinit[g], qinit[g], qinit[g], qinit[g]};
     const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
-    __syncthreads();  // q_lds is reused by the final merge
 
-
-    float m_run = kNegInf;  // running max of column n16 (log2 domain)
+    float m_run = kNegInf;  // softmax reference of column n16 (>= its running max)
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
     // acc[j]: 2^-24 * sum p s_v (c + 8) V rows of KV head j; corr: 2^-24 * 8 *
     // sum p s_v per scale group (shared by the heads: it depends on p only)
@@ -383,7 +508,7 @@ void split_mfma_kernel(SplitArgs a)
     for (int e = 0; e < 8; ++e) bcorr[e] = (_Float16)(kShift[e] ? 0x1p-17f : 0x1p-21f);
 
     // this lane's operands of the staged tile, into registers
-    auto read_stage = [&](TileLoads<D, P>& t) {
+    auto read_stage = [&](TileLoads<D, P>& t, const char* stage) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
@@ -417,8 +542,8 @@ void split_mfma_kernel(SplitArgs a)
 
     auto compute_tile = [&](const TileLoads<D, P>& t, int it) {
         const int tok0 = start + it * kTile;
-        // ---- scores
-        float S[2][4];
+        // ---- scores, as T = S / qmul (qmul > 0 is applied inside exp2)
+        float T[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -437,28 +562,32 @@ void split_mfma_kernel(SplitArgs a)
                     tot[i] = (g == 0) ? term : tot[i] + term;
                 });
             });
-            const bool full = tok0 + 16 * s + 16 <= end;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int tk = tok0 + 16 * s + 4 * r + i;
-                S[s][i] = (full || tk < end) ? tot[i] * qmul : kNegInf;
-            }
+            for (int i = 0; i < 4; ++i) T[s][i] = tot[i];
+        }
+        if (tok0 + kTile > end) {  // wave-uniform: the chunk's last, partial tile
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (tok0 + 16 * s + 4 * r + i >= end) T[s][i] = kNegInf;
         }
 
-        // ---- online softmax for column n16 over the tile's 32 tokens
+        // ---- online softmax for column n16 over the tile's 32 tokens (base-2
+        //      exponents).  The reference m_run only moves when a score passes
+        //      it, and then to kHeadroom above that score, so that most tiles
+        //      keep it and skip the rescale; every p stays <= 1.
         float mt = kNegInf;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, S[s][i]);
-        mt = max_xor32(max_xor16(mt));
-        const float m_new = fmaxf(m_run, mt);  // finite: the tile has a valid token
-        // alpha is computed by every lane (1 where the max did not move, 0 on
-        // the first tile); the rescale runs only when some column's max
-        // moved, decided for the whole wave so that the cross-lane moves see
-        // every lane.
-        const float alpha = exp2_approx(m_run - m_new);
-        if (__any(m_new != m_run)) {
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, T[s][i]);
+        mt = max_xor32(max_xor16(mt)) * qmul;  // finite: the tile has a valid token
+        // decided for the whole wave, so that the cross-lane moves of the
+        // rescale see every lane
+        if (__any(mt > m_run)) {
+            const float m_new = (mt > m_run) ? mt + kHeadroom : m_run;
+            const float alpha = exp2_approx(m_run - m_new);  // 0 on the first tile, 1 if unmoved
             l_lane *= alpha;
             static_for<4>([&](auto iI) {
                 constexpr int i = decltype(iI)::value;
@@ -470,14 +599,14 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
                 for (int g = 0; g < NG; ++g) corr[g][i] *= ai;
             });
+            m_run = m_new;
         }
-        m_run = m_new;
         float p[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[s][i] = exp2_approx(S[s][i] - m_run);
+                p[s][i] = exp2_approx(__builtin_fmaf(T[s][i], qmul, -m_run));
                 l_lane += p[s][i];
             }
 
@@ -500,7 +629,7 @@ void split_mfma_kernel(SplitArgs a)
                 const float x = p[s][i] * quad_bcast<i>(s == 0 ? sv0 : sv1);
                 const _Float16 hi = (_Float16)x;
                 pa[e] = hi;
-                pl[e] = (_Float16)(x - (float)hi);
+                pl[e] = (_Float16)__builtin_fmaf(x, 1.0f, -(float)hi);  // x - hi is exact
             });
             corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bcorr, corr[g], 0, 0, 0);
             corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bcorr, corr[g], 0, 0, 0);
@@ -519,29 +648,38 @@ void split_mfma_kernel(SplitArgs a)
         });
     };
 
-    // one LDS stage per wave: the next tile's copies are issued right after
-    // the current tile has been read into registers, and stream in while it
-    // is computed (the compute phase touches no LDS)
+    // NST LDS stages per wave, used in turn: tile it + (NST - 1) W streams
+    // in while tile it is computed.  Before reading a stage the wave waits
+    // until at most the copies issued after that stage's (the other stages'
+    // tiles still to come) are in flight; the vector-memory counter retires
+    // in issue order.
+    if (NST > 1 && wave + W < ntiles) dma_tile(wave + W, 1);
     if (wave >= ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // its tile is unused
-    for (int it = wave; it < ntiles; it += kWaves) {
+    int st = 0;
+    for (int it = wave; it < ntiles; it += W) {
+        if (NST > 1 && it + W < ntiles) __builtin_amdgcn_s_waitcnt(wait_vm(St::COPIES));
+        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        asm volatile("" ::: "memory");  // the stage's reads stay after the wait
         TileLoads<D, P> t;
-        read_stage(t);
-        if (it + kWaves < ntiles) {
+        read_stage(t, stage_of(st));
+        if (it + NST * W < ntiles) {
             // the copies overwrite the stage just read: let the reads finish
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            dma_tile(it + kWaves);
+            dma_tile(it + NST * W, st);
         }
         compute_tile(t, it);
+        st = (st + 1 == NST) ? 0 : st + 1;
     }
     __syncthreads();  // every wave is done with its stage before the merge reuses LDS
 
-    // ---- merge the 4 rows (l only: m and O are already wave-wide), then waves
-    float L = l_lane;
-    L += shfl_xor(L, 16);
-    L += shfl_xor(L, 32);
-    float* merge_o = lds;                                                  // [4][PG][D]
-    float2* merge_ml = reinterpret_cast<float2*>(lds + kWaves * PG * D);  // [4][PG]
-    if (lane < PG) merge_ml[wave * PG + lane] = make_float2(m_run, L);
+    // ---- merge: l over the 4 rows of each column (m and O are already
+    //      wave-wide), then the W waves, through LDS rows padded by 4 floats
+    //      so that the 4 rows of a wave's stores fall in distinct banks
+    constexpr int RS = D + 4;
+    const float L = sum_xor32(sum_xor16(l_lane));
+    float* merge_o = lds;                                            // [W][16][RS]
+    float2* merge_ml = reinterpret_cast<float2*>(lds + W * 16 * RS);  // [W][16]
+    if (lane < 16) merge_ml[wave * 16 + lane] = make_float2(m_run, L);
     // rows 4 r .. 4 r + 3 of O lie in one KV head (G >= 4): keep that head's set
     const int jr = min(4 * r / G, P - 1);
 #pragma unroll
@@ -553,49 +691,66 @@ void split_mfma_kernel(SplitArgs a)
                 float v = acc[0][cb][i];
 #pragma unroll
                 for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
-                merge_o[(wave * PG + h) * D + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
+                merge_o[(wave * 16 + h) * RS + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
             }
         }
     }
     __syncthreads();
-    for (int i = tid; i < PG * D; i += 256) {
-        const int h = i / D, c = i % D;
+    // one thread per (head, 4 channels)
+    for (int i = tid; i < PG * (D / 4); i += 64 * W) {
+        const int h = i / (D / 4), c = 4 * (i % (D / 4));
+        float2 ml[W];
         float Mb = kNegInf;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) Mb = fmaxf(Mb, merge_ml[w * PG + h].x);
-        float o = 0.0f, Ls = 0.0f;
+        for (int w = 0; w < W; ++w) {
+            ml[w] = merge_ml[w * 16 + h];
+            Mb = fmaxf(Mb, ml[w].x);
+        }
+        float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        float Ls = 0.0f;
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const float mw = merge_ml[w * PG + h].x;
-            const float f = (mw == kNegInf) ? 0.0f : exp2_approx(mw - Mb);
-            o += f * merge_o[(w * PG + h) * D + c];
-            Ls += f * merge_ml[w * PG + h].y;
+        for (int w = 0; w < W; ++w) {
+            const float f = (ml[w].x == kNegInf) ? 0.0f : exp2_approx(ml[w].x - Mb);
+            const float4 x = *reinterpret_cast<const float4*>(merge_o + (w * 16 + h) * RS + c);
+            o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
+            Ls += f * ml[w].y;
         }
         const size_t prow = ((size_t)b * a.Hq + hk0 * G + h) * a.num_splits + split;
-        a.part_o[prow * D + c] = o;
+        *reinterpret_cast<float4*>(a.part_o + prow * D + c) = o;
         if (c == 0) a.part_ml[prow] = make_float2(Mb, Ls);
     }
 }
 
 
+// Waves per block: 8 (two per SIMD, so one wave's VALU work runs under the
+// other's matrix products and copies) where the registers allow two waves
+// per SIMD, else 4.
+template <int D>
+constexpr int kBlockWaves = kWavesPerEU<D> >= 2 ? 8 : 4;
+
 template <int D, int P, bool ROT>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)
 {
-    const int G = a.Hq / a.H;
-    const size_t q_bytes = 16 * D * sizeof(float);
-    const size_t merge_bytes = (size_t)kWaves * P * G * (D * sizeof(float) + sizeof(float2));
-    const size_t stage_bytes = (size_t)kWaves * Stage<D, P>::BYTES + q_bytes;  // stages, then q
+    constexpr int W = kBlockWaves<D>;
+    const size_t merge_bytes = (size_t)W * 16 * ((D + 4) * sizeof(float) + sizeof(float2));
+    const size_t stage_bytes = (size_t)kStages<D, P, W> * W * Stage<D, P>::BYTES;
     const size_t lds = stage_bytes > merge_bytes ? stage_bytes : merge_bytes;
-    dim3 grid(a.num_splits, a.H / P, a.B), block(256);
-    split_mfma_kernel<D, P, ROT><<<grid, block, lds, stream>>>(a);
+    dim3 grid(a.num_splits, a.H / P, a.B), block(64 * W);
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&split_mfma_kernel<D, P, ROT, W>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    split_mfma_kernel<D, P, ROT, W><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch(const SplitArgs& a, hipStream_t stream)
 {
-    const int P = split_mfma_heads_per_wave(a.D, a.Hq / a.H, a.H);
-    if (P == 2) return a.signs ? launch<D, 2, true>(a, stream) : launch<D, 2, false>(a, stream);
+    if constexpr (D != 256) {  // head_dim 256 serves one KV head per wave
+        if (split_mfma_heads_per_wave(a.D, a.Hq / a.H, a.H) == 2)
+            return a.signs ? launch<D, 2, true>(a, stream) : launch<D, 2, false>(a, stream);
+    }
     return a.signs ? launch<D, 1, true>(a, stream) : launch<D, 1, false>(a, stream);
 }
 
@@ -606,6 +761,11 @@ hipError_t dispatch(const SplitArgs& a, hipStream_t stream)
 int split_mfma_heads_per_wave(int D, int G, int H)
 {
     return (D != 256 && G <= 8 && H % 2 == 0) ? 2 : 1;
+}
+
+int split_mfma_block_waves(int D)
+{
+    return D == 256 ? kBlockWaves<256> : D == 64 ? kBlockWaves<64> : kBlockWaves<128>;
 }
 
 bool split_mfma_supports(int D, int G)

@@ -22,13 +22,22 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2):
+def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spikes=(), beta=0.0):
     g = torch.Generator().manual_seed(seed)
     x = torch.randn((2, B, Hkv, cap, D), generator=g) * sigma
     oc = torch.randperm(D, generator=g)[:n_out]
     x[..., oc] *= 10
+    q = torch.randn((B, Hq, D), generator=g)
+    # score spikes: K of the given tokens = beta * unit vector of the first
+    # query head of the group, so that head's score there exceeds every other
+    # score by ~beta |q| scale log2(e) in the base-2 exponent
+    G = Hq // Hkv
+    for t in spikes:
+        for j in range(Hkv):
+            u = q[:, j * G] / q[:, j * G].norm(dim=-1, keepdim=True)
+            x[0, :, j, t] = beta * u
     x = x.to(dtype)
-    q = torch.randn((B, Hq, D), generator=g).to(dtype)
+    q = q.to(dtype)
     signs = None
     if rotate:
         signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
@@ -36,8 +45,8 @@ def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2):
 
 
 def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
-         rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None):
-    k, v, q, signs = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate)
+         rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0):
+    k, v, q, signs = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate, spikes=spikes, beta=beta)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     name = "fp16" if dtype == torch.float16 else "bf16"
     cache = build_cache(k.to(DEV), v.to(DEV), cap, signs=None if signs is None else signs.to(DEV),
@@ -86,6 +95,24 @@ def test_sdpa_small_parity_mfma(D, G, rotate):
                        chunk=128, rotate=rotate)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("variant,G,D", [(VEC, 1, 128), (VEC, 2, 64), (MF, 4, 128), (MF, 8, 128),
+                                         (MF, 16, 64), (MF, 8, 256)])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_sdpa_score_spikes(variant, G, D, rotate):
+    """A few tokens whose score exceeds the rest by ~140 in the base-2
+    exponent, placed in every row position of the score tiles (tokens 4 r + i
+    of both 16-token halves): the running maximum must be the column's true
+    maximum, or exp2 of the difference overflows fp32."""
+    Hkv = 2
+    spikes = [6, 37, 90, 255, 301]
+    got, ref, _ = _run(2, G * Hkv, Hkv, D, 320, [320, 260], seed=11 * G + D + rotate, variant=variant,
+                       chunk=128, rotate=rotate, spikes=spikes, beta=100.0)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
     assert ma <= MAX_ABS and rel <= REL_L2
 
 

@@ -61,6 +61,57 @@ def traffic_from_profile(variant, workload_name):
     return rec.get("hbm_bytes_per_launch")
 
 
+def counter_per_dispatch(run_dir, counter):
+    """{dispatch id: (kernel name, summed value)} from a rocprofv3 CSV counter run."""
+    import csv
+    import glob
+    out = {}
+    for path in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] != counter:
+                    continue
+                name, val = out.get(r["Dispatch_Id"], (r["Kernel_Name"], 0.0))
+                out[r["Dispatch_Id"]] = (name, val + float(r["Counter_Value"]))
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, workload, calib_mib, commands):
+    """Calibrated HBM bytes per split launch from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) of
+    `bench.py --no-graph --copy-calibration-mib N`: each counter is scaled by
+    what it reads for the plain elementwise copy of N MiB (N MiB read and N
+    MiB written).  Writes profiles/traffic_<kernel>_<workload>.json."""
+    import numpy as np
+    from int4_kv_cache_quant_amd import synth
+    w = synth.WORKLOADS[workload]
+    known_kib = calib_mib * 1024.0
+    rec = {"workload": w.name, "calibration_copy_mib": calib_mib, "commands": commands}
+    for counter, run_dir, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
+        per = counter_per_dispatch(run_dir, counter)
+        calib = sorted((v for n, v in per.values() if "elementwise" in n), reverse=True)[:5]
+        split = [v for n, v in per.values() if "split_mfma_kernel" in n]
+        if len(calib) < 5 or not split:
+            raise SystemExit(f"{run_dir}: no calibration copy or split dispatches for {counter}")
+        factor = known_kib / float(np.mean(calib))
+        rec[f"{key}_kib_per_launch_raw"] = float(np.mean(split))
+        rec[f"{key}_calibration_kib_raw"] = float(np.mean(calib))
+        rec[f"{key}_factor"] = factor
+        rec[f"{key}_bytes_per_launch"] = float(np.mean(split)) * factor * 1024.0
+        rec[f"{key}_launches"] = len(split)
+    unit = w.Hkv * 2 * (w.D // 2 + 4 * (w.D // 32))
+    lens_sum = int(synth.lens(w, 0).astype(np.int64).sum())
+    rec["algorithmic_bytes_per_launch"] = lens_sum * unit + w.B * w.Hq * w.D * 2
+    rec["hbm_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+    rec["kernel"] = "split_mfma"
+    rec["kernel_source_sha"] = source_sha(2)
+    path = os.path.join(PROFILE_DIR, f"traffic_split_mfma_{w.name}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+        f.write("\n")
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -75,7 +126,15 @@ def main():
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
                          "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_RUN_DIR", "WRITE_RUN_DIR"),
+                    help="write the calibrated HBM traffic of the split kernel from two rocprofv3 "
+                         "--pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/, then exit")
+    ap.add_argument("--pmc-commands", default="", help="the profiling commands, recorded with the summary")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
+                        args.copy_calibration_mib or 1024, args.pmc_commands)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -274,7 +333,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32 accumulate, f16 MFMA operands, int4 cache",
+        "dtype": "f16 mfma operands, f32 accumulate (int4 codes, f32 scales)",
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,

@@ -93,6 +93,20 @@ __device__ __forceinline__ half8_t unpack_codes(uint32_t w)
     return out;
 }
 
+// fp16 (x0 - h0, x1 - h1) packed, where (h0, h1) = h2 are x0, x1 rounded to
+// fp16: the differences are exact in fp32 and rounded once (v_fma_mix with
+// an fp16 operand; register-only instructions).
+typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint32_t lo_pair(float x0, float x1, uint32_t h2)
+{
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+        "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        : "=&v"(r)
+        : "v"(x0), "v"(x1), "v"(h2));
+    return r;
+}
+
 // Lane K (0..3) of each quad of lanes, broadcast to the quad (DPP quad_perm).
 template <int K>
 __device__ __forceinline__ float quad_bcast(float v)
@@ -315,6 +329,7 @@ void split_mfma_kernel(SplitArgs a)
 
     using St = Stage<D, P>;
     constexpr int NST = kStages<D, P, W>;
+    static_assert((NST - 1) * St::COPIES <= 63, "vmcnt holds at most 63");
     const size_t head0 = (size_t)b * a.H + hk0;
     // the wave's LDS stages: stage s of wave w at (s W + w) * BYTES
     auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (st * W + wave) * St::BYTES; };
@@ -601,36 +616,37 @@ void split_mfma_kernel(SplitArgs a)
             });
             m_run = m_new;
         }
+        // p of the tile's tokens.  Odd i hold the bit-4 nibbles of the V words
+        // (see below), whose 2^4 is cancelled here: p / 16 comes straight from
+        // the exponent, and l takes 16 (p / 16).
         float p[2][4];
+        const float m_odd = m_run + 4.0f;
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[s][i] = exp2_approx(__builtin_fmaf(T[s][i], qmul, -m_run));
-                l_lane += p[s][i];
+                p[s][i] = exp2_approx(__builtin_fmaf(T[s][i], qmul, -((i & 1) ? m_odd : m_run)));
+                l_lane = (i & 1) ? __builtin_fmaf(p[s][i], 16.0f, l_lane) : l_lane + p[s][i];
             }
 
         // ---- values, one scale group (two 16-channel blocks) at a time:
-        //      A_g = p * s_v[token][g] * 2^-kShift as fp16 hi + lo, B = V_j
-        //      codes.  Token slot j = kSlot[e] is token 4 r + j % 4 of sub-tile
-        //      j / 4; the odd slots are the bit-4 nibbles, so the quad lanes
-        //      holding odd tokens hand out s_v / 16.
-        const float vdown = (slot & 1) ? 0.0625f : 1.0f;
+        //      A_g = p * s_v[token][g] as fp16 hi + lo, B = V_j codes.  k slots
+        //      (2 m, 2 m + 1) are token m of the quad in sub-tiles 0 and 1; DPP
+        //      quad broadcasts hand out the s_v of token m.
         static_for<NG>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
-            const float sv0 = t.sv[0][g] * vdown, sv1 = t.sv[1][g] * vdown;
-            half8_t pa, pl;
-            static_for<8>([&](auto eI) {
-                // one product x, consumed by both conversions, so the quad
+            v4u_t ha, la;
+            static_for<4>([&](auto mI) {
+                // one product per element, consumed by both halves, so the
                 // broadcast folds into v_mul_f32_dpp
 #pragma clang fp contract(off)
-                constexpr int e = decltype(eI)::value;
-                constexpr int js = kSlot[e], s = js / 4, i = js % 4;
-                const float x = p[s][i] * quad_bcast<i>(s == 0 ? sv0 : sv1);
-                const _Float16 hi = (_Float16)x;
-                pa[e] = hi;
-                pl[e] = (_Float16)__builtin_fmaf(x, 1.0f, -(float)hi);  // x - hi is exact
+                constexpr int m = decltype(mI)::value;
+                const float x0 = p[0][m] * quad_bcast<m>(t.sv[0][g]);
+                const float x1 = p[1][m] * quad_bcast<m>(t.sv[1][g]);
+                ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
+                la[m] = lo_pair(x0, x1, ha[m]);
             });
+            const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
             corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bcorr, corr[g], 0, 0, 0);
             corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bcorr, corr[g], 0, 0, 0);
 #pragma unroll
@@ -653,12 +669,19 @@ void split_mfma_kernel(SplitArgs a)
     // until at most the copies issued after that stage's (the other stages'
     // tiles still to come) are in flight; the vector-memory counter retires
     // in issue order.
-    if (NST > 1 && wave + W < ntiles) dma_tile(wave + W, 1);
+#pragma unroll
+    for (int k = 1; k < NST; ++k)
+        if (wave + k * W < ntiles) dma_tile(wave + k * W, k);
     if (wave >= ntiles) __builtin_amdgcn_s_waitcnt(kWaitVm0);  // its tile is unused
     int st = 0;
     for (int it = wave; it < ntiles; it += W) {
-        if (NST > 1 && it + W < ntiles) __builtin_amdgcn_s_waitcnt(wait_vm(St::COPIES));
-        else __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        // tiles it + W .. it + (NST - 1) W, as far as they exist, were issued
+        // after this one and may stay in flight
+        const int n_after = min(NST - 1, (ntiles - 1 - it) / W);
+        static_for<NST>([&](auto kI) {
+            constexpr int k = decltype(kI)::value;
+            if (n_after == k) __builtin_amdgcn_s_waitcnt(wait_vm(k * St::COPIES));
+        });
         asm volatile("" ::: "memory");  // the stage's reads stay after the wait
         TileLoads<D, P> t;
         read_stage(t, stage_of(st));

@@ -251,6 +251,7 @@ def main():
 
     # ---------------------------------------------------------------- per-kernel durations
     def kernel_avg_us(fn, passes=3):
+        """Eager fallback: HIP events around every launch."""
         evs = []
         for _ in range(passes):
             for l in range(L):
@@ -262,9 +263,29 @@ def main():
         torch.cuda.synchronize()
         return float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1000.0
 
-    split_us = kernel_avg_us(split)
-    combine_us = kernel_avg_us(combine)
-    append_us = kernel_avg_us(append)
+    def graph_avg_us(fn):
+        """Average duration of one launch of fn, timed with HIP events over
+        replays of a graph holding one launch per layer (back to back, as in
+        the step; the same stream as the kernels)."""
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for l in range(L):
+                fn(l)
+        for _ in range(2):
+            g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(args.steps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1000.0 / (args.steps * L)
+
+    timer = kernel_avg_us if graph is None else graph_avg_us
+    split_us = timer(split)
+    combine_us = timer(combine)
+    append_us = timer(append)
     torch.cuda.synchronize()
     sdpa_graph_us = None
     if graph is not None:

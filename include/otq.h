@@ -215,8 +215,10 @@ int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_hea
  *   part_ml fp32 [B][Hq][num_splits][2]      at byte offset
  *           round_up(B*Hq*num_splits*D*4, 256)
  * where split s covers tokens [s*chunk, min((s+1)*chunk, lens[b])), m is the
- * split's max score in log2 units (score * log2(e)), l = sum 2^(S*log2e - m)
- * and o = sum 2^(S*log2e - m) V^.  Splits with s*chunk >= lens[b] are not
+ * split's softmax reference in log2 units (score * log2(e)): at least its
+ * largest score, and at most 2 above it, l = sum 2^(S*log2e - m) and
+ * o = sum 2^(S*log2e - m) V^ (any such m gives the same merged result).
+ * Splits with s*chunk >= lens[b] are not
  * written.  otq_sdpa_lse_combine merges the first ceil(lens[b]/chunk)
  * partials of each row into out.  Arguments and errors as for
  * otq_sdpa_int4_decode_planned.

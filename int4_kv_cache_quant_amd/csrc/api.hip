@@ -15,7 +15,7 @@ namespace {
 
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
 constexpr int kMaxChunk = 2048;
-constexpr int kTargetWaves = 2048;  // split waves aimed for (2 per SIMD)
+constexpr int kTargetWaves = 1024;  // split waves aimed for (one per SIMD)
 constexpr int kMaxSplits = 16384;
 
 bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }

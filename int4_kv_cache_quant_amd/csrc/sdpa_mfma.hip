@@ -745,11 +745,12 @@ void split_mfma_kernel(SplitArgs a)
 }
 
 
-// Waves per block: 8 (two per SIMD, so one wave's VALU work runs under the
-// other's matrix products and copies) where the registers allow two waves
-// per SIMD, else 4.
+// Waves per block: 4, one per SIMD, each with two LDS stages (80 KB per
+// block at head_dim 128).  Measured against 8 waves with one stage: equal on
+// one long sequence, faster on many ragged ones, where a second block fits
+// the CU beside the first.
 template <int D>
-constexpr int kBlockWaves = kWavesPerEU<D> >= 2 ? 8 : 4;
+constexpr int kBlockWaves = 4;
 
 template <int D, int P, bool ROT>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)

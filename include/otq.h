@@ -140,8 +140,8 @@ int otq_quantize_append(const void *k, const void *v, int32_t dtype, int32_t n_n
 /* Kernel variants of the split pass. */
 typedef enum otq_variant {
     OTQ_VARIANT_AUTO = 0,
-    OTQ_VARIANT_VECTOR = 1, /* fp32 vector FMA; chosen for G <= 2            */
-    OTQ_VARIANT_MFMA = 2    /* fp16 MFMA 16x16x32 for the GQA contraction, G >= 4 */
+    OTQ_VARIANT_VECTOR = 1, /* fp32 vector FMA, G in {1, 2, 4} (not G = 4 at D = 256) */
+    OTQ_VARIANT_MFMA = 2    /* fp16 MFMA 16x16x32, any G <= 16; the default */
 } otq_variant;
 
 /*

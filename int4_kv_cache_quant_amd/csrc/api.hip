@@ -14,7 +14,7 @@
 namespace {
 
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
-constexpr int kMaxChunk = 2048;
+constexpr int kMaxChunk = 8192;  // measured: larger chunks starve the grid on ragged batches
 constexpr int kTargetWaves = 1024;  // split waves aimed for (one per SIMD)
 constexpr int kMaxSplits = 16384;
 
@@ -52,7 +52,8 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
 
     int variant = variant_ov;
     if (variant == OTQ_VARIANT_AUTO) {
-        variant = (G >= 4 && otq::split_mfma_supports(D, G)) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
+        // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
+        variant = otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
     }
     if (variant == OTQ_VARIANT_VECTOR) {
         if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;

@@ -117,12 +117,31 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
     const int t0 = ((p0 >> 1) + slot) * 2;  // even absolute position
     const size_t head = (size_t)b * H + h;
 
-    int vcode[2][E];
     bool fresh[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int t = t0 + s;
         fresh[s] = t >= p0 && t < p0 + n_new && t >= 0 && t < cap;
+    }
+    if (!fresh[0] && !fresh[1]) return;  // wave-uniform
+
+    // Tokens t0 and t0 + 1 share one V byte per channel.  When only one of
+    // them is new, the other's nibbles are read first, so that the read
+    // overlaps the K/V loads instead of following the quantisation (t0 + 1 <
+    // cap: cap is even).
+    const int tile = t0 / kTile;
+    uint8_t* vt = vc + (head * (cap / kTile) + tile) * (size_t)(16 * D);
+    uint8_t old[E];
+    const bool partial = fresh[0] != fresh[1];
+    if (partial) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) old[e] = vt[v_tile_byte<D>(lane * E + e, t0 % kTile)];
+    }
+
+    int vcode[2][E];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const int t = t0 + s;
 #pragma unroll
         for (int e = 0; e < E; ++e) vcode[s][e] = 0;
         if (!fresh[s]) continue;  // wave-uniform
@@ -154,22 +173,16 @@ __global__ __launch_bounds__(256) void quantize_append_kernel(
         float sv = quantize_lane<D>(x, vcode[s], lane);
         if (lane % (kGroup / E) == 0) vs[row * NG + (lane * E) / kGroup] = sv;
     }
-    if (!fresh[0] && !fresh[1]) return;
-
-    // V nibbles: tokens t0 and t0+1 share one byte per channel.
-    const int tile = t0 / kTile;
-    uint8_t* vt = vc + (head * (cap / kTile) + tile) * (size_t)(16 * D);
+    // V nibbles of the pair
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         const int ch = lane * E + e;
-        uint8_t* p = vt + v_tile_byte<D>(ch, t0 % kTile);
         uint32_t lo = vcode[0][e] & 0xF, hi = vcode[1][e] & 0xF;
-        if (!(fresh[0] && fresh[1])) {
-            const uint8_t old = *p;
-            if (!fresh[0]) lo = old & 0xF;
-            if (!fresh[1]) hi = old >> 4;
+        if (partial) {
+            if (!fresh[0]) lo = old[e] & 0xF;
+            if (!fresh[1]) hi = old[e] >> 4;
         }
-        *p = (uint8_t)(lo | (hi << 4));
+        vt[v_tile_byte<D>(ch, t0 % kTile)] = (uint8_t)(lo | (hi << 4));
     }
 }
 

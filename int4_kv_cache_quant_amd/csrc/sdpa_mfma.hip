@@ -1,5 +1,5 @@
 // sdpa_mfma.hip - split pass of decode attention on the packed int4 cache,
-// MFMA variant for grouped-query attention (G >= 4 query heads per KV head).
+// MFMA variant (any G = query heads per KV head up to 16).
 //
 // With G heads sharing one KV head, scoring a tile of tokens and weighting
 // its values are both genuine matrix products (G x D by D x tokens, then
@@ -49,7 +49,11 @@
 //          are kept
 //  scales  lane k of each quad loads the fp32 scales of token 4 r + k of its
 //          head and DPP quad broadcasts hand them to the quad (every quad
-//          lies inside one head, as G >= 4).
+//          lies inside one head: two heads per wave only when G >= 4).
+// With G < 16 and one KV head per wave, columns G..15 are idle: the matrix
+// cores have room to spare, while the VALU work per token (unpacking, scale
+// products) is the same as for full columns and far below that of
+// per-channel fp32 dot products.
 #include <math.h>
 
 #include "common.hpp"
@@ -703,7 +707,8 @@ void split_mfma_kernel(SplitArgs a)
     float* merge_o = lds;                                            // [W][16][RS]
     float2* merge_ml = reinterpret_cast<float2*>(lds + W * 16 * RS);  // [W][16]
     if (lane < 16) merge_ml[wave * 16 + lane] = make_float2(m_run, L);
-    // rows 4 r .. 4 r + 3 of O lie in one KV head (G >= 4): keep that head's set
+    // rows 4 r .. 4 r + 3 of O lie in one KV head (two heads only if G >= 4):
+    // keep that head's set
     const int jr = min(4 * r / G, P - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -780,11 +785,12 @@ hipError_t dispatch(const SplitArgs& a, hipStream_t stream)
 
 }  // namespace
 
-// KV heads per wave: two (filling 16 MFMA columns at G = 8) when the head
-// count allows it and the registers suffice, else one.
+// KV heads per wave: two (filling 16 MFMA columns at G = 8) when G >= 4
+// (every quad of columns inside one head), the head count allows it and the
+// registers suffice, else one.
 int split_mfma_heads_per_wave(int D, int G, int H)
 {
-    return (D != 256 && G <= 8 && H % 2 == 0) ? 2 : 1;
+    return (D != 256 && G >= 4 && G <= 8 && H % 2 == 0) ? 2 : 1;
 }
 
 int split_mfma_block_waves(int D)
@@ -794,7 +800,7 @@ int split_mfma_block_waves(int D)
 
 bool split_mfma_supports(int D, int G)
 {
-    return (D == 64 || D == 128 || D == 256) && G >= 4 && G <= 16;
+    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16;
 }
 
 hipError_t launch_split_mfma(const SplitArgs& a, hipStream_t stream)

@@ -84,13 +84,13 @@ def test_plan_defaults_and_errors():
     d = _desc(B=1, H=8, D=128, cap=131072)
     p = otq.otq_sdpa_plan(64, d, 131072)
     assert p.variant == otq.OTQ_VARIANT_MFMA
-    assert otq.otq_sdpa_plan(16, d, 131072).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(16, d, 131072).variant == otq.OTQ_VARIANT_MFMA  # G = 2 too
     assert p.chunk % 128 == 0 and p.num_splits == -(-131072 // p.chunk)
     rows = 64 * p.num_splits
     assert p.workspace_bytes == -(-rows * 128 * 4 // 256) * 256 + rows * 8
     assert otq.otq_sdpa_workspace_bytes(64, d, 131072) == p.workspace_bytes
     assert otq.otq_sdpa_plan(64, d, 100, variant=otq.OTQ_VARIANT_VECTOR, check=False)[0] == otq.OTQ_EUNSUPPORTED
-    assert otq.otq_sdpa_plan(8, d, 100, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    assert otq.otq_sdpa_plan(8, d, 100, variant=otq.OTQ_VARIANT_MFMA).variant == otq.OTQ_VARIANT_MFMA  # G = 1
     p = otq.otq_sdpa_plan(8, d, 1000, chunk=256, variant=otq.OTQ_VARIANT_VECTOR, check=False)[1]
     assert (p.chunk, p.num_splits, p.variant) == (256, 4, otq.OTQ_VARIANT_VECTOR)
     rc = lambda *a, **k: otq.otq_sdpa_plan(*a, check=False, **k)[0]

@@ -87,7 +87,7 @@ def test_sdpa_small_parity_vector(D, G):
 
 
 @pytest.mark.parametrize("D", [64, 128, 256])
-@pytest.mark.parametrize("G", [4, 8, 16])
+@pytest.mark.parametrize("G", [1, 2, 4, 8, 16])
 @pytest.mark.parametrize("rotate", [False, True])
 def test_sdpa_small_parity_mfma(D, G, rotate):
     Hkv = 2

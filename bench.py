@@ -7,8 +7,9 @@ context (64 query heads / 8 KV heads, head_dim 128, bf16 inputs), cycling
 over 80 distinct caches (12.5 GiB, far larger than the 256 MB last-level
 cache, so every step streams from HBM).
 
-A step is one pass of the whole hot path over every layer: quantise-append
-the new token into the layer's cache, split pass, LSE combine.  The step is
+A step is one pass of the whole hot path over every layer: the split pass,
+which also quantises the new token into the layer's cache (the block whose
+chunk holds it), then the LSE combine.  The step is
 captured once in a HIP graph and replayed.  Inputs are synthetic and seeded
 (int4_kv_cache_quant_amd.synth); they are resident in HBM before timing.
 
@@ -187,8 +188,8 @@ def main():
             cache.append(k[:, :, t0:t1].contiguous(), v[:, :, t0:t1].contiguous(), pos)
         idx = (lens_t.long() - 1).clamp(min=0)
         ar = torch.arange(w.B, device=dev)
-        k_new.append(k[ar, :, idx][:, :, None].contiguous())
-        v_new.append(v[ar, :, idx][:, :, None].contiguous())
+        k_new.append(k[ar, :, idx].contiguous())  # [B, Hkv, D]: the token at lens - 1
+        v_new.append(v[ar, :, idx].contiguous())
         if l == 0 and not args.no_cpu:
             host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy())
         del k, v
@@ -208,8 +209,8 @@ def main():
     log(f"bench: setup {time.time() - t_setup:.1f}s, cache {cache_bytes / 2**30:.2f} GiB, "
         f"plan chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
 
-    def append(l):
-        otq.otq_quantize_append(k_new[l], v_new[l], caches[l].desc, pos_l[l])
+    def append(l):  # the separate append kernel (timed for reference; the step fuses it)
+        otq.otq_quantize_append(k_new[l][:, :, None], v_new[l][:, :, None], caches[l].desc, pos_l[l])
 
     def split(l):
         otq.otq_sdpa_int4_split(qs[l], caches[l].desc, lens_l[l], max_len, w.scale, ws, plan)
@@ -217,11 +218,13 @@ def main():
     def combine(l):
         otq.otq_sdpa_lse_combine(w.Hq, caches[l].desc, lens_l[l], max_len, ws, plan, outs[l])
 
+    def fused(l):  # append of the new token fused into the split pass, then the combine
+        otq.otq_sdpa_int4_decode_append(qs[l], k_new[l], v_new[l], caches[l].desc, lens_l[l],
+                                        max_len, w.scale, outs[l], ws, plan=plan)
+
     def step():
         for l in range(L):
-            append(l)
-            split(l)
-            combine(l)
+            fused(l)
 
     # ---------------------------------------------------------------- timed steps
     graph = None
@@ -304,7 +307,7 @@ def main():
         b.record()
         torch.cuda.synchronize()
         sdpa_graph_us = a.elapsed_time(b) * 1000.0 / (args.steps * L)
-    log(f"bench: split {split_us:.2f} us, combine {combine_us:.2f} us, append {append_us:.2f} us, "
+    log(f"bench: split {split_us:.2f} us, combine {combine_us:.2f} us, append (unfused kernel) {append_us:.2f} us, "
         f"sdpa (split+combine, graph) {sdpa_graph_us} us per layer")
 
     # algorithmic bytes: packed codes + fp32 scales of every attended token, q read; out write
@@ -362,10 +365,11 @@ def main():
             "cache_gib": round(cache_bytes / 2**30, 3), "chunk": plan.chunk,
             "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
             "graph": graph is not None,
-            "step": "per layer: quantize_append(1 token) + split + lse_combine",
+            "step": "per layer: split pass with the one-token quantise-append fused in, then "
+                    "lse_combine (otq_sdpa_int4_decode_append)",
         },
         "kernels_us": {"split": round(split_us, 3), "combine": round(combine_us, 3),
-                       "append": round(append_us, 3),
+                       "append_unfused_kernel": round(append_us, 3),
                        "sdpa_per_layer_graph": None if sdpa_graph_us is None else round(sdpa_graph_us, 3)},
         "sdpa_GBps": round(layer_bytes / ((sdpa_graph_us or (split_us + combine_us)) * 1e-6) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "split_mfma" if plan.variant == 2 else "split_vec",

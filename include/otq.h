@@ -205,6 +205,29 @@ int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_hea
                                  const otq_plan *plan, void *stream);
 
 /*
+ * One decode step: quantise the new token of every sequence into the cache
+ * at position lens[b] - 1 (as otq_quantize_append with n_new = 1 and
+ * pos = lens[b] - 1 would), and attend over tokens [0, lens[b]) as
+ * otq_sdpa_int4_decode does, with no separate append launch.  The token is
+ * quantised on the fly as it is produced and attention reads only the
+ * compressed form (Open-TQ-Metal abstract; zingnex page, sections on
+ * on-the-fly quantisation and compressed-domain attention): the split pass
+ * covers the cached tokens [0, lens[b] - 1), and the combine pass quantises
+ * the new token, writes it and merges it as one more term.
+ *
+ *  k_new, v_new  device [B][Hkv][D] fp16/bf16 (dtype): the new token's K, V.
+ *  plan          from otq_sdpa_plan, or NULL for the default plan.
+ * Sequences with lens[b] == 0 append nothing and get zeros.  Other arguments,
+ * contracts and errors as for otq_sdpa_int4_decode_planned; the cache must
+ * hold tokens [0, lens[b] - 1) already.
+ */
+int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_new,
+                                int32_t dtype, int32_t num_q_heads, const otq_cache *cache,
+                                const int32_t *lens, int32_t max_len, float scale, float *out,
+                                void *workspace, size_t workspace_bytes,
+                                const otq_plan *plan, void *stream);
+
+/*
  * The two phases of otq_sdpa_int4_decode as separate calls, for callers
  * that time them apart or merge partials computed elsewhere (each split of
  * the token axis is independent until the combine).

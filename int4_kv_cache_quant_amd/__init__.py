@@ -27,7 +27,7 @@ OTQ_GROUP, OTQ_TILE = 32, 32
 EXPORTED = [
     "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
     "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
-    "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned",
+    "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned", "otq_sdpa_int4_decode_append",
     "otq_sdpa_int4_split", "otq_sdpa_lse_combine",
 ]
 
@@ -87,6 +87,9 @@ def lib():
     L.otq_sdpa_int4_decode_planned.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, P, S,
                                                ctypes.POINTER(otq_plan), P]
     L.otq_sdpa_int4_decode_planned.restype = ctypes.c_int
+    L.otq_sdpa_int4_decode_append.argtypes = [P, P, P, I, I, CP, P, I, ctypes.c_float, P, P, S,
+                                              ctypes.POINTER(otq_plan), P]
+    L.otq_sdpa_int4_decode_append.restype = ctypes.c_int
     L.otq_sdpa_int4_split.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, S,
                                       ctypes.POINTER(otq_plan), P]
     L.otq_sdpa_int4_split.restype = ctypes.c_int
@@ -181,6 +184,24 @@ def otq_sdpa_int4_decode(q, cache_desc, lens, max_len, scale, out, workspace, pl
     return rc
 
 
+def otq_sdpa_int4_decode_append(q, k_new, v_new, cache_desc, lens, max_len, scale, out, workspace,
+                                plan=None, num_q_heads=None, dtype=None, workspace_bytes=None,
+                                stream=None, check=True):
+    """One decode step: quantise k_new, v_new (device [B, Hkv, D]) into the
+    cache at position lens[b] - 1 and attend over [0, lens[b])."""
+    Hq = q.shape[1] if num_q_heads is None else num_q_heads
+    dtype = dtype_code(q.dtype) if dtype is None else dtype
+    wsb = workspace.numel() * workspace.element_size() if workspace_bytes is None else workspace_bytes
+    rc = lib().otq_sdpa_int4_decode_append(_ptr(q), _ptr(k_new), _ptr(v_new), dtype, Hq,
+                                           ctypes.byref(cache_desc), _ptr(lens), max_len,
+                                           float(scale), _ptr(out), _ptr(workspace), wsb,
+                                           None if plan is None else ctypes.byref(plan),
+                                           _stream(stream))
+    if check:
+        _check(rc, "otq_sdpa_int4_decode_append")
+    return rc
+
+
 def otq_sdpa_int4_split(q, cache_desc, lens, max_len, scale, workspace, plan, num_q_heads=None,
                         dtype=None, workspace_bytes=None, stream=None, check=True):
     """Split pass only: partials into the workspace (layout in include/otq.h)."""
@@ -255,4 +276,16 @@ class Int4KVCache:
         if workspace is None:
             workspace = self.workspace(q.shape[1], max_len, plan)
         otq_sdpa_int4_decode(q, self.desc, lens, max_len, scale, out, workspace, plan=plan, stream=stream)
+        return out
+
+    def decode_append(self, q, k_new, v_new, lens, max_len, scale, out=None, workspace=None,
+                      plan=None, stream=None):
+        """Append the token at lens[b] - 1 (k_new, v_new: [B, Hkv, D]) and
+        attend over [0, lens[b]) in one pass."""
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        if workspace is None:
+            workspace = self.workspace(q.shape[1], max_len, plan)
+        otq_sdpa_int4_decode_append(q, k_new, v_new, self.desc, lens, max_len, scale, out,
+                                    workspace, plan=plan, stream=stream)
         return out

@@ -190,7 +190,7 @@ int check_plan(int32_t Hq, const otq_cache* c, int32_t max_len, const otq_plan* 
 
 int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache* cache,
               const int32_t* lens, int32_t max_len, float scale, void* workspace,
-              const otq_plan& chk, hipStream_t s)
+              const otq_plan& chk, hipStream_t s, int lens_offset = 0)
 {
     const int D = cache->head_dim;
     otq::SplitArgs a;
@@ -215,6 +215,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
                                           ml_offset(cache, num_q_heads, chk));
+    a.lens_offset = lens_offset;
     const hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
                                                          : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
@@ -222,14 +223,35 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
 
 int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens,
                 int32_t max_len, const void* workspace, const otq_plan& chk, float* out,
-                hipStream_t s)
+                hipStream_t s, const void* q = nullptr, const void* k_new = nullptr,
+                const void* v_new = nullptr, int32_t dtype = 0, float scale = 0.0f)
 {
-    const float* part_o = static_cast<const float*>(workspace);
-    const float2* part_ml = reinterpret_cast<const float2*>(
-        static_cast<const char*>(workspace) + ml_offset(cache, num_q_heads, chk));
-    const hipError_t e = otq::launch_lse_combine(part_o, part_ml, lens, max_len, chk.chunk,
-                                                 chk.num_splits, cache->batch, num_q_heads,
-                                                 cache->head_dim, out, s);
+    otq::CombineArgs a{};
+    a.part_o = static_cast<const float*>(workspace);
+    a.part_ml = reinterpret_cast<const float2*>(static_cast<const char*>(workspace) +
+                                                ml_offset(cache, num_q_heads, chk));
+    a.lens = lens;
+    a.max_len = max_len;
+    a.chunk = chk.chunk;
+    a.S = chk.num_splits;
+    a.B = cache->batch;
+    a.Hq = num_q_heads;
+    a.D = cache->head_dim;
+    a.out = out;
+    a.k_new = static_cast<const uint16_t*>(k_new);
+    a.v_new = static_cast<const uint16_t*>(v_new);
+    a.q = q;
+    a.dtype = dtype;
+    a.H = cache->num_kv_heads;
+    a.cap = cache->capacity;
+    a.kc = cache->k_codes;
+    a.ks = cache->k_scales;
+    a.vc = cache->v_codes;
+    a.vs = cache->v_scales;
+    a.signs = cache->k_rot_signs;
+    a.rot_norm = cache->rot_norm;
+    a.qscale = scale * otq::kLog2eHost;
+    const hipError_t e = otq::launch_lse_combine(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
@@ -283,6 +305,26 @@ int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_hea
     rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s);
     if (rc != OTQ_OK) return rc;
     return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s);
+}
+
+int otq_sdpa_int4_decode_append(const void* q, const void* k_new, const void* v_new, int32_t dtype,
+                                int32_t num_q_heads, const otq_cache* cache, const int32_t* lens,
+                                int32_t max_len, float scale, float* out, void* workspace,
+                                size_t workspace_bytes, const otq_plan* plan, void* stream)
+{
+    otq_plan chk;
+    int rc = plan ? check_plan(num_q_heads, cache, max_len, plan, &chk)
+                  : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (!q || !k_new || !v_new || !lens || !out) return OTQ_EINVAL;
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (!finite(scale)) return OTQ_EINVAL;
+    if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s, 1);
+    if (rc != OTQ_OK) return rc;
+    return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s, q, k_new, v_new,
+                       dtype, scale);
 }
 
 int otq_sdpa_int4_decode(const void* q, int32_t dtype, int32_t num_q_heads,

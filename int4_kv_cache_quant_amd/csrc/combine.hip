@@ -1,4 +1,5 @@
-// combine.hip - merge the split partials of decode attention.
+// combine.hip - merge the split partials of decode attention, optionally with
+// the step's new token appended.
 //
 // Each split s of a (sequence, query head) row carries (m_s, l_s, o_s): its
 // softmax reference (log2 domain; any value at or above its largest score),
@@ -8,8 +9,15 @@
 // evaluated in fp32 (the high-precision accumulation the zingnex
 // Open-TQ-Metal page asks for in its section on numerical stability).
 // A row with lens == 0 has no splits and gets zeros.
+//
+// With the append, the split pass covered [0, lens - 1) and this kernel
+// quantises the token at lens - 1 as it is produced (Open-TQ-Metal abstract;
+// zingnex page, section on on-the-fly quantisation), writes it into the
+// cache, and merges it as one more term (m = its score, l = 1, o = its
+// dequantised V).
 #include "common.hpp"
 #include "kernels.hpp"
+#include "quant_lane.hpp"
 
 namespace otq {
 
@@ -19,44 +27,111 @@ constexpr int kThreads = 256;
 constexpr int kCh = 32;                       // channels per block
 constexpr int kQuads = kCh / 4;               // threads sharing one split (a float4 each)
 constexpr int kLanesS = kThreads / kQuads;    // splits read side by side
+constexpr float kNegInf = -__builtin_huge_valf();
+
+// Sum over the block (every thread returns the total).
+__device__ __forceinline__ float block_sum(float v, float* red)
+{
+#pragma unroll
+    for (int k = 1; k < 64; k <<= 1) v += shfl_xor(v, k);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < kThreads / 64; ++w) r += red[w];
+    return r;
+}
+
+// In-place Walsh-Hadamard butterflies over one element per thread (threads
+// 0..D-1), stages in ascending stride: the lower element of a pair becomes
+// lower + upper, the upper one lower - upper.  Strides below 64 stay in the
+// wave; wider ones go through LDS.
+template <int D>
+__device__ __forceinline__ float fwht_thread(float y, float* xch)
+{
+#pragma clang fp contract(off)
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int h = 1; h < D; h <<= 1) {
+        float o;
+        if (h < 64) {
+            o = shfl_xor(y, h);
+        } else {  // threads past D hold no channel and stay out of xch
+            __syncthreads();
+            if (t < D) xch[t] = y;
+            __syncthreads();
+            o = t < D ? xch[t ^ h] : y;
+        }
+        y = (t & h) ? (o - y) : (y + o);
+    }
+    return y;
+}
 
 // Block (row, c0): row = b * Hq + h, channels [32 c0, 32 c0 + 32).  Thread
 // t reads channels 32 c0 + 4 (t % 8) .. + 3 of the splits s = t / 8 (mod 32),
 // so 32 splits stream in side by side; each thread folds its splits into a
 // running (m, l, o) (the same merge rule as above), then the block merges the
-// threads' triples: one pass over the partials.
-__global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float* __restrict__ part_o,
-                                                               const float2* __restrict__ part_ml,
-                                                               const int32_t* __restrict__ lens,
-                                                               int max_len, int chunk, int S,
-                                                               int Hq, int D,
-                                                               float* __restrict__ out)
+// threads' triples: one pass over the partials.  DA = head_dim when the
+// block also appends the new token (0 otherwise).
+template <int DA, bool ROT>
+__global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
 {
     __shared__ float red_m[kThreads / 64];
     __shared__ float4 red_o[kThreads / 64][kQuads];
     __shared__ float red_l[kThreads / 64];
+    __shared__ float red_s[kThreads / 64];
+    __shared__ float xch[DA > 0 ? DA : 1];   // butterflies, then the new token's V
+    constexpr bool APPEND = DA > 0;
+    const int D = APPEND ? DA : a.D;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int b = row / Hq;
+    const int b = row / a.Hq;
     const int q = tid % kQuads, g = tid / kQuads;
     const int c = kCh * blockIdx.y + 4 * q;
-    const int len = min(max(lens[b], 0), max_len);
-    const int ns = (len + chunk - 1) / chunk;
-    float4* dst = reinterpret_cast<float4*>(out + (size_t)row * D + c);
-    if (ns == 0) {
+    const int len = min(max(a.lens[b], 0), a.max_len);
+    const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
+    const int ns = (nsplit_tok + a.chunk - 1) / a.chunk;
+    float4* dst = reinterpret_cast<float4*>(a.out + (size_t)row * D + c);
+    if (len == 0) {  // block-uniform: nothing attended, nothing appended
         if (tid < kQuads) *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         return;
     }
-    const float2* ml = part_ml + (size_t)row * S;
-    const float* po = part_o + (size_t)row * S * D + c;
 
-    const float kNegInf = -__builtin_huge_valf();
+    // the new token's K, V and this row's q: one channel per thread (threads
+    // past D work on channel D - 1 and write nothing)
+    [[maybe_unused]] uint16_t kx = 0, vx = 0, qx = 0;
+    [[maybe_unused]] float sg = 1.0f;
+    [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
+    [[maybe_unused]] bool writer = false;
+    [[maybe_unused]] uint8_t vold = 0;
+    if constexpr (APPEND) {
+        const int G = a.Hq / a.H, h = row % a.Hq;
+        kvh = h / G;
+        pos = len - 1;
+        ch = min(tid, DA - 1);
+        const size_t src = ((size_t)b * a.H + kvh) * DA + ch;
+        kx = a.k_new[src];
+        vx = a.v_new[src];
+        qx = static_cast<const uint16_t*>(a.q)[(size_t)row * DA + ch];
+        if (ROT) sg = a.signs[ch];
+        // one block per KV head writes the token: the first query head's,
+        // first channel slice
+        writer = h % G == 0 && blockIdx.y == 0 && tid < DA;
+        if (writer)
+            vold = a.vc[(((size_t)b * a.H + kvh) * (a.cap / kTile) + pos / kTile) * (size_t)(16 * DA) +
+                        v_tile_byte<DA>(ch, (pos % kTile) & ~1)];
+    }
+
+    // ---- the splits
+    const float2* ml = a.part_ml + (size_t)row * a.S;
+    const float* po = a.part_o + (size_t)row * a.S * D + c;
     float m = kNegInf, l = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     auto fold = [&](float2 v, float4 x) {  // every written partial has a finite m
         const float mn = fmaxf(m, v.x);
-        const float a = exp2_approx(m - mn), w = exp2_approx(v.x - mn);
-        o = make_float4(o.x * a + x.x * w, o.y * a + x.y * w, o.z * a + x.z * w, o.w * a + x.w * w);
-        l = l * a + v.y * w;
+        const float al = exp2_approx(m - mn), w = exp2_approx(v.x - mn);
+        o = make_float4(o.x * al + x.x * w, o.y * al + x.y * w, o.z * al + x.z * w, o.w * al + x.w * w);
+        l = l * al + v.y * w;
         m = mn;
     };
     int s = g;
@@ -68,6 +143,51 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float* __re
         fold(v1, x1);
     }
     if (s < ns) fold(ml[s], *reinterpret_cast<const float4*>(po + (size_t)s * D));
+
+    // ---- the new token: quantise K and V exactly as the append kernel does
+    //      (same operations, same order), write them, score it
+    [[maybe_unused]] float s_new = kNegInf;
+    if constexpr (APPEND) {
+        float x = widen(kx, a.dtype);
+        if (ROT) {
+            x = x * sg;
+            x = fwht_thread<DA>(x, xch);
+            x = x * a.rot_norm;
+        }
+        float xk[1] = {x};
+        int ck[1];
+        // one channel per lane: the lane layout of a 64-channel vector, whose
+        // 32-lane groups are this vector's 32-channel groups
+        const float sk = quantize_lane<64>(xk, ck, lane);
+        float xv[1] = {widen(vx, a.dtype)};
+        int cv[1];
+        const float sv = quantize_lane<64>(xv, cv, lane);
+        if (writer) {
+            const size_t head = (size_t)b * a.H + kvh, krow = head * a.cap + pos;
+            const int cnext = __shfl_xor(ck[0], 1, 64);
+            if ((ch & 1) == 0)
+                a.kc[krow * (DA / 2) + k_row_byte<DA>(ch)] = (uint8_t)((ck[0] & 0xF) | ((cnext & 0xF) << 4));
+            const uint32_t nib = (uint32_t)cv[0] & 0xF;
+            a.vc[(head * (a.cap / kTile) + pos / kTile) * (size_t)(16 * DA) +
+                 v_tile_byte<DA>(ch, (pos % kTile) & ~1)] =
+                (uint8_t)((pos & 1) ? ((vold & 0x0F) | (nib << 4)) : ((vold & 0xF0) | nib));
+            if (ch % kGroup == 0) {
+                a.ks[krow * (DA / kGroup) + ch / kGroup] = sk;
+                a.vs[krow * (DA / kGroup) + ch / kGroup] = sv;
+            }
+        }
+        // score: q' . k^ (q rotated like K), in log2 units
+        float y = widen(qx, a.dtype);
+        if (ROT) {
+            y = y * sg;
+            y = fwht_thread<DA>(y, xch);
+            y = y * a.rot_norm;
+        }
+        const float kd = (float)ck[0] * sk;
+        s_new = block_sum(tid < DA ? y * kd : 0.0f, red_s) * a.qscale;
+        __syncthreads();  // xch is reused for V below
+        if (tid < DA) xch[tid] = (float)cv[0] * sv;
+    }
 
     // block maximum of the threads' references
     float M = m;
@@ -102,20 +222,45 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(const float* __re
             r.x += x.x; r.y += x.y; r.z += x.z; r.w += x.w;
             L += red_l[w];
         }
+        if constexpr (APPEND) {  // one more term: m = s_new, l = 1, o = V^ of the token
+            const float Mn = fmaxf(M, s_new);
+            const float a1 = (M == kNegInf) ? 0.0f : exp2_approx(M - Mn), a2 = exp2_approx(s_new - Mn);
+            const float* vh = xch + kCh * blockIdx.y + 4 * tid;
+            r = make_float4(r.x * a1 + vh[0] * a2, r.y * a1 + vh[1] * a2, r.z * a1 + vh[2] * a2,
+                            r.w * a1 + vh[3] * a2);
+            L = L * a1 + a2;
+        }
         *dst = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
     }
 }
 
 }  // namespace
 
-hipError_t launch_lse_combine(const float* part_o, const float2* part_ml, const int32_t* lens,
-                              int max_len, int chunk, int num_splits, int B, int Hq, int D,
-                              float* out, hipStream_t stream)
+hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
 {
-    if (D % kCh != 0) return hipErrorInvalidValue;
-    dim3 grid(B * Hq, D / kCh), block(kThreads);
-    lse_combine_kernel<<<grid, block, 0, stream>>>(part_o, part_ml, lens, max_len, chunk,
-                                                   num_splits, Hq, D, out);
+    if (a.D % kCh != 0) return hipErrorInvalidValue;
+    dim3 grid(a.B * a.Hq, a.D / kCh), block(kThreads);
+    if (a.k_new == nullptr) {
+        lse_combine_kernel<0, false><<<grid, block, 0, stream>>>(a);
+    } else {
+        const bool rot = a.signs != nullptr;
+        switch (a.D) {
+        case 64:
+            rot ? lse_combine_kernel<64, true><<<grid, block, 0, stream>>>(a)
+                : lse_combine_kernel<64, false><<<grid, block, 0, stream>>>(a);
+            break;
+        case 128:
+            rot ? lse_combine_kernel<128, true><<<grid, block, 0, stream>>>(a)
+                : lse_combine_kernel<128, false><<<grid, block, 0, stream>>>(a);
+            break;
+        case 256:
+            rot ? lse_combine_kernel<256, true><<<grid, block, 0, stream>>>(a)
+                : lse_combine_kernel<256, false><<<grid, block, 0, stream>>>(a);
+            break;
+        default:
+            return hipErrorInvalidValue;
+        }
+    }
     return hipGetLastError();
 }
 

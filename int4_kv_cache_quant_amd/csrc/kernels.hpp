@@ -18,10 +18,10 @@ struct SplitArgs {
     const void* q;
     int dtype;
     int B, Hq, H, D, cap;
-    const uint8_t* kc;
-    const float* ks;
-    const uint8_t* vc;
-    const float* vs;
+    uint8_t* kc;  // written only by the fused one-token append
+    float* ks;
+    uint8_t* vc;
+    float* vs;
     const float* signs;
     float rot_norm;
     const int32_t* lens;
@@ -31,6 +31,9 @@ struct SplitArgs {
     int num_splits;
     float* part_o;   // [B][Hq][S][D]
     float2* part_ml; // [B][Hq][S] (m, l)
+    // 1 when the token at lens[b] - 1 is appended by the combine of the same
+    // call (the split pass then covers [0, lens[b] - 1)), else 0.
+    int lens_offset;
 };
 
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
@@ -43,8 +46,28 @@ int split_mfma_heads_per_wave(int D, int G, int H);
 // Waves per workgroup of the MFMA split kernel.
 int split_mfma_block_waves(int D);
 
-hipError_t launch_lse_combine(const float* part_o, const float2* part_ml, const int32_t* lens,
-                              int max_len, int chunk, int num_splits, int B, int Hq, int D,
-                              float* out, hipStream_t stream);
+// Combine pass arguments.  With k_new set, the split pass covered
+// [0, lens[b] - 1) and the combine quantises the token at lens[b] - 1 into
+// the cache and merges it.
+struct CombineArgs {
+    const float* part_o;
+    const float2* part_ml;
+    const int32_t* lens;
+    int max_len, chunk, S, B, Hq, D;
+    float* out;
+    // fused one-token append (k_new == nullptr: none)
+    const uint16_t* k_new;  // [B][H][D]
+    const uint16_t* v_new;
+    const void* q;          // [B][Hq][D]
+    int dtype, H, cap;
+    uint8_t* kc;
+    float* ks;
+    uint8_t* vc;
+    float* vs;
+    const float* signs;
+    float rot_norm;
+    float qscale;           // softmax scale * log2(e)
+};
+hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
 
 }  // namespace otq

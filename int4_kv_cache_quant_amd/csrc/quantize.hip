@@ -11,94 +11,11 @@
 // correct evaluation of the same steps.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "quant_lane.hpp"
 
 namespace otq {
 
 namespace {
-
-// One wave quantises one vector of D elements; lane l owns elements
-// [l*E, l*E + E), E = D / 64.  Returns codes in [-8, 7] in c[] and the scale
-// of the lane's group (a group spans 32 / E lanes).
-template <int D>
-__device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 64], int lane)
-{
-    constexpr int E = D / 64;
-    constexpr int LANES_PER_GROUP = kGroup / E;
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
-#pragma unroll
-    for (int m = 1; m < LANES_PER_GROUP; m <<= 1) a = fmaxf(a, shfl_xor(a, m));
-    const float s = a / 7.0f;  // correctly rounded IEEE division
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-        int code = 0;
-        if (s != 0.0f) {
-            float r = rintf(x[e] / s);  // v_rndne_f32: half to even
-            r = fminf(fmaxf(r, -8.0f), 7.0f);
-            code = (int)r;
-        }
-        c[e] = code;
-    }
-    return s;
-}
-
-// y <- rot_norm * H (signs (.) y), Sylvester order, stages in ascending
-// stride; a butterfly replaces (lower, upper) with (lower + upper,
-// lower - upper) exactly as the in-place fast Walsh-Hadamard transform does.
-template <int D>
-__device__ __forceinline__ void rotate_lane(float (&y)[D / 64], const float* __restrict__ signs,
-                                            float rot_norm, int lane)
-{
-    constexpr int E = D / 64;
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = y[e] * signs[lane * E + e];
-#pragma unroll
-    for (int h = 1; h < E; h <<= 1) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            if ((e & h) == 0) {
-                const float lo = y[e], hi = y[e + h];
-                y[e] = lo + hi;
-                y[e + h] = lo - hi;
-            }
-        }
-    }
-#pragma unroll
-    for (int h = E; h < D; h <<= 1) {
-        const int m = h / E;
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float o = shfl_xor(y[e], m);
-            y[e] = upper ? (o - y[e]) : (y[e] + o);
-        }
-    }
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
-}
-
-// Byte offset, inside one K row, of the byte holding even channel c and
-// channel c + 1: word (r * NG + g) holds channels 32 g + 8 r + 0..7.
-template <int D>
-__device__ __forceinline__ int k_row_byte(int c)
-{
-    constexpr int NG = D / kGroup;
-    const int g = c >> 5, r = (c >> 3) & 3, k = c & 7;
-    return (r * NG + g) * 4 + (k >> 1);
-}
-
-// Byte offset, inside one V tile, of the byte holding (channel c, token pair
-// starting at even tile-relative token u).
-template <int D>
-__device__ __forceinline__ int v_tile_byte(int c, int u)
-{
-    const int r = (u & 15) >> 2;
-    const int j = 4 * (u >> 4) + (u & 3);
-    const int cb = c >> 4, n = c & 15, a = cb >> 2, b = cb & 3;
-    const int word = ((a * 4 + r) * 16 + n) * 4 + b;
-    return word * 4 + (j >> 1);
-}
 
 template <int D>
 __global__ __launch_bounds__(256) void quantize_append_kernel(

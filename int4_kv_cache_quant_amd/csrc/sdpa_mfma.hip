@@ -339,7 +339,7 @@ void split_mfma_kernel(SplitArgs a)
     auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (st * W + wave) * St::BYTES; };
 
     // sequence length first, as a scalar load: nothing has been written yet
-    const int len = min(max(a.lens[b], 0), a.max_len);
+    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
 
     // ---- q straight into registers, before any tile copy is queued: lane
     //      (n16, r) needs, per scale group g, channels 32 g + 8 r + 0..7 of

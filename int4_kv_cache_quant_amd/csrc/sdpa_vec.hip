@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
     const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
-    const int len = min(max(a.lens[b], 0), a.max_len);
+    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for empty chunks
     const int end = min(start + a.chunk, len);

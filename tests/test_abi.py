@@ -134,6 +134,13 @@ def test_decode_host_errors():
     cb = lambda out=FAKE, lens=FAKE, ws=4096, wsb=p.workspace_bytes: lib.otq_sdpa_lse_combine(
         4, ctypes.byref(d), P(lens), 256, P(ws), wsb, ctypes.byref(p), P(out), None)
     assert cb(out=0) == otq.OTQ_EINVAL and cb(lens=0) == otq.OTQ_EINVAL and cb(ws=0) == otq.OTQ_EWORKSPACE
+    fa = lambda q=FAKE, kn=FAKE, vn=FAKE, lens=FAKE, out=FAKE, ws=4096, wsb=p.workspace_bytes, plan=p, dt=1: \
+        lib.otq_sdpa_int4_decode_append(P(q), P(kn), P(vn), dt, 4, ctypes.byref(d), P(lens), 256, 0.1,
+                                        P(out), P(ws), wsb, None if plan is None else ctypes.byref(plan), None)
+    assert fa(q=0) == otq.OTQ_EINVAL and fa(kn=0) == otq.OTQ_EINVAL and fa(vn=0) == otq.OTQ_EINVAL
+    assert fa(lens=0) == otq.OTQ_EINVAL and fa(out=0) == otq.OTQ_EINVAL and fa(dt=2) == otq.OTQ_EUNSUPPORTED
+    assert fa(ws=0) == otq.OTQ_EWORKSPACE and fa(wsb=16) == otq.OTQ_EWORKSPACE
+    assert fa(plan=otq.otq_plan(100, 3, 1, 0, 0)) == otq.OTQ_EINVAL   # chunk not a multiple of 128
     bad = otq.otq_plan(100, 3, 1, 0, 0)            # chunk not a multiple of 128
     assert lib.otq_sdpa_lse_combine(4, ctypes.byref(d), P(FAKE), 256, P(4096), 1 << 20,
                                     ctypes.byref(bad), P(FAKE), None) == otq.OTQ_EINVAL

@@ -1,0 +1,121 @@
+"""GPU parity of otq_sdpa_int4_decode_append (one decode step: the split
+pass covers the cached tokens, the combine pass quantises the new token into
+the cache and merges it).
+
+Each case prefills every sequence, then poisons the slot of its new token
+(K codes and scales, the V scale and the token's own V nibble; the
+neighbour's nibble is kept) and runs the fused call with that token as
+k_new / v_new.  The whole cache must then equal the oracle's quantisation bit
+for bit, and the outputs must be within the usual tolerance of the fp64
+oracle over [0, lens[b])."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int4_kv_cache_quant_amd as otq
+import oracle
+from int4_kv_cache_quant_amd import layout
+
+from gpu_common import (MAX_ABS, REL_L2, build_cache, compare_codes, errors, host_cache,
+                        oracle_cache, rot_norm32, say, to_bits)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _poison(cache, lens):
+    """Overwrite the slot of token lens[b] - 1 of every sequence with junk."""
+    B, H, D, cap = cache.shape
+    vplain = layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D)
+    for b, n in enumerate(lens):
+        if n < 1:
+            continue
+        p = n - 1
+        cache.k_codes[b, :, p] = 0x5A
+        cache.k_scales[b, :, p] = 123.0
+        cache.v_scales[b, :, p] = -7.0
+        # token p's nibble of every channel pair: byte c // 2 of the plain row
+        vplain[b, :, p] = 0xA5
+    # keep the neighbours' nibbles: only token p's own nibbles change
+    orig = layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D)
+    mixed = orig.copy()
+    for b, n in enumerate(lens):
+        if n >= 1:
+            mixed[b, :, n - 1] = vplain[b, :, n - 1]
+    cache.v_codes.copy_(torch.from_numpy(layout.v_plain_to_tiled(mixed, D)).to(DEV))
+
+
+def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, seed=0, steps=1,
+         variant=otq.OTQ_VARIANT_MFMA):
+    g = torch.Generator().manual_seed(seed)
+    Hq = G * Hkv
+    T = max(lens) + steps - 1
+    k = torch.randn((B, Hkv, cap, D), generator=g)
+    v = torch.randn((B, Hkv, cap, D), generator=g)
+    k[..., 3] *= 10
+    v[..., 3] *= 10
+    k, v = k.to(dtype), v.to(dtype)
+    signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if rotate else None
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    scale = 1.0 / math.sqrt(D)
+    cache = build_cache(k[:, :, :T].to(DEV).contiguous(), v[:, :, :T].to(DEV).contiguous(), cap,
+                        signs=None if signs is None else signs.to(DEV), append_last=False)
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D))
+    for step in range(steps):
+        cur = [n + step for n in lens]
+        _poison(cache, cur)
+        lens_t = torch.tensor(cur, dtype=torch.int32, device=DEV)
+        idx = (lens_t.long() - 1).clamp(min=0)
+        ar = torch.arange(B, device=DEV)
+        kn = k.to(DEV)[ar, :, idx].contiguous()   # [B, Hkv, D]
+        vn = v.to(DEV)[ar, :, idx].contiguous()
+        q = torch.randn((B, Hq, D), generator=g).to(dtype)
+        max_len = max(1, max(cur))
+        plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
+        say(f"fused B={B} G={G} Hkv={Hkv} D={D} lens={cur} chunk={plan.chunk} rotate={rotate}")
+        out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max_len, scale, plan=plan)
+        torch.cuda.synchronize()
+        got_cache = host_cache(cache)
+        for b, n in enumerate(cur):
+            if n < 1:
+                continue
+            sub = tuple(x[b:b + 1, :, :n] for x in got_cache)
+            ref = tuple(x[b:b + 1, :, :n] for x in ref_cache)
+            assert compare_codes(sub, ref, n) == {
+                "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, f"seq {b}"
+        kc, ks, vc, vs = ref_cache
+        ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(cur, np.int32), scale,
+                          signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
+                          threads=8)
+        ma, rel = errors(out.cpu().numpy(), ref)
+        say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+        assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 4, 8, 16])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fused_append_parity(D, G, rotate):
+    # new tokens at an odd and an even position, in the middle of a chunk
+    _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=D + G + rotate)
+
+
+@pytest.mark.parametrize("lens", [[1, 2], [129, 128], [257, 33], [32, 31]])
+def test_fused_append_edges(lens):
+    """lens = 1 (no cached token at all), a new token opening a chunk (129
+    with chunk 128: that split has no cached token), chunk and tile ends."""
+    _run(2, 8, 2, 128, 384, lens, chunk=128, seed=sum(lens))
+
+
+def test_fused_append_consecutive_steps():
+    """Three decode steps in a row, default plan, fp16 and rotated."""
+    _run(3, 4, 2, 128, 512, [300, 77, 2], dtype=torch.float16, rotate=True, steps=3, seed=9)
+
+
+@pytest.mark.parametrize("G,D", [(1, 128), (2, 64)])
+def test_fused_append_vector_variant(G, D):
+    """The same call on the vector split variant."""
+    _run(2, G, 2, D, 320, [300, 77], chunk=128, seed=G + D, variant=otq.OTQ_VARIANT_VECTOR)

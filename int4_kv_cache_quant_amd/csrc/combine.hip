@@ -32,8 +32,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 // Sum over the block (every thread returns the total).
 __device__ __forceinline__ float block_sum(float v, float* red)
 {
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) v += shfl_xor(v, k);
+    v = group_sum<64>(v);
     __syncthreads();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     __syncthreads();
@@ -190,9 +189,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     }
 
     // block maximum of the threads' references
-    float M = m;
-#pragma unroll
-    for (int k = 1; k < 64; k <<= 1) M = fmaxf(M, shfl_xor(M, k));
+    float M = group_max<64>(m);
     if (lane == 0) red_m[wave] = M;
     __syncthreads();
     M = red_m[0];
@@ -201,15 +198,12 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     const float f = (m == kNegInf) ? 0.0f : exp2_approx(m - M);
     o = make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
     l = (q == 0) ? l * f : 0.0f;  // the kQuads threads of a split group hold the same l
-    // sum over the threads of one channel quad: lanes 8 apart, then waves
-#pragma unroll
-    for (int k = kQuads; k < 64; k <<= 1) {
-        o.x += shfl_xor(o.x, k);
-        o.y += shfl_xor(o.y, k);
-        o.z += shfl_xor(o.z, k);
-        o.w += shfl_xor(o.w, k);
-        l += shfl_xor(l, k);
-    }
+    // sum over the threads of one channel quad: lanes 8 apart (a row's
+    // rotation by 8, then the row swaps), then waves
+    static_assert(kQuads == 8, "lanes 8 apart");
+    auto sum8 = [](float v) { return sum_xor32(sum_xor16(v + dpp_mov<kDppRor8>(v))); };
+    o = make_float4(sum8(o.x), sum8(o.y), sum8(o.z), sum8(o.w));
+    l = sum8(l);
     if (lane < kQuads) red_o[wave][lane] = o;
     if (lane == 0) red_l[wave] = l;
     __syncthreads();

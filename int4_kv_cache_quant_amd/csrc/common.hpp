@@ -56,6 +56,95 @@ __device__ __forceinline__ float shfl_xor(float v, int m)
     return __shfl_xor(v, m, 64);
 }
 
+// Cross-row exchanges without LDS: v_permlane16_swap pairs rows (0,1) and
+// (2,3) of the wave, v_permlane32_swap its two halves; applied to two copies
+// of a value, each lane ends up with its own value and its partner's, one in
+// each register.  Written as inline asm (a register move, no memory access):
+// the compiler builtin's two results are treated as equal when both inputs
+// are one value, which would drop the partner's.  The s_nop covers the wait
+// states between a VALU write and the swap reading it.
+__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void swap_rows32(unsigned& a, unsigned& b)
+{
+    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+template <bool XOR16>
+__device__ __forceinline__ void pair_values(float v, float& x, float& y)
+{
+    unsigned a = __builtin_bit_cast(unsigned, v), b = a;
+    if constexpr (XOR16) swap_rows16(a, b);
+    else swap_rows32(a, b);
+    x = __builtin_bit_cast(float, a);
+    y = __builtin_bit_cast(float, b);
+}
+__device__ __forceinline__ float max_xor16(float v)
+{
+    float x, y;
+    pair_values<true>(v, x, y);
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float max_xor32(float v)
+{
+    float x, y;
+    pair_values<false>(v, x, y);
+    return fmaxf(x, y);
+}
+__device__ __forceinline__ float sum_xor16(float v)
+{
+    float x, y;
+    pair_values<true>(v, x, y);
+    return x + y;
+}
+__device__ __forceinline__ float sum_xor32(float v)
+{
+    float x, y;
+    pair_values<false>(v, x, y);
+    return x + y;
+}
+
+// Other DPP lane moves (bound_ctrl set: every source lane is valid), which the
+// compiler folds into the consuming v_max / v_add: quad_perm swaps of lanes
+// 1 and 2 apart, the mirror of each half-row of 8 and of each row of 16, and
+// the rotation of a row by 8 (lane i reads lane i ^ 8).
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+              kDppRor8 = 0x128;
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v)
+{
+    return __builtin_bit_cast(float,
+                              __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+// Maximum / sum over each aligned group of N lanes (N = 1, 2, 4, ..., 64),
+// every lane of the group getting the result; all 64 lanes must be active.
+template <int N>
+__device__ __forceinline__ float group_max(float v)
+{
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+    if constexpr (N >= 2) v = fmaxf(v, dpp_mov<kDppXor1>(v));
+    if constexpr (N >= 4) v = fmaxf(v, dpp_mov<kDppXor2>(v));
+    if constexpr (N >= 8) v = fmaxf(v, dpp_mov<kDppHalfMirror>(v));
+    if constexpr (N >= 16) v = fmaxf(v, dpp_mov<kDppMirror>(v));
+    if constexpr (N >= 32) v = max_xor16(v);
+    if constexpr (N >= 64) v = max_xor32(v);
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "group size");
+    if constexpr (N >= 2) v += dpp_mov<kDppXor1>(v);
+    if constexpr (N >= 4) v += dpp_mov<kDppXor2>(v);
+    if constexpr (N >= 8) v += dpp_mov<kDppHalfMirror>(v);
+    if constexpr (N >= 16) v += dpp_mov<kDppMirror>(v);
+    if constexpr (N >= 32) v = sum_xor16(v);
+    if constexpr (N >= 64) v = sum_xor32(v);
+    return v;
+}
+
 // Signed int4 nibble k (0..7) of a 32-bit word, as fp32.
 template <int K>
 __device__ __forceinline__ float nib_f32(uint32_t w)

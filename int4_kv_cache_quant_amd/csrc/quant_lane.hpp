@@ -23,8 +23,7 @@ __device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 
     float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
-#pragma unroll
-    for (int m = 1; m < LANES_PER_GROUP; m <<= 1) a = fmaxf(a, shfl_xor(a, m));
+    a = group_max<LANES_PER_GROUP>(a);  // exact in any order
     const float s = a / 7.0f;  // correctly rounded IEEE division
 #pragma unroll
     for (int e = 0; e < E; ++e) {

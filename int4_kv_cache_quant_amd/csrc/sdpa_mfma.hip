@@ -120,55 +120,6 @@ __device__ __forceinline__ float quad_bcast(float v)
         float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), K * 0x55, 0xF, 0xF, true));
 }
 
-// Cross-row exchanges without LDS: v_permlane16_swap pairs rows (0,1) and
-// (2,3) of the wave, v_permlane32_swap its two halves; applied to two copies
-// of a value, each lane ends up with its own value and its partner's, one in
-// each register.  Written as inline asm (a register move, no memory access):
-// the compiler builtin's two results are treated as equal when both inputs
-// are one value, which would drop the partner's.  The s_nop covers the wait
-// states between a VALU write and the swap reading it.
-__device__ __forceinline__ void swap_rows16(unsigned& a, unsigned& b)
-{
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-__device__ __forceinline__ void swap_rows32(unsigned& a, unsigned& b)
-{
-    asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-}
-template <bool XOR16>
-__device__ __forceinline__ void pair_values(float v, float& x, float& y)
-{
-    unsigned a = __builtin_bit_cast(unsigned, v), b = a;
-    if constexpr (XOR16) swap_rows16(a, b);
-    else swap_rows32(a, b);
-    x = __builtin_bit_cast(float, a);
-    y = __builtin_bit_cast(float, b);
-}
-__device__ __forceinline__ float max_xor16(float v)
-{
-    float x, y;
-    pair_values<true>(v, x, y);
-    return fmaxf(x, y);
-}
-__device__ __forceinline__ float max_xor32(float v)
-{
-    float x, y;
-    pair_values<false>(v, x, y);
-    return fmaxf(x, y);
-}
-__device__ __forceinline__ float sum_xor16(float v)
-{
-    float x, y;
-    pair_values<true>(v, x, y);
-    return x + y;
-}
-__device__ __forceinline__ float sum_xor32(float v)
-{
-    float x, y;
-    pair_values<false>(v, x, y);
-    return x + y;
-}
-
 // Butterfly across lane bit 4 (XOR16) or bit 5 (XOR32 = false): the lane with
 // that bit clear gets lo + hi, its partner lo - hi.  first_lo says whether the
 // swap's first register holds the value of the lane with the bit clear (told

@@ -29,19 +29,6 @@ constexpr int kQuads = kCh / 4;               // threads sharing one split (a fl
 constexpr int kLanesS = kThreads / kQuads;    // splits read side by side
 constexpr float kNegInf = -__builtin_huge_valf();
 
-// Sum over the block (every thread returns the total).
-__device__ __forceinline__ float block_sum(float v, float* red)
-{
-    v = group_sum<64>(v);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
-    float r = red[0];
-#pragma unroll
-    for (int w = 1; w < kThreads / 64; ++w) r += red[w];
-    return r;
-}
-
 // In-place Walsh-Hadamard butterflies over one element per thread (threads
 // 0..D-1), stages in ascending stride: the lower element of a pair becomes
 // lower + upper, the upper one lower - upper.  Strides below 64 stay in the
@@ -183,18 +170,26 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             y = y * a.rot_norm;
         }
         const float kd = (float)ck[0] * sk;
-        s_new = block_sum(tid < DA ? y * kd : 0.0f, red_s) * a.qscale;
-        __syncthreads();  // xch is reused for V below
+        s_new = group_sum<64>(tid < DA ? y * kd : 0.0f);  // this wave's part of q' . k^
+        if (ROT && DA > 64) __syncthreads();  // the butterflies' last reads of xch are done
         if (tid < DA) xch[tid] = (float)cv[0] * sv;
+        if (lane == 0) red_s[wave] = s_new;
     }
 
-    // block maximum of the threads' references
+    // block maximum of the threads' references (and the new token's score:
+    // one LDS round for both)
     float M = group_max<64>(m);
     if (lane == 0) red_m[wave] = M;
     __syncthreads();
     M = red_m[0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) M = fmaxf(M, red_m[w]);
+    if constexpr (APPEND) {
+        s_new = red_s[0];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) s_new += red_s[w];
+        s_new *= a.qscale;  // log2 units
+    }
     const float f = (m == kNegInf) ? 0.0f : exp2_approx(m - M);
     o = make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
     l = (q == 0) ? l * f : 0.0f;  // the kQuads threads of a split group hold the same l

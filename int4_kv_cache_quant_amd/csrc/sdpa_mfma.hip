@@ -69,8 +69,10 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 // Headroom (base-2 exponent) the softmax reference keeps above the largest
-// score seen when it has to move.
-constexpr float kHeadroom = 2.0f;
+// score seen when it has to move: 4 makes the moves (and their rescale of
+// every accumulator) rare after the first tiles, while the largest p just
+// after a move, 2^-4, still leaves p * s_v far inside fp16's normal range.
+constexpr float kHeadroom = 4.0f;
 
 // MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
 // word, scaled by 2^(kShift[e] - 24): registers are (0,4), (1,5), (2,6),
@@ -186,6 +188,62 @@ __device__ __forceinline__ void dma16(const v4i_t& rsrc, int voffset, int soffse
         : "memory");
 }
 
+// All copies of one tile in one asm statement.  M0 (the LDS destination
+// base) is saved once and restored at the end; each run of 1 KB pieces of
+// one head and array shares one lane offset and one M0 value and steps by the
+// instruction's offset field, which moves the global and the LDS address
+// alike.  The V-scale resource starts 1 KB before the V scales, so that its
+// piece lands 1 KB after the K-scale piece under the same M0.  At one wave
+// per SIMD every instruction costs an issue slot: this takes 2 + 2 runs + the
+// copies, against 5 per copy with M0 saved around each.
+#define OTQ_M0(M) "s_mov_b32 m0, %[" M "]\n\ts_nop 0\n\t"
+#define OTQ_LD(VO, RS, SO, OFF) "buffer_load_dwordx4 %[" VO "], %[" RS "], %[" SO "] offen offset:" OFF " lds\n\t"
+#define OTQ_RUN1(M, VO, RS) OTQ_M0(M) OTQ_LD(VO, RS, "soc", "0")
+#define OTQ_RUN2(M, VO, RS) OTQ_RUN1(M, VO, RS) OTQ_LD(VO, RS, "soc", "1024")
+#define OTQ_RUN4(M, VO, RS) OTQ_RUN2(M, VO, RS) OTQ_LD(VO, RS, "soc", "2048") OTQ_LD(VO, RS, "soc", "3072")
+#define OTQ_SCALES OTQ_M0("ms") OTQ_LD("vs", "rks", "sos", "0") OTQ_LD("vs", "rvs", "sos", "1024")
+#define OTQ_DMA_OPS                                                                     \
+    : [sv] "=&s"(saved)                                                                 \
+    : [vk0] "v"(vk[0]), [vk1] "v"(vk[P - 1]), [vv0] "v"(vv[0]), [vv1] "v"(vv[P - 1]),  \
+      [vs] "v"(vs), [rk] "s"(rk), [rv] "s"(rv), [rks] "s"(rks), [rvs] "s"(rvs),        \
+      [soc] "s"(so_code), [sos] "s"(so_scale), [mk0] "s"(mk[0]), [mk1] "s"(mk[P - 1]), \
+      [mv0] "s"(mv[0]), [mv1] "s"(mv[P - 1]), [ms] "s"(ms)                             \
+    : "memory"
+template <int NA, int P>
+__device__ __forceinline__ void dma_tile_asm(const v4i_t& rk, const v4i_t& rv, const v4i_t& rks,
+                                             const v4i_t& rvs, const int (&vk)[P], const int (&vv)[P],
+                                             int vs, int so_code, int so_scale, const uint32_t (&mk)[P],
+                                             const uint32_t (&mv)[P], uint32_t ms)
+{
+    int saved;
+    if constexpr (NA == 1 && P == 1) {
+        asm volatile("s_mov_b32 %[sv], m0\n\t" OTQ_RUN1("mk0", "vk0", "rk") OTQ_RUN1("mv0", "vv0", "rv")
+                     OTQ_SCALES "s_mov_b32 m0, %[sv]" OTQ_DMA_OPS);
+    } else if constexpr (NA == 1 && P == 2) {
+        asm volatile("s_mov_b32 %[sv], m0\n\t" OTQ_RUN1("mk0", "vk0", "rk") OTQ_RUN1("mk1", "vk1", "rk")
+                     OTQ_RUN1("mv0", "vv0", "rv") OTQ_RUN1("mv1", "vv1", "rv")
+                     OTQ_SCALES "s_mov_b32 m0, %[sv]" OTQ_DMA_OPS);
+    } else if constexpr (NA == 2 && P == 1) {
+        asm volatile("s_mov_b32 %[sv], m0\n\t" OTQ_RUN2("mk0", "vk0", "rk") OTQ_RUN2("mv0", "vv0", "rv")
+                     OTQ_SCALES "s_mov_b32 m0, %[sv]" OTQ_DMA_OPS);
+    } else if constexpr (NA == 2 && P == 2) {
+        asm volatile("s_mov_b32 %[sv], m0\n\t" OTQ_RUN2("mk0", "vk0", "rk") OTQ_RUN2("mk1", "vk1", "rk")
+                     OTQ_RUN2("mv0", "vv0", "rv") OTQ_RUN2("mv1", "vv1", "rv")
+                     OTQ_SCALES "s_mov_b32 m0, %[sv]" OTQ_DMA_OPS);
+    } else {
+        static_assert(NA == 4 && P == 1, "tiles: head_dim 64 or 128 with one or two heads, 256 with one");
+        asm volatile("s_mov_b32 %[sv], m0\n\t" OTQ_RUN4("mk0", "vk0", "rk") OTQ_RUN4("mv0", "vv0", "rv")
+                     OTQ_SCALES "s_mov_b32 m0, %[sv]" OTQ_DMA_OPS);
+    }
+}
+#undef OTQ_DMA_OPS
+#undef OTQ_SCALES
+#undef OTQ_RUN4
+#undef OTQ_RUN2
+#undef OTQ_RUN1
+#undef OTQ_LD
+#undef OTQ_M0
+
 // One tile of the P KV heads, staged in LDS:
 //  [K_0 .. K_{P-1}][V_0 .. V_{P-1}][scales]
 // K_j: 32 rows x D/2 bytes as 16-byte chunks, chunk c of row t at slot
@@ -245,15 +303,32 @@ __device__ __forceinline__ void load_scales(float (&dst)[NG], const float* __res
     }
 }
 
-// One tile's loads for the P KV heads of the block.
-template <int D, int P>
+// One tile's loads for the P KV heads of the block.  K scales: with ROWS,
+// those of tokens 4 r + 0..3 of the lane's head (every lane of a row reads
+// the same 16 bytes, so no broadcast instruction is needed); otherwise only
+// token 4 r + (lane % 4), handed out by DPP quad broadcasts (fewer registers).
+template <int D, int P, bool ROWS>
 struct TileLoads {
     static constexpr int NG = D / kGroup;
-    uint32_t kw[P][2][NG];   // K code words: head, sub-tile, group
-    uint4 vw[P][D / 64];     // V tile words: head, 128-bit load
-    float sk[2][NG];         // K scales of token 4 r + (lane % 4) of the lane's head
-    float sv[2][NG];         // V scales, same token
+    uint32_t kw[P][2][NG];       // K code words: head, sub-tile, group
+    uint4 vw[P][D / 64];         // V tile words: head, 128-bit load
+    float sk[2][ROWS ? 4 : 1][NG];
+    float sv[2][NG];             // V scales of token 4 r + (lane % 4)
 };
+
+// K scales loaded per row where the registers allow it: not at head_dim 256
+// (eight groups per token) nor for two rotated heads, whose q operands
+// already fill the register file.
+template <int D, int P, bool ROT>
+constexpr bool kScaleRows = D <= 128 && !(ROT && P == 2);
+
+// Where a wave refills the stage it has just read: after the tile's scores
+// (the reads have finished by then, so the wait before the copies costs
+// nothing), except where keeping the copy operands live across the scores
+// would spill registers (head_dim 256, two rotated heads); those refill
+// before computing.
+template <int D, int P, bool ROT>
+constexpr bool kRefillAfterScores = D <= 128 && !(ROT && P == 2);
 
 // Waves per SIMD the register allocation must allow: 2 (up to 256 VGPRs)
 // except at head_dim 256, whose accumulators alone take 64 VGPRs per head.
@@ -284,6 +359,7 @@ void split_mfma_kernel(SplitArgs a)
 
     using St = Stage<D, P>;
     constexpr int NST = kStages<D, P, W>;
+    constexpr bool ROWS = kScaleRows<D, P, ROT>;
     static_assert((NST - 1) * St::COPIES <= 63, "vmcnt holds at most 63");
     const size_t head0 = (size_t)b * a.H + hk0;
     // the wave's LDS stages: stage s of wave w at (s W + w) * BYTES
@@ -316,9 +392,14 @@ void split_mfma_kernel(SplitArgs a)
     const v4i_t rs_k = make_rsrc(a.kc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
     const v4i_t rs_v = make_rsrc(a.vc + head0 * a.cap * (D / 2), P * a.cap * (D / 2));
     const v4i_t rs_ks = make_rsrc(a.ks + head0 * a.cap * NG, P * a.cap * NG * 4);
-    const v4i_t rs_vs = make_rsrc(a.vs + head0 * a.cap * NG, P * a.cap * NG * 4);
+    static_assert(St::SPAD == 1024, "one 1 KB piece per scale array");
+    const v4i_t rs_vs = make_rsrc(reinterpret_cast<const char*>(a.vs + head0 * a.cap * NG) - 1024,
+                                  P * a.cap * NG * 4 + 1024);
     // per-lane byte offsets of each copy instruction (tile-independent; the
-    // tile enters as the scalar offset tok0 * D/2, or tok0 * D/8 for scales)
+    // tile enters as the scalar offset tok0 * D/2, or tok0 * D/8 for scales).
+    // Piece i of one head and array lies 1024 i bytes after piece 0 both in
+    // memory and in LDS (k_unslot keeps the rotation of a row when its token
+    // moves by 16 or 8), which the copy runs rely on.
     int vo_k[P][D / 64], vo_v[P][D / 64], vo_s;
 #pragma unroll
     for (int j = 0; j < P; ++j)
@@ -336,22 +417,18 @@ void split_mfma_kernel(SplitArgs a)
 
     // issue the St::COPIES direct-to-LDS copies of tile it into stage st
     // (no registers held)
+    int vk0[P], vv0[P];
+#pragma unroll
+    for (int j = 0; j < P; ++j) { vk0[j] = vo_k[j][0]; vv0[j] = vo_v[j][0]; }
     auto dma_tile = [&](int it, int st) {
         const int tok0 = start + it * kTile;
         const int so_code = tok0 * (D / 2), so_scale = tok0 * NG * 4;
         const uint32_t base = lds_address(stage_of(st));
+        uint32_t mk[P], mv[P];
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-#pragma unroll
-            for (int i = 0; i < D / 64; ++i) dma16(rs_k, vo_k[j][i], so_code, base + St::koff(j) + 1024 * i);
-#pragma unroll
-            for (int i = 0; i < D / 64; ++i) dma16(rs_v, vo_v[j][i], so_code, base + St::voff(j) + 1024 * i);
-        }
-#pragma unroll
-        for (int i = 0; i < St::SPAD / 1024; ++i) {
-            dma16(rs_ks, vo_s + 1024 * i, so_scale, base + St::KSOFF + 1024 * i);
-            dma16(rs_vs, vo_s + 1024 * i, so_scale, base + St::VSOFF + 1024 * i);
-        }
+        for (int j = 0; j < P; ++j) { mk[j] = base + St::koff(j); mv[j] = base + St::voff(j); }
+        dma_tile_asm<D / 64, P>(rs_k, rs_v, rs_ks, rs_vs, vk0, vv0, vo_s, so_code, so_scale, mk, mv,
+                                base + St::KSOFF);
     };
 
     // The first tile of every wave streams in without waiting for lens[b] to
@@ -478,7 +555,7 @@ void split_mfma_kernel(SplitArgs a)
     for (int e = 0; e < 8; ++e) bcorr[e] = (_Float16)(kShift[e] ? 0x1p-17f : 0x1p-21f);
 
     // this lane's operands of the staged tile, into registers
-    auto read_stage = [&](TileLoads<D, P>& t, const char* stage) {
+    auto read_stage = [&](TileLoads<D, P, ROWS>& t, const char* stage) {
 #pragma unroll
         for (int j = 0; j < P; ++j) {
 #pragma unroll
@@ -505,12 +582,20 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int tt = 16 * s + 4 * r + slot;
-            load_scales<NG>(t.sk[s], reinterpret_cast<const float*>(stage + St::KSOFF) + (jl * 32 + tt) * NG);
+            if constexpr (ROWS) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    load_scales<NG>(t.sk[s][i], reinterpret_cast<const float*>(stage + St::KSOFF) +
+                                                    (jl * 32 + 16 * s + 4 * r + i) * NG);
+            } else {
+                load_scales<NG>(t.sk[s][0], reinterpret_cast<const float*>(stage + St::KSOFF) +
+                                                (jl * 32 + tt) * NG);
+            }
             load_scales<NG>(t.sv[s], reinterpret_cast<const float*>(stage + St::VSOFF) + (jl * 32 + tt) * NG);
         }
     };
 
-    auto compute_tile = [&](const TileLoads<D, P>& t, int it) {
+    auto compute_tile = [&](const TileLoads<D, P, ROWS>& t, int it, auto&& after_scores) {
         const int tok0 = start + it * kTile;
         // ---- scores, as T = S / qmul (qmul > 0 is applied inside exp2)
         float T[2][4];
@@ -528,13 +613,16 @@ void split_mfma_kernel(SplitArgs a)
                 }
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
-                    const float term = quad_bcast<i>(t.sk[s][g]) * d[i];  // folds into v_mul_f32_dpp
+                    float term;
+                    if constexpr (ROWS) term = t.sk[s][i % (ROWS ? 4 : 1)][g] * d[i];
+                    else term = quad_bcast<i>(t.sk[s][0][g]) * d[i];  // folds into v_mul_f32_dpp
                     tot[i] = (g == 0) ? term : tot[i] + term;
                 });
             });
 #pragma unroll
             for (int i = 0; i < 4; ++i) T[s][i] = tot[i];
         }
+        after_scores();
         if (tok0 + kTile > end) {  // wave-uniform: the chunk's last, partial tile
 #pragma unroll
             for (int s = 0; s < 2; ++s)
@@ -638,14 +726,21 @@ void split_mfma_kernel(SplitArgs a)
             if (n_after == k) __builtin_amdgcn_s_waitcnt(wait_vm(k * St::COPIES));
         });
         asm volatile("" ::: "memory");  // the stage's reads stay after the wait
-        TileLoads<D, P> t;
+        TileLoads<D, P, ROWS> t;
         read_stage(t, stage_of(st));
-        if (it + NST * W < ntiles) {
-            // the copies overwrite the stage just read: let the reads finish
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            dma_tile(it + NST * W, st);
+        // the copies overwrite the stage just read: its reads must have finished
+        auto refill = [&] {
+            if (it + NST * W < ntiles) {
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                dma_tile(it + NST * W, st);
+            }
+        };
+        if constexpr (kRefillAfterScores<D, P, ROT>) {
+            compute_tile(t, it, refill);
+        } else {
+            refill();
+            compute_tile(t, it, [] {});
         }
-        compute_tile(t, it);
         st = (st + 1 == NST) ? 0 : st + 1;
     }
     __syncthreads();  // every wave is done with its stage before the merge reuses LDS

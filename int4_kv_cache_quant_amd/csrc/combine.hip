@@ -69,31 +69,26 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     __shared__ float red_s[kThreads / 64];
     __shared__ float xch[DA > 0 ? DA : 1];   // butterflies, then the new token's V
     constexpr bool APPEND = DA > 0;
+    // every argument the loads below need, fetched together: otherwise the
+    // fields arrive one scalar round trip after another, each gating the next
+    // address
+    asm volatile("" ::"s"(a.part_o), "s"(a.part_ml), "s"(a.lens), "s"(a.S), "s"(a.Hq), "s"(a.D),
+                 "s"(a.k_new), "s"(a.v_new), "s"(a.q), "s"(a.H), "s"(a.signs));
     const int D = APPEND ? DA : a.D;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = row / a.Hq;
     const int q = tid % kQuads, g = tid / kQuads;
     const int c = kCh * blockIdx.y + 4 * q;
-    const int len = min(max(a.lens[b], 0), a.max_len);
-    const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
-    const int ns = (nsplit_tok + a.chunk - 1) / a.chunk;
-    float4* dst = reinterpret_cast<float4*>(a.out + (size_t)row * D + c);
-    if (len == 0) {  // block-uniform: nothing attended, nothing appended
-        if (tid < kQuads) *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        return;
-    }
-
-    // the new token's K, V and this row's q: one channel per thread (threads
-    // past D work on channel D - 1 and write nothing)
+    // the new token's K, V and this row's q (one channel per thread; threads
+    // past D work on channel D - 1 and write nothing), loaded before lens[b]
+    // like the first splits below
     [[maybe_unused]] uint16_t kx = 0, vx = 0, qx = 0;
     [[maybe_unused]] float sg = 1.0f;
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
-    [[maybe_unused]] uint8_t vold = 0;
     if constexpr (APPEND) {
         const int G = a.Hq / a.H, h = row % a.Hq;
         kvh = h / G;
-        pos = len - 1;
         ch = min(tid, DA - 1);
         const size_t src = ((size_t)b * a.H + kvh) * DA + ch;
         kx = a.k_new[src];
@@ -103,14 +98,34 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         // one block per KV head writes the token: the first query head's,
         // first channel slice
         writer = h % G == 0 && blockIdx.y == 0 && tid < DA;
-        if (writer)
-            vold = a.vc[(((size_t)b * a.H + kvh) * (a.cap / kTile) + pos / kTile) * (size_t)(16 * DA) +
-                        v_tile_byte<DA>(ch, (pos % kTile) & ~1)];
+    }
+
+    // The first two splits of each thread (g and g + 32) are loaded before
+    // lens[b] is known, as far as the workspace holds them (the plan's split
+    // count), and folded below only if the split pass wrote them: these
+    // loads do not wait for the length's round trip.
+    const float2* ml = a.part_ml + (size_t)row * a.S;
+    const float* po = a.part_o + (size_t)row * a.S * D + c;
+    float2 v0 = make_float2(0.0f, 0.0f), v1 = v0;
+    float4 x0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), x1 = x0;
+    if (a.S > 0) {
+        const int s0 = min(g, a.S - 1), s1 = min(g + kLanesS, a.S - 1);
+        v0 = ml[s0];
+        v1 = ml[s1];
+        x0 = *reinterpret_cast<const float4*>(po + (size_t)s0 * D);
+        x1 = *reinterpret_cast<const float4*>(po + (size_t)s1 * D);
+    }
+    const int len = min(max(a.lens[b], 0), a.max_len);
+    const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
+    const int ns = (nsplit_tok + a.chunk - 1) / a.chunk;
+    if constexpr (APPEND) pos = len - 1;
+    float4* dst = reinterpret_cast<float4*>(a.out + (size_t)row * D + c);
+    if (len == 0) {  // block-uniform: nothing attended, nothing appended
+        if (tid < kQuads) *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        return;
     }
 
     // ---- the splits
-    const float2* ml = a.part_ml + (size_t)row * a.S;
-    const float* po = a.part_o + (size_t)row * a.S * D + c;
     float m = kNegInf, l = 0.0f;
     float4 o = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     auto fold = [&](float2 v, float4 x) {  // every written partial has a finite m
@@ -120,7 +135,9 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         l = l * al + v.y * w;
         m = mn;
     };
-    int s = g;
+    if (g < ns) fold(v0, x0);
+    if (g + kLanesS < ns) fold(v1, x1);
+    int s = g + 2 * kLanesS;
     for (; s + kLanesS < ns; s += 2 * kLanesS) {  // two splits in flight per thread
         const float2 v0 = ml[s], v1 = ml[s + kLanesS];
         const float4 x0 = *reinterpret_cast<const float4*>(po + (size_t)s * D);
@@ -153,10 +170,18 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             const int cnext = __shfl_xor(ck[0], 1, 64);
             if ((ch & 1) == 0)
                 a.kc[krow * (DA / 2) + k_row_byte<DA>(ch)] = (uint8_t)((ck[0] & 0xF) | ((cnext & 0xF) << 4));
-            const uint32_t nib = (uint32_t)cv[0] & 0xF;
-            a.vc[(head * (a.cap / kTile) + pos / kTile) * (size_t)(16 * DA) +
-                 v_tile_byte<DA>(ch, (pos % kTile) & ~1)] =
-                (uint8_t)((pos & 1) ? ((vold & 0x0F) | (nib << 4)) : ((vold & 0xF0) | nib));
+            // the V byte is shared with token pos ^ 1: replace only this
+            // token's nibble, by clearing and setting it with two atomics on
+            // the containing word (no read to wait for; the other nibbles of
+            // the word are other channels' and other tokens', and the same
+            // thread's two operations on one word take effect in order)
+            const size_t vbyte = (head * (a.cap / kTile) + pos / kTile) * (size_t)(16 * DA) +
+                                 v_tile_byte<DA>(ch, (pos % kTile) & ~1);
+            const int shift = 8 * (int)(vbyte & 3) + 4 * (pos & 1);
+            unsigned* vword = reinterpret_cast<unsigned*>(a.vc + (vbyte & ~(size_t)3));
+            __hip_atomic_fetch_and(vword, ~(0xFu << shift), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_fetch_or(vword, ((unsigned)cv[0] & 0xFu) << shift, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
             if (ch % kGroup == 0) {
                 a.ks[krow * (DA / kGroup) + ch / kGroup] = sk;
                 a.vs[krow * (DA / kGroup) + ch / kGroup] = sv;

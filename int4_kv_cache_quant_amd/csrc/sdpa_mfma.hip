@@ -362,8 +362,10 @@ void split_mfma_kernel(SplitArgs a)
     constexpr bool ROWS = kScaleRows<D, P, ROT>;
     static_assert((NST - 1) * St::COPIES <= 63, "vmcnt holds at most 63");
     const size_t head0 = (size_t)b * a.H + hk0;
-    // the wave's LDS stages: stage s of wave w at (s W + w) * BYTES
-    auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (st * W + wave) * St::BYTES; };
+    // the wave's LDS stages, contiguous per wave: stage s of wave w at
+    // (w NST + s) * BYTES; after its last tile a wave's stages hold its
+    // share of the merge
+    auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (wave * NST + st) * St::BYTES; };
 
     // sequence length first, as a scalar load: nothing has been written yet
     const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
@@ -743,19 +745,23 @@ void split_mfma_kernel(SplitArgs a)
         }
         st = (st + 1 == NST) ? 0 : st + 1;
     }
-    __syncthreads();  // every wave is done with its stage before the merge reuses LDS
 
     // ---- merge: l over the 4 rows of each column (m and O are already
-    //      wave-wide), then the W waves, through LDS rows padded by 4 floats
-    //      so that the 4 rows of a wave's stores fall in distinct banks
+    //      wave-wide), then the W waves.  Each wave leaves its (m, l) and its
+    //      O rows in its own stages, which no copy targets any more (every
+    //      copy it issued has been waited for), so it need not wait for the
+    //      other waves first; rows are padded by 4 floats so that the 4 rows
+    //      of a store fall in distinct banks.
     constexpr int RS = D + 4;
+    static_assert(16 * RS * 4 + 16 * 8 <= NST * St::BYTES, "a wave's merge share fits its stages");
+    auto merge_o = [&](int w) { return reinterpret_cast<float*>(lds) + w * (NST * St::BYTES / 4); };
+    auto merge_ml = [&](int w) { return reinterpret_cast<float2*>(merge_o(w) + 16 * RS); };
     const float L = sum_xor32(sum_xor16(l_lane));
-    float* merge_o = lds;                                            // [W][16][RS]
-    float2* merge_ml = reinterpret_cast<float2*>(lds + W * 16 * RS);  // [W][16]
-    if (lane < 16) merge_ml[wave * 16 + lane] = make_float2(m_run, L);
+    if (lane < 16) merge_ml(wave)[lane] = make_float2(m_run, L);
     // rows 4 r .. 4 r + 3 of O lie in one KV head (two heads only if G >= 4):
     // keep that head's set
     const int jr = min(4 * r / G, P - 1);
+    float* own = merge_o(wave);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
@@ -765,19 +771,24 @@ void split_mfma_kernel(SplitArgs a)
                 float v = acc[0][cb][i];
 #pragma unroll
                 for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
-                merge_o[(wave * 16 + h) * RS + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
+                own[h * RS + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
             }
         }
     }
     __syncthreads();
-    // one thread per (head, 4 channels)
-    for (int i = tid; i < PG * (D / 4); i += 64 * W) {
+    // one thread per (head, 4 channels); the iterations are unrolled so
+    // that their LDS reads are in flight together
+    constexpr int kMergeIters = (16 * (D / 4) + 64 * W - 1) / (64 * W);
+#pragma unroll
+    for (int k = 0; k < kMergeIters; ++k) {
+        const int i = tid + k * 64 * W;
+        if (i >= PG * (D / 4)) break;
         const int h = i / (D / 4), c = 4 * (i % (D / 4));
         float2 ml[W];
         float Mb = kNegInf;
 #pragma unroll
         for (int w = 0; w < W; ++w) {
-            ml[w] = merge_ml[w * 16 + h];
+            ml[w] = merge_ml(w)[h];
             Mb = fmaxf(Mb, ml[w].x);
         }
         float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -785,7 +796,7 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
         for (int w = 0; w < W; ++w) {
             const float f = (ml[w].x == kNegInf) ? 0.0f : exp2_approx(ml[w].x - Mb);
-            const float4 x = *reinterpret_cast<const float4*>(merge_o + (w * 16 + h) * RS + c);
+            const float4 x = *reinterpret_cast<const float4*>(merge_o(w) + h * RS + c);
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
             Ls += f * ml[w].y;
         }
@@ -807,9 +818,8 @@ template <int D, int P, bool ROT>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)
 {
     constexpr int W = kBlockWaves<D>;
-    const size_t merge_bytes = (size_t)W * 16 * ((D + 4) * sizeof(float) + sizeof(float2));
-    const size_t stage_bytes = (size_t)kStages<D, P, W> * W * Stage<D, P>::BYTES;
-    const size_t lds = stage_bytes > merge_bytes ? stage_bytes : merge_bytes;
+    // the merge lives in the stages (checked in the kernel)
+    const size_t lds = (size_t)kStages<D, P, W> * W * Stage<D, P>::BYTES;
     dim3 grid(a.num_splits, a.H / P, a.B), block(64 * W);
     static const hipError_t attr = hipFuncSetAttribute(
         reinterpret_cast<const void*>(&split_mfma_kernel<D, P, ROT, W>),

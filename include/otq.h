@@ -239,12 +239,20 @@ int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_
  *           round_up(B*Hq*num_splits*D*4, 256)
  * where split s covers tokens [s*chunk, min((s+1)*chunk, lens[b])), m is the
  * split's softmax reference in log2 units (score * log2(e)): at least its
- * largest score, and at most 2 above it, l = sum 2^(S*log2e - m) and
+ * largest score, and at most 4 above it, l = sum 2^(S*log2e - m) and
  * o = sum 2^(S*log2e - m) V^ (any such m gives the same merged result).
  * Splits with s*chunk >= lens[b] are not
  * written.  otq_sdpa_lse_combine merges the first ceil(lens[b]/chunk)
  * partials of each row into out.  Arguments and errors as for
  * otq_sdpa_int4_decode_planned.
+ *
+ * For a batch of 2..256 sequences the split pass is two launches: a
+ * one-workgroup kernel first writes, at byte offset
+ * round_up(part_ml offset + B*Hq*num_splits*8, 256) of the workspace, which
+ * work item (split, sequence) each split workgroup takes, longest first
+ * (the full chunks, then the last partial chunks by decreasing length), so
+ * that the hardware's in-order start of workgroups balances sequences of
+ * unequal length.  The partials are the same either way.
  */
 int otq_sdpa_int4_split(const void *q, int32_t dtype, int32_t num_q_heads,
                         const otq_cache *cache, const int32_t *lens, int32_t max_len,

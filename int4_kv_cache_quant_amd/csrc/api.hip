@@ -16,6 +16,7 @@ namespace {
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
 constexpr int kMaxChunk = 8192;  // measured: larger chunks starve the grid on ragged batches
 constexpr int kTargetWaves = 1024;  // split waves aimed for (one per SIMD)
+constexpr int kOrderedWaveFactor = 8;  // measured on the ragged 32-sequence batch: chunk 2048 over 8192
 constexpr int kMaxSplits = 16384;
 
 bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
@@ -38,6 +39,10 @@ int check_cache(const otq_cache* c)
     if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) return OTQ_EINVAL;
     return OTQ_OK;
 }
+
+// Batches whose split blocks take their items longest first (one sequence
+// needs no order: its chunks are equal but the last).
+bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
 int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
               int32_t variant_ov, otq_plan* p)
@@ -74,7 +79,10 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
             waves = otq::split_mfma_block_waves(D);
             align = waves * OTQ_TILE;  // one tile per wave and round
         }
-        const long long groups = kTargetWaves / waves;
+        // a batch takes its items longest first, which balances unequal
+        // lengths better the more (smaller) items there are
+        const long long target = ordered_batch(c->batch) ? kTargetWaves * kOrderedWaveFactor : kTargetWaves;
+        const long long groups = target / waves;
         long long want = ((long long)max_len * units + groups - 1) / groups;
         want = (want + align - 1) / align * align;
         if (want < kChunkAlign) want = kChunkAlign;
@@ -88,7 +96,12 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     const unsigned __int128 rows = (unsigned __int128)c->batch * Hq * S;
     const unsigned __int128 o_bytes = rows * D * sizeof(float);
     const unsigned __int128 o_aligned = (o_bytes + 255) / 256 * 256;
-    const unsigned __int128 total = o_aligned + rows * 2 * sizeof(float);
+    const unsigned __int128 ml_aligned = (rows * 2 * sizeof(float) + 255) / 256 * 256;
+    // a batch also holds the split blocks' longest-first items: (split,
+    // sequence) per block, at most S * Hkv * B blocks
+    const unsigned __int128 order_bytes =
+        ordered_batch(c->batch) ? (unsigned __int128)S * c->num_kv_heads * c->batch * 2 * sizeof(int32_t) : 0;
+    const unsigned __int128 total = o_aligned + ml_aligned + order_bytes;
     if (total > ((unsigned __int128)1 << 62)) return OTQ_EINVAL;
     p->chunk = chunk;
     p->num_splits = (int32_t)S;
@@ -180,6 +193,12 @@ size_t ml_offset(const otq_cache* c, int32_t Hq, const otq_plan& p)
     return (rows * c->head_dim * sizeof(float) + 255) / 256 * 256;
 }
 
+size_t order_offset(const otq_cache* c, int32_t Hq, const otq_plan& p)
+{
+    const size_t rows = (size_t)c->batch * Hq * p.num_splits;
+    return ml_offset(c, Hq, p) + (rows * 2 * sizeof(float) + 255) / 256 * 256;
+}
+
 // Validates a caller plan against the shape; on success *chk is the plan.
 int check_plan(int32_t Hq, const otq_cache* c, int32_t max_len, const otq_plan* plan,
                otq_plan* chk)
@@ -216,6 +235,18 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
                                           ml_offset(cache, num_q_heads, chk));
     a.lens_offset = lens_offset;
+    a.items = nullptr;
+    if (ordered_batch(a.B)) {
+        const int groups = chk.variant == OTQ_VARIANT_MFMA
+                               ? a.H / otq::split_mfma_heads_per_wave(D, num_q_heads / a.H, a.H)
+                               : a.H;
+        int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
+                                              order_offset(cache, num_q_heads, chk));
+        if (otq::launch_split_order(lens, lens_offset, max_len, chk.chunk, chk.num_splits, groups, a.B,
+                                    items, s) != hipSuccess)
+            return OTQ_EDEVICE;
+        a.items = items;
+    }
     const hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
                                                          : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;

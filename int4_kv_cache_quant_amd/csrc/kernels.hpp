@@ -31,6 +31,10 @@ struct SplitArgs {
     int num_splits;
     float* part_o;   // [B][Hq][S][D]
     float2* part_ml; // [B][Hq][S] (m, l)
+    // block k = x + S (y + groups z) takes item items[k] = (split, sequence)
+    // with KV-head group k % groups (longest first, written by the order
+    // kernel), or null: block (x, y, z) takes split x of group y of sequence z
+    const int2* items;
     // 1 when the token at lens[b] - 1 is appended by the combine of the same
     // call (the split pass then covers [0, lens[b] - 1)), else 0.
     int lens_offset;
@@ -38,6 +42,12 @@ struct SplitArgs {
 
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
 hipError_t launch_split_vector(const SplitArgs& a, hipStream_t stream);
+// Largest batch whose split blocks are ordered longest first.
+constexpr int kOrderMaxBatch = 256;
+// Writes items[S * groups * B] for batches of 2..kOrderMaxBatch sequences
+// (see SplitArgs::items).
+hipError_t launch_split_order(const int32_t* lens, int lens_offset, int max_len, int chunk, int S,
+                              int groups, int B, int2* items, hipStream_t stream);
 hipError_t launch_split_mfma(const SplitArgs& a, hipStream_t stream);
 bool split_vector_supports(int D, int G);
 bool split_mfma_supports(int D, int G);

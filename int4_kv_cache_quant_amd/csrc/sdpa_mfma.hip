@@ -349,7 +349,16 @@ void split_mfma_kernel(SplitArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
-    const int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
+    int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
+    if (a.items) {  // a batch: the block's item in longest-first order
+        const int groups = a.H / P;
+        const int k = blockIdx.x + a.num_splits * (blockIdx.y + groups * blockIdx.z);
+        const int2 it = a.items[k];
+        if (it.x < 0) return;  // block-uniform: no item
+        split = it.x;
+        b = it.y;
+        hk0 = (k % groups) * P;
+    }
     const int G = a.Hq / a.H;
     const int PG = P * G;  // query heads served by the block (<= 16)
     const int start = split * a.chunk;

@@ -62,7 +62,15 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar loop control
-    const int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    if (a.items) {  // a batch: the block's item in longest-first order
+        const int k = blockIdx.x + a.num_splits * (blockIdx.y + a.H * blockIdx.z);
+        const int2 it = a.items[k];
+        if (it.x < 0) return;  // block-uniform: no item
+        split = it.x;
+        b = it.y;
+        hk = k % a.H;
+    }
     const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for empty chunks

@@ -136,6 +136,33 @@ def test_sdpa_split_invariance(chunk, variant, Hq):
     assert ma <= MAX_ABS and rel <= REL_L2
 
 
+@pytest.mark.parametrize("variant,Hq,rotate", [(VEC, 4, False), (MF, 8, False), (MF, 8, True)])
+def test_sdpa_ragged_batch_order(variant, Hq, rotate):
+    """A batch takes its split items longest first (an order kernel writes
+    the block -> item table): empty sequences, one token, exact chunk
+    multiples and partial chunks of every size, in a mixed order."""
+    lens = [0, 1, 128, 129, 383, 256, 32, 300, 127, 384, 255, 2]
+    got, ref, plan = _run(len(lens), Hq, 2, 128, 384, lens, chunk=128, variant=variant, seed=21,
+                          rotate=rotate)
+    assert plan.num_splits == 3
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("B", [64, 257])
+def test_sdpa_ragged_batch_sizes(B):
+    """A larger batch in longest-first order (64) and one past the order
+    kernel's limit of 256 (257: blocks keep the grid order)."""
+    rng = np.random.default_rng(B)
+    lens = [int(x) for x in rng.integers(0, 161, size=B)]
+    rows = np.arange(0, B * 4, 7, dtype=np.int32)
+    got, ref, plan = _run(B, 4, 1, 64, 160, lens, chunk=128, variant=MF, seed=B, rows=rows)
+    ma, rel = errors(got, ref)
+    say(f"  B={B} max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
 def test_sdpa_fp16_rotated_and_scale_one():
     got, ref, _ = _run(3, 4, 2, 128, 256, [256, 200, 9], dtype=torch.float16, seed=3, rotate=True)
     ma, rel = errors(got, ref)

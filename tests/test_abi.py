@@ -80,6 +80,22 @@ def test_quantize_append_host_errors():
     assert lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, None, P(FAKE), None) == otq.OTQ_EINVAL
 
 
+def test_plan_batch_order_table():
+    """A batch of 2..256 sequences plans finer chunks (its split blocks take
+    their items longest first) and its workspace ends with the item table,
+    8 bytes per split block; one sequence, or more than 256, has no table."""
+    ru = lambda x: -(-x // 256) * 256
+    for B, table in ((1, False), (2, True), (32, True), (256, True), (257, False)):
+        d = _desc(B=B, H=8, D=128, cap=32768)
+        p = otq.otq_sdpa_plan(32, d, 32768)
+        rows = B * 32 * p.num_splits
+        want = ru(rows * 128 * 4) + ru(rows * 8) + (p.num_splits * 8 * B * 8 if table else 0)
+        assert p.workspace_bytes == want, (B, p.workspace_bytes, want)
+    # the ragged workload's shape: chunk 2048 (8x the waves of one sequence)
+    assert otq.otq_sdpa_plan(32, _desc(B=32, H=8, D=128, cap=32768), 32768).chunk == 2048
+    assert otq.otq_sdpa_plan(32, _desc(B=1, H=8, D=128, cap=32768), 32768).chunk == 512
+
+
 def test_plan_defaults_and_errors():
     d = _desc(B=1, H=8, D=128, cap=131072)
     p = otq.otq_sdpa_plan(64, d, 131072)

@@ -125,14 +125,15 @@ size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
  * into the cache at token positions pos[b] + t, t = 0..n_new-1 (Open-TQ-Metal
  * abstract: the cache is quantised to int4 on the fly).
  *
- *  k, v   device [B][H][n_new][D] fp16 or bf16 (dtype), contiguous.
+ *  k, v   device [B][H][n_new][D] fp16 or bf16 (dtype), contiguous and
+ *         16-byte aligned (read 8 channels at a time).
  *  pos    device int32 [B].  Contract: 0 <= pos[b] and
  *         pos[b] + n_new <= capacity.  Tokens that fall outside
  *         [0, capacity) are skipped (never written out of bounds).
  *  Codes and scales of every token not in the range are left untouched,
  *  including the neighbour that shares a V byte with a new token.
- *  Host errors: OTQ_EINVAL (null pointer, n_new < 1, bad dtype),
- *  OTQ_EUNSUPPORTED (head_dim), OTQ_ECAPACITY (n_new > capacity).
+ *  Host errors: OTQ_EINVAL (null pointer, misaligned k or v, n_new < 1,
+ *  bad dtype), OTQ_EUNSUPPORTED (head_dim), OTQ_ECAPACITY (n_new > capacity).
  */
 int otq_quantize_append(const void *k, const void *v, int32_t dtype, int32_t n_new,
                         const otq_cache *cache, const int32_t *pos, void *stream);

@@ -154,6 +154,8 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     const int rc = check_cache(cache);
     if (rc != OTQ_OK) return rc;
     if (!k || !v || !pos || n_new < 1) return OTQ_EINVAL;
+    // the kernel reads 8 channels per 16-byte load
+    if ((((uintptr_t)k) & 15) != 0 || (((uintptr_t)v) & 15) != 0) return OTQ_EINVAL;
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (n_new > cache->capacity) return OTQ_ECAPACITY;
     const hipError_t e = otq::launch_quantize_append(

@@ -1,6 +1,7 @@
-// quant_lane.hpp - the int4 quantiser of one vector by one wave, and the
-// byte positions of the cache layouts.  Shared by the append kernel and by
-// the split kernel's fused one-token append, so both write identical codes.
+// quant_lane.hpp - the int4 quantiser of a vector spread over a group of
+// lanes, and the byte positions of the cache layouts.  Shared by the append
+// kernel and by the combine's fused one-token append, so both write
+// identical codes.
 //
 // Every step is one IEEE fp32 operation with round-to-nearest-even (the
 // bodies forbid contraction into FMAs whatever the file's flags), so the codes
@@ -11,42 +12,50 @@
 
 namespace otq {
 
-// One wave quantises one vector of D elements; lane l owns elements
-// [l*E, l*E + E), E = D / 64.  Returns codes in [-8, 7] in c[] and the scale
-// of the lane's group (a group spans 32 / E lanes).
-template <int D>
-__device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 64], int lane)
+// E consecutive elements per lane, a scale group spanning the 32 / E
+// consecutive lanes of an aligned lane group: returns codes in [-8, 7] in
+// c[] and the scale of the lane's group.
+template <int E>
+__device__ __forceinline__ float quantize_elems(float (&x)[E], int (&c)[E])
 {
 #pragma clang fp contract(off)
-    constexpr int E = D / 64;
     constexpr int LANES_PER_GROUP = kGroup / E;
     float a = 0.0f;
 #pragma unroll
     for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
     a = group_max<LANES_PER_GROUP>(a);  // exact in any order
     const float s = a / 7.0f;  // correctly rounded IEEE division
+    // branch-free: with s == 0 the quotient is infinite or NaN, the clamp
+    // turns it into -8 or 7 (fmax ignores a NaN operand), and the select
+    // gives 0
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-        int code = 0;
-        if (s != 0.0f) {
-            float r = rintf(x[e] / s);  // v_rndne_f32: half to even
-            r = fminf(fmaxf(r, -8.0f), 7.0f);
-            code = (int)r;
-        }
-        c[e] = code;
+        float r = rintf(x[e] / s);  // correctly rounded IEEE division, then v_rndne_f32: half to even
+        r = fminf(fmaxf(r, -8.0f), 7.0f);
+        c[e] = s != 0.0f ? (int)r : 0;
     }
     return s;
+}
+
+// One wave quantises one vector of D elements; lane l owns elements
+// [l*E, l*E + E), E = D / 64.
+template <int D>
+__device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 64], int /*lane*/)
+{
+    return quantize_elems<D / 64>(x, c);
 }
 
 // y <- rot_norm * H (signs (.) y), Sylvester order, stages in ascending
 // stride; a butterfly replaces (lower, upper) with (lower + upper,
 // lower - upper) exactly as the in-place fast Walsh-Hadamard transform does.
-template <int D>
-__device__ __forceinline__ void rotate_lane(float (&y)[D / 64], const float* __restrict__ signs,
-                                            float rot_norm, int lane)
+// A vector of D elements spread over D / E consecutive lanes (an aligned
+// lane group), E consecutive elements per lane; `lane` is the lane's index
+// within its group.
+template <int D, int E>
+__device__ __forceinline__ void rotate_elems(float (&y)[E], const float* __restrict__ signs,
+                                             float rot_norm, int lane)
 {
 #pragma clang fp contract(off)
-    constexpr int E = D / 64;
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = y[e] * signs[lane * E + e];
 #pragma unroll
@@ -72,6 +81,14 @@ __device__ __forceinline__ void rotate_lane(float (&y)[D / 64], const float* __r
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
+}
+
+// One wave rotates one vector: lane l owns elements [l*E, l*E + E), E = D / 64.
+template <int D>
+__device__ __forceinline__ void rotate_lane(float (&y)[D / 64], const float* __restrict__ signs,
+                                            float rot_norm, int lane)
+{
+    rotate_elems<D, D / 64>(y, signs, rot_norm, lane);
 }
 
 // Byte offset, inside one K row, of the byte holding even channel c and

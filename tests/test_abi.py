@@ -70,6 +70,8 @@ def test_quantize_append_host_errors():
     assert call(0, FAKE, 1, 1, d, FAKE) == otq.OTQ_EINVAL
     assert call(FAKE, FAKE, 1, 1, d, 0) == otq.OTQ_EINVAL
     assert call(FAKE, FAKE, 1, 0, d, FAKE) == otq.OTQ_EINVAL
+    assert call(FAKE + 2, FAKE, 1, 1, d, FAKE) == otq.OTQ_EINVAL   # k, v read 16 bytes at a time
+    assert call(FAKE, FAKE + 8, 1, 1, d, FAKE) == otq.OTQ_EINVAL
     assert call(FAKE, FAKE, 2, 1, d, FAKE) == otq.OTQ_EUNSUPPORTED
     assert call(FAKE, FAKE, 1, 65, d, FAKE) == otq.OTQ_ECAPACITY
     assert call(FAKE, FAKE, 1, 1, _desc(D=96), FAKE) == otq.OTQ_EUNSUPPORTED

@@ -5,7 +5,9 @@
 //
 // Every step is one IEEE fp32 operation with round-to-nearest-even (the
 // bodies forbid contraction into FMAs whatever the file's flags), so the codes
-// and scales are bit-identical to any correct evaluation of the same steps.
+// and scales are bit-identical to any correct evaluation of the same steps
+// (quantize_word8 reaches the same correctly rounded quotients by another
+// sequence of exactly rounded operations).
 #pragma once
 
 #include "common.hpp"
@@ -35,6 +37,55 @@ __device__ __forceinline__ float quantize_elems(float (&x)[E], int (&c)[E])
         c[e] = s != 0.0f ? (int)r : 0;
     }
     return s;
+}
+
+// Eight consecutive elements per lane, a scale group spanning an aligned quad
+// of lanes: returns the 8 codes packed as one word (nibble e = code of x[e],
+// two's complement) and the group's scale in `scale`.  The same codes as
+// quantize_elems, with fewer operations for the lane's 8 divisions by s:
+//  - x / s is rounded correctly from one correctly rounded reciprocal y =
+//    RN(1 / s) per group (Markstein's division: P. Markstein, IBM J. Res.
+//    Dev. 34(1), 1990).  q = RN(x y) is within 1.5 ulp of x / s; a
+//    correction q <- RN(q + RN(x - q s) y) makes it faithful, and from a
+//    faithful q the remainder x - q s is exact, so a second correction rounds
+//    it correctly (Markstein's theorem, y within half an ulp of 1 / s).  The
+//    bounds on s keep 1 / s normal and every remainder above the subnormal
+//    range whenever |x / s| >= 2^-13; smaller quotients are not exact but
+//    stay far below 1/2, so their code (0) is unchanged.
+//  - |x| <= a and s = RN(a / 7) give |x / s| <= 7 (1 + 2^-23): the clamp
+//    never acts, and adding 1.5 * 2^23 rounds q to an integer, half to even
+//    (1.5 * 2^23 is even and the sum's ulp is 1), leaving the code in the low
+//    bits of the sum's encoding.
+// Zero, huge, infinite or NaN scales and scales below 2^-90 divide element
+// by element as quantize_elems does.
+__device__ __forceinline__ uint32_t quantize_word8(const float (&x)[8], float& scale)
+{
+#pragma clang fp contract(off)
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+    a = group_max<4>(a);  // exact in any order
+    const float s = a / 7.0f;  // correctly rounded IEEE division
+    scale = s;
+    uint32_t word = 0;
+    if (s >= 0x1p-90f && s <= 0x1p100f) {
+        const float y = 1.0f / s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float q = x[e] * y;
+            q = __builtin_fmaf(__builtin_fmaf(-q, s, x[e]), y, q);
+            q = __builtin_fmaf(__builtin_fmaf(-q, s, x[e]), y, q);
+            word |= (__builtin_bit_cast(uint32_t, q + 0x1.8p23f) & 0xFu) << (4 * e);
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            float r = rintf(x[e] / s);  // correctly rounded IEEE division, then half to even
+            r = fminf(fmaxf(r, -8.0f), 7.0f);
+            word |= ((uint32_t)(s != 0.0f ? (int)r : 0) & 0xFu) << (4 * e);
+        }
+    }
+    return word;
 }
 
 // One wave quantises one vector of D elements; lane l owns elements

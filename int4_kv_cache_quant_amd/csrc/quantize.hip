@@ -109,99 +109,122 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     }
 }
 
-// Lane layout: each token of the wave occupies LT = D / 8 consecutive lanes,
-// and lane j of a token holds its 8 consecutive channels 8 j .. 8 j + 7 (one
-// 16-byte load).  A scale group (32 channels) is then one aligned quad of
-// lanes, and a lane's 8 codes are exactly one 32-bit word of the K row
-// (quarter-interleaved: word r NG + g holds channels 32 g + 8 r + 0..7).
-// A wave covers TW = 64 / LT tokens starting at an even position, so the two
-// tokens sharing a V byte are in the wave, LT lanes apart.
-template <int D>
-__global__ __launch_bounds__(256) void quantize_append_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new,
+// One block per 32-token V tile of one head, so that every byte of the tile,
+// of its 32 K rows and of their scales is written from one CU (one L2) as
+// whole words.
+//
+// K: each token occupies LT = D / 8 consecutive lanes, lane j of a token
+// holding its channels 8 j .. 8 j + 7 (one 16-byte load).  A scale group
+// (32 channels) is then one aligned quad of lanes, and a lane's 8 codes are
+// exactly one 32-bit word of the K row (quarter-interleaved: word r NG + g
+// holds channels 32 g + 8 r + 0..7).
+//
+// V: a V word holds one channel of the 8 tokens 4 r + {0..3, 16..19} of a
+// tile (nibble m for token 4 r + (m & 3) + 16 (m >> 2)).  A wave takes one r
+// and 64 channels: lane bits 0-1 pick the channel block within a group (so a
+// group is still a quad), bits 2-4 the token m, bit 5 the group of the pair.
+// After the quantisation lane m holds token m's 8 codes of its channel block;
+// a transpose of the 8 x 8 nibbles across the lanes m (three exchange stages,
+// blocks of 4, 2 and 1 nibbles) leaves lane m with channel 8 j + m of the 8
+// tokens: an output word, the wave's 64 words filling 256 contiguous bytes.
+template <int D, int DTYPE>
+__global__ __launch_bounds__(256) void quantize_tile_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const int32_t* __restrict__ pos, int wave_slots)
+    const int32_t* __restrict__ pos)
 {
     constexpr int NG = D / kGroup;
-    constexpr int LT = D / 8;   // lanes per token
-    constexpr int TW = 64 / LT;  // tokens per wave
-    const int lane = threadIdx.x & 63;
-    const int slot = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (slot >= wave_slots) return;
+    constexpr int LT = D / 8;  // K lanes per token
+    constexpr int U = D / 64;  // K units and V units per thread
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
-    const int tw = lane / LT, j = lane % LT;  // token of the wave, channel block
-    const int t = (p0 & ~1) + slot * TW + tw;  // absolute position (the wave starts even)
+    const int t_tile = (p0 / kTile + (int)blockIdx.x) * kTile;
+    const int t_end = min(p0 + n_new, cap);
+    if (t_tile >= t_end) return;  // block-uniform
     const size_t head = (size_t)b * H + h;
-    const bool fresh = t >= p0 && t < p0 + n_new && t >= 0 && t < cap;
-    if (__ballot(fresh) == 0) return;  // wave-uniform
-    const bool fresh_pair = __shfl_xor(fresh ? 1 : 0, LT, 64) != 0;  // the token sharing t's V byte
-    const size_t row = head * cap + t;
-    const size_t src = (head * n_new + (t - p0)) * D + 8 * j;
-    const int c0 = 8 * j, g = j / 4, r = j % 4;
-
-    // Where only one token of a pair is new, the byte keeps the other's
-    // nibble: both lanes of the pair read the old bytes of the 4 channels
-    // they write (before the quantisation, so that the loads overlap).  Pairs
-    // are aligned to even positions and capacity is even, so both tokens of
-    // a partial pair lie inside the cache.
-    const bool partial = fresh != fresh_pair;
-    const int tt = t >= 0 ? t : 0;
-    uint8_t* vt = vc + (head * (cap / kTile) + tt / kTile) * (size_t)(16 * D);
-    const int u = (tt % kTile) & ~1;  // tile-relative even token of the pair
-    const int half = t & 1;           // writes channels c0 + 4 half .. + 3
-    uint32_t old4 = 0;
-    if (partial) {
+    auto fresh_at = [&](int t) { return t >= p0 && t < t_end && t >= 0; };
+    auto widen8 = [&](const uint4& q, float (&x)[8]) {
+        const uint32_t ww[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            old4 |= (uint32_t)vt[v_tile_byte<D>(c0 + 4 * half + e, u)] << (8 * e);
-    }
-
-    uint4 kraw = make_uint4(0, 0, 0, 0), vraw = make_uint4(0, 0, 0, 0);
-    if (fresh) {
-        kraw = *reinterpret_cast<const uint4*>(k + src);
-        vraw = *reinterpret_cast<const uint4*>(v + src);
-    }
-    auto widen8 = [&](const uint4& w, float (&x)[8]) {
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = widen((uint16_t)(ww[e / 2] >> (16 * (e % 2))), dtype);
+        for (int e = 0; e < 8; ++e) x[e] = widen((uint16_t)(ww[e / 2] >> (16 * (e % 2))), DTYPE);
     };
 
-    // K: widen, rotate, quantise; one code word and (per group) one scale
-    float x[8];
-    widen8(kraw, x);
-    if (signs) rotate_elems<D, 8>(x, signs, rot_norm, j);
-    int c[8];
-    const float sk = quantize_elems<8>(x, c);
-    uint32_t word = 0;
+    // V lane roles, and the nibble mask of the tokens a word takes (the same
+    // for the whole wave, which has one r)
+    const int jl = lane & 3, m = (lane >> 2) & 7, jh = lane >> 5;
+    auto v_token = [&](int r, int mm) { return 4 * r + (mm & 3) + 16 * (mm >> 2); };
+
+    // issue every load first
+    uint4 kraw[U], vraw[U];
+    uint32_t vold[U];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) word |= ((uint32_t)c[e] & 0xFu) << (4 * e);
-    if (fresh) {
-        reinterpret_cast<uint32_t*>(kc + row * (D / 2))[r * NG + g] = word;
-        if (r == 0) ks[row * NG + g] = sk;
+    for (int i = 0; i < U; ++i) {
+        const int L = i * 256 + tid, t = t_tile + L / LT;
+        kraw[i] = make_uint4(0, 0, 0, 0);
+        if (fresh_at(t)) kraw[i] = *reinterpret_cast<const uint4*>(k + (head * n_new + (t - p0)) * D + 8 * (L % LT));
+    }
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
+        const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
+        vraw[i] = make_uint4(0, 0, 0, 0);
+        if (fresh_at(t)) vraw[i] = *reinterpret_cast<const uint4*>(v + (head * n_new + (t - p0)) * D + 32 * g + 8 * jl);
+        uint32_t mask = 0;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) mask |= fresh_at(t_tile + v_token(r, mm)) ? 0xFu << (4 * mm) : 0u;
+        vold[i] = mask;  // replaced by the old word where the mask is partial
+    }
+    uint32_t* vtile = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + t_tile / kTile) * (size_t)(16 * D));
+    auto v_word = [&](int gp, int r) { return ((gp * 4 + r) * 16 + 8 * (jl & 1) + m) * 4 + 2 * jh + (jl >> 1); };
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
+        const uint32_t mask = vold[i];
+        if (mask != 0 && mask != 0xFFFFFFFFu) vold[i] = vtile[v_word(gp, r)];
     }
 
-    // V: widen, quantise; scales, then the nibbles of the pair
-    widen8(vraw, x);
-    const float sv = quantize_elems<8>(x, c);
-    if (fresh && r == 0) vs[row * NG + g] = sv;
-    word = 0;
+    // K: widen, rotate, quantise; one code word and (per group) one scale
 #pragma unroll
-    for (int e = 0; e < 8; ++e) word |= ((uint32_t)c[e] & 0xFu) << (4 * e);
-    const uint32_t other = (uint32_t)__shfl_xor((int)word, LT, 64);
-    const uint32_t even_w = half ? other : word, odd_w = half ? word : other;
-    const bool even_fresh = half ? fresh_pair : fresh, odd_fresh = half ? fresh : fresh_pair;
-    if (even_fresh || odd_fresh) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int ch = 4 * half + e;
-            const uint32_t ob = (old4 >> (8 * e)) & 0xFF;
-            const uint32_t lo = even_fresh ? (even_w >> (4 * ch)) & 0xF : ob & 0xF;
-            const uint32_t hi = odd_fresh ? (odd_w >> (4 * ch)) & 0xF : ob >> 4;
-            vt[v_tile_byte<D>(c0 + ch, u)] = (uint8_t)(lo | (hi << 4));
+    for (int i = 0; i < U; ++i) {
+        const int L = i * 256 + tid, t = t_tile + L / LT, j = L % LT;
+        float x[8];
+        widen8(kraw[i], x);
+        if (signs) rotate_elems<D, 8>(x, signs, rot_norm, j);
+        float sk;
+        const uint32_t word = quantize_word8(x, sk);
+        if (fresh_at(t)) {
+            const size_t row = head * cap + t;
+            reinterpret_cast<uint32_t*>(kc + row * (D / 2))[(j & 3) * NG + (j >> 2)] = word;
+            if ((j & 3) == 0) ks[row * NG + (j >> 2)] = sk;
         }
+    }
+
+    // V: widen, quantise, scales; transpose the nibbles and store whole words
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
+        const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
+        float x[8];
+        widen8(vraw[i], x);
+        float sv;
+        uint32_t word = quantize_word8(x, sv);
+        if (fresh_at(t) && jl == 0) vs[(head * cap + t) * NG + g] = sv;
+#pragma unroll
+        for (int s = 1; s <= 4; s <<= 1) {
+            const uint32_t keep = s == 1 ? 0x0F0F0F0Fu : s == 2 ? 0x00FF00FFu : 0x0000FFFFu;
+            const uint32_t other = (uint32_t)__shfl_xor((int)word, 4 * s, 64);
+            word = (m & s) ? (((other >> (4 * s)) & keep) | (word & ~keep))
+                           : ((word & keep) | ((other & keep) << (4 * s)));
+        }
+        // the mask is wave-uniform: whole words inside the appended range,
+        // merged with the old word at its ends, nothing outside it
+        uint32_t mask = 0;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) mask |= fresh_at(t_tile + v_token(r, mm)) ? 0xFu << (4 * mm) : 0u;
+        if (mask == 0xFFFFFFFFu) vtile[v_word(gp, r)] = word;
+        else if (mask != 0) vtile[v_word(gp, r)] = (vold[i] & ~mask) | (word & mask);
     }
 }
 
@@ -222,14 +245,14 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, pos,
                                          pair_slots);
     } else {
-        // waves of 512 / D tokens starting at pos & ~1: n_new + 1 positions at most
-        const int tw = 512 / D;
-        const int wave_slots = (n_new + 1 + tw - 1) / tw;
-        dim3 grid((wave_slots + 3) / 4, H, B), block(256);
-        auto kern = D == 64 ? quantize_append_kernel<64> : D == 128 ? quantize_append_kernel<128>
-                                                                    : quantize_append_kernel<256>;
-        kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, pos,
-                                         wave_slots);
+        // one block per tile touched: the range may start inside a tile
+        const int tiles = (n_new + 2 * kTile - 2) / kTile;
+        dim3 grid(tiles, H, B), block(256);
+        auto kern = dtype == 0 ? (D == 64 ? quantize_tile_kernel<64, 0> : D == 128 ? quantize_tile_kernel<128, 0>
+                                                                             : quantize_tile_kernel<256, 0>)
+                               : (D == 64 ? quantize_tile_kernel<64, 1> : D == 128 ? quantize_tile_kernel<128, 1>
+                                                                             : quantize_tile_kernel<256, 1>);
+        kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, pos);
     }
     return hipGetLastError();
 }

@@ -70,6 +70,31 @@ def test_quantize_adversarial_values():
     assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
 
 
+def test_quantize_adversarial_bf16_ranges():
+    """bf16 groups across the exponent range, with ties at every half-step and
+    the abs-max in every lane position: scales below 2^-90 (bf16 subnormal
+    inputs among them) and above 2^100, which divide element by element, and
+    scales just inside those bounds, which divide from one reciprocal."""
+    D = 256
+    exps = (-131, -120, -93, -87, 0, 95, 101, 120)
+    rows = []
+    for pos in range(32):
+        x = np.zeros(D, np.float32)
+        for g, e in enumerate(exps):
+            grp = (np.arange(32) % 15 - 7) / 2.0
+            grp[pos] = 7.0 if g % 2 == 0 else -7.0
+            x[32 * g:32 * g + 32] = np.ldexp(grp, e)
+        rows.append(x)
+    x = torch.tensor(np.stack(rows), dtype=torch.bfloat16)[None, None]   # [1,1,32,D]
+    assert torch.equal(x.float(), torch.tensor(np.stack(rows))[None, None])  # exact in bf16
+    say("quantize adversarial bf16 ranges")
+    cache = build_cache(x.to(DEV), (-x).to(DEV), 32, prefill_chunk=16)
+    torch.cuda.synchronize()
+    ref = oracle_cache(x, -x, "bf16")
+    bad = compare_codes(host_cache(cache), ref, 32)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
 def test_append_preserves_neighbours_and_skips_out_of_range():
     """Single-token appends at odd and even positions keep the other nibble of
     each shared V byte; positions outside [0, capacity) are not written."""
@@ -106,6 +131,37 @@ def test_append_preserves_neighbours_and_skips_out_of_range():
     ref1 = oracle_cache(k1, v1, "bf16")
     got = tuple(a[1:2] for a in host_cache(cache))
     assert compare_codes(got, ref1, cap) == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_bulk_append_merges_partial_tiles(D):
+    """Bulk appends (8 tokens and more) at unaligned positions write exactly
+    their range: whole V tiles inside it, the V words shared with older tokens
+    at both ends merged, and ranges clipped to [0, capacity)."""
+    B, H, cap = 3, 2, 128
+    zero = {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    k, v = _rand_kv(B, H, cap, D, torch.bfloat16, seed=D)
+    say(f"bulk append D={D}")
+    cache = build_cache(k, v, cap, prefill_chunk=cap, append_last=False)
+    kk, vv = k.cpu().clone(), v.cpu().clone()
+    rng = np.random.default_rng(D)
+    for step, n in enumerate([8, 9, 31, 33, 45, 64]):
+        p = rng.integers(0, cap - n + 1, size=B)
+        k2, v2 = _rand_kv(B, H, n, D, torch.bfloat16, seed=100 + step, outliers=(step,))
+        cache.append(k2, v2, torch.tensor(p, dtype=torch.int32, device=DEV))
+        for b in range(B):
+            kk[b, :, p[b]:p[b] + n] = k2[b].cpu()
+            vv[b, :, p[b]:p[b] + n] = v2[b].cpu()
+    # straddling the end, starting below zero, starting at the capacity
+    n = 20
+    k2, v2 = _rand_kv(B, H, n, D, torch.bfloat16, seed=7)
+    cache.append(k2, v2, torch.tensor([cap - 7, -11, cap], dtype=torch.int32, device=DEV))
+    kk[0, :, cap - 7:] = k2[0, :, :7].cpu()
+    vv[0, :, cap - 7:] = v2[0, :, :7].cpu()
+    kk[1, :, :9] = k2[1, :, 11:].cpu()
+    vv[1, :, :9] = v2[1, :, 11:].cpu()
+    torch.cuda.synchronize()
+    assert compare_codes(host_cache(cache), oracle_cache(kk, vv, "bf16"), cap) == zero
 
 
 @pytest.mark.parametrize("cfg", [1, 4, 5])

@@ -41,23 +41,41 @@ __device__ __forceinline__ float quantize_elems(float (&x)[E], int (&c)[E])
 
 // Eight consecutive elements per lane, a scale group spanning an aligned quad
 // of lanes: returns the 8 codes packed as one word (nibble e = code of x[e],
-// two's complement) and the group's scale in `scale`.  The same codes as
-// quantize_elems, with fewer operations for the lane's 8 divisions by s:
-//  - x / s is rounded correctly from one correctly rounded reciprocal y =
-//    RN(1 / s) per group (Markstein's division: P. Markstein, IBM J. Res.
-//    Dev. 34(1), 1990).  q = RN(x y) is within 1.5 ulp of x / s; a
-//    correction q <- RN(q + RN(x - q s) y) makes it faithful, and from a
-//    faithful q the remainder x - q s is exact, so a second correction rounds
-//    it correctly (Markstein's theorem, y within half an ulp of 1 / s).  The
-//    bounds on s keep 1 / s normal and every remainder above the subnormal
-//    range whenever |x / s| >= 2^-13; smaller quotients are not exact but
-//    stay far below 1/2, so their code (0) is unchanged.
+// two's complement) and the group's scale in `scale`.  The same codes and
+// scale as quantize_elems, with fewer operations:
+//  - a / 7 and the lane's 8 quotients x / s are rounded correctly by
+//    Markstein's division (P. Markstein, IBM J. Res. Dev. 34(1), 1990) from
+//    one correctly rounded reciprocal y = RN(1 / b) per divisor b: q =
+//    RN(x y) is within 1.5 ulp of x / b; a correction q <- RN(q + RN(x - q
+//    b) y) makes it faithful, and from a faithful q the remainder x - q b is
+//    exact, so a second correction rounds it correctly (Markstein's theorem,
+//    y within half an ulp of 1 / b).  The bounds on a keep every reciprocal
+//    normal and every remainder above the subnormal range whenever |x / s| >=
+//    2^-13; smaller quotients are not exact but stay far below 1/2, so their
+//    code (0) is unchanged.
 //  - |x| <= a and s = RN(a / 7) give |x / s| <= 7 (1 + 2^-23): the clamp
-//    never acts, and adding 1.5 * 2^23 rounds q to an integer, half to even
-//    (1.5 * 2^23 is even and the sum's ulp is 1), leaving the code in the low
-//    bits of the sum's encoding.
-// Zero, huge, infinite or NaN scales and scales below 2^-90 divide element
-// by element as quantize_elems does.
+//    never acts.  Adding 1.5 * 2^23 + 8 rounds q to an integer, half to even
+//    (the constant is even and the sum's ulp is 1), and leaves code + 8, in
+//    1..15, in the low nibble of the sum's encoding above a constant part:
+//    the shifted encodings add up without carries between nibbles, the sum of
+//    the constant parts is cancelled by the accumulator's start value, and
+//    an exclusive or with 8 per nibble turns code + 8 into the code's two's
+//    complement nibble.
+// Other group maxima (zero, below 2^-80, above 2^100, infinite, NaN) divide
+// element by element as quantize_elems does.
+namespace detail {
+constexpr float kRecip7 = 1.0f / 7.0f;  // RN(1/7)
+static_assert(__builtin_bit_cast(uint32_t, kRecip7) == 0x3E124925u, "RN(1/7)");
+constexpr float kRoundBias = 0x1.8p23f + 8.0f;  // 1.5 * 2^23 + 8
+constexpr uint32_t kRoundBiasHigh = 0x4B400000u;  // its encoding less the 8
+constexpr uint32_t pack_start()
+{
+    uint32_t j = 0;
+    for (int e = 0; e < 8; ++e) j += kRoundBiasHigh << (4 * e);
+    return 0u - j;
+}
+}  // namespace detail
+
 __device__ __forceinline__ uint32_t quantize_word8(const float (&x)[8], float& scale)
 {
 #pragma clang fp contract(off)
@@ -65,25 +83,31 @@ __device__ __forceinline__ uint32_t quantize_word8(const float (&x)[8], float& s
 #pragma unroll
     for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
     a = group_max<4>(a);  // exact in any order
-    const float s = a / 7.0f;  // correctly rounded IEEE division
-    scale = s;
-    uint32_t word = 0;
-    if (s >= 0x1p-90f && s <= 0x1p100f) {
-        const float y = 1.0f / s;
+    if (a >= 0x1p-80f && a <= 0x1p100f) {
+        constexpr float y7 = detail::kRecip7;
+        float s = a * y7;
+        s = __builtin_fmaf(__builtin_fmaf(-s, 7.0f, a), y7, s);
+        s = __builtin_fmaf(__builtin_fmaf(-s, 7.0f, a), y7, s);  // RN(a / 7)
+        scale = s;
+        const float y = 1.0f / s;  // correctly rounded IEEE division
+        uint32_t acc = detail::pack_start();
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             float q = x[e] * y;
             q = __builtin_fmaf(__builtin_fmaf(-q, s, x[e]), y, q);
-            q = __builtin_fmaf(__builtin_fmaf(-q, s, x[e]), y, q);
-            word |= (__builtin_bit_cast(uint32_t, q + 0x1.8p23f) & 0xFu) << (4 * e);
+            q = __builtin_fmaf(__builtin_fmaf(-q, s, x[e]), y, q);  // RN(x / s)
+            acc += __builtin_bit_cast(uint32_t, q + detail::kRoundBias) << (4 * e);
         }
-    } else {
+        return acc ^ 0x88888888u;
+    }
+    const float s = a / 7.0f;  // correctly rounded IEEE division
+    scale = s;
+    uint32_t word = 0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            float r = rintf(x[e] / s);  // correctly rounded IEEE division, then half to even
-            r = fminf(fmaxf(r, -8.0f), 7.0f);
-            word |= ((uint32_t)(s != 0.0f ? (int)r : 0) & 0xFu) << (4 * e);
-        }
+    for (int e = 0; e < 8; ++e) {
+        float r = rintf(x[e] / s);  // correctly rounded IEEE division, then half to even
+        r = fminf(fmaxf(r, -8.0f), 7.0f);
+        word |= ((uint32_t)(s != 0.0f ? (int)r : 0) & 0xFu) << (4 * e);
     }
     return word;
 }
@@ -96,19 +120,16 @@ __device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 
     return quantize_elems<D / 64>(x, c);
 }
 
-// y <- rot_norm * H (signs (.) y), Sylvester order, stages in ascending
-// stride; a butterfly replaces (lower, upper) with (lower + upper,
-// lower - upper) exactly as the in-place fast Walsh-Hadamard transform does.
-// A vector of D elements spread over D / E consecutive lanes (an aligned
-// lane group), E consecutive elements per lane; `lane` is the lane's index
-// within its group.
+// y <- rot_norm * H y (y already multiplied by the signs), Sylvester order,
+// stages in ascending stride; a butterfly replaces (lower, upper) with
+// (lower + upper, lower - upper) exactly as the in-place fast Walsh-Hadamard
+// transform does.  A vector of D elements spread over D / E consecutive
+// lanes (an aligned lane group), E consecutive elements per lane; `lane` is
+// the lane's index within its group.
 template <int D, int E>
-__device__ __forceinline__ void rotate_elems(float (&y)[E], const float* __restrict__ signs,
-                                             float rot_norm, int lane)
+__device__ __forceinline__ void rotate_signed(float (&y)[E], float rot_norm, int lane)
 {
 #pragma clang fp contract(off)
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = y[e] * signs[lane * E + e];
 #pragma unroll
     for (int h = 1; h < E; h <<= 1) {
 #pragma unroll
@@ -132,6 +153,17 @@ __device__ __forceinline__ void rotate_elems(float (&y)[E], const float* __restr
     }
 #pragma unroll
     for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
+}
+
+// y <- rot_norm * H (signs (.) y), the signs read for the lane's elements.
+template <int D, int E>
+__device__ __forceinline__ void rotate_elems(float (&y)[E], const float* __restrict__ signs,
+                                             float rot_norm, int lane)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = y[e] * signs[lane * E + e];
+    rotate_signed<D, E>(y, rot_norm, lane);
 }
 
 // One wave rotates one vector: lane l owns elements [l*E, l*E + E), E = D / 64.

@@ -127,24 +127,20 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 // a transpose of the 8 x 8 nibbles across the lanes m (three exchange stages,
 // blocks of 4, 2 and 1 nibbles) leaves lane m with channel 8 j + m of the 8
 // tokens: an output word, the wave's 64 words filling 256 contiguous bytes.
-template <int D, int DTYPE>
-__global__ __launch_bounds__(256) void quantize_tile_kernel(
-    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
-    int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
-    float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const int32_t* __restrict__ pos)
+// The tile's work; FULL when every token of the tile is appended (no
+// freshness tests, no merge with older V nibbles).
+template <int D, int DTYPE, bool FULL>
+__device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+                                              int n_new, int cap, size_t head, int p0, int t_tile, int t_end,
+                                              uint8_t* __restrict__ kc, float* __restrict__ ks,
+                                              uint8_t* __restrict__ vc, float* __restrict__ vs,
+                                              const float* __restrict__ signs, float rot_norm)
 {
     constexpr int NG = D / kGroup;
     constexpr int LT = D / 8;  // K lanes per token
     constexpr int U = D / 64;  // K units and V units per thread
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-    const int h = blockIdx.y, b = blockIdx.z;
-    const int p0 = pos[b];
-    const int t_tile = (p0 / kTile + (int)blockIdx.x) * kTile;
-    const int t_end = min(p0 + n_new, cap);
-    if (t_tile >= t_end) return;  // block-uniform
-    const size_t head = (size_t)b * H + h;
-    auto fresh_at = [&](int t) { return t >= p0 && t < t_end && t >= 0; };
+    auto fresh_at = [&](int t) { return FULL || (t >= p0 && t < t_end && t >= 0); };
     auto widen8 = [&](const uint4& q, float (&x)[8]) {
         const uint32_t ww[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
@@ -155,10 +151,20 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     // for the whole wave, which has one r)
     const int jl = lane & 3, m = (lane >> 2) & 7, jh = lane >> 5;
     auto v_token = [&](int r, int mm) { return 4 * r + (mm & 3) + 16 * (mm >> 2); };
+    auto v_mask = [&](int r) {
+        uint32_t mask = 0;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) mask |= fresh_at(t_tile + v_token(r, mm)) ? 0xFu << (4 * mm) : 0u;
+        return mask;
+    };
 
-    // issue every load first
+    // issue every load first; the K signs of a lane are the same in every unit
+    float sg[8];
+    if (signs) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sg[e] = signs[8 * (tid % LT) + e];
+    }
     uint4 kraw[U], vraw[U];
-    uint32_t vold[U];
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int L = i * 256 + tid, t = t_tile + L / LT;
@@ -171,18 +177,18 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
         const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
         vraw[i] = make_uint4(0, 0, 0, 0);
         if (fresh_at(t)) vraw[i] = *reinterpret_cast<const uint4*>(v + (head * n_new + (t - p0)) * D + 32 * g + 8 * jl);
-        uint32_t mask = 0;
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) mask |= fresh_at(t_tile + v_token(r, mm)) ? 0xFu << (4 * mm) : 0u;
-        vold[i] = mask;  // replaced by the old word where the mask is partial
     }
     uint32_t* vtile = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + t_tile / kTile) * (size_t)(16 * D));
     auto v_word = [&](int gp, int r) { return ((gp * 4 + r) * 16 + 8 * (jl & 1) + m) * 4 + 2 * jh + (jl >> 1); };
+    uint32_t vold[U];  // older nibbles of words the range shares at its ends
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
-        const uint32_t mask = vold[i];
-        if (mask != 0 && mask != 0xFFFFFFFFu) vold[i] = vtile[v_word(gp, r)];
+        vold[i] = 0;
+        if constexpr (!FULL) {
+            const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
+            const uint32_t mask = v_mask(r);
+            if (mask != 0 && mask != 0xFFFFFFFFu) vold[i] = vtile[v_word(gp, r)];
+        }
     }
 
     // K: widen, rotate, quantise; one code word and (per group) one scale
@@ -191,7 +197,11 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
         const int L = i * 256 + tid, t = t_tile + L / LT, j = L % LT;
         float x[8];
         widen8(kraw[i], x);
-        if (signs) rotate_elems<D, 8>(x, signs, rot_norm, j);
+        if (signs) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[e];
+            rotate_signed<D, 8>(x, rot_norm, j);
+        }
         float sk;
         const uint32_t word = quantize_word8(x, sk);
         if (fresh_at(t)) {
@@ -220,12 +230,33 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
         }
         // the mask is wave-uniform: whole words inside the appended range,
         // merged with the old word at its ends, nothing outside it
-        uint32_t mask = 0;
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) mask |= fresh_at(t_tile + v_token(r, mm)) ? 0xFu << (4 * mm) : 0u;
-        if (mask == 0xFFFFFFFFu) vtile[v_word(gp, r)] = word;
-        else if (mask != 0) vtile[v_word(gp, r)] = (vold[i] & ~mask) | (word & mask);
+        if constexpr (FULL) {
+            vtile[v_word(gp, r)] = word;
+        } else {
+            const uint32_t mask = v_mask(r);
+            if (mask == 0xFFFFFFFFu) vtile[v_word(gp, r)] = word;
+            else if (mask != 0) vtile[v_word(gp, r)] = (vold[i] & ~mask) | (word & mask);
+        }
     }
+}
+
+template <int D, int DTYPE>
+__global__ __launch_bounds__(256) void quantize_tile_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
+    int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
+    float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
+    const int32_t* __restrict__ pos)
+{
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int p0 = pos[b];
+    const int t_tile = (p0 / kTile + (int)blockIdx.x) * kTile;
+    const int t_end = min(p0 + n_new, cap);
+    if (t_tile >= t_end) return;  // block-uniform
+    const size_t head = (size_t)b * H + h;
+    if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
+        quantize_tile<D, DTYPE, true>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs, rot_norm);
+    else
+        quantize_tile<D, DTYPE, false>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs, rot_norm);
 }
 
 }  // namespace

@@ -147,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     }
     if (s < ns) fold(ml[s], *reinterpret_cast<const float4*>(po + (size_t)s * D));
 
-    // ---- the new token: quantise K and V exactly as the append kernel does
-    //      (same operations, same order), write them, score it
+    // ---- the new token: quantise K and V to the same bytes as the append kernels
+    //      (the small-append kernel's operations in its order), write them, score it
     [[maybe_unused]] float s_new = kNegInf;
     if constexpr (APPEND) {
         float x = widen(kx, a.dtype);

@@ -7,8 +7,12 @@
 // the AdapTQ page (section on Fast Hadamard Rotation).
 //
 // Built with -ffp-contract=off: every step is one IEEE fp32 operation with
-// round-to-nearest-even, so the codes and scales are bit-identical to any
-// correct evaluation of the same steps.
+// round-to-nearest-even (or, in the bulk kernel, an exact sequence that
+// reaches the same correctly rounded results), so the codes and scales are
+// bit-identical to any correct evaluation of the same steps.
+//
+// Fewer than 8 new tokens take quantize_pair_kernel (one wave per token
+// pair); more take quantize_tile_kernel (one block per 32-token V tile).
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_lane.hpp"
@@ -127,8 +131,9 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 // a transpose of the 8 x 8 nibbles across the lanes m (three exchange stages,
 // blocks of 4, 2 and 1 nibbles) leaves lane m with channel 8 j + m of the 8
 // tokens: an output word, the wave's 64 words filling 256 contiguous bytes.
-// The tile's work; FULL when every token of the tile is appended (no
-// freshness tests, no merge with older V nibbles).
+//
+// quantize_tile is one tile's work; FULL when every token of the tile is
+// appended (no freshness tests, no merge with older V nibbles).
 template <int D, int DTYPE, bool FULL>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                               int n_new, int cap, size_t head, int p0, int t_tile, int t_end,

@@ -40,15 +40,15 @@ def _load():
     lib.oracle_quantize_vector.argtypes = [P, ctypes.c_int, P, P]
     lib.oracle_quantize_vector.restype = None
     lib.oracle_quantize_rows.argtypes = [P, ctypes.c_int, ctypes.c_long, ctypes.c_int,
-                                         P, ctypes.c_float, P, P, ctypes.c_int]
+                                         P, ctypes.c_float, P, P, P, ctypes.c_int]
     lib.oracle_quantize_rows.restype = ctypes.c_int
     lib.oracle_attend_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                       ctypes.c_long, ctypes.c_double, P, ctypes.c_float,
-                                      P, P]
+                                      P, P, P]
     lib.oracle_attend_row.restype = None
     lib.oracle_sdpa.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_long, P, P, P, P, P,
-                                ctypes.c_double, P, ctypes.c_float, P, ctypes.c_long,
+                                ctypes.c_double, P, ctypes.c_float, P, P, ctypes.c_long,
                                 P, ctypes.c_int]
     lib.oracle_sdpa.restype = ctypes.c_int
     _lib = lib
@@ -103,8 +103,11 @@ def quantize_vector(x):
     return codes, scales
 
 
-def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1):
-    """[..., D] 16-bit rows -> codes [..., D/2], scales [..., D/32]."""
+def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None):
+    """[..., D] 16-bit rows -> codes [..., D/2], scales [..., D/32].
+
+    chan_scale: per-channel scale lambda [D] applied after the rotation
+    (the cache then holds lambda (.) y), or None."""
     lib = _load()
     bits = _c(bits, np.uint16)
     D = bits.shape[-1]
@@ -112,36 +115,39 @@ def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1):
     codes = np.zeros(bits.shape[:-1] + (D // 2,), np.uint8)
     scales = np.zeros(bits.shape[:-1] + (D // 32,), np.float32)
     s = None if signs is None else _c(signs, np.float32)
+    lam = None if chan_scale is None else _c(chan_scale, np.float32)
     rc = lib.oracle_quantize_rows(_ptr(bits), DTYPES[dtype], N, D, _ptr(s),
-                                  float(np.float32(rot_norm)), _ptr(codes), _ptr(scales),
-                                  int(threads))
+                                  float(np.float32(rot_norm)), _ptr(lam), _ptr(codes),
+                                  _ptr(scales), int(threads))
     if rc != 0:
         raise ValueError("oracle_quantize_rows rejected its arguments")
     return codes, scales
 
 
-def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0):
+def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0, chan_scale=None):
     lib = _load()
     q_bits = _c(q_bits, np.uint16)
     D = q_bits.shape[-1]
     kc, vc = _c(kc, np.uint8), _c(vc, np.uint8)
     ks, vs = _c(ks, np.float32), _c(vs, np.float32)
     s = None if signs is None else _c(signs, np.float32)
+    lam = None if chan_scale is None else _c(chan_scale, np.float32)
     work = np.zeros(max(int(T), 1), np.float64)
     out = np.zeros(D, np.float64)
     lib.oracle_attend_row(_ptr(q_bits), DTYPES[dtype], D, _ptr(kc), _ptr(ks), _ptr(vc),
                           _ptr(vs), int(T), float(scale), _ptr(s),
-                          float(np.float32(rot_norm)), _ptr(work), _ptr(out))
+                          float(np.float32(rot_norm)), _ptr(lam), _ptr(work), _ptr(out))
     return out
 
 
 def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
-         signs=None, rot_norm=0.0, rows=None, threads=1):
+         signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None):
     """Decode attention over a plain-layout cache.
 
     q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D/2]; scales
-    [B, Hkv, cap, D/32]; lens [B].  Returns float64 [B, Hq, D], or
-    [len(rows), D] for the listed rows (row = b * Hq + h).
+    [B, Hkv, cap, D/32]; lens [B]; chan_scale: the K cache's per-channel
+    scale lambda [D] or None.  Returns float64 [B, Hq, D], or [len(rows), D]
+    for the listed rows (row = b * Hq + h).
     """
     lib = _load()
     q_bits = _c(q_bits, np.uint16)
@@ -151,6 +157,7 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
     Hkv, cap = kc.shape[1], kc.shape[2]
     lens = _c(lens, np.int32)
     s = None if signs is None else _c(signs, np.float32)
+    lam = None if chan_scale is None else _c(chan_scale, np.float32)
     if rows is None:
         out = np.zeros((B, Hq, D), np.float64)
         r = None
@@ -161,7 +168,8 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
         out = np.zeros((nrows, D), np.float64)
     rc = lib.oracle_sdpa(_ptr(q_bits), DTYPES[dtype], B, Hq, Hkv, D, cap, _ptr(kc), _ptr(ks),
                          _ptr(vc), _ptr(vs), _ptr(lens), float(scale), _ptr(s),
-                         float(np.float32(rot_norm)), _ptr(r), nrows, _ptr(out), int(threads))
+                         float(np.float32(rot_norm)), _ptr(lam), _ptr(r), nrows, _ptr(out),
+                         int(threads))
     if rc != 0:
         raise ValueError("oracle_sdpa rejected its arguments")
     return out

@@ -35,6 +35,13 @@
  * anywhere in the fp32 quantiser (this file is built with
  * -ffp-contract=off).
  *
+ * Per-channel scale ("SRFT + int4 KV-cache", core-method section: a
+ * per-coordinate scale lambda is applied after the rotation and before the
+ * group abs-max).  Reading: when a scale vector is given, the quantised
+ * vector is z = lambda (.) y (one fp32 multiply per element, after the
+ * rotation if there is one), and the cache then stands for y = z / lambda:
+ * attention dequantises K^_i = code_i * s_g / lambda_i in fp64.
+ *
  * Parity pins for every function here live in the CPU test suite.
  */
 #include <math.h>
@@ -166,6 +173,7 @@ struct qrows_job {
     int D;
     const float *signs;
     float rot_norm;
+    const float *chan_scale;
     uint8_t *codes;
     float *scales;
 };
@@ -179,6 +187,9 @@ static void *qrows_worker(void *arg)
             x[i] = widen(j->src[n * j->D + i], j->dtype);
         if (j->signs)
             oracle_srht_f32(x, j->signs, j->D, j->rot_norm);
+        if (j->chan_scale)
+            for (int i = 0; i < j->D; ++i)
+                x[i] = x[i] * j->chan_scale[i];
         oracle_quantize_vector(x, j->D, j->codes + n * (j->D / 2),
                                j->scales + n * (j->D / ORACLE_GROUP));
     }
@@ -186,11 +197,12 @@ static void *qrows_worker(void *arg)
 }
 
 /* N rows of D 16-bit values (dtype 0 = fp16, 1 = bf16) -> N rows of codes
- * and scales.  signs == NULL means no rotation.  Rows are independent, so
- * spreading them over threads does not change any result. */
+ * and scales.  signs == NULL means no rotation, chan_scale == NULL no
+ * per-channel scale.  Rows are independent, so spreading them over threads
+ * does not change any result. */
 int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
-                         const float *signs, float rot_norm, uint8_t *codes,
-                         float *scales, int nthreads)
+                         const float *signs, float rot_norm, const float *chan_scale,
+                         uint8_t *codes, float *scales, int nthreads)
 {
     if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1)
         return -1;
@@ -206,7 +218,7 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
         long n0 = t * per, n1 = n0 + per > N ? N : n0 + per;
         if (n0 >= n1)
             break;
-        jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, codes, scales};
+        jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, chan_scale, codes, scales};
         if (nthreads == 1) {
             qrows_worker(&jobs[t]);
         } else {
@@ -222,7 +234,8 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
 /* ---------------------------------------------------------------- attend */
 
 /* One query row against one head's cache rows t < T:
- *   K^[t][i] = code * scale  (exact in fp64)
+ *   K^[t][i] = code * scale  (exact in fp64), divided by lambda_i when a
+ *              per-channel scale is given
  *   S_t      = scale_attn * sum_i q'_i K^[t][i]
  *   w_t      = exp(S_t - max_u S_u)
  *   out      = sum_t w_t V^[t] / sum_t w_t
@@ -232,7 +245,7 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
                        const uint8_t *kc, const float *ks,
                        const uint8_t *vc, const float *vs, long T,
                        double scale, const float *signs, float rot_norm,
-                       double *work, double *out)
+                       const float *chan_scale, double *work, double *out)
 {
     double qd[1024], kd[1024];
     int ng = D / ORACLE_GROUP;
@@ -249,8 +262,11 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
     for (long t = 0; t < T; ++t) {
         const uint8_t *row = kc + t * (D / 2);
         const float *srow = ks + t * ng;
-        for (int i = 0; i < D; ++i)
+        for (int i = 0; i < D; ++i) {
             kd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
+            if (chan_scale)
+                kd[i] /= (double)chan_scale[i];
+        }
         double dot = 0.0;
         for (int i = 0; i < D; ++i)
             dot += qd[i] * kd[i];
@@ -281,6 +297,7 @@ struct attn_job {
     double scale;
     const float *signs;
     float rot_norm;
+    const float *chan_scale;
     double *out;
     const int32_t *rows;
     long r0, r1;
@@ -303,7 +320,7 @@ static void *attn_worker(void *arg)
         oracle_attend_row(j->q + (size_t)row * j->D, j->dtype, j->D,
                           j->kc + head * j->cap * (j->D / 2), j->ks + head * j->cap * (j->D / ORACLE_GROUP),
                           j->vc + head * j->cap * (j->D / 2), j->vs + head * j->cap * (j->D / ORACLE_GROUP),
-                          T, j->scale, j->signs, j->rot_norm, work,
+                          T, j->scale, j->signs, j->rot_norm, j->chan_scale, work,
                           j->out + (size_t)r * j->D);
     }
     free(work);
@@ -318,7 +335,8 @@ static void *attn_worker(void *arg)
 int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, long cap,
                 const uint8_t *kc, const float *ks, const uint8_t *vc, const float *vs,
                 const int32_t *lens, double scale, const float *signs, float rot_norm,
-                const int32_t *rows, long nrows, double *out, int nthreads)
+                const float *chan_scale, const int32_t *rows, long nrows, double *out,
+                int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
         D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1)
@@ -337,7 +355,7 @@ int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, lon
         if (r0 >= r1)
             break;
         jobs[t] = (struct attn_job){q, dtype, B, Hq, Hkv, D, cap, kc, vc, ks, vs, lens,
-                                    scale, signs, rot_norm, out, rows, r0, r1};
+                                    scale, signs, rot_norm, chan_scale, out, rows, r0, r1};
         if (nthreads == 1) {
             attn_worker(&jobs[t]);
         } else {

@@ -324,6 +324,110 @@ def test_sdpa_row_subset_and_threads_agree():
     assert np.array_equal(sub, full.reshape(16, 128)[rows])
 
 
+# ------------------------------------------------------------------ per-channel scale
+
+def _rows(rng, shape, dtype, outliers=(), factor=1.0):
+    x = rng.standard_normal(shape).astype(np.float32)
+    for c in outliers:
+        x[..., c] *= factor
+    t = torch.from_numpy(x).to(torch.bfloat16 if dtype == "bf16" else torch.float16)
+    return t.view(torch.int16).numpy().view(np.uint16), t.float().numpy()
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_chan_scale_power_of_two_per_group_is_exact(dtype, D, rotate):
+    """lambda = 2^k_g, constant within each group: every product is exact, so
+    the codes are those without lambda and each scale is multiplied by 2^k_g;
+    attention, which divides lambda back out, is then bit-identical."""
+    rng = np.random.default_rng(D + rotate)
+    bits, _ = _rows(rng, (2, 3, 40, D), dtype, outliers=(5,), factor=8.0)
+    k = rng.integers(-6, 7, D // 32)
+    lam = np.repeat(np.ldexp(1.0, k), 32).astype(np.float32)
+    sg = np.where(rng.integers(0, 2, D) == 1, 1.0, -1.0).astype(np.float32) if rotate else None
+    c = np.float32(1 / math.sqrt(D))
+    c0, s0 = oracle.quantize(bits, dtype, signs=sg, rot_norm=c)
+    c1, s1 = oracle.quantize(bits, dtype, signs=sg, rot_norm=c, chan_scale=lam)
+    assert np.array_equal(c0, c1)
+    assert np.array_equal(s1, (s0 * np.ldexp(1.0, k)).astype(np.float32))
+    qb, _ = _q(rng, 2, 6, D, dtype)
+    vc, vs = oracle.quantize(bits[::-1].copy(), dtype)
+    lens = np.array([40, 23], np.int32)
+    o0 = oracle.sdpa(qb, dtype, c0, s0, vc, vs, lens, 0.1, signs=sg, rot_norm=c)
+    o1 = oracle.sdpa(qb, dtype, c1, s1, vc, vs, lens, 0.1, signs=sg, rot_norm=c, chan_scale=lam)
+    assert np.array_equal(o0, o1)
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_chan_scale_codes_bound_the_scaled_vector(dtype):
+    """With any positive lambda the codes quantise z = fp32(lambda x): the
+    error bound, the sign rule and max |c| = 7 hold against z, channel by
+    channel (a lambda applied to the wrong channel breaks them)."""
+    D = 128
+    rng = np.random.default_rng(21)
+    bits, x = _rows(rng, (300, D), dtype, outliers=(7, 70), factor=12.0)
+    lam = rng.uniform(0.25, 4.0, D).astype(np.float32)
+    codes, scales = oracle.quantize(bits, dtype, chan_scale=lam)
+    z = (x * lam).astype(np.float32).reshape(300, D // 32, 32).astype(np.float64)
+    cc = _codes(codes, D).reshape(300, D // 32, 32)
+    s = scales.astype(np.float64)[..., None]
+    assert np.all(np.abs(z - cc * s) <= s * (0.5 + 7 * 2.0 ** -23))
+    assert np.all(np.abs(cc).max(-1)[scales > 0] == 7)
+    assert np.all((np.sign(cc) == np.sign(z)) | (cc == 0))
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_sdpa_chan_scale_matches_torch(rotate):
+    D, T, B, Hq, Hkv = 128, 33, 2, 4, 2
+    rng = np.random.default_rng(22 + rotate)
+    bits, _ = _rows(rng, (2, B, Hkv, T, D), "bf16")
+    lam = rng.uniform(0.5, 2.0, D).astype(np.float32)
+    sg = np.where(rng.integers(0, 2, D) == 1, 1.0, -1.0).astype(np.float32) if rotate else None
+    c = np.float32(1 / math.sqrt(D))
+    kc, ks = oracle.quantize(bits[0], "bf16", signs=sg, rot_norm=c, chan_scale=lam)
+    vc, vs = oracle.quantize(bits[1], "bf16")
+    qb, qt = _q(rng, B, Hq, D)
+    lens = np.array([T, 19], np.int32)
+    out = oracle.sdpa(qb, "bf16", kc, ks, vc, vs, lens, 0.11, signs=sg, rot_norm=c, chan_scale=lam)
+    K = torch.from_numpy(oracle.dequantize(kc, ks) / lam.astype(np.float64))
+    V = torch.from_numpy(oracle.dequantize(vc, vs))
+    if rotate:
+        H = torch.from_numpy(scipy.linalg.hadamard(D).astype(np.float64))
+        qt = float(c) * (qt * torch.from_numpy(sg).double()) @ H.T
+    for b in range(B):
+        n = int(lens[b])
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qt[b][:, None, :], K[b, :, :n].repeat_interleave(2, 0), V[b, :, :n].repeat_interleave(2, 0),
+            scale=0.11)[:, 0]
+        assert torch.max(torch.abs(torch.from_numpy(out[b]) - ref)) < 1e-12
+
+
+def test_chan_scale_evens_out_outlier_channels():
+    """What the scale is for: with three K channels 20x larger than the rest,
+    lambda = 1/20 on them brings the attention on the quantised cache closer
+    to attention on the unquantised K."""
+    D, T = 128, 256
+    rng = np.random.default_rng(23)
+    out_ch = (3, 40, 100)
+    bits, x = _rows(rng, (1, 1, T, D), "bf16", outliers=out_ch, factor=20.0)
+    lam = np.ones(D, np.float32)
+    lam[list(out_ch)] = np.float32(1 / 20)
+    vbits, _ = _rows(rng, (1, 1, T, D), "bf16")
+    vc, vs = oracle.quantize(vbits, "bf16")
+    qb, qt = _q(rng, 1, 8, D)
+    lens = np.array([T], np.int32)
+    Kt = torch.from_numpy(x.astype(np.float64))[0].repeat_interleave(8, 0)
+    V = torch.from_numpy(oracle.dequantize(vc, vs))[0].repeat_interleave(8, 0)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt[0][:, None, :], Kt, V, scale=0.3)[:, 0].numpy()
+    errs = []
+    for ls in (None, lam):
+        kc, ks = oracle.quantize(bits, "bf16", chan_scale=ls)
+        out = oracle.sdpa(qb, "bf16", kc, ks, vc, vs, lens, 0.3, chan_scale=ls)
+        errs.append(np.linalg.norm(out[0] - ref) / np.linalg.norm(ref))
+    assert errs[1] < 0.5 * errs[0], errs
+
+
 # ------------------------------------------------------------------ closed forms
 
 def test_closed_form_storage_figures():

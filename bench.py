@@ -123,6 +123,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=0, help="force the split chunk (0 = planner default)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--chan-scale", action="store_true",
+                    help="give K a per-channel scale (seeded; 1/multiplier on the outlier channels)")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
@@ -177,7 +179,9 @@ def main():
     host_kv0 = None
     for l in range(L):
         signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if w.rotate else None
-        cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs)
+        lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if args.chan_scale else None
+        cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs,
+                                chan_scale=lam)
         k = synth.kv(w, l, "k", device=dev)
         v = synth.kv(w, l, "v", device=dev)
         lens = synth.lens(w, l)
@@ -191,7 +195,8 @@ def main():
         k_new.append(k[ar, :, idx].contiguous())  # [B, Hkv, D]: the token at lens - 1
         v_new.append(v[ar, :, idx].contiguous())
         if l == 0 and not args.no_cpu:
-            host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy())
+            host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy(),
+                        None if lam is None else lam.cpu().numpy())
         del k, v
         caches.append(cache)
         qs.append(synth.query(w, l, device=dev))
@@ -318,7 +323,8 @@ def main():
     n_chunks = max(1, min(8, w.capacity // n_bulk))
     bulk_in = [(synth.kv(w, i, "k", T=n_bulk, device=dev), synth.kv(w, i, "v", T=n_bulk, device=dev))
                for i in range(n_chunks)]
-    scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs)
+    scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs,
+                              chan_scale=caches[0].chan_scale)
     bulk_pos = [torch.full((w.B,), i * n_bulk, dtype=torch.int32, device=dev) for i in range(n_chunks)]
 
     def bulk_pass():
@@ -361,16 +367,17 @@ def main():
     if host_kv0 is not None:
         import oracle
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        kb, vb, sg = host_kv0
+        kb, vb, sg, lam0 = host_kv0
         t = time.time()
-        kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads)
+        kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
+                                 chan_scale=lam0)
         vc, vs = oracle.quantize(vb, w.dtype, threads=threads)
         log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
         lens0 = synth.lens(w, 0)
         q0 = synth.bits(qs[0])
         t = time.perf_counter()
         ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
-                          rot_norm=caches[0].rot_norm, threads=threads)
+                          rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0)
         cpu_s = time.perf_counter() - t
         got = outs[0].cpu().numpy().astype(np.float64)
         err = got - ref
@@ -401,7 +408,7 @@ def main():
             "head_dim": w.D, "context": w.T, "layers": L, "input_dtype": w.dtype,
             "cache_gib": round(cache_bytes / 2**30, 3), "chunk": plan.chunk,
             "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
-            "graph": graph is not None,
+            "graph": graph is not None, "k_chan_scale": bool(args.chan_scale),
             "step": "per layer: the split pass over the cached tokens, then the combine pass that "
                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)",
         },

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 1
+#define OTQ_ABI_VERSION 2
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -68,6 +68,12 @@ typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
  * butterflies (a + b, a - b) in ascending stride order, then one multiply by
  * rot_norm (pass fp32(1/sqrt(head_dim))).  The query is rotated the same way
  * inside otq_sdpa_int4_decode, so scores are unchanged by the rotation.
+ * K only, when k_chan_scale != NULL (a per-coordinate scale lambda applied
+ * after the rotation and before the group abs-max: "SRFT + int4 KV-cache"
+ * page, core-method section), x (rotated or not) is then replaced by
+ *     z_i = x_i * k_chan_scale[i]      (one fp32 multiply)
+ * and attention reads K^_i = code_i * s_g / k_chan_scale[i]: the query is
+ * divided by the scale inside otq_sdpa_int4_decode.
  *
  * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
  *  Codes are two's-complement int4 nibbles; a byte holds an even channel in
@@ -97,8 +103,9 @@ typedef struct otq_cache {
     float *k_scales;
     uint8_t *v_codes;
     float *v_scales;
-    const float *k_rot_signs; /* device [D] of +1.0f / -1.0f, or NULL */
+    const float *k_rot_signs; /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
     float rot_norm;           /* used only when k_rot_signs != NULL */
+    const float *k_chan_scale; /* device [D] fp32 lambda, finite and > 0, 16-byte aligned, or NULL */
 } otq_cache;
 
 /* Human-readable name of a status code (static string). */

@@ -37,6 +37,9 @@ int check_cache(const otq_cache* c)
     const int rc = check_dims(c->batch, c->num_kv_heads, c->head_dim, c->capacity);
     if (rc != OTQ_OK) return rc;
     if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) return OTQ_EINVAL;
+    // the per-channel vectors are read 4 floats at a time
+    if ((((uintptr_t)c->k_rot_signs) & 15) != 0 || (((uintptr_t)c->k_chan_scale) & 15) != 0)
+        return OTQ_EINVAL;
     return OTQ_OK;
 }
 
@@ -161,7 +164,7 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     const hipError_t e = otq::launch_quantize_append(
         k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
         cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
-        cache->rot_norm, pos, static_cast<hipStream_t>(stream));
+        cache->rot_norm, cache->k_chan_scale, pos, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
@@ -228,6 +231,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.vs = cache->v_scales;
     a.signs = cache->k_rot_signs;
     a.rot_norm = cache->rot_norm;
+    a.lam = cache->k_chan_scale;
     a.lens = lens;
     a.max_len = max_len;
     a.qscale = scale * otq::kLog2eHost;
@@ -283,6 +287,7 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.vs = cache->v_scales;
     a.signs = cache->k_rot_signs;
     a.rot_norm = cache->rot_norm;
+    a.lam = cache->k_chan_scale;
     a.qscale = scale * otq::kLog2eHost;
     const hipError_t e = otq::launch_lse_combine(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;

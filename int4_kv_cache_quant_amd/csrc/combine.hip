@@ -60,7 +60,7 @@ __device__ __forceinline__ float fwht_thread(float y, float* xch)
 // running (m, l, o) (the same merge rule as above), then the block merges the
 // threads' triples: one pass over the partials.  DA = head_dim when the
 // block also appends the new token (0 otherwise).
-template <int DA, bool ROT>
+template <int DA, bool ROT, bool LAM>
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
 {
     __shared__ float red_m[kThreads / 64];
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     // past D work on channel D - 1 and write nothing), loaded before lens[b]
     // like the first splits below
     [[maybe_unused]] uint16_t kx = 0, vx = 0, qx = 0;
-    [[maybe_unused]] float sg = 1.0f;
+    [[maybe_unused]] float sg = 1.0f, lm = 1.0f;
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
     if constexpr (APPEND) {
@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         vx = a.v_new[src];
         qx = static_cast<const uint16_t*>(a.q)[(size_t)row * DA + ch];
         if (ROT) sg = a.signs[ch];
+        if (LAM) lm = a.lam[ch];  // K's channel scale
         // one block per KV head writes the token: the first query head's,
         // first channel slice
         writer = h % G == 0 && blockIdx.y == 0 && tid < DA;
@@ -157,6 +158,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             x = fwht_thread<DA>(x, xch);
             x = x * a.rot_norm;
         }
+        if (LAM) x = x * lm;  // after the rotation
         float xk[1] = {x};
         int ck[1];
         // one channel per lane: the lane layout of a 64-channel vector, whose
@@ -187,13 +189,15 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
                 a.vs[krow * (DA / kGroup) + ch / kGroup] = sv;
             }
         }
-        // score: q' . k^ (q rotated like K), in log2 units
+        // score: q' . k^ (q rotated like K, then divided by K's channel
+        // scale), in log2 units
         float y = widen(qx, a.dtype);
         if (ROT) {
             y = y * sg;
             y = fwht_thread<DA>(y, xch);
             y = y * a.rot_norm;
         }
+        if (LAM) y = y / lm;
         const float kd = (float)ck[0] * sk;
         s_new = group_sum<64>(tid < DA ? y * kd : 0.0f);  // this wave's part of q' . k^
         if (ROT && DA > 64) __syncthreads();  // the butterflies' last reads of xch are done
@@ -255,25 +259,27 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
     if (a.D % kCh != 0) return hipErrorInvalidValue;
     dim3 grid(a.B * a.Hq, a.D / kCh), block(kThreads);
     if (a.k_new == nullptr) {
-        lse_combine_kernel<0, false><<<grid, block, 0, stream>>>(a);
+        lse_combine_kernel<0, false, false><<<grid, block, 0, stream>>>(a);
     } else {
-        const bool rot = a.signs != nullptr;
+        const int mode = (a.signs != nullptr ? 1 : 0) + (a.lam != nullptr ? 2 : 0);
+        using K = void (*)(CombineArgs);
+        auto pick = [&](auto d) -> K {
+            constexpr int DA = decltype(d)::value;
+            switch (mode) {
+            case 0: return lse_combine_kernel<DA, false, false>;
+            case 1: return lse_combine_kernel<DA, true, false>;
+            case 2: return lse_combine_kernel<DA, false, true>;
+            default: return lse_combine_kernel<DA, true, true>;
+            }
+        };
+        K kern = nullptr;
         switch (a.D) {
-        case 64:
-            rot ? lse_combine_kernel<64, true><<<grid, block, 0, stream>>>(a)
-                : lse_combine_kernel<64, false><<<grid, block, 0, stream>>>(a);
-            break;
-        case 128:
-            rot ? lse_combine_kernel<128, true><<<grid, block, 0, stream>>>(a)
-                : lse_combine_kernel<128, false><<<grid, block, 0, stream>>>(a);
-            break;
-        case 256:
-            rot ? lse_combine_kernel<256, true><<<grid, block, 0, stream>>>(a)
-                : lse_combine_kernel<256, false><<<grid, block, 0, stream>>>(a);
-            break;
-        default:
-            return hipErrorInvalidValue;
+        case 64: kern = pick(std::integral_constant<int, 64>{}); break;
+        case 128: kern = pick(std::integral_constant<int, 128>{}); break;
+        case 256: kern = pick(std::integral_constant<int, 256>{}); break;
+        default: return hipErrorInvalidValue;
         }
+        kern<<<grid, block, 0, stream>>>(a);
     }
     return hipGetLastError();
 }

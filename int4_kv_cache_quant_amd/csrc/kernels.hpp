@@ -10,8 +10,8 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                  const float* signs, float rot_norm, const int32_t* pos,
-                                  hipStream_t stream);
+                                  const float* signs, float rot_norm, const float* lam,
+                                  const int32_t* pos, hipStream_t stream);
 
 // Split pass arguments shared by both variants.
 struct SplitArgs {
@@ -24,6 +24,7 @@ struct SplitArgs {
     float* vs;
     const float* signs;
     float rot_norm;
+    const float* lam;  // K's per-channel scale [D] (q is divided by it), or null
     const int32_t* lens;
     int max_len;
     float qscale;  // softmax scale * log2(e): scores are kept in the log2 domain
@@ -76,6 +77,7 @@ struct CombineArgs {
     float* vs;
     const float* signs;
     float rot_norm;
+    const float* lam;       // K's per-channel scale [D], or null
     float qscale;           // softmax scale * log2(e)
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);

@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const int32_t* __restrict__ pos, int pair_slots)
+    const float* __restrict__ lam, const int32_t* __restrict__ pos, int pair_slots)
 {
     constexpr int E = D / 64;
     constexpr int NG = D / kGroup;
@@ -80,6 +80,10 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = widen(k[src + e], dtype);
         if (signs) rotate_lane<D>(x, signs, rot_norm, lane);
+        if (lam) {  // K's per-channel scale, after the rotation
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = x[e] * lam[lane * E + e];
+        }
         int c[E];
         float sk = quantize_lane<D>(x, c, lane);
         uint8_t* krow = kc + row * (D / 2);
@@ -139,7 +143,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
                                               int n_new, int cap, size_t head, int p0, int t_tile, int t_end,
                                               uint8_t* __restrict__ kc, float* __restrict__ ks,
                                               uint8_t* __restrict__ vc, float* __restrict__ vs,
-                                              const float* __restrict__ signs, float rot_norm)
+                                              const float* __restrict__ signs, float rot_norm,
+                                              const float* __restrict__ lam)
 {
     constexpr int NG = D / kGroup;
     constexpr int LT = D / 8;  // K lanes per token
@@ -163,11 +168,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
         return mask;
     };
 
-    // issue every load first; the K signs of a lane are the same in every unit
-    float sg[8];
+    // issue every load first; the K signs and channel scales of a lane are
+    // the same in every unit
+    float sg[8], lm[8];
     if (signs) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sg[e] = signs[8 * (tid % LT) + e];
+    }
+    if (lam) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) lm[e] = lam[8 * (tid % LT) + e];
     }
     uint4 kraw[U], vraw[U];
 #pragma unroll
@@ -206,6 +216,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[e];
             rotate_signed<D, 8>(x, rot_norm, j);
+        }
+        if (lam) {  // K's per-channel scale, after the rotation
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * lm[e];
         }
         float sk;
         const uint32_t word = quantize_word8(x, sk);
@@ -250,7 +264,7 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const int32_t* __restrict__ pos)
+    const float* __restrict__ lam, const int32_t* __restrict__ pos)
 {
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
@@ -259,17 +273,19 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     if (t_tile >= t_end) return;  // block-uniform
     const size_t head = (size_t)b * H + h;
     if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
-        quantize_tile<D, DTYPE, true>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs, rot_norm);
+        quantize_tile<D, DTYPE, true>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs,
+                                      rot_norm, lam);
     else
-        quantize_tile<D, DTYPE, false>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs, rot_norm);
+        quantize_tile<D, DTYPE, false>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs,
+                                       rot_norm, lam);
 }
 
 }  // namespace
 
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                  const float* signs, float rot_norm, const int32_t* pos,
-                                  hipStream_t stream)
+                                  const float* signs, float rot_norm, const float* lam,
+                                  const int32_t* pos, hipStream_t stream)
 {
     if (D != 64 && D != 128 && D != 256) return hipErrorInvalidValue;
     const auto* kk = static_cast<const uint16_t*>(k);
@@ -278,8 +294,8 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         const int pair_slots = (n_new + 2) / 2;
         dim3 grid((pair_slots + 3) / 4, H, B), block(256);
         auto kern = D == 64 ? quantize_pair_kernel<64> : D == 128 ? quantize_pair_kernel<128> : quantize_pair_kernel<256>;
-        kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, pos,
-                                         pair_slots);
+        kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam,
+                                         pos, pair_slots);
     } else {
         // one block per tile touched: the range may start inside a tile
         const int tiles = (n_new + 2 * kTile - 2) / kTile;
@@ -288,7 +304,7 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
                                                                              : quantize_tile_kernel<256, 0>)
                                : (D == 64 ? quantize_tile_kernel<64, 1> : D == 128 ? quantize_tile_kernel<128, 1>
                                                                              : quantize_tile_kernel<256, 1>);
-        kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, pos);
+        kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam, pos);
     }
     return hipGetLastError();
 }

@@ -316,19 +316,23 @@ struct TileLoads {
     float sv[2][NG];             // V scales of token 4 r + (lane % 4)
 };
 
+// HILO: the query is not exact in fp16 (a rotated cache, or K's per-channel
+// scale divides it), so each q operand is an fp16 hi + lo pair and every
+// score MFMA is issued twice.
+//
 // K scales loaded per row where the registers allow it: not at head_dim 256
-// (eight groups per token) nor for two rotated heads, whose q operands
+// (eight groups per token) nor for two heads with hi + lo q operands, which
 // already fill the register file.
-template <int D, int P, bool ROT>
-constexpr bool kScaleRows = D <= 128 && !(ROT && P == 2);
+template <int D, int P, bool HILO>
+constexpr bool kScaleRows = D <= 128 && !(HILO && P == 2);
 
 // Where a wave refills the stage it has just read: after the tile's scores
 // (the reads have finished by then, so the wait before the copies costs
 // nothing), except where keeping the copy operands live across the scores
-// would spill registers (head_dim 256, two rotated heads); those refill
-// before computing.
-template <int D, int P, bool ROT>
-constexpr bool kRefillAfterScores = D <= 128 && !(ROT && P == 2);
+// would spill registers (head_dim 256, two heads with hi + lo q operands);
+// those refill before computing.
+template <int D, int P, bool HILO>
+constexpr bool kRefillAfterScores = D <= 128 && !(HILO && P == 2);
 
 // Waves per SIMD the register allocation must allow: 2 (up to 256 VGPRs)
 // except at head_dim 256, whose accumulators alone take 64 VGPRs per head.
@@ -340,7 +344,7 @@ constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 template <int D, int P, int W>
 constexpr int kStages = 2 * W * Stage<D, P>::BYTES <= 80 * 1024 ? 2 : 1;
 
-template <int D, int P, bool ROT, int W>
+template <int D, int P, bool HILO, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
 void split_mfma_kernel(SplitArgs a)
 {
@@ -368,7 +372,7 @@ void split_mfma_kernel(SplitArgs a)
 
     using St = Stage<D, P>;
     constexpr int NST = kStages<D, P, W>;
-    constexpr bool ROWS = kScaleRows<D, P, ROT>;
+    constexpr bool ROWS = kScaleRows<D, P, HILO>;
     static_assert((NST - 1) * St::COPIES <= 63, "vmcnt holds at most 63");
     const size_t head0 = (size_t)b * a.H + hk0;
     // the wave's LDS stages, contiguous per wave: stage s of wave w at
@@ -381,19 +385,27 @@ void split_mfma_kernel(SplitArgs a)
 
     // ---- q straight into registers, before any tile copy is queued: lane
     //      (n16, r) needs, per scale group g, channels 32 g + 8 r + 0..7 of
-    //      query head n16 (one 16-byte load), and the same signs when rotated;
-    //      lanes of unused columns load head 0 of the block and drop it
+    //      query head n16 (one 16-byte load), and the same signs when rotated
+    //      and channel scales when K has them; lanes of unused columns load
+    //      head 0 of the block and drop it
+    const bool rot = a.signs != nullptr, scaled = a.lam != nullptr;  // HILO when either holds
     uint4 qraw[NG];
-    float4 sgn[ROT ? NG : 1][2];
+    float4 sgn[HILO ? NG : 1][2], lmv[HILO ? NG : 1][2];
     {
         const uint16_t* qsrc =
             static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G + (col_valid ? n16 : 0)) * D;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             qraw[g] = *reinterpret_cast<const uint4*>(qsrc + 32 * g + 8 * r);
-            if constexpr (ROT) {
-                sgn[g][0] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r);
-                sgn[g][1] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r + 4);
+            if constexpr (HILO) {
+                if (rot) {
+                    sgn[g][0] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r);
+                    sgn[g][1] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r + 4);
+                }
+                if (scaled) {
+                    lmv[g][0] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r);
+                    lmv[g][1] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r + 4);
+                }
             }
         }
     }
@@ -454,10 +466,11 @@ void split_mfma_kernel(SplitArgs a)
     const int end = min(start + a.chunk, len);
     const int ntiles = (end - start + kTile - 1) / kTile;
 
-    // ---- q prologue, registers only: widen, and rotate like K when the
-    //      cache is (channel c = 32 g + 8 r + e: the butterflies over bits
-    //      0-2 and 5.. stay in the lane, bits 3 and 4 pair lanes 16 and 32
-    //      apart; the stages of a Walsh-Hadamard transform commute)
+    // ---- q prologue, registers only: widen, rotate like K when the cache
+    //      is (channel c = 32 g + 8 r + e: the butterflies over bits 0-2 and
+    //      5.. stay in the lane, bits 3 and 4 pair lanes 16 and 32 apart; the
+    //      stages of a Walsh-Hadamard transform commute), then divide by K's
+    //      channel scales when it has them
     float qx[NG][8];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -468,7 +481,7 @@ void split_mfma_kernel(SplitArgs a)
             qx[g][e] = col_valid ? widen(h16, a.dtype) : 0.0f;
         }
     }
-    if constexpr (ROT) {
+    if (HILO && rot) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const float sg[8] = {sgn[g][0].x, sgn[g][0].y, sgn[g][0].z, sgn[g][0].w,
@@ -510,10 +523,19 @@ void split_mfma_kernel(SplitArgs a)
                         qx[g + h][e] = lo - hi;
                     }
     }
+    if (HILO && scaled) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float lm[8] = {lmv[g][0].x, lmv[g][0].y, lmv[g][0].z, lmv[g][0].w,
+                                 lmv[g][1].x, lmv[g][1].y, lmv[g][1].z, lmv[g][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[g][e] = qx[g][e] / lm[e];
+        }
+    }
     // B operands of the score MFMAs, one per KV head: column n16 holds q of
     // query head n16 in the set of head jl and zeros in the others; k slot e
     // = channel 32 g + 8 r + kSlot[e].
-    half8_t qb[P][NG], qb_lo[ROT ? P : 1][ROT ? NG : 1];
+    half8_t qb[P][NG], qb_lo[HILO ? P : 1][HILO ? NG : 1];
     floatx4_t qinit4[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -529,7 +551,7 @@ void split_mfma_kernel(SplitArgs a)
             const float down = kShift[e] ? 0.0625f : 1.0f, up = kShift[e] ? 16.0f : 1.0f;
             hv[e] = (_Float16)((float)h16 * down);
             t += (float)hv[e] * up;
-            if (ROT) {
+            if (HILO) {
                 lv[e] = (_Float16)((float)l16 * down);
                 t += (float)lv[e] * up;
             }
@@ -540,14 +562,14 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 qb[j][g][e] = mine ? hv[e] : (_Float16)0.0f;
-                if (ROT) qb_lo[j][g][e] = mine ? lv[e] : (_Float16)0.0f;
+                if (HILO) qb_lo[j][g][e] = mine ? lv[e] : (_Float16)0.0f;
             }
         }
         // the score accumulator starts at -8 * 2^-24 * sum(q over the group)
         const float qi = -8.0f * 0x1p-24f * sum_xor32(sum_xor16(t));
         qinit4[g] = floatx4_t{qi, qi, qi, qi};
     }
-    const float qmul = (ROT ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
+    const float qmul = (HILO && rot ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
 
     float m_run = kNegInf;  // softmax reference of column n16 (>= its running max)
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
@@ -620,7 +642,7 @@ void split_mfma_kernel(SplitArgs a)
                 for (int j = 0; j < P; ++j) {
                     const half8_t A = unpack_codes(t.kw[j][s][g]);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[j][g], d, 0, 0, 0);
-                    if constexpr (ROT) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
+                    if constexpr (HILO) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
                 }
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
@@ -746,7 +768,7 @@ void split_mfma_kernel(SplitArgs a)
                 dma_tile(it + NST * W, st);
             }
         };
-        if constexpr (kRefillAfterScores<D, P, ROT>) {
+        if constexpr (kRefillAfterScores<D, P, HILO>) {
             compute_tile(t, it, refill);
         } else {
             refill();
@@ -823,7 +845,7 @@ void split_mfma_kernel(SplitArgs a)
 template <int D>
 constexpr int kBlockWaves = 4;
 
-template <int D, int P, bool ROT>
+template <int D, int P, bool HILO>
 hipError_t launch(const SplitArgs& a, hipStream_t stream)
 {
     constexpr int W = kBlockWaves<D>;
@@ -831,21 +853,22 @@ hipError_t launch(const SplitArgs& a, hipStream_t stream)
     const size_t lds = (size_t)kStages<D, P, W> * W * Stage<D, P>::BYTES;
     dim3 grid(a.num_splits, a.H / P, a.B), block(64 * W);
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&split_mfma_kernel<D, P, ROT, W>),
+        reinterpret_cast<const void*>(&split_mfma_kernel<D, P, HILO, W>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
-    split_mfma_kernel<D, P, ROT, W><<<grid, block, lds, stream>>>(a);
+    split_mfma_kernel<D, P, HILO, W><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 
 template <int D>
 hipError_t dispatch(const SplitArgs& a, hipStream_t stream)
 {
+    const bool hilo = a.signs != nullptr || a.lam != nullptr;  // q not exact in fp16
     if constexpr (D != 256) {  // head_dim 256 serves one KV head per wave
         if (split_mfma_heads_per_wave(a.D, a.Hq / a.H, a.H) == 2)
-            return a.signs ? launch<D, 2, true>(a, stream) : launch<D, 2, false>(a, stream);
+            return hilo ? launch<D, 2, true>(a, stream) : launch<D, 2, false>(a, stream);
     }
-    return a.signs ? launch<D, 1, true>(a, stream) : launch<D, 1, false>(a, stream);
+    return hilo ? launch<D, 1, true>(a, stream) : launch<D, 1, false>(a, stream);
 }
 
 }  // namespace

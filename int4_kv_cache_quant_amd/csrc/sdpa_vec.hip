@@ -103,7 +103,17 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
 #pragma unroll
     for (int hh = 0; hh < G; ++hh)
 #pragma unroll
-        for (int i = 0; i < QC; ++i) qr[hh][i] = q_lds[hh][32 * (i / 8) + 8 * q4 + i % 8] * qmul;
+        for (int i = 0; i < QC; ++i) qr[hh][i] = q_lds[hh][32 * (i / 8) + 8 * q4 + i % 8];
+    if (a.lam) {  // K holds lambda (.) k: divide q by K's channel scale
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+            for (int i = 0; i < QC; ++i) qr[hh][i] = qr[hh][i] / a.lam[32 * (i / 8) + 8 * q4 + i % 8];
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int i = 0; i < QC; ++i) qr[hh][i] = qr[hh][i] * qmul;
 
     const size_t head = (size_t)b * a.H + hk;
     const uint8_t* kbase = a.kc + head * a.cap * (D / 2) + q4 * (D / 8);

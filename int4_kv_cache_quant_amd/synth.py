@@ -16,7 +16,9 @@ Recipe (all workloads):
     of 0..D-1, shared by K and V, all heads and all tokens.
   * q ~ N(0, 1) in the same dtype; rotation signs are a seeded +-1 vector.
   * seed = 20260000 + 1000 * workload + 10 * layer + slot, slot in
-    {K: 0, V: 1, q: 2, lens: 3, signs: 4, outliers: 5}.
+    {K: 0, V: 1, q: 2, lens: 3, signs: 4, outliers: 5, channel scales: 6}.
+  * K's per-channel scale, where a run asks for one: log-uniform in [1/4, 4]
+    per channel, and 1 / the outlier multiplier on the outlier channels.
   * "T cached tokens" is the attended length: the cache is prefilled with T-1
     tokens, one token is appended at position T-1, and attention runs with
     lens = T.
@@ -27,7 +29,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-SLOT = {"k": 0, "v": 1, "q": 2, "lens": 3, "signs": 4, "outliers": 5}
+SLOT = {"k": 0, "v": 1, "q": 2, "lens": 3, "signs": 4, "outliers": 5, "chan_scale": 6}
 
 
 @dataclass(frozen=True)
@@ -85,6 +87,14 @@ def torch_dtype(name: str):
 def outlier_channels(w: Workload, layer: int) -> np.ndarray:
     rng = np.random.default_rng(seed(w.cfg, layer, "outliers"))
     return np.sort(rng.permutation(w.D)[: w.n_out])
+
+
+def chan_scale(w: Workload, layer: int) -> np.ndarray:
+    """A per-channel scale for K [D] float32 (an input: seeded, not fitted)."""
+    rng = np.random.default_rng(seed(w.cfg, layer, "chan_scale"))
+    lam = np.exp2(rng.uniform(-2.0, 2.0, w.D))
+    lam[outlier_channels(w, layer)] = 1.0 / w.out_mult
+    return lam.astype(np.float32)
 
 
 def rot_signs(w: Workload, layer: int) -> np.ndarray:

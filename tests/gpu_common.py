@@ -22,11 +22,12 @@ def to_bits(t):
     return synth.bits(t)
 
 
-def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True):
+def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True, chan_scale=None):
     """Quantise K/V [B, H, T, D] (device) into a new cache: prefill T-1 tokens
     (optionally in chunks), then append the last token on its own."""
     B, H, T, D = k.shape
-    cache = otq.Int4KVCache(B, H, D, capacity, device=k.device, rot_signs=signs)
+    cache = otq.Int4KVCache(B, H, D, capacity, device=k.device, rot_signs=signs,
+                            chan_scale=chan_scale)
     n_pre = T - 1 if append_last else T
     step = n_pre if prefill_chunk is None else prefill_chunk
     for t0 in range(0, n_pre, max(step, 1)):
@@ -46,9 +47,10 @@ def host_cache(cache):
             layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D), cache.v_scales.cpu().numpy())
 
 
-def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8):
+def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=None):
     kb, vb = to_bits(k), to_bits(v)
-    kc, ks = oracle.quantize(kb, dtype, signs=signs, rot_norm=rot_norm, threads=threads)
+    kc, ks = oracle.quantize(kb, dtype, signs=signs, rot_norm=rot_norm, threads=threads,
+                             chan_scale=chan_scale)
     vc, vs = oracle.quantize(vb, dtype, threads=threads)
     return kc, ks, vc, vs
 
@@ -77,3 +79,13 @@ def errors(out, ref):
 
 def rot_norm32(D):
     return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def chan_scales(D, seed, outliers=()):
+    """A per-channel scale for K: log-uniform in [1/4, 4], and 1/10 on the
+    given outlier channels (whose values the tests multiply by 10)."""
+    g = torch.Generator().manual_seed(seed)
+    lam = torch.exp2(torch.rand(D, generator=g) * 4.0 - 2.0)
+    for c in outliers:
+        lam[c] = 0.1
+    return lam.to(torch.float32)

@@ -18,7 +18,7 @@ import int4_kv_cache_quant_amd as otq
 import oracle
 from int4_kv_cache_quant_amd import layout
 
-from gpu_common import (MAX_ABS, REL_L2, build_cache, compare_codes, errors, host_cache,
+from gpu_common import (MAX_ABS, REL_L2, build_cache, chan_scales, compare_codes, errors, host_cache,
                         oracle_cache, rot_norm32, say, to_bits)
 
 pytestmark = pytest.mark.gpu
@@ -49,7 +49,7 @@ def _poison(cache, lens):
 
 
 def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, seed=0, steps=1,
-         variant=otq.OTQ_VARIANT_MFMA):
+         variant=otq.OTQ_VARIANT_MFMA, scaled=False):
     g = torch.Generator().manual_seed(seed)
     Hq = G * Hkv
     T = max(lens) + steps - 1
@@ -59,11 +59,15 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
     v[..., 3] *= 10
     k, v = k.to(dtype), v.to(dtype)
     signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if rotate else None
+    lam = chan_scales(D, seed, outliers=(3,)) if scaled else None
+    lam_np = None if lam is None else lam.numpy()
     name = "fp16" if dtype == torch.float16 else "bf16"
     scale = 1.0 / math.sqrt(D)
     cache = build_cache(k[:, :, :T].to(DEV).contiguous(), v[:, :, :T].to(DEV).contiguous(), cap,
-                        signs=None if signs is None else signs.to(DEV), append_last=False)
-    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D))
+                        signs=None if signs is None else signs.to(DEV), append_last=False,
+                        chan_scale=None if lam is None else lam.to(DEV))
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
+                             chan_scale=lam_np)
     for step in range(steps):
         cur = [n + step for n in lens]
         _poison(cache, cur)
@@ -75,7 +79,8 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
         q = torch.randn((B, Hq, D), generator=g).to(dtype)
         max_len = max(1, max(cur))
         plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
-        say(f"fused B={B} G={G} Hkv={Hkv} D={D} lens={cur} chunk={plan.chunk} rotate={rotate}")
+        say(f"fused B={B} G={G} Hkv={Hkv} D={D} lens={cur} chunk={plan.chunk} rotate={rotate} "
+            f"scaled={scaled}")
         out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max_len, scale, plan=plan)
         torch.cuda.synchronize()
         got_cache = host_cache(cache)
@@ -89,7 +94,7 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
         kc, ks, vc, vs = ref_cache
         ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(cur, np.int32), scale,
                           signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                          threads=8)
+                          threads=8, chan_scale=lam_np)
         ma, rel = errors(out.cpu().numpy(), ref)
         say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
         assert ma <= MAX_ABS and rel <= REL_L2
@@ -101,6 +106,15 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
 def test_fused_append_parity(D, G, rotate):
     # new tokens at an odd and an even position, in the middle of a chunk
     _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=D + G + rotate)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_fused_append_chan_scale(D, G, rotate):
+    """K with a per-channel scale: the combine quantises the new token with
+    it and divides q by it for the token's score."""
+    _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=7 * D + G + rotate, scaled=True)
 
 
 @pytest.mark.parametrize("lens", [[1, 2], [129, 128], [257, 33], [32, 31]])
@@ -116,6 +130,8 @@ def test_fused_append_consecutive_steps():
 
 
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64)])
-def test_fused_append_vector_variant(G, D):
+@pytest.mark.parametrize("scaled", [False, True])
+def test_fused_append_vector_variant(G, D, scaled):
     """The same call on the vector split variant."""
-    _run(2, G, 2, D, 320, [300, 77], chunk=128, seed=G + D, variant=otq.OTQ_VARIANT_VECTOR)
+    _run(2, G, 2, D, 320, [300, 77], chunk=128, seed=G + D + scaled, variant=otq.OTQ_VARIANT_VECTOR,
+         scaled=scaled)

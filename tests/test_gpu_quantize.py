@@ -8,8 +8,8 @@ import torch
 import int4_kv_cache_quant_amd as otq
 from int4_kv_cache_quant_amd import synth
 
-from gpu_common import (build_cache, compare_codes, host_cache, oracle_cache, rot_norm32, say,
-                        to_bits)
+from gpu_common import (build_cache, chan_scales, compare_codes, host_cache, oracle_cache, rot_norm32,
+                        say, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -41,6 +41,29 @@ def test_quantize_bit_exact(D, dtype, rotate):
     name = "fp16" if dtype == torch.float16 else "bf16"
     ref = oracle_cache(k.cpu(), v.cpu(), name, None if signs is None else signs.cpu().numpy(),
                        rot_norm32(D))
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_quantize_chan_scale_bit_exact(D, dtype, rotate):
+    """K's per-channel scale, after the rotation: chunks of 19 tokens (the
+    bulk kernel) and a last single token (the small-append kernel)."""
+    B, H, T, cap = 2, 3, 77, 96
+    say(f"quantize chan_scale D={D} dtype={dtype} rotate={rotate}")
+    k, v = _rand_kv(B, H, T, D, dtype, seed=D + 11 * rotate + 5)
+    signs = None
+    if rotate:
+        s = torch.where(torch.rand(D, generator=torch.Generator().manual_seed(D + 1)) < 0.5, -1.0, 1.0)
+        signs = s.to(DEV)
+    lam = chan_scales(D, D + rotate, outliers=(3,))
+    cache = build_cache(k, v, cap, signs=signs, prefill_chunk=19, chan_scale=lam.to(DEV))
+    torch.cuda.synchronize()
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    ref = oracle_cache(k.cpu(), v.cpu(), name, None if signs is None else signs.cpu().numpy(),
+                       rot_norm32(D), chan_scale=lam.numpy())
     bad = compare_codes(host_cache(cache), ref, T)
     assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
 

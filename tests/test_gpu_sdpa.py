@@ -14,7 +14,7 @@ import int4_kv_cache_quant_amd as otq
 import oracle
 from int4_kv_cache_quant_amd import synth
 
-from gpu_common import (MAX_ABS, REL_L2, build_cache, compare_codes, errors, host_cache,
+from gpu_common import (MAX_ABS, REL_L2, build_cache, chan_scales, compare_codes, errors, host_cache,
                         oracle_cache, rot_norm32, say, to_bits)
 
 pytestmark = pytest.mark.gpu
@@ -22,11 +22,13 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spikes=(), beta=0.0):
+def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spikes=(), beta=0.0,
+          scaled=False):
     g = torch.Generator().manual_seed(seed)
     x = torch.randn((2, B, Hkv, cap, D), generator=g) * sigma
     oc = torch.randperm(D, generator=g)[:n_out]
     x[..., oc] *= 10
+    lam = chan_scales(D, seed, outliers=[int(c) for c in oc]) if scaled else None
     q = torch.randn((B, Hq, D), generator=g)
     # score spikes: K of the given tokens = beta * unit vector of the first
     # query head of the group, so that head's score there exceeds every other
@@ -41,30 +43,34 @@ def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spi
     signs = None
     if rotate:
         signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
-    return x[0], x[1], q, signs
+    return x[0], x[1], q, signs, lam
 
 
 def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
-         rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0):
-    k, v, q, signs = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate, spikes=spikes, beta=beta)
+         rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0,
+         scaled=False):
+    k, v, q, signs, lam = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate, spikes=spikes,
+                                beta=beta, scaled=scaled)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     name = "fp16" if dtype == torch.float16 else "bf16"
+    lam_np = None if lam is None else lam.numpy()
     cache = build_cache(k.to(DEV), v.to(DEV), cap, signs=None if signs is None else signs.to(DEV),
-                        prefill_chunk=max(1, cap // 3))
+                        prefill_chunk=max(1, cap // 3), chan_scale=None if lam is None else lam.to(DEV))
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     max_len = max(1, int(max(lens)))
     plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
     say(f"sdpa B={B} Hq={Hq} Hkv={Hkv} D={D} cap={cap} chunk={plan.chunk} "
-        f"splits={plan.num_splits} variant={plan.variant} rotate={rotate}")
+        f"splits={plan.num_splits} variant={plan.variant} rotate={rotate} scaled={scaled}")
     out = cache.decode(q.to(DEV), lens_t, max_len, scale, plan=plan)
     torch.cuda.synchronize()
-    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D))
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
+                             chan_scale=lam_np)
     assert compare_codes(host_cache(cache), ref_cache, cap) == {
         "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
     kc, ks, vc, vs = ref_cache
     ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(lens, np.int32), scale,
                       signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                      rows=rows, threads=8)
+                      rows=rows, threads=8, chan_scale=lam_np)
     got = out.cpu().numpy().astype(np.float64)
     if rows is not None:
         got = got.reshape(-1, D)[rows]
@@ -93,6 +99,19 @@ def test_sdpa_small_parity_mfma(D, G, rotate):
     Hkv = 2
     got, ref, _ = _run(2, G * Hkv, Hkv, D, 352, [350, 45], seed=3 * D + G + rotate, variant=MF,
                        chunk=128, rotate=rotate)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("variant,G,D", [(VEC, 1, 128), (VEC, 2, 64), (VEC, 4, 128), (MF, 1, 64),
+                                         (MF, 4, 128), (MF, 8, 128), (MF, 16, 64), (MF, 2, 256)])
+@pytest.mark.parametrize("rotate", [False, True])
+def test_sdpa_chan_scale(variant, G, D, rotate):
+    """K with a per-channel scale (1/10 on its outlier channels): multi-tile
+    ragged lengths, both variants, one and two heads per MFMA wave."""
+    got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 77], seed=31 + G + D + rotate, rotate=rotate,
+                       chunk=128, variant=variant, scaled=True)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
@@ -174,7 +193,7 @@ def test_sdpa_fp16_rotated_and_scale_one():
 
 
 def test_sdpa_deterministic():
-    k, v, q, _ = _case(1, 2, 1, 128, 512, torch.bfloat16, 9)
+    k, v, q, _, _ = _case(1, 2, 1, 128, 512, torch.bfloat16, 9)
     cache = build_cache(k.to(DEV), v.to(DEV), 512)
     lens = torch.tensor([512], dtype=torch.int32, device=DEV)
     a = cache.decode(q.to(DEV), lens, 512, 0.1)

@@ -37,6 +37,8 @@ def _load():
     lib.oracle_srht_f32.restype = None
     lib.oracle_srht_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
     lib.oracle_srht_f64.restype = None
+    lib.oracle_unrotate_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
+    lib.oracle_unrotate_f64.restype = None
     lib.oracle_quantize_vector.argtypes = [P, ctypes.c_int, P, P]
     lib.oracle_quantize_vector.restype = None
     lib.oracle_quantize_rows.argtypes = [P, ctypes.c_int, ctypes.c_long, ctypes.c_int,
@@ -44,11 +46,11 @@ def _load():
     lib.oracle_quantize_rows.restype = ctypes.c_int
     lib.oracle_attend_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                       ctypes.c_long, ctypes.c_double, P, ctypes.c_float,
-                                      P, P, P]
+                                      P, P, P, P]
     lib.oracle_attend_row.restype = None
     lib.oracle_sdpa.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_long, P, P, P, P, P,
-                                ctypes.c_double, P, ctypes.c_float, P, P, ctypes.c_long,
+                                ctypes.c_double, P, ctypes.c_float, P, P, P, ctypes.c_long,
                                 P, ctypes.c_int]
     lib.oracle_sdpa.restype = ctypes.c_int
     _lib = lib
@@ -92,6 +94,15 @@ def srht_f64(x, signs, c):
     return y
 
 
+def unrotate_f64(y, signs, c):
+    """The inverse rotation s (.) (c H y) in fp64."""
+    lib = _load()
+    y = _c(y, np.float64).copy()
+    s = _c(signs, np.float32)
+    lib.oracle_unrotate_f64(_ptr(y), _ptr(s), y.shape[-1], float(c))
+    return y
+
+
 def quantize_vector(x):
     """One fp32 vector -> (codes uint8[D/2], scales float32[D/32])."""
     lib = _load()
@@ -124,7 +135,8 @@ def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None):
     return codes, scales
 
 
-def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0, chan_scale=None):
+def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0, chan_scale=None,
+               v_signs=None):
     lib = _load()
     q_bits = _c(q_bits, np.uint16)
     D = q_bits.shape[-1]
@@ -132,21 +144,23 @@ def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0
     ks, vs = _c(ks, np.float32), _c(vs, np.float32)
     s = None if signs is None else _c(signs, np.float32)
     lam = None if chan_scale is None else _c(chan_scale, np.float32)
+    vsg = None if v_signs is None else _c(v_signs, np.float32)
     work = np.zeros(max(int(T), 1), np.float64)
     out = np.zeros(D, np.float64)
     lib.oracle_attend_row(_ptr(q_bits), DTYPES[dtype], D, _ptr(kc), _ptr(ks), _ptr(vc),
                           _ptr(vs), int(T), float(scale), _ptr(s),
-                          float(np.float32(rot_norm)), _ptr(lam), _ptr(work), _ptr(out))
+                          float(np.float32(rot_norm)), _ptr(lam), _ptr(vsg), _ptr(work), _ptr(out))
     return out
 
 
 def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
-         signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None):
+         signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None, v_signs=None):
     """Decode attention over a plain-layout cache.
 
     q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D/2]; scales
     [B, Hkv, cap, D/32]; lens [B]; chan_scale: the K cache's per-channel
-    scale lambda [D] or None.  Returns float64 [B, Hq, D], or [len(rows), D]
+    scale lambda [D] or None; v_signs: the signs V was rotated with (same
+    rot_norm as K) or None.  Returns float64 [B, Hq, D], or [len(rows), D]
     for the listed rows (row = b * Hq + h).
     """
     lib = _load()
@@ -158,6 +172,7 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
     lens = _c(lens, np.int32)
     s = None if signs is None else _c(signs, np.float32)
     lam = None if chan_scale is None else _c(chan_scale, np.float32)
+    vsg = None if v_signs is None else _c(v_signs, np.float32)
     if rows is None:
         out = np.zeros((B, Hq, D), np.float64)
         r = None
@@ -168,8 +183,8 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
         out = np.zeros((nrows, D), np.float64)
     rc = lib.oracle_sdpa(_ptr(q_bits), DTYPES[dtype], B, Hq, Hkv, D, cap, _ptr(kc), _ptr(ks),
                          _ptr(vc), _ptr(vs), _ptr(lens), float(scale), _ptr(s),
-                         float(np.float32(rot_norm)), _ptr(lam), _ptr(r), nrows, _ptr(out),
-                         int(threads))
+                         float(np.float32(rot_norm)), _ptr(lam), _ptr(vsg), _ptr(r), nrows,
+                         _ptr(out), int(threads))
     if rc != 0:
         raise ValueError("oracle_sdpa rejected its arguments")
     return out

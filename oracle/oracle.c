@@ -35,6 +35,13 @@
  * anywhere in the fp32 quantiser (this file is built with
  * -ffp-contract=off).
  *
+ * Rotated V (the same page's rotate-then-quantise applied to V as well,
+ * with the output brought back by the inverse rotation): V rows may be
+ * quantised with signs of their own, y = c * H_D * (s_v (.) v) exactly as K
+ * is; attention then dequantises every V row back to the original basis in
+ * fp64, v^ = s_v (.) (c * H_D * (code * scale)), since (c H_D S)^-1 =
+ * S H_D c for c = 1/sqrt(D) and S = diag(s_v) of +-1.
+ *
  * Per-channel scale ("SRFT + int4 KV-cache", core-method section: a
  * per-coordinate scale lambda is applied after the rotation and before the
  * group abs-max).  Reading: when a scale vector is given, the quantised
@@ -121,6 +128,20 @@ void oracle_srht_f64(double *y, const float *signs, int D, double c)
             }
     for (int i = 0; i < D; ++i)
         y[i] = y[i] * c;
+}
+
+/* The inverse rotation in fp64: y <- s (.) (c * H_D * y). */
+void oracle_unrotate_f64(double *y, const float *signs, int D, double c)
+{
+    for (int h = 1; h < D; h *= 2)
+        for (int blk = 0; blk < D; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                double a = y[j], b = y[j + h];
+                y[j] = a + b;
+                y[j + h] = a - b;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c * (double)signs[i];
 }
 
 /* ---------------------------------------------------------------- quantise */
@@ -238,6 +259,8 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
  *              per-channel scale is given
  *   S_t      = scale_attn * sum_i q'_i K^[t][i]
  *   w_t      = exp(S_t - max_u S_u)
+ *   V^[t][i] = code * scale, brought back to the original basis
+ *              (oracle_unrotate_f64) when v_signs != NULL
  *   out      = sum_t w_t V^[t] / sum_t w_t
  * T == 0 gives out = 0.  q' is q rotated in fp64 when signs != NULL.
  * work must hold T doubles. */
@@ -245,9 +268,10 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
                        const uint8_t *kc, const float *ks,
                        const uint8_t *vc, const float *vs, long T,
                        double scale, const float *signs, float rot_norm,
-                       const float *chan_scale, double *work, double *out)
+                       const float *chan_scale, const float *v_signs, double *work,
+                       double *out)
 {
-    double qd[1024], kd[1024];
+    double qd[1024], kd[1024], vd[1024];
     int ng = D / ORACLE_GROUP;
     for (int i = 0; i < D; ++i)
         qd[i] = (double)widen(q[i], dtype);
@@ -281,7 +305,11 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
         const uint8_t *row = vc + t * (D / 2);
         const float *srow = vs + t * ng;
         for (int i = 0; i < D; ++i)
-            out[i] += w * ((double)nibble(row, i) * (double)srow[i / ORACLE_GROUP]);
+            vd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
+        if (v_signs)
+            oracle_unrotate_f64(vd, v_signs, D, (double)rot_norm);
+        for (int i = 0; i < D; ++i)
+            out[i] += w * vd[i];
     }
     for (int i = 0; i < D; ++i)
         out[i] /= l;
@@ -298,6 +326,7 @@ struct attn_job {
     const float *signs;
     float rot_norm;
     const float *chan_scale;
+    const float *v_signs;
     double *out;
     const int32_t *rows;
     long r0, r1;
@@ -320,7 +349,7 @@ static void *attn_worker(void *arg)
         oracle_attend_row(j->q + (size_t)row * j->D, j->dtype, j->D,
                           j->kc + head * j->cap * (j->D / 2), j->ks + head * j->cap * (j->D / ORACLE_GROUP),
                           j->vc + head * j->cap * (j->D / 2), j->vs + head * j->cap * (j->D / ORACLE_GROUP),
-                          T, j->scale, j->signs, j->rot_norm, j->chan_scale, work,
+                          T, j->scale, j->signs, j->rot_norm, j->chan_scale, j->v_signs, work,
                           j->out + (size_t)r * j->D);
     }
     free(work);
@@ -335,8 +364,8 @@ static void *attn_worker(void *arg)
 int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, long cap,
                 const uint8_t *kc, const float *ks, const uint8_t *vc, const float *vs,
                 const int32_t *lens, double scale, const float *signs, float rot_norm,
-                const float *chan_scale, const int32_t *rows, long nrows, double *out,
-                int nthreads)
+                const float *chan_scale, const float *v_signs, const int32_t *rows, long nrows,
+                double *out, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
         D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1)
@@ -355,7 +384,7 @@ int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, lon
         if (r0 >= r1)
             break;
         jobs[t] = (struct attn_job){q, dtype, B, Hq, Hkv, D, cap, kc, vc, ks, vs, lens,
-                                    scale, signs, rot_norm, chan_scale, out, rows, r0, r1};
+                                    scale, signs, rot_norm, chan_scale, v_signs, out, rows, r0, r1};
         if (nthreads == 1) {
             attn_worker(&jobs[t]);
         } else {

@@ -125,6 +125,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--chan-scale", action="store_true",
                     help="give K a per-channel scale (seeded; 1/multiplier on the outlier channels)")
+    ap.add_argument("--v-rotate", action="store_true",
+                    help="rotate V too (seeded signs); outputs are brought back by the inverse rotation")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
@@ -180,8 +182,9 @@ def main():
     for l in range(L):
         signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if w.rotate else None
         lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if args.chan_scale else None
+        vsg = torch.from_numpy(synth.v_rot_signs(w, l)).to(dev) if args.v_rotate else None
         cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs,
-                                chan_scale=lam)
+                                chan_scale=lam, v_rot_signs=vsg)
         k = synth.kv(w, l, "k", device=dev)
         v = synth.kv(w, l, "v", device=dev)
         lens = synth.lens(w, l)
@@ -196,7 +199,8 @@ def main():
         v_new.append(v[ar, :, idx].contiguous())
         if l == 0 and not args.no_cpu:
             host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy(),
-                        None if lam is None else lam.cpu().numpy())
+                        None if lam is None else lam.cpu().numpy(),
+                        None if vsg is None else vsg.cpu().numpy())
         del k, v
         caches.append(cache)
         qs.append(synth.query(w, l, device=dev))
@@ -324,7 +328,7 @@ def main():
     bulk_in = [(synth.kv(w, i, "k", T=n_bulk, device=dev), synth.kv(w, i, "v", T=n_bulk, device=dev))
                for i in range(n_chunks)]
     scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs,
-                              chan_scale=caches[0].chan_scale)
+                              chan_scale=caches[0].chan_scale, v_rot_signs=caches[0].v_rot_signs)
     bulk_pos = [torch.full((w.B,), i * n_bulk, dtype=torch.int32, device=dev) for i in range(n_chunks)]
 
     def bulk_pass():
@@ -367,17 +371,17 @@ def main():
     if host_kv0 is not None:
         import oracle
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        kb, vb, sg, lam0 = host_kv0
+        kb, vb, sg, lam0, vsg0 = host_kv0
         t = time.time()
         kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
                                  chan_scale=lam0)
-        vc, vs = oracle.quantize(vb, w.dtype, threads=threads)
+        vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads)
         log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
         lens0 = synth.lens(w, 0)
         q0 = synth.bits(qs[0])
         t = time.perf_counter()
         ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
-                          rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0)
+                          rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0, v_signs=vsg0)
         cpu_s = time.perf_counter() - t
         got = outs[0].cpu().numpy().astype(np.float64)
         err = got - ref
@@ -409,6 +413,7 @@ def main():
             "cache_gib": round(cache_bytes / 2**30, 3), "chunk": plan.chunk,
             "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
             "graph": graph is not None, "k_chan_scale": bool(args.chan_scale),
+            "v_rotated": bool(args.v_rotate),
             "step": "per layer: the split pass over the cached tokens, then the combine pass that "
                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)",
         },

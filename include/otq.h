@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 2
+#define OTQ_ABI_VERSION 3
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -74,6 +74,10 @@ typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
  *     z_i = x_i * k_chan_scale[i]      (one fp32 multiply)
  * and attention reads K^_i = code_i * s_g / k_chan_scale[i]: the query is
  * divided by the scale inside otq_sdpa_int4_decode.
+ * V, when v_rot_signs != NULL, is rotated before quantisation exactly as K
+ * is (its own signs, the same rot_norm), and the attention output is brought
+ * back to the original basis, out <- v_rot_signs (.) (rot_norm * H out),
+ * the inverse of that rotation (rot_norm = fp32(1/sqrt(head_dim))).
  *
  * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
  *  Codes are two's-complement int4 nibbles; a byte holds an even channel in
@@ -106,6 +110,7 @@ typedef struct otq_cache {
     const float *k_rot_signs; /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
     float rot_norm;           /* used only when k_rot_signs != NULL */
     const float *k_chan_scale; /* device [D] fp32 lambda, finite and > 0, 16-byte aligned, or NULL */
+    const float *v_rot_signs;  /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
 } otq_cache;
 
 /* Human-readable name of a status code (static string). */

@@ -45,7 +45,7 @@ class otq_cache(ctypes.Structure):
         ("k_codes", ctypes.c_void_p), ("k_scales", ctypes.c_void_p),
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_rot_signs", ctypes.c_void_p), ("rot_norm", ctypes.c_float),
-        ("k_chan_scale", ctypes.c_void_p),
+        ("k_chan_scale", ctypes.c_void_p), ("v_rot_signs", ctypes.c_void_p),
     ]
 
 
@@ -236,10 +236,12 @@ class Int4KVCache:
     ``rot_signs`` (device float32 [D] of +-1) turns on the K rotation; the
     normalisation is fp32(1/sqrt(D)).  ``chan_scale`` (float32 [D], > 0)
     turns on K's per-channel scale, applied after the rotation.
+    ``v_rot_signs`` (float32 [D] of +-1) turns on V's rotation, whose inverse
+    the attention calls apply to their outputs.
     """
 
     def __init__(self, batch, num_kv_heads, head_dim, capacity, device="cuda", rot_signs=None,
-                 chan_scale=None):
+                 chan_scale=None, v_rot_signs=None):
         cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity)
         self.shape = (batch, num_kv_heads, head_dim, capacity)
         g = head_dim // OTQ_GROUP
@@ -252,12 +254,15 @@ class Int4KVCache:
         self.rot_norm = float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
         self.chan_scale = (None if chan_scale is None
                            else chan_scale.to(device=device, dtype=torch.float32).contiguous())
+        self.v_rot_signs = (None if v_rot_signs is None
+                            else v_rot_signs.to(device=device, dtype=torch.float32).contiguous())
         self.desc = otq_cache(batch, num_kv_heads, head_dim, capacity,
                               self.k_codes.data_ptr(), self.k_scales.data_ptr(),
                               self.v_codes.data_ptr(), self.v_scales.data_ptr(),
                               None if self.rot_signs is None else self.rot_signs.data_ptr(),
                               self.rot_norm,
-                              None if self.chan_scale is None else self.chan_scale.data_ptr())
+                              None if self.chan_scale is None else self.chan_scale.data_ptr(),
+                              None if self.v_rot_signs is None else self.v_rot_signs.data_ptr())
 
     @property
     def nbytes(self):

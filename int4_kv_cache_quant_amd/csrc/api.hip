@@ -38,7 +38,8 @@ int check_cache(const otq_cache* c)
     if (rc != OTQ_OK) return rc;
     if (!c->k_codes || !c->k_scales || !c->v_codes || !c->v_scales) return OTQ_EINVAL;
     // the per-channel vectors are read 4 floats at a time
-    if ((((uintptr_t)c->k_rot_signs) & 15) != 0 || (((uintptr_t)c->k_chan_scale) & 15) != 0)
+    if ((((uintptr_t)c->k_rot_signs) & 15) != 0 || (((uintptr_t)c->k_chan_scale) & 15) != 0 ||
+        (((uintptr_t)c->v_rot_signs) & 15) != 0)
         return OTQ_EINVAL;
     return OTQ_OK;
 }
@@ -164,7 +165,7 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     const hipError_t e = otq::launch_quantize_append(
         k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
         cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
-        cache->rot_norm, cache->k_chan_scale, pos, static_cast<hipStream_t>(stream));
+        cache->rot_norm, cache->k_chan_scale, cache->v_rot_signs, pos, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
@@ -288,8 +289,12 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.signs = cache->k_rot_signs;
     a.rot_norm = cache->rot_norm;
     a.lam = cache->k_chan_scale;
+    a.vsigns = cache->v_rot_signs;
     a.qscale = scale * otq::kLog2eHost;
-    const hipError_t e = otq::launch_lse_combine(a, s);
+    hipError_t e = otq::launch_lse_combine(a, s);
+    // V rotated: bring the output back to the original basis
+    if (e == hipSuccess && cache->v_rot_signs)
+        e = otq::launch_unrotate_rows(out, a.B * a.Hq, a.D, cache->v_rot_signs, cache->rot_norm, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 

@@ -60,7 +60,7 @@ __device__ __forceinline__ float fwht_thread(float y, float* xch)
 // running (m, l, o) (the same merge rule as above), then the block merges the
 // threads' triples: one pass over the partials.  DA = head_dim when the
 // block also appends the new token (0 otherwise).
-template <int DA, bool ROT, bool LAM>
+template <int DA, bool ROT, bool LAM, bool VROT>
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
 {
     __shared__ float red_m[kThreads / 64];
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     // past D work on channel D - 1 and write nothing), loaded before lens[b]
     // like the first splits below
     [[maybe_unused]] uint16_t kx = 0, vx = 0, qx = 0;
-    [[maybe_unused]] float sg = 1.0f, lm = 1.0f;
+    [[maybe_unused]] float sg = 1.0f, lm = 1.0f, vsg = 1.0f;
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
     if constexpr (APPEND) {
@@ -96,6 +96,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         qx = static_cast<const uint16_t*>(a.q)[(size_t)row * DA + ch];
         if (ROT) sg = a.signs[ch];
         if (LAM) lm = a.lam[ch];  // K's channel scale
+        if (VROT) vsg = a.vsigns[ch];
         // one block per KV head writes the token: the first query head's,
         // first channel slice
         writer = h % G == 0 && blockIdx.y == 0 && tid < DA;
@@ -165,6 +166,11 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         // 32-lane groups are this vector's 32-channel groups
         const float sk = quantize_lane<64>(xk, ck, lane);
         float xv[1] = {widen(vx, a.dtype)};
+        if (VROT) {  // V rotated as K is, with its own signs
+            xv[0] = xv[0] * vsg;
+            xv[0] = fwht_thread<DA>(xv[0], xch);
+            xv[0] = xv[0] * a.rot_norm;
+        }
         int cv[1];
         const float sv = quantize_lane<64>(xv, cv, lane);
         if (writer) {
@@ -200,7 +206,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         if (LAM) y = y / lm;
         const float kd = (float)ck[0] * sk;
         s_new = group_sum<64>(tid < DA ? y * kd : 0.0f);  // this wave's part of q' . k^
-        if (ROT && DA > 64) __syncthreads();  // the butterflies' last reads of xch are done
+        if ((ROT || VROT) && DA > 64) __syncthreads();  // the butterflies' last reads of xch are done
         if (tid < DA) xch[tid] = (float)cv[0] * sv;
         if (lane == 0) red_s[wave] = s_new;
     }
@@ -252,24 +258,62 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     }
 }
 
+// One wave per output row: out <- vsigns (.) (rot_norm * H out), the inverse
+// of V's rotation (H is symmetric and H H = D I, so (c H S)^-1 = S H c for
+// c = 1/sqrt(D)).  Lane l owns elements [l E, l E + E), E = D / 64.
+template <int D>
+__global__ __launch_bounds__(256) void unrotate_rows_kernel(float* __restrict__ out, int rows,
+                                                            const float* __restrict__ vsigns, float rot_norm)
+{
+    constexpr int E = D / 64;
+    const int lane = threadIdx.x & 63;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;  // wave-uniform
+    float* o = out + (size_t)row * D + lane * E;
+    float y[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = o[e];
+    rotate_signed<D, E>(y, rot_norm, lane);
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = y[e] * vsigns[lane * E + e];
+}
+
 }  // namespace
+
+hipError_t launch_unrotate_rows(float* out, int rows, int D, const float* vsigns, float rot_norm,
+                                hipStream_t stream)
+{
+    if (rows <= 0) return hipSuccess;
+    dim3 grid((rows + 3) / 4), block(256);
+    switch (D) {
+    case 64: unrotate_rows_kernel<64><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
+    case 128: unrotate_rows_kernel<128><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
+    case 256: unrotate_rows_kernel<256><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
 
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
 {
     if (a.D % kCh != 0) return hipErrorInvalidValue;
     dim3 grid(a.B * a.Hq, a.D / kCh), block(kThreads);
     if (a.k_new == nullptr) {
-        lse_combine_kernel<0, false, false><<<grid, block, 0, stream>>>(a);
+        lse_combine_kernel<0, false, false, false><<<grid, block, 0, stream>>>(a);
     } else {
-        const int mode = (a.signs != nullptr ? 1 : 0) + (a.lam != nullptr ? 2 : 0);
+        const int mode = (a.signs != nullptr ? 1 : 0) + (a.lam != nullptr ? 2 : 0) + (a.vsigns != nullptr ? 4 : 0);
         using K = void (*)(CombineArgs);
         auto pick = [&](auto d) -> K {
             constexpr int DA = decltype(d)::value;
             switch (mode) {
-            case 0: return lse_combine_kernel<DA, false, false>;
-            case 1: return lse_combine_kernel<DA, true, false>;
-            case 2: return lse_combine_kernel<DA, false, true>;
-            default: return lse_combine_kernel<DA, true, true>;
+            case 0: return lse_combine_kernel<DA, false, false, false>;
+            case 1: return lse_combine_kernel<DA, true, false, false>;
+            case 2: return lse_combine_kernel<DA, false, true, false>;
+            case 3: return lse_combine_kernel<DA, true, true, false>;
+            case 4: return lse_combine_kernel<DA, false, false, true>;
+            case 5: return lse_combine_kernel<DA, true, false, true>;
+            case 6: return lse_combine_kernel<DA, false, true, true>;
+            default: return lse_combine_kernel<DA, true, true, true>;
             }
         };
         K kern = nullptr;

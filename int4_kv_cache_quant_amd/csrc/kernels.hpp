@@ -11,7 +11,7 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                   const float* signs, float rot_norm, const float* lam,
-                                  const int32_t* pos, hipStream_t stream);
+                                  const float* vsigns, const int32_t* pos, hipStream_t stream);
 
 // Split pass arguments shared by both variants.
 struct SplitArgs {
@@ -78,8 +78,14 @@ struct CombineArgs {
     const float* signs;
     float rot_norm;
     const float* lam;       // K's per-channel scale [D], or null
+    const float* vsigns;    // V's rotation signs [D] (same rot_norm), or null
     float qscale;           // softmax scale * log2(e)
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
+
+// out[r] <- vsigns (.) (rot_norm * H out[r]) for rows r < rows of D floats:
+// the inverse of V's rotation, applied to attention outputs.
+hipError_t launch_unrotate_rows(float* out, int rows, int D, const float* vsigns, float rot_norm,
+                                hipStream_t stream);
 
 }  // namespace otq

@@ -32,7 +32,8 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const float* __restrict__ lam, const int32_t* __restrict__ pos, int pair_slots)
+    const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos,
+    int pair_slots)
 {
     constexpr int E = D / 64;
     constexpr int NG = D / kGroup;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
         // V: widen, quantise, store scales; nibbles are stored per pair below
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = widen(v[src + e], dtype);
+        if (vsigns) rotate_lane<D>(x, vsigns, rot_norm, lane);
         float sv = quantize_lane<D>(x, vcode[s], lane);
         if (lane % (kGroup / E) == 0) vs[row * NG + (lane * E) / kGroup] = sv;
     }
@@ -136,15 +138,20 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 // blocks of 4, 2 and 1 nibbles) leaves lane m with channel 8 j + m of the 8
 // tokens: an output word, the wave's 64 words filling 256 contiguous bytes.
 //
+// A rotated V (VROT) mixes all of a token's channels, which this V layout
+// spreads over several waves: then V is read, rotated and quantised in the K
+// layout instead, and its code words pass through LDS to the V layout.
+//
 // quantize_tile is one tile's work; FULL when every token of the tile is
 // appended (no freshness tests, no merge with older V nibbles).
-template <int D, int DTYPE, bool FULL>
+template <int D, int DTYPE, bool FULL, bool VROT>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                               int n_new, int cap, size_t head, int p0, int t_tile, int t_end,
                                               uint8_t* __restrict__ kc, float* __restrict__ ks,
                                               uint8_t* __restrict__ vc, float* __restrict__ vs,
                                               const float* __restrict__ signs, float rot_norm,
-                                              const float* __restrict__ lam)
+                                              const float* __restrict__ lam,
+                                              const float* __restrict__ vsigns)
 {
     constexpr int NG = D / kGroup;
     constexpr int LT = D / 8;  // K lanes per token
@@ -170,10 +177,14 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
 
     // issue every load first; the K signs and channel scales of a lane are
     // the same in every unit
-    float sg[8], lm[8];
+    float sg[8], lm[8], vsg[VROT ? 8 : 1];
     if (signs) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) sg[e] = signs[8 * (tid % LT) + e];
+    }
+    if constexpr (VROT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vsg[e] = vsigns[8 * (tid % LT) + e];
     }
     if (lam) {
 #pragma unroll
@@ -188,10 +199,15 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
     }
 #pragma unroll
     for (int i = 0; i < U; ++i) {
-        const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
-        const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
         vraw[i] = make_uint4(0, 0, 0, 0);
-        if (fresh_at(t)) vraw[i] = *reinterpret_cast<const uint4*>(v + (head * n_new + (t - p0)) * D + 32 * g + 8 * jl);
+        if constexpr (VROT) {  // the K layout
+            const int L = i * 256 + tid, t = t_tile + L / LT;
+            if (fresh_at(t)) vraw[i] = *reinterpret_cast<const uint4*>(v + (head * n_new + (t - p0)) * D + 8 * (L % LT));
+        } else {
+            const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
+            const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
+            if (fresh_at(t)) vraw[i] = *reinterpret_cast<const uint4*>(v + (head * n_new + (t - p0)) * D + 32 * g + 8 * jl);
+        }
     }
     uint32_t* vtile = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + t_tile / kTile) * (size_t)(16 * D));
     auto v_word = [&](int gp, int r) { return ((gp * 4 + r) * 16 + 8 * (jl & 1) + m) * 4 + 2 * jh + (jl >> 1); };
@@ -230,16 +246,41 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
         }
     }
 
-    // V: widen, quantise, scales; transpose the nibbles and store whole words
+    // V rotated: widen, rotate, quantise and store the scales in the K
+    // layout, then stage the code words in LDS (token u, channel block j)
+    __shared__ uint32_t vstage[VROT ? kTile * LT : 1];
+    if constexpr (VROT) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int L = i * 256 + tid, u = L / LT, t = t_tile + u, j = L % LT;
+            float x[8];
+            widen8(vraw[i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * vsg[e];
+            rotate_signed<D, 8>(x, rot_norm, j);
+            float sv;
+            vstage[u * LT + j] = quantize_word8(x, sv);
+            if (fresh_at(t) && (j & 3) == 0) vs[(head * cap + t) * NG + (j >> 2)] = sv;
+        }
+        __syncthreads();
+    }
+
+    // V: widen, quantise, scales (or the staged words of a rotated V);
+    // transpose the nibbles and store whole words
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int vt = i * 4 + w, gp = vt >> 2, r = vt & 3;
-        const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
-        float x[8];
-        widen8(vraw[i], x);
-        float sv;
-        uint32_t word = quantize_word8(x, sv);
-        if (fresh_at(t) && jl == 0) vs[(head * cap + t) * NG + g] = sv;
+        uint32_t word;
+        if constexpr (VROT) {
+            word = vstage[v_token(r, m) * LT + 8 * gp + 4 * jh + jl];
+        } else {
+            const int t = t_tile + v_token(r, m), g = 2 * gp + jh;
+            float x[8];
+            widen8(vraw[i], x);
+            float sv;
+            word = quantize_word8(x, sv);
+            if (fresh_at(t) && jl == 0) vs[(head * cap + t) * NG + g] = sv;
+        }
 #pragma unroll
         for (int s = 1; s <= 4; s <<= 1) {
             const uint32_t keep = s == 1 ? 0x0F0F0F0Fu : s == 2 ? 0x00FF00FFu : 0x0000FFFFu;
@@ -259,12 +300,12 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
     }
 }
 
-template <int D, int DTYPE>
+template <int D, int DTYPE, bool VROT>
 __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const float* __restrict__ lam, const int32_t* __restrict__ pos)
+    const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos)
 {
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
@@ -273,11 +314,11 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     if (t_tile >= t_end) return;  // block-uniform
     const size_t head = (size_t)b * H + h;
     if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
-        quantize_tile<D, DTYPE, true>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs,
-                                      rot_norm, lam);
+        quantize_tile<D, DTYPE, true, VROT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
+                                            signs, rot_norm, lam, vsigns);
     else
-        quantize_tile<D, DTYPE, false>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs, signs,
-                                       rot_norm, lam);
+        quantize_tile<D, DTYPE, false, VROT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
+                                             signs, rot_norm, lam, vsigns);
 }
 
 }  // namespace
@@ -285,7 +326,7 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                   const float* signs, float rot_norm, const float* lam,
-                                  const int32_t* pos, hipStream_t stream)
+                                  const float* vsigns, const int32_t* pos, hipStream_t stream)
 {
     if (D != 64 && D != 128 && D != 256) return hipErrorInvalidValue;
     const auto* kk = static_cast<const uint16_t*>(k);
@@ -295,16 +336,23 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         dim3 grid((pair_slots + 3) / 4, H, B), block(256);
         auto kern = D == 64 ? quantize_pair_kernel<64> : D == 128 ? quantize_pair_kernel<128> : quantize_pair_kernel<256>;
         kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam,
-                                         pos, pair_slots);
+                                         vsigns, pos, pair_slots);
     } else {
         // one block per tile touched: the range may start inside a tile
         const int tiles = (n_new + 2 * kTile - 2) / kTile;
         dim3 grid(tiles, H, B), block(256);
-        auto kern = dtype == 0 ? (D == 64 ? quantize_tile_kernel<64, 0> : D == 128 ? quantize_tile_kernel<128, 0>
-                                                                             : quantize_tile_kernel<256, 0>)
-                               : (D == 64 ? quantize_tile_kernel<64, 1> : D == 128 ? quantize_tile_kernel<128, 1>
-                                                                             : quantize_tile_kernel<256, 1>);
-        kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam, pos);
+        using K = void (*)(const uint16_t*, const uint16_t*, int, int, int, uint8_t*, float*, uint8_t*, float*,
+                           const float*, float, const float*, const float*, const int32_t*);
+        auto pick = [&](auto d) -> K {
+            constexpr int DD = decltype(d)::value;
+            if (vsigns) return dtype == 0 ? quantize_tile_kernel<DD, 0, true> : quantize_tile_kernel<DD, 1, true>;
+            return dtype == 0 ? quantize_tile_kernel<DD, 0, false> : quantize_tile_kernel<DD, 1, false>;
+        };
+        const K kern = D == 64 ? pick(std::integral_constant<int, 64>{})
+                     : D == 128 ? pick(std::integral_constant<int, 128>{})
+                                : pick(std::integral_constant<int, 256>{});
+        kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam, vsigns,
+                                         pos);
     }
     return hipGetLastError();
 }

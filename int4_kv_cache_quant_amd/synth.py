@@ -16,7 +16,8 @@ Recipe (all workloads):
     of 0..D-1, shared by K and V, all heads and all tokens.
   * q ~ N(0, 1) in the same dtype; rotation signs are a seeded +-1 vector.
   * seed = 20260000 + 1000 * workload + 10 * layer + slot, slot in
-    {K: 0, V: 1, q: 2, lens: 3, signs: 4, outliers: 5, channel scales: 6}.
+    {K: 0, V: 1, q: 2, lens: 3, signs: 4, outliers: 5, channel scales: 6,
+    V signs: 7}.
   * K's per-channel scale, where a run asks for one: log-uniform in [1/4, 4]
     per channel, and 1 / the outlier multiplier on the outlier channels.
   * "T cached tokens" is the attended length: the cache is prefilled with T-1
@@ -29,7 +30,7 @@ from dataclasses import dataclass, field
 import numpy as np
 import torch
 
-SLOT = {"k": 0, "v": 1, "q": 2, "lens": 3, "signs": 4, "outliers": 5, "chan_scale": 6}
+SLOT = {"k": 0, "v": 1, "q": 2, "lens": 3, "signs": 4, "outliers": 5, "chan_scale": 6, "v_signs": 7}
 
 
 @dataclass(frozen=True)
@@ -99,6 +100,12 @@ def chan_scale(w: Workload, layer: int) -> np.ndarray:
 
 def rot_signs(w: Workload, layer: int) -> np.ndarray:
     rng = np.random.default_rng(seed(w.cfg, layer, "signs"))
+    return np.where(rng.integers(0, 2, w.D) == 1, 1.0, -1.0).astype(np.float32)
+
+
+def v_rot_signs(w: Workload, layer: int) -> np.ndarray:
+    """Signs for V's rotation, where a run asks for one."""
+    rng = np.random.default_rng(seed(w.cfg, layer, "v_signs"))
     return np.where(rng.integers(0, 2, w.D) == 1, 1.0, -1.0).astype(np.float32)
 
 

@@ -22,12 +22,13 @@ def to_bits(t):
     return synth.bits(t)
 
 
-def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True, chan_scale=None):
+def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True, chan_scale=None,
+                v_signs=None):
     """Quantise K/V [B, H, T, D] (device) into a new cache: prefill T-1 tokens
     (optionally in chunks), then append the last token on its own."""
     B, H, T, D = k.shape
     cache = otq.Int4KVCache(B, H, D, capacity, device=k.device, rot_signs=signs,
-                            chan_scale=chan_scale)
+                            chan_scale=chan_scale, v_rot_signs=v_signs)
     n_pre = T - 1 if append_last else T
     step = n_pre if prefill_chunk is None else prefill_chunk
     for t0 in range(0, n_pre, max(step, 1)):
@@ -47,11 +48,11 @@ def host_cache(cache):
             layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D), cache.v_scales.cpu().numpy())
 
 
-def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=None):
+def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=None, v_signs=None):
     kb, vb = to_bits(k), to_bits(v)
     kc, ks = oracle.quantize(kb, dtype, signs=signs, rot_norm=rot_norm, threads=threads,
                              chan_scale=chan_scale)
-    vc, vs = oracle.quantize(vb, dtype, threads=threads)
+    vc, vs = oracle.quantize(vb, dtype, signs=v_signs, rot_norm=rot_norm, threads=threads)
     return kc, ks, vc, vs
 
 
@@ -79,6 +80,11 @@ def errors(out, ref):
 
 def rot_norm32(D):
     return float(np.float32(1.0 / math.sqrt(D)))
+
+
+def rand_signs(D, seed):
+    g = torch.Generator().manual_seed(seed)
+    return torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0).to(torch.float32)
 
 
 def chan_scales(D, seed, outliers=()):

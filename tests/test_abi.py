@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 2
+    assert lib.otq_abi_version() == 3
 
 
 def test_status_strings():
@@ -72,7 +72,7 @@ def test_quantize_append_host_errors():
     assert call(FAKE, FAKE, 1, 0, d, FAKE) == otq.OTQ_EINVAL
     assert call(FAKE + 2, FAKE, 1, 1, d, FAKE) == otq.OTQ_EINVAL   # k, v read 16 bytes at a time
     assert call(FAKE, FAKE + 8, 1, 1, d, FAKE) == otq.OTQ_EINVAL
-    for field in ("k_rot_signs", "k_chan_scale"):   # per-channel vectors read 16 bytes at a time
+    for field in ("k_rot_signs", "k_chan_scale", "v_rot_signs"):   # read 16 bytes at a time
         mis = _desc()
         setattr(mis, field, FAKE + 4)
         assert call(FAKE, FAKE, 1, 1, mis, FAKE) == otq.OTQ_EINVAL

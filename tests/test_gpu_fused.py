@@ -19,7 +19,7 @@ import oracle
 from int4_kv_cache_quant_amd import layout
 
 from gpu_common import (MAX_ABS, REL_L2, build_cache, chan_scales, compare_codes, errors, host_cache,
-                        oracle_cache, rot_norm32, say, to_bits)
+                        oracle_cache, rand_signs, rot_norm32, say, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -49,7 +49,7 @@ def _poison(cache, lens):
 
 
 def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, seed=0, steps=1,
-         variant=otq.OTQ_VARIANT_MFMA, scaled=False):
+         variant=otq.OTQ_VARIANT_MFMA, scaled=False, rotate_v=False):
     g = torch.Generator().manual_seed(seed)
     Hq = G * Hkv
     T = max(lens) + steps - 1
@@ -61,13 +61,16 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
     signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if rotate else None
     lam = chan_scales(D, seed, outliers=(3,)) if scaled else None
     lam_np = None if lam is None else lam.numpy()
+    vsg = rand_signs(D, seed + 1000) if rotate_v else None
+    vsg_np = None if vsg is None else vsg.numpy()
     name = "fp16" if dtype == torch.float16 else "bf16"
     scale = 1.0 / math.sqrt(D)
     cache = build_cache(k[:, :, :T].to(DEV).contiguous(), v[:, :, :T].to(DEV).contiguous(), cap,
                         signs=None if signs is None else signs.to(DEV), append_last=False,
-                        chan_scale=None if lam is None else lam.to(DEV))
+                        chan_scale=None if lam is None else lam.to(DEV),
+                        v_signs=None if vsg is None else vsg.to(DEV))
     ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
-                             chan_scale=lam_np)
+                             chan_scale=lam_np, v_signs=vsg_np)
     for step in range(steps):
         cur = [n + step for n in lens]
         _poison(cache, cur)
@@ -80,7 +83,7 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
         max_len = max(1, max(cur))
         plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
         say(f"fused B={B} G={G} Hkv={Hkv} D={D} lens={cur} chunk={plan.chunk} rotate={rotate} "
-            f"scaled={scaled}")
+            f"scaled={scaled} rotate_v={rotate_v}")
         out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max_len, scale, plan=plan)
         torch.cuda.synchronize()
         got_cache = host_cache(cache)
@@ -94,7 +97,7 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
         kc, ks, vc, vs = ref_cache
         ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(cur, np.int32), scale,
                           signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                          threads=8, chan_scale=lam_np)
+                          threads=8, chan_scale=lam_np, v_signs=vsg_np)
         ma, rel = errors(out.cpu().numpy(), ref)
         say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
         assert ma <= MAX_ABS and rel <= REL_L2
@@ -115,6 +118,16 @@ def test_fused_append_chan_scale(D, G, rotate):
     """K with a per-channel scale: the combine quantises the new token with
     it and divides q by it for the token's score."""
     _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=7 * D + G + rotate, scaled=True)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("rotate,scaled", [(False, False), (True, False), (True, True)])
+def test_fused_append_v_rotated(D, G, rotate, scaled):
+    """V rotated: the combine rotates the new token's V before quantising
+    it and the output is brought back by the inverse rotation."""
+    _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=11 * D + G + rotate + scaled,
+         scaled=scaled, rotate_v=True)
 
 
 @pytest.mark.parametrize("lens", [[1, 2], [129, 128], [257, 33], [32, 31]])

@@ -8,8 +8,8 @@ import torch
 import int4_kv_cache_quant_amd as otq
 from int4_kv_cache_quant_amd import synth
 
-from gpu_common import (build_cache, chan_scales, compare_codes, host_cache, oracle_cache, rot_norm32,
-                        say, to_bits)
+from gpu_common import (build_cache, chan_scales, compare_codes, host_cache, oracle_cache, rand_signs,
+                        rot_norm32, say, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -64,6 +64,27 @@ def test_quantize_chan_scale_bit_exact(D, dtype, rotate):
     name = "fp16" if dtype == torch.float16 else "bf16"
     ref = oracle_cache(k.cpu(), v.cpu(), name, None if signs is None else signs.cpu().numpy(),
                        rot_norm32(D), chan_scale=lam.numpy())
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rotate_k", [False, True])
+def test_quantize_v_rotated_bit_exact(D, dtype, rotate_k):
+    """V rotated with its own signs: chunks of 19 tokens (the bulk kernel's
+    rotated-V form, whole and edge tiles) and a last single token."""
+    B, H, T, cap = 2, 3, 77, 96
+    say(f"quantize v-rotated D={D} dtype={dtype} rotate_k={rotate_k}")
+    k, v = _rand_kv(B, H, T, D, dtype, seed=D + 13 * rotate_k + 3, outliers=(3, 17))
+    ks = rand_signs(D, D + 2) if rotate_k else None
+    vs = rand_signs(D, D + 3)
+    cache = build_cache(k, v, cap, signs=None if ks is None else ks.to(DEV), prefill_chunk=19,
+                        v_signs=vs.to(DEV))
+    torch.cuda.synchronize()
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    ref = oracle_cache(k.cpu(), v.cpu(), name, None if ks is None else ks.numpy(), rot_norm32(D),
+                       v_signs=vs.numpy())
     bad = compare_codes(host_cache(cache), ref, T)
     assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
 

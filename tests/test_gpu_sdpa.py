@@ -15,7 +15,7 @@ import oracle
 from int4_kv_cache_quant_amd import synth
 
 from gpu_common import (MAX_ABS, REL_L2, build_cache, chan_scales, compare_codes, errors, host_cache,
-                        oracle_cache, rot_norm32, say, to_bits)
+                        oracle_cache, rand_signs, rot_norm32, say, to_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,29 +48,33 @@ def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spi
 
 def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
          rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0,
-         scaled=False):
+         scaled=False, rotate_v=False):
     k, v, q, signs, lam = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate, spikes=spikes,
                                 beta=beta, scaled=scaled)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     name = "fp16" if dtype == torch.float16 else "bf16"
     lam_np = None if lam is None else lam.numpy()
+    vsg = rand_signs(D, seed + 1000) if rotate_v else None
+    vsg_np = None if vsg is None else vsg.numpy()
     cache = build_cache(k.to(DEV), v.to(DEV), cap, signs=None if signs is None else signs.to(DEV),
-                        prefill_chunk=max(1, cap // 3), chan_scale=None if lam is None else lam.to(DEV))
+                        prefill_chunk=max(1, cap // 3), chan_scale=None if lam is None else lam.to(DEV),
+                        v_signs=None if vsg is None else vsg.to(DEV))
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     max_len = max(1, int(max(lens)))
     plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
     say(f"sdpa B={B} Hq={Hq} Hkv={Hkv} D={D} cap={cap} chunk={plan.chunk} "
-        f"splits={plan.num_splits} variant={plan.variant} rotate={rotate} scaled={scaled}")
+        f"splits={plan.num_splits} variant={plan.variant} rotate={rotate} scaled={scaled} "
+        f"rotate_v={rotate_v}")
     out = cache.decode(q.to(DEV), lens_t, max_len, scale, plan=plan)
     torch.cuda.synchronize()
     ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
-                             chan_scale=lam_np)
+                             chan_scale=lam_np, v_signs=vsg_np)
     assert compare_codes(host_cache(cache), ref_cache, cap) == {
         "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
     kc, ks, vc, vs = ref_cache
     ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(lens, np.int32), scale,
                       signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                      rows=rows, threads=8, chan_scale=lam_np)
+                      rows=rows, threads=8, chan_scale=lam_np, v_signs=vsg_np)
     got = out.cpu().numpy().astype(np.float64)
     if rows is not None:
         got = got.reshape(-1, D)[rows]
@@ -112,6 +116,19 @@ def test_sdpa_chan_scale(variant, G, D, rotate):
     ragged lengths, both variants, one and two heads per MFMA wave."""
     got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 77], seed=31 + G + D + rotate, rotate=rotate,
                        chunk=128, variant=variant, scaled=True)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("variant,G,D", [(VEC, 1, 128), (VEC, 4, 64), (MF, 1, 256), (MF, 8, 128),
+                                         (MF, 16, 64), (MF, 2, 256)])
+@pytest.mark.parametrize("rotate,scaled", [(False, False), (True, False), (True, True)])
+def test_sdpa_v_rotated(variant, G, D, rotate, scaled):
+    """V quantised in a rotated basis: the output is brought back by the
+    inverse rotation; alone, with K rotated, and with K rotated and scaled."""
+    got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 70], seed=51 + G + D + rotate + scaled, rotate=rotate,
+                       chunk=128, variant=variant, scaled=scaled, rotate_v=True)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2

@@ -226,15 +226,21 @@ def test_sdpa_deterministic():
 
 # -------------------------------------------------------------- full workloads
 
-def _full(cfg, rows_per_seq=None, layer=0):
+def _full(cfg, rows_per_seq=None, layer=0, options=False):
+    """options: K's per-channel scale and a rotated V (seeded, as bench.py
+    --chan-scale --v-rotate makes them) on top of the workload's own."""
     w = synth.WORKLOADS[cfg]
-    say(f"sdpa full workload {cfg} {w.name}")
+    say(f"sdpa full workload {cfg} {w.name} options={options}")
     k = synth.kv(w, layer, "k", device=DEV)
     v = synth.kv(w, layer, "v", device=DEV)
     q = synth.query(w, layer, device=DEV)
     lens = synth.lens(w, layer)
     signs = torch.from_numpy(synth.rot_signs(w, layer)).to(DEV) if w.rotate else None
-    cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs)
+    lam = synth.chan_scale(w, layer) if options else None
+    vsg = synth.v_rot_signs(w, layer) if options else None
+    cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs,
+                            chan_scale=None if lam is None else torch.from_numpy(lam),
+                            v_rot_signs=None if vsg is None else torch.from_numpy(vsg))
     # prefill lens-1 tokens per sequence, then append token lens-1 (ragged-aware)
     for t0 in range(0, w.T, 8192):
         t1 = min(w.T, t0 + 8192)
@@ -249,7 +255,7 @@ def _full(cfg, rows_per_seq=None, layer=0):
     torch.cuda.synchronize()
     ref_cache = oracle_cache(k.cpu(), v.cpu(), w.dtype,
                              None if signs is None else signs.cpu().numpy(), rot_norm32(w.D),
-                             threads=16)
+                             threads=16, chan_scale=lam, v_signs=vsg)
     assert compare_codes(host_cache(cache), ref_cache, w.T) == {
         "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
     rng = np.random.default_rng(cfg)
@@ -261,7 +267,7 @@ def _full(cfg, rows_per_seq=None, layer=0):
     kc, ks, vc, vs = ref_cache
     ref = oracle.sdpa(to_bits(q), w.dtype, kc, ks, vc, vs, lens, w.scale,
                       signs=None if signs is None else signs.cpu().numpy(),
-                      rot_norm=rot_norm32(w.D), rows=rows, threads=16)
+                      rot_norm=rot_norm32(w.D), rows=rows, threads=16, chan_scale=lam, v_signs=vsg)
     got = out.cpu().numpy().reshape(-1, w.D)[rows].astype(np.float64)
     ma, rel = errors(got, ref)
     say(f"  rows={len(rows)} max_abs={ma:.3e} rel_l2={rel:.3e}")
@@ -286,3 +292,9 @@ def test_full_workload_4_gemma_scale1():
 
 def test_full_workload_5_ragged_rotated():
     _full(5, rows_per_seq=2)
+
+
+@pytest.mark.parametrize("cfg,rows_per_seq", [(3, 8), (4, 8), (5, 2)])
+def test_full_workload_with_options(cfg, rows_per_seq):
+    """The full workloads with K's per-channel scale and a rotated V."""
+    _full(cfg, rows_per_seq=rows_per_seq, options=True)

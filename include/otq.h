@@ -257,7 +257,9 @@ int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_
  * Splits with s*chunk >= lens[b] are not
  * written.  otq_sdpa_lse_combine merges the first ceil(lens[b]/chunk)
  * partials of each row into out.  Arguments and errors as for
- * otq_sdpa_int4_decode_planned.
+ * otq_sdpa_int4_decode_planned.  With cache->v_rot_signs set, V^ and so
+ * part_o are in V's rotated basis; otq_sdpa_lse_combine then applies the
+ * inverse rotation to out (a second launch).
  *
  * For a batch of 2..256 sequences the split pass is two launches: a
  * one-workgroup kernel first writes, at byte offset

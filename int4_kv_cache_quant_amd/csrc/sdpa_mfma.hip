@@ -174,20 +174,6 @@ __device__ __forceinline__ uint32_t lds_address(void* p)
 {
     return (uint32_t)(uintptr_t)(lds_char_t*)p;
 }
-__device__ __forceinline__ void dma16(const v4i_t& rsrc, int voffset, int soffset, uint32_t lds_addr)
-{
-    int saved;
-    asm volatile(
-        "s_mov_b32 %0, m0\n\t"
-        "s_mov_b32 m0, %4\n\t"
-        "s_nop 0\n\t"
-        "buffer_load_dwordx4 %1, %2, %3 offen lds\n\t"
-        "s_mov_b32 m0, %0"
-        : "=&s"(saved)
-        : "v"(voffset), "s"(rsrc), "s"(soffset), "s"(lds_addr)
-        : "memory");
-}
-
 // All copies of one tile in one asm statement.  M0 (the LDS destination
 // base) is saved once and restored at the end; each run of 1 KB pieces of
 // one head and array shares one lane offset and one M0 value and steps by the
@@ -197,7 +183,9 @@ __device__ __forceinline__ void dma16(const v4i_t& rsrc, int voffset, int soffse
 // per SIMD every instruction costs an issue slot: this takes 2 + 2 runs + the
 // copies, against 5 per copy with M0 saved around each.
 #define OTQ_M0(M) "s_mov_b32 m0, %[" M "]\n\ts_nop 0\n\t"
-#define OTQ_LD(VO, RS, SO, OFF) "buffer_load_dwordx4 %[" VO "], %[" RS "], %[" SO "] offen offset:" OFF " lds\n\t"
+// nt: the cache streams through once per step, so its lines are marked
+// non-temporal (measured on workload 3: the split from 34.4 to 32.2 us).
+#define OTQ_LD(VO, RS, SO, OFF) "buffer_load_dwordx4 %[" VO "], %[" RS "], %[" SO "] offen offset:" OFF " nt lds\n\t"
 #define OTQ_RUN1(M, VO, RS) OTQ_M0(M) OTQ_LD(VO, RS, "soc", "0")
 #define OTQ_RUN2(M, VO, RS) OTQ_RUN1(M, VO, RS) OTQ_LD(VO, RS, "soc", "1024")
 #define OTQ_RUN4(M, VO, RS) OTQ_RUN2(M, VO, RS) OTQ_LD(VO, RS, "soc", "2048") OTQ_LD(VO, RS, "soc", "3072")

@@ -259,7 +259,7 @@ int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_
  * partials of each row into out.  Arguments and errors as for
  * otq_sdpa_int4_decode_planned.  With cache->v_rot_signs set, V^ and so
  * part_o are in V's rotated basis; otq_sdpa_lse_combine then applies the
- * inverse rotation to out (a second launch).
+ * inverse rotation to out (one block per output row).
  *
  * For a batch of 2..256 sequences the split pass is two launches: a
  * one-workgroup kernel first writes, at byte offset

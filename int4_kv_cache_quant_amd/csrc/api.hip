@@ -291,10 +291,7 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.lam = cache->k_chan_scale;
     a.vsigns = cache->v_rot_signs;
     a.qscale = scale * otq::kLog2eHost;
-    hipError_t e = otq::launch_lse_combine(a, s);
-    // V rotated: bring the output back to the original basis
-    if (e == hipSuccess && cache->v_rot_signs)
-        e = otq::launch_unrotate_rows(out, a.B * a.Hq, a.D, cache->v_rot_signs, cache->rot_norm, s);
+    const hipError_t e = otq::launch_lse_combine(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 

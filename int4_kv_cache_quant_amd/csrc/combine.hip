@@ -24,10 +24,21 @@ namespace otq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kCh = 32;                       // channels per block
-constexpr int kQuads = kCh / 4;               // threads sharing one split (a float4 each)
-constexpr int kLanesS = kThreads / kQuads;    // splits read side by side
+constexpr int kCh = 32;  // channels per block of the slice form
 constexpr float kNegInf = -__builtin_huge_valf();
+
+// Sum over the lanes of a wave that share lane % CQ (CQ = 8, 16, 32 or 64
+// threads per split: lanes 8, 16 and 32 apart; a row's rotation by 8 is lane
+// i ^ 8).
+template <int CQ>
+__device__ __forceinline__ float sum_split_lanes(float v)
+{
+    static_assert(CQ == 8 || CQ == 16 || CQ == 32 || CQ == 64, "threads per split");
+    if constexpr (CQ <= 8) v = v + dpp_mov<kDppRor8>(v);
+    if constexpr (CQ <= 16) v = sum_xor16(v);
+    if constexpr (CQ <= 32) v = sum_xor32(v);
+    return v;
+}
 
 // In-place Walsh-Hadamard butterflies over one element per thread (threads
 // 0..D-1), stages in ascending stride: the lower element of a pair becomes
@@ -54,31 +65,44 @@ __device__ __forceinline__ float fwht_thread(float y, float* xch)
     return y;
 }
 
-// Block (row, c0): row = b * Hq + h, channels [32 c0, 32 c0 + 32).  Thread
-// t reads channels 32 c0 + 4 (t % 8) .. + 3 of the splits s = t / 8 (mod 32),
-// so 32 splits stream in side by side; each thread folds its splits into a
-// running (m, l, o) (the same merge rule as above), then the block merges the
-// threads' triples: one pass over the partials.  DA = head_dim when the
-// block also appends the new token (0 otherwise).
-template <int DA, bool ROT, bool LAM, bool VROT>
+// Block (row, c0): row = b * Hq + h, channels [CH c0, CH c0 + CH), CH = 32
+// (slices) or the whole head_dim (ROWS).  Thread t reads channels
+// CH c0 + 4 (t % CQ) .. + 3 of the splits s = t / CQ (mod LS), CQ = CH / 4,
+// LS = 256 / CQ, so LS splits stream in side by side; each thread folds its
+// splits into a running (m, l, o) (the same merge rule as above), then the
+// block merges the threads' triples: one pass over the partials.  DT =
+// head_dim, or 0 where it is read at run time (slices without the append).
+// Whole rows serve a rotated V, whose output the block brings back by the
+// inverse rotation, and a rotated K with the append, whose in-block
+// transforms then run once per row instead of once per slice.
+template <int DT, bool APPEND, bool ROWS, bool ROT, bool LAM, bool VROT>
 __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
 {
+    static_assert(DT > 0 || (!APPEND && !ROWS), "compile-time head_dim");
+    static_assert(!VROT || ROWS, "a rotated V needs whole rows");
+    constexpr int CH = ROWS ? DT : kCh;
+    constexpr int CQ = CH / 4;          // threads sharing one split (a float4 each)
+    constexpr int LS = kThreads / CQ;   // splits read side by side
+    // splits in flight per thread: whole rows read LS = 4..16 splits side by
+    // side, so each thread holds more of them
+    constexpr int NF = ROWS ? (LS >= 16 ? 4 : 8) : 2;
+    constexpr int DA = DT;
     __shared__ float red_m[kThreads / 64];
-    __shared__ float4 red_o[kThreads / 64][kQuads];
+    __shared__ float4 red_o[kThreads / 64][CQ];
     __shared__ float red_l[kThreads / 64];
     __shared__ float red_s[kThreads / 64];
-    __shared__ float xch[DA > 0 ? DA : 1];   // butterflies, then the new token's V
-    constexpr bool APPEND = DA > 0;
+    __shared__ float xch[DT > 0 ? DT : 1];   // butterflies, then the new token's V
+    __shared__ float orow[VROT ? DT : 1];    // the output row before the inverse rotation
     // every argument the loads below need, fetched together: otherwise the
     // fields arrive one scalar round trip after another, each gating the next
     // address
     asm volatile("" ::"s"(a.part_o), "s"(a.part_ml), "s"(a.lens), "s"(a.S), "s"(a.Hq), "s"(a.D),
                  "s"(a.k_new), "s"(a.v_new), "s"(a.q), "s"(a.H), "s"(a.signs));
-    const int D = APPEND ? DA : a.D;
+    const int D = DT > 0 ? DT : a.D;
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = row / a.Hq;
-    const int q = tid % kQuads, g = tid / kQuads;
-    const int c = kCh * blockIdx.y + 4 * q;
+    const int q = tid % CQ, g = tid / CQ;
+    const int c = CH * blockIdx.y + 4 * q;
     // the new token's K, V and this row's q (one channel per thread; threads
     // past D work on channel D - 1 and write nothing), loaded before lens[b]
     // like the first splits below
@@ -102,20 +126,26 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         writer = h % G == 0 && blockIdx.y == 0 && tid < DA;
     }
 
-    // The first two splits of each thread (g and g + 32) are loaded before
+    // The first NF splits of each thread (g, g + LS, ...) are loaded before
     // lens[b] is known, as far as the workspace holds them (the plan's split
     // count), and folded below only if the split pass wrote them: these
     // loads do not wait for the length's round trip.
     const float2* ml = a.part_ml + (size_t)row * a.S;
     const float* po = a.part_o + (size_t)row * a.S * D + c;
-    float2 v0 = make_float2(0.0f, 0.0f), v1 = v0;
-    float4 x0 = make_float4(0.0f, 0.0f, 0.0f, 0.0f), x1 = x0;
-    if (a.S > 0) {
-        const int s0 = min(g, a.S - 1), s1 = min(g + kLanesS, a.S - 1);
-        v0 = ml[s0];
-        v1 = ml[s1];
-        x0 = *reinterpret_cast<const float4*>(po + (size_t)s0 * D);
-        x1 = *reinterpret_cast<const float4*>(po + (size_t)s1 * D);
+    float2 vf[NF];
+    float4 xf[NF];
+#pragma unroll
+    for (int k = 0; k < NF; ++k) {
+        vf[k] = make_float2(0.0f, 0.0f);
+        xf[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    }
+#pragma unroll
+    for (int k = 0; k < NF; ++k) {
+        const int sk = g + k * LS;
+        if (sk < a.S) {
+            vf[k] = ml[sk];
+            xf[k] = *reinterpret_cast<const float4*>(po + (size_t)sk * D);
+        }
     }
     const int len = min(max(a.lens[b], 0), a.max_len);
     const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
@@ -123,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     if constexpr (APPEND) pos = len - 1;
     float4* dst = reinterpret_cast<float4*>(a.out + (size_t)row * D + c);
     if (len == 0) {  // block-uniform: nothing attended, nothing appended
-        if (tid < kQuads) *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (tid < CQ) *dst = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         return;
     }
 
@@ -137,17 +167,22 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         l = l * al + v.y * w;
         m = mn;
     };
-    if (g < ns) fold(v0, x0);
-    if (g + kLanesS < ns) fold(v1, x1);
-    int s = g + 2 * kLanesS;
-    for (; s + kLanesS < ns; s += 2 * kLanesS) {  // two splits in flight per thread
-        const float2 v0 = ml[s], v1 = ml[s + kLanesS];
-        const float4 x0 = *reinterpret_cast<const float4*>(po + (size_t)s * D);
-        const float4 x1 = *reinterpret_cast<const float4*>(po + (size_t)(s + kLanesS) * D);
-        fold(v0, x0);
-        fold(v1, x1);
+#pragma unroll
+    for (int k = 0; k < NF; ++k)
+        if (g + k * LS < ns) fold(vf[k], xf[k]);
+    for (int s = g + NF * LS; s < ns; s += NF * LS) {  // NF splits in flight per thread
+#pragma unroll
+        for (int k = 0; k < NF; ++k) {
+            const int sk = s + k * LS;
+            if (sk < ns) {
+                vf[k] = ml[sk];
+                xf[k] = *reinterpret_cast<const float4*>(po + (size_t)sk * D);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < NF; ++k)
+            if (s + k * LS < ns) fold(vf[k], xf[k]);
     }
-    if (s < ns) fold(ml[s], *reinterpret_cast<const float4*>(po + (size_t)s * D));
 
     // ---- the new token: quantise K and V to the same bytes as the append kernels
     //      (the small-append kernel's operations in its order), write them, score it
@@ -227,17 +262,15 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     }
     const float f = (m == kNegInf) ? 0.0f : exp2_approx(m - M);
     o = make_float4(o.x * f, o.y * f, o.z * f, o.w * f);
-    l = (q == 0) ? l * f : 0.0f;  // the kQuads threads of a split group hold the same l
-    // sum over the threads of one channel quad: lanes 8 apart (a row's
-    // rotation by 8, then the row swaps), then waves
-    static_assert(kQuads == 8, "lanes 8 apart");
-    auto sum8 = [](float v) { return sum_xor32(sum_xor16(v + dpp_mov<kDppRor8>(v))); };
-    o = make_float4(sum8(o.x), sum8(o.y), sum8(o.z), sum8(o.w));
-    l = sum8(l);
-    if (lane < kQuads) red_o[wave][lane] = o;
+    l = (q == 0) ? l * f : 0.0f;  // the CQ threads of a split group hold the same l
+    // sum over the threads of one channel quad: within the wave, then waves
+    o = make_float4(sum_split_lanes<CQ>(o.x), sum_split_lanes<CQ>(o.y), sum_split_lanes<CQ>(o.z),
+                    sum_split_lanes<CQ>(o.w));
+    l = sum_split_lanes<CQ>(l);  // lane 0 (q == 0): the wave's split lanes
+    if (lane < CQ) red_o[wave][lane] = o;
     if (lane == 0) red_l[wave] = l;
     __syncthreads();
-    if (tid < kQuads) {
+    if (tid < CQ) {
         float4 r = red_o[0][tid];
         float L = red_l[0];
 #pragma unroll
@@ -249,82 +282,68 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         if constexpr (APPEND) {  // one more term: m = s_new, l = 1, o = V^ of the token
             const float Mn = fmaxf(M, s_new);
             const float a1 = (M == kNegInf) ? 0.0f : exp2_approx(M - Mn), a2 = exp2_approx(s_new - Mn);
-            const float* vh = xch + kCh * blockIdx.y + 4 * tid;
+            const float* vh = xch + CH * blockIdx.y + 4 * tid;
             r = make_float4(r.x * a1 + vh[0] * a2, r.y * a1 + vh[1] * a2, r.z * a1 + vh[2] * a2,
                             r.w * a1 + vh[3] * a2);
             L = L * a1 + a2;
         }
-        *dst = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+        if constexpr (VROT) {
+            *reinterpret_cast<float4*>(orow + 4 * tid) = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+        } else {
+            *dst = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
+        }
     }
-}
-
-// One wave per output row: out <- vsigns (.) (rot_norm * H out), the inverse
-// of V's rotation (H is symmetric and H H = D I, so (c H S)^-1 = S H c for
-// c = 1/sqrt(D)).  Lane l owns elements [l E, l E + E), E = D / 64.
-template <int D>
-__global__ __launch_bounds__(256) void unrotate_rows_kernel(float* __restrict__ out, int rows,
-                                                            const float* __restrict__ vsigns, float rot_norm)
-{
-    constexpr int E = D / 64;
-    const int lane = threadIdx.x & 63;
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= rows) return;  // wave-uniform
-    float* o = out + (size_t)row * D + lane * E;
-    float y[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) y[e] = o[e];
-    rotate_signed<D, E>(y, rot_norm, lane);
-#pragma unroll
-    for (int e = 0; e < E; ++e) o[e] = y[e] * vsigns[lane * E + e];
+    if constexpr (VROT) {  // back to the original basis: s_v (.) (rot_norm * H row)
+        __syncthreads();
+        float y = tid < DT ? orow[tid] : 0.0f;
+        y = fwht_thread<DT>(y, xch);
+        if (tid < DT) a.out[(size_t)row * DT + tid] = y * a.rot_norm * a.vsigns[tid];
+    }
 }
 
 }  // namespace
 
-hipError_t launch_unrotate_rows(float* out, int rows, int D, const float* vsigns, float rot_norm,
-                                hipStream_t stream)
-{
-    if (rows <= 0) return hipSuccess;
-    dim3 grid((rows + 3) / 4), block(256);
-    switch (D) {
-    case 64: unrotate_rows_kernel<64><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
-    case 128: unrotate_rows_kernel<128><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
-    case 256: unrotate_rows_kernel<256><<<grid, block, 0, stream>>>(out, rows, vsigns, rot_norm); break;
-    default: return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
-}
-
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
 {
     if (a.D % kCh != 0) return hipErrorInvalidValue;
-    dim3 grid(a.B * a.Hq, a.D / kCh), block(kThreads);
-    if (a.k_new == nullptr) {
-        lse_combine_kernel<0, false, false, false><<<grid, block, 0, stream>>>(a);
-    } else {
-        const int mode = (a.signs != nullptr ? 1 : 0) + (a.lam != nullptr ? 2 : 0) + (a.vsigns != nullptr ? 4 : 0);
-        using K = void (*)(CombineArgs);
-        auto pick = [&](auto d) -> K {
-            constexpr int DA = decltype(d)::value;
-            switch (mode) {
-            case 0: return lse_combine_kernel<DA, false, false, false>;
-            case 1: return lse_combine_kernel<DA, true, false, false>;
-            case 2: return lse_combine_kernel<DA, false, true, false>;
-            case 3: return lse_combine_kernel<DA, true, true, false>;
-            case 4: return lse_combine_kernel<DA, false, false, true>;
-            case 5: return lse_combine_kernel<DA, true, false, true>;
-            case 6: return lse_combine_kernel<DA, false, true, true>;
-            default: return lse_combine_kernel<DA, true, true, true>;
-            }
-        };
-        K kern = nullptr;
-        switch (a.D) {
-        case 64: kern = pick(std::integral_constant<int, 64>{}); break;
-        case 128: kern = pick(std::integral_constant<int, 128>{}); break;
-        case 256: kern = pick(std::integral_constant<int, 256>{}); break;
-        default: return hipErrorInvalidValue;
-        }
-        kern<<<grid, block, 0, stream>>>(a);
+    const bool append = a.k_new != nullptr, rot = a.signs != nullptr, lam = a.lam != nullptr,
+               vrot = a.vsigns != nullptr;
+    // whole rows for a rotated V, for the append with a rotated K, and for a
+    // plain combine whose slices would take more than one round of resident
+    // blocks (2048)
+    const bool big = !append && (long)a.B * a.Hq * (a.D / kCh) > 2048;
+    const bool rows = vrot || (append && rot) || big;
+    dim3 grid(a.B * a.Hq, rows ? 1 : a.D / kCh), block(kThreads);
+    if (!append && !rows) {
+        lse_combine_kernel<0, false, false, false, false, false><<<grid, block, 0, stream>>>(a);
+        return hipGetLastError();
     }
+    using K = void (*)(CombineArgs);
+    auto pick = [&](auto d) -> K {
+        constexpr int DT = decltype(d)::value;
+        if (!append) return vrot ? lse_combine_kernel<DT, false, true, false, false, true>
+                                 : lse_combine_kernel<DT, false, true, false, false, false>;
+        if (!rows) return lam ? lse_combine_kernel<DT, true, false, false, true, false>
+                              : lse_combine_kernel<DT, true, false, false, false, false>;
+        switch ((rot ? 1 : 0) + (lam ? 2 : 0) + (vrot ? 4 : 0)) {
+        case 0: return lse_combine_kernel<DT, true, true, false, false, false>;
+        case 1: return lse_combine_kernel<DT, true, true, true, false, false>;
+        case 2: return lse_combine_kernel<DT, true, true, false, true, false>;
+        case 3: return lse_combine_kernel<DT, true, true, true, true, false>;
+        case 4: return lse_combine_kernel<DT, true, true, false, false, true>;
+        case 5: return lse_combine_kernel<DT, true, true, true, false, true>;
+        case 6: return lse_combine_kernel<DT, true, true, false, true, true>;
+        default: return lse_combine_kernel<DT, true, true, true, true, true>;
+        }
+    };
+    K kern = nullptr;
+    switch (a.D) {
+    case 64: kern = pick(std::integral_constant<int, 64>{}); break;
+    case 128: kern = pick(std::integral_constant<int, 128>{}); break;
+    case 256: kern = pick(std::integral_constant<int, 256>{}); break;
+    default: return hipErrorInvalidValue;
+    }
+    kern<<<grid, block, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -78,14 +78,11 @@ struct CombineArgs {
     const float* signs;
     float rot_norm;
     const float* lam;       // K's per-channel scale [D], or null
-    const float* vsigns;    // V's rotation signs [D] (same rot_norm), or null
+    const float* vsigns;    // V's rotation signs [D] (same rot_norm), or null: the
+                            // output is brought back to the original basis
     float qscale;           // softmax scale * log2(e)
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
 
-// out[r] <- vsigns (.) (rot_norm * H out[r]) for rows r < rows of D floats:
-// the inverse of V's rotation, applied to attention outputs.
-hipError_t launch_unrotate_rows(float* out, int rows, int D, const float* vsigns, float rot_norm,
-                                hipStream_t stream);
 
 }  // namespace otq

@@ -18,6 +18,8 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 _lib = None
 
 DTYPES = {"fp16": 0, "bf16": 1}
+# K rotation kinds: the sign-randomised Hadamard and Fourier transforms
+ROT_KINDS = {"srht": 0, "srft": 1}
 
 
 def _load():
@@ -39,19 +41,25 @@ def _load():
     lib.oracle_srht_f64.restype = None
     lib.oracle_unrotate_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
     lib.oracle_unrotate_f64.restype = None
+    lib.oracle_srft_f32.argtypes = [P, P, ctypes.c_int, ctypes.c_float]
+    lib.oracle_srft_f32.restype = None
+    lib.oracle_srft_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
+    lib.oracle_srft_f64.restype = None
+    lib.oracle_twiddle_f32.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
+    lib.oracle_twiddle_f32.restype = None
     lib.oracle_quantize_vector.argtypes = [P, ctypes.c_int, P, P]
     lib.oracle_quantize_vector.restype = None
     lib.oracle_quantize_rows.argtypes = [P, ctypes.c_int, ctypes.c_long, ctypes.c_int,
-                                         P, ctypes.c_float, P, P, P, ctypes.c_int]
+                                         P, ctypes.c_float, ctypes.c_int, P, P, P, ctypes.c_int]
     lib.oracle_quantize_rows.restype = ctypes.c_int
     lib.oracle_attend_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                       ctypes.c_long, ctypes.c_double, P, ctypes.c_float,
-                                      P, P, P, P]
+                                      ctypes.c_int, P, P, P, P]
     lib.oracle_attend_row.restype = None
     lib.oracle_sdpa.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_long, P, P, P, P, P,
-                                ctypes.c_double, P, ctypes.c_float, P, P, P, ctypes.c_long,
-                                P, ctypes.c_int]
+                                ctypes.c_double, P, ctypes.c_float, ctypes.c_int, P, P, P,
+                                ctypes.c_long, P, ctypes.c_int]
     lib.oracle_sdpa.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -94,6 +102,36 @@ def srht_f64(x, signs, c):
     return y
 
 
+def srft_f32(x, signs, rot_norm):
+    """fp32 sign-randomised FFT rotation of one vector (in-place radix-2
+    decimation-in-frequency order over the (even, odd) complex pairs)."""
+    lib = _load()
+    y = _c(x, np.float32).copy()
+    s = _c(signs, np.float32)
+    lib.oracle_srft_f32(_ptr(y), _ptr(s), y.shape[-1], float(np.float32(rot_norm)))
+    return y
+
+
+def srft_f64(x, signs, c):
+    lib = _load()
+    y = _c(x, np.float64).copy()
+    s = _c(signs, np.float32)
+    lib.oracle_srft_f64(_ptr(y), _ptr(s), y.shape[-1], float(c))
+    return y
+
+
+def twiddle_f32(t, N):
+    """The fp32 twiddle (cos, -sin) of 2 pi t / N the fp32 SRFT uses."""
+    lib = _load()
+    wr, wi = ctypes.c_float(), ctypes.c_float()
+    lib.oracle_twiddle_f32(int(t), int(N), ctypes.byref(wr), ctypes.byref(wi))
+    return np.float32(wr.value), np.float32(wi.value)
+
+
+def _kind(rot_kind):
+    return ROT_KINDS[rot_kind] if isinstance(rot_kind, str) else int(rot_kind)
+
+
 def unrotate_f64(y, signs, c):
     """The inverse rotation s (.) (c H y) in fp64."""
     lib = _load()
@@ -114,9 +152,10 @@ def quantize_vector(x):
     return codes, scales
 
 
-def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None):
+def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None, rot_kind="srht"):
     """[..., D] 16-bit rows -> codes [..., D/2], scales [..., D/32].
 
+    rot_kind: "srht" or "srft", the rotation applied when signs is given;
     chan_scale: per-channel scale lambda [D] applied after the rotation
     (the cache then holds lambda (.) y), or None."""
     lib = _load()
@@ -128,7 +167,7 @@ def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None):
     s = None if signs is None else _c(signs, np.float32)
     lam = None if chan_scale is None else _c(chan_scale, np.float32)
     rc = lib.oracle_quantize_rows(_ptr(bits), DTYPES[dtype], N, D, _ptr(s),
-                                  float(np.float32(rot_norm)), _ptr(lam), _ptr(codes),
+                                  float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(codes),
                                   _ptr(scales), int(threads))
     if rc != 0:
         raise ValueError("oracle_quantize_rows rejected its arguments")
@@ -136,7 +175,7 @@ def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None):
 
 
 def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0, chan_scale=None,
-               v_signs=None):
+               v_signs=None, rot_kind="srht"):
     lib = _load()
     q_bits = _c(q_bits, np.uint16)
     D = q_bits.shape[-1]
@@ -149,16 +188,19 @@ def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0
     out = np.zeros(D, np.float64)
     lib.oracle_attend_row(_ptr(q_bits), DTYPES[dtype], D, _ptr(kc), _ptr(ks), _ptr(vc),
                           _ptr(vs), int(T), float(scale), _ptr(s),
-                          float(np.float32(rot_norm)), _ptr(lam), _ptr(vsg), _ptr(work), _ptr(out))
+                          float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(vsg),
+                          _ptr(work), _ptr(out))
     return out
 
 
 def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
-         signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None, v_signs=None):
+         signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None, v_signs=None,
+         rot_kind="srht"):
     """Decode attention over a plain-layout cache.
 
     q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D/2]; scales
-    [B, Hkv, cap, D/32]; lens [B]; chan_scale: the K cache's per-channel
+    [B, Hkv, cap, D/32]; lens [B]; rot_kind: "srht" or "srft", K's rotation
+    when signs is given; chan_scale: the K cache's per-channel
     scale lambda [D] or None; v_signs: the signs V was rotated with (same
     rot_norm as K) or None.  Returns float64 [B, Hq, D], or [len(rows), D]
     for the listed rows (row = b * Hq + h).
@@ -183,7 +225,8 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
         out = np.zeros((nrows, D), np.float64)
     rc = lib.oracle_sdpa(_ptr(q_bits), DTYPES[dtype], B, Hq, Hkv, D, cap, _ptr(kc), _ptr(ks),
                          _ptr(vc), _ptr(vs), _ptr(lens), float(scale), _ptr(s),
-                         float(np.float32(rot_norm)), _ptr(lam), _ptr(vsg), _ptr(r), nrows,
+                         float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(vsg), _ptr(r),
+                         nrows,
                          _ptr(out), int(threads))
     if rc != 0:
         raise ValueError("oracle_sdpa rejected its arguments")

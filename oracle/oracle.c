@@ -42,6 +42,20 @@
  * fp64, v^ = s_v (.) (c * H_D * (code * scale)), since (c H_D S)^-1 =
  * S H_D c for c = 1/sqrt(D) and S = diag(s_v) of +-1.
  *
+ * SRFT ("SRFT + int4 KV-cache", core-method section: a sign-randomised FFT
+ * may take the place of the Hadamard rotation, with the same quality).
+ * Reading: the D reals of a vector are D/2 complex numbers z_j = x_2j +
+ * i x_2j+1 (after the signs), transformed by the radix-2 decimation-in-
+ * frequency FFT in place (stages of half-size N/2, N/4, ..., 1 for N = D/2;
+ * a stage replaces (a, b) with (a + b, (a - b) W^t), W = exp(-2 pi i / N),
+ * t = (j mod h) N / (2h) for the pair's lower index j), which leaves the
+ * DFT coefficient of index bitrev(k) at position k, and the result is
+ * multiplied by c = 1/sqrt(N).  That map is orthogonal on R^D, so a query
+ * rotated the same way keeps every dot product.  In fp32 every step is one
+ * IEEE operation: the complex product is (d_re w_re - d_im w_im, d_re w_im
+ * + d_im w_re), each product rounded, then the sum; twiddles are the
+ * correctly rounded fp32 values of cos and -sin of 2 pi t / N.
+ *
  * Per-channel scale ("SRFT + int4 KV-cache", core-method section: a
  * per-coordinate scale lambda is applied after the rotation and before the
  * group abs-max).  Reading: when a scale vector is given, the quantised
@@ -58,6 +72,7 @@
 #include <string.h>
 
 #define ORACLE_GROUP 32
+#define ORACLE_PI 3.14159265358979323846
 
 /* ---------------------------------------------------------------- widening */
 
@@ -144,6 +159,116 @@ void oracle_unrotate_f64(double *y, const float *signs, int D, double c)
         y[i] = y[i] * c * (double)signs[i];
 }
 
+/* Twiddle W_N^t = (cos(2 pi t / N), -sin(2 pi t / N)) for N a power of two
+ * up to 2^20 and 0 <= t < N, evaluated through the symmetries of the first
+ * octant, so that the quarter-turn values are exact and every other value
+ * comes from cos or sin of an angle in (0, pi/4], where the library's
+ * double results are accurate to an ulp. */
+static void twiddle(int t, int N, double *wr, double *wi)
+{
+    /* angle = 2 pi t / N = (pi / 4) * u / Q with u = 8 t, Q = N */
+    long u = 8L * t, Q = N;
+    int oct = (int)(u / Q);     /* octant 0..7 */
+    long rem = u - oct * Q;     /* angle inside the octant: (pi/4) rem / Q */
+    double c, s;
+    /* cos and sin of (pi/4) * m / Q for 0 <= m <= Q */
+#define CS_Q(m, cc, ss)                                                   \
+    do {                                                                  \
+        if ((m) == 0) { cc = 1.0; ss = 0.0; }                             \
+        else { double a_ = (ORACLE_PI / 4.0) * (double)(m) / (double)Q;        \
+               cc = cos(a_); ss = sin(a_); }                              \
+    } while (0)
+    double c1, s1;
+    switch (oct) {
+    case 0: CS_Q(rem, c1, s1); c = c1; s = s1; break;                    /* a        */
+    case 1: CS_Q(Q - rem, c1, s1); c = s1; s = c1; break;                /* pi/2 - b */
+    case 2: CS_Q(rem, c1, s1); c = -s1; s = c1; break;                   /* pi/2 + a */
+    case 3: CS_Q(Q - rem, c1, s1); c = -c1; s = s1; break;               /* pi - b   */
+    case 4: CS_Q(rem, c1, s1); c = -c1; s = -s1; break;                  /* pi + a   */
+    case 5: CS_Q(Q - rem, c1, s1); c = -s1; s = -c1; break;              /* 3pi/2 - b */
+    case 6: CS_Q(rem, c1, s1); c = s1; s = -c1; break;                   /* 3pi/2 + a */
+    default: CS_Q(Q - rem, c1, s1); c = c1; s = -s1; break;              /* 2pi - b  */
+    }
+#undef CS_Q
+    /* zeros are +0 */
+    *wr = c + 0.0;
+    *wi = -s + 0.0;
+}
+
+/* fp32 twiddle: the double value rounded once to fp32. */
+void oracle_twiddle_f32(int t, int N, float *wr, float *wi)
+{
+    double r, i;
+    twiddle(t, N, &r, &i);
+    *wr = (float)r;
+    *wi = (float)i;
+}
+
+/* y <- c * FFT_{D/2}(s (.) y) in fp32, the in-place radix-2 decimation-in-
+ * frequency FFT over z_j = (y[2j], y[2j+1]) described at the top. */
+void oracle_srft_f32(float *y, const float *signs, int D, float c)
+{
+    const int N = D / 2;
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * signs[i];
+    for (int h = N / 2; h >= 1; h /= 2)
+        for (int blk = 0; blk < N; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                float ar = y[2 * j], ai = y[2 * j + 1];
+                float br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
+                float wr, wi;
+                oracle_twiddle_f32((j - blk) * (N / (2 * h)), N, &wr, &wi);
+                float dr = ar - br, di = ai - bi;
+                y[2 * j] = ar + br;
+                y[2 * j + 1] = ai + bi;
+                float p1 = dr * wr, p2 = di * wi, p3 = dr * wi, p4 = di * wr;
+                y[2 * (j + h)] = p1 - p2;
+                y[2 * (j + h) + 1] = p3 + p4;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* The same transform in fp64 (twiddles in double), used on the query. */
+void oracle_srft_f64(double *y, const float *signs, int D, double c)
+{
+    const int N = D / 2;
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * (double)signs[i];
+    for (int h = N / 2; h >= 1; h /= 2)
+        for (int blk = 0; blk < N; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                double ar = y[2 * j], ai = y[2 * j + 1];
+                double br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
+                double wr, wi;
+                twiddle((j - blk) * (N / (2 * h)), N, &wr, &wi);
+                double dr = ar - br, di = ai - bi;
+                y[2 * j] = ar + br;
+                y[2 * j + 1] = ai + bi;
+                y[2 * (j + h)] = dr * wr - di * wi;
+                y[2 * (j + h) + 1] = dr * wi + di * wr;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* K's rotation by kind: 0 = SRHT, 1 = SRFT. */
+static void rotate_f32(float *y, const float *signs, int D, float c, int kind)
+{
+    if (kind == 1)
+        oracle_srft_f32(y, signs, D, c);
+    else
+        oracle_srht_f32(y, signs, D, c);
+}
+
+static void rotate_f64(double *y, const float *signs, int D, double c, int kind)
+{
+    if (kind == 1)
+        oracle_srft_f64(y, signs, D, c);
+    else
+        oracle_srht_f64(y, signs, D, c);
+}
+
 /* ---------------------------------------------------------------- quantise */
 
 /* One vector x[D] (already widened to fp32, already rotated if rotation is
@@ -194,6 +319,7 @@ struct qrows_job {
     int D;
     const float *signs;
     float rot_norm;
+    int rot_kind;
     const float *chan_scale;
     uint8_t *codes;
     float *scales;
@@ -207,7 +333,7 @@ static void *qrows_worker(void *arg)
         for (int i = 0; i < j->D; ++i)
             x[i] = widen(j->src[n * j->D + i], j->dtype);
         if (j->signs)
-            oracle_srht_f32(x, j->signs, j->D, j->rot_norm);
+            rotate_f32(x, j->signs, j->D, j->rot_norm, j->rot_kind);
         if (j->chan_scale)
             for (int i = 0; i < j->D; ++i)
                 x[i] = x[i] * j->chan_scale[i];
@@ -218,14 +344,15 @@ static void *qrows_worker(void *arg)
 }
 
 /* N rows of D 16-bit values (dtype 0 = fp16, 1 = bf16) -> N rows of codes
- * and scales.  signs == NULL means no rotation, chan_scale == NULL no
- * per-channel scale.  Rows are independent, so spreading them over threads
+ * and scales.  signs == NULL means no rotation (else rot_kind 0 = SRHT,
+ * 1 = SRFT), chan_scale == NULL no per-channel scale.  Rows are independent, so spreading them over threads
  * does not change any result. */
 int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
-                         const float *signs, float rot_norm, const float *chan_scale,
-                         uint8_t *codes, float *scales, int nthreads)
+                         const float *signs, float rot_norm, int rot_kind,
+                         const float *chan_scale, uint8_t *codes, float *scales, int nthreads)
 {
-    if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1)
+    if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1 ||
+        rot_kind < 0 || rot_kind > 1 || (D & (D - 1)) != 0)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -239,7 +366,8 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
         long n0 = t * per, n1 = n0 + per > N ? N : n0 + per;
         if (n0 >= n1)
             break;
-        jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, chan_scale, codes, scales};
+        jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, rot_kind,
+                                     chan_scale, codes, scales};
         if (nthreads == 1) {
             qrows_worker(&jobs[t]);
         } else {
@@ -262,12 +390,13 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
  *   V^[t][i] = code * scale, brought back to the original basis
  *              (oracle_unrotate_f64) when v_signs != NULL
  *   out      = sum_t w_t V^[t] / sum_t w_t
- * T == 0 gives out = 0.  q' is q rotated in fp64 when signs != NULL.
+ * T == 0 gives out = 0.  q' is q rotated in fp64 when signs != NULL (rot_kind
+ * 0 = SRHT, 1 = SRFT).
  * work must hold T doubles. */
 void oracle_attend_row(const uint16_t *q, int dtype, int D,
                        const uint8_t *kc, const float *ks,
                        const uint8_t *vc, const float *vs, long T,
-                       double scale, const float *signs, float rot_norm,
+                       double scale, const float *signs, float rot_norm, int rot_kind,
                        const float *chan_scale, const float *v_signs, double *work,
                        double *out)
 {
@@ -276,7 +405,7 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
     for (int i = 0; i < D; ++i)
         qd[i] = (double)widen(q[i], dtype);
     if (signs)
-        oracle_srht_f64(qd, signs, D, (double)rot_norm);
+        rotate_f64(qd, signs, D, (double)rot_norm, rot_kind);
     for (int i = 0; i < D; ++i)
         out[i] = 0.0;
     if (T <= 0)
@@ -325,6 +454,7 @@ struct attn_job {
     double scale;
     const float *signs;
     float rot_norm;
+    int rot_kind;
     const float *chan_scale;
     const float *v_signs;
     double *out;
@@ -349,7 +479,8 @@ static void *attn_worker(void *arg)
         oracle_attend_row(j->q + (size_t)row * j->D, j->dtype, j->D,
                           j->kc + head * j->cap * (j->D / 2), j->ks + head * j->cap * (j->D / ORACLE_GROUP),
                           j->vc + head * j->cap * (j->D / 2), j->vs + head * j->cap * (j->D / ORACLE_GROUP),
-                          T, j->scale, j->signs, j->rot_norm, j->chan_scale, j->v_signs, work,
+                          T, j->scale, j->signs, j->rot_norm, j->rot_kind, j->chan_scale,
+                          j->v_signs, work,
                           j->out + (size_t)r * j->D);
     }
     free(work);
@@ -364,11 +495,12 @@ static void *attn_worker(void *arg)
 int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, long cap,
                 const uint8_t *kc, const float *ks, const uint8_t *vc, const float *vs,
                 const int32_t *lens, double scale, const float *signs, float rot_norm,
-                const float *chan_scale, const float *v_signs, const int32_t *rows, long nrows,
-                double *out, int nthreads)
+                int rot_kind, const float *chan_scale, const float *v_signs, const int32_t *rows,
+                long nrows, double *out, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
-        D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1)
+        D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1 || rot_kind < 0 ||
+        rot_kind > 1 || (D & (D - 1)) != 0)
         return -1;
     long R = rows ? nrows : (long)B * Hq;
     if (nthreads < 1)
@@ -384,7 +516,8 @@ int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, lon
         if (r0 >= r1)
             break;
         jobs[t] = (struct attn_job){q, dtype, B, Hq, Hkv, D, cap, kc, vc, ks, vs, lens,
-                                    scale, signs, rot_norm, chan_scale, v_signs, out, rows, r0, r1};
+                                    scale, signs, rot_norm, rot_kind, chan_scale, v_signs, out,
+                                    rows, r0, r1};
         if (nthreads == 1) {
             attn_worker(&jobs[t]);
         } else {

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 3
+#define OTQ_ABI_VERSION 4
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -54,6 +54,12 @@ typedef enum otq_status {
 
 typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
 
+/* K's rotation when k_rot_signs != NULL (otq_cache.k_rot_kind). */
+typedef enum otq_rot_kind {
+    OTQ_ROT_SRHT = 0, /* sign-randomised Walsh-Hadamard transform */
+    OTQ_ROT_SRFT = 1  /* sign-randomised FFT                      */
+} otq_rot_kind;
+
 /*
  * A quantised KV cache for one attention layer: caller-owned device arrays,
  * described by a host struct.
@@ -66,18 +72,32 @@ typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
  *     y = rot_norm * H (k_rot_signs (.) x)
  * with H the Sylvester-ordered Walsh-Hadamard matrix, evaluated as in-place
  * butterflies (a + b, a - b) in ascending stride order, then one multiply by
- * rot_norm (pass fp32(1/sqrt(head_dim))).  The query is rotated the same way
- * inside otq_sdpa_int4_decode, so scores are unchanged by the rotation.
+ * rot_norm (pass fp32(1/sqrt(head_dim))).  That is k_rot_kind = OTQ_ROT_SRHT.
+ * With k_rot_kind = OTQ_ROT_SRFT ("SRFT + int4 KV-cache" page, core-method
+ * section: a sign-randomised FFT in place of the Hadamard rotation) the D
+ * reals are instead D/2 complex numbers z_j = (x_2j, x_2j+1), signs applied
+ * to the reals first, transformed by the radix-2 decimation-in-frequency FFT
+ * in place: stages of half-size h = N/2, ..., 1 (N = D/2) replace (z_j,
+ * z_j+h) with (z_j + z_j+h, (z_j - z_j+h) W^t), W = exp(-2 pi i / N), t = (j
+ * mod h) N / (2h), which leaves DFT coefficient bitrev(k) at position k;
+ * then one multiply by rot_norm (pass fp32(1/sqrt(head_dim / 2))).  Each
+ * step is one fp32 operation, the complex product (dr wr - di wi, dr wi +
+ * di wr) with products rounded before the sum, and the twiddles (wr, wi)
+ * are the correctly rounded fp32 cos and -sin of 2 pi t / N.
+ * The query is rotated the same way inside otq_sdpa_int4_decode, so scores
+ * are unchanged by the rotation.
  * K only, when k_chan_scale != NULL (a per-coordinate scale lambda applied
  * after the rotation and before the group abs-max: "SRFT + int4 KV-cache"
  * page, core-method section), x (rotated or not) is then replaced by
  *     z_i = x_i * k_chan_scale[i]      (one fp32 multiply)
  * and attention reads K^_i = code_i * s_g / k_chan_scale[i]: the query is
  * divided by the scale inside otq_sdpa_int4_decode.
- * V, when v_rot_signs != NULL, is rotated before quantisation exactly as K
- * is (its own signs, the same rot_norm), and the attention output is brought
- * back to the original basis, out <- v_rot_signs (.) (rot_norm * H out),
- * the inverse of that rotation (rot_norm = fp32(1/sqrt(head_dim))).
+ * V, when v_rot_signs != NULL, is rotated before quantisation by the
+ * Hadamard form above (its own signs, the same rot_norm), and the attention
+ * output is brought back to the original basis, out <- v_rot_signs (.)
+ * (rot_norm * H out), the inverse of that rotation (rot_norm =
+ * fp32(1/sqrt(head_dim))).  A rotated V needs k_rot_kind = OTQ_ROT_SRHT
+ * (or no K rotation): OTQ_EUNSUPPORTED otherwise.
  *
  * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
  *  Codes are two's-complement int4 nibbles; a byte holds an even channel in
@@ -111,6 +131,7 @@ typedef struct otq_cache {
     float rot_norm;           /* used only when k_rot_signs != NULL */
     const float *k_chan_scale; /* device [D] fp32 lambda, finite and > 0, 16-byte aligned, or NULL */
     const float *v_rot_signs;  /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
+    int32_t k_rot_kind;        /* otq_rot_kind; read only when k_rot_signs != NULL */
 } otq_cache;
 
 /* Human-readable name of a status code (static string). */

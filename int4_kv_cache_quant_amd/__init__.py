@@ -23,6 +23,8 @@ OTQ_OK, OTQ_EINVAL, OTQ_ECAPACITY, OTQ_EUNSUPPORTED, OTQ_EWORKSPACE, OTQ_EDEVICE
 OTQ_F16, OTQ_BF16 = 0, 1
 OTQ_VARIANT_AUTO, OTQ_VARIANT_VECTOR, OTQ_VARIANT_MFMA = 0, 1, 2
 OTQ_GROUP, OTQ_TILE = 32, 32
+OTQ_ROT_SRHT, OTQ_ROT_SRFT = 0, 1
+ROT_KINDS = {"srht": OTQ_ROT_SRHT, "srft": OTQ_ROT_SRFT}
 
 EXPORTED = [
     "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
@@ -46,6 +48,7 @@ class otq_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_rot_signs", ctypes.c_void_p), ("rot_norm", ctypes.c_float),
         ("k_chan_scale", ctypes.c_void_p), ("v_rot_signs", ctypes.c_void_p),
+        ("k_rot_kind", ctypes.c_int32),
     ]
 
 
@@ -233,15 +236,17 @@ def otq_sdpa_lse_combine(num_q_heads, cache_desc, lens, max_len, workspace, plan
 class Int4KVCache:
     """Owns the four device arrays of one layer's cache and its descriptor.
 
-    ``rot_signs`` (device float32 [D] of +-1) turns on the K rotation; the
-    normalisation is fp32(1/sqrt(D)).  ``chan_scale`` (float32 [D], > 0)
+    ``rot_signs`` (device float32 [D] of +-1) turns on the K rotation:
+    ``rot_kind`` "srht" (Walsh-Hadamard, normalisation fp32(1/sqrt(D))) or
+    "srft" (FFT over the (even, odd) complex pairs, normalisation
+    fp32(1/sqrt(D/2))).  ``chan_scale`` (float32 [D], > 0)
     turns on K's per-channel scale, applied after the rotation.
     ``v_rot_signs`` (float32 [D] of +-1) turns on V's rotation, whose inverse
     the attention calls apply to their outputs.
     """
 
     def __init__(self, batch, num_kv_heads, head_dim, capacity, device="cuda", rot_signs=None,
-                 chan_scale=None, v_rot_signs=None):
+                 chan_scale=None, v_rot_signs=None, rot_kind="srht"):
         cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity)
         self.shape = (batch, num_kv_heads, head_dim, capacity)
         g = head_dim // OTQ_GROUP
@@ -251,7 +256,9 @@ class Int4KVCache:
         self.v_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
         assert self.k_codes.numel() == cb and self.k_scales.numel() * 4 == sb
         self.rot_signs = None if rot_signs is None else rot_signs.to(device=device, dtype=torch.float32).contiguous()
-        self.rot_norm = float(torch.tensor(1.0 / math.sqrt(head_dim), dtype=torch.float32))
+        self.rot_kind = ROT_KINDS[rot_kind]
+        n = head_dim // 2 if self.rot_kind == OTQ_ROT_SRFT else head_dim
+        self.rot_norm = float(torch.tensor(1.0 / math.sqrt(n), dtype=torch.float32))
         self.chan_scale = (None if chan_scale is None
                            else chan_scale.to(device=device, dtype=torch.float32).contiguous())
         self.v_rot_signs = (None if v_rot_signs is None
@@ -262,7 +269,8 @@ class Int4KVCache:
                               None if self.rot_signs is None else self.rot_signs.data_ptr(),
                               self.rot_norm,
                               None if self.chan_scale is None else self.chan_scale.data_ptr(),
-                              None if self.v_rot_signs is None else self.v_rot_signs.data_ptr())
+                              None if self.v_rot_signs is None else self.v_rot_signs.data_ptr(),
+                              self.rot_kind)
 
     @property
     def nbytes(self):

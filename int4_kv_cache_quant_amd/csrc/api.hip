@@ -41,8 +41,16 @@ int check_cache(const otq_cache* c)
     if ((((uintptr_t)c->k_rot_signs) & 15) != 0 || (((uintptr_t)c->k_chan_scale) & 15) != 0 ||
         (((uintptr_t)c->v_rot_signs) & 15) != 0)
         return OTQ_EINVAL;
+    if (c->k_rot_signs) {
+        if (c->k_rot_kind != OTQ_ROT_SRHT && c->k_rot_kind != OTQ_ROT_SRFT) return OTQ_EINVAL;
+        // V's rotation is the Hadamard one and shares K's normalisation
+        if (c->k_rot_kind == OTQ_ROT_SRFT && c->v_rot_signs) return OTQ_EUNSUPPORTED;
+    }
     return OTQ_OK;
 }
+
+// K's rotation kind as the kernels take it (checked by check_cache).
+int rot_kind(const otq_cache* c) { return c->k_rot_signs && c->k_rot_kind == OTQ_ROT_SRFT ? 1 : 0; }
 
 // Batches whose split blocks take their items longest first (one sequence
 // needs no order: its chunks are equal but the last).
@@ -165,7 +173,8 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     const hipError_t e = otq::launch_quantize_append(
         k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
         cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
-        cache->rot_norm, cache->k_chan_scale, cache->v_rot_signs, pos, static_cast<hipStream_t>(stream));
+        cache->rot_norm, rot_kind(cache), cache->k_chan_scale, cache->v_rot_signs, pos,
+        static_cast<hipStream_t>(stream));
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
@@ -232,6 +241,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.vs = cache->v_scales;
     a.signs = cache->k_rot_signs;
     a.rot_norm = cache->rot_norm;
+    a.rot_kind = rot_kind(cache);
     a.lam = cache->k_chan_scale;
     a.lens = lens;
     a.max_len = max_len;
@@ -288,6 +298,7 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.vs = cache->v_scales;
     a.signs = cache->k_rot_signs;
     a.rot_norm = cache->rot_norm;
+    a.rot_kind = rot_kind(cache);
     a.lam = cache->k_chan_scale;
     a.vsigns = cache->v_rot_signs;
     a.qscale = scale * otq::kLog2eHost;

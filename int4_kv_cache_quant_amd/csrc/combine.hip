@@ -18,6 +18,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_lane.hpp"
+#include "srft.hpp"
 
 namespace otq {
 
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float x = widen(kx, a.dtype);
         if (ROT) {
             x = x * sg;
-            x = fwht_thread<DA>(x, xch);
+            x = a.rot_kind ? srft_thread<DA>(x, xch) : fwht_thread<DA>(x, xch);
             x = x * a.rot_norm;
         }
         if (LAM) x = x * lm;  // after the rotation
@@ -235,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float y = widen(qx, a.dtype);
         if (ROT) {
             y = y * sg;
-            y = fwht_thread<DA>(y, xch);
+            y = a.rot_kind ? srft_thread<DA>(y, xch) : fwht_thread<DA>(y, xch);
             y = y * a.rot_norm;
         }
         if (LAM) y = y / lm;

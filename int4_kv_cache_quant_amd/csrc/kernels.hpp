@@ -10,7 +10,7 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                  const float* signs, float rot_norm, const float* lam,
+                                  const float* signs, float rot_norm, int rot_kind, const float* lam,
                                   const float* vsigns, const int32_t* pos, hipStream_t stream);
 
 // Split pass arguments shared by both variants.
@@ -24,6 +24,7 @@ struct SplitArgs {
     float* vs;
     const float* signs;
     float rot_norm;
+    int rot_kind;      // with signs: 0 the Walsh-Hadamard rotation, 1 the FFT one
     const float* lam;  // K's per-channel scale [D] (q is divided by it), or null
     const int32_t* lens;
     int max_len;
@@ -77,6 +78,7 @@ struct CombineArgs {
     float* vs;
     const float* signs;
     float rot_norm;
+    int rot_kind;           // with signs: 0 the Walsh-Hadamard rotation, 1 the FFT one
     const float* lam;       // K's per-channel scale [D], or null
     const float* vsigns;    // V's rotation signs [D] (same rot_norm), or null: the
                             // output is brought back to the original basis

@@ -16,6 +16,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_lane.hpp"
+#include "srft.hpp"
 
 namespace otq {
 
@@ -48,7 +49,7 @@ template <int D>
 __global__ __launch_bounds__(256) void quantize_pair_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
-    float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
+    float* __restrict__ vs, const float* __restrict__ signs, float rot_norm, int rot_kind,
     const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos,
     int pair_slots)
 {
@@ -97,7 +98,15 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
         float x[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = widen(k[src + e], dtype);
-        if (signs) rotate_lane<D>(x, signs, rot_norm, lane);
+        if (signs) {
+            if (rot_kind) {  // the FFT rotation
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = x[e] * signs[lane * E + e];
+                srft_signed<D, E>(x, rot_norm, lane);
+            } else {
+                rotate_lane<D>(x, signs, rot_norm, lane);
+            }
+        }
         if (lam) {  // K's per-channel scale, after the rotation
 #pragma unroll
             for (int e = 0; e < E; ++e) x[e] = x[e] * lam[lane * E + e];
@@ -161,7 +170,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 //
 // quantize_tile is one tile's work; FULL when every token of the tile is
 // appended (no freshness tests, no merge with older V nibbles).
-template <int D, int DTYPE, bool FULL, bool VROT>
+template <int D, int DTYPE, bool FULL, bool VROT, bool SRFT>
 __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
                                               int n_new, int cap, size_t head, int p0, int t_tile, int t_end,
                                               uint8_t* __restrict__ kc, float* __restrict__ ks,
@@ -248,7 +257,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
         if (signs) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[e];
-            rotate_signed<D, 8>(x, rot_norm, j);
+            if constexpr (SRFT)
+                srft_signed<D, 8>(x, rot_norm, j);
+            else
+                rotate_signed<D, 8>(x, rot_norm, j);
         }
         if (lam) {  // K's per-channel scale, after the rotation
 #pragma unroll
@@ -317,7 +329,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
     }
 }
 
-template <int D, int DTYPE, bool VROT>
+template <int D, int DTYPE, bool VROT, bool SRFT>
 __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
@@ -331,10 +343,10 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     if (t_tile >= t_end) return;  // block-uniform
     const size_t head = (size_t)b * H + h;
     if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
-        quantize_tile<D, DTYPE, true, VROT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
+        quantize_tile<D, DTYPE, true, VROT, SRFT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
                                             signs, rot_norm, lam, vsigns);
     else
-        quantize_tile<D, DTYPE, false, VROT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
+        quantize_tile<D, DTYPE, false, VROT, SRFT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
                                              signs, rot_norm, lam, vsigns);
 }
 
@@ -342,7 +354,7 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
 
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                  const float* signs, float rot_norm, const float* lam,
+                                  const float* signs, float rot_norm, int rot_kind, const float* lam,
                                   const float* vsigns, const int32_t* pos, hipStream_t stream)
 {
     if (D != 64 && D != 128 && D != 256) return hipErrorInvalidValue;
@@ -352,8 +364,8 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         const int pair_slots = (n_new + 2) / 2;
         dim3 grid((pair_slots + 3) / 4, H, B), block(256);
         auto kern = D == 64 ? quantize_pair_kernel<64> : D == 128 ? quantize_pair_kernel<128> : quantize_pair_kernel<256>;
-        kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam,
-                                         vsigns, pos, pair_slots);
+        kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm,
+                                         signs ? rot_kind : 0, lam, vsigns, pos, pair_slots);
     } else {
         // one block per tile touched: the range may start inside a tile
         const int tiles = (n_new + 2 * kTile - 2) / kTile;
@@ -362,8 +374,12 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
                            const float*, float, const float*, const float*, const int32_t*);
         auto pick = [&](auto d) -> K {
             constexpr int DD = decltype(d)::value;
-            if (vsigns) return dtype == 0 ? quantize_tile_kernel<DD, 0, true> : quantize_tile_kernel<DD, 1, true>;
-            return dtype == 0 ? quantize_tile_kernel<DD, 0, false> : quantize_tile_kernel<DD, 1, false>;
+            // a rotated V goes with the Hadamard K rotation only (checked by the caller)
+            if (vsigns)
+                return dtype == 0 ? quantize_tile_kernel<DD, 0, true, false> : quantize_tile_kernel<DD, 1, true, false>;
+            if (signs && rot_kind)
+                return dtype == 0 ? quantize_tile_kernel<DD, 0, false, true> : quantize_tile_kernel<DD, 1, false, true>;
+            return dtype == 0 ? quantize_tile_kernel<DD, 0, false, false> : quantize_tile_kernel<DD, 1, false, false>;
         };
         const K kern = D == 64 ? pick(std::integral_constant<int, 64>{})
                      : D == 128 ? pick(std::integral_constant<int, 128>{})

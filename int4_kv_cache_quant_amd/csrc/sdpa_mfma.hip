@@ -58,6 +58,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "srft.hpp"
 
 namespace otq {
 
@@ -332,6 +333,62 @@ constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 template <int D, int P, int W>
 constexpr int kStages = 2 * W * Stage<D, P>::BYTES <= 80 * 1024 ? 2 : 1;
 
+// The query's FFT rotation (without rot_norm, which the score multiplier
+// carries) in the split kernel's query layout: lane (n16, r) holds channels
+// 32 g + 8 r + e in qx[g][e], i.e. complex number j = 16 g + 4 r + e / 2,
+// component e % 2.  Decimation-in-frequency stages of half-size h: h >= 16
+// pair g with g + h / 16 in the lane, h = 8 and 4 pair lanes 32 and 16
+// apart, h = 2 and 1 pair complex numbers inside an 8-channel run.
+template <int NG>
+__device__ __forceinline__ void srft_query(float (&qx)[NG][8], int r)
+{
+    constexpr int N = 16 * NG;
+    auto bfly = [](float& ar, float& ai, float& br, float& bi, int u) {
+        const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+        const float dr = ar - br, di = ai - bi;
+        ar = ar + br;
+        ai = ai + bi;
+        br = dr * wr - di * wi;
+        bi = dr * wi + di * wr;
+    };
+#pragma unroll
+    for (int h = N / 2; h >= 16; h >>= 1) {
+        const int gm = h / 16;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            if ((g & gm) == 0)
+#pragma unroll
+                for (int cp = 0; cp < 4; ++cp)
+                    bfly(qx[g][2 * cp], qx[g][2 * cp + 1], qx[g + gm][2 * cp], qx[g + gm][2 * cp + 1],
+                         (16 * (g % gm) + 4 * r + cp) * (64 / h));
+    }
+#pragma unroll
+    for (int h = 8; h >= 4; h >>= 1) {  // lanes 32 (r bit 1) and 16 (r bit 0) apart
+        const int m = h == 8 ? 32 : 16;
+        const bool upper = (r & (h / 4)) != 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int cp = 0; cp < 4; ++cp) {
+                const float ore = shfl_xor(qx[g][2 * cp], m), oim = shfl_xor(qx[g][2 * cp + 1], m);
+                const int u = ((4 * r + cp) & (h - 1)) * (64 / h);
+                const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                const float dr = ore - qx[g][2 * cp], di = oim - qx[g][2 * cp + 1];
+                const float ur = dr * wr - di * wi, ui = dr * wi + di * wr;
+                qx[g][2 * cp] = upper ? ur : qx[g][2 * cp] + ore;
+                qx[g][2 * cp + 1] = upper ? ui : qx[g][2 * cp + 1] + oim;
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        // h = 2: complex 0 with 2, 1 with 3; h = 1: 0 with 1, 2 with 3
+        bfly(qx[g][0], qx[g][1], qx[g][4], qx[g][5], 0);
+        bfly(qx[g][2], qx[g][3], qx[g][6], qx[g][7], 32);
+        bfly(qx[g][0], qx[g][1], qx[g][2], qx[g][3], 0);
+        bfly(qx[g][4], qx[g][5], qx[g][6], qx[g][7], 0);
+    }
+}
+
 template <int D, int P, bool HILO, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(kWavesPerEU<D>)))
 void split_mfma_kernel(SplitArgs a)
@@ -469,7 +526,16 @@ void split_mfma_kernel(SplitArgs a)
             qx[g][e] = col_valid ? widen(h16, a.dtype) : 0.0f;
         }
     }
-    if (HILO && rot) {
+    if (HILO && rot && a.rot_kind) {
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const float sg[8] = {sgn[g][0].x, sgn[g][0].y, sgn[g][0].z, sgn[g][0].w,
+                                 sgn[g][1].x, sgn[g][1].y, sgn[g][1].z, sgn[g][1].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[g][e] *= sg[e];
+        }
+        srft_query<NG>(qx, r);
+    } else if (HILO && rot) {
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const float sg[8] = {sgn[g][0].x, sgn[g][0].y, sgn[g][0].z, sgn[g][0].w,

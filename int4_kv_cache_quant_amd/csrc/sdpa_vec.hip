@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "srft.hpp"
 
 namespace otq {
 
@@ -85,7 +86,24 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
         q_lds[i / D][i % D] = x;
     }
     __syncthreads();
-    if (a.signs) {
+    if (a.signs && a.rot_kind) {  // the FFT rotation: complex pairs (2j, 2j + 1), DIF stages
+        for (int h = D / 4; h >= 1; h >>= 1) {
+            for (int i = tid; i < G * D / 4; i += 256) {
+                const int hh = i / (D / 4), kk = i % (D / 4);
+                const int j = (kk / h) * 2 * h + (kk % h);  // the pair's lower complex index
+                const int u = (kk % h) * (64 / h);
+                const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                const float ar = q_lds[hh][2 * j], ai = q_lds[hh][2 * j + 1];
+                const float br = q_lds[hh][2 * (j + h)], bi = q_lds[hh][2 * (j + h) + 1];
+                const float dr = ar - br, di = ai - bi;
+                q_lds[hh][2 * j] = ar + br;
+                q_lds[hh][2 * j + 1] = ai + bi;
+                q_lds[hh][2 * (j + h)] = dr * wr - di * wi;
+                q_lds[hh][2 * (j + h) + 1] = dr * wi + di * wr;
+            }
+            __syncthreads();
+        }
+    } else if (a.signs) {
         for (int h = 1; h < D; h <<= 1) {
             for (int i = tid; i < G * D / 2; i += 256) {
                 const int hh = i / (D / 2), kk = i % (D / 2);

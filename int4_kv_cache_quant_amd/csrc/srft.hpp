@@ -1,0 +1,176 @@
+// srft.hpp - the sign-randomised FFT rotation (SRFT) of K and of the query
+// ("SRFT + int4 KV-cache", core method: a sign-randomised FFT may take the
+// place of the Hadamard rotation, at the same quality).
+//
+// A vector of D reals is D/2 complex numbers z_j = (y_2j, y_2j+1).  After
+// the signs, the radix-2 decimation-in-frequency FFT runs in place: stages
+// of half-size h = N/2, N/4, ..., 1 (N = D/2) replace each pair (a, b) =
+// (z_j, z_j+h) with (a + b, (a - b) W^t), W = exp(-2 pi i / N), t = (j mod
+// h) N / (2h), which leaves the DFT coefficient of index bitrev(k) at
+// position k.  The result is multiplied by rot_norm = fp32(1/sqrt(N)); the
+// map is orthogonal, so a query rotated the same way keeps q . k.
+//
+// Every step is one IEEE fp32 operation (the bodies forbid contraction), the
+// complex product being (dr wr - di wi, dr wi + di wr) with each product
+// rounded before the sum, and the twiddles are the correctly rounded fp32
+// values of cos and -sin: the rotated values, and the codes quantised from
+// them, are the same bits in every kernel and in any other evaluation of the
+// same steps.
+#pragma once
+
+#include "common.hpp"
+
+namespace otq {
+namespace srft_detail {
+
+constexpr double kPi = 3.14159265358979323846;
+
+// cos and sin of x in [0, pi/4] by their Taylor series, in double: a few
+// ulps of double, far inside the distance of every twiddle below from an
+// fp32 rounding midpoint, so the fp32 roundings are the correct ones.
+constexpr void cos_sin(double x, double& c, double& s)
+{
+    double tc = 1.0, ts = x;
+    c = 0.0;
+    s = 0.0;
+    for (int n = 0; n < 30; ++n) {
+        c += tc;
+        s += ts;
+        tc = -tc * x * x / ((2.0 * n + 1.0) * (2.0 * n + 2.0));
+        ts = -ts * x * x / ((2.0 * n + 2.0) * (2.0 * n + 3.0));
+    }
+}
+
+// W_128^u = (cos, -sin)(2 pi u / 128), u < 64; a stage of half-size h of
+// any N <= 128 reads entry (j mod h) * 64 / h.  Angles are reduced to the
+// first octant, so the quarter-turn values are exact.
+struct Twiddles {
+    float re[64];
+    float im[64];
+};
+
+constexpr Twiddles make_twiddles()
+{
+    Twiddles t{};
+    for (int u = 0; u < 64; ++u) {
+        const int oct = u / 16, rem = u % 16;           // angle (pi/4) (oct + rem/16)
+        const int m = (oct & 1) ? 16 - rem : rem;       // odd octants: the complement
+        double c1 = 1.0, s1 = 0.0;
+        if (m != 0) cos_sin(kPi / 4.0 * m / 16.0, c1, s1);
+        double c = 0.0, s = 0.0;
+        switch (oct) {
+        case 0: c = c1; s = s1; break;      // a
+        case 1: c = s1; s = c1; break;      // pi/2 - b
+        case 2: c = -s1; s = c1; break;     // pi/2 + a
+        default: c = -c1; s = s1; break;    // pi - b
+        }
+        t.re[u] = static_cast<float>(c) + 0.0f;  // zeros are +0
+        t.im[u] = static_cast<float>(-s) + 0.0f;
+    }
+    return t;
+}
+
+static __constant__ Twiddles kTw = make_twiddles();
+
+// (a - b) W for the upper element of a pair, given d = a - b per component;
+// `d` is this element's component of a - b, `dd` the other one.
+__device__ __forceinline__ float twiddle_mul(float d, float dd, bool im, int u)
+{
+#pragma clang fp contract(off)
+    const float wr = kTw.re[u], wi = kTw.im[u];
+    return im ? dd * wi + d * wr : d * wr - dd * wi;
+}
+
+}  // namespace srft_detail
+
+// y <- rot_norm * FFT(y) (y already multiplied by the signs): a vector of D
+// reals spread over D / E consecutive lanes of an aligned lane group, E
+// consecutive reals per lane (E = 1 needs D <= 64); `lane` is the lane's
+// index within its group.
+template <int D, int E>
+__device__ __forceinline__ void srft_signed(float (&y)[E], float rot_norm, int lane)
+{
+#pragma clang fp contract(off)
+    constexpr int N = D / 2;
+    if constexpr (E == 1) {
+        static_assert(D <= 64, "one real per lane: one wave");
+        const int j = lane >> 1;
+        const bool im = (lane & 1) != 0;
+#pragma unroll
+        for (int h = N / 2; h >= 1; h >>= 1) {
+            const float o = shfl_xor(y[0], 2 * h);
+            const float d = o - y[0];          // a - b, used by upper elements
+            const float dd = shfl_xor(d, 1);   // the other component of the pair
+            const float up = srft_detail::twiddle_mul(d, dd, im, (j & (h - 1)) * (64 / h));
+            y[0] = (j & h) ? up : y[0] + o;
+        }
+    } else {
+        constexpr int CE = E / 2;  // complex numbers per lane
+#pragma unroll
+        for (int h = N / 2; h >= 1; h >>= 1) {
+            if (h >= CE) {  // pairs in lanes h / CE apart
+                const int m = h / CE;
+                const bool upper = (lane & m) != 0;
+#pragma unroll
+                for (int c = 0; c < CE; ++c) {
+                    const float ore = shfl_xor(y[2 * c], m), oim = shfl_xor(y[2 * c + 1], m);
+                    const int u = ((lane * CE + c) & (h - 1)) * (64 / h);
+                    const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                    const float dr = ore - y[2 * c], di = oim - y[2 * c + 1];
+                    const float ur = dr * wr - di * wi, ui = dr * wi + di * wr;
+                    y[2 * c] = upper ? ur : y[2 * c] + ore;
+                    y[2 * c + 1] = upper ? ui : y[2 * c + 1] + oim;
+                }
+            } else {  // pairs inside the lane: (lane CE + c) mod h = c mod h
+#pragma unroll
+                for (int c = 0; c < CE; ++c) {
+                    if ((c & h) == 0) {
+                        const int u = (c & (h - 1)) * (64 / h);
+                        const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                        const float ar = y[2 * c], ai = y[2 * c + 1];
+                        const float br = y[2 * (c + h)], bi = y[2 * (c + h) + 1];
+                        const float dr = ar - br, di = ai - bi;
+                        y[2 * c] = ar + br;
+                        y[2 * c + 1] = ai + bi;
+                        y[2 * (c + h)] = dr * wr - di * wi;
+                        y[2 * (c + h) + 1] = dr * wi + di * wr;
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
+}
+
+// The same transform over one real per thread (threads 0..D-1 of the block;
+// threads past D hold no element and stay out of xch), without the final
+// rot_norm: pairs up to 64 reals apart meet by lane exchange, wider ones
+// through LDS.
+template <int D>
+__device__ __forceinline__ float srft_thread(float y, float* xch)
+{
+#pragma clang fp contract(off)
+    constexpr int N = D / 2;
+    const int t = threadIdx.x, j = t >> 1;
+    const bool im = (t & 1) != 0;
+#pragma unroll
+    for (int h = N / 2; h >= 1; h >>= 1) {
+        float o;
+        if (2 * h < 64) {
+            o = shfl_xor(y, 2 * h);
+        } else {
+            __syncthreads();
+            if (t < D) xch[t] = y;
+            __syncthreads();
+            o = t < D ? xch[t ^ (2 * h)] : y;
+        }
+        const float d = o - y;
+        const float dd = shfl_xor(d, 1);
+        const float up = srft_detail::twiddle_mul(d, dd, im, (j & (h - 1)) * (64 / h));
+        y = (j & h) ? up : y + o;
+    }
+    return y;
+}
+
+}  // namespace otq

@@ -23,12 +23,12 @@ def to_bits(t):
 
 
 def build_cache(k, v, capacity, signs=None, prefill_chunk=None, append_last=True, chan_scale=None,
-                v_signs=None):
+                v_signs=None, rot_kind="srht"):
     """Quantise K/V [B, H, T, D] (device) into a new cache: prefill T-1 tokens
     (optionally in chunks), then append the last token on its own."""
     B, H, T, D = k.shape
     cache = otq.Int4KVCache(B, H, D, capacity, device=k.device, rot_signs=signs,
-                            chan_scale=chan_scale, v_rot_signs=v_signs)
+                            chan_scale=chan_scale, v_rot_signs=v_signs, rot_kind=rot_kind)
     n_pre = T - 1 if append_last else T
     step = n_pre if prefill_chunk is None else prefill_chunk
     for t0 in range(0, n_pre, max(step, 1)):
@@ -48,10 +48,11 @@ def host_cache(cache):
             layout.v_tiled_to_plain(cache.v_codes.cpu().numpy(), D), cache.v_scales.cpu().numpy())
 
 
-def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=None, v_signs=None):
+def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=None, v_signs=None,
+                 rot_kind="srht"):
     kb, vb = to_bits(k), to_bits(v)
     kc, ks = oracle.quantize(kb, dtype, signs=signs, rot_norm=rot_norm, threads=threads,
-                             chan_scale=chan_scale)
+                             chan_scale=chan_scale, rot_kind=rot_kind)
     vc, vs = oracle.quantize(vb, dtype, signs=v_signs, rot_norm=rot_norm, threads=threads)
     return kc, ks, vc, vs
 
@@ -78,8 +79,11 @@ def errors(out, ref):
     return max_abs, rel
 
 
-def rot_norm32(D):
-    return float(np.float32(1.0 / math.sqrt(D)))
+def rot_norm32(D, rot_kind="srht"):
+    """fp32(1/sqrt(n)): n = D for the Hadamard rotation, D/2 (complex
+    numbers) for the FFT one."""
+    n = D // 2 if rot_kind == "srft" else D
+    return float(np.float32(1.0 / math.sqrt(n)))
 
 
 def rand_signs(D, seed):

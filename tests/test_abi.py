@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 3
+    assert lib.otq_abi_version() == 4
 
 
 def test_status_strings():
@@ -85,6 +85,30 @@ def test_quantize_append_host_errors():
     bad.v_scales = None
     assert call(FAKE, FAKE, 1, 1, bad, FAKE) == otq.OTQ_EINVAL
     assert lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, None, P(FAKE), None) == otq.OTQ_EINVAL
+
+
+def test_rotation_kind_host_checks():
+    """K's rotation kind is read only with signs; it must be SRHT or SRFT,
+    and a rotated V goes with the Hadamard kind only."""
+    lib = otq.lib()
+    P = ctypes.c_void_p
+    call = lambda desc: lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, ctypes.byref(desc), P(FAKE), None)
+    plan = lambda desc: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, 0, ctypes.byref(otq.otq_plan()))
+    d = _desc()
+    d.k_rot_kind = 7                      # ignored without signs
+    assert plan(d) == otq.OTQ_OK
+    d = _desc(signs=FAKE)
+    for kind, want in ((otq.OTQ_ROT_SRHT, otq.OTQ_OK), (otq.OTQ_ROT_SRFT, otq.OTQ_OK), (2, otq.OTQ_EINVAL),
+                       (-1, otq.OTQ_EINVAL)):
+        d.k_rot_kind = kind
+        assert plan(d) == want, kind
+        if want != otq.OTQ_OK:
+            assert call(d) == want
+    d.k_rot_kind = otq.OTQ_ROT_SRFT
+    d.v_rot_signs = FAKE
+    assert plan(d) == otq.OTQ_EUNSUPPORTED and call(d) == otq.OTQ_EUNSUPPORTED
+    d.k_rot_kind = otq.OTQ_ROT_SRHT
+    assert plan(d) == otq.OTQ_OK
 
 
 def test_plan_batch_order_table():

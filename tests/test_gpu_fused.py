@@ -50,6 +50,8 @@ def _poison(cache, lens):
 
 def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, seed=0, steps=1,
          variant=otq.OTQ_VARIANT_MFMA, scaled=False, rotate_v=False):
+    """rotate: False, True (the Hadamard rotation) or "srft" (the FFT one)."""
+    kind = "srft" if rotate == "srft" else "srht"
     g = torch.Generator().manual_seed(seed)
     Hq = G * Hkv
     T = max(lens) + steps - 1
@@ -68,9 +70,9 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
     cache = build_cache(k[:, :, :T].to(DEV).contiguous(), v[:, :, :T].to(DEV).contiguous(), cap,
                         signs=None if signs is None else signs.to(DEV), append_last=False,
                         chan_scale=None if lam is None else lam.to(DEV),
-                        v_signs=None if vsg is None else vsg.to(DEV))
-    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
-                             chan_scale=lam_np, v_signs=vsg_np)
+                        v_signs=None if vsg is None else vsg.to(DEV), rot_kind=kind)
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D, kind),
+                             chan_scale=lam_np, v_signs=vsg_np, rot_kind=kind)
     for step in range(steps):
         cur = [n + step for n in lens]
         _poison(cache, cur)
@@ -96,8 +98,8 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
                 "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, f"seq {b}"
         kc, ks, vc, vs = ref_cache
         ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(cur, np.int32), scale,
-                          signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                          threads=8, chan_scale=lam_np, v_signs=vsg_np)
+                          signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D, kind),
+                          threads=8, chan_scale=lam_np, v_signs=vsg_np, rot_kind=kind)
         ma, rel = errors(out.cpu().numpy(), ref)
         say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
         assert ma <= MAX_ABS and rel <= REL_L2
@@ -128,6 +130,15 @@ def test_fused_append_v_rotated(D, G, rotate, scaled):
     it and the output is brought back by the inverse rotation."""
     _run(2, G, 2, D, 384, [351, 190], rotate=rotate, chunk=128, seed=11 * D + G + rotate + scaled,
          scaled=scaled, rotate_v=True)
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("G", [1, 8])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_fused_append_srft(D, G, scaled):
+    """K rotated by the sign-randomised FFT: the combine rotates the new
+    token's K (to the bulk kernel's bytes) and the query for its score."""
+    _run(2, G, 2, D, 384, [351, 190], rotate="srft", chunk=128, seed=13 * D + G + scaled, scaled=scaled)
 
 
 @pytest.mark.parametrize("lens", [[1, 2], [129, 128], [257, 33], [32, 31]])

@@ -139,6 +139,50 @@ def test_quantize_adversarial_bf16_ranges():
     assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("scaled", [False, True])
+@pytest.mark.parametrize("chunk", [19, 5])
+def test_quantize_srft_bit_exact(D, dtype, scaled, chunk):
+    """K rotated by the sign-randomised FFT (then, if scaled, by K's
+    per-channel scale): chunks of 19 tokens take the bulk kernel (whole and
+    edge tiles), chunks of 5 the small-append kernel; the last token comes
+    alone.  Codes and scales are the oracle's bit for bit."""
+    B, H, T, cap = 2, 3, 77, 96
+    say(f"quantize srft D={D} dtype={dtype} scaled={scaled} chunk={chunk}")
+    k, v = _rand_kv(B, H, T, D, dtype, seed=D + 23 + 2 * scaled + chunk, outliers=(3, 40))
+    signs = rand_signs(D, D + 29)
+    lam = chan_scales(D, D + 31, outliers=(3,)) if scaled else None
+    cache = build_cache(k, v, cap, signs=signs.to(DEV), prefill_chunk=chunk,
+                        chan_scale=None if lam is None else lam.to(DEV), rot_kind="srft")
+    torch.cuda.synchronize()
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    ref = oracle_cache(k.cpu(), v.cpu(), name, signs.numpy(), rot_norm32(D, "srft"),
+                       chan_scale=None if lam is None else lam.numpy(), rot_kind="srft")
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
+@pytest.mark.parametrize("D", [64, 256])
+def test_quantize_srft_exponent_ranges(D):
+    """FFT-rotated bf16 vectors scaled across the exponent range: twiddle
+    products in the subnormal range, scales below 2^-80 and above 2^100 (which
+    divide element by element) and just inside them."""
+    exps = (-131, -120, -93, -87, 0, 95, 101, 120)
+    g = torch.Generator().manual_seed(D + 61)
+    base = torch.randn((32, D), generator=g)
+    x = torch.stack([torch.ldexp(base[t], torch.tensor(exps[t % len(exps)])) for t in range(32)])
+    x = x.to(torch.bfloat16)[None, None]   # [1,1,32,D]
+    signs = rand_signs(D, D + 67)
+    say(f"quantize srft exponent ranges D={D}")
+    cache = build_cache(x.to(DEV), (-x).to(DEV), 32, prefill_chunk=16, signs=signs.to(DEV),
+                        rot_kind="srft")
+    torch.cuda.synchronize()
+    ref = oracle_cache(x, -x, "bf16", signs.numpy(), rot_norm32(D, "srft"), rot_kind="srft")
+    bad = compare_codes(host_cache(cache), ref, 32)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
 def test_append_preserves_neighbours_and_skips_out_of_range():
     """Single-token appends at odd and even positions keep the other nibble of
     each shared V byte; positions outside [0, capacity) are not written."""

@@ -49,7 +49,9 @@ def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spi
 def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
          rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0,
          scaled=False, rotate_v=False):
-    k, v, q, signs, lam = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, rotate, spikes=spikes,
+    """rotate: False, True (the Hadamard rotation) or "srft" (the FFT one)."""
+    kind = "srft" if rotate == "srft" else "srht"
+    k, v, q, signs, lam = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, bool(rotate), spikes=spikes,
                                 beta=beta, scaled=scaled)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     name = "fp16" if dtype == torch.float16 else "bf16"
@@ -58,7 +60,7 @@ def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sig
     vsg_np = None if vsg is None else vsg.numpy()
     cache = build_cache(k.to(DEV), v.to(DEV), cap, signs=None if signs is None else signs.to(DEV),
                         prefill_chunk=max(1, cap // 3), chan_scale=None if lam is None else lam.to(DEV),
-                        v_signs=None if vsg is None else vsg.to(DEV))
+                        v_signs=None if vsg is None else vsg.to(DEV), rot_kind=kind)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     max_len = max(1, int(max(lens)))
     plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
@@ -67,14 +69,14 @@ def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sig
         f"rotate_v={rotate_v}")
     out = cache.decode(q.to(DEV), lens_t, max_len, scale, plan=plan)
     torch.cuda.synchronize()
-    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D),
-                             chan_scale=lam_np, v_signs=vsg_np)
+    ref_cache = oracle_cache(k, v, name, None if signs is None else signs.numpy(), rot_norm32(D, kind),
+                             chan_scale=lam_np, v_signs=vsg_np, rot_kind=kind)
     assert compare_codes(host_cache(cache), ref_cache, cap) == {
         "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
     kc, ks, vc, vs = ref_cache
     ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(lens, np.int32), scale,
-                      signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D),
-                      rows=rows, threads=8, chan_scale=lam_np, v_signs=vsg_np)
+                      signs=None if signs is None else signs.numpy(), rot_norm=rot_norm32(D, kind),
+                      rows=rows, threads=8, chan_scale=lam_np, v_signs=vsg_np, rot_kind=kind)
     got = out.cpu().numpy().astype(np.float64)
     if rows is not None:
         got = got.reshape(-1, D)[rows]
@@ -129,6 +131,21 @@ def test_sdpa_v_rotated(variant, G, D, rotate, scaled):
     inverse rotation; alone, with K rotated, and with K rotated and scaled."""
     got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 70], seed=51 + G + D + rotate + scaled, rotate=rotate,
                        chunk=128, variant=variant, scaled=scaled, rotate_v=True)
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("variant,G,D", [(VEC, 1, 64), (VEC, 2, 256), (VEC, 4, 128), (MF, 1, 256),
+                                         (MF, 2, 256), (MF, 4, 64), (MF, 8, 128), (MF, 16, 128),
+                                         (MF, 8, 64)])
+@pytest.mark.parametrize("scaled", [False, True])
+def test_sdpa_srft(variant, G, D, scaled):
+    """K rotated by the sign-randomised FFT: the split kernels rotate the
+    query the same way (then divide it by K's channel scale if scaled); one
+    and two KV heads per MFMA wave, every head width."""
+    got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 77], seed=71 + G + D + scaled, rotate="srft",
+                       chunk=128, variant=variant, scaled=scaled)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2

@@ -127,6 +127,12 @@ def main():
                     help="give K a per-channel scale (seeded; 1/multiplier on the outlier channels)")
     ap.add_argument("--v-rotate", action="store_true",
                     help="rotate V too (seeded signs); outputs are brought back by the inverse rotation")
+    ap.add_argument("--srft", action="store_true",
+                    help="rotate K by the sign-randomised FFT (seeded signs); a workload that rotates K "
+                         "switches from the Walsh-Hadamard rotation to this one")
+    ap.add_argument("--srht", action="store_true",
+                    help="rotate K by the sign-randomised Walsh-Hadamard transform (seeded signs) on a "
+                         "workload that does not rotate it")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
@@ -176,15 +182,20 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- setup
+    rot_kind = "srft" if args.srft else "srht"
+    if args.srft and args.srht:
+        sys.exit("bench.py: --srft and --srht name two different K rotations")
+    if args.srft and args.v_rotate:
+        sys.exit("bench.py: a rotated V goes with the Walsh-Hadamard K rotation only (--srft excludes --v-rotate)")
     t_setup = time.time()
     caches, k_new, v_new, qs, lens_l, pos_l = [], [], [], [], [], []
     host_kv0 = None
     for l in range(L):
-        signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if w.rotate else None
+        signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if (w.rotate or args.srft or args.srht) else None
         lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if args.chan_scale else None
         vsg = torch.from_numpy(synth.v_rot_signs(w, l)).to(dev) if args.v_rotate else None
         cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs,
-                                chan_scale=lam, v_rot_signs=vsg)
+                                chan_scale=lam, v_rot_signs=vsg, rot_kind=rot_kind)
         k = synth.kv(w, l, "k", device=dev)
         v = synth.kv(w, l, "v", device=dev)
         lens = synth.lens(w, l)
@@ -328,7 +339,8 @@ def main():
     bulk_in = [(synth.kv(w, i, "k", T=n_bulk, device=dev), synth.kv(w, i, "v", T=n_bulk, device=dev))
                for i in range(n_chunks)]
     scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs,
-                              chan_scale=caches[0].chan_scale, v_rot_signs=caches[0].v_rot_signs)
+                              chan_scale=caches[0].chan_scale, v_rot_signs=caches[0].v_rot_signs,
+                              rot_kind=rot_kind)
     bulk_pos = [torch.full((w.B,), i * n_bulk, dtype=torch.int32, device=dev) for i in range(n_chunks)]
 
     def bulk_pass():
@@ -374,14 +386,15 @@ def main():
         kb, vb, sg, lam0, vsg0 = host_kv0
         t = time.time()
         kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
-                                 chan_scale=lam0)
+                                 chan_scale=lam0, rot_kind=rot_kind)
         vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads)
         log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
         lens0 = synth.lens(w, 0)
         q0 = synth.bits(qs[0])
         t = time.perf_counter()
         ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
-                          rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0, v_signs=vsg0)
+                          rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0, v_signs=vsg0,
+                          rot_kind=rot_kind)
         cpu_s = time.perf_counter() - t
         got = outs[0].cpu().numpy().astype(np.float64)
         err = got - ref
@@ -414,6 +427,7 @@ def main():
             "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
             "graph": graph is not None, "k_chan_scale": bool(args.chan_scale),
             "v_rotated": bool(args.v_rotate),
+            "k_rotation": ("none" if not (w.rotate or args.srft or args.srht) else rot_kind),
             "step": "per layer: the split pass over the cached tokens, then the combine pass that "
                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)",
         },

@@ -111,6 +111,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     [[maybe_unused]] float sg = 1.0f, lm = 1.0f, vsg = 1.0f;
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
+    [[maybe_unused]] SrftThreadTw<(DA > 0 ? DA : 64)> stw;  // the FFT rotation's twiddles
     if constexpr (APPEND) {
         const int G = a.Hq / a.H, h = row % a.Hq;
         kvh = h / G;
@@ -120,6 +121,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         vx = a.v_new[src];
         qx = static_cast<const uint16_t*>(a.q)[(size_t)row * DA + ch];
         if (ROT) sg = a.signs[ch];
+        if (ROT && a.rot_kind) stw.load(tid);
         if (LAM) lm = a.lam[ch];  // K's channel scale
         if (VROT) vsg = a.vsigns[ch];
         // one block per KV head writes the token: the first query head's,
@@ -192,7 +194,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float x = widen(kx, a.dtype);
         if (ROT) {
             x = x * sg;
-            x = a.rot_kind ? srft_thread<DA>(x, xch) : fwht_thread<DA>(x, xch);
+            x = a.rot_kind ? srft_thread<DA>(x, xch, stw) : fwht_thread<DA>(x, xch);
             x = x * a.rot_norm;
         }
         if (LAM) x = x * lm;  // after the rotation
@@ -236,7 +238,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float y = widen(qx, a.dtype);
         if (ROT) {
             y = y * sg;
-            y = a.rot_kind ? srft_thread<DA>(y, xch) : fwht_thread<DA>(y, xch);
+            y = a.rot_kind ? srft_thread<DA>(y, xch, stw) : fwht_thread<DA>(y, xch);
             y = y * a.rot_norm;
         }
         if (LAM) y = y / lm;

@@ -84,6 +84,9 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
         for (int e = 0; e < E; ++e) old[e] = vt[v_tile_byte<D>(lane * E + e, t0 % kTile)];
     }
 
+    SrftLaneTw<D, E> stw;  // the FFT rotation's twiddles of this lane
+    if (signs && rot_kind) stw.load(lane);
+
     int vcode[2][E];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
             if (rot_kind) {  // the FFT rotation
 #pragma unroll
                 for (int e = 0; e < E; ++e) x[e] = x[e] * signs[lane * E + e];
-                srft_signed<D, E>(x, rot_norm, lane);
+                srft_signed<D, E>(x, rot_norm, lane, stw);
             } else {
                 rotate_lane<D>(x, signs, rot_norm, lane);
             }
@@ -208,6 +211,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
 #pragma unroll
         for (int e = 0; e < 8; ++e) sg[e] = signs[8 * (tid % LT) + e];
     }
+    // the FFT rotation's twiddles: the lane's position in its token, hence
+    // its twiddles, is the same in every unit
+    [[maybe_unused]] SrftLaneTw<D, 8> stw;
+    if constexpr (SRFT) stw.load(tid % LT);
     if constexpr (VROT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vsg[e] = vsigns[8 * (tid % LT) + e];
@@ -258,7 +265,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[e];
             if constexpr (SRFT)
-                srft_signed<D, 8>(x, rot_norm, j);
+                srft_signed<D, 8>(x, rot_norm, j, stw);
             else
                 rotate_signed<D, 8>(x, rot_norm, j);
         }

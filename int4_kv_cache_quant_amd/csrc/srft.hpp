@@ -72,23 +72,82 @@ constexpr Twiddles make_twiddles()
 
 static __constant__ Twiddles kTw = make_twiddles();
 
-// (a - b) W for the upper element of a pair, given d = a - b per component;
-// `d` is this element's component of a - b, `dd` the other one.
-__device__ __forceinline__ float twiddle_mul(float d, float dd, bool im, int u)
+// The twiddles of a stage of half-size h in lane order: entry h + v holds
+// W_128^(v 64 / h) for v < h (h = 1, 2, ..., 64; entry 0 unused), so the
+// twiddles of consecutive complex numbers are adjacent and a lane reads its
+// share of a stage with 16-byte loads.
+struct Cf {
+    float re, im;
+};
+struct alignas(16) StageTwiddles {
+    Cf w[128];
+};
+
+constexpr StageTwiddles make_stage_twiddles()
 {
-#pragma clang fp contract(off)
-    const float wr = kTw.re[u], wi = kTw.im[u];
-    return im ? dd * wi + d * wr : d * wr - dd * wi;
+    const Twiddles t = make_twiddles();
+    StageTwiddles s{};
+    for (int h = 1; h <= 64; h *= 2)
+        for (int v = 0; v < h; ++v) s.w[h + v] = Cf{t.re[v * (64 / h)], t.im[v * (64 / h)]};
+    return s;
 }
 
+static __constant__ StageTwiddles kTwS = make_stage_twiddles();
+
+// n consecutive entries from entry i (i a multiple of 2 when n >= 2)
+template <int n>
+__device__ __forceinline__ void load_tw(Cf* dst, int i)
+{
+    if constexpr (n == 1) {
+        dst[0] = kTwS.w[i];
+    } else {
+#pragma unroll
+        for (int k = 0; k < n; k += 2) {
+            const float4 v = *reinterpret_cast<const float4*>(&kTwS.w[i + k]);
+            dst[k] = Cf{v.x, v.y};
+            dst[k + 1] = Cf{v.z, v.w};
+        }
+    }
+}
+
+
+constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }
+
 }  // namespace srft_detail
+
+// The lane-dependent twiddles of a vector of D reals spread over D / E
+// lanes, E reals per lane: for every stage whose pairs lie in different
+// lanes, those of the lane's complex numbers (E >= 2), or of the lane's
+// element's complex number (E = 1).  Loaded once, used for every vector the
+// lane rotates at the same position.
+template <int D, int E>
+struct SrftLaneTw {
+    static constexpr int N = D / 2;
+    static constexpr int CE = E >= 2 ? E / 2 : 1;
+    // stages of half-size N/2 ... CE (E >= 2) or N/2 ... 1 (E = 1)
+    static constexpr int S = srft_detail::ilog2(N) - (E >= 2 ? srft_detail::ilog2(CE) : 0);
+    srft_detail::Cf w[S][CE];
+
+    __device__ __forceinline__ void load(int lane)
+    {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int h = (N / 2) >> s;
+            if constexpr (E == 1)
+                srft_detail::load_tw<1>(w[s], h + ((lane >> 1) & (h - 1)));
+            else  // the lane's complex numbers lane CE + c, c < CE: (lane mod h / CE) CE + c
+                srft_detail::load_tw<CE>(w[s], h + ((lane & (h / CE - 1)) * CE));
+        }
+    }
+};
 
 // y <- rot_norm * FFT(y) (y already multiplied by the signs): a vector of D
 // reals spread over D / E consecutive lanes of an aligned lane group, E
 // consecutive reals per lane (E = 1 needs D <= 64); `lane` is the lane's
-// index within its group.
+// index within its group and tw its loaded twiddles.
 template <int D, int E>
-__device__ __forceinline__ void srft_signed(float (&y)[E], float rot_norm, int lane)
+__device__ __forceinline__ void srft_signed(float (&y)[E], float rot_norm, int lane,
+                                            const SrftLaneTw<D, E>& tw)
 {
 #pragma clang fp contract(off)
     constexpr int N = D / 2;
@@ -97,25 +156,28 @@ __device__ __forceinline__ void srft_signed(float (&y)[E], float rot_norm, int l
         const int j = lane >> 1;
         const bool im = (lane & 1) != 0;
 #pragma unroll
-        for (int h = N / 2; h >= 1; h >>= 1) {
+        for (int s = 0; s < SrftLaneTw<D, E>::S; ++s) {
+            const int h = (N / 2) >> s;
             const float o = shfl_xor(y[0], 2 * h);
             const float d = o - y[0];          // a - b, used by upper elements
             const float dd = shfl_xor(d, 1);   // the other component of the pair
-            const float up = srft_detail::twiddle_mul(d, dd, im, (j & (h - 1)) * (64 / h));
+            const float wr = tw.w[s][0].re, wi = tw.w[s][0].im;
+            const float up = im ? dd * wi + d * wr : d * wr - dd * wi;
             y[0] = (j & h) ? up : y[0] + o;
         }
     } else {
         constexpr int CE = E / 2;  // complex numbers per lane
+        constexpr int NS = srft_detail::ilog2(N);  // stages; the first S pair lanes
 #pragma unroll
-        for (int h = N / 2; h >= 1; h >>= 1) {
+        for (int s = 0; s < NS; ++s) {
+            const int h = (N / 2) >> s;
             if (h >= CE) {  // pairs in lanes h / CE apart
                 const int m = h / CE;
                 const bool upper = (lane & m) != 0;
 #pragma unroll
                 for (int c = 0; c < CE; ++c) {
                     const float ore = shfl_xor(y[2 * c], m), oim = shfl_xor(y[2 * c + 1], m);
-                    const int u = ((lane * CE + c) & (h - 1)) * (64 / h);
-                    const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                    const float wr = tw.w[s][c].re, wi = tw.w[s][c].im;
                     const float dr = ore - y[2 * c], di = oim - y[2 * c + 1];
                     const float ur = dr * wr - di * wi, ui = dr * wi + di * wr;
                     y[2 * c] = upper ? ur : y[2 * c] + ore;
@@ -143,19 +205,37 @@ __device__ __forceinline__ void srft_signed(float (&y)[E], float rot_norm, int l
     for (int e = 0; e < E; ++e) y[e] = y[e] * rot_norm;
 }
 
+// The twiddles of one real per thread: one per stage, for the thread's
+// complex number j = t / 2.
+template <int D>
+struct SrftThreadTw {
+    static constexpr int S = srft_detail::ilog2(D / 2);
+    srft_detail::Cf w[S];
+
+    __device__ __forceinline__ void load(int t)
+    {
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            const int h = (D / 4) >> s;
+            srft_detail::load_tw<1>(&w[s], h + ((t >> 1) & (h - 1)));
+        }
+    }
+};
+
 // The same transform over one real per thread (threads 0..D-1 of the block;
 // threads past D hold no element and stay out of xch), without the final
 // rot_norm: pairs up to 64 reals apart meet by lane exchange, wider ones
 // through LDS.
 template <int D>
-__device__ __forceinline__ float srft_thread(float y, float* xch)
+__device__ __forceinline__ float srft_thread(float y, float* xch, const SrftThreadTw<D>& tw)
 {
 #pragma clang fp contract(off)
     constexpr int N = D / 2;
     const int t = threadIdx.x, j = t >> 1;
     const bool im = (t & 1) != 0;
 #pragma unroll
-    for (int h = N / 2; h >= 1; h >>= 1) {
+    for (int s = 0; s < SrftThreadTw<D>::S; ++s) {
+        const int h = (N / 2) >> s;
         float o;
         if (2 * h < 64) {
             o = shfl_xor(y, 2 * h);
@@ -167,7 +247,8 @@ __device__ __forceinline__ float srft_thread(float y, float* xch)
         }
         const float d = o - y;
         const float dd = shfl_xor(d, 1);
-        const float up = srft_detail::twiddle_mul(d, dd, im, (j & (h - 1)) * (64 / h));
+        const float wr = tw.w[s].re, wi = tw.w[s].im;
+        const float up = im ? dd * wi + d * wr : d * wr - dd * wi;
         y = (j & h) ? up : y + o;
     }
     return y;

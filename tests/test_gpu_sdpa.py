@@ -243,21 +243,24 @@ def test_sdpa_deterministic():
 
 # -------------------------------------------------------------- full workloads
 
-def _full(cfg, rows_per_seq=None, layer=0, options=False):
+def _full(cfg, rows_per_seq=None, layer=0, options=False, srft=False):
     """options: K's per-channel scale and a rotated V (seeded, as bench.py
-    --chan-scale --v-rotate makes them) on top of the workload's own."""
+    --chan-scale --v-rotate makes them) on top of the workload's own; srft:
+    K rotated by the sign-randomised FFT (with K's channel scale when options
+    is set too; as bench.py --srft makes it)."""
     w = synth.WORKLOADS[cfg]
-    say(f"sdpa full workload {cfg} {w.name} options={options}")
+    kind = "srft" if srft else "srht"
+    say(f"sdpa full workload {cfg} {w.name} options={options} srft={srft}")
     k = synth.kv(w, layer, "k", device=DEV)
     v = synth.kv(w, layer, "v", device=DEV)
     q = synth.query(w, layer, device=DEV)
     lens = synth.lens(w, layer)
-    signs = torch.from_numpy(synth.rot_signs(w, layer)).to(DEV) if w.rotate else None
+    signs = torch.from_numpy(synth.rot_signs(w, layer)).to(DEV) if (w.rotate or srft) else None
     lam = synth.chan_scale(w, layer) if options else None
-    vsg = synth.v_rot_signs(w, layer) if options else None
+    vsg = synth.v_rot_signs(w, layer) if (options and not srft) else None
     cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs,
                             chan_scale=None if lam is None else torch.from_numpy(lam),
-                            v_rot_signs=None if vsg is None else torch.from_numpy(vsg))
+                            v_rot_signs=None if vsg is None else torch.from_numpy(vsg), rot_kind=kind)
     # prefill lens-1 tokens per sequence, then append token lens-1 (ragged-aware)
     for t0 in range(0, w.T, 8192):
         t1 = min(w.T, t0 + 8192)
@@ -271,8 +274,8 @@ def _full(cfg, rows_per_seq=None, layer=0, options=False):
     out = cache.decode(q, lens_t, int(lens.max()), w.scale)
     torch.cuda.synchronize()
     ref_cache = oracle_cache(k.cpu(), v.cpu(), w.dtype,
-                             None if signs is None else signs.cpu().numpy(), rot_norm32(w.D),
-                             threads=16, chan_scale=lam, v_signs=vsg)
+                             None if signs is None else signs.cpu().numpy(), rot_norm32(w.D, kind),
+                             threads=16, chan_scale=lam, v_signs=vsg, rot_kind=kind)
     assert compare_codes(host_cache(cache), ref_cache, w.T) == {
         "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
     rng = np.random.default_rng(cfg)
@@ -284,7 +287,8 @@ def _full(cfg, rows_per_seq=None, layer=0, options=False):
     kc, ks, vc, vs = ref_cache
     ref = oracle.sdpa(to_bits(q), w.dtype, kc, ks, vc, vs, lens, w.scale,
                       signs=None if signs is None else signs.cpu().numpy(),
-                      rot_norm=rot_norm32(w.D), rows=rows, threads=16, chan_scale=lam, v_signs=vsg)
+                      rot_norm=rot_norm32(w.D, kind), rows=rows, threads=16, chan_scale=lam, v_signs=vsg,
+                      rot_kind=kind)
     got = out.cpu().numpy().reshape(-1, w.D)[rows].astype(np.float64)
     ma, rel = errors(got, ref)
     say(f"  rows={len(rows)} max_abs={ma:.3e} rel_l2={rel:.3e}")
@@ -315,3 +319,10 @@ def test_full_workload_5_ragged_rotated():
 def test_full_workload_with_options(cfg, rows_per_seq):
     """The full workloads with K's per-channel scale and a rotated V."""
     _full(cfg, rows_per_seq=rows_per_seq, options=True)
+
+
+@pytest.mark.parametrize("cfg,rows_per_seq,options", [(3, 8, False), (4, 8, True), (5, 2, False)])
+def test_full_workload_srft(cfg, rows_per_seq, options):
+    """The full workloads with K rotated by the sign-randomised FFT (workload
+    5 switches from the Hadamard rotation to it)."""
+    _full(cfg, rows_per_seq=rows_per_seq, options=options, srft=True)

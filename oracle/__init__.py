@@ -45,6 +45,8 @@ def _load():
     lib.oracle_srft_f32.restype = None
     lib.oracle_srft_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
     lib.oracle_srft_f64.restype = None
+    lib.oracle_unsrft_f64.argtypes = [P, P, ctypes.c_int, ctypes.c_double]
+    lib.oracle_unsrft_f64.restype = None
     lib.oracle_twiddle_f32.argtypes = [ctypes.c_int, ctypes.c_int, P, P]
     lib.oracle_twiddle_f32.restype = None
     lib.oracle_quantize_vector.argtypes = [P, ctypes.c_int, P, P]
@@ -117,6 +119,15 @@ def srft_f64(x, signs, c):
     y = _c(x, np.float64).copy()
     s = _c(signs, np.float32)
     lib.oracle_srft_f64(_ptr(y), _ptr(s), y.shape[-1], float(c))
+    return y
+
+
+def unsrft_f64(y, signs, c):
+    """The inverse of srft_f64: s (.) (c U y), U the stages undone in reverse."""
+    lib = _load()
+    y = _c(y, np.float64).copy()
+    s = _c(signs, np.float32)
+    lib.oracle_unsrft_f64(_ptr(y), _ptr(s), y.shape[-1], float(c))
     return y
 
 
@@ -199,8 +210,8 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
     """Decode attention over a plain-layout cache.
 
     q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D/2]; scales
-    [B, Hkv, cap, D/32]; lens [B]; rot_kind: "srht" or "srft", K's rotation
-    when signs is given; chan_scale: the K cache's per-channel
+    [B, Hkv, cap, D/32]; lens [B]; rot_kind: "srht" or "srft", the kind of
+    K's rotation (signs) and of V's (v_signs); chan_scale: the K cache's per-channel
     scale lambda [D] or None; v_signs: the signs V was rotated with (same
     rot_norm as K) or None.  Returns float64 [B, Hq, D], or [len(rows), D]
     for the listed rows (row = b * Hq + h).

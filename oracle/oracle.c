@@ -51,7 +51,9 @@
  * t = (j mod h) N / (2h) for the pair's lower index j), which leaves the
  * DFT coefficient of index bitrev(k) at position k, and the result is
  * multiplied by c = 1/sqrt(N).  That map is orthogonal on R^D, so a query
- * rotated the same way keeps every dot product.  In fp32 every step is one
+ * rotated the same way keeps every dot product.  V may be rotated by the
+ * same kind (its own signs), and attention then brings every dequantised V
+ * row back by the inverse map in fp64.  In fp32 every step is one
  * IEEE operation: the complex product is (d_re w_re - d_im w_im, d_re w_im
  * + d_im w_re), each product rounded, then the sum; twiddles are the
  * correctly rounded fp32 values of cos and -sin of 2 pi t / N.
@@ -252,6 +254,32 @@ void oracle_srft_f64(double *y, const float *signs, int D, double c)
         y[i] = y[i] * c;
 }
 
+/* The inverse of oracle_srft_f64 in fp64: y <- s (.) (c * U(y)), where U
+ * undoes the stages in reverse order (half-size 1, 2, ..., N/2): a stage's
+ * pair (a', b') = (a + b, (a - b) W^t) gives back 2a = a' + b' conj(W^t) and
+ * 2b = a' - b' conj(W^t), and the log2(N) factors of 2 together with the
+ * forward c make the final factor c again (c = 1/sqrt(N)). */
+void oracle_unsrft_f64(double *y, const float *signs, int D, double c)
+{
+    const int N = D / 2;
+    for (int h = 1; h < N; h *= 2)
+        for (int blk = 0; blk < N; blk += 2 * h)
+            for (int j = blk; j < blk + h; ++j) {
+                double xr = y[2 * j], xi = y[2 * j + 1];
+                double br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
+                double wr, wi;
+                twiddle((j - blk) * (N / (2 * h)), N, &wr, &wi);
+                /* t = b' conj(W) */
+                double tr = br * wr + bi * wi, ti = bi * wr - br * wi;
+                y[2 * j] = xr + tr;
+                y[2 * j + 1] = xi + ti;
+                y[2 * (j + h)] = xr - tr;
+                y[2 * (j + h) + 1] = xi - ti;
+            }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c * (double)signs[i];
+}
+
 /* K's rotation by kind: 0 = SRHT, 1 = SRFT. */
 static void rotate_f32(float *y, const float *signs, int D, float c, int kind)
 {
@@ -267,6 +295,14 @@ static void rotate_f64(double *y, const float *signs, int D, double c, int kind)
         oracle_srft_f64(y, signs, D, c);
     else
         oracle_srht_f64(y, signs, D, c);
+}
+
+static void unrotate_f64(double *y, const float *signs, int D, double c, int kind)
+{
+    if (kind == 1)
+        oracle_unsrft_f64(y, signs, D, c);
+    else
+        oracle_unrotate_f64(y, signs, D, c);
 }
 
 /* ---------------------------------------------------------------- quantise */
@@ -387,11 +423,11 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
  *              per-channel scale is given
  *   S_t      = scale_attn * sum_i q'_i K^[t][i]
  *   w_t      = exp(S_t - max_u S_u)
- *   V^[t][i] = code * scale, brought back to the original basis
- *              (oracle_unrotate_f64) when v_signs != NULL
+ *   V^[t][i] = code * scale, brought back to the original basis (the
+ *              inverse rotation of kind rot_kind) when v_signs != NULL
  *   out      = sum_t w_t V^[t] / sum_t w_t
  * T == 0 gives out = 0.  q' is q rotated in fp64 when signs != NULL (rot_kind
- * 0 = SRHT, 1 = SRFT).
+ * 0 = SRHT, 1 = SRFT; the same kind serves V).
  * work must hold T doubles. */
 void oracle_attend_row(const uint16_t *q, int dtype, int D,
                        const uint8_t *kc, const float *ks,
@@ -436,7 +472,7 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
         for (int i = 0; i < D; ++i)
             vd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
         if (v_signs)
-            oracle_unrotate_f64(vd, v_signs, D, (double)rot_norm);
+            unrotate_f64(vd, v_signs, D, (double)rot_norm, rot_kind);
         for (int i = 0; i < D; ++i)
             out[i] += w * vd[i];
     }

@@ -263,3 +263,64 @@ def test_sdpa_srft_query_matches_torch():
         qt.unsqueeze(2), kd.repeat_interleave(G, 1), vd.repeat_interleave(G, 1),
         scale=scale).squeeze(2)
     assert np.allclose(got, ref.numpy(), rtol=0, atol=1e-10)
+
+
+# -------------------------------------------------------------- rotated V
+
+@pytest.mark.parametrize("D", [8, 64, 128, 256])
+def test_unsrft_inverts_srft_and_matches_numpy_ifft(D):
+    rng = np.random.default_rng(41 + D)
+    s = _signs(D, 43 + D)
+    c = 1.0 / math.sqrt(D // 2)
+    x = rng.standard_normal(D)
+    assert np.allclose(oracle.unsrft_f64(oracle.srft_f64(x, s, c), s, c), x, rtol=0, atol=1e-12)
+    # the inverse of y: undo the bit-reversed order, inverse DFT (numpy), signs
+    N = D // 2
+    bits = N.bit_length() - 1
+    y = rng.standard_normal(D)
+    Z = np.empty(N, complex)
+    for k in range(N):
+        Z[_bitrev(k, bits)] = y[2 * k] + 1j * y[2 * k + 1]
+    z = np.fft.ifft(Z) * math.sqrt(N)
+    want = np.empty(D)
+    want[0::2], want[1::2] = z.real, z.imag
+    assert np.allclose(oracle.unsrft_f64(y, s, c), want * s, rtol=0, atol=1e-12)
+
+
+def test_sdpa_srft_rotated_v_matches_torch():
+    """V quantised after the SRFT rotation (its own signs): attention equals
+    torch's fp64 SDPA with every dequantised V row brought back by numpy's
+    inverse FFT; K rotated by SRFT as well."""
+    rng = np.random.default_rng(19)
+    B, Hq, Hkv, D, T = 1, 4, 2, 64, 50
+    k = torch.from_numpy(rng.standard_normal((B, Hkv, T, D)).astype(np.float32)).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((B, Hkv, T, D)).astype(np.float32)).to(torch.bfloat16)
+    q = torch.from_numpy(rng.standard_normal((B, Hq, D)).astype(np.float32)).to(torch.bfloat16)
+    s, sv = _signs(D, 51), _signs(D, 52)
+    N = D // 2
+    bits = N.bit_length() - 1
+    c = np.float32(1.0 / math.sqrt(N))
+    u16 = lambda t: t.contiguous().view(torch.int16).numpy().view(np.uint16)
+    kc, ks = oracle.quantize(u16(k), "bf16", signs=s, rot_norm=c, rot_kind="srft")
+    vc, vs = oracle.quantize(u16(v), "bf16", signs=sv, rot_norm=c, rot_kind="srft")
+    lens = np.array([T], np.int32)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.sdpa(u16(q), "bf16", kc, ks, vc, vs, lens, scale, signs=s, rot_norm=c,
+                      v_signs=sv, rot_kind="srft")
+    kd = torch.from_numpy(oracle.dequantize(kc, ks))
+    vr = oracle.dequantize(vc, vs)  # rotated basis
+    Z = np.empty(vr.shape[:-1] + (N,), complex)
+    for kk in range(N):
+        Z[..., _bitrev(kk, bits)] = vr[..., 2 * kk] + 1j * vr[..., 2 * kk + 1]
+    z = np.fft.ifft(Z, axis=-1) * N * float(c)
+    vb = np.empty(vr.shape)
+    vb[..., 0::2], vb[..., 1::2] = z.real, z.imag
+    vd = torch.from_numpy(vb * sv.astype(np.float64))
+    qn = q.double().numpy()
+    qt = torch.from_numpy(np.stack([[_numpy_srft(qn[b, h], s) * (float(c) * math.sqrt(N))
+                                     for h in range(Hq)] for b in range(B)]))
+    G = Hq // Hkv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        qt.unsqueeze(2), kd.repeat_interleave(G, 1), vd.repeat_interleave(G, 1),
+        scale=scale).squeeze(2)
+    assert np.allclose(got, ref.numpy(), rtol=0, atol=1e-10)

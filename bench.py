@@ -185,8 +185,6 @@ def main():
     rot_kind = "srft" if args.srft else "srht"
     if args.srft and args.srht:
         sys.exit("bench.py: --srft and --srht name two different K rotations")
-    if args.srft and args.v_rotate:
-        sys.exit("bench.py: a rotated V goes with the Walsh-Hadamard K rotation only (--srft excludes --v-rotate)")
     t_setup = time.time()
     caches, k_new, v_new, qs, lens_l, pos_l = [], [], [], [], [], []
     host_kv0 = None
@@ -387,7 +385,8 @@ def main():
         t = time.time()
         kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
                                  chan_scale=lam0, rot_kind=rot_kind)
-        vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads)
+        vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads,
+                                 rot_kind=rot_kind)
         log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
         lens0 = synth.lens(w, 0)
         q0 = synth.bits(qs[0])

@@ -54,7 +54,8 @@ typedef enum otq_status {
 
 typedef enum otq_dtype { OTQ_F16 = 0, OTQ_BF16 = 1 } otq_dtype;
 
-/* K's rotation when k_rot_signs != NULL (otq_cache.k_rot_kind). */
+/* The kind of the cache's rotations (otq_cache.rot_kind): K's when
+ * k_rot_signs != NULL, V's when v_rot_signs != NULL. */
 typedef enum otq_rot_kind {
     OTQ_ROT_SRHT = 0, /* sign-randomised Walsh-Hadamard transform */
     OTQ_ROT_SRFT = 1  /* sign-randomised FFT                      */
@@ -72,8 +73,8 @@ typedef enum otq_rot_kind {
  *     y = rot_norm * H (k_rot_signs (.) x)
  * with H the Sylvester-ordered Walsh-Hadamard matrix, evaluated as in-place
  * butterflies (a + b, a - b) in ascending stride order, then one multiply by
- * rot_norm (pass fp32(1/sqrt(head_dim))).  That is k_rot_kind = OTQ_ROT_SRHT.
- * With k_rot_kind = OTQ_ROT_SRFT ("SRFT + int4 KV-cache" page, core-method
+ * rot_norm (pass fp32(1/sqrt(head_dim))).  That is rot_kind = OTQ_ROT_SRHT.
+ * With rot_kind = OTQ_ROT_SRFT ("SRFT + int4 KV-cache" page, core-method
  * section: a sign-randomised FFT in place of the Hadamard rotation) the D
  * reals are instead D/2 complex numbers z_j = (x_2j, x_2j+1), signs applied
  * to the reals first, transformed by the radix-2 decimation-in-frequency FFT
@@ -92,12 +93,13 @@ typedef enum otq_rot_kind {
  *     z_i = x_i * k_chan_scale[i]      (one fp32 multiply)
  * and attention reads K^_i = code_i * s_g / k_chan_scale[i]: the query is
  * divided by the scale inside otq_sdpa_int4_decode.
- * V, when v_rot_signs != NULL, is rotated before quantisation by the
- * Hadamard form above (its own signs, the same rot_norm), and the attention
- * output is brought back to the original basis, out <- v_rot_signs (.)
- * (rot_norm * H out), the inverse of that rotation (rot_norm =
- * fp32(1/sqrt(head_dim))).  A rotated V needs k_rot_kind = OTQ_ROT_SRHT
- * (or no K rotation): OTQ_EUNSUPPORTED otherwise.
+ * V, when v_rot_signs != NULL, is rotated before quantisation exactly as K
+ * would be (its own signs, the same rot_kind and rot_norm), and the
+ * attention output is brought back to the original basis by the inverse of
+ * that rotation: out <- v_rot_signs (.) (rot_norm * H out) for the Hadamard
+ * kind; for the FFT kind the stages undone in reverse order (half-size 1,
+ * 2, ..., N/2; a pair (a', b') becomes (a' + b' conj(W^t), a' - b'
+ * conj(W^t))), then rot_norm and the signs.
  *
  * Layouts (B = batch, H = num_kv_heads, D = head_dim, C = capacity):
  *  Codes are two's-complement int4 nibbles; a byte holds an even channel in
@@ -128,10 +130,11 @@ typedef struct otq_cache {
     uint8_t *v_codes;
     float *v_scales;
     const float *k_rot_signs; /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
-    float rot_norm;           /* used only when k_rot_signs != NULL */
+    float rot_norm;           /* used only when k_rot_signs or v_rot_signs != NULL */
     const float *k_chan_scale; /* device [D] fp32 lambda, finite and > 0, 16-byte aligned, or NULL */
     const float *v_rot_signs;  /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
-    int32_t k_rot_kind;        /* otq_rot_kind; read only when k_rot_signs != NULL */
+    int32_t rot_kind;          /* otq_rot_kind of both rotations; read only when
+                                  k_rot_signs or v_rot_signs != NULL */
 } otq_cache;
 
 /* Human-readable name of a status code (static string). */

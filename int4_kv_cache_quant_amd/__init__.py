@@ -48,7 +48,7 @@ class otq_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_rot_signs", ctypes.c_void_p), ("rot_norm", ctypes.c_float),
         ("k_chan_scale", ctypes.c_void_p), ("v_rot_signs", ctypes.c_void_p),
-        ("k_rot_kind", ctypes.c_int32),
+        ("rot_kind", ctypes.c_int32),
     ]
 
 
@@ -239,7 +239,7 @@ class Int4KVCache:
     ``rot_signs`` (device float32 [D] of +-1) turns on the K rotation:
     ``rot_kind`` "srht" (Walsh-Hadamard, normalisation fp32(1/sqrt(D))) or
     "srft" (FFT over the (even, odd) complex pairs, normalisation
-    fp32(1/sqrt(D/2))).  ``chan_scale`` (float32 [D], > 0)
+    fp32(1/sqrt(D/2))), the kind of V's rotation too.  ``chan_scale`` (float32 [D], > 0)
     turns on K's per-channel scale, applied after the rotation.
     ``v_rot_signs`` (float32 [D] of +-1) turns on V's rotation, whose inverse
     the attention calls apply to their outputs.

@@ -41,16 +41,16 @@ int check_cache(const otq_cache* c)
     if ((((uintptr_t)c->k_rot_signs) & 15) != 0 || (((uintptr_t)c->k_chan_scale) & 15) != 0 ||
         (((uintptr_t)c->v_rot_signs) & 15) != 0)
         return OTQ_EINVAL;
-    if (c->k_rot_signs) {
-        if (c->k_rot_kind != OTQ_ROT_SRHT && c->k_rot_kind != OTQ_ROT_SRFT) return OTQ_EINVAL;
-        // V's rotation is the Hadamard one and shares K's normalisation
-        if (c->k_rot_kind == OTQ_ROT_SRFT && c->v_rot_signs) return OTQ_EUNSUPPORTED;
-    }
+    if ((c->k_rot_signs || c->v_rot_signs) && c->rot_kind != OTQ_ROT_SRHT && c->rot_kind != OTQ_ROT_SRFT)
+        return OTQ_EINVAL;
     return OTQ_OK;
 }
 
-// K's rotation kind as the kernels take it (checked by check_cache).
-int rot_kind(const otq_cache* c) { return c->k_rot_signs && c->k_rot_kind == OTQ_ROT_SRFT ? 1 : 0; }
+// The rotations' kind as the kernels take it (checked by check_cache).
+int rot_kind(const otq_cache* c)
+{
+    return (c->k_rot_signs || c->v_rot_signs) && c->rot_kind == OTQ_ROT_SRFT ? 1 : 0;
+}
 
 // Batches whose split blocks take their items longest first (one sequence
 // needs no order: its chunks are equal but the last).

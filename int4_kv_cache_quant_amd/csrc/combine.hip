@@ -112,6 +112,9 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
     [[maybe_unused]] SrftThreadTw<(DA > 0 ? DA : 64)> stw;  // the FFT rotation's twiddles
+    if constexpr (ROT || VROT) {
+        if (a.rot_kind) stw.load(tid);
+    }
     if constexpr (APPEND) {
         const int G = a.Hq / a.H, h = row % a.Hq;
         kvh = h / G;
@@ -121,7 +124,6 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         vx = a.v_new[src];
         qx = static_cast<const uint16_t*>(a.q)[(size_t)row * DA + ch];
         if (ROT) sg = a.signs[ch];
-        if (ROT && a.rot_kind) stw.load(tid);
         if (LAM) lm = a.lam[ch];  // K's channel scale
         if (VROT) vsg = a.vsigns[ch];
         // one block per KV head writes the token: the first query head's,
@@ -206,7 +208,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float xv[1] = {widen(vx, a.dtype)};
         if (VROT) {  // V rotated as K is, with its own signs
             xv[0] = xv[0] * vsg;
-            xv[0] = fwht_thread<DA>(xv[0], xch);
+            xv[0] = a.rot_kind ? srft_thread<DA>(xv[0], xch, stw) : fwht_thread<DA>(xv[0], xch);
             xv[0] = xv[0] * a.rot_norm;
         }
         int cv[1];
@@ -296,10 +298,10 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             *dst = make_float4(r.x / L, r.y / L, r.z / L, r.w / L);
         }
     }
-    if constexpr (VROT) {  // back to the original basis: s_v (.) (rot_norm * H row)
+    if constexpr (VROT) {  // back to the original basis: s_v (.) (rot_norm * inverse(row))
         __syncthreads();
         float y = tid < DT ? orow[tid] : 0.0f;
-        y = fwht_thread<DT>(y, xch);
+        y = a.rot_kind ? isrft_thread<DT>(y, xch, stw) : fwht_thread<DT>(y, xch);
         if (tid < DT) a.out[(size_t)row * DT + tid] = y * a.rot_norm * a.vsigns[tid];
     }
 }

@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     }
 
     SrftLaneTw<D, E> stw;  // the FFT rotation's twiddles of this lane
-    if (signs && rot_kind) stw.load(lane);
+    if ((signs || vsigns) && rot_kind) stw.load(lane);
 
     int vcode[2][E];
 #pragma unroll
@@ -131,7 +131,15 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
         // V: widen, quantise, store scales; nibbles are stored per pair below
 #pragma unroll
         for (int e = 0; e < E; ++e) x[e] = widen(v[src + e], dtype);
-        if (vsigns) rotate_lane<D>(x, vsigns, rot_norm, lane);
+        if (vsigns) {
+            if (rot_kind) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = x[e] * vsigns[lane * E + e];
+                srft_signed<D, E>(x, rot_norm, lane, stw);
+            } else {
+                rotate_lane<D>(x, vsigns, rot_norm, lane);
+            }
+        }
         float sv = quantize_lane<D>(x, vcode[s], lane);
         if (lane % (kGroup / E) == 0) vs[row * NG + (lane * E) / kGroup] = sv;
     }
@@ -293,7 +301,10 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
             widen8(vraw[i], x);
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = x[e] * vsg[e];
-            rotate_signed<D, 8>(x, rot_norm, j);
+            if constexpr (SRFT)
+                srft_signed<D, 8>(x, rot_norm, j, stw);
+            else
+                rotate_signed<D, 8>(x, rot_norm, j);
             float sv;
             vstage[u * LT + j] = quantize_word8(x, sv);
             if (fresh_at(t) && (j & 3) == 0) vs[(head * cap + t) * NG + (j >> 2)] = sv;
@@ -372,7 +383,7 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         dim3 grid((pair_slots + 3) / 4, H, B), block(256);
         auto kern = D == 64 ? quantize_pair_kernel<64> : D == 128 ? quantize_pair_kernel<128> : quantize_pair_kernel<256>;
         kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm,
-                                         signs ? rot_kind : 0, lam, vsigns, pos, pair_slots);
+                                         (signs || vsigns) ? rot_kind : 0, lam, vsigns, pos, pair_slots);
     } else {
         // one block per tile touched: the range may start inside a tile
         const int tiles = (n_new + 2 * kTile - 2) / kTile;
@@ -381,7 +392,8 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
                            const float*, float, const float*, const float*, const int32_t*);
         auto pick = [&](auto d) -> K {
             constexpr int DD = decltype(d)::value;
-            // a rotated V goes with the Hadamard K rotation only (checked by the caller)
+            if (vsigns && rot_kind)
+                return dtype == 0 ? quantize_tile_kernel<DD, 0, true, true> : quantize_tile_kernel<DD, 1, true, true>;
             if (vsigns)
                 return dtype == 0 ? quantize_tile_kernel<DD, 0, true, false> : quantize_tile_kernel<DD, 1, true, false>;
             if (signs && rot_kind)

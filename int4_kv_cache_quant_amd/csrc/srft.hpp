@@ -254,4 +254,38 @@ __device__ __forceinline__ float srft_thread(float y, float* xch, const SrftThre
     return y;
 }
 
+// The inverse transform over one real per thread, without the final
+// rot_norm and signs: the stages undone in reverse order (half-size 1, 2,
+// ..., N/2), a pair (a', b') becoming (a' + b' conj(W), a' - b' conj(W)).
+// The upper element forms b' conj(W) and hands it to the lower one, which
+// hands back a'.
+template <int D>
+__device__ __forceinline__ float isrft_thread(float y, float* xch, const SrftThreadTw<D>& tw)
+{
+#pragma clang fp contract(off)
+    constexpr int N = D / 2;
+    const int t = threadIdx.x, j = t >> 1;
+    const bool im = (t & 1) != 0;
+#pragma unroll
+    for (int s = SrftThreadTw<D>::S - 1; s >= 0; --s) {
+        const int h = (N / 2) >> s;
+        const bool upper = (j & h) != 0;
+        const float yd = shfl_xor(y, 1);  // the other component of the element's number
+        const float wr = tw.w[s].re, wi = tw.w[s].im;
+        const float prod = im ? y * wr - yd * wi : y * wr + yd * wi;
+        const float send = upper ? prod : y;
+        float o;
+        if (2 * h < 64) {
+            o = shfl_xor(send, 2 * h);
+        } else {
+            __syncthreads();
+            if (t < D) xch[t] = send;
+            __syncthreads();
+            o = t < D ? xch[t ^ (2 * h)] : send;
+        }
+        y = upper ? o - prod : y + o;
+    }
+    return y;
+}
+
 }  // namespace otq

@@ -53,7 +53,7 @@ def oracle_cache(k, v, dtype, signs=None, rot_norm=0.0, threads=8, chan_scale=No
     kb, vb = to_bits(k), to_bits(v)
     kc, ks = oracle.quantize(kb, dtype, signs=signs, rot_norm=rot_norm, threads=threads,
                              chan_scale=chan_scale, rot_kind=rot_kind)
-    vc, vs = oracle.quantize(vb, dtype, signs=v_signs, rot_norm=rot_norm, threads=threads)
+    vc, vs = oracle.quantize(vb, dtype, signs=v_signs, rot_norm=rot_norm, threads=threads, rot_kind=rot_kind)
     return kc, ks, vc, vs
 
 

@@ -88,27 +88,24 @@ def test_quantize_append_host_errors():
 
 
 def test_rotation_kind_host_checks():
-    """K's rotation kind is read only with signs; it must be SRHT or SRFT,
-    and a rotated V goes with the Hadamard kind only."""
+    """The rotations' kind is read only with K or V signs, and must be SRHT or
+    SRFT; either kind serves K and V."""
     lib = otq.lib()
     P = ctypes.c_void_p
     call = lambda desc: lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, ctypes.byref(desc), P(FAKE), None)
     plan = lambda desc: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, 0, ctypes.byref(otq.otq_plan()))
     d = _desc()
-    d.k_rot_kind = 7                      # ignored without signs
+    d.rot_kind = 7                        # ignored without signs
     assert plan(d) == otq.OTQ_OK
-    d = _desc(signs=FAKE)
-    for kind, want in ((otq.OTQ_ROT_SRHT, otq.OTQ_OK), (otq.OTQ_ROT_SRFT, otq.OTQ_OK), (2, otq.OTQ_EINVAL),
-                       (-1, otq.OTQ_EINVAL)):
-        d.k_rot_kind = kind
-        assert plan(d) == want, kind
-        if want != otq.OTQ_OK:
-            assert call(d) == want
-    d.k_rot_kind = otq.OTQ_ROT_SRFT
-    d.v_rot_signs = FAKE
-    assert plan(d) == otq.OTQ_EUNSUPPORTED and call(d) == otq.OTQ_EUNSUPPORTED
-    d.k_rot_kind = otq.OTQ_ROT_SRHT
-    assert plan(d) == otq.OTQ_OK
+    for k_signs, v_signs in ((FAKE, None), (None, FAKE), (FAKE, FAKE)):
+        d = _desc(signs=k_signs)
+        d.v_rot_signs = v_signs
+        for kind, want in ((otq.OTQ_ROT_SRHT, otq.OTQ_OK), (otq.OTQ_ROT_SRFT, otq.OTQ_OK), (2, otq.OTQ_EINVAL),
+                           (-1, otq.OTQ_EINVAL)):
+            d.rot_kind = kind
+            assert plan(d) == want, (k_signs, v_signs, kind)
+            if want != otq.OTQ_OK:
+                assert call(d) == want
 
 
 def test_plan_batch_order_table():

@@ -134,11 +134,14 @@ def test_fused_append_v_rotated(D, G, rotate, scaled):
 
 @pytest.mark.parametrize("D", [64, 128, 256])
 @pytest.mark.parametrize("G", [1, 8])
-@pytest.mark.parametrize("scaled", [False, True])
-def test_fused_append_srft(D, G, scaled):
+@pytest.mark.parametrize("scaled,rotate_v", [(False, False), (True, False), (False, True), (True, True)])
+def test_fused_append_srft(D, G, scaled, rotate_v):
     """K rotated by the sign-randomised FFT: the combine rotates the new
-    token's K (to the bulk kernel's bytes) and the query for its score."""
-    _run(2, G, 2, D, 384, [351, 190], rotate="srft", chunk=128, seed=13 * D + G + scaled, scaled=scaled)
+    token's K (to the bulk kernel's bytes) and the query for its score; with
+    V rotated by the same kind it also rotates the new V and brings the output
+    row back by the inverse transform."""
+    _run(2, G, 2, D, 384, [351, 190], rotate="srft", chunk=128, seed=13 * D + G + scaled + 2 * rotate_v,
+         scaled=scaled, rotate_v=rotate_v)
 
 
 @pytest.mark.parametrize("lens", [[1, 2], [129, 128], [257, 33], [32, 31]])

@@ -163,6 +163,28 @@ def test_quantize_srft_bit_exact(D, dtype, scaled, chunk):
     assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
 
 
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("rotate_k", [False, True])
+def test_quantize_srft_v_rotated_bit_exact(D, dtype, rotate_k):
+    """V rotated by the sign-randomised FFT (its own signs), K too or not:
+    chunks of 19 (the bulk kernel's rotated-V form, whole and edge tiles) and
+    a last single token."""
+    B, H, T, cap = 2, 3, 77, 96
+    say(f"quantize srft v-rotated D={D} dtype={dtype} rotate_k={rotate_k}")
+    k, v = _rand_kv(B, H, T, D, dtype, seed=D + 17 * rotate_k + 9, outliers=(3, 17))
+    ks = rand_signs(D, D + 71) if rotate_k else None
+    vs = rand_signs(D, D + 73)
+    cache = build_cache(k, v, cap, signs=None if ks is None else ks.to(DEV), prefill_chunk=19,
+                        v_signs=vs.to(DEV), rot_kind="srft")
+    torch.cuda.synchronize()
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    ref = oracle_cache(k.cpu(), v.cpu(), name, None if ks is None else ks.numpy(), rot_norm32(D, "srft"),
+                       v_signs=vs.numpy(), rot_kind="srft")
+    bad = compare_codes(host_cache(cache), ref, T)
+    assert bad == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}, bad
+
+
 @pytest.mark.parametrize("D", [64, 256])
 def test_quantize_srft_exponent_ranges(D):
     """FFT-rotated bf16 vectors scaled across the exponent range: twiddle

@@ -139,13 +139,14 @@ def test_sdpa_v_rotated(variant, G, D, rotate, scaled):
 @pytest.mark.parametrize("variant,G,D", [(VEC, 1, 64), (VEC, 2, 256), (VEC, 4, 128), (MF, 1, 256),
                                          (MF, 2, 256), (MF, 4, 64), (MF, 8, 128), (MF, 16, 128),
                                          (MF, 8, 64)])
-@pytest.mark.parametrize("scaled", [False, True])
-def test_sdpa_srft(variant, G, D, scaled):
+@pytest.mark.parametrize("scaled,rotate_v", [(False, False), (True, False), (False, True), (True, True)])
+def test_sdpa_srft(variant, G, D, scaled, rotate_v):
     """K rotated by the sign-randomised FFT: the split kernels rotate the
     query the same way (then divide it by K's channel scale if scaled); one
-    and two KV heads per MFMA wave, every head width."""
-    got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 77], seed=71 + G + D + scaled, rotate="srft",
-                       chunk=128, variant=variant, scaled=scaled)
+    and two KV heads per MFMA wave, every head width; V rotated by the same
+    kind or not (its output brought back by the inverse transform)."""
+    got, ref, _ = _run(2, 2 * G, 2, D, 192, [192, 77], seed=71 + G + D + scaled + 2 * rotate_v,
+                       rotate="srft", chunk=128, variant=variant, scaled=scaled, rotate_v=rotate_v)
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
@@ -257,7 +258,7 @@ def _full(cfg, rows_per_seq=None, layer=0, options=False, srft=False):
     lens = synth.lens(w, layer)
     signs = torch.from_numpy(synth.rot_signs(w, layer)).to(DEV) if (w.rotate or srft) else None
     lam = synth.chan_scale(w, layer) if options else None
-    vsg = synth.v_rot_signs(w, layer) if (options and not srft) else None
+    vsg = synth.v_rot_signs(w, layer) if options else None
     cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs,
                             chan_scale=None if lam is None else torch.from_numpy(lam),
                             v_rot_signs=None if vsg is None else torch.from_numpy(vsg), rot_kind=kind)
@@ -324,5 +325,6 @@ def test_full_workload_with_options(cfg, rows_per_seq):
 @pytest.mark.parametrize("cfg,rows_per_seq,options", [(3, 8, False), (4, 8, True), (5, 2, False)])
 def test_full_workload_srft(cfg, rows_per_seq, options):
     """The full workloads with K rotated by the sign-randomised FFT (workload
-    5 switches from the Hadamard rotation to it)."""
+    5 switches from the Hadamard rotation to it); workload 4 with K's channel
+    scale and V rotated by the same kind."""
     _full(cfg, rows_per_seq=rows_per_seq, options=options, srft=True)

@@ -23,6 +23,9 @@ DEV = "cuda"
 
 
 def _setup(B, G, Hkv, D, cap, lens, extras, seed):
+    """extras: False, True (K rotated and scaled, V rotated: the Hadamard
+    kind) or "srft" (the same with the FFT kind)."""
+    kind = "srft" if extras == "srft" else "srht"
     g = torch.Generator().manual_seed(seed)
     k = torch.randn((B, Hkv, cap, D), generator=g)
     v = torch.randn((B, Hkv, cap, D), generator=g)
@@ -36,16 +39,17 @@ def _setup(B, G, Hkv, D, cap, lens, extras, seed):
     cache = build_cache(k[:, :, :T].to(DEV).contiguous(), v[:, :, :T].to(DEV).contiguous(), cap,
                         signs=None if sk is None else sk.to(DEV), append_last=False,
                         chan_scale=None if lam is None else lam.to(DEV),
-                        v_signs=None if sv is None else sv.to(DEV))
-    return k, v, q, sk, lam, sv, cache
+                        v_signs=None if sv is None else sv.to(DEV), rot_kind=kind)
+    return k, v, q, sk, lam, sv, cache, kind
 
 
 @pytest.mark.parametrize("B,lens,extras", [(1, [700], False), (3, [700, 129, 333], False),
-                                          (3, [700, 129, 333], True)])
+                                          (3, [700, 129, 333], True), (3, [700, 129, 333], "srft")])
 def test_graph_replays_match_eager(B, lens, extras):
     G, Hkv, D, cap = 8, 2, 128, 768
     say(f"graph B={B} lens={lens} extras={extras}")
-    k, v, q, sk, lam, sv, cache = _setup(B, G, Hkv, D, cap, lens, extras, seed=B + 10 * extras)
+    seed = B + {False: 0, True: 10, "srft": 20}[extras]
+    k, v, q, sk, lam, sv, cache, kind = _setup(B, G, Hkv, D, cap, lens, extras, seed=seed)
     Hq = G * Hkv
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     idx = (lens_t.long() - 1).clamp(min=0)
@@ -83,23 +87,24 @@ def test_graph_replays_match_eager(B, lens, extras):
         assert torch.isfinite(junk)
     # and the eager result against the oracle
     name = "bf16"
-    kc, ks, vc, vs = oracle_cache(k, v, name, None if sk is None else sk.numpy(), rot_norm32(D),
+    kc, ks, vc, vs = oracle_cache(k, v, name, None if sk is None else sk.numpy(), rot_norm32(D, kind),
                                   chan_scale=None if lam is None else lam.numpy(),
-                                  v_signs=None if sv is None else sv.numpy())
+                                  v_signs=None if sv is None else sv.numpy(), rot_kind=kind)
     ref = oracle.sdpa(to_bits(q), name, kc, ks, vc, vs, np.array(lens, np.int32), 0.09,
-                      signs=None if sk is None else sk.numpy(), rot_norm=rot_norm32(D), threads=8,
+                      signs=None if sk is None else sk.numpy(), rot_norm=rot_norm32(D, kind), threads=8,
                       chan_scale=None if lam is None else lam.numpy(),
-                      v_signs=None if sv is None else sv.numpy())
+                      v_signs=None if sv is None else sv.numpy(), rot_kind=kind)
     ma, rel = errors(out_e.cpu().numpy(), ref)
     assert ma <= MAX_ABS and rel <= REL_L2
 
 
-@pytest.mark.parametrize("extras", [False, True])
+@pytest.mark.parametrize("extras", [False, True, "srft"])
 @pytest.mark.parametrize("variant", [otq.OTQ_VARIANT_VECTOR, otq.OTQ_VARIANT_MFMA])
 def test_two_phase_equals_single_call(extras, variant):
     B, G, Hkv, D, cap, lens = 2, 2, 2, 128, 512, [500, 77]
     say(f"two-phase variant={variant} extras={extras}")
-    k, v, q, sk, lam, sv, cache = _setup(B, G, Hkv, D, cap, lens, extras, seed=20 + extras)
+    seed = 20 + {False: 0, True: 1, "srft": 2}[extras]
+    k, v, q, sk, lam, sv, cache, kind = _setup(B, G, Hkv, D, cap, lens, extras, seed=seed)
     Hq = G * Hkv
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     qd = q.to(DEV)

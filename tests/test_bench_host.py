@@ -1,5 +1,5 @@
-"""CPU tests of bench.py's host logic: the single-GPU guard, the option
-checks, and the calibration of rocprofv3 counter runs into HBM bytes."""
+"""CPU tests of bench.py's host logic: the single-GPU guard and the
+calibration of rocprofv3 counter runs into HBM bytes."""
 import csv
 import importlib.util
 import json
@@ -7,7 +7,6 @@ import os
 import subprocess
 import sys
 
-import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))

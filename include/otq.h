@@ -168,8 +168,9 @@ size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
  *         [0, capacity) are skipped (never written out of bounds).
  *  Codes and scales of every token not in the range are left untouched,
  *  including the neighbour that shares a V byte with a new token.
- *  Host errors: OTQ_EINVAL (null pointer, misaligned k or v, n_new < 1,
- *  bad dtype), OTQ_EUNSUPPORTED (head_dim), OTQ_ECAPACITY (n_new > capacity).
+ *  Host errors: OTQ_EINVAL (null pointer, misaligned k or v, n_new < 1, a
+ *  misaligned per-channel vector or an unknown rot_kind in the descriptor),
+ *  OTQ_EUNSUPPORTED (head_dim, dtype), OTQ_ECAPACITY (n_new > capacity).
  */
 int otq_quantize_append(const void *k, const void *v, int32_t dtype, int32_t n_new,
                         const otq_cache *cache, const int32_t *pos, void *stream);

@@ -51,17 +51,20 @@ def _load():
     lib.oracle_twiddle_f32.restype = None
     lib.oracle_quantize_vector.argtypes = [P, ctypes.c_int, P, P]
     lib.oracle_quantize_vector.restype = None
+    lib.oracle_quantize_vector_bits.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P]
+    lib.oracle_quantize_vector_bits.restype = None
     lib.oracle_quantize_rows.argtypes = [P, ctypes.c_int, ctypes.c_long, ctypes.c_int,
-                                         P, ctypes.c_float, ctypes.c_int, P, P, P, ctypes.c_int]
+                                         P, ctypes.c_float, ctypes.c_int, P, ctypes.c_int, P, P,
+                                         ctypes.c_int]
     lib.oracle_quantize_rows.restype = ctypes.c_int
     lib.oracle_attend_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P, P, P, P,
                                       ctypes.c_long, ctypes.c_double, P, ctypes.c_float,
-                                      ctypes.c_int, P, P, P, P]
+                                      ctypes.c_int, P, P, ctypes.c_int, P, P]
     lib.oracle_attend_row.restype = None
     lib.oracle_sdpa.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                 ctypes.c_int, ctypes.c_long, P, P, P, P, P,
-                                ctypes.c_double, P, ctypes.c_float, ctypes.c_int, P, P, P,
-                                ctypes.c_long, P, ctypes.c_int]
+                                ctypes.c_double, P, ctypes.c_float, ctypes.c_int, P, P,
+                                ctypes.c_int, P, ctypes.c_long, P, ctypes.c_int]
     lib.oracle_sdpa.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -163,30 +166,42 @@ def quantize_vector(x):
     return codes, scales
 
 
-def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None, rot_kind="srht"):
-    """[..., D] 16-bit rows -> codes [..., D/2], scales [..., D/32].
+def quantize_vector_bits(x, nbits):
+    """One fp32 vector -> (b-bit codes uint8[D b / 8], scales float32[D/32])."""
+    lib = _load()
+    x = _c(x, np.float32)
+    D = x.shape[-1]
+    codes = np.zeros(D * nbits // 8, np.uint8)
+    scales = np.zeros(D // 32, np.float32)
+    lib.oracle_quantize_vector_bits(_ptr(x), D, int(nbits), _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def quantize(bits, dtype, signs=None, rot_norm=0.0, threads=1, chan_scale=None, rot_kind="srht",
+             code_bits=4):
+    """[..., D] 16-bit rows -> codes [..., D code_bits / 8], scales [..., D/32].
 
     rot_kind: "srht" or "srft", the rotation applied when signs is given;
     chan_scale: per-channel scale lambda [D] applied after the rotation
-    (the cache then holds lambda (.) y), or None."""
+    (the cache then holds lambda (.) y), or None; code_bits: 4, 3 or 2."""
     lib = _load()
     bits = _c(bits, np.uint16)
     D = bits.shape[-1]
     N = bits.size // D
-    codes = np.zeros(bits.shape[:-1] + (D // 2,), np.uint8)
+    codes = np.zeros(bits.shape[:-1] + (D * code_bits // 8,), np.uint8)
     scales = np.zeros(bits.shape[:-1] + (D // 32,), np.float32)
     s = None if signs is None else _c(signs, np.float32)
     lam = None if chan_scale is None else _c(chan_scale, np.float32)
     rc = lib.oracle_quantize_rows(_ptr(bits), DTYPES[dtype], N, D, _ptr(s),
-                                  float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(codes),
-                                  _ptr(scales), int(threads))
+                                  float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), int(code_bits),
+                                  _ptr(codes), _ptr(scales), int(threads))
     if rc != 0:
         raise ValueError("oracle_quantize_rows rejected its arguments")
     return codes, scales
 
 
 def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0, chan_scale=None,
-               v_signs=None, rot_kind="srht"):
+               v_signs=None, rot_kind="srht", code_bits=4):
     lib = _load()
     q_bits = _c(q_bits, np.uint16)
     D = q_bits.shape[-1]
@@ -200,16 +215,16 @@ def attend_row(q_bits, dtype, kc, ks, vc, vs, T, scale, signs=None, rot_norm=0.0
     lib.oracle_attend_row(_ptr(q_bits), DTYPES[dtype], D, _ptr(kc), _ptr(ks), _ptr(vc),
                           _ptr(vs), int(T), float(scale), _ptr(s),
                           float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(vsg),
-                          _ptr(work), _ptr(out))
+                          int(code_bits), _ptr(work), _ptr(out))
     return out
 
 
 def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
          signs=None, rot_norm=0.0, rows=None, threads=1, chan_scale=None, v_signs=None,
-         rot_kind="srht"):
+         rot_kind="srht", code_bits=4):
     """Decode attention over a plain-layout cache.
 
-    q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D/2]; scales
+    q_bits [B, Hq, D] uint16; k/v codes [B, Hkv, cap, D code_bits / 8]; scales
     [B, Hkv, cap, D/32]; lens [B]; rot_kind: "srht" or "srft", the kind of
     K's rotation (signs) and of V's (v_signs); chan_scale: the K cache's per-channel
     scale lambda [D] or None; v_signs: the signs V was rotated with (same
@@ -236,20 +251,22 @@ def sdpa(q_bits, dtype, k_codes, k_scales, v_codes, v_scales, lens, scale,
         out = np.zeros((nrows, D), np.float64)
     rc = lib.oracle_sdpa(_ptr(q_bits), DTYPES[dtype], B, Hq, Hkv, D, cap, _ptr(kc), _ptr(ks),
                          _ptr(vc), _ptr(vs), _ptr(lens), float(scale), _ptr(s),
-                         float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(vsg), _ptr(r),
-                         nrows,
+                         float(np.float32(rot_norm)), _kind(rot_kind), _ptr(lam), _ptr(vsg),
+                         int(code_bits), _ptr(r), nrows,
                          _ptr(out), int(threads))
     if rc != 0:
         raise ValueError("oracle_sdpa rejected its arguments")
     return out
 
 
-def dequantize(codes, scales):
+def dequantize(codes, scales, code_bits=4):
     """Exact fp64 dequantisation code * scale of a plain-layout array."""
     codes = np.asarray(codes, np.uint8)
-    lo = (codes & 0xF).astype(np.int16)
-    hi = (codes >> 4).astype(np.int16)
-    c = np.stack([lo, hi], axis=-1).reshape(codes.shape[:-1] + (codes.shape[-1] * 2,))
-    c = np.where(c >= 8, c - 16, c).astype(np.float64)
+    # element i at bits [b i, b i + b) of the row's little-endian bit stream
+    bitstream = np.unpackbits(codes, axis=-1, bitorder="little")
+    n = bitstream.shape[-1] // code_bits
+    b = bitstream.reshape(codes.shape[:-1] + (n, code_bits)).astype(np.int16)
+    u = (b << np.arange(code_bits, dtype=np.int16)).sum(axis=-1)
+    c = np.where(u >= (1 << (code_bits - 1)), u - (1 << code_bits), u).astype(np.float64)
     s = np.repeat(np.asarray(scales, np.float64), 32, axis=-1)
     return c * s

@@ -58,6 +58,13 @@
  * + d_im w_re), each product rounded, then the sum; twiddles are the
  * correctly rounded fp32 values of cos and -sin of 2 pi t / N.
  *
+ * Other code widths (the AdapTQ page lists 2-bit and 3-bit quantisation
+ * beside 4-bit; int2 is named as later work elsewhere).  Reading: b-bit
+ * codes follow the same steps with the symmetric range of b bits, s = a /
+ * (2^(b-1) - 1) and codes clamped to [-2^(b-1), 2^(b-1) - 1], and element i
+ * of a row occupies bits [b i, b i + b) of the row's little-endian bit
+ * stream, two's complement (for b = 4: the nibble order above).
+ *
  * Per-channel scale ("SRFT + int4 KV-cache", core-method section: a
  * per-coordinate scale lambda is applied after the rotation and before the
  * group abs-max).  Reading: when a scale vector is given, the quantised
@@ -341,11 +348,53 @@ void oracle_quantize_vector(const float *x, int D, uint8_t *codes, float *scales
         codes[j] = (uint8_t)((c[2 * j] & 0xF) | ((c[2 * j + 1] & 0xF) << 4));
 }
 
-/* Signed value of nibble i of a packed row. */
-static int nibble(const uint8_t *row, int i)
+/* One vector x[D] -> b-bit codes (b = 2, 3 or 4) packed into D b / 8 bytes
+ * (element i at bits [b i, b i + b) of the little-endian bit stream) and
+ * scales[D/32], s = abs-max / (2^(b-1) - 1) in IEEE fp32. */
+void oracle_quantize_vector_bits(const float *x, int D, int bits, uint8_t *codes, float *scales)
 {
-    int u = (row[i >> 1] >> ((i & 1) * 4)) & 0xF;
-    return u >= 8 ? u - 16 : u;
+    const float qmax = (float)((1 << (bits - 1)) - 1);
+    const float qmin = -(float)(1 << (bits - 1));
+    memset(codes, 0, (size_t)D * bits / 8);
+    for (int g = 0; g < D / ORACLE_GROUP; ++g) {
+        const float *xg = x + g * ORACLE_GROUP;
+        float a = 0.0f;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            float v = fabsf(xg[i]);
+            if (v > a)
+                a = v;
+        }
+        float s = a / qmax;
+        scales[g] = s;
+        for (int i = 0; i < ORACLE_GROUP; ++i) {
+            int code = 0;
+            if (s != 0.0f) {
+                float r = rintf(xg[i] / s);
+                if (r != r)
+                    r = 0.0f;
+                if (r > qmax)
+                    r = qmax;
+                if (r < qmin)
+                    r = qmin;
+                code = (int)r;
+            }
+            const unsigned u = (unsigned)code & ((1u << bits) - 1u);
+            const long pos = (long)(g * ORACLE_GROUP + i) * bits;
+            for (int k = 0; k < bits; ++k)
+                if ((u >> k) & 1u)
+                    codes[(pos + k) >> 3] |= (uint8_t)(1u << ((pos + k) & 7));
+        }
+    }
+}
+
+/* Signed value of the b-bit code of element i of a packed row. */
+static int code_at(const uint8_t *row, int i, int bits)
+{
+    const long pos = (long)i * bits;
+    unsigned u = 0;
+    for (int k = 0; k < bits; ++k)
+        u |= (unsigned)((row[(pos + k) >> 3] >> ((pos + k) & 7)) & 1) << k;
+    return u >= (1u << (bits - 1)) ? (int)u - (1 << bits) : (int)u;
 }
 
 struct qrows_job {
@@ -357,6 +406,7 @@ struct qrows_job {
     float rot_norm;
     int rot_kind;
     const float *chan_scale;
+    int bits;
     uint8_t *codes;
     float *scales;
 };
@@ -373,8 +423,8 @@ static void *qrows_worker(void *arg)
         if (j->chan_scale)
             for (int i = 0; i < j->D; ++i)
                 x[i] = x[i] * j->chan_scale[i];
-        oracle_quantize_vector(x, j->D, j->codes + n * (j->D / 2),
-                               j->scales + n * (j->D / ORACLE_GROUP));
+        oracle_quantize_vector_bits(x, j->D, j->bits, j->codes + n * (j->D * j->bits / 8),
+                                    j->scales + n * (j->D / ORACLE_GROUP));
     }
     return NULL;
 }
@@ -385,10 +435,11 @@ static void *qrows_worker(void *arg)
  * does not change any result. */
 int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
                          const float *signs, float rot_norm, int rot_kind,
-                         const float *chan_scale, uint8_t *codes, float *scales, int nthreads)
+                         const float *chan_scale, int bits, uint8_t *codes, float *scales,
+                         int nthreads)
 {
     if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1 ||
-        rot_kind < 0 || rot_kind > 1 || (D & (D - 1)) != 0)
+        rot_kind < 0 || rot_kind > 1 || (D & (D - 1)) != 0 || bits < 2 || bits > 4)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -403,7 +454,7 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
         if (n0 >= n1)
             break;
         jobs[t] = (struct qrows_job){src, dtype, n0, n1, D, signs, rot_norm, rot_kind,
-                                     chan_scale, codes, scales};
+                                     chan_scale, bits, codes, scales};
         if (nthreads == 1) {
             qrows_worker(&jobs[t]);
         } else {
@@ -433,7 +484,7 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
                        const uint8_t *kc, const float *ks,
                        const uint8_t *vc, const float *vs, long T,
                        double scale, const float *signs, float rot_norm, int rot_kind,
-                       const float *chan_scale, const float *v_signs, double *work,
+                       const float *chan_scale, const float *v_signs, int bits, double *work,
                        double *out)
 {
     double qd[1024], kd[1024], vd[1024];
@@ -449,10 +500,10 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
 
     double m = -INFINITY;
     for (long t = 0; t < T; ++t) {
-        const uint8_t *row = kc + t * (D / 2);
+        const uint8_t *row = kc + t * (D * bits / 8);
         const float *srow = ks + t * ng;
         for (int i = 0; i < D; ++i) {
-            kd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
+            kd[i] = (double)code_at(row, i, bits) * (double)srow[i / ORACLE_GROUP];
             if (chan_scale)
                 kd[i] /= (double)chan_scale[i];
         }
@@ -467,10 +518,10 @@ void oracle_attend_row(const uint16_t *q, int dtype, int D,
     for (long t = 0; t < T; ++t) {
         double w = exp(work[t] - m);
         l += w;
-        const uint8_t *row = vc + t * (D / 2);
+        const uint8_t *row = vc + t * (D * bits / 8);
         const float *srow = vs + t * ng;
         for (int i = 0; i < D; ++i)
-            vd[i] = (double)nibble(row, i) * (double)srow[i / ORACLE_GROUP];
+            vd[i] = (double)code_at(row, i, bits) * (double)srow[i / ORACLE_GROUP];
         if (v_signs)
             unrotate_f64(vd, v_signs, D, (double)rot_norm, rot_kind);
         for (int i = 0; i < D; ++i)
@@ -493,6 +544,7 @@ struct attn_job {
     int rot_kind;
     const float *chan_scale;
     const float *v_signs;
+    int bits;
     double *out;
     const int32_t *rows;
     long r0, r1;
@@ -512,11 +564,12 @@ static void *attn_worker(void *arg)
         if (T > j->cap)
             T = j->cap;
         size_t head = (size_t)b * j->Hkv + hk;
+        const size_t rb = (size_t)j->D * j->bits / 8;  /* code bytes per row */
         oracle_attend_row(j->q + (size_t)row * j->D, j->dtype, j->D,
-                          j->kc + head * j->cap * (j->D / 2), j->ks + head * j->cap * (j->D / ORACLE_GROUP),
-                          j->vc + head * j->cap * (j->D / 2), j->vs + head * j->cap * (j->D / ORACLE_GROUP),
+                          j->kc + head * j->cap * rb, j->ks + head * j->cap * (j->D / ORACLE_GROUP),
+                          j->vc + head * j->cap * rb, j->vs + head * j->cap * (j->D / ORACLE_GROUP),
                           T, j->scale, j->signs, j->rot_norm, j->rot_kind, j->chan_scale,
-                          j->v_signs, work,
+                          j->v_signs, j->bits, work,
                           j->out + (size_t)r * j->D);
     }
     free(work);
@@ -531,12 +584,12 @@ static void *attn_worker(void *arg)
 int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, long cap,
                 const uint8_t *kc, const float *ks, const uint8_t *vc, const float *vs,
                 const int32_t *lens, double scale, const float *signs, float rot_norm,
-                int rot_kind, const float *chan_scale, const float *v_signs, const int32_t *rows,
-                long nrows, double *out, int nthreads)
+                int rot_kind, const float *chan_scale, const float *v_signs, int bits,
+                const int32_t *rows, long nrows, double *out, int nthreads)
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
         D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1 || rot_kind < 0 ||
-        rot_kind > 1 || (D & (D - 1)) != 0)
+        rot_kind > 1 || (D & (D - 1)) != 0 || bits < 2 || bits > 4)
         return -1;
     long R = rows ? nrows : (long)B * Hq;
     if (nthreads < 1)
@@ -552,8 +605,8 @@ int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, lon
         if (r0 >= r1)
             break;
         jobs[t] = (struct attn_job){q, dtype, B, Hq, Hkv, D, cap, kc, vc, ks, vs, lens,
-                                    scale, signs, rot_norm, rot_kind, chan_scale, v_signs, out,
-                                    rows, r0, r1};
+                                    scale, signs, rot_norm, rot_kind, chan_scale, v_signs, bits,
+                                    out, rows, r0, r1};
         if (nthreads == 1) {
             attn_worker(&jobs[t]);
         } else {

@@ -36,7 +36,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 4
+#define OTQ_ABI_VERSION 5
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -119,6 +119,16 @@ typedef enum otq_rot_kind {
  *           Tokens 2m and 2m+1 always share a byte.
  *
  * Bytes per array: codes B*H*C*D/2, scales B*H*C*(D/32)*4.
+ *
+ * 2- and 3-bit codes (code_bits = 2 or 3; AdapTQ page, core mechanisms: 2-,
+ * 3- and 4-bit quantisation): s_g = max_i |x_i| / (2^(b-1) - 1) and c_i =
+ * clamp(rint(x_i / s_g), -2^(b-1), 2^(b-1) - 1), otherwise as above; K and
+ * V rows are plain little-endian bit streams, element i at bits [b i,
+ * b i + b), two's complement: k_codes and v_codes uint8 [B][H][C][D*b/8],
+ * scales as above.  Such caches take no rotation and no per-channel scale
+ * (OTQ_EUNSUPPORTED), their split pass is the vector variant (any G <= 16),
+ * and otq_sdpa_int4_decode_append returns OTQ_EUNSUPPORTED for them (append
+ * with otq_quantize_append, then call otq_sdpa_int4_decode).
  */
 typedef struct otq_cache {
     int32_t batch;
@@ -135,6 +145,7 @@ typedef struct otq_cache {
     const float *v_rot_signs;  /* device [D] of +1.0f / -1.0f, 16-byte aligned, or NULL */
     int32_t rot_kind;          /* otq_rot_kind of both rotations; read only when
                                   k_rot_signs or v_rot_signs != NULL */
+    int32_t code_bits;         /* 4 (or 0) for the int4 layouts above; 2 or 3 for b-bit codes */
 } otq_cache;
 
 /* Human-readable name of a status code (static string). */

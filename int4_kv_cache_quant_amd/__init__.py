@@ -48,7 +48,7 @@ class otq_cache(ctypes.Structure):
         ("v_codes", ctypes.c_void_p), ("v_scales", ctypes.c_void_p),
         ("k_rot_signs", ctypes.c_void_p), ("rot_norm", ctypes.c_float),
         ("k_chan_scale", ctypes.c_void_p), ("v_rot_signs", ctypes.c_void_p),
-        ("rot_kind", ctypes.c_int32),
+        ("rot_kind", ctypes.c_int32), ("code_bits", ctypes.c_int32),
     ]
 
 
@@ -246,15 +246,23 @@ class Int4KVCache:
     """
 
     def __init__(self, batch, num_kv_heads, head_dim, capacity, device="cuda", rot_signs=None,
-                 chan_scale=None, v_rot_signs=None, rot_kind="srht"):
+                 chan_scale=None, v_rot_signs=None, rot_kind="srht", code_bits=4):
         cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity)
         self.shape = (batch, num_kv_heads, head_dim, capacity)
+        self.code_bits = code_bits
         g = head_dim // OTQ_GROUP
-        self.k_codes = torch.zeros((batch, num_kv_heads, capacity, head_dim // 2), dtype=torch.uint8, device=device)
         self.k_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
-        self.v_codes = torch.zeros((batch, num_kv_heads, capacity // OTQ_TILE, 16 * head_dim), dtype=torch.uint8, device=device)
         self.v_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
-        assert self.k_codes.numel() == cb and self.k_scales.numel() * 4 == sb
+        if code_bits == 4:
+            self.k_codes = torch.zeros((batch, num_kv_heads, capacity, head_dim // 2), dtype=torch.uint8,
+                                       device=device)
+            self.v_codes = torch.zeros((batch, num_kv_heads, capacity // OTQ_TILE, 16 * head_dim),
+                                       dtype=torch.uint8, device=device)
+            assert self.k_codes.numel() == cb and self.k_scales.numel() * 4 == sb
+        else:  # plain bit-stream rows of D * b / 8 bytes for K and V
+            rb = head_dim * code_bits // 8
+            self.k_codes = torch.zeros((batch, num_kv_heads, capacity, rb), dtype=torch.uint8, device=device)
+            self.v_codes = torch.zeros((batch, num_kv_heads, capacity, rb), dtype=torch.uint8, device=device)
         self.rot_signs = None if rot_signs is None else rot_signs.to(device=device, dtype=torch.float32).contiguous()
         self.rot_kind = ROT_KINDS[rot_kind]
         n = head_dim // 2 if self.rot_kind == OTQ_ROT_SRFT else head_dim
@@ -270,7 +278,7 @@ class Int4KVCache:
                               self.rot_norm,
                               None if self.chan_scale is None else self.chan_scale.data_ptr(),
                               None if self.v_rot_signs is None else self.v_rot_signs.data_ptr(),
-                              self.rot_kind)
+                              self.rot_kind, code_bits)
 
     @property
     def nbytes(self):

@@ -31,6 +31,9 @@ int check_dims(int32_t B, int32_t H, int32_t D, int32_t cap)
     return OTQ_OK;
 }
 
+// Code width of a cache: 0 (a descriptor that predates the field) is int4.
+int code_bits(const otq_cache* c) { return c->code_bits == 0 ? 4 : c->code_bits; }
+
 int check_cache(const otq_cache* c)
 {
     if (!c) return OTQ_EINVAL;
@@ -43,6 +46,9 @@ int check_cache(const otq_cache* c)
         return OTQ_EINVAL;
     if ((c->k_rot_signs || c->v_rot_signs) && c->rot_kind != OTQ_ROT_SRHT && c->rot_kind != OTQ_ROT_SRFT)
         return OTQ_EINVAL;
+    if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 3 && c->code_bits != 4) return OTQ_EINVAL;
+    // 2- and 3-bit caches: unrotated, unscaled (the int4 path serves those options)
+    if (code_bits(c) != 4 && (c->k_rot_signs || c->v_rot_signs || c->k_chan_scale)) return OTQ_EUNSUPPORTED;
     return OTQ_OK;
 }
 
@@ -70,9 +76,13 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     int variant = variant_ov;
     if (variant == OTQ_VARIANT_AUTO) {
         // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
-        variant = otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
+        variant = code_bits(c) != 4                      ? OTQ_VARIANT_VECTOR
+                  : otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA
+                                                   : OTQ_VARIANT_VECTOR;
     }
-    if (variant == OTQ_VARIANT_VECTOR) {
+    if (code_bits(c) != 4) {  // the b-bit split pass: vector arithmetic, any G <= 16
+        if (variant != OTQ_VARIANT_VECTOR) return OTQ_EUNSUPPORTED;
+    } else if (variant == OTQ_VARIANT_VECTOR) {
         if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_MFMA) {
         if (!otq::split_mfma_supports(D, G)) return OTQ_EUNSUPPORTED;
@@ -170,6 +180,13 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     if ((((uintptr_t)k) & 15) != 0 || (((uintptr_t)v) & 15) != 0) return OTQ_EINVAL;
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (n_new > cache->capacity) return OTQ_ECAPACITY;
+    if (code_bits(cache) != 4) {
+        const hipError_t e = otq::launch_quantize_bits(
+            k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
+            code_bits(cache), cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, pos,
+            static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+    }
     const hipError_t e = otq::launch_quantize_append(
         k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
         cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
@@ -264,8 +281,9 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
             return OTQ_EDEVICE;
         a.items = items;
     }
-    const hipError_t e = chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
-                                                         : otq::launch_split_vector(a, s);
+    const hipError_t e = code_bits(cache) != 4 ? otq::launch_split_bits(a, code_bits(cache), s)
+                         : chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
+                                                           : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
@@ -368,6 +386,7 @@ int otq_sdpa_int4_decode_append(const void* q, const void* k_new, const void* v_
                   : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &chk);
     if (rc != OTQ_OK) return rc;
     if (!q || !k_new || !v_new || !lens || !out) return OTQ_EINVAL;
+    if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;

@@ -1,0 +1,265 @@
+// bits.hip - 2- and 3-bit codes: quantise-append and the split pass over
+// caches whose rows are plain little-endian bit streams.
+//
+// The code widths the AdapTQ page lists beside 4-bit (its section on the
+// core mechanisms: 2-, 3- and 4-bit quantisation): b-bit codes take the
+// int4 steps with the symmetric range of b bits, s = abs-max / (2^(b-1) - 1)
+// in IEEE fp32 and c = clamp(rint(x / s), -2^(b-1), 2^(b-1) - 1), s == 0
+// giving zero codes; element i of a row occupies bits [b i, b i + b) of the
+// row's little-endian bit stream, two's complement.  K and V rows have the
+// same layout, [B][H][capacity][D b / 8] bytes, scales as for int4.
+//
+// A first path, for correctness: the split kernel computes scores and the
+// value sum with fp32 vector arithmetic, one token per thread for the
+// scores and one channel per thread for the value sum, and writes the same
+// (m, l, o) partials as the int4 kernels, so the same combine merges them.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace otq {
+
+namespace {
+
+constexpr float kNegInfB = -__builtin_huge_valf();
+
+// Signed b-bit code of element i of a row (bits may straddle two bytes).
+template <int BITS>
+__device__ __forceinline__ int code_at(const uint8_t* __restrict__ row, int i)
+{
+    const int pos = i * BITS, byte = pos >> 3, sh = pos & 7;
+    uint32_t u = row[byte];
+    if (sh + BITS > 8) u |= (uint32_t)row[byte + 1] << 8;
+    u = (u >> sh) & ((1u << BITS) - 1u);
+    return u >= (1u << (BITS - 1)) ? (int)u - (1 << BITS) : (int)u;
+}
+
+// One wave per new vector (K tokens, then V tokens), E = D / 64 elements per
+// lane; the codes pass through LDS so that D b / 32 lanes assemble the row's
+// 32-bit words.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void quantize_bits_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
+    uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
+    const int32_t* __restrict__ pos)
+{
+#pragma clang fp contract(off)
+    constexpr int E = D / 64, NG = D / kGroup, RB = D * BITS / 8, NWORD = RB / 4;
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1), qmin = -(float)(1 << (BITS - 1));
+    static_assert(RB % 4 == 0, "whole words per row");
+    __shared__ int8_t cs[4][D];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int vec = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
+    const bool is_v = vec >= n_new;
+    const int tok = is_v ? vec - n_new : vec;
+    const int t = pos[b] + tok;
+    // every thread reaches the barrier; inactive waves do no memory access
+    const bool active = vec < 2 * n_new && t >= 0 && t < cap;
+    const size_t head = (size_t)b * H + h;
+    float sc = 0.0f;
+    if (active) {
+        const uint16_t* src = (is_v ? v : k) + (head * n_new + tok) * D + lane * E;
+        float x[E];
+        float a = 0.0f;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            x[e] = widen(src[e], dtype);
+            a = fmaxf(a, fabsf(x[e]));
+        }
+        a = group_max<kGroup / E>(a);  // exact in any order
+        sc = a / qmax;                 // correctly rounded IEEE division
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            float r = rintf(x[e] / sc);  // IEEE division, then half to even
+            r = fminf(fmaxf(r, qmin), qmax);
+            cs[wave][lane * E + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
+        }
+    }
+    __syncthreads();
+    if (!active) return;
+    const size_t row = head * cap + t;
+    if (lane % (kGroup / E) == 0) (is_v ? vs : ks)[row * NG + (lane * E) / kGroup] = sc;
+    if (lane < NWORD) {  // word w holds bits [32 w, 32 w + 32) of the row
+        uint32_t word = 0;
+        const int i0 = (32 * lane) / BITS, i1 = min((32 * lane + 31) / BITS, D - 1);
+        for (int i = i0; i <= i1; ++i) {
+            const uint32_t u = (uint32_t)cs[wave][i] & ((1u << BITS) - 1u);
+            const int off = i * BITS - 32 * lane;  // may be negative for the first element
+            word |= off >= 0 ? u << off : u >> -off;
+        }
+        reinterpret_cast<uint32_t*>((is_v ? vc : kc) + row * RB)[lane] = word;
+    }
+}
+
+// One block per (split, KV head, sequence): q of the G heads in LDS (scaled
+// by scale log2(e)); per 256-token tile, one token per thread scores all G
+// heads, then per head 16 threads find the tile maximum and turn the scores
+// into probabilities, and one channel per thread accumulates p * V for the
+// G heads.
+template <int D, int BITS>
+__global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
+{
+    constexpr int NG = D / kGroup, RB = D * BITS / 8, TT = 256;
+    __shared__ float q_lds[16][D];
+    __shared__ float p_lds[16][TT];
+    __shared__ float3 step[16];  // per head: (rescale of the old state, new reference, tile sum)
+
+    const int tid = threadIdx.x;
+    int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    if (a.items) {  // a batch: the block's item in longest-first order
+        const int kk = blockIdx.x + a.num_splits * (blockIdx.y + a.H * blockIdx.z);
+        const int2 it = a.items[kk];
+        if (it.x < 0) return;  // block-uniform: no item
+        split = it.x;
+        b = it.y;
+        hk = kk % a.H;
+    }
+    const int G = a.Hq / a.H;
+    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
+    const int start = split * a.chunk;
+    if (start >= len) return;  // block-uniform: no partial for empty chunks
+    const int end = min(start + a.chunk, len);
+
+    const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
+    for (int i = tid; i < G * D; i += TT) q_lds[i / D][i % D] = widen(qsrc[i], a.dtype) * a.qscale;
+    __syncthreads();
+
+    const size_t head = (size_t)b * a.H + hk;
+    const uint8_t* krows = a.kc + head * a.cap * RB;
+    const uint8_t* vrows = a.vc + head * a.cap * RB;
+    const float* kscl = a.ks + head * a.cap * NG;
+    const float* vscl = a.vs + head * a.cap * NG;
+
+    float m[16], l[16], o[16];
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+        m[g] = kNegInfB;
+        l[g] = 0.0f;
+        o[g] = 0.0f;
+    }
+    const int hg = tid / 16, hl = tid % 16;  // reduction role: head hg, 16 threads per head
+    for (int t0 = start; t0 < end; t0 += TT) {
+        const int n = min(TT, end - t0);
+        // scores, one token per thread
+        {
+            float acc[16];
+#pragma unroll
+            for (int g = 0; g < 16; ++g) acc[g] = 0.0f;
+            if (tid < n) {
+                const uint8_t* row = krows + (size_t)(t0 + tid) * RB;
+                for (int gr = 0; gr < NG; ++gr) {
+                    const float s = kscl[(size_t)(t0 + tid) * NG + gr];
+                    for (int i = 32 * gr; i < 32 * gr + 32; ++i) {
+                        const float kd = (float)code_at<BITS>(row, i) * s;
+#pragma unroll
+                        for (int g = 0; g < 16; ++g)
+                            if (g < G) acc[g] += q_lds[g][i] * kd;
+                    }
+                }
+            }
+#pragma unroll
+            for (int g = 0; g < 16; ++g)
+                if (g < G) p_lds[g][tid] = tid < n ? acc[g] : kNegInfB;
+        }
+        __syncthreads();
+        // per head: the tile's maximum, the probabilities and their sum
+        if (hg < G) {
+            float mx = kNegInfB;
+            for (int j = hl; j < TT; j += 16) mx = fmaxf(mx, p_lds[hg][j]);
+#pragma unroll
+            for (int s = 8; s >= 1; s >>= 1) mx = fmaxf(mx, shfl_xor(mx, s));
+            const float old = m[hg];
+            const float mn = fmaxf(old, mx);
+            float sum = 0.0f;
+            for (int j = hl; j < TT; j += 16) {
+                const float p = j < n ? exp2_approx(p_lds[hg][j] - mn) : 0.0f;
+                p_lds[hg][j] = p;
+                sum += p;
+            }
+#pragma unroll
+            for (int s = 8; s >= 1; s >>= 1) sum += shfl_xor(sum, s);
+            if (hl == 0) step[hg] = make_float3(old == kNegInfB ? 0.0f : exp2_approx(old - mn), mn, sum);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int g = 0; g < 16; ++g) {
+            if (g < G) {
+                const float3 st = step[g];
+                l[g] = l[g] * st.x + st.z;
+                m[g] = st.y;
+                o[g] *= st.x;
+            }
+        }
+        // value sum, one channel per thread
+        if (tid < D) {
+            const int gr = tid / kGroup;
+            for (int j = 0; j < n; ++j) {
+                const float vd = (float)code_at<BITS>(vrows + (size_t)(t0 + j) * RB, tid) *
+                                 vscl[(size_t)(t0 + j) * NG + gr];
+#pragma unroll
+                for (int g = 0; g < 16; ++g)
+                    if (g < G) o[g] += p_lds[g][j] * vd;
+            }
+        }
+        __syncthreads();  // p_lds and step are rewritten by the next tile
+    }
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+        if (g < G) {
+            const size_t prow = ((size_t)b * a.Hq + hk * G + g) * a.num_splits + split;
+            if (tid < D) a.part_o[prow * D + tid] = o[g];
+            if (tid == 0) a.part_ml[prow] = make_float2(m[g], l[g]);
+        }
+    }
+}
+
+template <int D, int BITS>
+hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, int H, int cap,
+                    uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, hipStream_t s)
+{
+    dim3 grid((2 * n_new + 3) / 4, H, B), block(256);
+    quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
+                                                          static_cast<const uint16_t*>(v), dtype, n_new,
+                                                          H, cap, kc, ks, vc, vs, pos);
+    return hipGetLastError();
+}
+
+template <int D, int BITS>
+hipError_t launch_s(const SplitArgs& a, hipStream_t s)
+{
+    dim3 grid(a.num_splits, a.H, a.B), block(256);
+    split_bits_kernel<D, BITS><<<grid, block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
+                                int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
+                                const int32_t* pos, hipStream_t s)
+{
+    switch (D * 10 + bits) {
+    case 642: return launch_q<64, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 643: return launch_q<64, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 1282: return launch_q<128, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 1283: return launch_q<128, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 2562: return launch_q<256, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 2563: return launch_q<256, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t s)
+{
+    if (a.Hq / a.H > 16) return hipErrorInvalidValue;
+    switch (a.D * 10 + bits) {
+    case 642: return launch_s<64, 2>(a, s);
+    case 643: return launch_s<64, 3>(a, s);
+    case 1282: return launch_s<128, 2>(a, s);
+    case 1283: return launch_s<128, 3>(a, s);
+    case 2562: return launch_s<256, 2>(a, s);
+    case 2563: return launch_s<256, 3>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace otq

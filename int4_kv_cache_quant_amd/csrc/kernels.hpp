@@ -42,6 +42,13 @@ struct SplitArgs {
     int lens_offset;
 };
 
+// 2- and 3-bit codes (plain bit-stream rows for K and V): the append and the
+// split pass; the combine is shared.
+hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
+                                int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
+                                const int32_t* pos, hipStream_t stream);
+hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
+
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
 hipError_t launch_split_vector(const SplitArgs& a, hipStream_t stream);
 // Largest batch whose split blocks are ordered longest first.

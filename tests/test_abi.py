@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 4
+    assert lib.otq_abi_version() == 5
 
 
 def test_status_strings():
@@ -225,3 +225,35 @@ def test_k_row_layout_roundtrip_and_fixed_points(D):
     p[0, 16] = 0x30           # channel 33 = 3
     r = layout.k_plain_to_rows(p, D)[0]
     assert r[4 * NG] == 0x05 and r[4] == 0x30 and np.count_nonzero(r) == 2
+
+
+def test_code_bits_host_checks():
+    """code_bits 0 or 4 is int4, 2 and 3 the b-bit path (vector split pass, no
+    rotation or channel scale, no fused append); other values are invalid."""
+    lib = otq.lib()
+    P = ctypes.c_void_p
+    plan = lambda desc, variant=0: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, variant,
+                                                     ctypes.byref(otq.otq_plan()))
+    for bits, want in ((0, otq.OTQ_OK), (4, otq.OTQ_OK), (2, otq.OTQ_OK), (3, otq.OTQ_OK),
+                       (1, otq.OTQ_EINVAL), (5, otq.OTQ_EINVAL), (-3, otq.OTQ_EINVAL)):
+        d = _desc()
+        d.code_bits = bits
+        assert plan(d) == want, bits
+    d = _desc()
+    d.code_bits = 3
+    p = otq.otq_plan()
+    assert lib.otq_sdpa_plan(16, ctypes.byref(d), 64, 0, 0, ctypes.byref(p)) == otq.OTQ_OK
+    assert p.variant == otq.OTQ_VARIANT_VECTOR
+    assert plan(d, otq.OTQ_VARIANT_MFMA) == otq.OTQ_EUNSUPPORTED
+    assert plan(d, otq.OTQ_VARIANT_VECTOR) == otq.OTQ_OK
+    for field in ("k_rot_signs", "v_rot_signs", "k_chan_scale"):
+        e = _desc()
+        e.code_bits = 2
+        setattr(e, field, FAKE)
+        assert plan(e) == otq.OTQ_EUNSUPPORTED, field
+    ws = lib.otq_sdpa_workspace_bytes(16, ctypes.byref(d), 64)
+    rc = lib.otq_sdpa_int4_decode_append(P(FAKE), P(FAKE), P(FAKE), 1, 16, ctypes.byref(d), P(FAKE), 64,
+                                         ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws), None,
+                                         None)
+    assert rc == otq.OTQ_EUNSUPPORTED
+

@@ -1,0 +1,134 @@
+"""GPU parity of the 2- and 3-bit path (plain bit-stream rows): codes and
+scales bit-exact against the oracle's b-bit quantiser, outputs of the split
++ combine within the same tolerance as int4 against the oracle's fp64
+attention over the cache it quantised itself."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import int4_kv_cache_quant_amd as otq
+import oracle
+from int4_kv_cache_quant_amd import synth
+
+from gpu_common import MAX_ABS, REL_L2, errors, say, to_bits
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _kv(B, H, T, D, dtype, seed):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((2, B, H, T, D), generator=g)
+    x[..., 3] *= 10
+    x = x.to(dtype)
+    return x[0], x[1]
+
+
+def _build(k, v, cap, bits, chunk):
+    B, H, T, D = k.shape
+    cache = otq.Int4KVCache(B, H, D, cap, device=DEV, code_bits=bits)
+    for t0 in range(0, T, chunk):
+        t1 = min(T, t0 + chunk)
+        pos = torch.full((B,), t0, dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t0:t1].to(DEV).contiguous(), v[:, :, t0:t1].to(DEV).contiguous(), pos)
+    torch.cuda.synchronize()
+    return cache
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("dtype", [torch.float16, torch.bfloat16])
+@pytest.mark.parametrize("chunk", [19, 1])
+def test_bits_quantize_bit_exact(bits, D, dtype, chunk):
+    B, H, T, cap = 2, 3, 45, 64
+    say(f"bits quantize b={bits} D={D} dtype={dtype} chunk={chunk}")
+    k, v = _kv(B, H, T, D, dtype, seed=bits * 1000 + D + chunk)
+    cache = _build(k, v, cap, bits, chunk)
+    name = "fp16" if dtype == torch.float16 else "bf16"
+    kc, ks = oracle.quantize(to_bits(k), name, code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v), name, code_bits=bits)
+    got = [t.cpu().numpy()[:, :, :T] for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales)]
+    for g, r in zip(got, (kc, ks, vc, vs)):
+        if g.dtype == np.float32:
+            g, r = g.view(np.uint32), r.view(np.uint32)
+        assert np.array_equal(g, r)
+    # tokens past the appended range stay untouched
+    assert not np.any(cache.k_codes.cpu().numpy()[:, :, T:]) and not np.any(cache.v_scales.cpu().numpy()[:, :, T:])
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("G,D", [(1, 64), (4, 128), (8, 128), (16, 64), (2, 256)])
+def test_bits_sdpa_parity(bits, G, D):
+    B, Hkv, cap = 2, 2, 448
+    lens = [448, 77]
+    say(f"bits sdpa b={bits} G={G} D={D}")
+    k, v = _kv(B, Hkv, cap, D, torch.bfloat16, seed=bits * 100 + G + D)
+    g = torch.Generator().manual_seed(G + D)
+    q = torch.randn((B, G * Hkv, D), generator=g).to(torch.bfloat16)
+    cache = _build(k, v, cap, bits, 100)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    plan = cache.plan(G * Hkv, max(lens), chunk=128)
+    assert plan.variant == otq.OTQ_VARIANT_VECTOR
+    scale = 1.0 / math.sqrt(D)
+    out = cache.decode(q.to(DEV), lens_t, max(lens), scale, plan=plan)
+    torch.cuda.synchronize()
+    kc, ks = oracle.quantize(to_bits(k), "bf16", code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v), "bf16", code_bits=bits)
+    ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale, threads=8,
+                      code_bits=bits)
+    ma, rel = errors(out.cpu().numpy(), ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_bits_edge_lengths_and_ragged_batch(bits):
+    B, Hkv, G, D, cap = 5, 2, 4, 128, 384
+    lens = [0, 1, 256, 129, 384]
+    k, v = _kv(B, Hkv, cap, D, torch.float16, seed=bits + 7)
+    g = torch.Generator().manual_seed(bits)
+    q = torch.randn((B, G * Hkv, D), generator=g).to(torch.float16)
+    cache = _build(k, v, cap, bits, cap)
+    out = cache.decode(q.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV), cap, 0.1)
+    torch.cuda.synchronize()
+    kc, ks = oracle.quantize(to_bits(k), "fp16", code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v), "fp16", code_bits=bits)
+    ref = oracle.sdpa(to_bits(q), "fp16", kc, ks, vc, vs, np.array(lens, np.int32), 0.1, threads=8,
+                      code_bits=bits)
+    got = out.cpu().numpy()
+    assert np.all(got[0] == 0.0)
+    ma, rel = errors(got, ref)
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+def test_bits_full_workload_3(bits):
+    """The 70B layer at 131072 tokens with b-bit codes: codes of sampled
+    tokens bit-exact, outputs of sampled rows within tolerance."""
+    w = synth.WORKLOADS[3]
+    say(f"bits full workload 3 b={bits}")
+    k = synth.kv(w, 0, "k", device=DEV)
+    v = synth.kv(w, 0, "v", device=DEV)
+    q = synth.query(w, 0, device=DEV)
+    cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, code_bits=bits)
+    for t0 in range(0, w.T, 16384):
+        pos = torch.full((w.B,), t0, dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t0:t0 + 16384].contiguous(), v[:, :, t0:t0 + 16384].contiguous(), pos)
+    lens = synth.lens(w, 0)
+    out = cache.decode(q, torch.from_numpy(lens).to(DEV), int(lens.max()), w.scale)
+    torch.cuda.synchronize()
+    kc, ks = oracle.quantize(to_bits(k.cpu()), w.dtype, threads=16, code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v.cpu()), w.dtype, threads=16, code_bits=bits)
+    rng = np.random.default_rng(bits)
+    toks = rng.choice(w.T, 64, replace=False)
+    assert np.array_equal(cache.k_codes.cpu().numpy()[:, :, toks], kc[:, :, toks])
+    assert np.array_equal(cache.v_codes.cpu().numpy()[:, :, toks], vc[:, :, toks])
+    rows = np.sort(rng.choice(w.Hq, 8, replace=False)).astype(np.int32)
+    ref = oracle.sdpa(to_bits(q.cpu()), w.dtype, kc, ks, vc, vs, lens, w.scale, rows=rows, threads=16,
+                      code_bits=bits)
+    ma, rel = errors(out.cpu().numpy().reshape(-1, w.D)[rows], ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2

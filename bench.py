@@ -133,6 +133,9 @@ def main():
     ap.add_argument("--srht", action="store_true",
                     help="rotate K by the sign-randomised Walsh-Hadamard transform (seeded signs) on a "
                          "workload that does not rotate it")
+    ap.add_argument("--code-bits", type=int, default=4, choices=(2, 3, 4),
+                    help="code width of the caches; 2 and 3 take the b-bit path (no rotation or channel "
+                         "scale; the step is the append kernel, then split + combine)")
     ap.add_argument("--cpu-threads", type=int, default=None)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
@@ -183,6 +186,9 @@ def main():
 
     # ---------------------------------------------------------------- setup
     rot_kind = "srft" if args.srft else "srht"
+    bits = args.code_bits
+    if bits != 4 and (args.srft or args.srht or args.chan_scale or args.v_rotate or w.rotate):
+        sys.exit("bench.py: 2- and 3-bit caches take no rotation or channel scale")
     if args.srft and args.srht:
         sys.exit("bench.py: --srft and --srht name two different K rotations")
     t_setup = time.time()
@@ -193,7 +199,7 @@ def main():
         lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if args.chan_scale else None
         vsg = torch.from_numpy(synth.v_rot_signs(w, l)).to(dev) if args.v_rotate else None
         cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs,
-                                chan_scale=lam, v_rot_signs=vsg, rot_kind=rot_kind)
+                                chan_scale=lam, v_rot_signs=vsg, rot_kind=rot_kind, code_bits=bits)
         k = synth.kv(w, l, "k", device=dev)
         v = synth.kv(w, l, "v", device=dev)
         lens = synth.lens(w, l)
@@ -237,6 +243,11 @@ def main():
         otq.otq_sdpa_lse_combine(w.Hq, caches[l].desc, lens_l[l], max_len, ws, plan, outs[l])
 
     def fused(l):  # split over the cached tokens, then the combine that appends the new token
+        if bits != 4:  # b-bit caches: the append kernel, then split + combine over lens
+            append(l)
+            split(l)
+            combine(l)
+            return
         otq.otq_sdpa_int4_decode_append(qs[l], k_new[l], v_new[l], caches[l].desc, lens_l[l],
                                         max_len, w.scale, outs[l], ws, plan=plan)
 
@@ -338,7 +349,7 @@ def main():
                for i in range(n_chunks)]
     scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs,
                               chan_scale=caches[0].chan_scale, v_rot_signs=caches[0].v_rot_signs,
-                              rot_kind=rot_kind)
+                              rot_kind=rot_kind, code_bits=bits)
     bulk_pos = [torch.full((w.B,), i * n_bulk, dtype=torch.int32, device=dev) for i in range(n_chunks)]
 
     def bulk_pass():
@@ -362,18 +373,18 @@ def main():
     b.record()
     torch.cuda.synchronize()
     bulk_us = a.elapsed_time(b) * 1000.0 / (reps * n_chunks)
-    bulk_bytes = w.B * w.Hkv * n_bulk * (2 * w.D * 2 + 2 * (w.D // 2 + 4 * (w.D // 32)))
+    bulk_bytes = w.B * w.Hkv * n_bulk * (2 * w.D * 2 + 2 * (w.D * bits // 8 + 4 * (w.D // 32)))
     log(f"bench: bulk append of {n_bulk} tokens x {w.B * w.Hkv} heads: {bulk_us:.2f} us, "
         f"{bulk_bytes / (bulk_us * 1e-6) / 1e9:.0f} GB/s")
     del bulk_in, scratch
 
     # algorithmic bytes: packed codes + fp32 scales of every attended token, q read; out write
     lens_sum = [int(x.long().sum()) for x in lens_l]
-    unit = w.Hkv * 2 * (w.D // 2 + 4 * (w.D // 32))            # bytes per attended token (K+V)
+    unit = w.Hkv * 2 * (w.D * bits // 8 + 4 * (w.D // 32))     # bytes per attended token (K+V)
     split_bytes = float(np.mean([s * unit for s in lens_sum])) + w.B * w.Hq * w.D * 2
     layer_bytes = split_bytes + w.B * w.Hq * w.D * 4
     achieved = split_bytes / (split_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(plan.variant, w.name)
+    traffic = traffic_from_profile(plan.variant, w.name) if bits == 4 else None
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -384,9 +395,9 @@ def main():
         kb, vb, sg, lam0, vsg0 = host_kv0
         t = time.time()
         kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
-                                 chan_scale=lam0, rot_kind=rot_kind)
+                                 chan_scale=lam0, rot_kind=rot_kind, code_bits=bits)
         vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads,
-                                 rot_kind=rot_kind)
+                                 rot_kind=rot_kind, code_bits=bits)
         log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
         lens0 = synth.lens(w, 0)
         q0 = synth.bits(qs[0])
@@ -396,7 +407,7 @@ def main():
         while True:
             ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
                               rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0, v_signs=vsg0,
-                              rot_kind=rot_kind)
+                              rot_kind=rot_kind, code_bits=bits)
             reps += 1
             if time.perf_counter() - t >= 10.0 or reps >= 200:
                 break
@@ -434,6 +445,7 @@ def main():
             "graph": graph is not None, "k_chan_scale": bool(args.chan_scale),
             "v_rotated": bool(args.v_rotate),
             "k_rotation": ("none" if not (w.rotate or args.srft or args.srht) else rot_kind),
+            "code_bits": bits,
             "step": "per layer: the split pass over the cached tokens, then the combine pass that "
                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)",
         },
@@ -447,11 +459,12 @@ def main():
             "append_unfused_kernel": round(append_us, 3),
             "sdpa_per_layer_graph": None if sdpa_graph_us is None else round(sdpa_graph_us, 3)},
         "sdpa_GBps": round(layer_bytes / ((sdpa_graph_us or (split_us + combine_us)) * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "split_mfma" if plan.variant == 2 else "split_vec",
+        "roofline": {"bound": "hbm",
+                     "kernel": "split_bits" if bits != 4 else ("split_mfma" if plan.variant == 2 else "split_vec"),
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
                      "algorithmic_bytes_per_launch": int(split_bytes)},
-        "append_bulk": {"kernel": "quantize_tile", "tokens_per_sequence": n_bulk,
+        "append_bulk": {"kernel": "quantize_tile" if bits == 4 else "quantize_bits", "tokens_per_sequence": n_bulk,
                         "sequences": w.B, "kv_heads": w.Hkv, "us": round(bulk_us, 3),
                         "algorithmic_bytes": int(bulk_bytes),
                         "GBps": round(bulk_bytes / (bulk_us * 1e-6) / 1e9, 1),

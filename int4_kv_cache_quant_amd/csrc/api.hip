@@ -103,7 +103,10 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         }
         // a batch takes its items longest first, which balances unequal
         // lengths better the more (smaller) items there are
-        const long long target = ordered_batch(c->batch) ? kTargetWaves * kOrderedWaveFactor : kTargetWaves;
+        // the b-bit split pass hides latency only with several blocks per CU
+        const long long target = (ordered_batch(c->batch) || code_bits(c) != 4)
+                                     ? kTargetWaves * kOrderedWaveFactor
+                                     : kTargetWaves;
         const long long groups = target / waves;
         long long want = ((long long)max_len * units + groups - 1) / groups;
         want = (want + align - 1) / align * align;

@@ -22,15 +22,16 @@ namespace {
 
 constexpr float kNegInfB = -__builtin_huge_valf();
 
-// Signed b-bit code of element i of a row (bits may straddle two bytes).
+// Signed b-bit code of element i of a row held as 32-bit words (the bits
+// may straddle two words).
 template <int BITS>
-__device__ __forceinline__ int code_at(const uint8_t* __restrict__ row, int i)
+__device__ __forceinline__ int code_in_words(const uint32_t* w, int i)
 {
-    const int pos = i * BITS, byte = pos >> 3, sh = pos & 7;
-    uint32_t u = row[byte];
-    if (sh + BITS > 8) u |= (uint32_t)row[byte + 1] << 8;
-    u = (u >> sh) & ((1u << BITS) - 1u);
-    return u >= (1u << (BITS - 1)) ? (int)u - (1 << BITS) : (int)u;
+    const int pos = i * BITS, k = pos >> 5, sh = pos & 31;
+    uint32_t u = w[k] >> sh;
+    if (sh + BITS > 32) u |= w[k + 1] << (32 - sh);
+    // sign-extend the low BITS bits
+    return (int)(u << (32 - BITS)) >> (32 - BITS);
 }
 
 // One wave per new vector (K tokens, then V tokens), E = D / 64 elements per
@@ -98,10 +99,12 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 {
-    constexpr int NG = D / kGroup, RB = D * BITS / 8, TT = 256;
-    __shared__ float q_lds[16][D];
+    constexpr int NG = D / kGroup, RB = D * BITS / 8, RW = RB / 4, TT = 256;
+    __shared__ __align__(16) float q_lds[16][D];
     __shared__ float p_lds[16][TT];
     __shared__ float3 step[16];  // per head: (rescale of the old state, new reference, tile sum)
+    __shared__ uint32_t v_lds[TT * RW];  // the tile's V rows
+    __shared__ float vs_lds[TT * NG];    // and their scales
 
     const int tid = threadIdx.x;
     int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -137,6 +140,8 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         o[g] = 0.0f;
     }
     const int hg = tid / 16, hl = tid % 16;  // reduction role: head hg, 16 threads per head
+    constexpr int TS = TT / D;                // value role: channel vc_, token subset vts of TS
+    const int vc_ = tid % D, vts = tid / D;
     for (int t0 = start; t0 < end; t0 += TT) {
         const int n = min(TT, end - t0);
         // scores, one token per thread
@@ -145,16 +150,33 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 #pragma unroll
             for (int g = 0; g < 16; ++g) acc[g] = 0.0f;
             if (tid < n) {
-                const uint8_t* row = krows + (size_t)(t0 + tid) * RB;
+                uint32_t kw[RW];  // the token's K row, read as words
+                const uint32_t* row = reinterpret_cast<const uint32_t*>(krows + (size_t)(t0 + tid) * RB);
+#pragma unroll
+                for (int k = 0; k < RW; ++k) kw[k] = row[k];
+#pragma unroll
                 for (int gr = 0; gr < NG; ++gr) {
                     const float s = kscl[(size_t)(t0 + tid) * NG + gr];
-                    for (int i = 32 * gr; i < 32 * gr + 32; ++i) {
-                        const float kd = (float)code_at<BITS>(row, i) * s;
 #pragma unroll
-                        for (int g = 0; g < 16; ++g)
-                            if (g < G) acc[g] += q_lds[g][i] * kd;
+                    for (int i = 32 * gr; i < 32 * gr + 32; i += 4) {
+                        float kd[4];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) kd[e] = (float)code_in_words<BITS>(kw, i + e) * s;
+#pragma unroll
+                        for (int g = 0; g < 16; ++g) {
+                            if (g < G) {
+                                const float4 qv = *reinterpret_cast<const float4*>(&q_lds[g][i]);
+                                acc[g] += qv.x * kd[0] + qv.y * kd[1] + qv.z * kd[2] + qv.w * kd[3];
+                            }
+                        }
                     }
                 }
+            }
+            // the tile's V rows and scales into LDS (coalesced)
+            {
+                const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vrows + (size_t)t0 * RB);
+                for (int k = tid; k < n * RW; k += TT) v_lds[k] = vsrc[k];
+                for (int k = tid; k < n * NG; k += TT) vs_lds[k] = vscl[(size_t)t0 * NG + k];
             }
 #pragma unroll
             for (int g = 0; g < 16; ++g)
@@ -189,12 +211,12 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
                 o[g] *= st.x;
             }
         }
-        // value sum, one channel per thread
-        if (tid < D) {
-            const int gr = tid / kGroup;
-            for (int j = 0; j < n; ++j) {
-                const float vd = (float)code_at<BITS>(vrows + (size_t)(t0 + j) * RB, tid) *
-                                 vscl[(size_t)(t0 + j) * NG + gr];
+        // value sum: channel c of every TS-th token of the tile per thread
+        {
+            const int gr = vc_ / kGroup;
+#pragma unroll 4
+            for (int j = vts; j < n; j += TS) {
+                const float vd = (float)code_in_words<BITS>(&v_lds[j * RW], vc_) * vs_lds[j * NG + gr];
 #pragma unroll
                 for (int g = 0; g < 16; ++g)
                     if (g < G) o[g] += p_lds[g][j] * vd;
@@ -202,11 +224,20 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         }
         __syncthreads();  // p_lds and step are rewritten by the next tile
     }
+    // the TS token subsets of each channel, added through LDS (p_lds is free)
 #pragma unroll
     for (int g = 0; g < 16; ++g) {
         if (g < G) {
+            float* red = &p_lds[0][0];
+            if (TS > 1) {
+                red[vts * D + vc_] = o[g];
+                __syncthreads();
+                if (vts == 0)
+                    for (int k = 1; k < TS; ++k) o[g] += red[k * D + vc_];
+                __syncthreads();
+            }
             const size_t prow = ((size_t)b * a.Hq + hk * G + g) * a.num_splits + split;
-            if (tid < D) a.part_o[prow * D + tid] = o[g];
+            if (vts == 0) a.part_o[prow * D + vc_] = o[g];
             if (tid == 0) a.part_ml[prow] = make_float2(m[g], l[g]);
         }
     }

@@ -96,10 +96,12 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
 // heads, then per head 16 threads find the tile maximum and turn the scores
 // into probabilities, and one channel per thread accumulates p * V for the
 // G heads.
-template <int D, int BITS>
+template <int D, int BITS, int GT>
 __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 {
+    // GT: the query heads per KV head when fixed at compile time, else 0
     constexpr int NG = D / kGroup, RB = D * BITS / 8, RW = RB / 4, TT = 256;
+    constexpr int GM = GT > 0 ? GT : 16;  // loop bound over heads
     __shared__ __align__(16) float q_lds[16][D];
     __shared__ float p_lds[16][TT];
     __shared__ float3 step[16];  // per head: (rescale of the old state, new reference, tile sum)
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         b = it.y;
         hk = kk % a.H;
     }
-    const int G = a.Hq / a.H;
+    const int G = GT > 0 ? GT : a.Hq / a.H;
     const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for empty chunks
@@ -132,9 +134,9 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
     const float* kscl = a.ks + head * a.cap * NG;
     const float* vscl = a.vs + head * a.cap * NG;
 
-    float m[16], l[16], o[16];
+    float m[GM], l[GM], o[GM];
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < GM; ++g) {
         m[g] = kNegInfB;
         l[g] = 0.0f;
         o[g] = 0.0f;
@@ -146,14 +148,25 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         const int n = min(TT, end - t0);
         // scores, one token per thread
         {
-            float acc[16];
+            float acc[GM];
 #pragma unroll
-            for (int g = 0; g < 16; ++g) acc[g] = 0.0f;
+            for (int g = 0; g < GM; ++g) acc[g] = 0.0f;
             if (tid < n) {
-                uint32_t kw[RW];  // the token's K row, read as words
+                uint32_t kw[RW];  // the token's K row, read 16 or 8 bytes at a time
                 const uint32_t* row = reinterpret_cast<const uint32_t*>(krows + (size_t)(t0 + tid) * RB);
+                if constexpr (RW % 4 == 0) {
 #pragma unroll
-                for (int k = 0; k < RW; ++k) kw[k] = row[k];
+                    for (int k = 0; k < RW; k += 4) {
+                        const uint4 w4 = *reinterpret_cast<const uint4*>(row + k);
+                        kw[k] = w4.x; kw[k + 1] = w4.y; kw[k + 2] = w4.z; kw[k + 3] = w4.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int k = 0; k < RW; k += 2) {
+                        const uint2 w2 = *reinterpret_cast<const uint2*>(row + k);
+                        kw[k] = w2.x; kw[k + 1] = w2.y;
+                    }
+                }
 #pragma unroll
                 for (int gr = 0; gr < NG; ++gr) {
                     const float s = kscl[(size_t)(t0 + tid) * NG + gr];
@@ -163,7 +176,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 #pragma unroll
                         for (int e = 0; e < 4; ++e) kd[e] = (float)code_in_words<BITS>(kw, i + e) * s;
 #pragma unroll
-                        for (int g = 0; g < 16; ++g) {
+                        for (int g = 0; g < GM; ++g) {
                             if (g < G) {
                                 const float4 qv = *reinterpret_cast<const float4*>(&q_lds[g][i]);
                                 acc[g] += qv.x * kd[0] + qv.y * kd[1] + qv.z * kd[2] + qv.w * kd[3];
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
                 for (int k = tid; k < n * NG; k += TT) vs_lds[k] = vscl[(size_t)t0 * NG + k];
             }
 #pragma unroll
-            for (int g = 0; g < 16; ++g)
+            for (int g = 0; g < GM; ++g)
                 if (g < G) p_lds[g][tid] = tid < n ? acc[g] : kNegInfB;
         }
         __syncthreads();
@@ -203,7 +216,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         }
         __syncthreads();
 #pragma unroll
-        for (int g = 0; g < 16; ++g) {
+        for (int g = 0; g < GM; ++g) {
             if (g < G) {
                 const float3 st = step[g];
                 l[g] = l[g] * st.x + st.z;
@@ -218,7 +231,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
             for (int j = vts; j < n; j += TS) {
                 const float vd = (float)code_in_words<BITS>(&v_lds[j * RW], vc_) * vs_lds[j * NG + gr];
 #pragma unroll
-                for (int g = 0; g < 16; ++g)
+                for (int g = 0; g < GM; ++g)
                     if (g < G) o[g] += p_lds[g][j] * vd;
             }
         }
@@ -226,7 +239,7 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
     }
     // the TS token subsets of each channel, added through LDS (p_lds is free)
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
+    for (int g = 0; g < GM; ++g) {
         if (g < G) {
             float* red = &p_lds[0][0];
             if (TS > 1) {
@@ -258,7 +271,13 @@ template <int D, int BITS>
 hipError_t launch_s(const SplitArgs& a, hipStream_t s)
 {
     dim3 grid(a.num_splits, a.H, a.B), block(256);
-    split_bits_kernel<D, BITS><<<grid, block, 0, s>>>(a);
+    switch (a.Hq / a.H) {
+    case 1: split_bits_kernel<D, BITS, 1><<<grid, block, 0, s>>>(a); break;
+    case 2: split_bits_kernel<D, BITS, 2><<<grid, block, 0, s>>>(a); break;
+    case 4: split_bits_kernel<D, BITS, 4><<<grid, block, 0, s>>>(a); break;
+    case 8: split_bits_kernel<D, BITS, 8><<<grid, block, 0, s>>>(a); break;
+    default: split_bits_kernel<D, BITS, 0><<<grid, block, 0, s>>>(a); break;
+    }
     return hipGetLastError();
 }
 

@@ -21,6 +21,7 @@ namespace otq {
 namespace {
 
 constexpr float kNegInfB = -__builtin_huge_valf();
+constexpr int kVecsPerWave = 8;  // vectors one wave of a bulk append quantises (one for short appends)
 
 // Signed b-bit code of element i of a row held as 32-bit words (the bits
 // may straddle two words).
@@ -41,7 +42,7 @@ template <int D, int BITS>
 __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
-    const int32_t* __restrict__ pos)
+    const int32_t* __restrict__ pos, int vpw)
 {
 #pragma clang fp contract(off)
     constexpr int E = D / 64, NG = D / kGroup, RB = D * BITS / 8, NWORD = RB / 4;
@@ -49,10 +50,15 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     static_assert(RB % 4 == 0, "whole words per row");
     __shared__ int8_t cs[4][D];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int vec = blockIdx.x * 4 + wave, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int p0 = pos[b];
+    // each wave takes vpw vectors in turn (the block's barrier count is the
+    // same for all its threads)
+    for (int iv = 0; iv < vpw; ++iv) {
+    const int vec = (blockIdx.x * 4 + wave) * vpw + iv;
     const bool is_v = vec >= n_new;
     const int tok = is_v ? vec - n_new : vec;
-    const int t = pos[b] + tok;
+    const int t = p0 + tok;
     // every thread reaches the barrier; inactive waves do no memory access
     const bool active = vec < 2 * n_new && t >= 0 && t < cap;
     const size_t head = (size_t)b * H + h;
@@ -76,18 +82,21 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
         }
     }
     __syncthreads();
-    if (!active) return;
-    const size_t row = head * cap + t;
-    if (lane % (kGroup / E) == 0) (is_v ? vs : ks)[row * NG + (lane * E) / kGroup] = sc;
-    if (lane < NWORD) {  // word w holds bits [32 w, 32 w + 32) of the row
-        uint32_t word = 0;
-        const int i0 = (32 * lane) / BITS, i1 = min((32 * lane + 31) / BITS, D - 1);
-        for (int i = i0; i <= i1; ++i) {
-            const uint32_t u = (uint32_t)cs[wave][i] & ((1u << BITS) - 1u);
-            const int off = i * BITS - 32 * lane;  // may be negative for the first element
-            word |= off >= 0 ? u << off : u >> -off;
+    if (active) {
+        const size_t row = head * cap + t;
+        if (lane % (kGroup / E) == 0) (is_v ? vs : ks)[row * NG + (lane * E) / kGroup] = sc;
+        if (lane < NWORD) {  // word w holds bits [32 w, 32 w + 32) of the row
+            uint32_t word = 0;
+            const int i0 = (32 * lane) / BITS, i1 = min((32 * lane + 31) / BITS, D - 1);
+            for (int i = i0; i <= i1; ++i) {
+                const uint32_t u = (uint32_t)cs[wave][i] & ((1u << BITS) - 1u);
+                const int off = i * BITS - 32 * lane;  // may be negative for the first element
+                word |= off >= 0 ? u << off : u >> -off;
+            }
+            reinterpret_cast<uint32_t*>((is_v ? vc : kc) + row * RB)[lane] = word;
         }
-        reinterpret_cast<uint32_t*>((is_v ? vc : kc) + row * RB)[lane] = word;
+    }
+    __syncthreads();  // cs is rewritten by the next vector
     }
 }
 
@@ -260,10 +269,11 @@ template <int D, int BITS>
 hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, int H, int cap,
                     uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, hipStream_t s)
 {
-    dim3 grid((2 * n_new + 3) / 4, H, B), block(256);
+    const int vpw = n_new >= 64 ? kVecsPerWave : 1;
+    dim3 grid((2 * n_new + 4 * vpw - 1) / (4 * vpw), H, B), block(256);
     quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
                                                           static_cast<const uint16_t*>(v), dtype, n_new,
-                                                          H, cap, kc, ks, vc, vs, pos);
+                                                          H, cap, kc, ks, vc, vs, pos, vpw);
     return hipGetLastError();
 }
 

@@ -125,10 +125,10 @@ typedef enum otq_rot_kind {
  * clamp(rint(x_i / s_g), -2^(b-1), 2^(b-1) - 1), otherwise as above; K and
  * V rows are plain little-endian bit streams, element i at bits [b i,
  * b i + b), two's complement: k_codes and v_codes uint8 [B][H][C][D*b/8],
- * scales as above.  Such caches take no rotation and no per-channel scale
- * (OTQ_EUNSUPPORTED), their split pass is the vector variant (any G <= 16),
- * and otq_sdpa_int4_decode_append returns OTQ_EUNSUPPORTED for them (append
- * with otq_quantize_append, then call otq_sdpa_int4_decode).
+ * scales as above.  Rotations and the per-channel scale apply as for int4.
+ * The split pass of such caches is the vector variant (any G <= 16), and
+ * otq_sdpa_int4_decode_append returns OTQ_EUNSUPPORTED for them (append with
+ * otq_quantize_append, then call otq_sdpa_int4_decode).
  */
 typedef struct otq_cache {
     int32_t batch;

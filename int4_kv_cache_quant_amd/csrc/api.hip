@@ -47,8 +47,6 @@ int check_cache(const otq_cache* c)
     if ((c->k_rot_signs || c->v_rot_signs) && c->rot_kind != OTQ_ROT_SRHT && c->rot_kind != OTQ_ROT_SRFT)
         return OTQ_EINVAL;
     if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 3 && c->code_bits != 4) return OTQ_EINVAL;
-    // 2- and 3-bit caches: unrotated, unscaled (the int4 path serves those options)
-    if (code_bits(c) != 4 && (c->k_rot_signs || c->v_rot_signs || c->k_chan_scale)) return OTQ_EUNSUPPORTED;
     return OTQ_OK;
 }
 
@@ -187,6 +185,8 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
         const hipError_t e = otq::launch_quantize_bits(
             k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
             code_bits(cache), cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, pos,
+            otq::BitsRot{cache->k_rot_signs, cache->rot_norm, rot_kind(cache), cache->k_chan_scale,
+                         cache->v_rot_signs},
             static_cast<hipStream_t>(stream));
         return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
     }

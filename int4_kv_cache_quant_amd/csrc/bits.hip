@@ -15,6 +15,8 @@
 // (m, l, o) partials as the int4 kernels, so the same combine merges them.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "quant_lane.hpp"
+#include "srft.hpp"
 
 namespace otq {
 
@@ -42,7 +44,8 @@ template <int D, int BITS>
 __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
-    const int32_t* __restrict__ pos, int vpw)
+    const int32_t* __restrict__ pos, int vpw, const float* __restrict__ signs, float rot_norm, int rot_kind,
+    const float* __restrict__ lam, const float* __restrict__ vsigns)
 {
 #pragma clang fp contract(off)
     constexpr int E = D / 64, NG = D / kGroup, RB = D * BITS / 8, NWORD = RB / 4;
@@ -52,6 +55,8 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
+    SrftLaneTw<D, E> stw;  // the FFT rotation's twiddles of this lane
+    if ((signs || vsigns) && rot_kind) stw.load(lane);
     // each wave takes vpw vectors in turn (the block's barrier count is the
     // same for all its threads)
     for (int iv = 0; iv < vpw; ++iv) {
@@ -68,10 +73,25 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
         float x[E];
         float a = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            x[e] = widen(src[e], dtype);
-            a = fmaxf(a, fabsf(x[e]));
+        for (int e = 0; e < E; ++e) x[e] = widen(src[e], dtype);
+        // the same rotation and channel scale as the int4 appends (K: signs,
+        // then lambda; V: its own signs)
+        const float* sg = is_v ? vsigns : signs;
+        if (sg) {
+            if (rot_kind) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = x[e] * sg[lane * E + e];
+                srft_signed<D, E>(x, rot_norm, lane, stw);
+            } else {
+                rotate_lane<D>(x, sg, rot_norm, lane);
+            }
         }
+        if (!is_v && lam) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) x[e] = x[e] * lam[lane * E + e];
+        }
+#pragma unroll
+        for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
         a = group_max<kGroup / E>(a);  // exact in any order
         sc = a / qmax;                 // correctly rounded IEEE division
 #pragma unroll
@@ -134,8 +154,53 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
     const int end = min(start + a.chunk, len);
 
     const uint16_t* qsrc = static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk * G) * D;
-    for (int i = tid; i < G * D; i += TT) q_lds[i / D][i % D] = widen(qsrc[i], a.dtype) * a.qscale;
+    for (int i = tid; i < G * D; i += TT) {
+        float x = widen(qsrc[i], a.dtype) * a.qscale;
+        if (a.signs) x *= a.signs[i % D];
+        q_lds[i / D][i % D] = x;
+    }
     __syncthreads();
+    // the query rotated as K is (then rot_norm), and divided by K's channel scale
+    if (a.signs) {
+        if (a.rot_kind) {  // FFT stages over the (even, odd) complex pairs
+            for (int h = D / 4; h >= 1; h >>= 1) {
+                for (int i = tid; i < G * D / 4; i += TT) {
+                    const int hh = i / (D / 4), kk = i % (D / 4);
+                    const int j = (kk / h) * 2 * h + (kk % h);
+                    const int u = (kk % h) * (64 / h);
+                    const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                    const float ar = q_lds[hh][2 * j], ai = q_lds[hh][2 * j + 1];
+                    const float br = q_lds[hh][2 * (j + h)], bi = q_lds[hh][2 * (j + h) + 1];
+                    const float dr = ar - br, di = ai - bi;
+                    q_lds[hh][2 * j] = ar + br;
+                    q_lds[hh][2 * j + 1] = ai + bi;
+                    q_lds[hh][2 * (j + h)] = dr * wr - di * wi;
+                    q_lds[hh][2 * (j + h) + 1] = dr * wi + di * wr;
+                }
+                __syncthreads();
+            }
+        } else {  // Walsh-Hadamard butterflies
+            for (int h = 1; h < D; h <<= 1) {
+                for (int i = tid; i < G * D / 2; i += TT) {
+                    const int hh = i / (D / 2), kk = i % (D / 2);
+                    const int j = (kk / h) * 2 * h + (kk % h);
+                    const float lo = q_lds[hh][j], hi = q_lds[hh][j + h];
+                    q_lds[hh][j] = lo + hi;
+                    q_lds[hh][j + h] = lo - hi;
+                }
+                __syncthreads();
+            }
+        }
+    }
+    if (a.signs || a.lam) {
+        for (int i = tid; i < G * D; i += TT) {
+            float x = q_lds[i / D][i % D];
+            if (a.signs) x *= a.rot_norm;
+            if (a.lam) x /= a.lam[i % D];
+            q_lds[i / D][i % D] = x;
+        }
+        __syncthreads();
+    }
 
     const size_t head = (size_t)b * a.H + hk;
     const uint8_t* krows = a.kc + head * a.cap * RB;
@@ -267,13 +332,15 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 
 template <int D, int BITS>
 hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, int H, int cap,
-                    uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, hipStream_t s)
+                    uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, const BitsRot& r,
+                    hipStream_t s)
 {
     const int vpw = n_new >= 64 ? kVecsPerWave : 1;
     dim3 grid((2 * n_new + 4 * vpw - 1) / (4 * vpw), H, B), block(256);
     quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
                                                           static_cast<const uint16_t*>(v), dtype, n_new,
-                                                          H, cap, kc, ks, vc, vs, pos, vpw);
+                                                          H, cap, kc, ks, vc, vs, pos, vpw, r.signs,
+                                                          r.rot_norm, r.rot_kind, r.lam, r.vsigns);
     return hipGetLastError();
 }
 
@@ -295,15 +362,15 @@ hipError_t launch_s(const SplitArgs& a, hipStream_t s)
 
 hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                const int32_t* pos, hipStream_t s)
+                                const int32_t* pos, const BitsRot& r, hipStream_t s)
 {
     switch (D * 10 + bits) {
-    case 642: return launch_q<64, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
-    case 643: return launch_q<64, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
-    case 1282: return launch_q<128, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
-    case 1283: return launch_q<128, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
-    case 2562: return launch_q<256, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
-    case 2563: return launch_q<256, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, s);
+    case 642: return launch_q<64, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 643: return launch_q<64, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 1282: return launch_q<128, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 1283: return launch_q<128, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 2562: return launch_q<256, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 2563: return launch_q<256, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -44,9 +44,18 @@ struct SplitArgs {
 
 // 2- and 3-bit codes (plain bit-stream rows for K and V): the append and the
 // split pass; the combine is shared.
+// The options of a b-bit append: K's rotation signs and kind, its channel
+// scale, V's rotation signs (each null when off).
+struct BitsRot {
+    const float* signs;
+    float rot_norm;
+    int rot_kind;
+    const float* lam;
+    const float* vsigns;
+};
 hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                const int32_t* pos, hipStream_t stream);
+                                const int32_t* pos, const BitsRot& rot, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
 
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.

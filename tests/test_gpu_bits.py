@@ -132,3 +132,48 @@ def test_bits_full_workload_3(bits):
     ma, rel = errors(out.cpu().numpy().reshape(-1, w.D)[rows], ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("opts", ["srht", "srft+lam", "srht+vrot", "srft+vrot+lam"])
+@pytest.mark.parametrize("G,D", [(8, 128), (2, 64), (1, 256)])
+def test_bits_with_rotations_and_scale(bits, opts, G, D):
+    """b-bit caches with K rotated (either kind), K's channel scale and V
+    rotated: codes bit-exact, outputs within tolerance (the combine brings a
+    rotated V's rows back)."""
+    B, Hkv, cap = 2, 2, 320
+    lens = [320, 99]
+    kind = "srft" if "srft" in opts else "srht"
+    say(f"bits options b={bits} opts={opts} G={G} D={D}")
+    k, v = _kv(B, Hkv, cap, D, torch.bfloat16, seed=bits * 31 + G + D + len(opts))
+    g = torch.Generator().manual_seed(G * D + bits)
+    q = torch.randn((B, G * Hkv, D), generator=g).to(torch.bfloat16)
+    sk = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0)
+    sv = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if "vrot" in opts else None
+    lam = torch.exp2(torch.rand(D, generator=g) * 4.0 - 2.0) if "lam" in opts else None
+    cache = otq.Int4KVCache(B, Hkv, D, cap, device=DEV, code_bits=bits, rot_signs=sk.to(DEV), rot_kind=kind,
+                            chan_scale=None if lam is None else lam.to(DEV),
+                            v_rot_signs=None if sv is None else sv.to(DEV))
+    for t0 in range(0, cap, 100):
+        pos = torch.full((B,), t0, dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t0:t0 + 100].to(DEV).contiguous(), v[:, :, t0:t0 + 100].to(DEV).contiguous(), pos)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    scale = 1.0 / math.sqrt(D)
+    out = cache.decode(q.to(DEV), lens_t, max(lens), scale)
+    torch.cuda.synchronize()
+    rn = cache.rot_norm
+    lam_np = None if lam is None else lam.numpy()
+    sv_np = None if sv is None else sv.numpy()
+    kc, ks = oracle.quantize(to_bits(k), "bf16", signs=sk.numpy(), rot_norm=rn, chan_scale=lam_np, rot_kind=kind,
+                             code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v), "bf16", signs=sv_np, rot_norm=rn, rot_kind=kind, code_bits=bits)
+    assert np.array_equal(cache.k_codes.cpu().numpy(), kc)
+    assert np.array_equal(cache.k_scales.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(cache.v_codes.cpu().numpy(), vc)
+    assert np.array_equal(cache.v_scales.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale, signs=sk.numpy(),
+                      rot_norm=rn, threads=8, chan_scale=lam_np, v_signs=sv_np, rot_kind=kind, code_bits=bits)
+    ma, rel = errors(out.cpu().numpy(), ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+

@@ -17,12 +17,18 @@
  *
  * Conventions for every entry point:
  *  - All tensor pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing.  Its only state is one device word per GPU (set up
+ *    by the first call on that GPU) that collects device-side contract
+ *    violations for otq_last_device_error.
  *  - Descriptor structs (otq_cache, otq_plan) live in HOST memory and are
  *    read during the call only.
- *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
- *    asynchronously; the return value reports only what the host can check
- *    (arguments) and launch failures.
+ *  - `stream` is a hipStream_t (NULL = the default stream) of the current
+ *    device.  Work is enqueued asynchronously; the return value reports only
+ *    what the host can check (arguments) and launch failures.
+ *  - Device-side preconditions (positions and lengths inside the cache) are
+ *    the caller's contract.  A kernel that meets a value outside it clamps or
+ *    skips as documented per call, never touches memory outside the cache,
+ *    and records the violation for otq_last_device_error.
  *  - No entry point throws; all return an otq_status (0 = OTQ_OK).
  *  - Argument errors are detected on the host before any HIP call is made.
  */
@@ -36,7 +42,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 5
+#define OTQ_ABI_VERSION 6
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -156,16 +162,34 @@ int otq_abi_version(void);
 
 /*
  * Byte sizes of one codes array and one scales array of a cache with these
- * dimensions (K and V have the same sizes).  Returns OTQ_OK, or
- * OTQ_EINVAL / OTQ_EUNSUPPORTED for dimensions the cache does not support.
- * Pure host arithmetic.
+ * dimensions and code width (code_bits 4 or 0 for int4, 2 or 3; K and V
+ * have the same sizes): codes B*H*C*D*code_bits/8, scales B*H*C*(D/32)*4.
+ * Returns OTQ_OK, or OTQ_EINVAL / OTQ_EUNSUPPORTED for dimensions or a code
+ * width the cache does not support.  Pure host arithmetic.
  */
 int otq_cache_array_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t capacity, size_t *codes_bytes, size_t *scales_bytes);
+                          int32_t capacity, int32_t code_bits, size_t *codes_bytes,
+                          size_t *scales_bytes);
 
 /* Total bytes of the four arrays (0 for unsupported dimensions). */
 size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
-                       int32_t capacity);
+                       int32_t capacity, int32_t code_bits);
+
+/* Bits of the device error word (otq_last_device_error). */
+#define OTQ_DEVERR_POS 1u  /* otq_quantize_append met pos[b] < 0 or pos[b] + n_new > capacity
+                              (the tokens outside [0, capacity) were skipped) */
+#define OTQ_DEVERR_LENS 2u /* a decode call met lens[b] < 0 or lens[b] > max_len
+                              (it was clamped to [0, max_len]) */
+
+/*
+ * The device-side contract violations (a bit-or of OTQ_DEVERR_*) recorded on
+ * the current device since the previous call, which clears them.  The word
+ * is read and cleared in one atomic step on `stream` after the work queued
+ * before it; the call then waits for the stream.  Returns OTQ_OK, OTQ_EINVAL
+ * (flags NULL) or OTQ_EDEVICE.  The word is shared by every call on the
+ * device, whatever its stream.
+ */
+int otq_last_device_error(void *stream, uint32_t *flags);
 
 /*
  * Quantise n_new new K and V vectors per (sequence, KV head) and store them
@@ -176,7 +200,8 @@ size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
  *         16-byte aligned (read 8 channels at a time).
  *  pos    device int32 [B].  Contract: 0 <= pos[b] and
  *         pos[b] + n_new <= capacity.  Tokens that fall outside
- *         [0, capacity) are skipped (never written out of bounds).
+ *         [0, capacity) are skipped (never written out of bounds), and the
+ *         violation sets OTQ_DEVERR_POS.
  *  Codes and scales of every token not in the range are left untouched,
  *  including the neighbour that shares a V byte with a new token.
  *  Host errors: OTQ_EINVAL (null pointer, misaligned k or v, n_new < 1, a
@@ -230,15 +255,25 @@ size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache *cache, int
  * with K^ = code * s (V^ likewise), kv(h) = h / (num_q_heads / H), q' = q
  * rotated as K was when cache->k_rot_signs != NULL.  lens[b] == 0 gives 0.
  *
- *  q        device [B][Hq][D] fp16/bf16 (dtype).
- *  lens     device int32 [B]; values are clamped to [0, max_len].
+ *  q        device [B][Hq][D] fp16/bf16 (dtype), 16-byte aligned; any finite
+ *           values (the MFMA variant scales each row by a power of two
+ *           before its fp16 products).
+ *  lens     device int32 [B]; values are clamped to [0, max_len] (a value
+ *           outside sets OTQ_DEVERR_LENS).  Cache slots at or past lens[b]
+ *           are never read into the result, whatever they hold.
  *  max_len  host bound on lens, 1..capacity; sizes the split grid.
- *  out      device fp32 [B][Hq][D].
+ *  out      device fp32 [B][Hq][D], 16-byte aligned.
  *  workspace device scratch of at least otq_sdpa_workspace_bytes(...) bytes
  *           (or plan->workspace_bytes); contents need no initialisation.
- * Host errors: OTQ_EINVAL, OTQ_EUNSUPPORTED (head_dim, dtype, G > 16, or a
- * forced variant that does not support G), OTQ_ECAPACITY (max_len >
- * capacity), OTQ_EWORKSPACE.
+ * Host errors: OTQ_EINVAL (null or misaligned pointers, Hq % H != 0, a
+ * non-finite scale), OTQ_EUNSUPPORTED (head_dim, dtype, G > 16, or a forced
+ * variant that does not support G), OTQ_ECAPACITY (max_len > capacity),
+ * OTQ_EWORKSPACE.
+ *
+ * Value range of the MFMA variant: the value operand p * s_v * 2^E is kept
+ * inside fp16's range by a power of two E that follows the largest V scale
+ * seen (over the whole fp32 range of scales), so V of any finite magnitude
+ * keeps full precision.
  */
 int otq_sdpa_int4_decode(const void *q, int32_t dtype, int32_t num_q_heads,
                          const otq_cache *cache, const int32_t *lens, int32_t max_len,
@@ -266,9 +301,11 @@ int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_hea
  *
  *  k_new, v_new  device [B][Hkv][D] fp16/bf16 (dtype): the new token's K, V.
  *  plan          from otq_sdpa_plan, or NULL for the default plan.
- * Sequences with lens[b] == 0 append nothing and get zeros.  Other arguments,
- * contracts and errors as for otq_sdpa_int4_decode_planned; the cache must
- * hold tokens [0, lens[b] - 1) already.
+ * Sequences with lens[b] == 0 append nothing and get zeros.  lens[b] is
+ * clamped to [0, max_len] before anything else, by every kernel of the
+ * call alike (so lens[b] > max_len appends at max_len - 1).  Other
+ * arguments, contracts and errors as for otq_sdpa_int4_decode_planned; the
+ * cache must hold tokens [0, lens[b] - 1) already.
  */
 int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_new,
                                 int32_t dtype, int32_t num_q_heads, const otq_cache *cache,
@@ -287,9 +324,10 @@ int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_
  *   part_ml fp32 [B][Hq][num_splits][2]      at byte offset
  *           round_up(B*Hq*num_splits*D*4, 256)
  * where split s covers tokens [s*chunk, min((s+1)*chunk, lens[b])), m is the
- * split's softmax reference in log2 units (score * log2(e)): at least its
- * largest score, and at most 4 above it, l = sum 2^(S*log2e - m) and
- * o = sum 2^(S*log2e - m) V^ (any such m gives the same merged result).
+ * split's reference in log2 units (score * log2(e)), l = sum 2^(S*log2e - m)
+ * and o = sum 2^(S*log2e - m) V^; the kernel chooses m (near the largest
+ * score, shifted by a power of two that keeps o in range) and any m gives
+ * the same merged result.
  * Splits with s*chunk >= lens[b] are not
  * written.  otq_sdpa_lse_combine merges the first ceil(lens[b]/chunk)
  * partials of each row into out.  Arguments and errors as for

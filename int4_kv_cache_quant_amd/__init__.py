@@ -26,8 +26,11 @@ OTQ_GROUP, OTQ_TILE = 32, 32
 OTQ_ROT_SRHT, OTQ_ROT_SRFT = 0, 1
 ROT_KINDS = {"srht": OTQ_ROT_SRHT, "srft": OTQ_ROT_SRFT}
 
+OTQ_DEVERR_POS, OTQ_DEVERR_LENS = 1, 2
+
 EXPORTED = [
     "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
+    "otq_last_device_error",
     "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
     "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned", "otq_sdpa_int4_decode_append",
     "otq_sdpa_int4_split", "otq_sdpa_lse_combine",
@@ -76,10 +79,12 @@ def lib():
     L.otq_status_str.restype = ctypes.c_char_p
     L.otq_abi_version.argtypes = []
     L.otq_abi_version.restype = ctypes.c_int
-    L.otq_cache_array_bytes.argtypes = [I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(S)]
+    L.otq_cache_array_bytes.argtypes = [I, I, I, I, I, ctypes.POINTER(S), ctypes.POINTER(S)]
     L.otq_cache_array_bytes.restype = ctypes.c_int
-    L.otq_cache_bytes.argtypes = [I, I, I, I]
+    L.otq_cache_bytes.argtypes = [I, I, I, I, I]
     L.otq_cache_bytes.restype = S
+    L.otq_last_device_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
+    L.otq_last_device_error.restype = ctypes.c_int
     L.otq_quantize_append.argtypes = [P, P, I, I, CP, P, P]
     L.otq_quantize_append.restype = ctypes.c_int
     L.otq_sdpa_plan.argtypes = [I, CP, I, I, I, ctypes.POINTER(otq_plan)]
@@ -131,15 +136,23 @@ def dtype_code(dt):
 
 
 # ---------------------------------------------------------------- raw ABI
-def otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity):
+def otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity, code_bits=4):
     cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
-    _check(lib().otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity,
+    _check(lib().otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity, code_bits,
                                        ctypes.byref(cb), ctypes.byref(sb)), "otq_cache_array_bytes")
     return cb.value, sb.value
 
 
-def otq_cache_bytes(batch, num_kv_heads, head_dim, capacity):
-    return lib().otq_cache_bytes(batch, num_kv_heads, head_dim, capacity)
+def otq_cache_bytes(batch, num_kv_heads, head_dim, capacity, code_bits=4):
+    return lib().otq_cache_bytes(batch, num_kv_heads, head_dim, capacity, code_bits)
+
+
+def otq_last_device_error(stream=None):
+    """Device-side contract violations (OTQ_DEVERR_* bits) recorded on the
+    current device since the previous call (which this one clears)."""
+    flags = ctypes.c_uint32()
+    _check(lib().otq_last_device_error(_stream(stream), ctypes.byref(flags)), "otq_last_device_error")
+    return flags.value
 
 
 def otq_quantize_append(k, v, cache_desc, pos, n_new=None, dtype=None, stream=None, check=True):
@@ -247,22 +260,21 @@ class Int4KVCache:
 
     def __init__(self, batch, num_kv_heads, head_dim, capacity, device="cuda", rot_signs=None,
                  chan_scale=None, v_rot_signs=None, rot_kind="srht", code_bits=4):
-        cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity)
+        # the library sizes the arrays; the tensors only give them a shape
+        cb, sb = otq_cache_array_bytes(batch, num_kv_heads, head_dim, capacity, code_bits)
         self.shape = (batch, num_kv_heads, head_dim, capacity)
         self.code_bits = code_bits
-        g = head_dim // OTQ_GROUP
-        self.k_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
-        self.v_scales = torch.zeros((batch, num_kv_heads, capacity, g), dtype=torch.float32, device=device)
-        if code_bits == 4:
-            self.k_codes = torch.zeros((batch, num_kv_heads, capacity, head_dim // 2), dtype=torch.uint8,
-                                       device=device)
-            self.v_codes = torch.zeros((batch, num_kv_heads, capacity // OTQ_TILE, 16 * head_dim),
-                                       dtype=torch.uint8, device=device)
-            assert self.k_codes.numel() == cb and self.k_scales.numel() * 4 == sb
-        else:  # plain bit-stream rows of D * b / 8 bytes for K and V
-            rb = head_dim * code_bits // 8
-            self.k_codes = torch.zeros((batch, num_kv_heads, capacity, rb), dtype=torch.uint8, device=device)
-            self.v_codes = torch.zeros((batch, num_kv_heads, capacity, rb), dtype=torch.uint8, device=device)
+        rows = batch * num_kv_heads * capacity
+        self.k_scales = torch.zeros(sb // 4, dtype=torch.float32, device=device).view(
+            batch, num_kv_heads, capacity, sb // 4 // rows)
+        self.v_scales = torch.zeros_like(self.k_scales)
+        if code_bits == 4:  # V in tiles of 32 tokens
+            self.k_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(batch, num_kv_heads, capacity, -1)
+            self.v_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(
+                batch, num_kv_heads, capacity // OTQ_TILE, -1)
+        else:  # plain bit-stream rows for K and V
+            self.k_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(batch, num_kv_heads, capacity, -1)
+            self.v_codes = torch.zeros_like(self.k_codes)
         self.rot_signs = None if rot_signs is None else rot_signs.to(device=device, dtype=torch.float32).contiguous()
         self.rot_kind = ROT_KINDS[rot_kind]
         n = head_dim // 2 if self.rot_kind == OTQ_ROT_SRFT else head_dim

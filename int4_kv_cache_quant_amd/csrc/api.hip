@@ -8,10 +8,55 @@
 #include <limits.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/otq.h"
 #include "kernels.hpp"
 
+// The device error word of each GPU: [0] collects the kernels' contract
+// violations (OTQ_DEVERR_*), [1] receives the value otq_last_device_error
+// takes.  Host code uses the address hipGetSymbolAddress gives per device,
+// never this name (which on the host is only a stand-in for the symbol).
+__device__ unsigned otq_device_error_word[2];
+
 namespace {
+
+// Reads and clears the live word in one atomic step.
+__global__ void take_device_error_kernel(unsigned* w)
+{
+    w[1] = __hip_atomic_exchange(&w[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Per-device set-up, done once per device on the first call that launches
+// work there (with that device current).
+constexpr int kMaxDevices = 64;
+struct DeviceState {
+    std::once_flag once;
+    hipError_t rc = hipSuccess;
+    unsigned* err = nullptr;
+};
+DeviceState g_devices[kMaxDevices];
+
+// The current device's state, or null if it could not be set up.
+DeviceState* device_state()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    DeviceState& d = g_devices[dev];
+    std::call_once(d.once, [&d] {
+        void* p = nullptr;
+        d.rc = hipGetSymbolAddress(&p, HIP_SYMBOL(otq_device_error_word));
+        d.err = static_cast<unsigned*>(p);
+    });
+    return d.rc == hipSuccess && d.err ? &d : nullptr;
+}
+
+// The current device's error word for a launch (null: OTQ_EDEVICE).
+unsigned* error_word()
+{
+    DeviceState* d = device_state();
+    return d ? d->err : nullptr;
+}
 
 constexpr int kChunkAlign = 128;  // 4 waves x 32-token tiles
 constexpr int kMaxChunk = 8192;  // measured: larger chunks starve the grid on ragged batches
@@ -153,22 +198,39 @@ const char* otq_status_str(int status)
 
 int otq_abi_version(void) { return OTQ_ABI_VERSION; }
 
-int otq_cache_array_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, size_t* codes_bytes,
-                          size_t* scales_bytes)
+int otq_cache_array_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, int32_t code_bits,
+                          size_t* codes_bytes, size_t* scales_bytes)
 {
     const int rc = check_dims(B, H, D, cap);
     if (rc != OTQ_OK) return rc;
+    const int bits = code_bits == 0 ? 4 : code_bits;
+    if (bits != 2 && bits != 3 && bits != 4) return OTQ_EINVAL;
     const size_t n = (size_t)B * H * cap;
-    if (codes_bytes) *codes_bytes = n * (size_t)(D / 2);
+    if (codes_bytes) *codes_bytes = n * (size_t)(D * bits / 8);
     if (scales_bytes) *scales_bytes = n * (size_t)(D / OTQ_GROUP) * sizeof(float);
     return OTQ_OK;
 }
 
-size_t otq_cache_bytes(int32_t B, int32_t H, int32_t D, int32_t cap)
+size_t otq_cache_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, int32_t code_bits)
 {
     size_t cb = 0, sb = 0;
-    if (otq_cache_array_bytes(B, H, D, cap, &cb, &sb) != OTQ_OK) return 0;
+    if (otq_cache_array_bytes(B, H, D, cap, code_bits, &cb, &sb) != OTQ_OK) return 0;
     return 2 * (cb + sb);
+}
+
+int otq_last_device_error(void* stream, uint32_t* flags)
+{
+    if (!flags) return OTQ_EINVAL;
+    unsigned* w = error_word();
+    if (!w) return OTQ_EDEVICE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    take_device_error_kernel<<<1, 1, 0, s>>>(w);
+    if (hipGetLastError() != hipSuccess) return OTQ_EDEVICE;
+    unsigned v = 0;
+    if (hipMemcpyAsync(&v, w + 1, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess) return OTQ_EDEVICE;
+    if (hipStreamSynchronize(s) != hipSuccess) return OTQ_EDEVICE;
+    *flags = v;
+    return OTQ_OK;
 }
 
 int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_new,
@@ -181,19 +243,21 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     if ((((uintptr_t)k) & 15) != 0 || (((uintptr_t)v) & 15) != 0) return OTQ_EINVAL;
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (n_new > cache->capacity) return OTQ_ECAPACITY;
+    unsigned* err = error_word();
+    if (!err) return OTQ_EDEVICE;
     if (code_bits(cache) != 4) {
         const hipError_t e = otq::launch_quantize_bits(
             k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
             code_bits(cache), cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, pos,
             otq::BitsRot{cache->k_rot_signs, cache->rot_norm, rot_kind(cache), cache->k_chan_scale,
                          cache->v_rot_signs},
-            static_cast<hipStream_t>(stream));
+            err, static_cast<hipStream_t>(stream));
         return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
     }
     const hipError_t e = otq::launch_quantize_append(
         k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
         cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
-        cache->rot_norm, rot_kind(cache), cache->k_chan_scale, cache->v_rot_signs, pos,
+        cache->rot_norm, rot_kind(cache), cache->k_chan_scale, cache->v_rot_signs, pos, err,
         static_cast<hipStream_t>(stream));
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
@@ -273,6 +337,8 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
                                           ml_offset(cache, num_q_heads, chk));
     a.lens_offset = lens_offset;
     a.items = nullptr;
+    a.err = error_word();
+    if (!a.err) return OTQ_EDEVICE;
     if (ordered_batch(a.B)) {
         const int groups = chk.variant == OTQ_VARIANT_MFMA
                                ? a.H / otq::split_mfma_heads_per_wave(D, num_q_heads / a.H, a.H)
@@ -280,7 +346,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
         int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
                                               order_offset(cache, num_q_heads, chk));
         if (otq::launch_split_order(lens, lens_offset, max_len, chk.chunk, chk.num_splits, groups, a.B,
-                                    items, s) != hipSuccess)
+                                    items, a.err, s) != hipSuccess)
             return OTQ_EDEVICE;
         a.items = items;
     }
@@ -323,11 +389,16 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.lam = cache->k_chan_scale;
     a.vsigns = cache->v_rot_signs;
     a.qscale = scale * otq::kLog2eHost;
+    a.err = error_word();
+    if (!a.err) return OTQ_EDEVICE;
     const hipError_t e = otq::launch_lse_combine(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
 }
 
 bool finite(float x) { return x == x && x != __builtin_huge_valf() && x != -__builtin_huge_valf(); }
+
+// q is read 8 elements (16 bytes) at a time and out written 4 floats at a time.
+bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
 
 }  // namespace
 
@@ -340,7 +411,7 @@ int otq_sdpa_int4_split(const void* q, int32_t dtype, int32_t num_q_heads, const
     otq_plan chk;
     int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
     if (rc != OTQ_OK) return rc;
-    if (!q || !lens) return OTQ_EINVAL;
+    if (!q || !lens || !aligned16(q)) return OTQ_EINVAL;
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
@@ -355,7 +426,7 @@ int otq_sdpa_lse_combine(int32_t num_q_heads, const otq_cache* cache, const int3
     otq_plan chk;
     int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
     if (rc != OTQ_OK) return rc;
-    if (!lens || !out) return OTQ_EINVAL;
+    if (!lens || !out || !aligned16(out)) return OTQ_EINVAL;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
     return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out,
                        static_cast<hipStream_t>(stream));
@@ -369,7 +440,7 @@ int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_hea
     otq_plan chk;
     int rc = check_plan(num_q_heads, cache, max_len, plan, &chk);
     if (rc != OTQ_OK) return rc;
-    if (!q || !lens || !out) return OTQ_EINVAL;
+    if (!q || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
@@ -388,7 +459,7 @@ int otq_sdpa_int4_decode_append(const void* q, const void* k_new, const void* v_
     int rc = plan ? check_plan(num_q_heads, cache, max_len, plan, &chk)
                   : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &chk);
     if (rc != OTQ_OK) return rc;
-    if (!q || !k_new || !v_new || !lens || !out) return OTQ_EINVAL;
+    if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
     if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;

@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
     const int32_t* __restrict__ pos, int vpw, const float* __restrict__ signs, float rot_norm, int rot_kind,
-    const float* __restrict__ lam, const float* __restrict__ vsigns)
+    const float* __restrict__ lam, const float* __restrict__ vsigns, unsigned* __restrict__ err)
 {
 #pragma clang fp contract(off)
     constexpr int E = D / 64, NG = D / kGroup, RB = D * BITS / 8, NWORD = RB / 4;
@@ -55,6 +55,8 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
+    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
+        report_error(err, kErrPos);  // the tokens outside [0, cap) are skipped below
     SrftLaneTw<D, E> stw;  // the FFT rotation's twiddles of this lane
     if ((signs || vsigns) && rot_kind) stw.load(lane);
     // each wave takes vpw vectors in turn (the block's barrier count is the
@@ -148,7 +150,11 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
         hk = kk % a.H;
     }
     const int G = GT > 0 ? GT : a.Hq / a.H;
-    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
+    // lens clamped to [0, max_len] first, as the combine does, then the
+    // fused append's token (lens_offset = 1) left to the combine
+    const int raw_len = a.lens[b];
+    const int len = max(min(max(raw_len, 0), a.max_len) - a.lens_offset, 0);
+    if (tid == 0 && split == 0 && hk == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for empty chunks
     const int end = min(start + a.chunk, len);
@@ -333,14 +339,14 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
 template <int D, int BITS>
 hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, int H, int cap,
                     uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, const BitsRot& r,
-                    hipStream_t s)
+                    unsigned* err, hipStream_t s)
 {
     const int vpw = n_new >= 64 ? kVecsPerWave : 1;
     dim3 grid((2 * n_new + 4 * vpw - 1) / (4 * vpw), H, B), block(256);
     quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
                                                           static_cast<const uint16_t*>(v), dtype, n_new,
                                                           H, cap, kc, ks, vc, vs, pos, vpw, r.signs,
-                                                          r.rot_norm, r.rot_kind, r.lam, r.vsigns);
+                                                          r.rot_norm, r.rot_kind, r.lam, r.vsigns, err);
     return hipGetLastError();
 }
 
@@ -362,15 +368,15 @@ hipError_t launch_s(const SplitArgs& a, hipStream_t s)
 
 hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                const int32_t* pos, const BitsRot& r, hipStream_t s)
+                                const int32_t* pos, const BitsRot& r, unsigned* err, hipStream_t s)
 {
     switch (D * 10 + bits) {
-    case 642: return launch_q<64, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
-    case 643: return launch_q<64, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
-    case 1282: return launch_q<128, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
-    case 1283: return launch_q<128, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
-    case 2562: return launch_q<256, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
-    case 2563: return launch_q<256, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, s);
+    case 642: return launch_q<64, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
+    case 643: return launch_q<64, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
+    case 1282: return launch_q<128, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
+    case 1283: return launch_q<128, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
+    case 2562: return launch_q<256, 2>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
+    case 2563: return launch_q<256, 3>(k, v, dtype, n_new, B, H, cap, kc, ks, vc, vs, pos, r, err, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -2,8 +2,9 @@
 // the step's new token appended.
 //
 // Each split s of a (sequence, query head) row carries (m_s, l_s, o_s): its
-// softmax reference (log2 domain; any value at or above its largest score),
-// its sum of 2^(S_t - m_s), and its unnormalised value sum.  The exact
+// softmax reference (log2 domain; any value the split pass chose to keep l_s
+// and o_s in fp32's range), its sum of 2^(S_t - m_s), and its unnormalised
+// value sum with the same weights.  The exact
 // softmax over the union of splits is
 //   M = max_s m_s,  L = sum_s l_s 2^(m_s - M),  out = sum_s 2^(m_s - M) o_s / L
 // evaluated in fp32 (the high-precision accumulation the zingnex
@@ -152,7 +153,10 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             xf[k] = *reinterpret_cast<const float4*>(po + (size_t)sk * D);
         }
     }
-    const int len = min(max(a.lens[b], 0), a.max_len);
+    const int raw_len = a.lens[b];
+    const int len = min(max(raw_len, 0), a.max_len);
+    if (tid == 0 && blockIdx.y == 0 && row % a.Hq == 0 && (raw_len < 0 || raw_len > a.max_len))
+        report_error(a.err, kErrLens);
     const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
     const int ns = (nsplit_tok + a.chunk - 1) / a.chunk;
     if constexpr (APPEND) pos = len - 1;

@@ -152,6 +152,18 @@ __device__ __forceinline__ float nib_f32(uint32_t w)
     return (float)(((int32_t)(w << (28 - 4 * K))) >> 28);
 }
 
+// ------------------------------------------------------------ contract violations
+// Bits of the library's device error word (otq_last_device_error): set with
+// a device-scope atomic or, only on the rare path where a kernel meets an
+// argument outside the caller's contract (the kernel then clamps or skips as
+// documented and carries on).
+constexpr unsigned kErrPos = 1u;   // an append position outside [0, capacity - n_new]
+constexpr unsigned kErrLens = 2u;  // a length outside [0, max_len]
+__device__ __forceinline__ void report_error(unsigned* err, unsigned flag)
+{
+    __hip_atomic_fetch_or(err, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __device__ __forceinline__ float exp2_approx(float x)
 {
     return __builtin_amdgcn_exp2f(x);  // v_exp_f32; exp2(-inf) = 0

@@ -8,10 +8,12 @@ namespace otq {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
+// err: the library's device error word (see common.hpp), in every launcher.
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                   const float* signs, float rot_norm, int rot_kind, const float* lam,
-                                  const float* vsigns, const int32_t* pos, hipStream_t stream);
+                                  const float* vsigns, const int32_t* pos, unsigned* err,
+                                  hipStream_t stream);
 
 // Split pass arguments shared by both variants.
 struct SplitArgs {
@@ -40,6 +42,7 @@ struct SplitArgs {
     // 1 when the token at lens[b] - 1 is appended by the combine of the same
     // call (the split pass then covers [0, lens[b] - 1)), else 0.
     int lens_offset;
+    unsigned* err;  // the device error word
 };
 
 // 2- and 3-bit codes (plain bit-stream rows for K and V): the append and the
@@ -55,7 +58,7 @@ struct BitsRot {
 };
 hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
-                                const int32_t* pos, const BitsRot& rot, hipStream_t stream);
+                                const int32_t* pos, const BitsRot& rot, unsigned* err, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
 
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
@@ -65,7 +68,7 @@ constexpr int kOrderMaxBatch = 256;
 // Writes items[S * groups * B] for batches of 2..kOrderMaxBatch sequences
 // (see SplitArgs::items).
 hipError_t launch_split_order(const int32_t* lens, int lens_offset, int max_len, int chunk, int S,
-                              int groups, int B, int2* items, hipStream_t stream);
+                              int groups, int B, int2* items, unsigned* err, hipStream_t stream);
 hipError_t launch_split_mfma(const SplitArgs& a, hipStream_t stream);
 bool split_vector_supports(int D, int G);
 bool split_mfma_supports(int D, int G);
@@ -99,6 +102,7 @@ struct CombineArgs {
     const float* vsigns;    // V's rotation signs [D] (same rot_norm), or null: the
                             // output is brought back to the original basis
     float qscale;           // softmax scale * log2(e)
+    unsigned* err;          // the device error word
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
 

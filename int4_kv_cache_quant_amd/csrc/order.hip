@@ -28,13 +28,16 @@ constexpr int kThreads = 256;
 // Block k takes item k / groups with KV-head group k % groups.
 __global__ __launch_bounds__(kThreads) void split_order_kernel(const int32_t* __restrict__ lens, int lens_offset,
                                                                int max_len, int chunk, int S, int groups,
-                                                               int B, int2* __restrict__ items)
+                                                               int B, int2* __restrict__ items,
+                                                               unsigned* __restrict__ err)
 {
     __shared__ int nf[kOrderMaxBatch], rem[kOrderMaxBatch], pf[kOrderMaxBatch + 1];
     __shared__ int by_rank[kOrderMaxBatch];
     const int t = threadIdx.x;
     for (int b = t; b < B; b += kThreads) {
-        const int len = min(max(lens[b] - lens_offset, 0), max_len);
+        const int raw = lens[b];
+        if (raw < 0 || raw > max_len) report_error(err, kErrLens);
+        const int len = max(min(max(raw, 0), max_len) - lens_offset, 0);  // as the split kernels
         nf[b] = len / chunk;
         rem[b] = len - nf[b] * chunk;
     }
@@ -81,10 +84,10 @@ __global__ __launch_bounds__(kThreads) void split_order_kernel(const int32_t* __
 }  // namespace
 
 hipError_t launch_split_order(const int32_t* lens, int lens_offset, int max_len, int chunk, int S,
-                              int groups, int B, int2* items, hipStream_t stream)
+                              int groups, int B, int2* items, unsigned* err, hipStream_t stream)
 {
     if (B < 2 || B > kOrderMaxBatch || chunk <= 0) return hipErrorInvalidValue;
-    split_order_kernel<<<1, kThreads, 0, stream>>>(lens, lens_offset, max_len, chunk, S, groups, B, items);
+    split_order_kernel<<<1, kThreads, 0, stream>>>(lens, lens_offset, max_len, chunk, S, groups, B, items, err);
     return hipGetLastError();
 }
 

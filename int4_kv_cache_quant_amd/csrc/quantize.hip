@@ -51,7 +51,7 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm, int rot_kind,
     const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos,
-    int pair_slots)
+    int pair_slots, unsigned* __restrict__ err)
 {
     constexpr int E = D / 64;
     constexpr int NG = D / kGroup;
@@ -60,6 +60,8 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     if (slot >= pair_slots) return;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
+    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
+        report_error(err, kErrPos);  // the tokens outside [0, cap) are skipped below
     const int t0 = ((p0 >> 1) + slot) * 2;  // even absolute position
     const size_t head = (size_t)b * H + h;
 
@@ -352,10 +354,13 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int n_new,
     int H, int cap, uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc,
     float* __restrict__ vs, const float* __restrict__ signs, float rot_norm,
-    const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos)
+    const float* __restrict__ lam, const float* __restrict__ vsigns, const int32_t* __restrict__ pos,
+    unsigned* __restrict__ err)
 {
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
+    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
+        report_error(err, kErrPos);  // the tokens outside [0, cap) are skipped below
     const int t_tile = (p0 / kTile + (int)blockIdx.x) * kTile;
     const int t_end = min(p0 + n_new, cap);
     if (t_tile >= t_end) return;  // block-uniform
@@ -373,7 +378,8 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                   const float* signs, float rot_norm, int rot_kind, const float* lam,
-                                  const float* vsigns, const int32_t* pos, hipStream_t stream)
+                                  const float* vsigns, const int32_t* pos, unsigned* err,
+                                  hipStream_t stream)
 {
     if (D != 64 && D != 128 && D != 256) return hipErrorInvalidValue;
     const auto* kk = static_cast<const uint16_t*>(k);
@@ -383,13 +389,13 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
         dim3 grid((pair_slots + 3) / 4, H, B), block(256);
         auto kern = D == 64 ? quantize_pair_kernel<64> : D == 128 ? quantize_pair_kernel<128> : quantize_pair_kernel<256>;
         kern<<<grid, block, 0, stream>>>(kk, vv, dtype, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm,
-                                         (signs || vsigns) ? rot_kind : 0, lam, vsigns, pos, pair_slots);
+                                         (signs || vsigns) ? rot_kind : 0, lam, vsigns, pos, pair_slots, err);
     } else {
         // one block per tile touched: the range may start inside a tile
         const int tiles = (n_new + 2 * kTile - 2) / kTile;
         dim3 grid(tiles, H, B), block(256);
         using K = void (*)(const uint16_t*, const uint16_t*, int, int, int, uint8_t*, float*, uint8_t*, float*,
-                           const float*, float, const float*, const float*, const int32_t*);
+                           const float*, float, const float*, const float*, const int32_t*, unsigned*);
         auto pick = [&](auto d) -> K {
             constexpr int DD = decltype(d)::value;
             if (vsigns && rot_kind)
@@ -404,7 +410,7 @@ hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n
                      : D == 128 ? pick(std::integral_constant<int, 128>{})
                                 : pick(std::integral_constant<int, 256>{});
         kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam, vsigns,
-                                         pos);
+                                         pos, err);
     }
     return hipGetLastError();
 }

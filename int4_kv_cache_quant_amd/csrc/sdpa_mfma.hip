@@ -12,17 +12,20 @@
 // page, section on numerical stability).
 //
 // Exactness of the products:
-//  * codes enter the MFMAs as fp16 subnormals of their offset-binary value
-//    n = c + 8: a nibble left at bit 0 (or bit 4) of a 16-bit half reads as
-//    n * 2^-24 (or n * 2^-20), so one shift and four masks give all eight
-//    operands of a 32-bit word; the 2^4 of the bit-4 nibbles is cancelled
-//    exactly by a power-of-two factor on the other operand, and the +8 is
-//    removed by starting the score accumulator at -8 * 2^-24 * sum(q) and,
-//    for values, by a correction product against a constant operand (the
-//    matrix cores keep fp16 subnormals); 2^24 is folded into the softmax
-//    scale and the final merge;
-//  * q is converted to fp16 (bf16 values convert exactly in fp16's normal
-//    range); a rotated q is split into fp16 hi + lo parts and both are
+//  * K and V codes enter the MFMAs as signed normal fp16 integers: a
+//    nibble's offset-binary value n = c + 8 goes into the mantissa of 1024.0
+//    (whose ulp is 1), at bit 0 or bit 4 of a 16-bit half, so one shift and
+//    four and-xor operations give the eight operands of a 32-bit word, and
+//    one packed fp16 subtraction per pair leaves c (or 16 c for a bit-4
+//    nibble) exactly; the 16 of the bit-4 nibbles is cancelled exactly by a
+//    power of two on the other operand.  Every product is exact and the sums
+//    are fp32: no offset term, and no subnormal operand, whose rounding
+//    would grow with the scores or with the context;
+//  * q is converted to fp16 after each query head's row is scaled by a power
+//    of two that puts its largest |element| in [2^14, 2^15) (bf16 inputs of
+//    any magnitude fit, and the factor is undone in the softmax scale); bf16
+//    values then convert exactly; a rotated q (or one divided by K's
+//    per-channel scale) is split into fp16 hi + lo parts and both are
 //    multiplied, so the score keeps ~22 bits of q;
 //  * the per-token, per-group K scale is applied in fp32 after the MFMA,
 //    since one MFMA of K = 32 covers exactly one scale group;
@@ -30,7 +33,10 @@
 //    into the probability operand, x = p * s_v in fp32, and x enters as two
 //    fp16 MFMA operands hi = fp16(x), lo = fp16(x - hi) (~22 significant
 //    bits); fp16(x) alone (2^-11 relative) is too coarse when a handful of
-//    tokens carry the softmax and a channel is an outlier.
+//    tokens carry the softmax and a channel is an outlier.  p carries a
+//    power of two 2^E chosen from the largest V scale seen so far (moved like
+//    the softmax reference, and folded into it), so that x stays inside
+//    fp16's normal range for V of any magnitude.
 //
 // One wave serves P = 16 / G KV heads at once (P = 2 for G = 8): MFMA column
 // n is query head n of the block, which belongs to KV head n / G, so no
@@ -71,44 +77,62 @@ typedef float floatx4_t __attribute__((ext_vector_type(4)));
 constexpr float kNegInf = -__builtin_huge_valf();
 // Headroom (base-2 exponent) the softmax reference keeps above the largest
 // score seen when it has to move: 4 makes the moves (and their rescale of
-// every accumulator) rare after the first tiles, while the largest p just
-// after a move, 2^-4, still leaves p * s_v far inside fp16's normal range.
+// every accumulator) rare after the first tiles; every p stays <= 1.
 constexpr float kHeadroom = 4.0f;
+// The value operand x = p * s_v * 2^E: E puts the largest V scale seen so
+// far at [2^11, 2^12) when it is set, and moves again only once a V scale
+// passes 2^15 / 2^E, so x (p <= 1) never leaves fp16's range while the
+// dominant terms keep fp16's normal precision.  The bounds cover every fp32
+// scale (2^-149 .. 2^128); the partial written at the end splits 2^E
+// between l and o (see the merge), which keeps both inside fp32's range.
+constexpr int kVTarget = 12;
+constexpr int kVLimit = 15;
+constexpr int kEMin = -120, kEMax = 165;
 
 // MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
-// word, scaled by 2^(kShift[e] - 24): registers are (0,4), (1,5), (2,6),
-// (3,7), each one mask of the word or of the word shifted by 8 bits.
+// word, scaled by 2^kShift[e]: registers are (0,4), (1,5), (2,6), (3,7),
+// each one mask of the word or of the word shifted by 8 bits.
 constexpr int kSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 constexpr int kShift[8] = {0, 0, 4, 4, 0, 0, 4, 4};
 
-// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^(kShift[e] - 24).
-__device__ __forceinline__ half8_t unpack_codes(uint32_t w)
+// 8 signed nibbles -> 8 normal fp16 values c * 2^kShift[e] (exact): the
+// offset-binary value n = c + 8 of a nibble goes into the mantissa of 1024.0
+// (0x6400, ulp 1), at bit 0 (1024 + n) or bit 4 (1024 + 16 n); one packed
+// subtraction of 1032 or 1152 then leaves c or 16 c.  One and-xor per
+// register, as for the subnormal form, plus one packed fp16 subtraction.
+__device__ __forceinline__ half8_t unpack_codes_signed(uint32_t w)
 {
     const uint32_t w8 = w >> 8;
-    uint32_t r[4];
-    r[0] = (w ^ 0x88888888u) & 0x000F000Fu;   // elements 0, 4 at bit 0
-    r[1] = (w ^ 0x88888888u) & 0x00F000F0u;   // elements 1, 5 at bit 4
-    r[2] = (w8 ^ 0x00888888u) & 0x000F000Fu;  // elements 2, 6 at bit 0
-    r[3] = (w8 ^ 0x00888888u) & 0x00F000F0u;  // elements 3, 7 at bit 4
+    const half2_t b0 = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
+    const half2_t b4 = half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
+    half2_t h[4];
+    h[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u) - b0;   // elements 0, 4
+    h[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ 0x64806480u) - b4;   // elements 1, 5
+    h[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) ^ 0x64086408u) - b0;  // elements 2, 6
+    h[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) ^ 0x64806480u) - b4;  // elements 3, 7
     half8_t out;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const half2_t p = __builtin_bit_cast(half2_t, r[m]);
-        out[2 * m] = p[0];
-        out[2 * m + 1] = p[1];
+        out[2 * m] = h[m][0];
+        out[2 * m + 1] = h[m][1];
     }
     return out;
 }
 
 // fp16 (x0 - h0, x1 - h1) packed, where (h0, h1) = h2 are x0, x1 rounded to
 // fp16: the differences are exact in fp32 and rounded once (v_fma_mix with
-// an fp16 operand; register-only instructions).
+// an fp16 operand; register-only instructions).  The result feeds an MFMA,
+// which must not read a VGPR within 2 wait states of a VALU write; the
+// compiler counts no wait states for instructions inside inline asm, so the
+// asm ends with them (without, the MFMA could read the register's previous
+// contents: measured, the lo half of p * s_v was lost).
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint32_t lo_pair(float x0, float x1, uint32_t h2)
 {
     uint32_t r;
     asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
-        "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+        "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+        "s_nop 1"
         : "=&v"(r)
         : "v"(x0), "v"(x1), "v"(h2));
     return r;
@@ -328,6 +352,13 @@ constexpr bool kRefillAfterScores = D <= 128 && !(HILO && P == 2);
 template <int D>
 constexpr int kWavesPerEU = D == 256 ? 1 : 2;
 
+// Whether the query prologue loads K's channel scales together with q and the
+// rotation signs (before the first tile's copies), or only once the rotation
+// is done: at head_dim 256 the three sets (192 registers) do not fit beside
+// each other.
+template <int D>
+constexpr bool kLamEarly = D < 256;
+
 // LDS stages per wave: two where the copies a block keeps in flight stay
 // within 80 KB, else one (measured: deeper queues per CU slow the stream).
 template <int D, int P, int W>
@@ -426,7 +457,11 @@ void split_mfma_kernel(SplitArgs a)
     auto stage_of = [&](int st) { return reinterpret_cast<char*>(lds) + (wave * NST + st) * St::BYTES; };
 
     // sequence length first, as a scalar load: nothing has been written yet
-    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
+    // lens clamped to [0, max_len] first, as the combine does, then the
+    // fused append's token (lens_offset = 1) left to the combine
+    const int raw_len = a.lens[b];
+    const int len = max(min(max(raw_len, 0), a.max_len) - a.lens_offset, 0);
+    if (tid == 0 && split == 0 && hk0 == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
 
     // ---- q straight into registers, before any tile copy is queued: lane
     //      (n16, r) needs, per scale group g, channels 32 g + 8 r + 0..7 of
@@ -447,7 +482,7 @@ void split_mfma_kernel(SplitArgs a)
                     sgn[g][0] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r);
                     sgn[g][1] = *reinterpret_cast<const float4*>(a.signs + 32 * g + 8 * r + 4);
                 }
-                if (scaled) {
+                if (kLamEarly<D> && scaled) {
                     lmv[g][0] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r);
                     lmv[g][1] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r + 4);
                 }
@@ -578,6 +613,13 @@ void split_mfma_kernel(SplitArgs a)
                     }
     }
     if (HILO && scaled) {
+        if constexpr (!kLamEarly<D>) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                lmv[g][0] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r);
+                lmv[g][1] = *reinterpret_cast<const float4*>(a.lam + 32 * g + 8 * r + 4);
+            }
+        }
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const float lm[8] = {lmv[g][0].x, lmv[g][0].y, lmv[g][0].z, lmv[g][0].w,
@@ -586,29 +628,41 @@ void split_mfma_kernel(SplitArgs a)
             for (int e = 0; e < 8; ++e) qx[g][e] = qx[g][e] / lm[e];
         }
     }
+    // Each query head's row is scaled by a power of two 2^qk that puts its
+    // largest |element| in [2^14, 2^15): any bf16 row then fits fp16's range,
+    // and a row of small values keeps its bits instead of turning subnormal.
+    // The factor is exact and is undone in qmul.  The row's channels are
+    // spread over the lanes of column n16 (r = lane / 16).
+    int qk = 0;
+    {
+        float qa = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qa = fmaxf(qa, fabsf(qx[g][e]));
+        qa = max_xor32(max_xor16(qa));
+        qk = qa > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(qa) : 0;  // qa = f 2^e, f in [0.5, 1)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qx[g][e] = __builtin_ldexpf(qx[g][e], qk);
+    }
     // B operands of the score MFMAs, one per KV head: column n16 holds q of
     // query head n16 in the set of head jl and zeros in the others; k slot e
     // = channel 32 g + 8 r + kSlot[e].
     half8_t qb[P][NG], qb_lo[HILO ? P : 1][HILO ? NG : 1];
-    floatx4_t qinit4[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         half8_t hv, lv;
-        float t = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = qx[g][kSlot[e]];
             const _Float16 h16 = (_Float16)x;
             const _Float16 l16 = (_Float16)(x - (float)h16);
-            // cancel the code's 2^kShift (a power of two); the offset sum
-            // below uses the operands exactly as the MFMA sees them
-            const float down = kShift[e] ? 0.0625f : 1.0f, up = kShift[e] ? 16.0f : 1.0f;
+            // cancel the code's 2^kShift (a power of two)
+            const float down = kShift[e] ? 0.0625f : 1.0f;
             hv[e] = (_Float16)((float)h16 * down);
-            t += (float)hv[e] * up;
-            if (HILO) {
-                lv[e] = (_Float16)((float)l16 * down);
-                t += (float)lv[e] * up;
-            }
+            if (HILO) lv[e] = (_Float16)((float)l16 * down);
         }
 #pragma unroll
         for (int j = 0; j < P; ++j) {
@@ -619,27 +673,19 @@ void split_mfma_kernel(SplitArgs a)
                 if (HILO) qb_lo[j][g][e] = mine ? lv[e] : (_Float16)0.0f;
             }
         }
-        // the score accumulator starts at -8 * 2^-24 * sum(q over the group)
-        const float qi = -8.0f * 0x1p-24f * sum_xor32(sum_xor16(t));
-        qinit4[g] = floatx4_t{qi, qi, qi, qi};
     }
-    const float qmul = (HILO && rot ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f;
+    const float qmul = __builtin_ldexpf(HILO && rot ? a.qscale * a.rot_norm : a.qscale, -qk);
 
-    float m_run = kNegInf;  // softmax reference of column n16 (>= its running max)
+    float m_run = kNegInf;  // softmax reference M of column n16 (>= its running max)
+    int e_v = 0;            // E (wave-uniform): the value operand carries 2^E
+    float v_lim = 0.0f;     // V scales above this move E (0 until the first nonzero one)
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
-    // acc[j]: 2^-24 * sum p s_v (c + 8) V rows of KV head j; corr: 2^-24 * 8 *
-    // sum p s_v per scale group (shared by the heads: it depends on p only)
-    floatx4_t acc[P][NCB], corr[NG];
+    // acc[j]: sum p s_v c V rows of KV head j (p with its 2^E)
+    floatx4_t acc[P][NCB];
 #pragma unroll
     for (int j = 0; j < P; ++j)
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int g = 0; g < NG; ++g) corr[g] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    // B operand of the correction product: 8 * 2^(kShift[e] - 24) in every column
-    half8_t bcorr;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) bcorr[e] = (_Float16)(kShift[e] ? 0x1p-17f : 0x1p-21f);
 
     // this lane's operands of the staged tile, into registers
     auto read_stage = [&](TileLoads<D, P, ROWS>& t, const char* stage) {
@@ -682,7 +728,7 @@ void split_mfma_kernel(SplitArgs a)
         }
     };
 
-    auto compute_tile = [&](const TileLoads<D, P, ROWS>& t, int it, auto&& after_scores) {
+    auto compute_tile = [&](TileLoads<D, P, ROWS>& t, int it, auto&& after_scores) {
         const int tok0 = start + it * kTile;
         // ---- scores, as T = S / qmul (qmul > 0 is applied inside exp2)
         float T[2][4];
@@ -691,10 +737,10 @@ void split_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
             static_for<NG>([&](auto gI) {
                 constexpr int g = decltype(gI)::value;
-                floatx4_t d = qinit4[g];
+                floatx4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    const half8_t A = unpack_codes(t.kw[j][s][g]);
+                    const half8_t A = unpack_codes_signed(t.kw[j][s][g]);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[j][g], d, 0, 0, 0);
                     if constexpr (HILO) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
                 }
@@ -712,10 +758,18 @@ void split_mfma_kernel(SplitArgs a)
         after_scores();
         if (tok0 + kTile > end) {  // wave-uniform: the chunk's last, partial tile
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+            for (int s = 0; s < 2; ++s) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (tok0 + 16 * s + 4 * r + i >= end) T[s][i] = kNegInf;
+                // the V scales of tokens past the end (whatever bits the cache
+                // holds there) must not reach the value products, where 0 * Inf
+                // or 0 * NaN would poison the row
+                if (tok0 + 16 * s + 4 * r + slot >= end) {
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) t.sv[s][g] = 0.0f;
+                }
+            }
         }
 
         // ---- online softmax for column n16 over the tile's 32 tokens (base-2
@@ -728,24 +782,45 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
             for (int i = 0; i < 4; ++i) mt = fmaxf(mt, T[s][i]);
         mt = max_xor32(max_xor16(mt)) * qmul;  // finite: the tile has a valid token
+        // the largest V scale of the lane's tokens (0 past the end)
+        float svm = t.sv[0][0];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) svm = fmaxf(svm, t.sv[s][g]);
+        const bool vmove = __any(svm > v_lim);
         // decided for the whole wave, so that the cross-lane moves of the
         // rescale see every lane
-        if (__any(mt > m_run)) {
+        if (__any(mt > m_run) || vmove) {
             const float m_new = (mt > m_run) ? mt + kHeadroom : m_run;
-            const float alpha = exp2_approx(m_run - m_new);  // 0 on the first tile, 1 if unmoved
+            int e_new = e_v;
+            if (vmove) {  // wave-uniform: E from the wave's largest V scale
+                const int ve = __builtin_amdgcn_frexp_expf(group_max<64>(svm));
+                const int en = min(max(kVTarget - ve, kEMin), kEMax);
+                e_new = en;
+                v_lim = __builtin_ldexpf(1.0f, kVLimit - en);
+            }
+            // 0 on the first tile, 1 if unmoved
+            const float alpha = exp2_approx(m_run - m_new);
+            // the accumulators also take 2^(E' - E) (exact)
+            const float alpha_o = __builtin_ldexpf(alpha, e_new - e_v);
             l_lane *= alpha;
             static_for<4>([&](auto iI) {
                 constexpr int i = decltype(iI)::value;
-                const float ai = row_quad_gather<i>(alpha, r);  // alpha of column 4 r + i
+                const float ai = row_quad_gather<i>(alpha_o, r);  // of column 4 r + i
 #pragma unroll
                 for (int j = 0; j < P; ++j)
 #pragma unroll
                     for (int cb = 0; cb < NCB; ++cb) acc[j][cb][i] *= ai;
-#pragma unroll
-                for (int g = 0; g < NG; ++g) corr[g][i] *= ai;
             });
             m_run = m_new;
+            e_v = e_new;
         }
+        // the tile's V scales carry 2^E (exact)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) t.sv[s][g] = __builtin_ldexpf(t.sv[s][g], e_v);
         // p of the tile's tokens.  Odd i hold the bit-4 nibbles of the V words
         // (see below), whose 2^4 is cancelled here: p / 16 comes straight from
         // the exponent, and l takes 16 (p / 16).
@@ -777,8 +852,6 @@ void split_mfma_kernel(SplitArgs a)
                 la[m] = lo_pair(x0, x1, ha[m]);
             });
             const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
-            corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bcorr, corr[g], 0, 0, 0);
-            corr[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, bcorr, corr[g], 0, 0, 0);
 #pragma unroll
             for (int j = 0; j < P; ++j) {
                 static_for<2>([&](auto hI) {
@@ -786,7 +859,7 @@ void split_mfma_kernel(SplitArgs a)
                     constexpr int av = cb / 4, bv = cb % 4;
                     const uint32_t word = bv == 0 ? t.vw[j][av].x : bv == 1 ? t.vw[j][av].y
                                         : bv == 2 ? t.vw[j][av].z : t.vw[j][av].w;
-                    const half8_t B = unpack_codes(word);
+                    const half8_t B = unpack_codes_signed(word);
                     acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[j][cb], 0, 0, 0);
                     acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[j][cb], 0, 0, 0);
                 });
@@ -842,7 +915,11 @@ void split_mfma_kernel(SplitArgs a)
     auto merge_o = [&](int w) { return reinterpret_cast<float*>(lds) + w * (NST * St::BYTES / 4); };
     auto merge_ml = [&](int w) { return reinterpret_cast<float2*>(merge_o(w) + 16 * RS); };
     const float L = sum_xor32(sum_xor16(l_lane));
-    if (lane < 16) merge_ml(wave)[lane] = make_float2(m_run, L);
+    // acc carries 2^E.  With F = floor(E / 2), (M - F, l 2^F, acc 2^(F - E))
+    // is the partial (M, l, acc 2^-E), with both sums inside fp32's range for
+    // every E the V scales can give
+    const int f_e = e_v >> 1;
+    if (lane < 16) merge_ml(wave)[lane] = make_float2(m_run - (float)f_e, __builtin_ldexpf(L, f_e));
     // rows 4 r .. 4 r + 3 of O lie in one KV head (two heads only if G >= 4):
     // keep that head's set
     const int jr = min(4 * r / G, P - 1);
@@ -856,7 +933,7 @@ void split_mfma_kernel(SplitArgs a)
                 float v = acc[0][cb][i];
 #pragma unroll
                 for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
-                own[h * RS + 16 * cb + n16] = (v - corr[cb / 2][i]) * 0x1p24f;
+                own[h * RS + 16 * cb + n16] = __builtin_ldexpf(v, f_e - e_v);
             }
         }
     }

@@ -72,7 +72,11 @@ __global__ __launch_bounds__(256) void split_vec_kernel(SplitArgs a)
         b = it.y;
         hk = k % a.H;
     }
-    const int len = min(max(a.lens[b] - a.lens_offset, 0), a.max_len);
+    // lens clamped to [0, max_len] first, as the combine does, then the
+    // fused append's token (lens_offset = 1) left to the combine
+    const int raw_len = a.lens[b];
+    const int len = max(min(max(raw_len, 0), a.max_len) - a.lens_offset, 0);
+    if (tid == 0 && split == 0 && hk == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for empty chunks
     const int end = min(start + a.chunk, len);

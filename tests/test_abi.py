@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 5
+    assert lib.otq_abi_version() == 6
 
 
 def test_status_strings():
@@ -45,7 +45,7 @@ def _desc(B=1, H=2, D=128, cap=64, signs=None):
 
 def test_cache_bytes_closed_form_llama70b_128k():
     g = json.load(open(os.path.join(GOLDEN, "storage_closed_forms.json")))["llama31_70b_128k"]
-    per_layer = otq.otq_cache_bytes(1, g["kv_heads"], g["head_dim"], g["tokens"])
+    per_layer = otq.otq_cache_bytes(1, g["kv_heads"], g["head_dim"], g["tokens"], 4)
     assert per_layer * g["layers"] == g["int4_bytes"]
     fp16 = g["layers"] * g["kv_heads"] * g["head_dim"] * g["tokens"] * 2 * 2
     assert fp16 / (per_layer * g["layers"]) == g["ratio"]
@@ -56,10 +56,54 @@ def test_cache_bytes_closed_form_llama70b_128k():
 def test_cache_bytes_rejects_bad_dims():
     lib = otq.lib()
     c, s = ctypes.c_size_t(), ctypes.c_size_t()
-    assert lib.otq_cache_array_bytes(1, 1, 96, 64, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EUNSUPPORTED
-    assert lib.otq_cache_array_bytes(1, 1, 128, 48, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
-    assert lib.otq_cache_array_bytes(0, 1, 128, 64, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
-    assert lib.otq_cache_bytes(1, 1, 100, 64) == 0
+    assert lib.otq_cache_array_bytes(1, 1, 96, 64, 4, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EUNSUPPORTED
+    assert lib.otq_cache_array_bytes(1, 1, 128, 48, 4, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
+    assert lib.otq_cache_array_bytes(0, 1, 128, 64, 4, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
+    for bits in (1, 5, 8, -4):
+        assert lib.otq_cache_array_bytes(1, 1, 128, 64, bits, ctypes.byref(c), ctypes.byref(s)) == otq.OTQ_EINVAL
+        assert lib.otq_cache_bytes(1, 1, 128, 64, bits) == 0
+    assert lib.otq_cache_bytes(1, 1, 100, 64, 4) == 0
+
+
+@pytest.mark.parametrize("bits", [0, 2, 3, 4])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_cache_bytes_by_code_width(bits, D):
+    """Codes take D * b / 8 bytes per token and head (b = 4 for code_bits 0),
+    scales D / 32 fp32 words whatever the width."""
+    B, H, cap = 3, 5, 96
+    cb, sb = otq.otq_cache_array_bytes(B, H, D, cap, bits)
+    b = bits or 4
+    assert cb == B * H * cap * D * b // 8
+    assert sb == B * H * cap * (D // 32) * 4
+    assert otq.otq_cache_bytes(B, H, D, cap, bits) == 2 * (cb + sb)
+
+
+def test_query_and_output_alignment():
+    """q is read and out written 16 bytes at a time: a misaligned pointer is
+    rejected on the host by every attention entry point."""
+    lib = otq.lib()
+    d = _desc(B=2, H=2, D=128, cap=256)
+    p = otq.otq_sdpa_plan(4, d, 256)
+    P = ctypes.c_void_p
+    wsb = p.workspace_bytes
+    for off_q, off_o in ((8, 0), (2, 0), (0, 4), (0, 8)):
+        q, o = FAKE + off_q, FAKE + off_o
+        assert lib.otq_sdpa_int4_decode(P(q), 1, 4, ctypes.byref(d), P(FAKE), 256, 0.1, P(o), P(4096), wsb,
+                                        None) == otq.OTQ_EINVAL
+        assert lib.otq_sdpa_int4_decode_planned(P(q), 1, 4, ctypes.byref(d), P(FAKE), 256, 0.1, P(o), P(4096),
+                                                wsb, ctypes.byref(p), None) == otq.OTQ_EINVAL
+        assert lib.otq_sdpa_int4_decode_append(P(q), P(FAKE), P(FAKE), 1, 4, ctypes.byref(d), P(FAKE), 256,
+                                               0.1, P(o), P(4096), wsb, ctypes.byref(p), None) == otq.OTQ_EINVAL
+        if off_q:
+            assert lib.otq_sdpa_int4_split(P(q), 1, 4, ctypes.byref(d), P(FAKE), 256, 0.1, P(4096), wsb,
+                                           ctypes.byref(p), None) == otq.OTQ_EINVAL
+        if off_o:
+            assert lib.otq_sdpa_lse_combine(4, ctypes.byref(d), P(FAKE), 256, P(4096), wsb, ctypes.byref(p),
+                                            P(o), None) == otq.OTQ_EINVAL
+
+
+def test_last_device_error_rejects_null_flags():
+    assert otq.lib().otq_last_device_error(None, None) == otq.OTQ_EINVAL
 
 
 def test_quantize_append_host_errors():

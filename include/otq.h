@@ -314,6 +314,29 @@ int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_
                                 const otq_plan *plan, void *stream);
 
 /*
+ * For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): otq_sdpa_int4_decode_append
+ * with its workspace in a fixed array of OTQ_NOALLOC_SCRATCH_BYTES bytes that
+ * the library keeps on each GPU (set up on the first call on that GPU and
+ * held until the process ends).  The call itself allocates nothing.
+ *
+ *  Arguments, results and errors as for otq_sdpa_int4_decode_append, except
+ *  OTQ_EWORKSPACE when the plan's workspace_bytes exceeds
+ *  OTQ_NOALLOC_SCRATCH_BYTES (checked on the host), and OTQ_EDEVICE when the
+ *  array's address cannot be obtained.
+ *  Every call on one GPU shares that GPU's array: calls that overlap on one
+ *  GPU (other streams, other host threads) race and must be serialised by
+ *  the caller.  The array needs no clearing between calls (the split pass
+ *  writes every partial the combine reads).
+ */
+#define OTQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int otq_sdpa_int4_decode_append_noalloc(const void *q, const void *k_new, const void *v_new,
+                                        int32_t dtype, int32_t num_q_heads,
+                                        const otq_cache *cache, const int32_t *lens,
+                                        int32_t max_len, float scale, float *out,
+                                        const otq_plan *plan, void *stream);
+
+/*
  * The two phases of otq_sdpa_int4_decode as separate calls, for callers
  * that time them apart or merge partials computed elsewhere (each split of
  * the token axis is independent until the combine).

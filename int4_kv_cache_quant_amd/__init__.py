@@ -33,6 +33,7 @@ EXPORTED = [
     "otq_last_device_error",
     "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
     "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned", "otq_sdpa_int4_decode_append",
+    "otq_sdpa_int4_decode_append_noalloc",
     "otq_sdpa_int4_split", "otq_sdpa_lse_combine",
 ]
 
@@ -99,6 +100,9 @@ def lib():
     L.otq_sdpa_int4_decode_append.argtypes = [P, P, P, I, I, CP, P, I, ctypes.c_float, P, P, S,
                                               ctypes.POINTER(otq_plan), P]
     L.otq_sdpa_int4_decode_append.restype = ctypes.c_int
+    L.otq_sdpa_int4_decode_append_noalloc.argtypes = [P, P, P, I, I, CP, P, I, ctypes.c_float, P,
+                                                      ctypes.POINTER(otq_plan), P]
+    L.otq_sdpa_int4_decode_append_noalloc.restype = ctypes.c_int
     L.otq_sdpa_int4_split.argtypes = [P, I, I, CP, P, I, ctypes.c_float, P, S,
                                       ctypes.POINTER(otq_plan), P]
     L.otq_sdpa_int4_split.restype = ctypes.c_int
@@ -216,6 +220,25 @@ def otq_sdpa_int4_decode_append(q, k_new, v_new, cache_desc, lens, max_len, scal
                                            _stream(stream))
     if check:
         _check(rc, "otq_sdpa_int4_decode_append")
+    return rc
+
+
+OTQ_NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def otq_sdpa_int4_decode_append_noalloc(q, k_new, v_new, cache_desc, lens, max_len, scale, out,
+                                        plan=None, num_q_heads=None, dtype=None, stream=None, check=True):
+    """otq_sdpa_int4_decode_append with the library's per-device scratch
+    array as the workspace (no allocation by the caller or the call)."""
+    Hq = q.shape[1] if num_q_heads is None else num_q_heads
+    dtype = dtype_code(q.dtype) if dtype is None else dtype
+    rc = lib().otq_sdpa_int4_decode_append_noalloc(_ptr(q), _ptr(k_new), _ptr(v_new), dtype, Hq,
+                                                   ctypes.byref(cache_desc), _ptr(lens), max_len,
+                                                   float(scale), _ptr(out),
+                                                   None if plan is None else ctypes.byref(plan),
+                                                   _stream(stream))
+    if check:
+        _check(rc, "otq_sdpa_int4_decode_append_noalloc")
     return rc
 
 

@@ -17,7 +17,12 @@
 // violations (OTQ_DEVERR_*), [1] receives the value otq_last_device_error
 // takes.  Host code uses the address hipGetSymbolAddress gives per device,
 // never this name (which on the host is only a stand-in for the symbol).
-__device__ unsigned otq_device_error_word[2];
+static __device__ unsigned otq_device_error_word[2];
+
+// The workspace of otq_sdpa_int4_decode_append_noalloc: one copy per GPU,
+// held until the process ends.  As above, host code only ever uses the
+// per-device address from hipGetSymbolAddress.
+static __device__ __align__(256) unsigned char scratch[OTQ_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -33,7 +38,8 @@ constexpr int kMaxDevices = 64;
 struct DeviceState {
     std::once_flag once;
     hipError_t rc = hipSuccess;
-    unsigned* err = nullptr;
+    unsigned* err = nullptr;  // this device's otq_device_error_word
+    void* scratch = nullptr;  // this device's scratch array
 };
 DeviceState g_devices[kMaxDevices];
 
@@ -46,9 +52,14 @@ DeviceState* device_state()
     std::call_once(d.once, [&d] {
         void* p = nullptr;
         d.rc = hipGetSymbolAddress(&p, HIP_SYMBOL(otq_device_error_word));
+        if (d.rc != hipSuccess) return;
         d.err = static_cast<unsigned*>(p);
+        p = nullptr;
+        d.rc = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (d.rc != hipSuccess) return;
+        d.scratch = p;
     });
-    return d.rc == hipSuccess && d.err ? &d : nullptr;
+    return d.rc == hipSuccess && d.err && d.scratch ? &d : nullptr;
 }
 
 // The current device's error word for a launch (null: OTQ_EDEVICE).
@@ -450,25 +461,62 @@ int otq_sdpa_int4_decode_planned(const void* q, int32_t dtype, int32_t num_q_hea
     return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s);
 }
 
+}  // extern "C"
+
+namespace {
+
+// The host checks of the fused decode step, but for the workspace; on
+// success *chk is the plan to run.
+int check_decode_append(const void* q, const void* k_new, const void* v_new, int32_t dtype,
+                        int32_t num_q_heads, const otq_cache* cache, const int32_t* lens, int32_t max_len,
+                        float scale, const float* out, const otq_plan* plan, otq_plan* chk)
+{
+    const int rc = plan ? check_plan(num_q_heads, cache, max_len, plan, chk)
+                        : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, chk);
+    if (rc != OTQ_OK) return rc;
+    if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
+    if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
+    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
+    if (!finite(scale)) return OTQ_EINVAL;
+    return OTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
 int otq_sdpa_int4_decode_append(const void* q, const void* k_new, const void* v_new, int32_t dtype,
                                 int32_t num_q_heads, const otq_cache* cache, const int32_t* lens,
                                 int32_t max_len, float scale, float* out, void* workspace,
                                 size_t workspace_bytes, const otq_plan* plan, void* stream)
 {
     otq_plan chk;
-    int rc = plan ? check_plan(num_q_heads, cache, max_len, plan, &chk)
-                  : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &chk);
+    int rc = check_decode_append(q, k_new, v_new, dtype, num_q_heads, cache, lens, max_len, scale, out,
+                                 plan, &chk);
     if (rc != OTQ_OK) return rc;
-    if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
-    if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
-    if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
-    if (!finite(scale)) return OTQ_EINVAL;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
     rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s, 1);
     if (rc != OTQ_OK) return rc;
     return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s, q, k_new, v_new,
                        dtype, scale);
+}
+
+int otq_sdpa_int4_decode_append_noalloc(const void* q, const void* k_new, const void* v_new,
+                                        int32_t dtype, int32_t num_q_heads, const otq_cache* cache,
+                                        const int32_t* lens, int32_t max_len, float scale, float* out,
+                                        const otq_plan* plan, void* stream)
+{
+    otq_plan chk;
+    const int rc = check_decode_append(q, k_new, v_new, dtype, num_q_heads, cache, lens, max_len, scale,
+                                       out, plan, &chk);
+    if (rc != OTQ_OK) return rc;
+    if (chk.workspace_bytes > OTQ_NOALLOC_SCRATCH_BYTES) return OTQ_EWORKSPACE;
+    DeviceState* d = device_state();
+    if (!d) return OTQ_EDEVICE;
+    // the same kernels as the caller-workspace call, on this device's array
+    return otq_sdpa_int4_decode_append(q, k_new, v_new, dtype, num_q_heads, cache, lens, max_len, scale,
+                                       out, d->scratch, OTQ_NOALLOC_SCRATCH_BYTES, &chk, stream);
 }
 
 int otq_sdpa_int4_decode(const void* q, int32_t dtype, int32_t num_q_heads,

@@ -302,3 +302,24 @@ def test_code_bits_host_checks():
                                          None)
     assert rc == otq.OTQ_EUNSUPPORTED
 
+
+
+def test_noalloc_scratch_limit_on_host():
+    """The scratch-array decode step refuses, before any HIP call, a plan
+    whose workspace exceeds OTQ_NOALLOC_SCRATCH_BYTES, and validates its
+    arguments like the workspace call."""
+    lib = otq.lib()
+    P = ctypes.c_void_p
+    d = _desc(B=64, H=8, D=128, cap=8192)
+    p = otq.otq_sdpa_plan(64, d, 8192, chunk=128)
+    assert p.workspace_bytes > otq.OTQ_NOALLOC_SCRATCH_BYTES
+    call = lambda q=FAKE, plan=p: lib.otq_sdpa_int4_decode_append_noalloc(
+        P(q), P(FAKE), P(FAKE), 1, 64, ctypes.byref(d), P(FAKE), 8192, 0.1, P(FAKE),
+        None if plan is None else ctypes.byref(plan), None)
+    assert call() == otq.OTQ_EWORKSPACE
+    bad = otq.otq_plan(100, 3, otq.OTQ_VARIANT_MFMA, 0, 0)  # chunk not a multiple of 128
+    assert call(plan=bad) == otq.OTQ_EINVAL
+    small = _desc(B=1, H=2, D=128, cap=256)
+    ps = otq.otq_sdpa_plan(4, small, 256)
+    assert lib.otq_sdpa_int4_decode_append_noalloc(P(0), P(FAKE), P(FAKE), 1, 4, ctypes.byref(small), P(FAKE),
+                                                   256, 0.1, P(FAKE), ctypes.byref(ps), None) == otq.OTQ_EINVAL

@@ -58,6 +58,22 @@
  * + d_im w_re), each product rounded, then the sum; twiddles are the
  * correctly rounded fp32 values of cos and -sin of 2 pi t / N.
  *
+ * Mixed radix ("SRFT + int4 KV-cache", core-method section and the
+ * comparison of methods: the FFT's advantage over the Hadamard form is that
+ * it is not tied to powers of two).  Reading: for N = 3 * 2^k complex
+ * numbers, the decimation-in-frequency FFT takes one radix-3 stage first,
+ * over the triples (a0, a1, a2) = (z_j, z_j+M, z_j+2M), M = N / 3, j < M:
+ * the 3-point DFT with omega = exp(-2 pi i / 3), evaluated as s = a1 + a2,
+ * d = a1 - a2, m = a0 - s / 2, t = c3 d (c3 = sqrt(3) / 2),
+ * b0 = a0 + s, b1 = m - i t, b2 = m + i t, then z_j = b0,
+ * z_j+M = b1 W_N^j, z_j+2M = b2 W_N^2j; then the radix-2 stages above run
+ * inside each block of M.  Position M m + p then holds the DFT coefficient
+ * of index 3 bitrev(p) + m, and c = 1/sqrt(N) as before.  In fp32 each of
+ * those steps is one IEEE operation (s / 2 is the product by 0.5, and c3 is
+ * the correctly rounded fp32 value).  The inverse undoes the radix-2
+ * stages, then the radix-3 one: the twiddles are divided out (times their
+ * conjugates) and the 3-point DFT with the conjugate root is applied.
+ *
  * Other code widths (the AdapTQ page lists 2-bit and 3-bit quantisation
  * beside 4-bit; int2 is named as later work elsewhere).  Reading: b-bit
  * codes follow the same steps with the symmetric range of b bits, s = a /
@@ -213,15 +229,25 @@ void oracle_twiddle_f32(int t, int N, float *wr, float *wi)
     *wi = (float)i;
 }
 
-/* y <- c * FFT_{D/2}(s (.) y) in fp32, the in-place radix-2 decimation-in-
- * frequency FFT over z_j = (y[2j], y[2j+1]) described at the top. */
-void oracle_srft_f32(float *y, const float *signs, int D, float c)
+/* N complex numbers for the FFT rotation: a power of two, or three times
+ * one (mixed radix); 0 for other N. */
+static int fft_size_ok(int N)
 {
-    const int N = D / 2;
-    for (int i = 0; i < D; ++i)
-        y[i] = y[i] * signs[i];
-    for (int h = N / 2; h >= 1; h /= 2)
-        for (int blk = 0; blk < N; blk += 2 * h)
+    if (N < 1)
+        return 0;
+    if (N % 3 == 0)
+        N /= 3;
+    return (N & (N - 1)) == 0;
+}
+
+/* The radix-2 decimation-in-frequency stages over complex numbers
+ * [base, base + n) of y (n a power of two), as part of an N-point
+ * transform: the pair's twiddle exponent is (j mod h) n / (2h) of W_n, that
+ * is (j mod h) N / (2h) of W_N. */
+static void radix2_stages_f32(float *y, int base, int n, int N)
+{
+    for (int h = n / 2; h >= 1; h /= 2)
+        for (int blk = base; blk < base + n; blk += 2 * h)
             for (int j = blk; j < blk + h; ++j) {
                 float ar = y[2 * j], ai = y[2 * j + 1];
                 float br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
@@ -234,18 +260,12 @@ void oracle_srft_f32(float *y, const float *signs, int D, float c)
                 y[2 * (j + h)] = p1 - p2;
                 y[2 * (j + h) + 1] = p3 + p4;
             }
-    for (int i = 0; i < D; ++i)
-        y[i] = y[i] * c;
 }
 
-/* The same transform in fp64 (twiddles in double), used on the query. */
-void oracle_srft_f64(double *y, const float *signs, int D, double c)
+static void radix2_stages_f64(double *y, int base, int n, int N)
 {
-    const int N = D / 2;
-    for (int i = 0; i < D; ++i)
-        y[i] = y[i] * (double)signs[i];
-    for (int h = N / 2; h >= 1; h /= 2)
-        for (int blk = 0; blk < N; blk += 2 * h)
+    for (int h = n / 2; h >= 1; h /= 2)
+        for (int blk = base; blk < base + n; blk += 2 * h)
             for (int j = blk; j < blk + h; ++j) {
                 double ar = y[2 * j], ai = y[2 * j + 1];
                 double br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
@@ -257,20 +277,15 @@ void oracle_srft_f64(double *y, const float *signs, int D, double c)
                 y[2 * (j + h)] = dr * wr - di * wi;
                 y[2 * (j + h) + 1] = dr * wi + di * wr;
             }
-    for (int i = 0; i < D; ++i)
-        y[i] = y[i] * c;
 }
 
-/* The inverse of oracle_srft_f64 in fp64: y <- s (.) (c * U(y)), where U
- * undoes the stages in reverse order (half-size 1, 2, ..., N/2): a stage's
- * pair (a', b') = (a + b, (a - b) W^t) gives back 2a = a' + b' conj(W^t) and
- * 2b = a' - b' conj(W^t), and the log2(N) factors of 2 together with the
- * forward c make the final factor c again (c = 1/sqrt(N)). */
-void oracle_unsrft_f64(double *y, const float *signs, int D, double c)
+/* The radix-2 stages undone in reverse order (half-size 1, 2, ..., n/2),
+ * without the factor 1/2 per stage: 2a = a' + b' conj(W), 2b = a' - b'
+ * conj(W). */
+static void unradix2_stages_f64(double *y, int base, int n, int N)
 {
-    const int N = D / 2;
-    for (int h = 1; h < N; h *= 2)
-        for (int blk = 0; blk < N; blk += 2 * h)
+    for (int h = 1; h < n; h *= 2)
+        for (int blk = base; blk < base + n; blk += 2 * h)
             for (int j = blk; j < blk + h; ++j) {
                 double xr = y[2 * j], xi = y[2 * j + 1];
                 double br = y[2 * (j + h)], bi = y[2 * (j + h) + 1];
@@ -283,8 +298,153 @@ void oracle_unsrft_f64(double *y, const float *signs, int D, double c)
                 y[2 * (j + h)] = xr - tr;
                 y[2 * (j + h) + 1] = xi - ti;
             }
+}
+
+/* sqrt(3) / 2, correctly rounded to fp32 and in double. */
+static float c3_f32(void) { return (float)(sqrt(3.0) / 2.0); }
+
+/* The radix-3 stage of an N-point transform (N = 3 M) in fp32, in the
+ * order of operations given at the top. */
+static void radix3_stage_f32(float *y, int N)
+{
+    const int M = N / 3;
+    const float c3 = c3_f32();
+    for (int j = 0; j < M; ++j) {
+        float a0r = y[2 * j], a0i = y[2 * j + 1];
+        float a1r = y[2 * (j + M)], a1i = y[2 * (j + M) + 1];
+        float a2r = y[2 * (j + 2 * M)], a2i = y[2 * (j + 2 * M) + 1];
+        float sr = a1r + a2r, si = a1i + a2i;
+        float dr = a1r - a2r, di = a1i - a2i;
+        float hr = 0.5f * sr, hi = 0.5f * si;
+        float mr = a0r - hr, mi = a0i - hi;
+        float tr = c3 * dr, ti = c3 * di;
+        float b1r = mr + ti, b1i = mi - tr;   /* m - i t */
+        float b2r = mr - ti, b2i = mi + tr;   /* m + i t */
+        y[2 * j] = a0r + sr;
+        y[2 * j + 1] = a0i + si;
+        float wr, wi;
+        oracle_twiddle_f32(j, N, &wr, &wi);
+        float p1 = b1r * wr, p2 = b1i * wi, p3 = b1r * wi, p4 = b1i * wr;
+        y[2 * (j + M)] = p1 - p2;
+        y[2 * (j + M) + 1] = p3 + p4;
+        oracle_twiddle_f32(2 * j, N, &wr, &wi);
+        p1 = b2r * wr; p2 = b2i * wi; p3 = b2r * wi; p4 = b2i * wr;
+        y[2 * (j + 2 * M)] = p1 - p2;
+        y[2 * (j + 2 * M) + 1] = p3 + p4;
+    }
+}
+
+static void radix3_stage_f64(double *y, int N)
+{
+    const int M = N / 3;
+    const double c3 = sqrt(3.0) / 2.0;
+    for (int j = 0; j < M; ++j) {
+        double a0r = y[2 * j], a0i = y[2 * j + 1];
+        double a1r = y[2 * (j + M)], a1i = y[2 * (j + M) + 1];
+        double a2r = y[2 * (j + 2 * M)], a2i = y[2 * (j + 2 * M) + 1];
+        double sr = a1r + a2r, si = a1i + a2i;
+        double dr = a1r - a2r, di = a1i - a2i;
+        double mr = a0r - 0.5 * sr, mi = a0i - 0.5 * si;
+        double tr = c3 * dr, ti = c3 * di;
+        double b1r = mr + ti, b1i = mi - tr, b2r = mr - ti, b2i = mi + tr;
+        y[2 * j] = a0r + sr;
+        y[2 * j + 1] = a0i + si;
+        double wr, wi;
+        twiddle(j, N, &wr, &wi);
+        y[2 * (j + M)] = b1r * wr - b1i * wi;
+        y[2 * (j + M) + 1] = b1r * wi + b1i * wr;
+        twiddle(2 * j, N, &wr, &wi);
+        y[2 * (j + 2 * M)] = b2r * wr - b2i * wi;
+        y[2 * (j + 2 * M) + 1] = b2r * wi + b2i * wr;
+    }
+}
+
+/* The radix-3 stage undone without its factor 1/3: the twiddles divided
+ * out, then the 3-point DFT with the conjugate root. */
+static void unradix3_stage_f64(double *y, int N)
+{
+    const int M = N / 3;
+    const double c3 = sqrt(3.0) / 2.0;
+    for (int j = 0; j < M; ++j) {
+        double wr, wi;
+        double b0r = y[2 * j], b0i = y[2 * j + 1];
+        double zr = y[2 * (j + M)], zi = y[2 * (j + M) + 1];
+        twiddle(j, N, &wr, &wi);
+        double b1r = zr * wr + zi * wi, b1i = zi * wr - zr * wi;   /* z conj(W^j) */
+        zr = y[2 * (j + 2 * M)]; zi = y[2 * (j + 2 * M) + 1];
+        twiddle(2 * j, N, &wr, &wi);
+        double b2r = zr * wr + zi * wi, b2i = zi * wr - zr * wi;
+        double sr = b1r + b2r, si = b1i + b2i, dr = b1r - b2r, di = b1i - b2i;
+        double mr = b0r - 0.5 * sr, mi = b0i - 0.5 * si;
+        double tr = c3 * dr, ti = c3 * di;
+        y[2 * j] = b0r + sr;
+        y[2 * j + 1] = b0i + si;
+        y[2 * (j + M)] = mr - ti;          /* m + i t: the conjugate root */
+        y[2 * (j + M) + 1] = mi + tr;
+        y[2 * (j + 2 * M)] = mr + ti;      /* m - i t */
+        y[2 * (j + 2 * M) + 1] = mi - tr;
+    }
+}
+
+/* y <- c * FFT_{D/2}(s (.) y) in fp32: the in-place decimation-in-frequency
+ * FFT over z_j = (y[2j], y[2j+1]) described at the top (a radix-3 stage
+ * first when D/2 is three times a power of two). */
+void oracle_srft_f32(float *y, const float *signs, int D, float c)
+{
+    const int N = D / 2;
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * signs[i];
+    if (N % 3 == 0) {
+        radix3_stage_f32(y, N);
+        for (int b = 0; b < 3; ++b)
+            radix2_stages_f32(y, b * (N / 3), N / 3, N);
+    } else {
+        radix2_stages_f32(y, 0, N, N);
+    }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* The same transform in fp64 (twiddles in double), used on the query. */
+void oracle_srft_f64(double *y, const float *signs, int D, double c)
+{
+    const int N = D / 2;
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * (double)signs[i];
+    if (N % 3 == 0) {
+        radix3_stage_f64(y, N);
+        for (int b = 0; b < 3; ++b)
+            radix2_stages_f64(y, b * (N / 3), N / 3, N);
+    } else {
+        radix2_stages_f64(y, 0, N, N);
+    }
+    for (int i = 0; i < D; ++i)
+        y[i] = y[i] * c;
+}
+
+/* The inverse of oracle_srft_f64 in fp64: y <- s (.) (c * U(y)), where U
+ * undoes the stages in reverse order without their factors 1/2 and 1/3:
+ * together those factors are N, which with the forward c = 1/sqrt(N) makes
+ * the final factor c again. */
+void oracle_unsrft_f64(double *y, const float *signs, int D, double c)
+{
+    const int N = D / 2;
+    if (N % 3 == 0) {
+        for (int b = 0; b < 3; ++b)
+            unradix2_stages_f64(y, b * (N / 3), N / 3, N);
+        unradix3_stage_f64(y, N);
+    } else {
+        unradix2_stages_f64(y, 0, N, N);
+    }
     for (int i = 0; i < D; ++i)
         y[i] = y[i] * c * (double)signs[i];
+}
+
+/* Whether a head width admits rotation kind `kind` (0 = SRHT: a power of
+ * two; 1 = SRFT: D/2 a power of two or three times one). */
+static int rotation_ok(int D, int kind)
+{
+    return kind == 1 ? (D % 2 == 0 && fft_size_ok(D / 2)) : (D & (D - 1)) == 0;
 }
 
 /* K's rotation by kind: 0 = SRHT, 1 = SRFT. */
@@ -439,7 +599,9 @@ int oracle_quantize_rows(const uint16_t *src, int dtype, long N, int D,
                          int nthreads)
 {
     if (D <= 0 || D > 1024 || D % ORACLE_GROUP != 0 || N < 0 || dtype < 0 || dtype > 1 ||
-        rot_kind < 0 || rot_kind > 1 || (D & (D - 1)) != 0 || bits < 2 || bits > 4)
+        rot_kind < 0 || rot_kind > 1 || bits < 2 || bits > 4)
+        return -1;
+    if (signs && !rotation_ok(D, rot_kind))
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -589,7 +751,9 @@ int oracle_sdpa(const uint16_t *q, int dtype, int B, int Hq, int Hkv, int D, lon
 {
     if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || D <= 0 || D > 1024 ||
         D % ORACLE_GROUP != 0 || cap < 0 || dtype < 0 || dtype > 1 || rot_kind < 0 ||
-        rot_kind > 1 || (D & (D - 1)) != 0 || bits < 2 || bits > 4)
+        rot_kind > 1 || bits < 2 || bits > 4)
+        return -1;
+    if ((signs || v_signs) && !rotation_ok(D, rot_kind))
         return -1;
     long R = rows ? nrows : (long)B * Hq;
     if (nthreads < 1)

@@ -23,12 +23,14 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libotq.so")
 ROOT = os.path.dirname(HERE)
 
-SOURCES = ["api.hip", "quantize.hip", "sdpa_vec.hip", "sdpa_mfma.hip", "combine.hip", "order.hip", "bits.hip"]
+SOURCES = ["api.hip", "quantize.hip", "sdpa_vec.hip", "sdpa_mfma.hip", "combine.hip", "order.hip", "bits.hip",
+           "wide.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
           "-Wall", "-Wno-unused-function", "-I", os.path.join(ROOT, "include")]
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"], "bits.hip": ["-ffp-contract=off"],
+            "wide.hip": ["-ffp-contract=off"],
             # keep MFMA accumulators in VGPRs: they are rescaled by VALU ops
             "sdpa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 

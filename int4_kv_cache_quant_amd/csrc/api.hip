@@ -75,7 +75,9 @@ constexpr int kTargetWaves = 1024;  // split waves aimed for (one per SIMD)
 constexpr int kOrderedWaveFactor = 8;  // measured on the ragged 32-sequence batch: chunk 2048 over 8192
 constexpr int kMaxSplits = 16384;
 
-bool supported_dim(int D) { return D == 64 || D == 128 || D == 256; }
+// Power-of-two widths take every kernel; 192 (three times 64) the wide ones.
+bool pow2_dim(int D) { return D == 64 || D == 128 || D == 256; }
+bool supported_dim(int D) { return pow2_dim(D) || otq::wide_supported_dim(D); }
 
 int check_dims(int32_t B, int32_t H, int32_t D, int32_t cap)
 {
@@ -103,6 +105,13 @@ int check_cache(const otq_cache* c)
     if ((c->k_rot_signs || c->v_rot_signs) && c->rot_kind != OTQ_ROT_SRHT && c->rot_kind != OTQ_ROT_SRFT)
         return OTQ_EINVAL;
     if (c->code_bits != 0 && c->code_bits != 2 && c->code_bits != 3 && c->code_bits != 4) return OTQ_EINVAL;
+    if (!pow2_dim(c->head_dim)) {
+        // the wide widths: int4 codes; K rotated by the FFT kind only (the
+        // Hadamard form needs a power of two); V unrotated
+        if (c->code_bits != 0 && c->code_bits != 4) return OTQ_EUNSUPPORTED;
+        if (c->k_rot_signs && c->rot_kind != OTQ_ROT_SRFT) return OTQ_EUNSUPPORTED;
+        if (c->v_rot_signs) return OTQ_EUNSUPPORTED;
+    }
     return OTQ_OK;
 }
 
@@ -128,13 +137,18 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     if (G > 16) return OTQ_EUNSUPPORTED;
 
     int variant = variant_ov;
-    if (variant == OTQ_VARIANT_AUTO) {
+    if (!pow2_dim(D)) {  // the wide split pass is vector arithmetic, any G <= 16
+        if (variant == OTQ_VARIANT_AUTO) variant = OTQ_VARIANT_VECTOR;
+        if (variant == OTQ_VARIANT_MFMA) return OTQ_EUNSUPPORTED;
+    } else if (variant == OTQ_VARIANT_AUTO) {
         // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
         variant = code_bits(c) != 4                      ? OTQ_VARIANT_VECTOR
                   : otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA
                                                    : OTQ_VARIANT_VECTOR;
     }
-    if (code_bits(c) != 4) {  // the b-bit split pass: vector arithmetic, any G <= 16
+    if (!pow2_dim(D)) {
+        if (variant != OTQ_VARIANT_VECTOR) return OTQ_EINVAL;
+    } else if (code_bits(c) != 4) {  // the b-bit split pass: vector arithmetic, any G <= 16
         if (variant != OTQ_VARIANT_VECTOR) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_VECTOR) {
         if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;
@@ -216,6 +230,7 @@ int otq_cache_array_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, int32_t 
     if (rc != OTQ_OK) return rc;
     const int bits = code_bits == 0 ? 4 : code_bits;
     if (bits != 2 && bits != 3 && bits != 4) return OTQ_EINVAL;
+    if (bits != 4 && !pow2_dim(D)) return OTQ_EUNSUPPORTED;  // the wide widths hold int4 codes
     const size_t n = (size_t)B * H * cap;
     if (codes_bytes) *codes_bytes = n * (size_t)(D * bits / 8);
     if (scales_bytes) *scales_bytes = n * (size_t)(D / OTQ_GROUP) * sizeof(float);
@@ -256,6 +271,13 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
     if (n_new > cache->capacity) return OTQ_ECAPACITY;
     unsigned* err = error_word();
     if (!err) return OTQ_EDEVICE;
+    if (!pow2_dim(cache->head_dim)) {
+        const hipError_t e = otq::launch_quantize_wide(
+            k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
+            cache->k_codes, cache->k_scales, cache->v_codes, cache->v_scales, cache->k_rot_signs,
+            cache->rot_norm, cache->k_chan_scale, cache->v_rot_signs, pos, err, static_cast<hipStream_t>(stream));
+        return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
+    }
     if (code_bits(cache) != 4) {
         const hipError_t e = otq::launch_quantize_bits(
             k, v, dtype, n_new, cache->batch, cache->num_kv_heads, cache->head_dim, cache->capacity,
@@ -361,7 +383,8 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
             return OTQ_EDEVICE;
         a.items = items;
     }
-    const hipError_t e = code_bits(cache) != 4 ? otq::launch_split_bits(a, code_bits(cache), s)
+    const hipError_t e = !pow2_dim(D)            ? otq::launch_split_wide(a, s)
+                         : code_bits(cache) != 4 ? otq::launch_split_bits(a, code_bits(cache), s)
                          : chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
                                                            : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
@@ -476,6 +499,7 @@ int check_decode_append(const void* q, const void* k_new, const void* v_new, int
     if (rc != OTQ_OK) return rc;
     if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
     if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
+    if (!pow2_dim(cache->head_dim)) return OTQ_EUNSUPPORTED;  // its combine has power-of-two forms only
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;
     return OTQ_OK;

@@ -320,7 +320,8 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
     // whole rows for a rotated V, for the append with a rotated K, and for a
     // plain combine whose slices would take more than one round of resident
     // blocks (2048)
-    const bool big = !append && (long)a.B * a.Hq * (a.D / kCh) > 2048;
+    const bool pow2 = a.D == 64 || a.D == 128 || a.D == 256;  // the whole-row forms' widths
+    const bool big = !append && pow2 && (long)a.B * a.Hq * (a.D / kCh) > 2048;
     const bool rows = vrot || (append && rot) || big;
     dim3 grid(a.B * a.Hq, rows ? 1 : a.D / kCh), block(kThreads);
     if (!append && !rows) {

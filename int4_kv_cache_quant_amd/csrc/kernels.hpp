@@ -61,6 +61,16 @@ hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_n
                                 const int32_t* pos, const BitsRot& rot, unsigned* err, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
 
+// Head widths that are multiples of 64 but not powers of two (192): the
+// append (K optionally rotated by the mixed-radix FFT, V optionally too) and
+// the split pass (any G <= 16) for the int4 layouts.
+bool wide_supported_dim(int D);
+hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
+                                int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs, const float* signs,
+                                float rot_norm, const float* lam, const float* vsigns, const int32_t* pos,
+                                unsigned* err, hipStream_t stream);
+hipError_t launch_split_wide(const SplitArgs& a, hipStream_t stream);
+
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
 hipError_t launch_split_vector(const SplitArgs& a, hipStream_t stream);
 // Largest batch whose split blocks are ordered longest first.

@@ -124,6 +124,7 @@ def test_quantize_append_host_errors():
     assert call(FAKE, FAKE, 2, 1, d, FAKE) == otq.OTQ_EUNSUPPORTED
     assert call(FAKE, FAKE, 1, 65, d, FAKE) == otq.OTQ_ECAPACITY
     assert call(FAKE, FAKE, 1, 1, _desc(D=96), FAKE) == otq.OTQ_EUNSUPPORTED
+    assert call(FAKE, FAKE, 1, 1, _desc(D=160), FAKE) == otq.OTQ_EUNSUPPORTED
     assert call(FAKE, FAKE, 1, 1, _desc(cap=40), FAKE) == otq.OTQ_EINVAL
     bad = _desc()
     bad.v_scales = None
@@ -323,3 +324,37 @@ def test_noalloc_scratch_limit_on_host():
     ps = otq.otq_sdpa_plan(4, small, 256)
     assert lib.otq_sdpa_int4_decode_append_noalloc(P(0), P(FAKE), P(FAKE), 1, 4, ctypes.byref(small), P(FAKE),
                                                    256, 0.1, P(FAKE), ctypes.byref(ps), None) == otq.OTQ_EINVAL
+
+
+def test_head_dim_192_host_checks():
+    """head_dim 192 (D/2 = 3 * 32): int4 only, K rotated by the FFT kind only
+    (the Hadamard form needs a power of two), V unrotated, the split pass's
+    vector variant only, no fused append; sizes by the int4 closed form."""
+    lib = otq.lib()
+    P = ctypes.c_void_p
+    cb, sb = otq.otq_cache_array_bytes(2, 3, 192, 64, 4)
+    assert cb == 2 * 3 * 64 * 96 and sb == 2 * 3 * 64 * 6 * 4
+    assert lib.otq_cache_bytes(1, 1, 192, 64, 2) == 0   # no b-bit codes at this width
+    plan = lambda desc, variant=0: otq.otq_sdpa_plan(8, desc, 64, variant=variant, check=False)
+    d = _desc(D=192)
+    rc, p = plan(d)
+    assert rc == otq.OTQ_OK and p.variant == otq.OTQ_VARIANT_VECTOR
+    assert plan(d, otq.OTQ_VARIANT_MFMA)[0] == otq.OTQ_EUNSUPPORTED
+    r = _desc(D=192, signs=FAKE)
+    r.rot_kind = otq.OTQ_ROT_SRFT
+    assert plan(r)[0] == otq.OTQ_OK
+    r.rot_kind = otq.OTQ_ROT_SRHT
+    assert plan(r)[0] == otq.OTQ_EUNSUPPORTED
+    vr = _desc(D=192)
+    vr.v_rot_signs = FAKE
+    vr.rot_kind = otq.OTQ_ROT_SRFT
+    assert plan(vr)[0] == otq.OTQ_EUNSUPPORTED
+    b3 = _desc(D=192)
+    b3.code_bits = 3
+    assert plan(b3)[0] == otq.OTQ_EUNSUPPORTED
+    ws = lib.otq_sdpa_workspace_bytes(8, ctypes.byref(d), 64)
+    rc = lib.otq_sdpa_int4_decode_append(P(FAKE), P(FAKE), P(FAKE), 1, 8, ctypes.byref(d), P(FAKE), 64,
+                                         ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws), None, None)
+    assert rc == otq.OTQ_EUNSUPPORTED
+    for bad in (96, 160, 320):
+        assert lib.otq_cache_bytes(1, 1, bad, 64, 4) == 0

@@ -12,15 +12,20 @@
 // page, section on numerical stability).
 //
 // Exactness of the products:
-//  * K and V codes enter the MFMAs as signed normal fp16 integers: a
-//    nibble's offset-binary value n = c + 8 goes into the mantissa of 1024.0
-//    (whose ulp is 1), at bit 0 or bit 4 of a 16-bit half, so one shift and
-//    four and-xor operations give the eight operands of a 32-bit word, and
-//    one packed fp16 subtraction per pair leaves c (or 16 c for a bit-4
-//    nibble) exactly; the 16 of the bit-4 nibbles is cancelled exactly by a
-//    power of two on the other operand.  Every product is exact and the sums
-//    are fp32: no offset term, and no subnormal operand, whose rounding
-//    would grow with the scores or with the context;
+//  * K codes enter the score MFMAs as fp16 subnormals of their offset-binary
+//    value n = c + 8: a nibble left at bit 0 (or bit 4) of a 16-bit half
+//    reads as n * 2^-24 (or n * 2^-20), so one shift and four masks give all
+//    eight operands of a 32-bit word; the 2^4 of the bit-4 nibbles is
+//    cancelled exactly by a power of two on the q operand, the +8 by starting
+//    the score accumulator at -8 * 2^-24 * sum(q) (a shift shared by every
+//    token of a query head's score), and 2^24 is folded into the softmax
+//    scale.  The score's rounding is per token and does not accumulate;
+//  * V codes enter the value MFMAs as signed normal fp16 integers: a
+//    nibble's offset-binary value goes into the mantissa of 1024.0 (whose
+//    ulp is 1) and one packed fp16 subtraction per pair leaves c (or 16 c for
+//    a bit-4 nibble) exactly, so every value product is exact and the sums
+//    are plain fp32: no offset term whose rounding would grow with the
+//    context (the 16 of the bit-4 nibbles is cancelled on p);
 //  * q is converted to fp16 after each query head's row is scaled by a power
 //    of two that puts its largest |element| in [2^14, 2^15) (bf16 inputs of
 //    any magnitude fit, and the factor is undone in the softmax scale); bf16
@@ -90,10 +95,31 @@ constexpr int kVLimit = 15;
 constexpr int kEMin = -120, kEMax = 165;
 
 // MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
-// word, scaled by 2^kShift[e]: registers are (0,4), (1,5), (2,6), (3,7),
-// each one mask of the word or of the word shifted by 8 bits.
+// word, scaled by 2^kShift[e] (times 2^-24 for the subnormal form):
+// registers are (0,4), (1,5), (2,6), (3,7), each one mask of the word or of
+// the word shifted by 8 bits.
 constexpr int kSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
 constexpr int kShift[8] = {0, 0, 4, 4, 0, 0, 4, 4};
+
+// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^(kShift[e] - 24) (the K
+// operand of the score products).
+__device__ __forceinline__ half8_t unpack_codes_sub(uint32_t w)
+{
+    const uint32_t w8 = w >> 8;
+    uint32_t r[4];
+    r[0] = (w ^ 0x88888888u) & 0x000F000Fu;
+    r[1] = (w ^ 0x88888888u) & 0x00F000F0u;
+    r[2] = (w8 ^ 0x00888888u) & 0x000F000Fu;
+    r[3] = (w8 ^ 0x00888888u) & 0x00F000F0u;
+    half8_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const half2_t p = __builtin_bit_cast(half2_t, r[m]);
+        out[2 * m] = p[0];
+        out[2 * m + 1] = p[1];
+    }
+    return out;
+}
 
 // 8 signed nibbles -> 8 normal fp16 values c * 2^kShift[e] (exact): the
 // offset-binary value n = c + 8 of a nibble goes into the mantissa of 1024.0
@@ -121,20 +147,30 @@ __device__ __forceinline__ half8_t unpack_codes_signed(uint32_t w)
 
 // fp16 (x0 - h0, x1 - h1) packed, where (h0, h1) = h2 are x0, x1 rounded to
 // fp16: the differences are exact in fp32 and rounded once (v_fma_mix with
-// an fp16 operand; register-only instructions).  The result feeds an MFMA,
+// an fp16 operand; register-only instructions).  The results feed an MFMA,
 // which must not read a VGPR within 2 wait states of a VALU write; the
-// compiler counts no wait states for instructions inside inline asm, so the
-// asm ends with them (without, the MFMA could read the register's previous
-// contents: measured, the lo half of p * s_v was lost).
+// compiler counts no wait states for instructions inside inline asm (without
+// them the MFMA read the registers' previous contents: measured, the lo half
+// of p * s_v was lost).  The MFMA reads the four pairs of a group together,
+// so only the last of them (LAST) ends with the two wait states: the others
+// were written earlier still.
 typedef uint32_t v4u_t __attribute__((ext_vector_type(4)));
+template <bool LAST>
 __device__ __forceinline__ uint32_t lo_pair(float x0, float x1, uint32_t h2)
 {
     uint32_t r;
-    asm("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
-        "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
-        "s_nop 1"
-        : "=&v"(r)
-        : "v"(x0), "v"(x1), "v"(h2));
+    if constexpr (LAST) {
+        asm volatile("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+                     "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]\n\t"
+                     "s_nop 1"
+                     : "=&v"(r)
+                     : "v"(x0), "v"(x1), "v"(h2));
+    } else {
+        asm volatile("v_fma_mixlo_f16 %0, %1, 1.0, -%3 op_sel_hi:[0,0,1]\n\t"
+                     "v_fma_mixhi_f16 %0, %2, 1.0, -%3 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+                     : "=&v"(r)
+                     : "v"(x0), "v"(x1), "v"(h2));
+    }
     return r;
 }
 
@@ -347,10 +383,17 @@ constexpr bool kScaleRows = D <= 128 && !(HILO && P == 2);
 template <int D, int P, bool HILO>
 constexpr bool kRefillAfterScores = D <= 128 && !(HILO && P == 2);
 
-// Waves per SIMD the register allocation must allow: 2 (up to 256 VGPRs)
-// except at head_dim 256, whose accumulators alone take 64 VGPRs per head.
+// Waves per SIMD the register allocation must allow: 2 (up to 256 VGPRs),
+// so that a second block on the CU can hide the first one's latencies.
 template <int D>
-constexpr int kWavesPerEU = D == 256 ? 1 : 2;
+constexpr int kWavesPerEU = 2;
+
+// Where the score accumulator starts at the offset correction (a register
+// quad per group, live through the loop) rather than taking it after the
+// MFMA (four adds per group and sub-tile): everywhere but head_dim 256 with
+// hi + lo q operands, whose registers are full.
+template <int D, bool HILO>
+constexpr bool kQinitInAcc = !(D == 256 && HILO);
 
 // Whether the query prologue loads K's channel scales together with q and the
 // rotation signs (before the first tile's copies), or only once the rotation
@@ -651,19 +694,30 @@ void split_mfma_kernel(SplitArgs a)
     // query head n16 in the set of head jl and zeros in the others; k slot e
     // = channel 32 g + 8 r + kSlot[e].
     half8_t qb[P][NG], qb_lo[HILO ? P : 1][HILO ? NG : 1];
+    floatx4_t qinit4[kQinitInAcc<D, HILO> ? NG : 1];
+    float qinit1[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
         half8_t hv, lv;
+        float tq = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float x = qx[g][kSlot[e]];
             const _Float16 h16 = (_Float16)x;
             const _Float16 l16 = (_Float16)(x - (float)h16);
             // cancel the code's 2^kShift (a power of two)
-            const float down = kShift[e] ? 0.0625f : 1.0f;
+            const float down = kShift[e] ? 0.0625f : 1.0f, up = kShift[e] ? 16.0f : 1.0f;
             hv[e] = (_Float16)((float)h16 * down);
-            if (HILO) lv[e] = (_Float16)((float)l16 * down);
+            tq += (float)hv[e] * up;
+            if (HILO) {
+                lv[e] = (_Float16)((float)l16 * down);
+                tq += (float)lv[e] * up;
+            }
         }
+        // the score accumulator starts at -8 * 2^-24 * sum(q over the group)
+        const float qi = -8.0f * 0x1p-24f * sum_xor32(sum_xor16(tq));
+        if constexpr (kQinitInAcc<D, HILO>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
+        qinit1[g] = qi;
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             const bool mine = col_valid && j == jl;
@@ -674,7 +728,7 @@ void split_mfma_kernel(SplitArgs a)
             }
         }
     }
-    const float qmul = __builtin_ldexpf(HILO && rot ? a.qscale * a.rot_norm : a.qscale, -qk);
+    const float qmul = __builtin_ldexpf((HILO && rot ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f, -qk);
 
     float m_run = kNegInf;  // softmax reference M of column n16 (>= its running max)
     int e_v = 0;            // E (wave-uniform): the value operand carries 2^E
@@ -737,18 +791,19 @@ void split_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
             static_for<NG>([&](auto gI) {
                 constexpr int g = decltype(gI)::value;
-                floatx4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+                floatx4_t d = kQinitInAcc<D, HILO> ? qinit4[g] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
-                    const half8_t A = unpack_codes_signed(t.kw[j][s][g]);
+                    const half8_t A = unpack_codes_sub(t.kw[j][s][g]);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb[j][g], d, 0, 0, 0);
                     if constexpr (HILO) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qb_lo[j][g], d, 0, 0, 0);
                 }
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
                     float term;
-                    if constexpr (ROWS) term = t.sk[s][i % (ROWS ? 4 : 1)][g] * d[i];
-                    else term = quad_bcast<i>(t.sk[s][0][g]) * d[i];  // folds into v_mul_f32_dpp
+                    const float di = kQinitInAcc<D, HILO> ? d[i] : d[i] + qinit1[g];
+                    if constexpr (ROWS) term = t.sk[s][i % (ROWS ? 4 : 1)][g] * di;
+                    else term = quad_bcast<i>(t.sk[s][0][g]) * di;  // folds into v_mul_f32_dpp
                     tot[i] = (g == 0) ? term : tot[i] + term;
                 });
             });
@@ -849,7 +904,7 @@ void split_mfma_kernel(SplitArgs a)
                 const float x0 = p[0][m] * quad_bcast<m>(t.sv[0][g]);
                 const float x1 = p[1][m] * quad_bcast<m>(t.sv[1][g]);
                 ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
-                la[m] = lo_pair(x0, x1, ha[m]);
+                la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
             });
             const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
 #pragma unroll

@@ -119,10 +119,17 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, help="workload number (3 = 70B layer at 128K)")
+    ap.add_argument("--also", default="1,2,4,5",
+                    help="other workloads timed in the same run (step and split only), comma-separated; "
+                         "'' for none")
     ap.add_argument("--layers", type=int, default=None, help="distinct caches (default: the workload's)")
     ap.add_argument("--chunk", type=int, default=0, help="force the split chunk (0 = planner default)")
+    ap.add_argument("--splits", type=int, default=0,
+                    help="force the split count (0 = planner default; below max_len / chunk the pieces "
+                         "interleave)")
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a graph")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling probe")
     ap.add_argument("--chan-scale", action="store_true",
                     help="give K a per-channel scale (seeded; 1/multiplier on the outlier channels)")
     ap.add_argument("--v-rotate", action="store_true",
@@ -135,8 +142,10 @@ def main():
                          "workload that does not rotate it")
     ap.add_argument("--code-bits", type=int, default=4, choices=(2, 3, 4),
                     help="code width of the caches; 2 and 3 take the b-bit path (no rotation or channel "
-                         "scale; the step is the append kernel, then split + combine)")
-    ap.add_argument("--cpu-threads", type=int, default=None)
+                         "scale)")
+    ap.add_argument("--cpu-threads", type=int, default=None,
+                    help="threads of the multi-threaded oracle leg (default: the cores this process may "
+                         "use, at most 16)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device-to-device copy of this many MiB (5 times), "
                          "whose counter readings calibrate FETCH_SIZE / WRITE_SIZE")
@@ -157,11 +166,9 @@ def main():
               "in the design document).", file=sys.stderr, flush=True)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import int4_kv_cache_quant_amd as otq
-    from int4_kv_cache_quant_amd import synth
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -169,11 +176,6 @@ def main():
     otq.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = synth.WORKLOADS[args.workload]
-    L = w.layers if args.layers is None else args.layers
-    log(f"bench: workload {args.workload} {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
-        f"T={w.T} layers={L}")
-
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * 2**20 // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -184,22 +186,126 @@ def main():
         log(f"bench: copy calibration {args.copy_calibration_mib} MiB x 5 done")
         del src, dst
 
+    rec = bench_workload(args.workload, args, primary=True)
+    others = []
+    for tok in [t for t in args.also.split(",") if t.strip()]:
+        wn = int(tok)
+        if wn == args.workload:
+            continue
+        torch.cuda.empty_cache()
+        others.append(bench_workload(wn, args, primary=False))
+    rec["other_workloads"] = others
+    print(json.dumps(rec), flush=True)
+
+
+def stream_ceiling(torch, otq, dev, nbytes, copies, steps):
+    """The streaming-read rate of this GPU for reads of nbytes per launch:
+    the probe kernel over `copies` distinct buffers (as the split pass cycles
+    over distinct caches), replayed in a graph; the best of a few grid sizes."""
+    nbytes = (nbytes + 15) // 16 * 16
+    bufs = [torch.full((nbytes // 4,), i + 1, dtype=torch.int32, device=dev) for i in range(copies)]
+    best = None
+    sweep = {}
+    for blocks in (512, 1024, 2048, 4096, 8192):
+        sink = torch.empty(blocks, dtype=torch.int32, device=dev)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for b in bufs:
+                otq.otq_stream_read_probe(b, sink, nbytes=nbytes, blocks=blocks)
+        g.replay()
+        torch.cuda.synchronize()
+        a, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            g.replay()
+        e.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(e) * 1000.0 / (steps * copies)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        log(f"bench: stream ceiling {nbytes / 2**20:.1f} MiB x {copies}, {blocks} blocks: {us:.2f} us, "
+            f"{gbps:.0f} GB/s")
+        sweep[blocks] = round(gbps, 1)
+        if best is None or gbps > best["GBps"]:
+            best = {"GBps": round(gbps, 1), "us_per_launch": round(us, 3), "blocks": blocks}
+        del g, sink
+    del bufs
+    torch.cuda.empty_cache()
+    best.update({"kernel": "stream_read (otq_stream_read_probe)", "bytes_per_launch": int(nbytes),
+                 "buffers": copies, "frac_of_peak": round(best["GBps"] / HBM_PEAK_GBPS, 4),
+                 "GBps_by_blocks": sweep})
+    return best
+
+
+def oracle_cache(oracle, w, host_kv0, rot_norm, rot_kind, bits, threads):
+    """Layer 0's K/V quantised by the oracle (not timed)."""
+    kb, vb, sg, lam0, vsg0 = host_kv0
+    kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=rot_norm, threads=threads,
+                             chan_scale=lam0, rot_kind=rot_kind, code_bits=bits)
+    vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=rot_norm, threads=threads,
+                             rot_kind=rot_kind, code_bits=bits)
+    return kc, ks, vc, vs
+
+
+def oracle_leg(oracle, w, host_kv0, qc, q0, rot_norm, rot_kind, bits, threads, budget_s, max_reps):
+    """The oracle's fp64 layer-step of layer 0 on `threads` threads, repeated
+    until budget_s of wall time (at least once, at most max_reps times)."""
+    _, _, sg, lam0, vsg0 = host_kv0
+    kc, ks, vc, vs = qc
+    lens0 = synth_lens(w)
+    reps = 0
+    t = time.perf_counter()
+    while True:
+        ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg, rot_norm=rot_norm,
+                          threads=threads, chan_scale=lam0, v_signs=vsg0, rot_kind=rot_kind, code_bits=bits)
+        reps += 1
+        if time.perf_counter() - t >= budget_s or reps >= max_reps:
+            break
+    return ref, (time.perf_counter() - t) / reps, reps
+
+
+def synth_lens(w):
+    from int4_kv_cache_quant_amd import synth
+    return synth.lens(w, 0)
+
+
+def bench_workload(wnum, args, primary):
+    """Build the workload's caches, time the step, and (for the primary
+    workload) the per-kernel durations, bulk append, streaming ceiling and
+    the CPU oracle legs.  Returns the record."""
+    import numpy as np
+    import torch
+
+    import int4_kv_cache_quant_amd as otq
+    from int4_kv_cache_quant_amd import synth
+
+    dev = torch.device("cuda:0")
+    w = synth.WORKLOADS[wnum]
+    L = w.layers if (args.layers is None or not primary) else args.layers
+    log(f"bench: workload {wnum} {w.name}: B={w.B} Hq={w.Hq} Hkv={w.Hkv} D={w.D} "
+        f"T={w.T} layers={L}")
+
     # ---------------------------------------------------------------- setup
     rot_kind = "srft" if args.srft else "srht"
     bits = args.code_bits
-    if bits != 4 and (args.srft or args.srht or args.chan_scale or args.v_rotate or w.rotate):
-        sys.exit("bench.py: 2- and 3-bit caches take no rotation or channel scale")
+    extra_rot = primary and (args.srft or args.srht)
+    chan = primary and args.chan_scale
+    vrot = primary and args.v_rotate
+    if bits != 4 and (extra_rot or chan or vrot or w.rotate):
+        if primary:
+            sys.exit("bench.py: 2- and 3-bit caches take no rotation or channel scale")
+        log(f"bench: workload {wnum} rotates K: timed with 4-bit codes")
+    wbits = 4 if (bits != 4 and w.rotate) else bits
     if args.srft and args.srht:
         sys.exit("bench.py: --srft and --srht name two different K rotations")
     t_setup = time.time()
     caches, k_new, v_new, qs, lens_l, pos_l = [], [], [], [], [], []
     host_kv0 = None
     for l in range(L):
-        signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if (w.rotate or args.srft or args.srht) else None
-        lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if args.chan_scale else None
-        vsg = torch.from_numpy(synth.v_rot_signs(w, l)).to(dev) if args.v_rotate else None
+        signs = torch.from_numpy(synth.rot_signs(w, l)).to(dev) if (w.rotate or extra_rot) else None
+        lam = torch.from_numpy(synth.chan_scale(w, l)).to(dev) if chan else None
+        vsg = torch.from_numpy(synth.v_rot_signs(w, l)).to(dev) if vrot else None
         cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=signs,
-                                chan_scale=lam, v_rot_signs=vsg, rot_kind=rot_kind, code_bits=bits)
+                                chan_scale=lam, v_rot_signs=vsg, rot_kind=rot_kind, code_bits=wbits)
         k = synth.kv(w, l, "k", device=dev)
         v = synth.kv(w, l, "v", device=dev)
         lens = synth.lens(w, l)
@@ -212,7 +318,7 @@ def main():
         ar = torch.arange(w.B, device=dev)
         k_new.append(k[ar, :, idx].contiguous())  # [B, Hkv, D]: the token at lens - 1
         v_new.append(v[ar, :, idx].contiguous())
-        if l == 0 and not args.no_cpu:
+        if l == 0 and primary and not args.no_cpu:
             host_kv0 = (synth.bits(k), synth.bits(v), None if signs is None else signs.cpu().numpy(),
                         None if lam is None else lam.cpu().numpy(),
                         None if vsg is None else vsg.cpu().numpy())
@@ -225,7 +331,8 @@ def main():
             torch.cuda.synchronize()
             log(f"bench: built {l + 1}/{L} caches ({time.time() - t_setup:.1f}s)")
     max_len = int(max(int(x.max()) for x in lens_l))
-    plan = caches[0].plan(w.Hq, max_len, chunk=args.chunk)
+    plan = caches[0].plan(w.Hq, max_len, chunk=args.chunk if primary else 0,
+                          splits=args.splits if primary else 0)
     ws = caches[0].workspace(w.Hq, max_len, plan)
     outs = [torch.empty((w.B, w.Hq, w.D), dtype=torch.float32, device=dev) for _ in range(L)]
     torch.cuda.synchronize()
@@ -233,7 +340,7 @@ def main():
     log(f"bench: setup {time.time() - t_setup:.1f}s, cache {cache_bytes / 2**30:.2f} GiB, "
         f"plan chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
 
-    def append(l):  # the separate append kernel (timed for reference; the step fuses it)
+    def append(l):  # the separate append kernel (timed for reference; the 4-bit step fuses it)
         otq.otq_quantize_append(k_new[l][:, :, None], v_new[l][:, :, None], caches[l].desc, pos_l[l])
 
     def split(l):
@@ -243,7 +350,7 @@ def main():
         otq.otq_sdpa_lse_combine(w.Hq, caches[l].desc, lens_l[l], max_len, ws, plan, outs[l])
 
     def fused(l):  # split over the cached tokens, then the combine that appends the new token
-        if bits != 4:  # b-bit caches: the append kernel, then split + combine over lens
+        if wbits != 4:  # b-bit caches: the append kernel, then split + combine over lens
             append(l)
             split(l)
             combine(l)
@@ -316,11 +423,11 @@ def main():
 
     timer = kernel_avg_us if graph is None else graph_avg_us
     split_us = timer(split)
-    combine_us = timer(combine)
-    append_us = timer(append)
+    combine_us = timer(combine) if primary else None
+    append_us = timer(append) if primary else None
     torch.cuda.synchronize()
     sdpa_graph_us = None
-    if graph is not None:
+    if graph is not None and primary:
         g2 = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g2):
             for l in range(L):
@@ -336,8 +443,26 @@ def main():
         b.record()
         torch.cuda.synchronize()
         sdpa_graph_us = a.elapsed_time(b) * 1000.0 / (args.steps * L)
-    log(f"bench: split {split_us:.2f} us, combine {combine_us:.2f} us, append (unfused kernel) {append_us:.2f} us, "
+    log(f"bench: split {split_us:.2f} us, combine {combine_us} us, append (unfused kernel) {append_us} us, "
         f"sdpa (split+combine, graph) {sdpa_graph_us} us per layer")
+
+    # algorithmic bytes: packed codes + fp32 scales of every attended token, q read; out write
+    lens_sum = [int(x.long().sum()) for x in lens_l]
+    unit = w.Hkv * 2 * (w.D * wbits // 8 + 4 * (w.D // 32))     # bytes per attended token (K+V)
+    split_bytes = float(np.mean([s * unit for s in lens_sum])) + w.B * w.Hq * w.D * 2
+    layer_bytes = split_bytes + w.B * w.Hq * w.D * 4
+    achieved = split_bytes / (split_us * 1e-6) / 1e9
+    step_gbps = layer_bytes / (us_layer_step * 1e-6) / 1e9
+    kname = "split_bits" if wbits != 4 else ("split_mfma" if plan.variant == 2 else "split_vec")
+    if not primary:
+        del caches, outs, ws, qs, k_new, v_new
+        return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+                "context": w.T, "layers": L, "code_bits": wbits, "chunk": plan.chunk,
+                "num_splits": plan.num_splits, "kernel": kname,
+                "us_layer_step": round(us_layer_step, 3), "split_us": round(split_us, 3),
+                "split_GBps": round(achieved, 1), "split_frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "step_GBps": round(step_gbps, 1), "step_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                "algorithmic_bytes_per_split_launch": int(split_bytes)}
 
     # ---------------------------------------------------------------- bulk append (cache build)
     # Chunks of the workload's K/V quantised into a scratch cache of the same
@@ -349,7 +474,7 @@ def main():
                for i in range(n_chunks)]
     scratch = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=dev, rot_signs=caches[0].rot_signs,
                               chan_scale=caches[0].chan_scale, v_rot_signs=caches[0].v_rot_signs,
-                              rot_kind=rot_kind, code_bits=bits)
+                              rot_kind=rot_kind, code_bits=wbits)
     bulk_pos = [torch.full((w.B,), i * n_bulk, dtype=torch.int32, device=dev) for i in range(n_chunks)]
 
     def bulk_pass():
@@ -373,58 +498,71 @@ def main():
     b.record()
     torch.cuda.synchronize()
     bulk_us = a.elapsed_time(b) * 1000.0 / (reps * n_chunks)
-    bulk_bytes = w.B * w.Hkv * n_bulk * (2 * w.D * 2 + 2 * (w.D * bits // 8 + 4 * (w.D // 32)))
+    bulk_bytes = w.B * w.Hkv * n_bulk * (2 * w.D * 2 + 2 * (w.D * wbits // 8 + 4 * (w.D // 32)))
     log(f"bench: bulk append of {n_bulk} tokens x {w.B * w.Hkv} heads: {bulk_us:.2f} us, "
         f"{bulk_bytes / (bulk_us * 1e-6) / 1e9:.0f} GB/s")
     del bulk_in, scratch
+    if graph is not None:
+        del gb
+    torch.cuda.empty_cache()
 
-    # algorithmic bytes: packed codes + fp32 scales of every attended token, q read; out write
-    lens_sum = [int(x.long().sum()) for x in lens_l]
-    unit = w.Hkv * 2 * (w.D * bits // 8 + 4 * (w.D // 32))     # bytes per attended token (K+V)
-    split_bytes = float(np.mean([s * unit for s in lens_sum])) + w.B * w.Hq * w.D * 2
-    layer_bytes = split_bytes + w.B * w.Hq * w.D * 4
-    achieved = split_bytes / (split_us * 1e-6) / 1e9
-    traffic = traffic_from_profile(plan.variant, w.name) if bits == 4 else None
+    ceiling = None
+    if not args.no_ceiling:
+        ceiling = stream_ceiling(torch, otq, dev, int(split_bytes), min(L, 16), max(4, args.steps // 2))
+        ceiling["split_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
+        ceiling["step_frac_of_ceiling"] = round(step_gbps / ceiling["GBps"], 4)
+
+    traffic = traffic_from_profile(plan.variant, w.name) if wbits == 4 else None
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     check = None
     if host_kv0 is not None:
         import oracle
-        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
-        kb, vb, sg, lam0, vsg0 = host_kv0
-        t = time.time()
-        kc, ks = oracle.quantize(kb, w.dtype, signs=sg, rot_norm=caches[0].rot_norm, threads=threads,
-                                 chan_scale=lam0, rot_kind=rot_kind, code_bits=bits)
-        vc, vs = oracle.quantize(vb, w.dtype, signs=vsg0, rot_norm=caches[0].rot_norm, threads=threads,
-                                 rot_kind=rot_kind, code_bits=bits)
-        log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s")
-        lens0 = synth.lens(w, 0)
+        try:
+            share = len(os.sched_getaffinity(0))
+        except AttributeError:
+            share = os.cpu_count() or 1
+        threads = args.cpu_threads or min(16, share)
         q0 = synth.bits(qs[0])
-        # the same layer-step repeated until about 10 s of CPU work (at most 200 times)
-        reps = 0
-        t = time.perf_counter()
-        while True:
-            ref = oracle.sdpa(q0, w.dtype, kc, ks, vc, vs, lens0, w.scale, signs=sg,
-                              rot_norm=caches[0].rot_norm, threads=threads, chan_scale=lam0, v_signs=vsg0,
-                              rot_kind=rot_kind, code_bits=bits)
-            reps += 1
-            if time.perf_counter() - t >= 10.0 or reps >= 200:
-                break
-        cpu_s = (time.perf_counter() - t) / reps
+        rot_norm = caches[0].rot_norm
+        t = time.time()
+        qc = oracle_cache(oracle, w, host_kv0, rot_norm, rot_kind, wbits, threads)
+        log(f"bench: oracle quantised layer 0 in {time.time() - t:.1f}s on {threads} threads")
+        tok = int(np.asarray(synth.lens(w, 0), dtype=np.int64).sum())
+        legs = []
+        ref = None
+        for nt, budget, max_reps in ((1, 10.0, 50), (threads, 10.0, 200)):
+            ref_n, sdpa_s, nrep = oracle_leg(oracle, w, host_kv0, qc, q0, rot_norm, rot_kind, wbits,
+                                             nt, budget, max_reps)
+            ref = ref_n if ref is None else ref
+            log(f"bench: oracle on {nt} thread(s): layer-step {sdpa_s:.3f}s ({nrep} runs)")
+            legs.append({"threads": nt, "us_layer_step": round(sdpa_s * 1e6, 1), "runs": nrep})
         got = outs[0].cpu().numpy().astype(np.float64)
         err = got - ref
         check = {"layer": 0, "rows": int(w.B * w.Hq), "max_abs": float(np.abs(err).max()),
                  "rel_l2": float(np.linalg.norm(err) / np.linalg.norm(ref)),
                  "codes_note": "outputs of the last timed step vs the fp64 oracle"}
-        cpu = {"value": cpu_s * 1e6, "unit": "us/layer-step", "cores": threads, "kind": "oracle",
-               "sample": f"one full layer-step of layer 0 (all {w.B * w.Hq} query rows, "
-                         f"{sum(lens0)} tokens per KV head row set), fp64 attention in plain C, "
-                         f"timed {reps} times over {cpu_s * reps:.1f} s; mean per layer-step"}
-        log(f"bench: oracle layer-step {cpu_s:.2f}s ({reps} runs) on {threads} threads; GPU vs oracle "
-            f"max_abs={check['max_abs']:.2e} rel_l2={check['rel_l2']:.2e}")
+        multi = legs[1]
+        cpu = {"value": multi["us_layer_step"], "unit": "us/layer-step", "cores": multi["threads"],
+               "kind": "oracle",
+               "sample": f"one full layer-step of layer 0 (all {w.B * w.Hq} query rows, {tok} cached "
+                         f"tokens per KV head), fp64 attention in plain C over the oracle's quantised "
+                         f"cache, timed {multi['runs']} times; mean per layer-step",
+               "single_thread_us_layer_step": legs[0]["us_layer_step"],
+               "legs": legs, "host_cpu_count": os.cpu_count(), "host_cpu_share": share}
+        log(f"bench: GPU vs oracle max_abs={check['max_abs']:.2e} rel_l2={check['rel_l2']:.2e}")
 
-    rec = {
+    if wbits == 4:
+        dtype = "f16 mfma operands, f32 accumulate (int4 codes, f32 scales)" if plan.variant == 2 else \
+            "f32 vector arithmetic (int4 codes, f32 scales)"
+        step_desc = ("per layer: the split pass over the cached tokens, then the combine pass that "
+                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)")
+    else:
+        dtype = f"f32 vector arithmetic ({wbits}-bit codes, f32 scales)"
+        step_desc = (f"per layer: the append kernel quantises the new token into the {wbits}-bit cache, then "
+                     "the split pass and the combine over every token up to lens")
+    return {
         "metric": METRIC,
         "value": round(us_layer_step, 3),
         "unit": "us/layer-step",
@@ -435,19 +573,18 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 mfma operands, f32 accumulate (int4 codes, f32 scales)",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
             "head_dim": w.D, "context": w.T, "layers": L, "input_dtype": w.dtype,
             "cache_gib": round(cache_bytes / 2**30, 3), "chunk": plan.chunk,
             "num_splits": plan.num_splits, "variant": "mfma" if plan.variant == 2 else "vector",
-            "graph": graph is not None, "k_chan_scale": bool(args.chan_scale),
-            "v_rotated": bool(args.v_rotate),
-            "k_rotation": ("none" if not (w.rotate or args.srft or args.srht) else rot_kind),
-            "code_bits": bits,
-            "step": "per layer: the split pass over the cached tokens, then the combine pass that "
-                    "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)",
+            "graph": graph is not None, "k_chan_scale": bool(chan),
+            "v_rotated": bool(vrot),
+            "k_rotation": ("none" if not (w.rotate or extra_rot) else rot_kind),
+            "code_bits": wbits,
+            "step": step_desc,
         },
         "kernels_us": {
             "split": round(split_us, 3),
@@ -459,12 +596,17 @@ def main():
             "append_unfused_kernel": round(append_us, 3),
             "sdpa_per_layer_graph": None if sdpa_graph_us is None else round(sdpa_graph_us, 3)},
         "sdpa_GBps": round(layer_bytes / ((sdpa_graph_us or (split_us + combine_us)) * 1e-6) / 1e9, 1),
-        "roofline": {"bound": "hbm",
-                     "kernel": "split_bits" if bits != 4 else ("split_mfma" if plan.variant == 2 else "split_vec"),
+        "roofline": {"bound": "hbm", "kernel": kname,
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": traffic,
-                     "algorithmic_bytes_per_launch": int(split_bytes)},
-        "append_bulk": {"kernel": "quantize_tile" if bits == 4 else "quantize_bits", "tokens_per_sequence": n_bulk,
+                     "algorithmic_bytes_per_launch": int(split_bytes),
+                     "note": "achieved = algorithmic bytes of one split launch / its mean duration"},
+        "step_roofline": {"achieved": round(step_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+                          "algorithmic_bytes_per_layer_step": int(layer_bytes),
+                          "note": "whole layer-step (split + combine + append) over µs per layer-step"},
+        "stream_ceiling": ceiling,
+        "append_bulk": {"kernel": "quantize_tile" if wbits == 4 else "quantize_bits", "tokens_per_sequence": n_bulk,
                         "sequences": w.B, "kv_heads": w.Hkv, "us": round(bulk_us, 3),
                         "algorithmic_bytes": int(bulk_bytes),
                         "GBps": round(bulk_bytes / (bulk_us * 1e-6) / 1e9, 1),
@@ -472,7 +614,6 @@ def main():
         "cpu_baseline": cpu,
         "check": check,
     }
-    print(json.dumps(rec), flush=True)
 
 
 if __name__ == "__main__":

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 6
+#define OTQ_ABI_VERSION 7
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -175,6 +175,16 @@ int otq_cache_array_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
 size_t otq_cache_bytes(int32_t batch, int32_t num_kv_heads, int32_t head_dim,
                        int32_t capacity, int32_t code_bits);
 
+/*
+ * Measurement aid, not a step of the method: read every byte of buf once
+ * with non-temporal 16-byte loads (as the split pass reads the cache), over
+ * `blocks` workgroups of 256 threads, and write one word per workgroup into
+ * sink (device uint32 [blocks]).  Timing it gives the streaming-read rate the
+ * decode kernels' bandwidth is compared with.  buf: device, 16-byte aligned,
+ * bytes a nonzero multiple of 16.  Returns OTQ_OK, OTQ_EINVAL or OTQ_EDEVICE.
+ */
+int otq_stream_read_probe(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks, void *stream);
+
 /* Bits of the device error word (otq_last_device_error). */
 #define OTQ_DEVERR_POS 1u  /* otq_quantize_append met pos[b] < 0 or pos[b] + n_new > capacity
                               (the tokens outside [0, capacity) were skipped) */
@@ -220,26 +230,37 @@ typedef enum otq_variant {
 
 /*
  * Work split of one decode call (flash-decoding style): the token axis of
- * every (sequence, KV head) is cut into chunks of `chunk` tokens; each chunk
- * is one workgroup producing an unnormalised partial (m, l, o), and a second
- * kernel merges the partials of each (sequence, query head).
+ * every (sequence, KV head) is cut into pieces of `chunk` tokens; split s
+ * takes pieces s, s + S, s + 2S, ... (S = num_splits) and is one workgroup
+ * producing an unnormalised partial (m, l, o) over them, and a second kernel
+ * merges the partials of each (sequence, query head).  When S * chunk >=
+ * max_len every split has one contiguous piece; otherwise the pieces of a
+ * head's splits interleave, so that the splits read one compact window of
+ * the cache at a time (the MFMA variant on a single sequence only).
  */
 typedef struct otq_plan {
-    int32_t chunk;       /* tokens per split, multiple of 128 */
-    int32_t num_splits;  /* ceil(max_len / chunk), >= 1 */
+    int32_t chunk;       /* tokens per piece, multiple of 128 */
+    int32_t num_splits;  /* workgroups per (sequence, KV-head group), >= 1 */
     int32_t variant;     /* OTQ_VARIANT_VECTOR or OTQ_VARIANT_MFMA */
     int32_t reserved;
     size_t workspace_bytes;
 } otq_plan;
 
 /*
- * Choose the plan for a decode call.  chunk_override = 0 and
- * variant_override = OTQ_VARIANT_AUTO pick defaults from the shape; nonzero
- * values force them (chunk must be a positive multiple of 128).  Any valid
- * plan gives the same result up to fp32 rounding.  Pure host arithmetic.
+ * Choose the plan for a decode call.  chunk_override = 0,
+ * variant_override = OTQ_VARIANT_AUTO and splits_override = 0 pick defaults
+ * from the shape; nonzero values force them (chunk must be a positive
+ * multiple of 128).  A split count below ceil(max_len / chunk) interleaves
+ * the pieces; it is honoured only where that is supported (the MFMA variant,
+ * batch 1, chunk / 32 a power of two) and otherwise replaced by
+ * ceil(max_len / chunk), as is any larger count.  A plan passed to a decode
+ * call is re-derived the same way from its chunk, variant and num_splits for
+ * the call's max_len.  Any valid plan gives the same result up to fp32
+ * rounding.  Pure host arithmetic.
  */
 int otq_sdpa_plan(int32_t num_q_heads, const otq_cache *cache, int32_t max_len,
-                  int32_t chunk_override, int32_t variant_override, otq_plan *plan);
+                  int32_t chunk_override, int32_t variant_override, int32_t splits_override,
+                  otq_plan *plan);
 
 /* Workspace bytes otq_sdpa_int4_decode needs for the default plan (0 on error). */
 size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache *cache, int32_t max_len);

@@ -30,7 +30,7 @@ OTQ_DEVERR_POS, OTQ_DEVERR_LENS = 1, 2
 
 EXPORTED = [
     "otq_status_str", "otq_abi_version", "otq_cache_array_bytes", "otq_cache_bytes",
-    "otq_last_device_error",
+    "otq_last_device_error", "otq_stream_read_probe",
     "otq_quantize_append", "otq_sdpa_plan", "otq_sdpa_workspace_bytes",
     "otq_sdpa_int4_decode", "otq_sdpa_int4_decode_planned", "otq_sdpa_int4_decode_append",
     "otq_sdpa_int4_decode_append_noalloc",
@@ -86,9 +86,11 @@ def lib():
     L.otq_cache_bytes.restype = S
     L.otq_last_device_error.argtypes = [P, ctypes.POINTER(ctypes.c_uint32)]
     L.otq_last_device_error.restype = ctypes.c_int
+    L.otq_stream_read_probe.argtypes = [P, S, P, I, P]
+    L.otq_stream_read_probe.restype = ctypes.c_int
     L.otq_quantize_append.argtypes = [P, P, I, I, CP, P, P]
     L.otq_quantize_append.restype = ctypes.c_int
-    L.otq_sdpa_plan.argtypes = [I, CP, I, I, I, ctypes.POINTER(otq_plan)]
+    L.otq_sdpa_plan.argtypes = [I, CP, I, I, I, I, ctypes.POINTER(otq_plan)]
     L.otq_sdpa_plan.restype = ctypes.c_int
     L.otq_sdpa_workspace_bytes.argtypes = [I, CP, I]
     L.otq_sdpa_workspace_bytes.restype = S
@@ -151,6 +153,15 @@ def otq_cache_bytes(batch, num_kv_heads, head_dim, capacity, code_bits=4):
     return lib().otq_cache_bytes(batch, num_kv_heads, head_dim, capacity, code_bits)
 
 
+def otq_stream_read_probe(buf, sink, nbytes=None, blocks=None, stream=None):
+    """Read every byte of the device tensor buf once (the streaming-read
+    reference); sink: device uint32 tensor with one word per block."""
+    nbytes = buf.numel() * buf.element_size() if nbytes is None else nbytes
+    blocks = sink.numel() if blocks is None else blocks
+    _check(lib().otq_stream_read_probe(_ptr(buf), nbytes, _ptr(sink), blocks, _stream(stream)),
+           "otq_stream_read_probe")
+
+
 def otq_last_device_error(stream=None):
     """Device-side contract violations (OTQ_DEVERR_* bits) recorded on the
     current device since the previous call (which this one clears)."""
@@ -170,9 +181,9 @@ def otq_quantize_append(k, v, cache_desc, pos, n_new=None, dtype=None, stream=No
     return rc
 
 
-def otq_sdpa_plan(num_q_heads, cache_desc, max_len, chunk=0, variant=OTQ_VARIANT_AUTO, check=True):
+def otq_sdpa_plan(num_q_heads, cache_desc, max_len, chunk=0, variant=OTQ_VARIANT_AUTO, check=True, splits=0):
     p = otq_plan()
-    rc = lib().otq_sdpa_plan(num_q_heads, ctypes.byref(cache_desc), max_len, chunk, variant,
+    rc = lib().otq_sdpa_plan(num_q_heads, ctypes.byref(cache_desc), max_len, chunk, variant, splits,
                              ctypes.byref(p))
     if check:
         _check(rc, "otq_sdpa_plan")
@@ -322,8 +333,8 @@ class Int4KVCache:
     def append(self, k, v, pos, stream=None):
         return otq_quantize_append(k, v, self.desc, pos, stream=stream)
 
-    def plan(self, num_q_heads, max_len, chunk=0, variant=OTQ_VARIANT_AUTO):
-        return otq_sdpa_plan(num_q_heads, self.desc, max_len, chunk, variant)
+    def plan(self, num_q_heads, max_len, chunk=0, variant=OTQ_VARIANT_AUTO, splits=0):
+        return otq_sdpa_plan(num_q_heads, self.desc, max_len, chunk, variant, splits=splits)
 
     def workspace(self, num_q_heads, max_len, plan=None):
         n = (plan.workspace_bytes if plan is not None

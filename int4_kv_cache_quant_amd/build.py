@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libotq.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.hip", "quantize.hip", "sdpa_vec.hip", "sdpa_mfma.hip", "combine.hip", "order.hip", "bits.hip",
-           "wide.hip"]
+           "wide.hip", "probe.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",

@@ -74,6 +74,14 @@ constexpr int kMaxChunk = 8192;  // measured: larger chunks starve the grid on r
 constexpr int kTargetWaves = 1024;  // split waves aimed for (one per SIMD)
 constexpr int kOrderedWaveFactor = 8;  // measured on the ragged 32-sequence batch: chunk 2048 over 8192
 constexpr int kMaxSplits = 16384;
+bool pow2_int(long long x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(long long x)
+{
+    int k = 0;
+    while ((1LL << (k + 1)) <= x) ++k;
+    return k;
+}
 
 // Power-of-two widths take every kernel; 192 (three times 64) the wide ones.
 bool pow2_dim(int D) { return D == 64 || D == 128 || D == 256; }
@@ -126,7 +134,7 @@ int rot_kind(const otq_cache* c)
 bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
 int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
-              int32_t variant_ov, otq_plan* p)
+              int32_t variant_ov, int32_t splits_ov, otq_plan* p)
 {
     int rc = check_cache(c);
     if (rc != OTQ_OK) return rc;
@@ -184,7 +192,16 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     } else if (chunk < 0 || chunk % kChunkAlign != 0) {
         return OTQ_EINVAL;
     }
-    const long long S = ((long long)max_len + chunk - 1) / chunk;
+    if (splits_ov < 0) return OTQ_EINVAL;
+    // interleaved pieces (several per split): the MFMA pass on one sequence
+    // (a batch orders its blocks by whole chunks), 2^k tiles per piece
+    const bool can_interleave = variant == OTQ_VARIANT_MFMA && pow2_dim(D) && code_bits(c) == 4 &&
+                                !ordered_batch(c->batch) && pow2_int(chunk / OTQ_TILE) &&
+                                chunk % OTQ_TILE == 0;
+    long long S = ((long long)max_len + chunk - 1) / chunk;
+    if (splits_ov != 0 && splits_ov < S && can_interleave) {
+        S = splits_ov;  // the caller's split count, over interleaved pieces
+    }
     if (S > kMaxSplits) return OTQ_EINVAL;  // bounds the partials' workspace
     const unsigned __int128 rows = (unsigned __int128)c->batch * Hq * S;
     const unsigned __int128 o_bytes = rows * D * sizeof(float);
@@ -244,6 +261,15 @@ size_t otq_cache_bytes(int32_t B, int32_t H, int32_t D, int32_t cap, int32_t cod
     return 2 * (cb + sb);
 }
 
+int otq_stream_read_probe(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks, void* stream)
+{
+    if (!buf || !sink || blocks < 1 || bytes == 0 || bytes % 16 != 0 || (((uintptr_t)buf) & 15) != 0)
+        return OTQ_EINVAL;
+    return otq::launch_stream_read(buf, bytes, sink, blocks, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? OTQ_OK
+               : OTQ_EDEVICE;
+}
+
 int otq_last_device_error(void* stream, uint32_t* flags)
 {
     if (!flags) return OTQ_EINVAL;
@@ -296,15 +322,16 @@ int otq_quantize_append(const void* k, const void* v, int32_t dtype, int32_t n_n
 }
 
 int otq_sdpa_plan(int32_t num_q_heads, const otq_cache* cache, int32_t max_len,
-                  int32_t chunk_override, int32_t variant_override, otq_plan* plan)
+                  int32_t chunk_override, int32_t variant_override, int32_t splits_override,
+                  otq_plan* plan)
 {
-    return make_plan(num_q_heads, cache, max_len, chunk_override, variant_override, plan);
+    return make_plan(num_q_heads, cache, max_len, chunk_override, variant_override, splits_override, plan);
 }
 
 size_t otq_sdpa_workspace_bytes(int32_t num_q_heads, const otq_cache* cache, int32_t max_len)
 {
     otq_plan p;
-    if (make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &p) != OTQ_OK) return 0;
+    if (make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, 0, &p) != OTQ_OK) return 0;
     return p.workspace_bytes;
 }
 
@@ -336,7 +363,7 @@ int check_plan(int32_t Hq, const otq_cache* c, int32_t max_len, const otq_plan* 
                otq_plan* chk)
 {
     if (!plan) return OTQ_EINVAL;
-    return make_plan(Hq, c, max_len, plan->chunk, plan->variant, chk);
+    return make_plan(Hq, c, max_len, plan->chunk, plan->variant, plan->num_splits, chk);
 }
 
 int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache* cache,
@@ -365,6 +392,8 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.qscale = scale * otq::kLog2eHost;
     a.chunk = chk.chunk;
     a.num_splits = chk.num_splits;
+    a.piece_stride = chk.chunk * chk.num_splits;
+    a.piece_shift = (long long)chk.chunk * chk.num_splits >= max_len ? 30 : ilog2(chk.chunk / OTQ_TILE);
     a.part_o = static_cast<float*>(workspace);
     a.part_ml = reinterpret_cast<float2*>(static_cast<char*>(workspace) +
                                           ml_offset(cache, num_q_heads, chk));
@@ -495,7 +524,7 @@ int check_decode_append(const void* q, const void* k_new, const void* v_new, int
                         float scale, const float* out, const otq_plan* plan, otq_plan* chk)
 {
     const int rc = plan ? check_plan(num_q_heads, cache, max_len, plan, chk)
-                        : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, chk);
+                        : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, 0, chk);
     if (rc != OTQ_OK) return rc;
     if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
     if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
@@ -549,7 +578,7 @@ int otq_sdpa_int4_decode(const void* q, int32_t dtype, int32_t num_q_heads,
                          void* stream)
 {
     otq_plan p;
-    const int rc = make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, &p);
+    const int rc = make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, 0, &p);
     if (rc != OTQ_OK) return rc;
     return otq_sdpa_int4_decode_planned(q, dtype, num_q_heads, cache, lens, max_len, scale, out,
                                         workspace, workspace_bytes, &p, stream);

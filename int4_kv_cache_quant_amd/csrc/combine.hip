@@ -158,7 +158,9 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     if (tid == 0 && blockIdx.y == 0 && row % a.Hq == 0 && (raw_len < 0 || raw_len > a.max_len))
         report_error(a.err, kErrLens);
     const int nsplit_tok = APPEND ? max(len - 1, 0) : len;  // tokens the split pass covered
-    const int ns = (nsplit_tok + a.chunk - 1) / a.chunk;
+    // splits holding a partial: those whose first piece starts below the
+    // covered length (each split's later pieces follow S chunk further on)
+    const int ns = min((nsplit_tok + a.chunk - 1) / a.chunk, a.S);
     if constexpr (APPEND) pos = len - 1;
     float4* dst = reinterpret_cast<float4*>(a.out + (size_t)row * D + c);
     if (len == 0) {  // block-uniform: nothing attended, nothing appended

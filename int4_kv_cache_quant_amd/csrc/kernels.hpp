@@ -31,8 +31,16 @@ struct SplitArgs {
     const int32_t* lens;
     int max_len;
     float qscale;  // softmax scale * log2(e): scores are kept in the log2 domain
+    // Split s takes the pieces s, s + S, s + 2 S, ... of `chunk` tokens each
+    // (one piece when S chunk >= max_len).  Tile it (32 tokens) of split s
+    // starts at token s chunk + (it >> piece_shift) piece_stride +
+    // (it & (2^piece_shift - 1)) 32, with piece_stride = S chunk and
+    // 2^piece_shift = chunk / 32 tiles per piece; piece_shift = 30 when every
+    // split has a single piece.
     int chunk;
     int num_splits;
+    int piece_shift;
+    int piece_stride;
     float* part_o;   // [B][Hq][S][D]
     float2* part_ml; // [B][Hq][S] (m, l)
     // block k = x + S (y + groups z) takes item items[k] = (split, sequence)
@@ -115,6 +123,9 @@ struct CombineArgs {
     unsigned* err;          // the device error word
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
+
+// The streaming-read probe: reads bytes / 16 uint4 of buf, writes blocks words.
+hipError_t launch_stream_read(const void* buf, size_t bytes, uint32_t* sink, int blocks, hipStream_t stream);
 
 
 }  // namespace otq

@@ -485,6 +485,12 @@ void split_mfma_kernel(SplitArgs a)
     const int G = a.Hq / a.H;
     const int PG = P * G;  // query heads served by the block (<= 16)
     const int start = split * a.chunk;
+    // first token of the block's tile it (its pieces interleave with the
+    // other splits' at piece_stride; one piece: start + 32 it)
+    const int pshift = a.piece_shift;
+    auto tile_tok = [&](int it) {
+        return start + (it >> pshift) * a.piece_stride + (it & ((1 << pshift) - 1)) * kTile;
+    };
     const int n16 = lane & 15, r = lane >> 4, slot = lane & 3;
     const bool col_valid = n16 < PG;
     const int jl = col_valid ? n16 / G : P - 1;  // KV head of this lane's column
@@ -567,7 +573,7 @@ void split_mfma_kernel(SplitArgs a)
 #pragma unroll
     for (int j = 0; j < P; ++j) { vk0[j] = vo_k[j][0]; vv0[j] = vo_v[j][0]; }
     auto dma_tile = [&](int it, int st) {
-        const int tok0 = start + it * kTile;
+        const int tok0 = tile_tok(it);
         const int so_code = tok0 * (D / 2), so_scale = tok0 * NG * 4;
         const uint32_t base = lds_address(stage_of(st));
         uint32_t mk[P], mv[P];
@@ -581,13 +587,26 @@ void split_mfma_kernel(SplitArgs a)
     // arrive, if it lies inside the cache (capacity is a multiple of 32, so a
     // tile starting below it is whole); tokens past lens[b] are masked later,
     // or the block leaves.
-    if (start + wave * kTile < a.cap) dma_tile(wave, 0);
-    if (start >= len) {  // block-uniform: no partial for an empty chunk
+    if (tile_tok(wave) < a.cap) dma_tile(wave, 0);
+    if (start >= len) {  // block-uniform: no partial for an empty split
         __builtin_amdgcn_s_waitcnt(kWaitVm0);  // no copy may land after the block is gone
         return;
     }
-    const int end = min(start + a.chunk, len);
-    const int ntiles = (end - start + kTile - 1) / kTile;
+    // tiles of the split: with one piece, those of [start, min(start + chunk,
+    // len)); with interleaved pieces, whole rounds of S pieces and the part
+    // of the last round that falls to this split
+    int ntiles;
+    {
+        const int nt = (len + kTile - 1) / kTile;  // tiles of the sequence
+        if (pshift >= 30) {
+            ntiles = (min(start + a.chunk, len) - start + kTile - 1) / kTile;
+        } else {
+            const int tpp = 1 << pshift, round = a.num_splits << pshift;
+            const int full = nt / round, rest = nt - full * round;
+            ntiles = full * tpp + min(max(rest - split * tpp, 0), tpp);
+        }
+    }
+    const int end = len;  // only the sequence's last tile can be partial
 
     // ---- q prologue, registers only: widen, rotate like K when the cache
     //      is (channel c = 32 g + 8 r + e: the butterflies over bits 0-2 and
@@ -783,7 +802,7 @@ void split_mfma_kernel(SplitArgs a)
     };
 
     auto compute_tile = [&](TileLoads<D, P, ROWS>& t, int it, auto&& after_scores) {
-        const int tok0 = start + it * kTile;
+        const int tok0 = tile_tok(it);
         // ---- scores, as T = S / qmul (qmul > 0 is applied inside exp2)
         float T[2][4];
 #pragma unroll
@@ -811,7 +830,7 @@ void split_mfma_kernel(SplitArgs a)
             for (int i = 0; i < 4; ++i) T[s][i] = tot[i];
         }
         after_scores();
-        if (tok0 + kTile > end) {  // wave-uniform: the chunk's last, partial tile
+        if (tok0 + kTile > end) {  // wave-uniform: the sequence's last, partial tile
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
 #pragma unroll

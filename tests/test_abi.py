@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 6
+    assert lib.otq_abi_version() == 7
 
 
 def test_status_strings():
@@ -120,7 +120,7 @@ def test_quantize_append_host_errors():
         mis = _desc()
         setattr(mis, field, FAKE + 4)
         assert call(FAKE, FAKE, 1, 1, mis, FAKE) == otq.OTQ_EINVAL
-        assert otq.lib().otq_sdpa_plan(16, ctypes.byref(mis), 64, 0, 0, ctypes.byref(otq.otq_plan())) == otq.OTQ_EINVAL
+        assert otq.lib().otq_sdpa_plan(16, ctypes.byref(mis), 64, 0, 0, 0, ctypes.byref(otq.otq_plan())) == otq.OTQ_EINVAL
     assert call(FAKE, FAKE, 2, 1, d, FAKE) == otq.OTQ_EUNSUPPORTED
     assert call(FAKE, FAKE, 1, 65, d, FAKE) == otq.OTQ_ECAPACITY
     assert call(FAKE, FAKE, 1, 1, _desc(D=96), FAKE) == otq.OTQ_EUNSUPPORTED
@@ -138,7 +138,7 @@ def test_rotation_kind_host_checks():
     lib = otq.lib()
     P = ctypes.c_void_p
     call = lambda desc: lib.otq_quantize_append(P(FAKE), P(FAKE), 1, 1, ctypes.byref(desc), P(FAKE), None)
-    plan = lambda desc: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, 0, ctypes.byref(otq.otq_plan()))
+    plan = lambda desc: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, 0, 0, ctypes.byref(otq.otq_plan()))
     d = _desc()
     d.rot_kind = 7                        # ignored without signs
     assert plan(d) == otq.OTQ_OK
@@ -278,7 +278,7 @@ def test_code_bits_host_checks():
     invalid."""
     lib = otq.lib()
     P = ctypes.c_void_p
-    plan = lambda desc, variant=0: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, variant,
+    plan = lambda desc, variant=0: lib.otq_sdpa_plan(16, ctypes.byref(desc), 64, 0, variant, 0,
                                                      ctypes.byref(otq.otq_plan()))
     for bits, want in ((0, otq.OTQ_OK), (4, otq.OTQ_OK), (2, otq.OTQ_OK), (3, otq.OTQ_OK),
                        (1, otq.OTQ_EINVAL), (5, otq.OTQ_EINVAL), (-3, otq.OTQ_EINVAL)):
@@ -288,7 +288,7 @@ def test_code_bits_host_checks():
     d = _desc()
     d.code_bits = 3
     p = otq.otq_plan()
-    assert lib.otq_sdpa_plan(16, ctypes.byref(d), 64, 0, 0, ctypes.byref(p)) == otq.OTQ_OK
+    assert lib.otq_sdpa_plan(16, ctypes.byref(d), 64, 0, 0, 0, ctypes.byref(p)) == otq.OTQ_OK
     assert p.variant == otq.OTQ_VARIANT_VECTOR
     assert plan(d, otq.OTQ_VARIANT_MFMA) == otq.OTQ_EUNSUPPORTED
     assert plan(d, otq.OTQ_VARIANT_VECTOR) == otq.OTQ_OK
@@ -358,3 +358,42 @@ def test_head_dim_192_host_checks():
     assert rc == otq.OTQ_EUNSUPPORTED
     for bad in (96, 160, 320):
         assert lib.otq_cache_bytes(1, 1, bad, 64, 4) == 0
+
+
+def test_stream_read_probe_host_checks():
+    lib = otq.lib()
+    P = ctypes.c_void_p
+    assert lib.otq_stream_read_probe(P(0), 1024, P(FAKE), 4, None) == otq.OTQ_EINVAL
+    assert lib.otq_stream_read_probe(P(FAKE), 1000, P(FAKE), 4, None) == otq.OTQ_EINVAL
+    assert lib.otq_stream_read_probe(P(FAKE + 8), 1024, P(FAKE), 4, None) == otq.OTQ_EINVAL
+    assert lib.otq_stream_read_probe(P(FAKE), 1024, P(0), 4, None) == otq.OTQ_EINVAL
+    assert lib.otq_stream_read_probe(P(FAKE), 1024, P(FAKE), 0, None) == otq.OTQ_EINVAL
+    assert lib.otq_stream_read_probe(P(FAKE), 0, P(FAKE), 4, None) == otq.OTQ_EINVAL
+
+
+def test_plan_interleaved_pieces():
+    """A split count below ceil(max_len / chunk) interleaves the pieces: kept
+    for the MFMA variant on one sequence with 2^k tiles per piece, replaced by
+    ceil(max_len / chunk) elsewhere; the workspace follows the split count."""
+    one = _desc(B=1, H=8, D=128, cap=131072)
+    p = otq.otq_sdpa_plan(64, one, 131072, chunk=256, splits=32)
+    assert (p.chunk, p.num_splits, p.variant) == (256, 32, otq.OTQ_VARIANT_MFMA)
+    rows = 64 * 32
+    assert p.workspace_bytes == -(-rows * 128 * 4 // 256) * 256 + rows * 8
+    # more splits than pieces: one piece each
+    assert otq.otq_sdpa_plan(64, one, 1000, chunk=256, splits=64).num_splits == 4
+    # 3 tiles per piece, the vector variant, a batch: no interleaving
+    assert otq.otq_sdpa_plan(64, one, 131072, chunk=384, splits=32).num_splits == -(-131072 // 384)
+    pv = otq.otq_sdpa_plan(8, one, 4096, chunk=256, variant=otq.OTQ_VARIANT_VECTOR, splits=4)
+    assert (pv.chunk, pv.num_splits) == (256, 16)
+    batch = _desc(B=4, H=8, D=128, cap=32768)
+    assert otq.otq_sdpa_plan(32, batch, 32768, chunk=256, splits=8).num_splits == 128
+    # 2- and 3-bit caches take one piece per split
+    b3 = _desc(B=1, H=8, D=128, cap=32768)
+    b3.code_bits = 3
+    assert otq.otq_sdpa_plan(32, b3, 32768, chunk=256, splits=8).num_splits == 128
+    assert otq.otq_sdpa_plan(64, one, 1000, splits=-1, check=False)[0] == otq.OTQ_EINVAL
+    # the default plans take one piece per split
+    for desc in (one, batch):
+        d = otq.otq_sdpa_plan(32 if desc is batch else 64, desc, 32768)
+        assert d.num_splits == -(-32768 // d.chunk)

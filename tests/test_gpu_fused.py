@@ -16,7 +16,7 @@ import torch
 
 import int4_kv_cache_quant_amd as otq
 import oracle
-from int4_kv_cache_quant_amd import layout
+from int4_kv_cache_quant_amd import layout, synth
 
 from gpu_common import (MAX_ABS, REL_L2, build_cache, chan_scales, compare_codes, errors, host_cache,
                         oracle_cache, rand_signs, rot_norm32, say, to_bits)
@@ -49,7 +49,7 @@ def _poison(cache, lens):
 
 
 def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, seed=0, steps=1,
-         variant=otq.OTQ_VARIANT_MFMA, scaled=False, rotate_v=False):
+         variant=otq.OTQ_VARIANT_MFMA, scaled=False, rotate_v=False, splits=0):
     """rotate: False, True (the Hadamard rotation) or "srft" (the FFT one)."""
     kind = "srft" if rotate == "srft" else "srht"
     g = torch.Generator().manual_seed(seed)
@@ -83,7 +83,7 @@ def _run(B, G, Hkv, D, cap, lens, dtype=torch.bfloat16, rotate=False, chunk=0, s
         vn = v.to(DEV)[ar, :, idx].contiguous()
         q = torch.randn((B, Hq, D), generator=g).to(dtype)
         max_len = max(1, max(cur))
-        plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
+        plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant, splits=splits)
         say(f"fused B={B} G={G} Hkv={Hkv} D={D} lens={cur} chunk={plan.chunk} rotate={rotate} "
             f"scaled={scaled} rotate_v={rotate_v}")
         out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max_len, scale, plan=plan)
@@ -156,9 +156,70 @@ def test_fused_append_consecutive_steps():
     _run(3, 4, 2, 128, 512, [300, 77, 2], dtype=torch.float16, rotate=True, steps=3, seed=9)
 
 
+@pytest.mark.parametrize("lens", [[1000], [641], [129], [1]])
+def test_fused_append_interleaved_pieces(lens):
+    """The fused step with fewer splits than pieces (3 splits of 128-token
+    pieces): the split pass covers [0, lens - 1) over interleaved pieces,
+    the combine appends the token at lens - 1."""
+    _run(1, 8, 2, 128, 1024, lens, chunk=128, splits=3, seed=lens[0], rotate=True)
+
+
 @pytest.mark.parametrize("G,D", [(1, 128), (2, 64)])
 @pytest.mark.parametrize("scaled", [False, True])
 def test_fused_append_vector_variant(G, D, scaled):
     """The same call on the vector split variant."""
     _run(2, G, 2, D, 320, [300, 77], chunk=128, seed=G + D + scaled, variant=otq.OTQ_VARIANT_VECTOR,
          scaled=scaled)
+
+
+# -------------------------------------------------------------- full workloads
+
+def _full_fused(cfg):
+    """One decode step of layer 0 of a full workload, in the launch
+    configuration the benchmark times (the planner's default plan): every
+    sequence prefilled, the slot of its new token poisoned, then the fused
+    call.  The whole cache must equal the oracle's quantisation bit for bit
+    and every output row must match the fp64 oracle."""
+    w = synth.WORKLOADS[cfg]
+    say(f"fused full workload {cfg} {w.name}")
+    k = synth.kv(w, 0, "k", device=DEV)
+    v = synth.kv(w, 0, "v", device=DEV)
+    q = synth.query(w, 0, device=DEV)
+    lens = synth.lens(w, 0)
+    signs = torch.from_numpy(synth.rot_signs(w, 0)).to(DEV) if w.rotate else None
+    cache = otq.Int4KVCache(w.B, w.Hkv, w.D, w.capacity, device=DEV, rot_signs=signs)
+    for t0 in range(0, w.T, 16384):
+        t1 = min(w.T, t0 + 16384)
+        pos = torch.full((w.B,), t0, dtype=torch.int32, device=DEV)
+        cache.append(k[:, :, t0:t1].contiguous(), v[:, :, t0:t1].contiguous(), pos)
+    _poison(cache, [int(n) for n in lens])
+    lens_t = torch.from_numpy(lens).to(DEV)
+    idx = (lens_t.long() - 1).clamp(min=0)
+    ar = torch.arange(w.B, device=DEV)
+    kn = k[ar, :, idx].contiguous()
+    vn = v[ar, :, idx].contiguous()
+    max_len = int(lens.max())
+    plan = cache.plan(w.Hq, max_len)
+    say(f"  plan chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
+    out = cache.decode_append(q, kn, vn, lens_t, max_len, w.scale, plan=plan)
+    torch.cuda.synchronize()
+    assert otq.otq_last_device_error() == 0
+    ref_cache = oracle_cache(k.cpu(), v.cpu(), w.dtype, None if signs is None else signs.cpu().numpy(),
+                             rot_norm32(w.D, "srht"), threads=16)
+    assert compare_codes(host_cache(cache), ref_cache, w.T) == {
+        "k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    kc, ks, vc, vs = ref_cache
+    ref = oracle.sdpa(to_bits(q), w.dtype, kc, ks, vc, vs, lens, w.scale,
+                      signs=None if signs is None else signs.cpu().numpy(), rot_norm=rot_norm32(w.D, "srht"),
+                      threads=16)
+    ma, rel = errors(out.cpu().numpy(), ref)
+    say(f"  rows={w.B * w.Hq} max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_fused_full_workload_3_llama70b_128k():
+    _full_fused(3)
+
+
+def test_fused_full_workload_5_ragged_rotated():
+    _full_fused(5)

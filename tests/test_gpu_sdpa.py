@@ -48,7 +48,7 @@ def _case(B, Hq, Hkv, D, cap, dtype, seed, sigma=1.0, rotate=False, n_out=2, spi
 
 def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sigma=1.0,
          rotate=False, chunk=0, variant=otq.OTQ_VARIANT_AUTO, rows=None, spikes=(), beta=0.0,
-         scaled=False, rotate_v=False):
+         scaled=False, rotate_v=False, splits=0):
     """rotate: False, True (the Hadamard rotation) or "srft" (the FFT one)."""
     kind = "srft" if rotate == "srft" else "srht"
     k, v, q, signs, lam = _case(B, Hq, Hkv, D, cap, dtype, seed, sigma, bool(rotate), spikes=spikes,
@@ -63,7 +63,7 @@ def _run(B, Hq, Hkv, D, cap, lens, dtype=torch.bfloat16, scale=None, seed=0, sig
                         v_signs=None if vsg is None else vsg.to(DEV), rot_kind=kind)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     max_len = max(1, int(max(lens)))
-    plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant)
+    plan = cache.plan(Hq, max_len, chunk=chunk, variant=variant, splits=splits)
     say(f"sdpa B={B} Hq={Hq} Hkv={Hkv} D={D} cap={cap} chunk={plan.chunk} "
         f"splits={plan.num_splits} variant={plan.variant} rotate={rotate} scaled={scaled} "
         f"rotate_v={rotate_v}")
@@ -187,6 +187,40 @@ def test_sdpa_split_invariance(chunk, variant, Hq):
     got, ref, plan = _run(1, Hq, 1, 128, 1024, [1000], seed=11, chunk=chunk, variant=variant)
     ma, rel = errors(got, ref)
     assert plan.num_splits == -(-1000 // chunk)
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("D,Hq", [(64, 8), (128, 16), (128, 2), (256, 4)])
+@pytest.mark.parametrize("chunk,splits,lens", [(128, 3, 1000), (256, 2, 1000), (128, 5, 641),
+                                               (128, 7, 896), (128, 4, 33), (128, 8, 1)])
+def test_sdpa_interleaved_pieces(D, Hq, chunk, splits, lens):
+    """Fewer splits than pieces: split s takes pieces s, s + S, ...; the last
+    round of pieces is partial (641, 1000), exactly full (896 = 7 x 128), or
+    covers fewer splits than S (33, 1), and the sequence's last tile is
+    partial."""
+    got, ref, plan = _run(1, Hq, 2, D, 1024, [lens], seed=D + chunk + splits + lens, chunk=chunk,
+                          variant=MF, splits=splits)
+    assert (plan.chunk, plan.num_splits) == (chunk, min(splits, -(-lens // chunk)))
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+def test_sdpa_interleaved_plan_reused_at_longer_length():
+    """A plan made for a short max_len, passed to a call with a longer one:
+    the call keeps its split count and interleaves the pieces."""
+    k, v, q, _, _ = _case(1, 8, 2, 128, 1024, torch.bfloat16, 5)
+    cache = build_cache(k.to(DEV), v.to(DEV), 1024)
+    plan = cache.plan(8, 300, chunk=128)  # 3 splits
+    assert plan.num_splits == 3
+    ws = cache.workspace(8, 300, plan)
+    out = cache.decode(q.to(DEV), torch.tensor([1000], dtype=torch.int32, device=DEV), 1000, 0.1,
+                       workspace=ws, plan=plan)
+    torch.cuda.synchronize()
+    kc, ks, vc, vs = oracle_cache(k, v, "bf16")
+    ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array([1000], np.int32), 0.1, threads=8)
+    ma, rel = errors(out.cpu().numpy(), ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
 
 

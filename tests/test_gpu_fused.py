@@ -201,6 +201,8 @@ def _full_fused(cfg):
     max_len = int(lens.max())
     plan = cache.plan(w.Hq, max_len)
     say(f"  plan chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
+    torch.cuda.synchronize()
+    otq.otq_last_device_error()  # start from a clear word (earlier tests may leave flags)
     out = cache.decode_append(q, kn, vn, lens_t, max_len, w.scale, plan=plan)
     torch.cuda.synchronize()
     assert otq.otq_last_device_error() == 0

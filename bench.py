@@ -350,11 +350,6 @@ def bench_workload(wnum, args, primary):
         otq.otq_sdpa_lse_combine(w.Hq, caches[l].desc, lens_l[l], max_len, ws, plan, outs[l])
 
     def fused(l):  # split over the cached tokens, then the combine that appends the new token
-        if wbits != 4:  # b-bit caches: the append kernel, then split + combine over lens
-            append(l)
-            split(l)
-            combine(l)
-            return
         otq.otq_sdpa_int4_decode_append(qs[l], k_new[l], v_new[l], caches[l].desc, lens_l[l],
                                         max_len, w.scale, outs[l], ws, plan=plan)
 
@@ -453,7 +448,10 @@ def bench_workload(wnum, args, primary):
     layer_bytes = split_bytes + w.B * w.Hq * w.D * 4
     achieved = split_bytes / (split_us * 1e-6) / 1e9
     step_gbps = layer_bytes / (us_layer_step * 1e-6) / 1e9
-    kname = "split_bits" if wbits != 4 else ("split_mfma" if plan.variant == 2 else "split_vec")
+    if wbits != 4:
+        kname = "split_b2_mfma" if plan.variant == 2 else "split_bits"
+    else:
+        kname = "split_mfma" if plan.variant == 2 else "split_vec"
     if not primary:
         del caches, outs, ws, qs, k_new, v_new
         return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
@@ -553,15 +551,11 @@ def bench_workload(wnum, args, primary):
                "legs": legs, "host_cpu_count": os.cpu_count(), "host_cpu_share": share}
         log(f"bench: GPU vs oracle max_abs={check['max_abs']:.2e} rel_l2={check['rel_l2']:.2e}")
 
-    if wbits == 4:
-        dtype = "f16 mfma operands, f32 accumulate (int4 codes, f32 scales)" if plan.variant == 2 else \
-            "f32 vector arithmetic (int4 codes, f32 scales)"
-        step_desc = ("per layer: the split pass over the cached tokens, then the combine pass that "
-                     "quantises the new token into the cache and merges it (otq_sdpa_int4_decode_append)")
-    else:
-        dtype = f"f32 vector arithmetic ({wbits}-bit codes, f32 scales)"
-        step_desc = (f"per layer: the append kernel quantises the new token into the {wbits}-bit cache, then "
-                     "the split pass and the combine over every token up to lens")
+    codes = "int4 codes" if wbits == 4 else f"{wbits}-bit codes"
+    dtype = (f"f16 mfma operands, f32 accumulate ({codes}, f32 scales)" if plan.variant == 2
+             else f"f32 vector arithmetic ({codes}, f32 scales)")
+    step_desc = (f"per layer: the split pass over the cached tokens, then the combine pass that quantises "
+                 f"the new token into the cache ({codes}) and merges it (otq_sdpa_int4_decode_append)")
     return {
         "metric": METRIC,
         "value": round(us_layer_step, 3),

@@ -132,9 +132,11 @@ typedef enum otq_rot_kind {
  * V rows are plain little-endian bit streams, element i at bits [b i,
  * b i + b), two's complement: k_codes and v_codes uint8 [B][H][C][D*b/8],
  * scales as above.  Rotations and the per-channel scale apply as for int4.
- * The split pass of such caches is the vector variant (any G <= 16), and
- * otq_sdpa_int4_decode_append returns OTQ_EUNSUPPORTED for them (append with
- * otq_quantize_append, then call otq_sdpa_int4_decode).
+ * Split passes: 2-bit caches whose K is neither rotated nor channel-scaled
+ * take the MFMA variant (the default; any G <= 16), the others the vector
+ * variant (any G <= 16; OTQ_EUNSUPPORTED if MFMA is forced).
+ * otq_sdpa_int4_decode_append takes these caches too: its combine quantises
+ * the new token with the b-bit rule and writes its rows whole.
  */
 typedef struct otq_cache {
     int32_t batch;

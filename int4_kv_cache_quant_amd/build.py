@@ -24,7 +24,7 @@ LIB = os.path.join(HERE, "libotq.so")
 ROOT = os.path.dirname(HERE)
 
 SOURCES = ["api.hip", "quantize.hip", "sdpa_vec.hip", "sdpa_mfma.hip", "combine.hip", "order.hip", "bits.hip",
-           "wide.hip", "probe.hip"]
+           "wide.hip", "probe.hip", "bits_mfma.hip"]
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-fhip-fp32-correctly-rounded-divide-sqrt", "-fno-gpu-flush-denormals-to-zero",
@@ -32,7 +32,8 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
 PER_FILE = {"quantize.hip": ["-ffp-contract=off"], "bits.hip": ["-ffp-contract=off"],
             "wide.hip": ["-ffp-contract=off"],
             # keep MFMA accumulators in VGPRs: they are rescaled by VALU ops
-            "sdpa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+            "sdpa_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+            "bits_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc():

@@ -133,6 +133,13 @@ int rot_kind(const otq_cache* c)
 // needs no order: its chunks are equal but the last).
 bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
+// The 2-bit MFMA split pass: power-of-two head_dim, G <= 16, a K that is
+// neither rotated nor channel-scaled (q must be exact in fp16).
+bool b2_mfma_ok(const otq_cache* c, int G)
+{
+    return code_bits(c) == 2 && otq::split_b2_mfma_supports(c->head_dim, G, c->k_rot_signs || c->k_chan_scale);
+}
+
 int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
               int32_t variant_ov, int32_t splits_ov, otq_plan* p)
 {
@@ -150,14 +157,19 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         if (variant == OTQ_VARIANT_MFMA) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_AUTO) {
         // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
-        variant = code_bits(c) != 4                      ? OTQ_VARIANT_VECTOR
-                  : otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA
-                                                   : OTQ_VARIANT_VECTOR;
+        // (2-bit codes too, on a K that is neither rotated nor channel-scaled)
+        variant = code_bits(c) == 4   ? (otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR)
+                  : b2_mfma_ok(c, G) ? OTQ_VARIANT_MFMA
+                                     : OTQ_VARIANT_VECTOR;
     }
     if (!pow2_dim(D)) {
         if (variant != OTQ_VARIANT_VECTOR) return OTQ_EINVAL;
-    } else if (code_bits(c) != 4) {  // the b-bit split pass: vector arithmetic, any G <= 16
-        if (variant != OTQ_VARIANT_VECTOR) return OTQ_EUNSUPPORTED;
+    } else if (code_bits(c) != 4) {  // the b-bit split passes: vector (any), MFMA (2-bit, plain K)
+        if (variant == OTQ_VARIANT_MFMA) {
+            if (!b2_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
+        } else if (variant != OTQ_VARIANT_VECTOR) {
+            return OTQ_EINVAL;
+        }
     } else if (variant == OTQ_VARIANT_VECTOR) {
         if (!otq::split_vector_supports(D, G)) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_MFMA) {
@@ -172,17 +184,22 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     if (chunk == 0) {
         long long units = (long long)c->batch * c->num_kv_heads;
         int waves = 4, align = kChunkAlign;
-        if (variant == OTQ_VARIANT_MFMA) {
+        if (variant == OTQ_VARIANT_MFMA && code_bits(c) == 4) {
             units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
             waves = otq::split_mfma_block_waves(D);
             align = waves * OTQ_TILE;  // one tile per wave and round
         }
         // a batch takes its items longest first, which balances unequal
         // lengths better the more (smaller) items there are
-        // the b-bit split pass hides latency only with several blocks per CU
-        const long long target = (ordered_batch(c->batch) || code_bits(c) != 4)
-                                     ? kTargetWaves * kOrderedWaveFactor
-                                     : kTargetWaves;
+        // the vector b-bit split pass hides latency only with several blocks per CU
+        const bool bits_vec = code_bits(c) != 4 && variant == OTQ_VARIANT_VECTOR;
+        // the 2-bit MFMA pass (one KV head per block) is measured fastest
+        // with two waves per SIMD: on the 70B layer at 128K, 49.7 us at
+        // chunk 2048 against 76.2 us at 4096 and 53.5 us at 1024
+        const bool bits_mfma = code_bits(c) != 4 && variant == OTQ_VARIANT_MFMA;
+        const long long target = (ordered_batch(c->batch) || bits_vec) ? kTargetWaves * kOrderedWaveFactor
+                                 : bits_mfma                           ? kTargetWaves * 2
+                                                                       : kTargetWaves;
         const long long groups = target / waves;
         long long want = ((long long)max_len * units + groups - 1) / groups;
         want = (want + align - 1) / align * align;
@@ -402,7 +419,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.err = error_word();
     if (!a.err) return OTQ_EDEVICE;
     if (ordered_batch(a.B)) {
-        const int groups = chk.variant == OTQ_VARIANT_MFMA
+        const int groups = chk.variant == OTQ_VARIANT_MFMA && code_bits(cache) == 4
                                ? a.H / otq::split_mfma_heads_per_wave(D, num_q_heads / a.H, a.H)
                                : a.H;
         int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
@@ -413,7 +430,8 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
         a.items = items;
     }
     const hipError_t e = !pow2_dim(D)            ? otq::launch_split_wide(a, s)
-                         : code_bits(cache) != 4 ? otq::launch_split_bits(a, code_bits(cache), s)
+                         : code_bits(cache) != 4 ? (chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_b2_mfma(a, s)
+                                                                              : otq::launch_split_bits(a, code_bits(cache), s))
                          : chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
                                                            : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;
@@ -452,6 +470,7 @@ int run_combine(int32_t num_q_heads, const otq_cache* cache, const int32_t* lens
     a.lam = cache->k_chan_scale;
     a.vsigns = cache->v_rot_signs;
     a.qscale = scale * otq::kLog2eHost;
+    a.bits = code_bits(cache);
     a.err = error_word();
     if (!a.err) return OTQ_EDEVICE;
     const hipError_t e = otq::launch_lse_combine(a, s);
@@ -527,7 +546,6 @@ int check_decode_append(const void* q, const void* k_new, const void* v_new, int
                         : make_plan(num_q_heads, cache, max_len, 0, OTQ_VARIANT_AUTO, 0, chk);
     if (rc != OTQ_OK) return rc;
     if (!q || !k_new || !v_new || !lens || !out || !aligned16(q) || !aligned16(out)) return OTQ_EINVAL;
-    if (code_bits(cache) != 4) return OTQ_EUNSUPPORTED;  // the fused append writes int4 codes
     if (!pow2_dim(cache->head_dim)) return OTQ_EUNSUPPORTED;  // its combine has power-of-two forms only
     if (dtype != OTQ_F16 && dtype != OTQ_BF16) return OTQ_EUNSUPPORTED;
     if (!finite(scale)) return OTQ_EINVAL;

@@ -1,0 +1,512 @@
+// bits_mfma.hip - split pass of decode attention on 2-bit caches, on the
+// matrix cores.
+//
+// The 2-bit codes of the AdapTQ page (its core-mechanism section lists 2-,
+// 3- and 4-bit quantisation behind one pipeline) go through the same kind of
+// products as the int4 cache: G query heads sharing a KV head make scoring a
+// tile and weighting its values two genuine matrix products, run here as
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  The cache keeps the plain
+// b-bit rows (element i of a row at bits [2 i, 2 i + 2) of its little-endian
+// bit stream, K and V alike, fp32 group scales), so the append kernels and
+// the vector split pass share it.
+//
+// Exactness, as in the int4 split pass:
+//  * K codes enter as fp16 subnormals n 2^(2k - 24) of their offset-binary
+//    value n = c + 2: the 8 codes of one lane's k slots (channels 32 g + 8 r
+//    + 0..7, 16 consecutive bits of the row) are spread by one byte permute
+//    to bytes 0 and 2 of a register, and four and-xor masks give the four
+//    half pairs (channel 8 r + k, 8 r + k + 4) at bit 2k; the 4^k is
+//    cancelled by q's operand, the +2 by starting each group's accumulator at
+//    -2 * 2^-24 * sum(q), 2^24 is folded into the softmax scale;
+//  * V codes enter as signed normal fp16 integers: each code is extracted
+//    from its token's row (the lane's channel sits at the same bit of every
+//    row word), the two codes of a slot pair go into the mantissas of
+//    1024.0, and one packed subtraction of 1026 leaves c exactly, so the
+//    value products are exact and their sums plain fp32;
+//  * q rows are scaled by a power of two that puts the largest |element| in
+//    [2^14, 2^15) before the fp16 conversion (bf16 and fp16 inputs convert
+//    exactly), undone in the softmax scale;
+//  * x = p * s_v * 2^E is split into fp16 hi + lo operands; E follows the
+//    largest V scale seen, as in the int4 pass.
+// A 2-bit cache with a rotated or channel-scaled K takes the vector split
+// pass (its q is not exact in fp16); a rotated V is undone by the combine.
+//
+// Block = 4 waves, one (split, KV head, sequence); wave w takes the tiles w,
+// w + 4, ... of the split (32 tokens each).  Each tile (K rows, V rows, K and
+// V scales: 24 D bytes) is loaded into registers two tiles ahead, written to
+// the wave's LDS stage when its turn comes, and read back in the operand
+// layouts below.  Lane l = 16 r + n:
+//  scores  A = K codes (row = token 16 s + n, k = channels 32 g + 8 r + the
+//          slot order), B = q of query head n (columns >= G are zero);
+//          C = S[token 16 s + 4 r + i][head n]
+//  values  A = x (row = head n, k slots (2m, 2m + 1) = tokens 4 r + m and
+//          16 + 4 r + m: the tokens whose scores this lane holds), B = V codes
+//          (column = channel 16 cb + n, the same tokens), C = O[head 4 r + i]
+//          [channel 16 cb + n].
+#include "common.hpp"
+#include "kernels.hpp"
+#include "mfma_common.hpp"
+
+namespace otq {
+
+namespace {
+
+using namespace mfma;
+
+constexpr int kB2Waves = 4;  // waves per block
+// Tiles each wave holds in registers ahead of the one it computes (one at
+// head_dim 256, whose tiles take twice the registers).
+template <int D>
+constexpr int kB2Ahead = D == 256 ? 1 : 2;
+// Where the score accumulator starts at the offset correction (a register
+// quad per group, live through the loop) rather than taking it after the
+// MFMA: everywhere but head_dim 256, whose registers are full.
+template <int D>
+constexpr bool kB2QinitInAcc = D != 256;
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One tile of a KV head in a wave's LDS stage: K rows, V rows (32 x RB bytes
+// each, as in the cache), then the K and V scales (32 x NG fp32 each).
+template <int D>
+struct B2Tile {
+    static constexpr int RB = D / 4;   // bytes per 2-bit row
+    static constexpr int NG = D / kGroup;
+    static constexpr int KOFF = 0, VOFF = 32 * RB, KSOFF = 64 * RB, VSOFF = KSOFF + 32 * NG * 4;
+    static constexpr int BYTES = VSOFF + 32 * NG * 4;  // 24 D
+    static constexpr int SLOTS = BYTES / 16;            // 16-byte pieces
+    static constexpr int LOADS = (SLOTS + 63) / 64;     // pieces per lane
+    // the merge of the block's waves reuses the stages: 16 O rows padded by
+    // 4 floats, then 16 (m, l) pairs
+    static constexpr int RS = D + 4;
+    static constexpr int MERGE = 16 * RS * 4 + 16 * 8;
+    static constexpr int STAGE = BYTES > MERGE ? BYTES : MERGE;
+};
+
+// K: 8 codes (16 bits of a row, the lane's channels 32 g + 8 r + 0..7 at bit
+// 2e) -> 8 fp16 subnormals (c + 2) 2^(2k - 24); k slot (2k, 2k + 1) holds
+// channels (8 r + k, 8 r + k + 4).  sel moves the row word's half r & 1 to
+// bytes 0 and 2.
+__device__ __forceinline__ half8_t unpack_k2(uint32_t w, uint32_t sel)
+{
+    const uint32_t x = __builtin_amdgcn_perm(w, w, sel);
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t m = 0x00030003u << (2 * k), f = 0x00020002u << (2 * k);
+        h[k] = (x & m) ^ f;  // one v_bitop3: the sign bit flip makes c + 2
+    }
+    half8_t out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const half2_t p = __builtin_bit_cast(half2_t, h[k]);
+        out[2 * k] = p[0];
+        out[2 * k + 1] = p[1];
+    }
+    return out;
+}
+
+// V: the codes at bit sh of the row words of tokens (a[m], b[m]) -> k slots
+// (2m, 2m + 1) as exact fp16 integers c.
+__device__ __forceinline__ half8_t unpack_v2(const uint32_t (&wa)[4], const uint32_t (&wb)[4], int sh)
+{
+    const half2_t bias = half2_t{(_Float16)1026.0f, (_Float16)1026.0f};
+    half8_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t fa = __builtin_amdgcn_ubfe(wa[m], sh, 2), fb = __builtin_amdgcn_ubfe(wb[m], sh, 2);
+        const uint32_t u = (fa | (fb << 16)) ^ 0x64026402u;  // 1024 + (c + 2) in both halves
+        const half2_t p = __builtin_bit_cast(half2_t, u) - bias;
+        out[2 * m] = p[0];
+        out[2 * m + 1] = p[1];
+    }
+    return out;
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2)))
+void split_b2_mfma_kernel(SplitArgs a)
+{
+    using T = B2Tile<D>;
+    constexpr int NG = T::NG, NCB = D / 16, RB = T::RB, W = kB2Waves;
+    extern __shared__ __align__(16) char lds[];  // W stages of T::STAGE bytes
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    if (a.items) {  // a batch: the block's item in longest-first order
+        const int k = blockIdx.x + a.num_splits * (blockIdx.y + a.H * blockIdx.z);
+        const int2 it = a.items[k];
+        if (it.x < 0) return;  // block-uniform: no item
+        split = it.x;
+        b = it.y;
+        hk = k % a.H;
+    }
+    const int G = a.Hq / a.H;
+    const int n16 = lane & 15, r = lane >> 4;
+    const bool col_valid = n16 < G;
+    char* stage = lds + wave * T::STAGE;
+
+    // lens clamped to [0, max_len], then the fused append's token left to
+    // the combine
+    const int raw_len = a.lens[b];
+    const int len = max(min(max(raw_len, 0), a.max_len) - a.lens_offset, 0);
+    if (tid == 0 && split == 0 && hk == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
+    const int start = split * a.chunk;
+    if (start >= len) return;  // block-uniform: no partial for an empty split
+    const int end = min(start + a.chunk, len);
+    const int ntiles = (end - start + kTile - 1) / kTile;
+
+    // ---- per-lane sources of the tile's 16-byte pieces: K rows, V rows,
+    //      K scales, V scales, each contiguous for the tile's 32 tokens
+    const size_t head = (size_t)b * a.H + hk;
+    const char* src_base[T::LOADS];
+    int src_stride[T::LOADS];
+    bool src_on[T::LOADS];
+#pragma unroll
+    for (int k = 0; k < T::LOADS; ++k) {
+        const int i = 64 * k + lane;
+        src_on[k] = i < T::SLOTS;
+        const int o = 16 * i;
+        if (o < T::VOFF) {
+            src_base[k] = reinterpret_cast<const char*>(a.kc) + head * a.cap * RB + o;
+            src_stride[k] = RB;
+        } else if (o < T::KSOFF) {
+            src_base[k] = reinterpret_cast<const char*>(a.vc) + head * a.cap * RB + (o - T::VOFF);
+            src_stride[k] = RB;
+        } else if (o < T::VSOFF) {
+            src_base[k] = reinterpret_cast<const char*>(a.ks + head * a.cap * NG) + (o - T::KSOFF);
+            src_stride[k] = NG * 4;
+        } else {
+            src_base[k] = reinterpret_cast<const char*>(a.vs + head * a.cap * NG) + (o - T::VSOFF);
+            src_stride[k] = NG * 4;
+        }
+    }
+    constexpr int AH = kB2Ahead<D>;
+    u32x4_t pf[AH][T::LOADS];
+    auto load_tile = [&](u32x4_t (&dst)[T::LOADS], int it) {
+        const int tok0 = start + it * kTile;
+#pragma unroll
+        for (int k = 0; k < T::LOADS; ++k)
+            if (src_on[k])
+                dst[k] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t*>(src_base[k] + (size_t)tok0 * src_stride[k]));
+    };
+#pragma unroll
+    for (int k = 0; k < AH; ++k)
+        if (wave + k * W < ntiles) load_tile(pf[k], wave + k * W);
+
+    // ---- q: column n16 = query head hk G + n16, lane r holds channels
+    //      32 g + 8 r + 0..7; scaled by 2^qk (largest |q| in [2^14, 2^15))
+    float qx[NG][8];
+    {
+        const uint16_t* qsrc =
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk * G + (col_valid ? n16 : 0)) * D;
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const uint4 raw = *reinterpret_cast<const uint4*>(qsrc + 32 * g + 8 * r);
+            const uint32_t w4[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                qx[g][e] = col_valid ? widen((uint16_t)(w4[e / 2] >> (16 * (e % 2))), a.dtype) : 0.0f;
+        }
+    }
+    int qk = 0;
+    {
+        float qa = 0.0f;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qa = fmaxf(qa, fabsf(qx[g][e]));
+        qa = max_xor32(max_xor16(qa));
+        qk = qa > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(qa) : 0;  // qa = f 2^e, f in [0.5, 1)
+    }
+    // B operands: k slot (2k, 2k + 1) = channels (8 r + k, 8 r + k + 4) of the
+    // group, divided by 4^k (the code's position); the accumulator starts at
+    // -2 * 2^-24 * sum(q over the group)
+    half8_t qb[NG];
+    floatx4_t qinit4[kB2QinitInAcc<D> ? NG : 1];
+    float qinit1[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        float tq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const _Float16 v = (_Float16)__builtin_ldexpf(qx[g][k + 4 * h], qk);
+                qb[g][2 * k + h] = (_Float16)((float)v * __builtin_ldexpf(1.0f, -2 * k));
+                tq += (float)v;
+            }
+        const float qi = -2.0f * 0x1p-24f * sum_xor32(sum_xor16(tq));
+        if constexpr (kB2QinitInAcc<D>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
+        qinit1[g] = qi;
+    }
+    const float qmul = __builtin_ldexpf(a.qscale * 0x1p24f, -qk);
+    const uint32_t ksel = (r & 1) ? 0x0C030C02u : 0x0C010C00u;  // half r & 1 of a K row word
+    const int vsh = 2 * n16;                                   // the lane's channel in a V row word
+
+    float m_run = kNegInf;  // softmax reference of column n16
+    int e_v = 0;            // E (wave-uniform): the value operand carries 2^E
+    float v_lim = 0.0f;     // V scales above this move E
+    float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
+    floatx4_t acc[NCB];
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+
+    int slot = 0;
+    for (int it = wave; it < ntiles; it += W) {
+        // ---- the tile's registers into the stage, then the next load into them
+#pragma unroll
+        for (int k = 0; k < T::LOADS; ++k)
+            if (src_on[k])
+                *reinterpret_cast<u32x4_t*>(stage + 16 * (64 * k + lane)) = (AH > 1 && slot) ? pf[AH - 1][k] : pf[0][k];
+        if (it + AH * W < ntiles) {
+            if (AH == 1 || slot == 0) load_tile(pf[0], it + AH * W);
+            else load_tile(pf[AH - 1], it + AH * W);
+        }
+        slot = AH > 1 ? slot ^ 1 : 0;
+        const int tok0 = start + it * kTile;
+
+        // the scales of the lane's tokens 16 s + 4 r + i, group g
+        const float* ksc = reinterpret_cast<const float*>(stage + T::KSOFF);
+        const float* vsc = reinterpret_cast<const float*>(stage + T::VSOFF);
+        auto tok_of = [&](int s, int i) { return 16 * s + 4 * r + i; };
+        // a token past the end (only in the split's last tile) counts as
+        // absent: its score is -inf and its V scale 0 (set after the loads,
+        // so that no load is predicated)
+        const int nvalid = end - tok0;  // >= 32 but in the split's last tile
+        const bool tail = nvalid < kTile;  // wave-uniform
+        bool valid[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) valid[s][i] = tok_of(s, i) < nvalid;
+        // the V scales of the lane's tokens: in registers up to head_dim 128
+        // (zeroed past the end), read where used at 256 (and masked there)
+        constexpr bool SVR = D <= 128;
+        float svr[SVR ? 2 : 1][4][SVR ? NG : 1];
+        if constexpr (SVR) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int g = 0; g < NG; ++g) svr[s][i][g] = vsc[tok_of(s, i) * NG + g];
+            if (tail) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+#pragma unroll
+                        for (int g = 0; g < NG; ++g) svr[s][i][g] = valid[s][i] ? svr[s][i][g] : 0.0f;
+            }
+        }
+        auto vscale = [&](int s, int i, int g) {
+            if constexpr (SVR) {
+                return svr[s][i][g];
+            } else {
+                const float sc = vsc[tok_of(s, i) * NG + g];
+                return valid[s][i] ? sc : 0.0f;
+            }
+        };
+
+        // ---- scores T[s][i] (token 16 s + 4 r + i, column n16), / qmul
+        float Tt[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const char* krow = stage + T::KOFF + (16 * s + n16) * RB;
+            floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int g = 0; g < NG; ++g) {
+                const uint32_t w = *reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1)));
+                const floatx4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    unpack_k2(w, ksel), qb[g],
+                    kB2QinitInAcc<D> ? qinit4[kB2QinitInAcc<D> ? g : 0] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float di = kB2QinitInAcc<D> ? d[i] : d[i] + qinit1[g];
+                    const float term = ksc[tok_of(s, i) * NG + g] * di;
+                    tot[i] = (g == 0) ? term : tot[i] + term;
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Tt[s][i] = tot[i];
+        }
+        if (tail) {
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) Tt[s][i] = valid[s][i] ? Tt[s][i] : kNegInf;
+        }
+
+        // ---- online softmax of column n16 (base 2), reference with headroom
+        float mt = kNegInf;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) mt = fmaxf(mt, Tt[s][i]);
+        mt = max_xor32(max_xor16(mt)) * qmul;  // finite: the tile has a valid token
+        // the largest V scale of the lane's tokens (whatever the cache holds
+        // past the end is left out)
+        float svm = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int g = 0; g < NG; ++g) svm = fmaxf(svm, vscale(s, i, g));
+        const bool vmove = __any(svm > v_lim);
+        if (__any(mt > m_run) || vmove) {
+            const float m_new = (mt > m_run) ? mt + kHeadroom : m_run;
+            int e_new = e_v;
+            if (vmove) {  // wave-uniform: E from the wave's largest V scale
+                const int ve = __builtin_amdgcn_frexp_expf(group_max<64>(svm));
+                const int en = min(max(kVTarget - ve, kEMin), kEMax);
+                e_new = en;
+                v_lim = __builtin_ldexpf(1.0f, kVLimit - en);
+            }
+            const float alpha = exp2_approx(m_run - m_new);  // 0 on the first tile
+            const float alpha_o = __builtin_ldexpf(alpha, e_new - e_v);
+            l_lane *= alpha;
+            static_for<4>([&](auto iI) {
+                constexpr int i = decltype(iI)::value;
+                const float ai = row_quad_gather<i>(alpha_o, r);  // of column 4 r + i
+#pragma unroll
+                for (int cb = 0; cb < NCB; ++cb) acc[cb][i] *= ai;
+            });
+            m_run = m_new;
+            e_v = e_new;
+        }
+        float p[2][4];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                p[s][i] = exp2_approx(__builtin_fmaf(Tt[s][i], qmul, -m_run));
+                l_lane += p[s][i];
+            }
+
+        // ---- values: the row words of the lane's 8 tokens, NCB / 4 channel
+        //      blocks at a time (one 16-byte read per token)
+#pragma unroll
+        for (int q = 0; q < NCB / 4; ++q) {
+            uint32_t wv[2][4][4];  // [s][m][block cb - 4 q]
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) {
+                    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(
+                        stage + T::VOFF + (16 * s + 4 * r + m) * RB + 16 * q);
+                    wv[s][m][0] = w.x; wv[s][m][1] = w.y; wv[s][m][2] = w.z; wv[s][m][3] = w.w;
+                }
+            static_for<2>([&](auto gI) {
+                constexpr int gq = decltype(gI)::value;
+                const int g = 2 * q + gq;  // scale group of channel blocks 2 g, 2 g + 1
+                v4u_t ha, la;
+                static_for<4>([&](auto mI) {
+#pragma clang fp contract(off)
+                    constexpr int m = decltype(mI)::value;
+                    // a token past the end has scale 0 (not 0 times whatever the cache holds)
+                    const float x0 = p[0][m] * __builtin_ldexpf(vscale(0, m, g), e_v);
+                    const float x1 = p[1][m] * __builtin_ldexpf(vscale(1, m, g), e_v);
+                    ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
+                    la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
+                });
+                const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
+                static_for<2>([&](auto hI) {
+                    constexpr int h = decltype(hI)::value;
+                    const int cbq = 2 * gq + h;  // block 4 q + cbq = 2 g + h
+                    const uint32_t wa[4] = {wv[0][0][cbq], wv[0][1][cbq], wv[0][2][cbq], wv[0][3][cbq]};
+                    const uint32_t wb[4] = {wv[1][0][cbq], wv[1][1][cbq], wv[1][2][cbq], wv[1][3][cbq]};
+                    const half8_t B = unpack_v2(wa, wb, vsh);
+                    const int cb = 4 * q + cbq;
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
+                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
+                });
+            });
+        }
+    }
+
+    // ---- merge of the W waves (each writes its share into its own stage,
+    //      which it no longer reads), then the block's partial
+    auto merge_o = [&](int w) { return reinterpret_cast<float*>(lds + w * T::STAGE); };
+    auto merge_ml = [&](int w) { return reinterpret_cast<float2*>(merge_o(w) + 16 * T::RS); };
+    const float L = sum_xor32(sum_xor16(l_lane));
+    // acc carries 2^E: (M - F, l 2^F, acc 2^(F - E)) with F = floor(E / 2)
+    // keeps both sums inside fp32's range
+    const int f_e = e_v >> 1;
+    if (lane < 16) merge_ml(wave)[lane] = make_float2(m_run - (float)f_e, __builtin_ldexpf(L, f_e));
+    float* own = merge_o(wave);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * r + i;
+        if (h < G) {
+#pragma unroll
+            for (int cb = 0; cb < NCB; ++cb) own[h * T::RS + 16 * cb + n16] = __builtin_ldexpf(acc[cb][i], f_e - e_v);
+        }
+    }
+    __syncthreads();
+    constexpr int kMergeIters = (16 * (D / 4) + 64 * W - 1) / (64 * W);
+#pragma unroll
+    for (int k = 0; k < kMergeIters; ++k) {
+        const int i = tid + k * 64 * W;
+        if (i >= G * (D / 4)) break;
+        const int h = i / (D / 4), c = 4 * (i % (D / 4));
+        float2 ml[W];
+        float Mb = kNegInf;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {  // a wave without tiles left m = -inf, l = 0, O = 0
+            ml[w] = merge_ml(w)[h];
+            Mb = fmaxf(Mb, ml[w].x);
+        }
+        float4 o = {0.0f, 0.0f, 0.0f, 0.0f};
+        float Ls = 0.0f;
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            const float f = (ml[w].x == kNegInf) ? 0.0f : exp2_approx(ml[w].x - Mb);
+            const float4 x = *reinterpret_cast<const float4*>(merge_o(w) + h * T::RS + c);
+            o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
+            Ls += f * ml[w].y;
+        }
+        const size_t prow = ((size_t)b * a.Hq + hk * G + h) * a.num_splits + split;
+        *reinterpret_cast<float4*>(a.part_o + prow * D + c) = o;
+        if (c == 0) a.part_ml[prow] = make_float2(Mb, Ls);
+    }
+}
+
+}  // namespace
+
+bool split_b2_mfma_supports(int D, int G, bool rotated_or_scaled_k)
+{
+    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && !rotated_or_scaled_k;
+}
+
+namespace {
+
+template <int D>
+hipError_t launch_b2(const SplitArgs& a, hipStream_t stream)
+{
+    const size_t lds = (size_t)kB2Waves * B2Tile<D>::STAGE;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_b2_mfma_kernel<D>),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    dim3 grid(a.num_splits, a.H, a.B), block(64 * kB2Waves);
+    split_b2_mfma_kernel<D><<<grid, block, lds, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_split_b2_mfma(const SplitArgs& a, hipStream_t stream)
+{
+    if (a.signs || a.lam || a.Hq / a.H > 16) return hipErrorInvalidValue;
+    switch (a.D) {
+    case 64: return launch_b2<64>(a, stream);
+    case 128: return launch_b2<128>(a, stream);
+    case 256: return launch_b2<256>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace otq

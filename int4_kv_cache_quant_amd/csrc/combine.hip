@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     __shared__ float red_s[kThreads / 64];
     __shared__ float xch[DT > 0 ? DT : 1];   // butterflies, then the new token's V
     __shared__ float orow[VROT ? DT : 1];    // the output row before the inverse rotation
+    __shared__ int8_t bcodes[2][APPEND ? DT : 1];  // a b-bit token's K and V codes, before packing
     // every argument the loads below need, fetched together: otherwise the
     // fields arrive one scalar round trip after another, each gating the next
     // address
@@ -210,7 +211,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         int ck[1];
         // one channel per lane: the lane layout of a 64-channel vector, whose
         // 32-lane groups are this vector's 32-channel groups
-        const float sk = quantize_lane<64>(xk, ck, lane);
+        const int bits = a.bits;  // block-uniform: 4, or 2 / 3 (plain bit-stream rows)
+        const float sk = bits == 4 ? quantize_lane<64>(xk, ck, lane) : quantize_lane_bits(xk[0], ck[0], bits);
         float xv[1] = {widen(vx, a.dtype)};
         if (VROT) {  // V rotated as K is, with its own signs
             xv[0] = xv[0] * vsg;
@@ -218,8 +220,32 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
             xv[0] = xv[0] * a.rot_norm;
         }
         int cv[1];
-        const float sv = quantize_lane<64>(xv, cv, lane);
-        if (writer) {
+        const float sv = bits == 4 ? quantize_lane<64>(xv, cv, lane) : quantize_lane_bits(xv[0], cv[0], bits);
+        if (bits != 4) {  // block-uniform: b-bit rows, written whole from the staged codes
+            const size_t head = (size_t)b * a.H + kvh, krow = head * a.cap + pos;
+            if (writer) {
+                bcodes[0][ch] = (int8_t)ck[0];
+                bcodes[1][ch] = (int8_t)cv[0];
+                if (ch % kGroup == 0) {
+                    a.ks[krow * (DA / kGroup) + ch / kGroup] = sk;
+                    a.vs[krow * (DA / kGroup) + ch / kGroup] = sv;
+                }
+            }
+            __syncthreads();
+            const int nword = DA * bits / 32;  // words per row
+            if (writer && tid < 2 * nword) {   // thread t: word t % nword of the K (t < nword) or V row
+                const int which = tid / nword, wi = tid % nword;
+                uint32_t word = 0;
+                const int i0 = (32 * wi) / bits, i1 = min((32 * wi + 31) / bits, DA - 1);
+                for (int i = i0; i <= i1; ++i) {
+                    const uint32_t u = (uint32_t)bcodes[which][i] & ((1u << bits) - 1u);
+                    const int off = i * bits - 32 * wi;  // negative for a code that starts in the word before
+                    word |= off >= 0 ? u << off : u >> -off;
+                }
+                uint8_t* rows = which == 0 ? a.kc : a.vc;
+                reinterpret_cast<uint32_t*>(rows + krow * (size_t)(DA * bits / 8))[wi] = word;
+            }
+        } else if (writer) {
             const size_t head = (size_t)b * a.H + kvh, krow = head * a.cap + pos;
             const int cnext = __shfl_xor(ck[0], 1, 64);
             if ((ch & 1) == 0)
@@ -324,7 +350,8 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
     // blocks (2048)
     const bool pow2 = a.D == 64 || a.D == 128 || a.D == 256;  // the whole-row forms' widths
     const bool big = !append && pow2 && (long)a.B * a.Hq * (a.D / kCh) > 2048;
-    const bool rows = vrot || (append && rot) || big;
+    // (and for the append of b-bit codes, whose rows one block packs)
+    const bool rows = vrot || (append && rot) || big || (append && a.bits != 4);
     dim3 grid(a.B * a.Hq, rows ? 1 : a.D / kCh), block(kThreads);
     if (!append && !rows) {
         lse_combine_kernel<0, false, false, false, false, false><<<grid, block, 0, stream>>>(a);

@@ -68,6 +68,10 @@ hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_n
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                 const int32_t* pos, const BitsRot& rot, unsigned* err, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
+// 2-bit codes on the matrix cores (head_dim 64, 128, 256; G <= 16; no K
+// rotation or channel scale).
+bool split_b2_mfma_supports(int D, int G, bool rotated_or_scaled_k);
+hipError_t launch_split_b2_mfma(const SplitArgs& a, hipStream_t stream);
 
 // Head widths that are multiples of 64 but not powers of two (192): the
 // append (K optionally rotated by the mixed-radix FFT, V optionally too) and
@@ -121,6 +125,7 @@ struct CombineArgs {
                             // output is brought back to the original basis
     float qscale;           // softmax scale * log2(e)
     unsigned* err;          // the device error word
+    int bits;               // code width of the appended token: 4, or 2 / 3 (plain rows)
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
 

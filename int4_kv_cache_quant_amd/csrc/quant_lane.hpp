@@ -120,6 +120,21 @@ __device__ __forceinline__ float quantize_lane(float (&x)[D / 64], int (&c)[D / 
     return quantize_elems<D / 64>(x, c);
 }
 
+// One element per lane, b-bit codes (b = 2 or 3): the group of 32 lanes
+// shares s = abs-max / (2^(b-1) - 1) (IEEE division), c = clamp(rint(x / s),
+// -2^(b-1), 2^(b-1) - 1), 0 when s == 0 -- the steps of the b-bit append.
+__device__ __forceinline__ float quantize_lane_bits(float x, int& c, int bits)
+{
+#pragma clang fp contract(off)
+    const float qmax = (float)((1 << (bits - 1)) - 1), qmin = -(float)(1 << (bits - 1));
+    const float a = group_max<kGroup>(fabsf(x));  // exact in any order
+    const float s = a / qmax;                     // correctly rounded IEEE division
+    float r = rintf(x / s);
+    r = fminf(fmaxf(r, qmin), qmax);
+    c = s != 0.0f ? (int)r : 0;
+    return s;
+}
+
 // y <- rot_norm * H y (y already multiplied by the signs), Sylvester order,
 // stages in ascending stride; a butterfly replaces (lower, upper) with
 // (lower + upper, lower - upper) exactly as the in-place fast Walsh-Hadamard

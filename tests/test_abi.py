@@ -297,11 +297,17 @@ def test_code_bits_host_checks():
         e.code_bits = 2
         setattr(e, field, FAKE)
         assert plan(e) == otq.OTQ_OK, field
+    # the fused step takes b-bit caches too; here it stops at the host checks
+    # (an input dtype it does not read), before any launch
     ws = lib.otq_sdpa_workspace_bytes(16, ctypes.byref(d), 64)
-    rc = lib.otq_sdpa_int4_decode_append(P(FAKE), P(FAKE), P(FAKE), 1, 16, ctypes.byref(d), P(FAKE), 64,
+    rc = lib.otq_sdpa_int4_decode_append(P(FAKE), P(FAKE), P(FAKE), 7, 16, ctypes.byref(d), P(FAKE), 64,
                                          ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws), None,
                                          None)
     assert rc == otq.OTQ_EUNSUPPORTED
+    rc = lib.otq_sdpa_int4_decode_append(P(FAKE + 8), P(FAKE), P(FAKE), 1, 16, ctypes.byref(d), P(FAKE), 64,
+                                         ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws), None,
+                                         None)
+    assert rc == otq.OTQ_EINVAL  # q not 16-byte aligned
 
 
 
@@ -397,3 +403,31 @@ def test_plan_interleaved_pieces():
     for desc in (one, batch):
         d = otq.otq_sdpa_plan(32 if desc is batch else 64, desc, 32768)
         assert d.num_splits == -(-32768 // d.chunk)
+
+
+def test_plan_variants_of_b_bit_caches():
+    """2-bit caches take the MFMA split pass by default unless K is rotated
+    or channel-scaled; 3-bit caches take the vector pass; forcing MFMA where
+    it does not apply is OTQ_EUNSUPPORTED."""
+    lib = otq.lib()
+    plain2 = _desc(B=1, H=8, D=128, cap=4096)
+    plain2.code_bits = 2
+    assert otq.otq_sdpa_plan(64, plain2, 4096).variant == otq.OTQ_VARIANT_MFMA
+    assert otq.otq_sdpa_plan(64, plain2, 4096, variant=otq.OTQ_VARIANT_VECTOR).variant == otq.OTQ_VARIANT_VECTOR
+    rot2 = _desc(B=1, H=8, D=128, cap=4096, signs=FAKE)
+    rot2.code_bits = 2
+    assert otq.otq_sdpa_plan(64, rot2, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(64, rot2, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    lam2 = _desc(B=1, H=8, D=128, cap=4096)
+    lam2.code_bits = 2
+    lam2.k_chan_scale = FAKE
+    assert otq.otq_sdpa_plan(64, lam2, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    three = _desc(B=1, H=8, D=128, cap=4096)
+    three.code_bits = 3
+    assert otq.otq_sdpa_plan(64, three, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(64, three, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    # the MFMA 2-bit plan: one KV head per block, four waves per chunk round
+    p = otq.otq_sdpa_plan(64, _desc(B=1, H=8, D=128, cap=131072), 131072)
+    p2 = otq.otq_sdpa_plan(64, plain2, 4096)
+    assert p2.chunk % 128 == 0 and p2.num_splits == -(-4096 // p2.chunk)
+    assert p.variant == otq.OTQ_VARIANT_MFMA

@@ -61,17 +61,20 @@ def test_bits_quantize_bit_exact(bits, D, dtype, chunk):
 
 @pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("G,D", [(1, 64), (4, 128), (8, 128), (16, 64), (2, 256)])
-def test_bits_sdpa_parity(bits, G, D):
+@pytest.mark.parametrize("variant", [otq.OTQ_VARIANT_AUTO, otq.OTQ_VARIANT_VECTOR])
+def test_bits_sdpa_parity(bits, G, D, variant):
     B, Hkv, cap = 2, 2, 448
     lens = [448, 77]
-    say(f"bits sdpa b={bits} G={G} D={D}")
+    say(f"bits sdpa b={bits} G={G} D={D} variant={variant}")
     k, v = _kv(B, Hkv, cap, D, torch.bfloat16, seed=bits * 100 + G + D)
     g = torch.Generator().manual_seed(G + D)
     q = torch.randn((B, G * Hkv, D), generator=g).to(torch.bfloat16)
     cache = _build(k, v, cap, bits, 100)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    plan = cache.plan(G * Hkv, max(lens), chunk=128)
-    assert plan.variant == otq.OTQ_VARIANT_VECTOR
+    plan = cache.plan(G * Hkv, max(lens), chunk=128, variant=variant)
+    # 2-bit codes default to the MFMA split pass, 3-bit ones take the vector one
+    want = otq.OTQ_VARIANT_MFMA if (bits == 2 and variant == otq.OTQ_VARIANT_AUTO) else otq.OTQ_VARIANT_VECTOR
+    assert plan.variant == want
     scale = 1.0 / math.sqrt(D)
     out = cache.decode(q.to(DEV), lens_t, max(lens), scale, plan=plan)
     torch.cuda.synchronize()
@@ -177,3 +180,70 @@ def test_bits_with_rotations_and_scale(bits, opts, G, D):
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
 
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("opts", ["plain", "vrot", "srht+lam", "srft+vrot"])
+@pytest.mark.parametrize("G,D", [(8, 128), (4, 64), (2, 256)])
+def test_bits_fused_decode_step(bits, opts, G, D):
+    """One decode step of a b-bit cache in one call: the split pass covers
+    [0, lens - 1), the combine quantises the token at lens - 1 into its b-bit
+    rows and merges it.  The token's slot holds junk before the call (code
+    bytes and Inf/NaN scales); afterwards the whole cache equals the oracle's
+    quantisation bit for bit and the outputs match the fp64 oracle.  2-bit
+    caches with a plain K take the MFMA split pass, the others the vector
+    one."""
+    B, Hkv, cap = 3, 2, 320
+    lens = [301, 96, 1]  # a token inside a tile, one opening a tile, one alone
+    kind = "srft" if "srft" in opts else "srht"
+    say(f"bits fused b={bits} opts={opts} G={G} D={D}")
+    k, v = _kv(B, Hkv, cap, D, torch.bfloat16, seed=bits * 53 + G + D + len(opts))
+    g = torch.Generator().manual_seed(G * D + bits + 5)
+    q = torch.randn((B, G * Hkv, D), generator=g).to(torch.bfloat16)
+    sk = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if ("srht" in opts or "srft" in opts) else None
+    sv = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if "vrot" in opts else None
+    lam = torch.exp2(torch.rand(D, generator=g) * 4.0 - 2.0) if "lam" in opts else None
+    cache = otq.Int4KVCache(B, Hkv, D, cap, device=DEV, code_bits=bits,
+                            rot_signs=None if sk is None else sk.to(DEV), rot_kind=kind,
+                            chan_scale=None if lam is None else lam.to(DEV),
+                            v_rot_signs=None if sv is None else sv.to(DEV))
+    pos = torch.zeros(B, dtype=torch.int32, device=DEV)
+    cache.append(k.to(DEV).contiguous(), v.to(DEV).contiguous(), pos)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(bits + D)
+    for b, n in enumerate(lens):  # junk in the new token's slot
+        cache.k_codes[b, :, n - 1] = torch.from_numpy(rng.integers(0, 256, size=(Hkv, D * bits // 8),
+                                                                   dtype=np.uint8)).to(DEV)
+        cache.v_codes[b, :, n - 1] = torch.from_numpy(rng.integers(0, 256, size=(Hkv, D * bits // 8),
+                                                                   dtype=np.uint8)).to(DEV)
+        cache.k_scales[b, :, n - 1] = float("nan")
+        cache.v_scales[b, :, n - 1] = float("inf")
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    idx = (lens_t.long() - 1)
+    ar = torch.arange(B, device=DEV)
+    kn = k.to(DEV)[ar, :, idx].contiguous()
+    vn = v.to(DEV)[ar, :, idx].contiguous()
+    scale = 1.0 / math.sqrt(D)
+    plan = cache.plan(G * Hkv, max(lens), chunk=128)
+    want = otq.OTQ_VARIANT_MFMA if (bits == 2 and sk is None and lam is None) else otq.OTQ_VARIANT_VECTOR
+    assert plan.variant == want
+    otq.otq_last_device_error()
+    out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max(lens), scale, plan=plan)
+    torch.cuda.synchronize()
+    assert otq.otq_last_device_error() == 0
+    rn = cache.rot_norm
+    lam_np = None if lam is None else lam.numpy()
+    sk_np = None if sk is None else sk.numpy()
+    sv_np = None if sv is None else sv.numpy()
+    kc, ks = oracle.quantize(to_bits(k), "bf16", signs=sk_np, rot_norm=rn, chan_scale=lam_np, rot_kind=kind,
+                             code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(v), "bf16", signs=sv_np, rot_norm=rn, rot_kind=kind, code_bits=bits)
+    assert np.array_equal(cache.k_codes.cpu().numpy(), kc)
+    assert np.array_equal(cache.k_scales.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(cache.v_codes.cpu().numpy(), vc)
+    assert np.array_equal(cache.v_scales.cpu().numpy().view(np.uint32), vs.view(np.uint32))
+    ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale, signs=sk_np,
+                      rot_norm=rn, threads=8, chan_scale=lam_np, v_signs=sv_np, rot_kind=kind, code_bits=bits)
+    ma, rel = errors(out.cpu().numpy(), ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert ma <= MAX_ABS and rel <= REL_L2

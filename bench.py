@@ -449,7 +449,7 @@ def bench_workload(wnum, args, primary):
     achieved = split_bytes / (split_us * 1e-6) / 1e9
     step_gbps = layer_bytes / (us_layer_step * 1e-6) / 1e9
     if wbits != 4:
-        kname = "split_b2_mfma" if plan.variant == 2 else "split_bits"
+        kname = "split_bits_mfma" if plan.variant == 2 else "split_bits"
     else:
         kname = "split_mfma" if plan.variant == 2 else "split_vec"
     if not primary:

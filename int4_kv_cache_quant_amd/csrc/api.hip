@@ -133,11 +133,12 @@ int rot_kind(const otq_cache* c)
 // needs no order: its chunks are equal but the last).
 bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
-// The 2-bit MFMA split pass: power-of-two head_dim, G <= 16, a K that is
-// neither rotated nor channel-scaled (q must be exact in fp16).
-bool b2_mfma_ok(const otq_cache* c, int G)
+// The b-bit MFMA split pass: 2- or 3-bit codes, power-of-two head_dim,
+// G <= 16, a K that is neither rotated nor channel-scaled (q must be exact
+// in fp16).
+bool bits_mfma_ok(const otq_cache* c, int G)
 {
-    return code_bits(c) == 2 && otq::split_b2_mfma_supports(c->head_dim, G, c->k_rot_signs || c->k_chan_scale);
+    return otq::split_bits_mfma_supports(c->head_dim, G, code_bits(c), c->k_rot_signs || c->k_chan_scale);
 }
 
 int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
@@ -157,16 +158,16 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         if (variant == OTQ_VARIANT_MFMA) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_AUTO) {
         // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
-        // (2-bit codes too, on a K that is neither rotated nor channel-scaled)
+        // (2- and 3-bit codes too, on a K that is neither rotated nor channel-scaled)
         variant = code_bits(c) == 4   ? (otq::split_mfma_supports(D, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR)
-                  : b2_mfma_ok(c, G) ? OTQ_VARIANT_MFMA
+                  : bits_mfma_ok(c, G) ? OTQ_VARIANT_MFMA
                                      : OTQ_VARIANT_VECTOR;
     }
     if (!pow2_dim(D)) {
         if (variant != OTQ_VARIANT_VECTOR) return OTQ_EINVAL;
-    } else if (code_bits(c) != 4) {  // the b-bit split passes: vector (any), MFMA (2-bit, plain K)
+    } else if (code_bits(c) != 4) {  // the b-bit split passes: vector (any), MFMA (plain K)
         if (variant == OTQ_VARIANT_MFMA) {
-            if (!b2_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
+            if (!bits_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
         } else if (variant != OTQ_VARIANT_VECTOR) {
             return OTQ_EINVAL;
         }
@@ -430,8 +431,9 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
         a.items = items;
     }
     const hipError_t e = !pow2_dim(D)            ? otq::launch_split_wide(a, s)
-                         : code_bits(cache) != 4 ? (chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_b2_mfma(a, s)
-                                                                              : otq::launch_split_bits(a, code_bits(cache), s))
+                         : code_bits(cache) != 4 ? (chk.variant == OTQ_VARIANT_MFMA
+                                                        ? otq::launch_split_bits_mfma(a, code_bits(cache), s)
+                                                        : otq::launch_split_bits(a, code_bits(cache), s))
                          : chk.variant == OTQ_VARIANT_MFMA ? otq::launch_split_mfma(a, s)
                                                            : otq::launch_split_vector(a, s);
     return e == hipSuccess ? OTQ_OK : OTQ_EDEVICE;

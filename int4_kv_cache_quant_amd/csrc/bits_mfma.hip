@@ -1,41 +1,44 @@
-// bits_mfma.hip - split pass of decode attention on 2-bit caches, on the
-// matrix cores.
+// bits_mfma.hip - split pass of decode attention on 2- and 3-bit caches, on
+// the matrix cores.
 //
-// The 2-bit codes of the AdapTQ page (its core-mechanism section lists 2-,
-// 3- and 4-bit quantisation behind one pipeline) go through the same kind of
+// The 2- and 3-bit codes of the AdapTQ page (its core-mechanism section
+// lists 2-, 3- and 4-bit quantisation behind one pipeline) go through the same kind of
 // products as the int4 cache: G query heads sharing a KV head make scoring a
 // tile and weighting its values two genuine matrix products, run here as
 // v_mfma_f32_16x16x32_f16 with fp32 accumulation.  The cache keeps the plain
-// b-bit rows (element i of a row at bits [2 i, 2 i + 2) of its little-endian
+// b-bit rows (element i of a row at bits [b i, b i + b) of its little-endian
 // bit stream, K and V alike, fp32 group scales), so the append kernels and
 // the vector split pass share it.
 //
 // Exactness, as in the int4 split pass:
-//  * K codes enter as fp16 subnormals n 2^(2k - 24) of their offset-binary
-//    value n = c + 2: the 8 codes of one lane's k slots (channels 32 g + 8 r
-//    + 0..7, 16 consecutive bits of the row) are spread by one byte permute
-//    to bytes 0 and 2 of a register, and four and-xor masks give the four
-//    half pairs (channel 8 r + k, 8 r + k + 4) at bit 2k; the 4^k is
-//    cancelled by q's operand, the +2 by starting each group's accumulator at
-//    -2 * 2^-24 * sum(q), 2^24 is folded into the softmax scale;
+//  * K codes enter as fp16 subnormals n 2^(e_k - 24) of their offset-binary
+//    value n = c + 2^(b-1): the 8 codes of one lane's k slots (channels
+//    32 g + 8 r + 0..7, 8b consecutive bits of the row) are brought to bit 0
+//    (a byte permute at 2 bits, a funnel shift at 3), channels 4..7 are
+//    moved to the upper half, and and-xor masks give the four half pairs
+//    (channel 8 r + k, 8 r + k + 4) at a position e_k (2k at 2 bits; 0, 3, 6
+//    and, after a shift, 0 at 3); 2^e_k is cancelled by q's operand, the
+//    offset by starting each group's accumulator at -2^(b-1) 2^-24 sum(q),
+//    2^24 is folded into the softmax scale;
 //  * V codes enter as signed normal fp16 integers: each code is extracted
-//    from its token's row (the lane's channel sits at the same bit of every
-//    row word), the two codes of a slot pair go into the mantissas of
-//    1024.0, and one packed subtraction of 1026 leaves c exactly, so the
-//    value products are exact and their sums plain fp32;
+//    from its token's row (a bit-field extract at 2 bits, a funnel shift at
+//    3), the two codes of a slot pair go into the mantissas of 1024.0, and
+//    one packed subtraction of 1024 + 2^(b-1) leaves c exactly, so the value
+//    products are exact and their sums plain fp32;
 //  * q rows are scaled by a power of two that puts the largest |element| in
 //    [2^14, 2^15) before the fp16 conversion (bf16 and fp16 inputs convert
 //    exactly), undone in the softmax scale;
 //  * x = p * s_v * 2^E is split into fp16 hi + lo operands; E follows the
 //    largest V scale seen, as in the int4 pass.
-// A 2-bit cache with a rotated or channel-scaled K takes the vector split
-// pass (its q is not exact in fp16); a rotated V is undone by the combine.
+// A b-bit cache with a rotated or channel-scaled K takes the vector split
+// pass (its q is not exact in fp16), as do 3-bit codes at head_dim 256; a
+// rotated V is undone by the combine.
 //
 // Block = 4 waves, one (split, KV head, sequence); wave w takes the tiles w,
 // w + 4, ... of the split (32 tokens each).  Each tile (K rows, V rows, K and
-// V scales: 24 D bytes) is loaded into registers two tiles ahead, written to
+// V scales: (8 b + 8) D bytes) is loaded into registers two tiles ahead, written to
 // the wave's LDS stage when its turn comes, and read back in the operand
-// layouts below.  Lane l = 16 r + n:
+// layouts below ((8 b + 8) D bytes per tile).  Lane l = 16 r + n:
 //  scores  A = K codes (row = token 16 s + n, k = channels 32 g + 8 r + the
 //          slot order), B = q of query head n (columns >= G are zero);
 //          C = S[token 16 s + 4 r + i][head n]
@@ -68,12 +71,12 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // One tile of a KV head in a wave's LDS stage: K rows, V rows (32 x RB bytes
 // each, as in the cache), then the K and V scales (32 x NG fp32 each).
-template <int D>
-struct B2Tile {
-    static constexpr int RB = D / 4;   // bytes per 2-bit row
+template <int D, int BITS>
+struct BTile {
+    static constexpr int RB = D * BITS / 8;  // bytes per row
     static constexpr int NG = D / kGroup;
     static constexpr int KOFF = 0, VOFF = 32 * RB, KSOFF = 64 * RB, VSOFF = KSOFF + 32 * NG * 4;
-    static constexpr int BYTES = VSOFF + 32 * NG * 4;  // 24 D
+    static constexpr int BYTES = VSOFF + 32 * NG * 4;  // (8 BITS + 8) D
     static constexpr int SLOTS = BYTES / 16;            // 16-byte pieces
     static constexpr int LOADS = (SLOTS + 63) / 64;     // pieces per lane
     // the merge of the block's waves reuses the stages: 16 O rows padded by
@@ -106,16 +109,46 @@ __device__ __forceinline__ half8_t unpack_k2(uint32_t w, uint32_t sel)
     return out;
 }
 
-// V: the codes at bit sh of the row words of tokens (a[m], b[m]) -> k slots
-// (2m, 2m + 1) as exact fp16 integers c.
-__device__ __forceinline__ half8_t unpack_v2(const uint32_t (&wa)[4], const uint32_t (&wb)[4], int sh)
+// K, 3-bit: 8 codes (24 bits from bit 0 of f, the lane's channels 32 g +
+// 8 r + 0..7 at bit 3e) -> 8 fp16 subnormals (c + 4) 2^(kK3Exp[k] - 24); k
+// slot (2k, 2k + 1) holds channels (8 r + k, 8 r + k + 4).  The channels
+// 4..7 are first moved to bit 16; the fourth pair (bits 9..11 and 25..27)
+// is shifted down, as it would reach into the fp16 exponent.
+constexpr int kK3Exp[4] = {0, 3, 6, 0};
+__device__ __forceinline__ half8_t unpack_k3(uint32_t f)
 {
-    const half2_t bias = half2_t{(_Float16)1026.0f, (_Float16)1026.0f};
+    const uint32_t x = (f & 0x00000FFFu) | ((f << 4) & 0x0FFF0000u);
+    uint32_t h[4];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const uint32_t m = 0x00070007u << (3 * k), fl = 0x00040004u << (3 * k);
+        h[k] = (x & m) ^ fl;  // the sign bit flip makes c + 4
+    }
+    h[3] = ((x >> 9) & 0x00070007u) ^ 0x00040004u;
+    half8_t out;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const half2_t p = __builtin_bit_cast(half2_t, h[k]);
+        out[2 * k] = p[0];
+        out[2 * k + 1] = p[1];
+    }
+    return out;
+}
+
+// V: the b-bit codes (raw two's complement fields, at bit 0) of tokens
+// (a[m], b[m]) -> k slots (2m, 2m + 1) as exact fp16 integers c: 1024 +
+// (c + 2^(b-1)) in each half (the flip of the field's top bit is the
+// offset), less 1024 + 2^(b-1).
+template <int BITS>
+__device__ __forceinline__ half8_t unpack_v(const uint32_t (&fa)[4], const uint32_t (&fb)[4])
+{
+    constexpr uint32_t half_magic = 0x6400u | (1u << (BITS - 1));
+    constexpr float off = 1024.0f + (float)(1 << (BITS - 1));
+    const half2_t bias = half2_t{(_Float16)off, (_Float16)off};
     half8_t out;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t fa = __builtin_amdgcn_ubfe(wa[m], sh, 2), fb = __builtin_amdgcn_ubfe(wb[m], sh, 2);
-        const uint32_t u = (fa | (fb << 16)) ^ 0x64026402u;  // 1024 + (c + 2) in both halves
+        const uint32_t u = (fa[m] | (fb[m] << 16)) ^ (half_magic | (half_magic << 16));
         const half2_t p = __builtin_bit_cast(half2_t, u) - bias;
         out[2 * m] = p[0];
         out[2 * m + 1] = p[1];
@@ -123,11 +156,12 @@ __device__ __forceinline__ half8_t unpack_v2(const uint32_t (&wa)[4], const uint
     return out;
 }
 
-template <int D>
+template <int D, int BITS>
 __global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2)))
-void split_b2_mfma_kernel(SplitArgs a)
+void split_bits_mfma_kernel(SplitArgs a)
 {
-    using T = B2Tile<D>;
+    static_assert(BITS == 2 || BITS == 3, "2- or 3-bit codes");
+    using T = BTile<D, BITS>;
     constexpr int NG = T::NG, NCB = D / 16, RB = T::RB, W = kB2Waves;
     extern __shared__ __align__(16) char lds[];  // W stages of T::STAGE bytes
 
@@ -222,8 +256,9 @@ void split_b2_mfma_kernel(SplitArgs a)
         qk = qa > 0.0f ? 15 - __builtin_amdgcn_frexp_expf(qa) : 0;  // qa = f 2^e, f in [0.5, 1)
     }
     // B operands: k slot (2k, 2k + 1) = channels (8 r + k, 8 r + k + 4) of the
-    // group, divided by 4^k (the code's position); the accumulator starts at
-    // -2 * 2^-24 * sum(q over the group)
+    // group, divided by the code's positional power of two (4^k at 2 bits,
+    // kK3Exp at 3); the accumulator starts at -2^(b-1) * 2^-24 * sum(q over
+    // the group)
     half8_t qb[NG];
     floatx4_t qinit4[kB2QinitInAcc<D> ? NG : 1];
     float qinit1[NG];
@@ -235,16 +270,19 @@ void split_b2_mfma_kernel(SplitArgs a)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const _Float16 v = (_Float16)__builtin_ldexpf(qx[g][k + 4 * h], qk);
-                qb[g][2 * k + h] = (_Float16)((float)v * __builtin_ldexpf(1.0f, -2 * k));
+                const int pe = BITS == 2 ? 2 * k : kK3Exp[k];
+                qb[g][2 * k + h] = (_Float16)((float)v * __builtin_ldexpf(1.0f, -pe));
                 tq += (float)v;
             }
-        const float qi = -2.0f * 0x1p-24f * sum_xor32(sum_xor16(tq));
+        const float qi = -(float)(1 << (BITS - 1)) * 0x1p-24f * sum_xor32(sum_xor16(tq));
         if constexpr (kB2QinitInAcc<D>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
         qinit1[g] = qi;
     }
     const float qmul = __builtin_ldexpf(a.qscale * 0x1p24f, -qk);
-    const uint32_t ksel = (r & 1) ? 0x0C030C02u : 0x0C010C00u;  // half r & 1 of a K row word
-    const int vsh = 2 * n16;                                   // the lane's channel in a V row word
+    // 2 bits: the lane's K field is half r & 1 of word 2 g + r / 2 of a row;
+    // 3 bits: it starts at bit 24 r of the group's three words
+    const uint32_t ksel = (r & 1) ? 0x0C030C02u : 0x0C010C00u;
+    const int k3w = (24 * r) >> 5, k3s = (24 * r) & 31;
 
     float m_run = kNegInf;  // softmax reference of column n16
     int e_v = 0;            // E (wave-uniform): the value operand carries 2^E
@@ -319,9 +357,17 @@ void split_b2_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                const uint32_t w = *reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1)));
+                half8_t A;
+                if constexpr (BITS == 2) {
+                    A = unpack_k2(*reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1))), ksel);
+                } else {
+                    // the word after the field's first lies inside the stage
+                    // even for the tile's last row (the V rows follow)
+                    const uint32_t* kw = reinterpret_cast<const uint32_t*>(krow) + 3 * g + k3w;
+                    A = unpack_k3(__builtin_amdgcn_alignbit(kw[1], kw[0], k3s));
+                }
                 const floatx4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    unpack_k2(w, ksel), qb[g],
+                    A, qb[g],
                     kB2QinitInAcc<D> ? qinit4[kB2QinitInAcc<D> ? g : 0] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -388,18 +434,45 @@ void split_b2_mfma_kernel(SplitArgs a)
             }
 
         // ---- values: the row words of the lane's 8 tokens, NCB / 4 channel
-        //      blocks at a time (one 16-byte read per token)
+        //      blocks (64 channels: 4 words at 2 bits, 6 at 3) at a time
+        constexpr int QW = 2 * BITS;  // row words per 4 channel blocks
 #pragma unroll
         for (int q = 0; q < NCB / 4; ++q) {
-            uint32_t wv[2][4][4];  // [s][m][block cb - 4 q]
+            uint32_t wv[2][4][QW];  // [s][m][word of the block set]
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) {
-                    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(
-                        stage + T::VOFF + (16 * s + 4 * r + m) * RB + 16 * q);
-                    wv[s][m][0] = w.x; wv[s][m][1] = w.y; wv[s][m][2] = w.z; wv[s][m][3] = w.w;
+                    const char* src = stage + T::VOFF + (16 * s + 4 * r + m) * RB + 4 * QW * q;
+                    if constexpr (BITS == 2) {
+                        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
+                        wv[s][m][0] = w.x; wv[s][m][1] = w.y; wv[s][m][2] = w.z; wv[s][m][3] = w.w;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 3; ++j) {  // 8-byte aligned: rows are 48 D / 128 words apart
+                            const uint2 w = *reinterpret_cast<const uint2*>(src + 8 * j);
+                            wv[s][m][2 * j] = w.x; wv[s][m][2 * j + 1] = w.y;
+                        }
+                    }
                 }
+            // the lane's field (channel 16 cb + n16) in the block set's words
+            // (CBQ a compile-time block index, so that every word index is one)
+            auto field = [&](int s, int m, auto cbqI) -> uint32_t {
+                constexpr int CBQ = decltype(cbqI)::value;
+                if constexpr (BITS == 2) {
+                    return __builtin_amdgcn_ubfe(wv[s][m][CBQ], 2 * n16, 2);
+                } else {
+                    // bits [48 CBQ + 3 n16, + 3) of the 192: inside the word
+                    // pair starting at word (48 CBQ) / 32, at bit sh < 62 of
+                    // the pair (32-bit operations only, so that the words
+                    // stay in registers)
+                    constexpr int P0 = (3 * CBQ) >> 1, O0 = (48 * CBQ) & 31;
+                    const uint32_t lo = wv[s][m][P0], hi = wv[s][m][P0 + 1];
+                    const int sh = O0 + 3 * n16;
+                    const uint32_t x = sh < 32 ? __builtin_amdgcn_alignbit(hi, lo, sh) : hi >> (sh - 32);
+                    return x & 7u;
+                }
+            };
             static_for<2>([&](auto gI) {
                 constexpr int gq = decltype(gI)::value;
                 const int g = 2 * q + gq;  // scale group of channel blocks 2 g, 2 g + 1
@@ -416,10 +489,11 @@ void split_b2_mfma_kernel(SplitArgs a)
                 const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
                 static_for<2>([&](auto hI) {
                     constexpr int h = decltype(hI)::value;
-                    const int cbq = 2 * gq + h;  // block 4 q + cbq = 2 g + h
-                    const uint32_t wa[4] = {wv[0][0][cbq], wv[0][1][cbq], wv[0][2][cbq], wv[0][3][cbq]};
-                    const uint32_t wb[4] = {wv[1][0][cbq], wv[1][1][cbq], wv[1][2][cbq], wv[1][3][cbq]};
-                    const half8_t B = unpack_v2(wa, wb, vsh);
+                    constexpr int cbq = 2 * gq + h;  // block 4 q + cbq = 2 g + h
+                    const std::integral_constant<int, cbq> cI;
+                    const uint32_t fa[4] = {field(0, 0, cI), field(0, 1, cI), field(0, 2, cI), field(0, 3, cI)};
+                    const uint32_t fb[4] = {field(1, 0, cI), field(1, 1, cI), field(1, 2, cI), field(1, 3, cI)};
+                    const half8_t B = unpack_v<BITS>(fa, fb);
                     const int cb = 4 * q + cbq;
                     acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
                     acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
@@ -477,34 +551,39 @@ void split_b2_mfma_kernel(SplitArgs a)
 
 }  // namespace
 
-bool split_b2_mfma_supports(int D, int G, bool rotated_or_scaled_k)
+bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
 {
-    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && !rotated_or_scaled_k;
+    // (3-bit codes at head_dim 256 would spill: the vector pass serves them)
+    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (bits == 2 || (bits == 3 && D <= 128)) &&
+           !rotated_or_scaled_k;
 }
 
 namespace {
 
-template <int D>
-hipError_t launch_b2(const SplitArgs& a, hipStream_t stream)
+template <int D, int BITS>
+hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 {
-    const size_t lds = (size_t)kB2Waves * B2Tile<D>::STAGE;
-    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(&split_b2_mfma_kernel<D>),
-                                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const size_t lds = (size_t)kB2Waves * BTile<D, BITS>::STAGE;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&split_bits_mfma_kernel<D, BITS>), hipFuncAttributeMaxDynamicSharedMemorySize,
+        (int)lds);
     if (attr != hipSuccess) return attr;
     dim3 grid(a.num_splits, a.H, a.B), block(64 * kB2Waves);
-    split_b2_mfma_kernel<D><<<grid, block, lds, stream>>>(a);
+    split_bits_mfma_kernel<D, BITS><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_split_b2_mfma(const SplitArgs& a, hipStream_t stream)
+hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream)
 {
     if (a.signs || a.lam || a.Hq / a.H > 16) return hipErrorInvalidValue;
-    switch (a.D) {
-    case 64: return launch_b2<64>(a, stream);
-    case 128: return launch_b2<128>(a, stream);
-    case 256: return launch_b2<256>(a, stream);
+    switch (a.D * 10 + bits) {
+    case 642: return launch_b<64, 2>(a, stream);
+    case 643: return launch_b<64, 3>(a, stream);
+    case 1282: return launch_b<128, 2>(a, stream);
+    case 1283: return launch_b<128, 3>(a, stream);
+    case 2562: return launch_b<256, 2>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

@@ -68,10 +68,10 @@ hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_n
                                 int cap, int bits, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
                                 const int32_t* pos, const BitsRot& rot, unsigned* err, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
-// 2-bit codes on the matrix cores (head_dim 64, 128, 256; G <= 16; no K
-// rotation or channel scale).
-bool split_b2_mfma_supports(int D, int G, bool rotated_or_scaled_k);
-hipError_t launch_split_b2_mfma(const SplitArgs& a, hipStream_t stream);
+// 2- and 3-bit codes on the matrix cores (head_dim 64, 128, 256; G <= 16;
+// no K rotation or channel scale).
+bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k);
+hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream);
 
 // Head widths that are multiples of 64 but not powers of two (192): the
 // append (K optionally rotated by the mixed-radix FFT, V optionally too) and

@@ -289,8 +289,8 @@ def test_code_bits_host_checks():
     d.code_bits = 3
     p = otq.otq_plan()
     assert lib.otq_sdpa_plan(16, ctypes.byref(d), 64, 0, 0, 0, ctypes.byref(p)) == otq.OTQ_OK
-    assert p.variant == otq.OTQ_VARIANT_VECTOR
-    assert plan(d, otq.OTQ_VARIANT_MFMA) == otq.OTQ_EUNSUPPORTED
+    assert p.variant == otq.OTQ_VARIANT_MFMA
+    assert plan(d, otq.OTQ_VARIANT_MFMA) == otq.OTQ_OK
     assert plan(d, otq.OTQ_VARIANT_VECTOR) == otq.OTQ_OK
     for field in ("k_rot_signs", "v_rot_signs", "k_chan_scale"):
         e = _desc()
@@ -406,9 +406,9 @@ def test_plan_interleaved_pieces():
 
 
 def test_plan_variants_of_b_bit_caches():
-    """2-bit caches take the MFMA split pass by default unless K is rotated
-    or channel-scaled; 3-bit caches take the vector pass; forcing MFMA where
-    it does not apply is OTQ_EUNSUPPORTED."""
+    """b-bit caches take the MFMA split pass by default unless K is rotated
+    or channel-scaled (3-bit codes at D = 256: the vector pass); forcing MFMA
+    where it does not apply is OTQ_EUNSUPPORTED."""
     lib = otq.lib()
     plain2 = _desc(B=1, H=8, D=128, cap=4096)
     plain2.code_bits = 2
@@ -424,8 +424,11 @@ def test_plan_variants_of_b_bit_caches():
     assert otq.otq_sdpa_plan(64, lam2, 4096).variant == otq.OTQ_VARIANT_VECTOR
     three = _desc(B=1, H=8, D=128, cap=4096)
     three.code_bits = 3
-    assert otq.otq_sdpa_plan(64, three, 4096).variant == otq.OTQ_VARIANT_VECTOR
-    assert otq.otq_sdpa_plan(64, three, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    assert otq.otq_sdpa_plan(64, three, 4096).variant == otq.OTQ_VARIANT_MFMA
+    wide3 = _desc(B=1, H=8, D=256, cap=4096)  # 3-bit codes at D = 256: vector only
+    wide3.code_bits = 3
+    assert otq.otq_sdpa_plan(64, wide3, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(64, wide3, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
     # the MFMA 2-bit plan: one KV head per block, four waves per chunk round
     p = otq.otq_sdpa_plan(64, _desc(B=1, H=8, D=128, cap=131072), 131072)
     p2 = otq.otq_sdpa_plan(64, plain2, 4096)

@@ -72,8 +72,9 @@ def test_bits_sdpa_parity(bits, G, D, variant):
     cache = _build(k, v, cap, bits, 100)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     plan = cache.plan(G * Hkv, max(lens), chunk=128, variant=variant)
-    # 2-bit codes default to the MFMA split pass, 3-bit ones take the vector one
-    want = otq.OTQ_VARIANT_MFMA if (bits == 2 and variant == otq.OTQ_VARIANT_AUTO) else otq.OTQ_VARIANT_VECTOR
+    # b-bit codes default to the MFMA split pass (3-bit ones at D = 256 to the vector one)
+    mfma_ok = bits == 2 or D <= 128
+    want = otq.OTQ_VARIANT_MFMA if (mfma_ok and variant == otq.OTQ_VARIANT_AUTO) else otq.OTQ_VARIANT_VECTOR
     assert plan.variant == want
     scale = 1.0 / math.sqrt(D)
     out = cache.decode(q.to(DEV), lens_t, max(lens), scale, plan=plan)
@@ -190,9 +191,9 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     [0, lens - 1), the combine quantises the token at lens - 1 into its b-bit
     rows and merges it.  The token's slot holds junk before the call (code
     bytes and Inf/NaN scales); afterwards the whole cache equals the oracle's
-    quantisation bit for bit and the outputs match the fp64 oracle.  2-bit
-    caches with a plain K take the MFMA split pass, the others the vector
-    one."""
+    quantisation bit for bit and the outputs match the fp64 oracle.  Caches
+    with a plain K take the MFMA split pass (3-bit ones at D = 256 the vector
+    one), the others the vector one."""
     B, Hkv, cap = 3, 2, 320
     lens = [301, 96, 1]  # a token inside a tile, one opening a tile, one alone
     kind = "srft" if "srft" in opts else "srht"
@@ -225,7 +226,8 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     vn = v.to(DEV)[ar, :, idx].contiguous()
     scale = 1.0 / math.sqrt(D)
     plan = cache.plan(G * Hkv, max(lens), chunk=128)
-    want = otq.OTQ_VARIANT_MFMA if (bits == 2 and sk is None and lam is None) else otq.OTQ_VARIANT_VECTOR
+    plain_k = sk is None and lam is None
+    want = otq.OTQ_VARIANT_MFMA if (plain_k and (bits == 2 or D <= 128)) else otq.OTQ_VARIANT_VECTOR
     assert plan.variant == want
     otq.otq_last_device_error()
     out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max(lens), scale, plan=plan)

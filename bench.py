@@ -31,9 +31,12 @@ sys.path.insert(0, ROOT)
 METRIC = "sdpa_int4 decode µs/layer-step + achieved HBM GB/s (% peak) at 128K ctx"
 HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {
-    2: ["int4_kv_cache_quant_amd/csrc/sdpa_mfma.hip", "int4_kv_cache_quant_amd/csrc/common.hpp"],
-    1: ["int4_kv_cache_quant_amd/csrc/sdpa_vec.hip", "int4_kv_cache_quant_amd/csrc/common.hpp"],
+CSRC = "int4_kv_cache_quant_amd/csrc/"
+KERNEL_SOURCES = {  # the sources a split kernel's traffic summary is tagged with
+    "split_mfma": [CSRC + "sdpa_mfma.hip", CSRC + "mfma_common.hpp", CSRC + "common.hpp"],
+    "split_vec": [CSRC + "sdpa_vec.hip", CSRC + "common.hpp"],
+    "split_bits_mfma": [CSRC + "bits_mfma.hip", CSRC + "mfma_common.hpp", CSRC + "common.hpp"],
+    "split_bits": [CSRC + "bits.hip", CSRC + "common.hpp"],
 }
 
 
@@ -41,23 +44,28 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_sha(variant):
+def source_sha(kernel):
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES[variant]:
+    for rel in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def traffic_from_profile(variant, workload_name):
+def traffic_path(kernel, workload_name, bits):
+    tag = "" if bits == 4 else f"-{bits}bit"
+    return os.path.join(PROFILE_DIR, f"traffic_{kernel}_{workload_name}{tag}.json")
+
+
+def traffic_from_profile(kernel, workload_name, bits=4):
     """HBM bytes per launch from committed rocprofv3 counter runs, or None
     when the kernel source changed since they were taken."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{'split_mfma' if variant == 2 else 'split_vec'}_{workload_name}.json")
+    path = traffic_path(kernel, workload_name, bits)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha") != source_sha(variant):
+    if rec.get("kernel_source_sha") != source_sha(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -77,12 +85,12 @@ def counter_per_dispatch(run_dir, counter):
     return out
 
 
-def traffic_summary(fetch_dir, write_dir, workload, calib_mib, commands):
+def traffic_summary(fetch_dir, write_dir, workload, calib_mib, commands, kernel="split_mfma", bits=4):
     """Calibrated HBM bytes per split launch from two rocprofv3 --pmc runs
     (FETCH_SIZE, then WRITE_SIZE, in KiB per dispatch) of
     `bench.py --no-graph --copy-calibration-mib N`: each counter is scaled by
     what it reads for the plain elementwise copy of N MiB (N MiB read and N
-    MiB written).  Writes profiles/traffic_<kernel>_<workload>.json."""
+    MiB written).  Writes profiles/traffic_<kernel>_<workload>[-<b>bit].json."""
     import numpy as np
     from int4_kv_cache_quant_amd import synth
     w = synth.WORKLOADS[workload]
@@ -91,7 +99,7 @@ def traffic_summary(fetch_dir, write_dir, workload, calib_mib, commands):
     for counter, run_dir, key in (("FETCH_SIZE", fetch_dir, "fetch"), ("WRITE_SIZE", write_dir, "write")):
         per = counter_per_dispatch(run_dir, counter)
         calib = sorted((v for n, v in per.values() if "elementwise" in n), reverse=True)[:5]
-        split = [v for n, v in per.values() if "split_mfma_kernel" in n]
+        split = [v for n, v in per.values() if kernel + "_kernel" in n]
         if len(calib) < 5 or not split:
             raise SystemExit(f"{run_dir}: no calibration copy or split dispatches for {counter}")
         factor = known_kib / float(np.mean(calib))
@@ -100,13 +108,14 @@ def traffic_summary(fetch_dir, write_dir, workload, calib_mib, commands):
         rec[f"{key}_factor"] = factor
         rec[f"{key}_bytes_per_launch"] = float(np.mean(split)) * factor * 1024.0
         rec[f"{key}_launches"] = len(split)
-    unit = w.Hkv * 2 * (w.D // 2 + 4 * (w.D // 32))
+    unit = w.Hkv * 2 * (w.D * bits // 8 + 4 * (w.D // 32))
     lens_sum = int(synth.lens(w, 0).astype(np.int64).sum())
     rec["algorithmic_bytes_per_launch"] = lens_sum * unit + w.B * w.Hq * w.D * 2
     rec["hbm_bytes_per_launch"] = rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
-    rec["kernel"] = "split_mfma"
-    rec["kernel_source_sha"] = source_sha(2)
-    path = os.path.join(PROFILE_DIR, f"traffic_split_mfma_{w.name}.json")
+    rec["kernel"] = kernel
+    rec["code_bits"] = bits
+    rec["kernel_source_sha"] = source_sha(kernel)
+    path = traffic_path(kernel, w.name, bits)
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
         f.write("\n")
@@ -153,10 +162,13 @@ def main():
                     help="write the calibrated HBM traffic of the split kernel from two rocprofv3 "
                          "--pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/, then exit")
     ap.add_argument("--pmc-commands", default="", help="the profiling commands, recorded with the summary")
+    ap.add_argument("--traffic-kernel", default="split_mfma", choices=sorted(KERNEL_SOURCES),
+                    help="the split kernel whose dispatches --traffic-summary reads")
     args = ap.parse_args()
     if args.traffic_summary:
         traffic_summary(args.traffic_summary[0], args.traffic_summary[1], args.workload,
-                        args.copy_calibration_mib or 1024, args.pmc_commands)
+                        args.copy_calibration_mib or 1024, args.pmc_commands, args.traffic_kernel,
+                        args.code_bits)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -510,7 +522,7 @@ def bench_workload(wnum, args, primary):
         ceiling["split_frac_of_ceiling"] = round(achieved / ceiling["GBps"], 4)
         ceiling["step_frac_of_ceiling"] = round(step_gbps / ceiling["GBps"], 4)
 
-    traffic = traffic_from_profile(plan.variant, w.name) if wbits == 4 else None
+    traffic = traffic_from_profile(kname, w.name, wbits)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None

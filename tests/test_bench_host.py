@@ -65,12 +65,32 @@ def test_traffic_summary_calibrates_by_the_copy(tmp_path, monkeypatch):
     assert rec["fetch_launches"] == 2 and rec["write_launches"] == 2
     # workload 3: 131072 tokens x 8 KV heads x (64 + 16) bytes for K and V, and q
     assert rec["algorithmic_bytes_per_launch"] == 131072 * 8 * 2 * (64 + 16) + 64 * 128 * 2
-    assert rec["kernel_source_sha"] == b.source_sha(2)
+    assert rec["kernel_source_sha"] == b.source_sha("split_mfma")
     # the bench reads it back only while the kernel source is unchanged
-    assert b.traffic_from_profile(2, synth.WORKLOADS[3].name) == pytest.approx(rec["hbm_bytes_per_launch"])
+    assert b.traffic_from_profile("split_mfma", synth.WORKLOADS[3].name) == pytest.approx(rec["hbm_bytes_per_launch"])
     rec["kernel_source_sha"] = "0" * 16
     json.dump(rec, open(tmp_path / f"traffic_split_mfma_{synth.WORKLOADS[3].name}.json", "w"))
-    assert b.traffic_from_profile(2, synth.WORKLOADS[3].name) is None
+    assert b.traffic_from_profile("split_mfma", synth.WORKLOADS[3].name) is None
+
+
+def test_traffic_summary_of_the_b_bit_split(tmp_path, monkeypatch):
+    """The same calibration for the 2-bit MFMA split: its own dispatches, its
+    algorithmic bytes (D/4 bytes of codes per token and head), its own file."""
+    b = _bench()
+    monkeypatch.setattr(b, "PROFILE_DIR", str(tmp_path))
+    copy = ("void at::native::elementwise_kernel<...>", [1024.0])
+    fetch_rows = [copy] * 5 + [("split_bits_mfma_kernel<128, 2>", [300.0]), ("split_mfma_kernel<128, 2, false, 4>", [1.0])]
+    write_rows = [copy] * 5 + [("split_bits_mfma_kernel<128, 2>", [4.0])]
+    _write_run(str(tmp_path / "fetch"), "FETCH_SIZE", fetch_rows)
+    _write_run(str(tmp_path / "write"), "WRITE_SIZE", write_rows)
+    b.traffic_summary(str(tmp_path / "fetch"), str(tmp_path / "write"), 3, 1, "cmds", "split_bits_mfma", 2)
+    from int4_kv_cache_quant_amd import synth
+    rec = json.load(open(tmp_path / f"traffic_split_bits_mfma_{synth.WORKLOADS[3].name}-2bit.json"))
+    assert rec["fetch_kib_per_launch_raw"] == pytest.approx(300.0) and rec["fetch_launches"] == 1
+    assert rec["algorithmic_bytes_per_launch"] == 131072 * 8 * 2 * (32 + 16) + 64 * 128 * 2
+    assert rec["kernel_source_sha"] == b.source_sha("split_bits_mfma")
+    assert b.traffic_from_profile("split_bits_mfma", synth.WORKLOADS[3].name, 2) == pytest.approx(
+        rec["hbm_bytes_per_launch"])
 
 
 def test_traffic_summary_needs_the_calibration_copy(tmp_path, monkeypatch):
@@ -90,6 +110,6 @@ def test_committed_traffic_reads_the_cache_once():
     from int4_kv_cache_quant_amd import synth
     path = os.path.join(ROOT, "profiles", f"traffic_split_mfma_{synth.WORKLOADS[3].name}.json")
     rec = json.load(open(path))
-    if rec["kernel_source_sha"] != b.source_sha(2):
+    if rec["kernel_source_sha"] != b.source_sha("split_mfma"):
         pytest.skip("the counter summary predates the current split kernel source")
     assert 1.0 <= rec["fetch_bytes_per_launch"] / rec["algorithmic_bytes_per_launch"] < 1.02

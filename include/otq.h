@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define OTQ_ABI_VERSION 7
+#define OTQ_ABI_VERSION 8
 
 /* Elements per quantisation group (one fp32 scale each), along head_dim. */
 #define OTQ_GROUP 32
@@ -128,15 +128,27 @@ typedef enum otq_rot_kind {
  *
  * 2- and 3-bit codes (code_bits = 2 or 3; AdapTQ page, core mechanisms: 2-,
  * 3- and 4-bit quantisation): s_g = max_i |x_i| / (2^(b-1) - 1) and c_i =
- * clamp(rint(x_i / s_g), -2^(b-1), 2^(b-1) - 1), otherwise as above; K and
- * V rows are plain little-endian bit streams, element i at bits [b i,
- * b i + b), two's complement: k_codes and v_codes uint8 [B][H][C][D*b/8],
- * scales as above.  Rotations and the per-channel scale apply as for int4.
- * Split passes: 2-bit caches whose K is neither rotated nor channel-scaled
+ * clamp(rint(x_i / s_g), -2^(b-1), 2^(b-1) - 1), otherwise as above; fields
+ * are the codes' two's complement b bits.
+ *  k_codes  uint8 [B][H][C][D*b/8]: plain little-endian bit-stream rows,
+ *           element i at bits [b i, b i + b) of the row.
+ *  v_codes  uint8 [B][H][C/32][32*D*b/8]: per tile of 32 tokens, read as
+ *           32-bit words (little-endian).  For tile-relative token u let
+ *           h = u / 16, r = (u % 16) / 4, m = u % 4; for channel c let
+ *           cb = c / 16, n = c % 16, l = 16 r + n.
+ *           b = 2: the field of (u, c) is at bit 16 h + 8 (cb % 2) + 2 m of
+ *                  word l (D/32) + cb / 2.
+ *           b = 3: with qd = cb / 4 and w = cb % 4, for w < 3 the field is at
+ *                  bit 16 h + 3 m of word l (3D/64) + 3 qd + w; for w = 3,
+ *                  bit i (0..2) of the field is at bit 16 h + 12 + p % 4 of
+ *                  word l (3D/64) + 3 qd + p / 4, p = 3 m + i.
+ *  scales as above.  Rotations and the per-channel scale apply as for int4.
+ * Split passes: b-bit caches whose K is neither rotated nor channel-scaled
  * take the MFMA variant (the default; any G <= 16), the others the vector
  * variant (any G <= 16; OTQ_EUNSUPPORTED if MFMA is forced).
  * otq_sdpa_int4_decode_append takes these caches too: its combine quantises
- * the new token with the b-bit rule and writes its rows whole.
+ * the new token with the b-bit rule, writes its K row whole and sets its V
+ * fields in their tile.
  */
 typedef struct otq_cache {
     int32_t batch;

@@ -302,13 +302,10 @@ class Int4KVCache:
         self.k_scales = torch.zeros(sb // 4, dtype=torch.float32, device=device).view(
             batch, num_kv_heads, capacity, sb // 4 // rows)
         self.v_scales = torch.zeros_like(self.k_scales)
-        if code_bits == 4:  # V in tiles of 32 tokens
-            self.k_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(batch, num_kv_heads, capacity, -1)
-            self.v_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(
-                batch, num_kv_heads, capacity // OTQ_TILE, -1)
-        else:  # plain bit-stream rows for K and V
-            self.k_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(batch, num_kv_heads, capacity, -1)
-            self.v_codes = torch.zeros_like(self.k_codes)
+        # K in rows of one token; V in tiles of 32 tokens (int4 and b-bit alike)
+        self.k_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(batch, num_kv_heads, capacity, -1)
+        self.v_codes = torch.zeros(cb, dtype=torch.uint8, device=device).view(
+            batch, num_kv_heads, capacity // OTQ_TILE, -1)
         self.rot_signs = None if rot_signs is None else rot_signs.to(device=device, dtype=torch.float32).contiguous()
         self.rot_kind = ROT_KINDS[rot_kind]
         n = head_dim // 2 if self.rot_kind == OTQ_ROT_SRFT else head_dim

@@ -1,18 +1,20 @@
-// bits.hip - 2- and 3-bit codes: quantise-append and the split pass over
-// caches whose rows are plain little-endian bit streams.
+// bits.hip - 2- and 3-bit codes: quantise-append and the vector split pass.
 //
 // The code widths the AdapTQ page lists beside 4-bit (its section on the
 // core mechanisms: 2-, 3- and 4-bit quantisation): b-bit codes take the
 // int4 steps with the symmetric range of b bits, s = abs-max / (2^(b-1) - 1)
 // in IEEE fp32 and c = clamp(rint(x / s), -2^(b-1), 2^(b-1) - 1), s == 0
-// giving zero codes; element i of a row occupies bits [b i, b i + b) of the
-// row's little-endian bit stream, two's complement.  K and V rows have the
-// same layout, [B][H][capacity][D b / 8] bytes, scales as for int4.
+// giving zero codes, two's complement.  A K row is a plain little-endian bit
+// stream (element i at bits [b i, b i + b)), [B][H][capacity][D b / 8]
+// bytes; V codes are regrouped per tile of 32 tokens (bits_layout.hpp), the
+// same bytes per tile; scales as for int4.
 //
-// A first path, for correctness: the split kernel computes scores and the
-// value sum with fp32 vector arithmetic, one token per thread for the
-// scores and one channel per thread for the value sum, and writes the same
-// (m, l, o) partials as the int4 kernels, so the same combine merges them.
+// The vector split pass (for caches whose K is rotated or channel-scaled,
+// and 3-bit codes at head_dim 256) computes scores and the value sum with
+// fp32 vector arithmetic, one token per thread for the scores and one
+// channel per thread for the value sum, and writes the same (m, l, o)
+// partials as the int4 kernels, so the same combine merges them.
+#include "bits_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_lane.hpp"
@@ -23,7 +25,6 @@ namespace otq {
 namespace {
 
 constexpr float kNegInfB = -__builtin_huge_valf();
-constexpr int kVecsPerWave = 8;  // vectors one wave of a bulk append quantises (one for short appends)
 
 // Signed b-bit code of element i of a row held as 32-bit words (the bits
 // may straddle two words).
@@ -37,88 +38,118 @@ __device__ __forceinline__ int code_in_words(const uint32_t* w, int i)
     return (int)(u << (32 - BITS)) >> (32 - BITS);
 }
 
-// One wave per new vector (K tokens, then V tokens), E = D / 64 elements per
-// lane; the codes pass through LDS so that D b / 32 lanes assemble the row's
-// 32-bit words.
+// One block per (32-token tile touched by the append, KV head, sequence):
+// its waves quantise the tile's new K and V vectors in turn (one wave per
+// vector, E = D / 64 elements per lane).  A K row is written whole from the
+// wave's codes (D b / 32 lanes assemble its 32-bit words); the V codes of
+// the tile are staged in LDS and the tile's V words are written whole, merged
+// with the old words under a mask where only part of the tile is new (only
+// this block writes the tile in this launch).
 template <int D, int BITS>
 __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
-    const int32_t* __restrict__ pos, int vpw, const float* __restrict__ signs, float rot_norm, int rot_kind,
+    const int32_t* __restrict__ pos, const float* __restrict__ signs, float rot_norm, int rot_kind,
     const float* __restrict__ lam, const float* __restrict__ vsigns, unsigned* __restrict__ err)
 {
 #pragma clang fp contract(off)
     constexpr int E = D / 64, NG = D / kGroup, RB = D * BITS / 8, NWORD = RB / 4;
     constexpr float qmax = (float)((1 << (BITS - 1)) - 1), qmin = -(float)(1 << (BITS - 1));
+    using VT = VBitsTile<D, BITS>;
     static_assert(RB % 4 == 0, "whole words per row");
-    __shared__ int8_t cs[4][D];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ int8_t cs[4][D];       // a wave's K codes
+    __shared__ int8_t cvt[kTile][D];  // the tile's V codes
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
-    if (threadIdx.x == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
+    if (tid == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
         report_error(err, kErrPos);  // the tokens outside [0, cap) are skipped below
+    // the block's tile: the appended range clipped to [0, cap), tiles counted
+    // from the one holding its first token
+    const long long lo_all = max((long long)p0, 0LL), hi_all = min((long long)p0 + n_new, (long long)cap);
+    if (lo_all >= hi_all) return;  // block-uniform: nothing inside the cache
+    const int tile = (int)(lo_all / kTile) + blockIdx.x;
+    const int lo = (int)max(lo_all, (long long)kTile * tile), hi = (int)min(hi_all, (long long)kTile * tile + kTile);
+    if (lo >= hi) return;  // block-uniform: past the range
+    const int nt = hi - lo, u0 = lo - kTile * tile;
     SrftLaneTw<D, E> stw;  // the FFT rotation's twiddles of this lane
     if ((signs || vsigns) && rot_kind) stw.load(lane);
-    // each wave takes vpw vectors in turn (the block's barrier count is the
-    // same for all its threads)
-    for (int iv = 0; iv < vpw; ++iv) {
-    const int vec = (blockIdx.x * 4 + wave) * vpw + iv;
-    const bool is_v = vec >= n_new;
-    const int tok = is_v ? vec - n_new : vec;
-    const int t = p0 + tok;
-    // every thread reaches the barrier; inactive waves do no memory access
-    const bool active = vec < 2 * n_new && t >= 0 && t < cap;
     const size_t head = (size_t)b * H + h;
-    float sc = 0.0f;
-    if (active) {
-        const uint16_t* src = (is_v ? v : k) + (head * n_new + tok) * D + lane * E;
-        float x[E];
-        float a = 0.0f;
+    // 2 nt vectors (the K tokens, then the V tokens), four at a time (the
+    // block's barrier count is the same for all its threads)
+    const int iters = (2 * nt + 3) / 4;
+    for (int it = 0; it < iters; ++it) {
+        const int vec = 4 * it + wave;
+        const bool active = vec < 2 * nt;
+        const bool is_v = vec >= nt;
+        const int tr = is_v ? vec - nt : vec;  // token lo + tr
+        const int t = lo + tr;
+        float sc = 0.0f;
+        if (active) {
+            const uint16_t* src = (is_v ? v : k) + (head * n_new + (t - p0)) * D + lane * E;
+            float x[E];
+            float a = 0.0f;
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[e] = widen(src[e], dtype);
-        // the same rotation and channel scale as the int4 appends (K: signs,
-        // then lambda; V: its own signs)
-        const float* sg = is_v ? vsigns : signs;
-        if (sg) {
-            if (rot_kind) {
+            for (int e = 0; e < E; ++e) x[e] = widen(src[e], dtype);
+            // the same rotation and channel scale as the int4 appends (K: signs,
+            // then lambda; V: its own signs)
+            const float* sg = is_v ? vsigns : signs;
+            if (sg) {
+                if (rot_kind) {
 #pragma unroll
-                for (int e = 0; e < E; ++e) x[e] = x[e] * sg[lane * E + e];
-                srft_signed<D, E>(x, rot_norm, lane, stw);
-            } else {
-                rotate_lane<D>(x, sg, rot_norm, lane);
+                    for (int e = 0; e < E; ++e) x[e] = x[e] * sg[lane * E + e];
+                    srft_signed<D, E>(x, rot_norm, lane, stw);
+                } else {
+                    rotate_lane<D>(x, sg, rot_norm, lane);
+                }
+            }
+            if (!is_v && lam) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) x[e] = x[e] * lam[lane * E + e];
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
+            a = group_max<kGroup / E>(a);  // exact in any order
+            sc = a / qmax;                 // correctly rounded IEEE division
+            int8_t* dst = is_v ? &cvt[u0 + tr][0] : &cs[wave][0];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                float r = rintf(x[e] / sc);  // IEEE division, then half to even
+                r = fminf(fmaxf(r, qmin), qmax);
+                dst[lane * E + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
             }
         }
-        if (!is_v && lam) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) x[e] = x[e] * lam[lane * E + e];
-        }
-#pragma unroll
-        for (int e = 0; e < E; ++e) a = fmaxf(a, fabsf(x[e]));
-        a = group_max<kGroup / E>(a);  // exact in any order
-        sc = a / qmax;                 // correctly rounded IEEE division
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            float r = rintf(x[e] / sc);  // IEEE division, then half to even
-            r = fminf(fmaxf(r, qmin), qmax);
-            cs[wave][lane * E + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
-        }
-    }
-    __syncthreads();
-    if (active) {
-        const size_t row = head * cap + t;
-        if (lane % (kGroup / E) == 0) (is_v ? vs : ks)[row * NG + (lane * E) / kGroup] = sc;
-        if (lane < NWORD) {  // word w holds bits [32 w, 32 w + 32) of the row
-            uint32_t word = 0;
-            const int i0 = (32 * lane) / BITS, i1 = min((32 * lane + 31) / BITS, D - 1);
-            for (int i = i0; i <= i1; ++i) {
-                const uint32_t u = (uint32_t)cs[wave][i] & ((1u << BITS) - 1u);
-                const int off = i * BITS - 32 * lane;  // may be negative for the first element
-                word |= off >= 0 ? u << off : u >> -off;
+        __syncthreads();
+        if (active) {
+            const size_t row = head * cap + t;
+            if (lane % (kGroup / E) == 0) (is_v ? vs : ks)[row * NG + (lane * E) / kGroup] = sc;
+            if (!is_v && lane < NWORD) {  // word w holds bits [32 w, 32 w + 32) of the K row
+                uint32_t word = 0;
+                const int i0 = (32 * lane) / BITS, i1 = min((32 * lane + 31) / BITS, D - 1);
+                for (int i = i0; i <= i1; ++i) {
+                    const uint32_t u = (uint32_t)cs[wave][i] & ((1u << BITS) - 1u);
+                    const int off = i * BITS - 32 * lane;  // may be negative for the first element
+                    word |= off >= 0 ? u << off : u >> -off;
+                }
+                reinterpret_cast<uint32_t*>(kc + row * RB)[lane] = word;
             }
-            reinterpret_cast<uint32_t*>((is_v ? vc : kc) + row * RB)[lane] = word;
         }
+        __syncthreads();  // cs is rewritten by the next vectors
     }
-    __syncthreads();  // cs is rewritten by the next vector
+    // the tile's V words: the new tokens' fields from the staged codes
+    uint32_t* vt = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + tile) * (size_t)(kTile * RB));
+    for (int W = tid; W < VT::WORDS; W += 256) {
+        uint32_t val = 0, mask = 0;
+        vtile_fields<D, BITS>(W, [&](int u, int c, int bpos, int width, int shift) {
+            if (u >= u0 && u < u0 + nt) {
+                const uint32_t fm = (1u << width) - 1u;
+                val |= (((uint32_t)(int)cvt[u][c] >> shift) & fm) << bpos;
+                mask |= fm << bpos;
+            }
+        });
+        if (mask == 0) continue;
+        if (mask != 0xFFFFFFFFu) val |= vt[W] & ~mask;
+        vt[W] = val;
     }
 }
 
@@ -265,10 +296,12 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
                     }
                 }
             }
-            // the tile's V rows and scales into LDS (coalesced)
+            // the step's V tiles (whole: the fields of a token spread over
+            // its tile) and scales into LDS (coalesced); t0 is tile-aligned
             {
                 const uint32_t* vsrc = reinterpret_cast<const uint32_t*>(vrows + (size_t)t0 * RB);
-                for (int k = tid; k < n * RW; k += TT) v_lds[k] = vsrc[k];
+                const int nw = (n + kTile - 1) / kTile * kTile * RW;
+                for (int k = tid; k < nw; k += TT) v_lds[k] = vsrc[k];
                 for (int k = tid; k < n * NG; k += TT) vs_lds[k] = vscl[(size_t)t0 * NG + k];
             }
 #pragma unroll
@@ -309,7 +342,8 @@ __global__ __launch_bounds__(256) void split_bits_kernel(SplitArgs a)
             const int gr = vc_ / kGroup;
 #pragma unroll 4
             for (int j = vts; j < n; j += TS) {
-                const float vd = (float)code_in_words<BITS>(&v_lds[j * RW], vc_) * vs_lds[j * NG + gr];
+                const float vd = (float)vtile_code<D, BITS>(&v_lds[(j / kTile) * (kTile * RW)], j % kTile, vc_) *
+                                 vs_lds[j * NG + gr];
 #pragma unroll
                 for (int g = 0; g < GM; ++g)
                     if (g < G) o[g] += p_lds[g][j] * vd;
@@ -341,11 +375,11 @@ hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, i
                     uint8_t* kc, float* ks, uint8_t* vc, float* vs, const int32_t* pos, const BitsRot& r,
                     unsigned* err, hipStream_t s)
 {
-    const int vpw = n_new >= 64 ? kVecsPerWave : 1;
-    dim3 grid((2 * n_new + 4 * vpw - 1) / (4 * vpw), H, B), block(256);
+    // an unaligned range of n_new tokens touches at most n_new / 32 + 2 tiles
+    dim3 grid(n_new / kTile + 2, H, B), block(256);
     quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
                                                           static_cast<const uint16_t*>(v), dtype, n_new,
-                                                          H, cap, kc, ks, vc, vs, pos, vpw, r.signs,
+                                                          H, cap, kc, ks, vc, vs, pos, r.signs,
                                                           r.rot_norm, r.rot_kind, r.lam, r.vsigns, err);
     return hipGetLastError();
 }

@@ -5,10 +5,11 @@
 // lists 2-, 3- and 4-bit quantisation behind one pipeline) go through the same kind of
 // products as the int4 cache: G query heads sharing a KV head make scoring a
 // tile and weighting its values two genuine matrix products, run here as
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  The cache keeps the plain
-// b-bit rows (element i of a row at bits [b i, b i + b) of its little-endian
-// bit stream, K and V alike, fp32 group scales), so the append kernels and
-// the vector split pass share it.
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  K rows are plain b-bit
+// rows (element i at bits [b i, b i + b) of the row's little-endian bit
+// stream); V codes are regrouped per 32-token tile (bits_layout.hpp) so that
+// each lane's value operands come from its own words of the tile; fp32 group
+// scales.
 //
 // Exactness, as in the int4 split pass:
 //  * K codes enter as fp16 subnormals n 2^(e_k - 24) of their offset-binary
@@ -20,10 +21,12 @@
 //    and, after a shift, 0 at 3); 2^e_k is cancelled by q's operand, the
 //    offset by starting each group's accumulator at -2^(b-1) 2^-24 sum(q),
 //    2^24 is folded into the softmax scale;
-//  * V codes enter as signed normal fp16 integers: each code is extracted
-//    from its token's row (a bit-field extract at 2 bits, a funnel shift at
-//    3), the two codes of a slot pair go into the mantissas of 1024.0, and
-//    one packed subtraction of 1024 + 2^(b-1) leaves c exactly, so the value
+//  * V codes enter as signed normal fp16 integers: the two codes of a k-slot
+//    pair sit at the same offset e_m of the two halves of one tile word
+//    (2 m at 2 bits; 3 m, and 0 after a shift, at 3), so one and-xor mask
+//    puts 1024 + (c + 2^(b-1)) 2^e_m in each half (0x6400 is the exponent of
+//    1024, the flipped top bit of the field the offset) and one packed
+//    subtraction leaves c 2^e_m exactly; 2^-e_m goes onto p.  The value
 //    products are exact and their sums plain fp32;
 //  * q rows are scaled by a power of two that puts the largest |element| in
 //    [2^14, 2^15) before the fp16 conversion (bf16 and fp16 inputs convert
@@ -31,14 +34,13 @@
 //  * x = p * s_v * 2^E is split into fp16 hi + lo operands; E follows the
 //    largest V scale seen, as in the int4 pass.
 // A b-bit cache with a rotated or channel-scaled K takes the vector split
-// pass (its q is not exact in fp16), as do 3-bit codes at head_dim 256; a
-// rotated V is undone by the combine.
+// pass (its q is not exact in fp16); a rotated V is undone by the combine.
 //
 // Block = 4 waves, one (split, KV head, sequence); wave w takes the tiles w,
-// w + 4, ... of the split (32 tokens each).  Each tile (K rows, V rows, K and
-// V scales: (8 b + 8) D bytes) is loaded into registers two tiles ahead, written to
-// the wave's LDS stage when its turn comes, and read back in the operand
-// layouts below ((8 b + 8) D bytes per tile).  Lane l = 16 r + n:
+// w + 4, ... of the split (32 tokens each).  Each tile (K rows, the V tile,
+// K and V scales: (8 b + 8) D bytes) is loaded into registers two tiles
+// ahead (one at head_dim 256), written to the wave's LDS stage when its turn
+// comes, and read back in the operand layouts below.  Lane l = 16 r + n:
 //  scores  A = K codes (row = token 16 s + n, k = channels 32 g + 8 r + the
 //          slot order), B = q of query head n (columns >= G are zero);
 //          C = S[token 16 s + 4 r + i][head n]
@@ -46,6 +48,7 @@
 //          16 + 4 r + m: the tokens whose scores this lane holds), B = V codes
 //          (column = channel 16 cb + n, the same tokens), C = O[head 4 r + i]
 //          [channel 16 cb + n].
+#include "bits_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mfma_common.hpp"
@@ -69,7 +72,7 @@ constexpr bool kB2QinitInAcc = D != 256;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// One tile of a KV head in a wave's LDS stage: K rows, V rows (32 x RB bytes
+// One tile of a KV head in a wave's LDS stage: K rows, the V tile (32 x RB bytes
 // each, as in the cache), then the K and V scales (32 x NG fp32 each).
 template <int D, int BITS>
 struct BTile {
@@ -135,26 +138,45 @@ __device__ __forceinline__ half8_t unpack_k3(uint32_t f)
     return out;
 }
 
-// V: the b-bit codes (raw two's complement fields, at bit 0) of tokens
-// (a[m], b[m]) -> k slots (2m, 2m + 1) as exact fp16 integers c: 1024 +
-// (c + 2^(b-1)) in each half (the flip of the field's top bit is the
-// offset), less 1024 + 2^(b-1).
-template <int BITS>
-__device__ __forceinline__ half8_t unpack_v(const uint32_t (&fa)[4], const uint32_t (&fb)[4])
+// V, 2 bits: one word of the lane (fields at bit 2 m of each half: tokens
+// 4 r + m below, 16 + 4 r + m above) -> k slots (2 m, 2 m + 1) as exact fp16
+// values c 4^m: 1024 + (c + 2) 4^m in each half (the flip of the field's top
+// bit is the offset, 0x6400 the exponent of 1024), less 1024 + 2 4^m.
+__device__ __forceinline__ half8_t unpack_v2(uint32_t w)
 {
-    constexpr uint32_t half_magic = 0x6400u | (1u << (BITS - 1));
-    constexpr float off = 1024.0f + (float)(1 << (BITS - 1));
-    const half2_t bias = half2_t{(_Float16)off, (_Float16)off};
     half8_t out;
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
-        const uint32_t u = (fa[m] | (fb[m] << 16)) ^ (half_magic | (half_magic << 16));
-        const half2_t p = __builtin_bit_cast(half2_t, u) - bias;
-        out[2 * m] = p[0];
-        out[2 * m + 1] = p[1];
+        const uint32_t u = (w & (0x00030003u << (2 * m))) ^ (0x64006400u | (0x00020002u << (2 * m)));
+        const _Float16 off = (_Float16)(1024.0f + 2.0f * (float)(1 << (2 * m)));
+        const half2_t h = __builtin_bit_cast(half2_t, u) - half2_t{off, off};
+        out[2 * m] = h[0];
+        out[2 * m + 1] = h[1];
     }
     return out;
 }
+
+// V, 3 bits: 12 bits per half (fields at bit 3 m) -> k slots (2 m, 2 m + 1)
+// as exact fp16 values c 2^kVExp<3>[m]; the slot-3 fields are shifted down
+// first, as they would reach into the fp16 exponent.
+__device__ __forceinline__ half8_t unpack_v3(uint32_t x)
+{
+    half8_t out;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        const uint32_t u = m < 3 ? (x & (0x00070007u << (3 * m))) ^ (0x64006400u | (0x00040004u << (3 * m)))
+                                 : ((x >> 9) & 0x00070007u) ^ 0x64046404u;
+        const _Float16 off = (_Float16)(1024.0f + 4.0f * (float)(1 << (m < 3 ? 3 * m : 0)));
+        const half2_t h = __builtin_bit_cast(half2_t, u) - half2_t{off, off};
+        out[2 * m] = h[0];
+        out[2 * m + 1] = h[1];
+    }
+    return out;
+}
+
+// The power of two (log2) that slot pair m of an unpacked V word carries.
+template <int BITS>
+constexpr int kVExp[4] = {0, BITS == 2 ? 2 : 3, BITS == 2 ? 4 : 6, BITS == 2 ? 6 : 0};
 
 template <int D, int BITS>
 __global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2)))
@@ -162,6 +184,7 @@ void split_bits_mfma_kernel(SplitArgs a)
 {
     static_assert(BITS == 2 || BITS == 3, "2- or 3-bit codes");
     using T = BTile<D, BITS>;
+    using VT = VBitsTile<D, BITS>;
     constexpr int NG = T::NG, NCB = D / 16, RB = T::RB, W = kB2Waves;
     extern __shared__ __align__(16) char lds[];  // W stages of T::STAGE bytes
 
@@ -433,73 +456,61 @@ void split_bits_mfma_kernel(SplitArgs a)
                 l_lane += p[s][i];
             }
 
-        // ---- values: the row words of the lane's 8 tokens, NCB / 4 channel
-        //      blocks (64 channels: 4 words at 2 bits, 6 at 3) at a time
-        constexpr int QW = 2 * BITS;  // row words per 4 channel blocks
+        // ---- values: the lane's words of the V tile (channel column n16 of
+        //      every block, tokens 4 r + m and 16 + 4 r + m in the two halves)
+        uint32_t vw[VT::WPL];
+        {
+            const char* src = stage + T::VOFF + lane * 4 * VT::WPL;
+            if constexpr (VT::WPL % 4 == 0) {
 #pragma unroll
-        for (int q = 0; q < NCB / 4; ++q) {
-            uint32_t wv[2][4][QW];  // [s][m][word of the block set]
+                for (int k = 0; k < VT::WPL; k += 4) {
+                    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + 4 * k);
+                    vw[k] = w.x; vw[k + 1] = w.y; vw[k + 2] = w.z; vw[k + 3] = w.w;
+                }
+            } else if constexpr (VT::WPL % 2 == 0) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                for (int k = 0; k < VT::WPL; k += 2) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(src + 4 * k);
+                    vw[k] = w.x; vw[k + 1] = w.y;
+                }
+            } else {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) {
-                    const char* src = stage + T::VOFF + (16 * s + 4 * r + m) * RB + 4 * QW * q;
-                    if constexpr (BITS == 2) {
-                        const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src);
-                        wv[s][m][0] = w.x; wv[s][m][1] = w.y; wv[s][m][2] = w.z; wv[s][m][3] = w.w;
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 3; ++j) {  // 8-byte aligned: rows are 48 D / 128 words apart
-                            const uint2 w = *reinterpret_cast<const uint2*>(src + 8 * j);
-                            wv[s][m][2 * j] = w.x; wv[s][m][2 * j + 1] = w.y;
-                        }
+                for (int k = 0; k < VT::WPL; ++k) vw[k] = reinterpret_cast<const uint32_t*>(src)[k];
+            }
+        }
+        static_for<NG>([&](auto gI) {
+            constexpr int g = decltype(gI)::value;  // scale group: channel blocks 2 g, 2 g + 1
+            v4u_t ha, la;
+            static_for<4>([&](auto mI) {
+#pragma clang fp contract(off)
+                constexpr int m = decltype(mI)::value;
+                // the code of slot pair m carries 2^kVExp<BITS>[m]: taken off p
+                const int ex = e_v - kVExp<BITS>[m];
+                // a token past the end has scale 0 (not 0 times whatever the cache holds)
+                const float x0 = p[0][m] * __builtin_ldexpf(vscale(0, m, g), ex);
+                const float x1 = p[1][m] * __builtin_ldexpf(vscale(1, m, g), ex);
+                ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
+                la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
+            });
+            const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
+            static_for<2>([&](auto hI) {
+                constexpr int cb = 2 * g + decltype(hI)::value;
+                half8_t B;
+                if constexpr (BITS == 2) {
+                    B = unpack_v2((cb & 1) ? (vw[cb >> 1] >> 8) : vw[cb >> 1]);
+                } else {
+                    constexpr int qd = cb >> 2, t = cb & 3;
+                    if constexpr (t < 3) {
+                        B = unpack_v3(vw[3 * qd + t]);
+                    } else {  // the block held in the top nibbles of the quad's words
+                        B = unpack_v3(((vw[3 * qd] >> 12) & 0x000F000Fu) | ((vw[3 * qd + 1] >> 8) & 0x00F000F0u) |
+                                      ((vw[3 * qd + 2] >> 4) & 0x0F000F00u));
                     }
                 }
-            // the lane's field (channel 16 cb + n16) in the block set's words
-            // (CBQ a compile-time block index, so that every word index is one)
-            auto field = [&](int s, int m, auto cbqI) -> uint32_t {
-                constexpr int CBQ = decltype(cbqI)::value;
-                if constexpr (BITS == 2) {
-                    return __builtin_amdgcn_ubfe(wv[s][m][CBQ], 2 * n16, 2);
-                } else {
-                    // bits [48 CBQ + 3 n16, + 3) of the 192: inside the word
-                    // pair starting at word (48 CBQ) / 32, at bit sh < 62 of
-                    // the pair (32-bit operations only, so that the words
-                    // stay in registers)
-                    constexpr int P0 = (3 * CBQ) >> 1, O0 = (48 * CBQ) & 31;
-                    const uint32_t lo = wv[s][m][P0], hi = wv[s][m][P0 + 1];
-                    const int sh = O0 + 3 * n16;
-                    const uint32_t x = sh < 32 ? __builtin_amdgcn_alignbit(hi, lo, sh) : hi >> (sh - 32);
-                    return x & 7u;
-                }
-            };
-            static_for<2>([&](auto gI) {
-                constexpr int gq = decltype(gI)::value;
-                const int g = 2 * q + gq;  // scale group of channel blocks 2 g, 2 g + 1
-                v4u_t ha, la;
-                static_for<4>([&](auto mI) {
-#pragma clang fp contract(off)
-                    constexpr int m = decltype(mI)::value;
-                    // a token past the end has scale 0 (not 0 times whatever the cache holds)
-                    const float x0 = p[0][m] * __builtin_ldexpf(vscale(0, m, g), e_v);
-                    const float x1 = p[1][m] * __builtin_ldexpf(vscale(1, m, g), e_v);
-                    ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
-                    la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
-                });
-                const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
-                static_for<2>([&](auto hI) {
-                    constexpr int h = decltype(hI)::value;
-                    constexpr int cbq = 2 * gq + h;  // block 4 q + cbq = 2 g + h
-                    const std::integral_constant<int, cbq> cI;
-                    const uint32_t fa[4] = {field(0, 0, cI), field(0, 1, cI), field(0, 2, cI), field(0, 3, cI)};
-                    const uint32_t fb[4] = {field(1, 0, cI), field(1, 1, cI), field(1, 2, cI), field(1, 3, cI)};
-                    const half8_t B = unpack_v<BITS>(fa, fb);
-                    const int cb = 4 * q + cbq;
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
-                    acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
-                });
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
             });
-        }
+        });
     }
 
     // ---- merge of the W waves (each writes its share into its own stage,
@@ -553,8 +564,7 @@ void split_bits_mfma_kernel(SplitArgs a)
 
 bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
 {
-    // (3-bit codes at head_dim 256 would spill: the vector pass serves them)
-    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (bits == 2 || (bits == 3 && D <= 128)) &&
+    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (bits == 2 || bits == 3) &&
            !rotated_or_scaled_k;
 }
 
@@ -584,6 +594,7 @@ hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stre
     case 1282: return launch_b<128, 2>(a, stream);
     case 1283: return launch_b<128, 3>(a, stream);
     case 2562: return launch_b<256, 2>(a, stream);
+    case 2563: return launch_b<256, 3>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

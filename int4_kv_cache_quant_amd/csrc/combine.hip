@@ -16,6 +16,7 @@
 // zingnex page, section on on-the-fly quantisation), writes it into the
 // cache, and merges it as one more term (m = its score, l = 1, o = its
 // dequantised V).
+#include "bits_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
 #include "quant_lane.hpp"
@@ -65,6 +66,30 @@ __device__ __forceinline__ float fwht_thread(float y, float* xch)
         y = (t & h) ? (o - y) : (y + o);
     }
     return y;
+}
+
+// The V fields of token pos (codes[c], c < D) in its b-bit tile: word x of
+// the VBitsTile<D, BITS>::TOKEN_WORDS words that hold them (x past them:
+// nothing).  The other fields of the word are other tokens', so this token's
+// bits are cleared and set with two atomics (no read to wait for; one
+// thread's two operations on a word take effect in order).
+template <int D, int BITS>
+__device__ __forceinline__ void put_v_bits(uint8_t* vc, size_t head, int cap, int pos, int x, const int8_t* codes)
+{
+    if (x >= VBitsTile<D, BITS>::TOKEN_WORDS) return;
+    const int u = pos % kTile;
+    const int W = vtile_token_word<D, BITS>(u, x);
+    uint32_t val = 0, mask = 0;
+    vtile_fields<D, BITS>(W, [&](int fu, int c, int bpos, int width, int shift) {
+        if (fu == u) {
+            const uint32_t fm = (1u << width) - 1u;
+            val |= (((uint32_t)(int)codes[c] >> shift) & fm) << bpos;
+            mask |= fm << bpos;
+        }
+    });
+    unsigned* w = reinterpret_cast<unsigned*>(vc + (head * (cap / kTile) + pos / kTile) * (size_t)(kTile * D * BITS / 8)) + W;
+    __hip_atomic_fetch_and(w, ~mask, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_or(w, val, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Block (row, c0): row = b * Hq + h, channels [CH c0, CH c0 + CH), CH = 32
@@ -211,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         int ck[1];
         // one channel per lane: the lane layout of a 64-channel vector, whose
         // 32-lane groups are this vector's 32-channel groups
-        const int bits = a.bits;  // block-uniform: 4, or 2 / 3 (plain bit-stream rows)
+        const int bits = a.bits;  // block-uniform: 4, or 2 / 3
         const float sk = bits == 4 ? quantize_lane<64>(xk, ck, lane) : quantize_lane_bits(xk[0], ck[0], bits);
         float xv[1] = {widen(vx, a.dtype)};
         if (VROT) {  // V rotated as K is, with its own signs
@@ -221,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         }
         int cv[1];
         const float sv = bits == 4 ? quantize_lane<64>(xv, cv, lane) : quantize_lane_bits(xv[0], cv[0], bits);
-        if (bits != 4) {  // block-uniform: b-bit rows, written whole from the staged codes
+        if (bits != 4) {  // block-uniform: b-bit codes, staged in LDS, then packed
             const size_t head = (size_t)b * a.H + kvh, krow = head * a.cap + pos;
             if (writer) {
                 bcodes[0][ch] = (int8_t)ck[0];
@@ -232,18 +257,19 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
                 }
             }
             __syncthreads();
-            const int nword = DA * bits / 32;  // words per row
-            if (writer && tid < 2 * nword) {   // thread t: word t % nword of the K (t < nword) or V row
-                const int which = tid / nword, wi = tid % nword;
+            const int nword = DA * bits / 32;  // words per K row
+            if (writer && tid < nword) {       // the K row, written whole
                 uint32_t word = 0;
-                const int i0 = (32 * wi) / bits, i1 = min((32 * wi + 31) / bits, DA - 1);
+                const int i0 = (32 * tid) / bits, i1 = min((32 * tid + 31) / bits, DA - 1);
                 for (int i = i0; i <= i1; ++i) {
-                    const uint32_t u = (uint32_t)bcodes[which][i] & ((1u << bits) - 1u);
-                    const int off = i * bits - 32 * wi;  // negative for a code that starts in the word before
+                    const uint32_t u = (uint32_t)bcodes[0][i] & ((1u << bits) - 1u);
+                    const int off = i * bits - 32 * tid;  // negative for a code that starts in the word before
                     word |= off >= 0 ? u << off : u >> -off;
                 }
-                uint8_t* rows = which == 0 ? a.kc : a.vc;
-                reinterpret_cast<uint32_t*>(rows + krow * (size_t)(DA * bits / 8))[wi] = word;
+                reinterpret_cast<uint32_t*>(a.kc + krow * (size_t)(DA * bits / 8))[tid] = word;
+            } else if (writer) {  // this token's V fields, word by word of its tile
+                if (bits == 2) put_v_bits<DA, 2>(a.vc, head, a.cap, pos, tid - nword, bcodes[1]);
+                else put_v_bits<DA, 3>(a.vc, head, a.cap, pos, tid - nword, bcodes[1]);
             }
         } else if (writer) {
             const size_t head = (size_t)b * a.H + kvh, krow = head * a.cap + pos;

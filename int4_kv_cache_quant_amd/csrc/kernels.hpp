@@ -53,7 +53,7 @@ struct SplitArgs {
     unsigned* err;  // the device error word
 };
 
-// 2- and 3-bit codes (plain bit-stream rows for K and V): the append and the
+// 2- and 3-bit codes (plain bit-stream K rows, V in 32-token tiles): the append and the
 // split pass; the combine is shared.
 // The options of a b-bit append: K's rotation signs and kind, its channel
 // scale, V's rotation signs (each null when off).
@@ -125,7 +125,7 @@ struct CombineArgs {
                             // output is brought back to the original basis
     float qscale;           // softmax scale * log2(e)
     unsigned* err;          // the device error word
-    int bits;               // code width of the appended token: 4, or 2 / 3 (plain rows)
+    int bits;               // code width of the appended token: 4, or 2 / 3
 };
 hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream);
 

@@ -80,3 +80,63 @@ def k_rows_to_plain(rows, D):
 def k_plain_to_rows(plain, D):
     """[..., T, D/2] plain layout -> [..., T, D/2] K row layout."""
     return np.asarray(plain, np.uint8)[..., _k_row_map(D)]
+
+
+# ---------------------------------------------------------------- b-bit V tiles
+# Plain b-bit rows: element c of a token's row at bits [b c, b c + b) of the
+# row's little-endian bit stream.  V tile layout of 2- and 3-bit caches
+# (include/otq.h): per tile of 32 tokens, 32 D b / 8 bytes; tile-relative
+# token u has h = u // 16, r = (u % 16) // 4, m = u % 4; channel c has
+# cb = c // 16, n = c % 16; lane l = 16 r + n.
+#   2 bits: word l (D/32) + cb // 2, field at bit 16 h + 8 (cb % 2) + 2 m.
+#   3 bits: words l (3D/64) + 3 (cb // 4) + w; for w = cb % 4 < 3 the field at
+#           bit 16 h + 3 m of word w; for cb % 4 = 3, bit i of the field is
+#           chunk bit p = 3 m + i, at bit 16 h + 12 + p % 4 of word p // 4.
+# Tile bit index = 32 word + bit (little-endian bytes).
+
+@functools.lru_cache(maxsize=None)
+def _vbits_map(D, bits):
+    """src[t]: the plain bit (u * D * bits + c * bits + i) that tile bit t holds."""
+    u = np.arange(32)[:, None, None]
+    c = np.arange(D)[None, :, None]
+    i = np.arange(bits)[None, None, :]
+    h, r, m = u // 16, (u % 16) // 4, u % 4
+    cb, n = c // 16, c % 16
+    lane = 16 * r + n
+    if bits == 2:
+        word = lane * (D // 32) + cb // 2
+        bit = 16 * h + 8 * (cb % 2) + 2 * m + i
+    elif bits == 3:
+        wpl = 3 * D // 64
+        qd, w = cb // 4, cb % 4
+        p = 3 * m + i
+        word = np.where(w < 3, lane * wpl + 3 * qd + w, lane * wpl + 3 * qd + p // 4)
+        bit = np.where(w < 3, 16 * h + 3 * m + i, 16 * h + 12 + p % 4)
+    else:
+        raise ValueError("2- or 3-bit codes")
+    word, bit = np.broadcast_arrays(word, bit)
+    tbit = (32 * word + bit).reshape(-1)
+    plain = (u * D * bits + c * bits + i)
+    plain = np.broadcast_to(plain, word.shape).reshape(-1)
+    src = np.full(32 * D * bits, -1, np.int64)
+    src[tbit] = plain
+    return src
+
+
+def v_bits_plain_to_tiled(plain, D, bits):
+    """[..., C, D*bits/8] plain rows -> [..., C/32, 32*D*bits/8] tile layout."""
+    plain = np.asarray(plain, np.uint8)
+    lead, C = plain.shape[:-2], plain.shape[-2]
+    pb = np.unpackbits(plain.reshape(lead + (C // 32, 32 * D * bits // 8)), axis=-1, bitorder="little")
+    tb = pb[..., _vbits_map(D, bits)]
+    return np.packbits(tb, axis=-1, bitorder="little")
+
+
+def v_bits_tiled_to_plain(tiled, D, bits):
+    """[..., C/32, 32*D*bits/8] tile layout -> [..., C, D*bits/8] plain rows."""
+    tiled = np.asarray(tiled, np.uint8)
+    lead, ntile = tiled.shape[:-2], tiled.shape[-2]
+    tb = np.unpackbits(tiled, axis=-1, bitorder="little")
+    pb = np.empty_like(tb)
+    pb[..., _vbits_map(D, bits)] = tb
+    return np.packbits(pb, axis=-1, bitorder="little").reshape(lead + (ntile * 32, D * bits // 8))

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(otq.EXPORTED)
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.otq_abi_version() == 7
+    assert lib.otq_abi_version() == 8
 
 
 def test_status_strings():
@@ -407,8 +407,8 @@ def test_plan_interleaved_pieces():
 
 def test_plan_variants_of_b_bit_caches():
     """b-bit caches take the MFMA split pass by default unless K is rotated
-    or channel-scaled (3-bit codes at D = 256: the vector pass); forcing MFMA
-    where it does not apply is OTQ_EUNSUPPORTED."""
+    or channel-scaled; forcing MFMA where it does not apply is
+    OTQ_EUNSUPPORTED."""
     lib = otq.lib()
     plain2 = _desc(B=1, H=8, D=128, cap=4096)
     plain2.code_bits = 2
@@ -425,12 +425,63 @@ def test_plan_variants_of_b_bit_caches():
     three = _desc(B=1, H=8, D=128, cap=4096)
     three.code_bits = 3
     assert otq.otq_sdpa_plan(64, three, 4096).variant == otq.OTQ_VARIANT_MFMA
-    wide3 = _desc(B=1, H=8, D=256, cap=4096)  # 3-bit codes at D = 256: vector only
+    wide3 = _desc(B=1, H=8, D=256, cap=4096)
     wide3.code_bits = 3
-    assert otq.otq_sdpa_plan(64, wide3, 4096).variant == otq.OTQ_VARIANT_VECTOR
-    assert otq.otq_sdpa_plan(64, wide3, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    assert otq.otq_sdpa_plan(64, wide3, 4096).variant == otq.OTQ_VARIANT_MFMA
+    wide3r = _desc(B=1, H=8, D=256, cap=4096, signs=FAKE)
+    wide3r.code_bits = 3
+    assert otq.otq_sdpa_plan(64, wide3r, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
     # the MFMA 2-bit plan: one KV head per block, four waves per chunk round
     p = otq.otq_sdpa_plan(64, _desc(B=1, H=8, D=128, cap=131072), 131072)
     p2 = otq.otq_sdpa_plan(64, plain2, 4096)
     assert p2.chunk % 128 == 0 and p2.num_splits == -(-4096 // p2.chunk)
     assert p.variant == otq.OTQ_VARIANT_MFMA
+
+
+# ---------------------------------------------------------------- b-bit V tiles
+def _one_code_plain(D, bits, u, c, code):
+    """Plain rows of one 32-token tile with a single non-zero field."""
+    rows = np.zeros((32, D * bits), np.uint8)
+    for i in range(bits):
+        rows[u, c * bits + i] = (code >> i) & 1
+    return np.packbits(rows, axis=-1, bitorder="little")
+
+
+def _set_bits(tiled):
+    bits = np.unpackbits(tiled.reshape(-1), bitorder="little")
+    return [int(x) for x in np.nonzero(bits)[0]]
+
+
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3])
+def test_v_bits_tile_layout_is_a_permutation(D, bits):
+    """The b-bit V tile map is a bijection on a tile's bits and round-trips."""
+    src = layout._vbits_map(D, bits)
+    assert src.min() == 0 and np.array_equal(np.sort(src), np.arange(32 * D * bits))
+    rng = np.random.default_rng(D + bits)
+    plain = rng.integers(0, 256, size=(2, 3, 96, D * bits // 8), dtype=np.uint8)
+    tiled = layout.v_bits_plain_to_tiled(plain, D, bits)
+    assert tiled.shape == (2, 3, 3, 32 * D * bits // 8)
+    assert np.array_equal(layout.v_bits_tiled_to_plain(tiled, D, bits), plain)
+
+
+def test_v_bits_tile_layout_positions():
+    """Field positions worked out by hand from the layout rule in otq.h."""
+    # 2 bits, D = 128: token 21 (h 1, r 1, m 1), channel 37 (cb 2, n 5):
+    # lane 21, word 21 * 4 + 1 = 85, bit 16 + 0 + 2 = 18; code -1 = 0b11
+    t = layout.v_bits_plain_to_tiled(_one_code_plain(128, 2, 21, 37, 0b11)[None], 128, 2)
+    assert _set_bits(t) == [32 * 85 + 18, 32 * 85 + 19]
+    # same token, channel 53 (cb 3: the upper byte of the same word)
+    t = layout.v_bits_plain_to_tiled(_one_code_plain(128, 2, 21, 53, 0b01)[None], 128, 2)
+    assert _set_bits(t) == [32 * 85 + 26]
+    # 3 bits, D = 64: token 6 (h 0, r 1, m 2), channel 35 (cb 2, n 3): lane 19,
+    # words 19 * 3 + 0..2, cb % 4 = 2 < 3: word 59, bit 6; code 0b101
+    t = layout.v_bits_plain_to_tiled(_one_code_plain(64, 3, 6, 35, 0b101)[None], 64, 3)
+    assert _set_bits(t) == [32 * 59 + 6, 32 * 59 + 8]
+    # channel 51 (cb 3, n 3: the top nibbles): chunk bits p = 6, 7, 8 -> word
+    # 57 + 1 bits 14, 15 and word 57 + 2 bit 12; code 0b101 sets p = 6 and 8
+    t = layout.v_bits_plain_to_tiled(_one_code_plain(64, 3, 6, 51, 0b101)[None], 64, 3)
+    assert _set_bits(t) == [32 * 58 + 14, 32 * 59 + 12]
+    # token 22 (h 1, r 1, m 2), same channel: 16 bits higher
+    t = layout.v_bits_plain_to_tiled(_one_code_plain(64, 3, 22, 51, 0b111)[None], 64, 3)
+    assert _set_bits(t) == [32 * 58 + 30, 32 * 58 + 31, 32 * 59 + 28]

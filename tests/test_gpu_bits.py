@@ -1,7 +1,8 @@
-"""GPU parity of the 2- and 3-bit path (plain bit-stream rows): codes and
-scales bit-exact against the oracle's b-bit quantiser, outputs of the split
-+ combine within the same tolerance as int4 against the oracle's fp64
-attention over the cache it quantised itself."""
+"""GPU parity of the 2- and 3-bit path (plain bit-stream K rows, V in
+32-token tiles): codes and scales bit-exact against the oracle's b-bit
+quantiser (its plain rows, with the V tiles converted back by layout.py),
+outputs of the split + combine within the same tolerance as int4 against the
+oracle's fp64 attention over the cache it quantised itself."""
 import math
 
 import numpy as np
@@ -10,7 +11,7 @@ import torch
 
 import int4_kv_cache_quant_amd as otq
 import oracle
-from int4_kv_cache_quant_amd import synth
+from int4_kv_cache_quant_amd import layout, synth
 
 from gpu_common import MAX_ABS, REL_L2, errors, say, to_bits
 
@@ -25,6 +26,17 @@ def _kv(B, H, T, D, dtype, seed):
     x[..., 3] *= 10
     x = x.to(dtype)
     return x[0], x[1]
+
+
+def _vplain(cache):
+    """The cache's V codes as plain b-bit rows [B, H, C, D*b/8]."""
+    D = cache.shape[2]
+    return layout.v_bits_tiled_to_plain(cache.v_codes.cpu().numpy(), D, cache.code_bits)
+
+
+def _set_vplain(cache, plain):
+    D = cache.shape[2]
+    cache.v_codes.copy_(torch.from_numpy(layout.v_bits_plain_to_tiled(plain, D, cache.code_bits)).to(DEV))
 
 
 def _build(k, v, cap, bits, chunk):
@@ -50,13 +62,16 @@ def test_bits_quantize_bit_exact(bits, D, dtype, chunk):
     name = "fp16" if dtype == torch.float16 else "bf16"
     kc, ks = oracle.quantize(to_bits(k), name, code_bits=bits)
     vc, vs = oracle.quantize(to_bits(v), name, code_bits=bits)
-    got = [t.cpu().numpy()[:, :, :T] for t in (cache.k_codes, cache.k_scales, cache.v_codes, cache.v_scales)]
+    vp = _vplain(cache)
+    got = [cache.k_codes.cpu().numpy()[:, :, :T], cache.k_scales.cpu().numpy()[:, :, :T], vp[:, :, :T],
+           cache.v_scales.cpu().numpy()[:, :, :T]]
     for g, r in zip(got, (kc, ks, vc, vs)):
         if g.dtype == np.float32:
             g, r = g.view(np.uint32), r.view(np.uint32)
         assert np.array_equal(g, r)
-    # tokens past the appended range stay untouched
+    # tokens past the appended range stay untouched (T = 45 ends inside a V tile)
     assert not np.any(cache.k_codes.cpu().numpy()[:, :, T:]) and not np.any(cache.v_scales.cpu().numpy()[:, :, T:])
+    assert not np.any(vp[:, :, T:])
 
 
 @pytest.mark.parametrize("bits", [2, 3])
@@ -72,8 +87,8 @@ def test_bits_sdpa_parity(bits, G, D, variant):
     cache = _build(k, v, cap, bits, 100)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     plan = cache.plan(G * Hkv, max(lens), chunk=128, variant=variant)
-    # b-bit codes default to the MFMA split pass (3-bit ones at D = 256 to the vector one)
-    mfma_ok = bits == 2 or D <= 128
+    # b-bit codes default to the MFMA split pass
+    mfma_ok = True
     want = otq.OTQ_VARIANT_MFMA if (mfma_ok and variant == otq.OTQ_VARIANT_AUTO) else otq.OTQ_VARIANT_VECTOR
     assert plan.variant == want
     scale = 1.0 / math.sqrt(D)
@@ -129,7 +144,7 @@ def test_bits_full_workload_3(bits):
     rng = np.random.default_rng(bits)
     toks = rng.choice(w.T, 64, replace=False)
     assert np.array_equal(cache.k_codes.cpu().numpy()[:, :, toks], kc[:, :, toks])
-    assert np.array_equal(cache.v_codes.cpu().numpy()[:, :, toks], vc[:, :, toks])
+    assert np.array_equal(_vplain(cache)[:, :, toks], vc[:, :, toks])
     rows = np.sort(rng.choice(w.Hq, 8, replace=False)).astype(np.int32)
     ref = oracle.sdpa(to_bits(q.cpu()), w.dtype, kc, ks, vc, vs, lens, w.scale, rows=rows, threads=16,
                       code_bits=bits)
@@ -173,7 +188,7 @@ def test_bits_with_rotations_and_scale(bits, opts, G, D):
     vc, vs = oracle.quantize(to_bits(v), "bf16", signs=sv_np, rot_norm=rn, rot_kind=kind, code_bits=bits)
     assert np.array_equal(cache.k_codes.cpu().numpy(), kc)
     assert np.array_equal(cache.k_scales.cpu().numpy().view(np.uint32), ks.view(np.uint32))
-    assert np.array_equal(cache.v_codes.cpu().numpy(), vc)
+    assert np.array_equal(_vplain(cache), vc)
     assert np.array_equal(cache.v_scales.cpu().numpy().view(np.uint32), vs.view(np.uint32))
     ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale, signs=sk.numpy(),
                       rot_norm=rn, threads=8, chan_scale=lam_np, v_signs=sv_np, rot_kind=kind, code_bits=bits)
@@ -192,8 +207,7 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     rows and merges it.  The token's slot holds junk before the call (code
     bytes and Inf/NaN scales); afterwards the whole cache equals the oracle's
     quantisation bit for bit and the outputs match the fp64 oracle.  Caches
-    with a plain K take the MFMA split pass (3-bit ones at D = 256 the vector
-    one), the others the vector one."""
+    with a plain K take the MFMA split pass, the others the vector one."""
     B, Hkv, cap = 3, 2, 320
     lens = [301, 96, 1]  # a token inside a tile, one opening a tile, one alone
     kind = "srft" if "srft" in opts else "srht"
@@ -212,13 +226,14 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     cache.append(k.to(DEV).contiguous(), v.to(DEV).contiguous(), pos)
     torch.cuda.synchronize()
     rng = np.random.default_rng(bits + D)
+    vp = _vplain(cache)
     for b, n in enumerate(lens):  # junk in the new token's slot
         cache.k_codes[b, :, n - 1] = torch.from_numpy(rng.integers(0, 256, size=(Hkv, D * bits // 8),
                                                                    dtype=np.uint8)).to(DEV)
-        cache.v_codes[b, :, n - 1] = torch.from_numpy(rng.integers(0, 256, size=(Hkv, D * bits // 8),
-                                                                   dtype=np.uint8)).to(DEV)
+        vp[b, :, n - 1] = rng.integers(0, 256, size=(Hkv, D * bits // 8), dtype=np.uint8)
         cache.k_scales[b, :, n - 1] = float("nan")
         cache.v_scales[b, :, n - 1] = float("inf")
+    _set_vplain(cache, vp)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
     idx = (lens_t.long() - 1)
     ar = torch.arange(B, device=DEV)
@@ -227,7 +242,7 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     scale = 1.0 / math.sqrt(D)
     plan = cache.plan(G * Hkv, max(lens), chunk=128)
     plain_k = sk is None and lam is None
-    want = otq.OTQ_VARIANT_MFMA if (plain_k and (bits == 2 or D <= 128)) else otq.OTQ_VARIANT_VECTOR
+    want = otq.OTQ_VARIANT_MFMA if plain_k else otq.OTQ_VARIANT_VECTOR
     assert plan.variant == want
     otq.otq_last_device_error()
     out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max(lens), scale, plan=plan)
@@ -242,7 +257,7 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     vc, vs = oracle.quantize(to_bits(v), "bf16", signs=sv_np, rot_norm=rn, rot_kind=kind, code_bits=bits)
     assert np.array_equal(cache.k_codes.cpu().numpy(), kc)
     assert np.array_equal(cache.k_scales.cpu().numpy().view(np.uint32), ks.view(np.uint32))
-    assert np.array_equal(cache.v_codes.cpu().numpy(), vc)
+    assert np.array_equal(_vplain(cache), vc)
     assert np.array_equal(cache.v_scales.cpu().numpy().view(np.uint32), vs.view(np.uint32))
     ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale, signs=sk_np,
                       rot_norm=rn, threads=8, chan_scale=lam_np, v_signs=sv_np, rot_kind=kind, code_bits=bits)

@@ -1,7 +1,6 @@
 """GPU parity of the 2- and 3-bit split pass on the matrix cores (the
-default for b-bit caches whose K is neither rotated nor channel-scaled; at
-head_dim 256 for 2-bit codes only), through the C ABI, against the oracle's
-b-bit quantiser and fp64 attention.
+default for b-bit caches whose K is neither rotated nor channel-scaled),
+through the C ABI, against the oracle's b-bit quantiser and fp64 attention.
 
 Covers every G up to 16 at head_dim 64, 128 and 256, tails and chunk ends,
 ragged batches in longest-first order, a rotated V (undone by the combine),
@@ -16,6 +15,8 @@ import torch
 
 import int4_kv_cache_quant_amd as otq
 import oracle
+
+from int4_kv_cache_quant_amd import layout
 
 from gpu_common import MAX_ABS, REL_L2, errors, rand_signs, say, to_bits
 
@@ -75,8 +76,8 @@ def test_bits_mfma_parity(bits, D, G):
     k, v, q = _inputs(B, G * Hkv, Hkv, D, cap, seed=D + G + 100 * bits)
     cache = _cache(k, v, bits=bits)
     got, plan = _decode(cache, q, lens, 1.0 / math.sqrt(D), chunk=128)
-    # the default for a plain b-bit cache (3-bit codes at D = 256: vector)
-    assert plan.variant == (MF if (bits == 2 or D <= 128) else VEC)
+    # the default for a plain b-bit cache
+    assert plan.variant == MF
     ref = _ref(q, k, v, lens, 1.0 / math.sqrt(D), bits=bits)
     ma, rel = errors(got, ref)
     say(f"b{bits} mfma D={D} G={G}: max_abs={ma:.3e} rel_l2={rel:.3e}")
@@ -154,15 +155,17 @@ def test_bits_mfma_junk_past_lens(bits):
     cache = _cache(k, v, bits=bits)
     rng = np.random.default_rng(5)
     pattern = torch.tensor([float("inf"), float("nan"), -float("inf"), float("nan")], device=DEV)
+    vp = layout.v_bits_tiled_to_plain(cache.v_codes.cpu().numpy(), D, bits)
     for b, f in enumerate(lens):
         n = cap - f
         idx = torch.arange(n * (D // 32), device=DEV) % 4
         cache.k_scales[b, :, f:] = pattern[idx].reshape(n, D // 32)
         cache.v_scales[b, :, f:] = pattern[(idx + 1) % 4].reshape(n, D // 32)
-        junk = lambda: torch.from_numpy(rng.integers(0, 256, size=(Hkv, n, D * bits // 8),
-                                                     dtype=np.uint8)).to(DEV)
-        cache.k_codes[b, :, f:] = junk()
-        cache.v_codes[b, :, f:] = junk()
+        cache.k_codes[b, :, f:] = torch.from_numpy(rng.integers(0, 256, size=(Hkv, n, D * bits // 8),
+                                                                dtype=np.uint8)).to(DEV)
+        # V: junk in the fields of tokens f.. only (a tile also holds tokens below f)
+        vp[b, :, f:] = rng.integers(0, 256, size=(Hkv, n, D * bits // 8), dtype=np.uint8)
+    cache.v_codes.copy_(torch.from_numpy(layout.v_bits_plain_to_tiled(vp, D, bits)).to(DEV))
     got, _ = _decode(cache, q, lens, 1.0 / math.sqrt(D), chunk=128, variant=MF)
     ref = _ref(q, k, v, lens, 1.0 / math.sqrt(D), bits=bits)
     assert np.all(np.isfinite(got))

@@ -194,9 +194,9 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         // lengths better the more (smaller) items there are
         // the vector b-bit split pass hides latency only with several blocks per CU
         const bool bits_vec = code_bits(c) != 4 && variant == OTQ_VARIANT_VECTOR;
-        // the 2-bit MFMA pass (one KV head per block) is measured fastest
-        // with two waves per SIMD: on the 70B layer at 128K, 49.7 us at
-        // chunk 2048 against 76.2 us at 4096 and 53.5 us at 1024
+        // the b-bit MFMA pass (one KV head per block) is measured fastest
+        // with two waves per SIMD: on the 70B layer at 128K (2-bit codes),
+        // 32.8 us at chunk 2048 against 37.3 us at 1024
         const bool bits_mfma = code_bits(c) != 4 && variant == OTQ_VARIANT_MFMA;
         const long long target = (ordered_batch(c->batch) || bits_vec) ? kTargetWaves * kOrderedWaveFactor
                                  : bits_mfma                           ? kTargetWaves * 2

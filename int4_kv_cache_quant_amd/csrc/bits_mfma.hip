@@ -315,18 +315,13 @@ void split_bits_mfma_kernel(SplitArgs a)
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
-    int slot = 0;
-    for (int it = wave; it < ntiles; it += W) {
-        // ---- the tile's registers into the stage, then the next load into them
+    // one tile: its registers (rg) into the wave's stage, the tile AH rounds
+    // ahead into rg, then the tile's products
+    auto tile_step = [&](int it, u32x4_t (&rg)[T::LOADS]) {
 #pragma unroll
         for (int k = 0; k < T::LOADS; ++k)
-            if (src_on[k])
-                *reinterpret_cast<u32x4_t*>(stage + 16 * (64 * k + lane)) = (AH > 1 && slot) ? pf[AH - 1][k] : pf[0][k];
-        if (it + AH * W < ntiles) {
-            if (AH == 1 || slot == 0) load_tile(pf[0], it + AH * W);
-            else load_tile(pf[AH - 1], it + AH * W);
-        }
-        slot = AH > 1 ? slot ^ 1 : 0;
+            if (src_on[k]) *reinterpret_cast<u32x4_t*>(stage + 16 * (64 * k + lane)) = rg[k];
+        if (it + AH * W < ntiles) load_tile(rg, it + AH * W);
         const int tok0 = start + it * kTile;
 
         // the scales of the lane's tokens 16 s + 4 r + i, group g
@@ -343,34 +338,18 @@ void split_bits_mfma_kernel(SplitArgs a)
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) valid[s][i] = tok_of(s, i) < nvalid;
-        // the V scales of the lane's tokens: in registers up to head_dim 128
-        // (zeroed past the end), read where used at 256 (and masked there)
-        constexpr bool SVR = D <= 128;
-        float svr[SVR ? 2 : 1][4][SVR ? NG : 1];
-        if constexpr (SVR) {
+        // the V scales of the lane's token 16 s + 4 r + slot (slot = lane % 4),
+        // every group, zero past the end (whatever the cache holds there);
+        // DPP quad broadcasts hand token 4 r + m's to the quad
+        const int slot = lane & 3;
+        float sv[2][NG];
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+        for (int s = 0; s < 2; ++s) {
+            const float* src = vsc + tok_of(s, slot) * NG;
+            const bool in = !tail || tok_of(s, slot) < nvalid;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-#pragma unroll
-                    for (int g = 0; g < NG; ++g) svr[s][i][g] = vsc[tok_of(s, i) * NG + g];
-            if (tail) {
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-#pragma unroll
-                        for (int g = 0; g < NG; ++g) svr[s][i][g] = valid[s][i] ? svr[s][i][g] : 0.0f;
-            }
+            for (int g = 0; g < NG; ++g) sv[s][g] = in ? src[g] : 0.0f;
         }
-        auto vscale = [&](int s, int i, int g) {
-            if constexpr (SVR) {
-                return svr[s][i][g];
-            } else {
-                const float sc = vsc[tok_of(s, i) * NG + g];
-                return valid[s][i] ? sc : 0.0f;
-            }
-        };
 
         // ---- scores T[s][i] (token 16 s + 4 r + i, column n16), / qmul
         float Tt[2][4];
@@ -422,9 +401,7 @@ void split_bits_mfma_kernel(SplitArgs a)
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int g = 0; g < NG; ++g) svm = fmaxf(svm, vscale(s, i, g));
+            for (int g = 0; g < NG; ++g) svm = fmaxf(svm, sv[s][g]);
         const bool vmove = __any(svm > v_lim);
         if (__any(mt > m_run) || vmove) {
             const float m_new = (mt > m_run) ? mt + kHeadroom : m_run;
@@ -447,13 +424,21 @@ void split_bits_mfma_kernel(SplitArgs a)
             m_run = m_new;
             e_v = e_new;
         }
+        // the tile's V scales carry 2^E (exact)
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int g = 0; g < NG; ++g) sv[s][g] = __builtin_ldexpf(sv[s][g], e_v);
+        // p of the lane's tokens; the V codes of slot pair i carry
+        // 2^kVExp<BITS>[i], taken off p here (exact), after l has taken p
         float p[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                p[s][i] = exp2_approx(__builtin_fmaf(Tt[s][i], qmul, -m_run));
-                l_lane += p[s][i];
+                const float pf = exp2_approx(__builtin_fmaf(Tt[s][i], qmul, -m_run));
+                l_lane += pf;
+                p[s][i] = kVExp<BITS>[i] ? __builtin_ldexpf(pf, -kVExp<BITS>[i]) : pf;
             }
 
         // ---- values: the lane's words of the V tile (channel column n16 of
@@ -484,11 +469,10 @@ void split_bits_mfma_kernel(SplitArgs a)
             static_for<4>([&](auto mI) {
 #pragma clang fp contract(off)
                 constexpr int m = decltype(mI)::value;
-                // the code of slot pair m carries 2^kVExp<BITS>[m]: taken off p
-                const int ex = e_v - kVExp<BITS>[m];
-                // a token past the end has scale 0 (not 0 times whatever the cache holds)
-                const float x0 = p[0][m] * __builtin_ldexpf(vscale(0, m, g), ex);
-                const float x1 = p[1][m] * __builtin_ldexpf(vscale(1, m, g), ex);
+                // one product per element, consumed by both halves, so the
+                // broadcast folds into v_mul_f32_dpp
+                const float x0 = p[0][m] * quad_bcast<m>(sv[0][g]);
+                const float x1 = p[1][m] * quad_bcast<m>(sv[1][g]);
                 ha[m] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)x0, (_Float16)x1});
                 la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
             });
@@ -511,6 +495,15 @@ void split_bits_mfma_kernel(SplitArgs a)
                 acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
             });
         });
+    };
+    // the register sets in turn, each index fixed at compile time
+    if constexpr (AH == 2) {
+        for (int it = wave; it < ntiles; it += 2 * W) {
+            tile_step(it, pf[0]);
+            if (it + W < ntiles) tile_step(it + W, pf[1]);
+        }
+    } else {
+        for (int it = wave; it < ntiles; it += W) tile_step(it, pf[0]);
     }
 
     // ---- merge of the W waves (each writes its share into its own stage,

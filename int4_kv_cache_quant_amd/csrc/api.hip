@@ -189,6 +189,8 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
             units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
             waves = otq::split_mfma_block_waves(D);
             align = waves * OTQ_TILE;  // one tile per wave and round
+        } else if (variant == OTQ_VARIANT_MFMA) {
+            units /= otq::split_bits_mfma_heads_per_wave(D, G, c->num_kv_heads);
         }
         // a batch takes its items longest first, which balances unequal
         // lengths better the more (smaller) items there are
@@ -420,9 +422,10 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     a.err = error_word();
     if (!a.err) return OTQ_EDEVICE;
     if (ordered_batch(a.B)) {
-        const int groups = chk.variant == OTQ_VARIANT_MFMA && code_bits(cache) == 4
-                               ? a.H / otq::split_mfma_heads_per_wave(D, num_q_heads / a.H, a.H)
-                               : a.H;
+        const int G = num_q_heads / a.H;
+        const int groups = chk.variant != OTQ_VARIANT_MFMA ? a.H
+                           : code_bits(cache) == 4     ? a.H / otq::split_mfma_heads_per_wave(D, G, a.H)
+                                                       : a.H / otq::split_bits_mfma_heads_per_wave(D, G, a.H);
         int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
                                               order_offset(cache, num_q_heads, chk));
         if (otq::launch_split_order(lens, lens_offset, max_len, chk.chunk, chk.num_splits, groups, a.B,

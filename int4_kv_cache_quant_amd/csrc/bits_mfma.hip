@@ -61,14 +61,15 @@ using namespace mfma;
 
 constexpr int kB2Waves = 4;  // waves per block
 // Tiles each wave holds in registers ahead of the one it computes (one at
-// head_dim 256, whose tiles take twice the registers).
-template <int D>
-constexpr int kB2Ahead = D == 256 ? 1 : 2;
+// head_dim 256 and for two KV heads per wave, whose tiles take twice the
+// registers).
+template <int D, int P>
+constexpr int kB2Ahead = (D == 256 || P == 2) ? 1 : 2;
 // Where the score accumulator starts at the offset correction (a register
 // quad per group, live through the loop) rather than taking it after the
 // MFMA: everywhere but head_dim 256, whose registers are full.
-template <int D>
-constexpr bool kB2QinitInAcc = D != 256;
+template <int D, int P>
+constexpr bool kB2QinitInAcc = D != 256 && P == 1;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -87,6 +88,16 @@ struct BTile {
     static constexpr int RS = D + 4;
     static constexpr int MERGE = 16 * RS * 4 + 16 * 8;
     static constexpr int STAGE = BYTES > MERGE ? BYTES : MERGE;
+};
+
+// A wave's LDS stage for P KV heads: their tiles one after the other (head j
+// at j BYTES); the merge reuses it.
+template <int D, int BITS, int P>
+struct BStage {
+    using T = BTile<D, BITS>;
+    static constexpr int SLOTS = P * T::SLOTS;
+    static constexpr int LOADS = (SLOTS + 63) / 64;
+    static constexpr int BYTES = P * T::BYTES > T::MERGE ? P * T::BYTES : T::MERGE;
 };
 
 // K: 8 codes (16 bits of a row, the lane's channels 32 g + 8 r + 0..7 at bit
@@ -178,53 +189,58 @@ __device__ __forceinline__ half8_t unpack_v3(uint32_t x)
 template <int BITS>
 constexpr int kVExp[4] = {0, BITS == 2 ? 2 : 3, BITS == 2 ? 4 : 6, BITS == 2 ? 6 : 0};
 
-template <int D, int BITS>
-__global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2)))
+template <int D, int BITS, int P>
+__global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 4 : 2)))
 void split_bits_mfma_kernel(SplitArgs a)
 {
     static_assert(BITS == 2 || BITS == 3, "2- or 3-bit codes");
     using T = BTile<D, BITS>;
+    using SG = BStage<D, BITS, P>;
     using VT = VBitsTile<D, BITS>;
     constexpr int NG = T::NG, NCB = D / 16, RB = T::RB, W = kB2Waves;
-    extern __shared__ __align__(16) char lds[];  // W stages of T::STAGE bytes
+    extern __shared__ __align__(16) char lds[];  // W stages of SG::BYTES
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    int split = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
+    int split = blockIdx.x, hk0 = blockIdx.y * P, b = blockIdx.z;
     if (a.items) {  // a batch: the block's item in longest-first order
-        const int k = blockIdx.x + a.num_splits * (blockIdx.y + a.H * blockIdx.z);
+        const int groups = a.H / P;
+        const int k = blockIdx.x + a.num_splits * (blockIdx.y + groups * blockIdx.z);
         const int2 it = a.items[k];
         if (it.x < 0) return;  // block-uniform: no item
         split = it.x;
         b = it.y;
-        hk = k % a.H;
+        hk0 = (k % groups) * P;
     }
     const int G = a.Hq / a.H;
+    const int PG = P * G;  // query heads served by the block (<= 16)
     const int n16 = lane & 15, r = lane >> 4;
-    const bool col_valid = n16 < G;
-    char* stage = lds + wave * T::STAGE;
+    const bool col_valid = n16 < PG;
+    const int jl = col_valid ? n16 / G : 0;  // KV head (of the block's P) of this lane's column
+    char* stage = lds + wave * SG::BYTES;
 
     // lens clamped to [0, max_len], then the fused append's token left to
     // the combine
     const int raw_len = a.lens[b];
     const int len = max(min(max(raw_len, 0), a.max_len) - a.lens_offset, 0);
-    if (tid == 0 && split == 0 && hk == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
+    if (tid == 0 && split == 0 && hk0 == 0 && (raw_len < 0 || raw_len > a.max_len)) report_error(a.err, kErrLens);
     const int start = split * a.chunk;
     if (start >= len) return;  // block-uniform: no partial for an empty split
     const int end = min(start + a.chunk, len);
     const int ntiles = (end - start + kTile - 1) / kTile;
 
-    // ---- per-lane sources of the tile's 16-byte pieces: K rows, V rows,
-    //      K scales, V scales, each contiguous for the tile's 32 tokens
-    const size_t head = (size_t)b * a.H + hk;
-    const char* src_base[T::LOADS];
-    int src_stride[T::LOADS];
-    bool src_on[T::LOADS];
+    // ---- per-lane sources of the tile's 16-byte pieces: per KV head, K rows,
+    //      the V tile, K scales, V scales, each contiguous for the tile's 32
+    //      tokens
+    const char* src_base[SG::LOADS];
+    int src_stride[SG::LOADS];
+    bool src_on[SG::LOADS];
 #pragma unroll
-    for (int k = 0; k < T::LOADS; ++k) {
+    for (int k = 0; k < SG::LOADS; ++k) {
         const int i = 64 * k + lane;
-        src_on[k] = i < T::SLOTS;
-        const int o = 16 * i;
+        src_on[k] = i < SG::SLOTS;
+        const size_t head = (size_t)b * a.H + hk0 + min(i / T::SLOTS, P - 1);
+        const int o = 16 * (i % T::SLOTS);
         if (o < T::VOFF) {
             src_base[k] = reinterpret_cast<const char*>(a.kc) + head * a.cap * RB + o;
             src_stride[k] = RB;
@@ -239,12 +255,12 @@ void split_bits_mfma_kernel(SplitArgs a)
             src_stride[k] = NG * 4;
         }
     }
-    constexpr int AH = kB2Ahead<D>;
-    u32x4_t pf[AH][T::LOADS];
-    auto load_tile = [&](u32x4_t (&dst)[T::LOADS], int it) {
+    constexpr int AH = kB2Ahead<D, P>;
+    u32x4_t pf[AH][SG::LOADS];
+    auto load_tile = [&](u32x4_t (&dst)[SG::LOADS], int it) {
         const int tok0 = start + it * kTile;
 #pragma unroll
-        for (int k = 0; k < T::LOADS; ++k)
+        for (int k = 0; k < SG::LOADS; ++k)
             if (src_on[k])
                 dst[k] = __builtin_nontemporal_load(
                     reinterpret_cast<const u32x4_t*>(src_base[k] + (size_t)tok0 * src_stride[k]));
@@ -253,12 +269,12 @@ void split_bits_mfma_kernel(SplitArgs a)
     for (int k = 0; k < AH; ++k)
         if (wave + k * W < ntiles) load_tile(pf[k], wave + k * W);
 
-    // ---- q: column n16 = query head hk G + n16, lane r holds channels
+    // ---- q: column n16 = query head hk0 G + n16, lane r holds channels
     //      32 g + 8 r + 0..7; scaled by 2^qk (largest |q| in [2^14, 2^15))
     float qx[NG][8];
     {
         const uint16_t* qsrc =
-            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk * G + (col_valid ? n16 : 0)) * D;
+            static_cast<const uint16_t*>(a.q) + ((size_t)b * a.Hq + hk0 * G + (col_valid ? n16 : 0)) * D;
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
             const uint4 raw = *reinterpret_cast<const uint4*>(qsrc + 32 * g + 8 * r);
@@ -281,9 +297,10 @@ void split_bits_mfma_kernel(SplitArgs a)
     // B operands: k slot (2k, 2k + 1) = channels (8 r + k, 8 r + k + 4) of the
     // group, divided by the code's positional power of two (4^k at 2 bits,
     // kK3Exp at 3); the accumulator starts at -2^(b-1) * 2^-24 * sum(q over
-    // the group)
+    // the group).  With two KV heads per wave, head j's products take q
+    // masked to its columns (qbj[j]), so both accumulate into one C.
     half8_t qb[NG];
-    floatx4_t qinit4[kB2QinitInAcc<D> ? NG : 1];
+    floatx4_t qinit4[kB2QinitInAcc<D, P> ? NG : 1];
     float qinit1[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -298,9 +315,17 @@ void split_bits_mfma_kernel(SplitArgs a)
                 tq += (float)v;
             }
         const float qi = -(float)(1 << (BITS - 1)) * 0x1p-24f * sum_xor32(sum_xor16(tq));
-        if constexpr (kB2QinitInAcc<D>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
+        if constexpr (kB2QinitInAcc<D, P>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
         qinit1[g] = qi;
     }
+    half8_t qbj[P][NG];
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+            const half8_t zero = {};
+            qbj[j][g] = (P == 1 || jl == j) ? qb[g] : zero;
+        }
     const float qmul = __builtin_ldexpf(a.qscale * 0x1p24f, -qk);
     // 2 bits: the lane's K field is half r & 1 of word 2 g + r / 2 of a row;
     // 3 bits: it starts at bit 24 r of the group's three words
@@ -311,22 +336,25 @@ void split_bits_mfma_kernel(SplitArgs a)
     int e_v = 0;            // E (wave-uniform): the value operand carries 2^E
     float v_lim = 0.0f;     // V scales above this move E
     float l_lane = 0.0f;    // sum of this lane's probabilities (column n16)
-    floatx4_t acc[NCB];
+    floatx4_t acc[P][NCB];  // per KV head: O[query head 4 r + i][channel 16 cb + n16]
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) acc[cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[j][cb] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
     // one tile: its registers (rg) into the wave's stage, the tile AH rounds
     // ahead into rg, then the tile's products
-    auto tile_step = [&](int it, u32x4_t (&rg)[T::LOADS]) {
+    auto tile_step = [&](int it, u32x4_t (&rg)[SG::LOADS]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int k = 0; k < T::LOADS; ++k)
+        for (int k = 0; k < SG::LOADS; ++k)
             if (src_on[k]) *reinterpret_cast<u32x4_t*>(stage + 16 * (64 * k + lane)) = rg[k];
         if (it + AH * W < ntiles) load_tile(rg, it + AH * W);
         const int tok0 = start + it * kTile;
 
-        // the scales of the lane's tokens 16 s + 4 r + i, group g
-        const float* ksc = reinterpret_cast<const float*>(stage + T::KSOFF);
-        const float* vsc = reinterpret_cast<const float*>(stage + T::VSOFF);
+        // the scales of the lane's tokens 16 s + 4 r + i, group g, in its
+        // column's KV head
+        const float* ksc = reinterpret_cast<const float*>(stage + jl * T::BYTES + T::KSOFF);
+        const float* vsc = reinterpret_cast<const float*>(stage + jl * T::BYTES + T::VSOFF);
         auto tok_of = [&](int s, int i) { return 16 * s + 4 * r + i; };
         // a token past the end (only in the split's last tile) counts as
         // absent: its score is -inf and its V scale 0 (set after the loads,
@@ -355,25 +383,28 @@ void split_bits_mfma_kernel(SplitArgs a)
         float Tt[2][4];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const char* krow = stage + T::KOFF + (16 * s + n16) * RB;
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                half8_t A;
-                if constexpr (BITS == 2) {
-                    A = unpack_k2(*reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1))), ksel);
-                } else {
-                    // the word after the field's first lies inside the stage
-                    // even for the tile's last row (the V rows follow)
-                    const uint32_t* kw = reinterpret_cast<const uint32_t*>(krow) + 3 * g + k3w;
-                    A = unpack_k3(__builtin_amdgcn_alignbit(kw[1], kw[0], k3s));
+                floatx4_t d = kB2QinitInAcc<D, P> ? qinit4[kB2QinitInAcc<D, P> ? g : 0]
+                                                  : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int j = 0; j < P; ++j) {
+                    const char* krow = stage + j * T::BYTES + T::KOFF + (16 * s + n16) * RB;
+                    half8_t A;
+                    if constexpr (BITS == 2) {
+                        A = unpack_k2(*reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1))), ksel);
+                    } else {
+                        // the word after the field's first lies inside the stage
+                        // even for the tile's last row (the V tile follows)
+                        const uint32_t* kw = reinterpret_cast<const uint32_t*>(krow) + 3 * g + k3w;
+                        A = unpack_k3(__builtin_amdgcn_alignbit(kw[1], kw[0], k3s));
+                    }
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qbj[j][g], d, 0, 0, 0);
                 }
-                const floatx4_t d = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-                    A, qb[g],
-                    kB2QinitInAcc<D> ? qinit4[kB2QinitInAcc<D> ? g : 0] : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float di = kB2QinitInAcc<D> ? d[i] : d[i] + qinit1[g];
+                    const float di = kB2QinitInAcc<D, P> ? d[i] : d[i] + qinit1[g];
                     const float term = ksc[tok_of(s, i) * NG + g] * di;
                     tot[i] = (g == 0) ? term : tot[i] + term;
                 }
@@ -419,7 +450,9 @@ void split_bits_mfma_kernel(SplitArgs a)
                 constexpr int i = decltype(iI)::value;
                 const float ai = row_quad_gather<i>(alpha_o, r);  // of column 4 r + i
 #pragma unroll
-                for (int cb = 0; cb < NCB; ++cb) acc[cb][i] *= ai;
+                for (int j = 0; j < P; ++j)
+#pragma unroll
+                    for (int cb = 0; cb < NCB; ++cb) acc[j][cb][i] *= ai;
             });
             m_run = m_new;
             e_v = e_new;
@@ -443,24 +476,25 @@ void split_bits_mfma_kernel(SplitArgs a)
 
         // ---- values: the lane's words of the V tile (channel column n16 of
         //      every block, tokens 4 r + m and 16 + 4 r + m in the two halves)
-        uint32_t vw[VT::WPL];
-        {
-            const char* src = stage + T::VOFF + lane * 4 * VT::WPL;
+        uint32_t vw[P][VT::WPL];
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            const char* src = stage + j * T::BYTES + T::VOFF + lane * 4 * VT::WPL;
             if constexpr (VT::WPL % 4 == 0) {
 #pragma unroll
                 for (int k = 0; k < VT::WPL; k += 4) {
                     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + 4 * k);
-                    vw[k] = w.x; vw[k + 1] = w.y; vw[k + 2] = w.z; vw[k + 3] = w.w;
+                    vw[j][k] = w.x; vw[j][k + 1] = w.y; vw[j][k + 2] = w.z; vw[j][k + 3] = w.w;
                 }
             } else if constexpr (VT::WPL % 2 == 0) {
 #pragma unroll
                 for (int k = 0; k < VT::WPL; k += 2) {
                     const uint2 w = *reinterpret_cast<const uint2*>(src + 4 * k);
-                    vw[k] = w.x; vw[k + 1] = w.y;
+                    vw[j][k] = w.x; vw[j][k + 1] = w.y;
                 }
             } else {
 #pragma unroll
-                for (int k = 0; k < VT::WPL; ++k) vw[k] = reinterpret_cast<const uint32_t*>(src)[k];
+                for (int k = 0; k < VT::WPL; ++k) vw[j][k] = reinterpret_cast<const uint32_t*>(src)[k];
             }
         }
         static_for<NG>([&](auto gI) {
@@ -477,38 +511,41 @@ void split_bits_mfma_kernel(SplitArgs a)
                 la[m] = lo_pair<m == 3>(x0, x1, ha[m]);
             });
             const half8_t pa = __builtin_bit_cast(half8_t, ha), pl = __builtin_bit_cast(half8_t, la);
-            static_for<2>([&](auto hI) {
-                constexpr int cb = 2 * g + decltype(hI)::value;
-                half8_t B;
-                if constexpr (BITS == 2) {
-                    B = unpack_v2((cb & 1) ? (vw[cb >> 1] >> 8) : vw[cb >> 1]);
-                } else {
-                    constexpr int qd = cb >> 2, t = cb & 3;
-                    if constexpr (t < 3) {
-                        B = unpack_v3(vw[3 * qd + t]);
-                    } else {  // the block held in the top nibbles of the quad's words
-                        B = unpack_v3(((vw[3 * qd] >> 12) & 0x000F000Fu) | ((vw[3 * qd + 1] >> 8) & 0x00F000F0u) |
-                                      ((vw[3 * qd + 2] >> 4) & 0x0F000F00u));
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                static_for<2>([&](auto hI) {
+                    constexpr int cb = 2 * g + decltype(hI)::value;
+                    half8_t B;
+                    if constexpr (BITS == 2) {
+                        B = unpack_v2((cb & 1) ? (vw[j][cb >> 1] >> 8) : vw[j][cb >> 1]);
+                    } else {
+                        constexpr int qd = cb >> 2, t = cb & 3;
+                        if constexpr (t < 3) {
+                            B = unpack_v3(vw[j][3 * qd + t]);
+                        } else {  // the block held in the top nibbles of the quad's words
+                            B = unpack_v3(((vw[j][3 * qd] >> 12) & 0x000F000Fu) |
+                                          ((vw[j][3 * qd + 1] >> 8) & 0x00F000F0u) |
+                                          ((vw[j][3 * qd + 2] >> 4) & 0x0F000F00u));
+                        }
                     }
-                }
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[cb], 0, 0, 0);
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[cb], 0, 0, 0);
-            });
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[j][cb], 0, 0, 0);
+                    acc[j][cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl, B, acc[j][cb], 0, 0, 0);
+                });
+            }
         });
     };
     // the register sets in turn, each index fixed at compile time
-    if constexpr (AH == 2) {
-        for (int it = wave; it < ntiles; it += 2 * W) {
-            tile_step(it, pf[0]);
-            if (it + W < ntiles) tile_step(it + W, pf[1]);
-        }
-    } else {
-        for (int it = wave; it < ntiles; it += W) tile_step(it, pf[0]);
+    for (int it = wave; it < ntiles; it += AH * W) {
+        tile_step(it, pf[0]);
+        static_for<AH - 1>([&](auto kI) {
+            constexpr int k = decltype(kI)::value + 1;
+            if (it + k * W < ntiles) tile_step(it + k * W, pf[k]);
+        });
     }
 
     // ---- merge of the W waves (each writes its share into its own stage,
     //      which it no longer reads), then the block's partial
-    auto merge_o = [&](int w) { return reinterpret_cast<float*>(lds + w * T::STAGE); };
+    auto merge_o = [&](int w) { return reinterpret_cast<float*>(lds + w * SG::BYTES); };
     auto merge_ml = [&](int w) { return reinterpret_cast<float2*>(merge_o(w) + 16 * T::RS); };
     const float L = sum_xor32(sum_xor16(l_lane));
     // acc carries 2^E: (M - F, l 2^F, acc 2^(F - E)) with F = floor(E / 2)
@@ -516,12 +553,20 @@ void split_bits_mfma_kernel(SplitArgs a)
     const int f_e = e_v >> 1;
     if (lane < 16) merge_ml(wave)[lane] = make_float2(m_run - (float)f_e, __builtin_ldexpf(L, f_e));
     float* own = merge_o(wave);
+    // rows 4 r .. 4 r + 3 lie in one KV head (two heads per wave only when
+    // G >= 4): keep that head's accumulators
+    const int jr = min(4 * r / G, P - 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int h = 4 * r + i;
-        if (h < G) {
+        if (h < PG) {
 #pragma unroll
-            for (int cb = 0; cb < NCB; ++cb) own[h * T::RS + 16 * cb + n16] = __builtin_ldexpf(acc[cb][i], f_e - e_v);
+            for (int cb = 0; cb < NCB; ++cb) {
+                float v = acc[0][cb][i];
+#pragma unroll
+                for (int j = 1; j < P; ++j) v = (jr == j) ? acc[j][cb][i] : v;
+                own[h * T::RS + 16 * cb + n16] = __builtin_ldexpf(v, f_e - e_v);
+            }
         }
     }
     __syncthreads();
@@ -529,7 +574,7 @@ void split_bits_mfma_kernel(SplitArgs a)
 #pragma unroll
     for (int k = 0; k < kMergeIters; ++k) {
         const int i = tid + k * 64 * W;
-        if (i >= G * (D / 4)) break;
+        if (i >= PG * (D / 4)) break;
         const int h = i / (D / 4), c = 4 * (i % (D / 4));
         float2 ml[W];
         float Mb = kNegInf;
@@ -547,13 +592,20 @@ void split_bits_mfma_kernel(SplitArgs a)
             o.x += f * x.x; o.y += f * x.y; o.z += f * x.z; o.w += f * x.w;
             Ls += f * ml[w].y;
         }
-        const size_t prow = ((size_t)b * a.Hq + hk * G + h) * a.num_splits + split;
+        const size_t prow = ((size_t)b * a.Hq + hk0 * G + h) * a.num_splits + split;
         *reinterpret_cast<float4*>(a.part_o + prow * D + c) = o;
         if (c == 0) a.part_ml[prow] = make_float2(Mb, Ls);
     }
 }
 
 }  // namespace
+
+// KV heads per wave: two (filling 16 MFMA columns at G = 8) when 4 <= G <= 8,
+// the head count is even and the registers suffice (head_dim < 256), else one.
+int split_bits_mfma_heads_per_wave(int D, int G, int H)
+{
+    return (D != 256 && G >= 4 && G <= 8 && H % 2 == 0) ? 2 : 1;
+}
 
 bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
 {
@@ -563,17 +615,26 @@ bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
 
 namespace {
 
+template <int D, int BITS, int P>
+hipError_t launch_bp(const SplitArgs& a, hipStream_t stream)
+{
+    const size_t lds = (size_t)kB2Waves * BStage<D, BITS, P>::BYTES;
+    static const hipError_t attr = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&split_bits_mfma_kernel<D, BITS, P>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (attr != hipSuccess) return attr;
+    dim3 grid(a.num_splits, a.H / P, a.B), block(64 * kB2Waves);
+    split_bits_mfma_kernel<D, BITS, P><<<grid, block, lds, stream>>>(a);
+    return hipGetLastError();
+}
+
 template <int D, int BITS>
 hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 {
-    const size_t lds = (size_t)kB2Waves * BTile<D, BITS>::STAGE;
-    static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&split_bits_mfma_kernel<D, BITS>), hipFuncAttributeMaxDynamicSharedMemorySize,
-        (int)lds);
-    if (attr != hipSuccess) return attr;
-    dim3 grid(a.num_splits, a.H, a.B), block(64 * kB2Waves);
-    split_bits_mfma_kernel<D, BITS><<<grid, block, lds, stream>>>(a);
-    return hipGetLastError();
+    if constexpr (D != 256) {
+        if (split_bits_mfma_heads_per_wave(D, a.Hq / a.H, a.H) == 2) return launch_bp<D, BITS, 2>(a, stream);
+    }
+    return launch_bp<D, BITS, 1>(a, stream);
 }
 
 }  // namespace

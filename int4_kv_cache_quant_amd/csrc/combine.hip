@@ -376,8 +376,7 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
     // blocks (2048)
     const bool pow2 = a.D == 64 || a.D == 128 || a.D == 256;  // the whole-row forms' widths
     const bool big = !append && pow2 && (long)a.B * a.Hq * (a.D / kCh) > 2048;
-    // (and for the append of b-bit codes, whose rows one block packs)
-    const bool rows = vrot || (append && rot) || big || (append && a.bits != 4);
+    const bool rows = vrot || (append && rot) || big;
     dim3 grid(a.B * a.Hq, rows ? 1 : a.D / kCh), block(kThreads);
     if (!append && !rows) {
         lse_combine_kernel<0, false, false, false, false, false><<<grid, block, 0, stream>>>(a);

@@ -71,6 +71,7 @@ hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
 // 2- and 3-bit codes on the matrix cores (head_dim 64, 128, 256; G <= 16;
 // no K rotation or channel scale).
 bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k);
+int split_bits_mfma_heads_per_wave(int D, int G, int H);
 hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream);
 
 // Head widths that are multiples of 64 but not powers of two (192): the

@@ -114,19 +114,21 @@ def test_bits_mfma_matches_vector_variant(bits):
 
 @pytest.mark.parametrize("bits", [2, 3])
 @pytest.mark.parametrize("B", [12, 64])
-def test_bits_mfma_ragged_batch(bits, B):
+@pytest.mark.parametrize("Hkv", [1, 2])
+def test_bits_mfma_ragged_batch(bits, B, Hkv):
     """A batch in longest-first order: empty sequences, one token, chunk
-    multiples and partial chunks."""
+    multiples and partial chunks; one KV head (one per wave) and two (G = 8:
+    both in one wave)."""
     rng = np.random.default_rng(B)
     lens = [int(x) for x in rng.integers(0, 385, size=B)]
     lens[0], lens[1], lens[2] = 0, 1, 384
-    k, v, q = _inputs(B, 8, 1, 64, 384, seed=B + bits)
+    k, v, q = _inputs(B, 8 * Hkv, Hkv, 64, 384, seed=B + bits + Hkv)
     cache = _cache(k, v, bits=bits)
     got, plan = _decode(cache, q, lens, 0.125, chunk=128, variant=MF)
     ref = _ref(q, k, v, lens, 0.125, bits=bits)
     assert np.all(got[0] == 0.0)
     ma, rel = errors(got, ref)
-    say(f"b{bits} mfma ragged B={B}: max_abs={ma:.3e} rel_l2={rel:.3e}")
+    say(f"b{bits} mfma ragged B={B} Hkv={Hkv}: max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
 
 

@@ -24,6 +24,8 @@ namespace otq {
 
 namespace {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 constexpr float kNegInfB = -__builtin_huge_valf();
 
 // Signed b-bit code of element i of a row held as 32-bit words (the bits
@@ -38,15 +40,18 @@ __device__ __forceinline__ int code_in_words(const uint32_t* w, int i)
     return (int)(u << (32 - BITS)) >> (32 - BITS);
 }
 
-// One block per (32-token tile touched by the append, KV head, sequence):
-// its waves quantise the tile's new K and V vectors in turn (one wave per
-// vector, E = D / 64 elements per lane).  A K row is written whole from the
+constexpr int kBitsSmallAppend = 8;
+
+// Appends of fewer than kBitsSmallAppend tokens (a decode step's token): one
+// block per (32-token tile touched, KV head, sequence) whose waves quantise
+// the tile's new K and V vectors in turn (one wave per vector, E = D / 64
+// elements per lane), a short dependency chain per token.  A K row is written whole from the
 // wave's codes (D b / 32 lanes assemble its 32-bit words); the V codes of
 // the tile are staged in LDS and the tile's V words are written whole, merged
 // with the old words under a mask where only part of the tile is new (only
 // this block writes the tile in this launch).
 template <int D, int BITS>
-__global__ __launch_bounds__(256) void quantize_bits_kernel(
+__global__ __launch_bounds__(256) void quantize_bits_small_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
     const int32_t* __restrict__ pos, const float* __restrict__ signs, float rot_norm, int rot_kind,
@@ -144,6 +149,140 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
             if (u >= u0 && u < u0 + nt) {
                 const uint32_t fm = (1u << width) - 1u;
                 val |= (((uint32_t)(int)cvt[u][c] >> shift) & fm) << bpos;
+                mask |= fm << bpos;
+            }
+        });
+        if (mask == 0) continue;
+        if (mask != 0xFFFFFFFFu) val |= vt[W] & ~mask;
+        vt[W] = val;
+    }
+}
+
+// Bulk appends: one block per (32-token tile touched by the append, KV
+// head, sequence).  K and V alike: a token occupies LT = D / 8 consecutive threads, thread j of
+// a token holding its channels 8 j .. 8 j + 7 (one 16-byte load), so a scale
+// group is one aligned quad of lanes; every load of the block is issued
+// before any arithmetic.  Each vector is widened, rotated (its own signs, in
+// the same order of operations as the other append kernels), K scaled by its
+// channel scale, and quantised: s = abs-max / (2^(b-1) - 1) and c =
+// clamp(rint(x / s)) by IEEE division.  The codes pass through LDS; then the
+// block writes the tile's K rows and V words whole, merging V words with
+// their old contents under a mask where only part of the tile is new (only
+// this block writes the tile in this launch).
+template <int D, int BITS, bool SRFT>
+__global__ __launch_bounds__(256) void quantize_bits_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
+    uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
+    const int32_t* __restrict__ pos, const float* __restrict__ signs, float rot_norm,
+    const float* __restrict__ lam, const float* __restrict__ vsigns, unsigned* __restrict__ err)
+{
+#pragma clang fp contract(off)
+    constexpr int NG = D / kGroup, RB = D * BITS / 8, RW = RB / 4;
+    constexpr int LT = D / 8;           // threads per token
+    constexpr int U = kTile * LT / 256;  // units (16-byte pieces) per thread, of K and of V
+    constexpr float qmax = (float)((1 << (BITS - 1)) - 1), qmin = -(float)(1 << (BITS - 1));
+    using VT = VBitsTile<D, BITS>;
+    static_assert(RB % 4 == 0, "whole words per row");
+    __shared__ int8_t ccs[2][kTile][D];  // the tile's K and V codes
+    const int tid = threadIdx.x, j = tid % LT;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int p0 = pos[b];
+    if (tid == 0 && blockIdx.x == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new))
+        report_error(err, kErrPos);  // the tokens outside [0, cap) are skipped below
+    // the block's tile: the appended range clipped to [0, cap), tiles counted
+    // from the one holding its first token
+    const long long lo_all = max((long long)p0, 0LL), hi_all = min((long long)p0 + n_new, (long long)cap);
+    if (lo_all >= hi_all) return;  // block-uniform: nothing inside the cache
+    const int tile = (int)(lo_all / kTile) + blockIdx.x;
+    const int t0 = kTile * tile;
+    const int lo = (int)max(lo_all, (long long)t0), hi = (int)min(hi_all, (long long)t0 + kTile);
+    if (lo >= hi) return;  // block-uniform: past the range
+    const int u0 = lo - t0, nt = hi - lo;
+    auto fresh = [&](int u) { return u >= u0 && u < u0 + nt; };
+    const size_t head = (size_t)b * H + h;
+
+    // every load first: unit i of this thread is token u = (256 i + tid) / LT
+    // of the tile, channels 8 j .. 8 j + 7
+    u32x4_t raw[2][U];
+#pragma unroll
+    for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int u = (256 * i + tid) / LT;
+            raw[w][i] = u32x4_t{0u, 0u, 0u, 0u};
+            if (fresh(u))
+                raw[w][i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+                    (w ? v : k) + (head * n_new + (t0 + u - p0)) * D + 8 * j));
+        }
+    float sg[8], vsg[8], lm[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sg[e] = signs ? signs[8 * j + e] : 1.0f;
+        vsg[e] = vsigns ? vsigns[8 * j + e] : 1.0f;
+        lm[e] = lam ? lam[8 * j + e] : 1.0f;
+    }
+    [[maybe_unused]] SrftLaneTw<D, 8> stw;  // the FFT rotation's twiddles of this lane position
+    if constexpr (SRFT) stw.load(j);
+
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        const bool rot = w ? vsigns != nullptr : signs != nullptr;
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int u = (256 * i + tid) / LT;
+            // the same for the LT lanes of a token, which alone exchange values
+            if (!fresh(u)) continue;
+            float x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = widen((uint16_t)(raw[w][i][e / 2] >> (16 * (e % 2))), dtype);
+            if (rot) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * (w ? vsg[e] : sg[e]);
+                if constexpr (SRFT)
+                    srft_signed<D, 8>(x, rot_norm, j, stw);
+                else
+                    rotate_signed<D, 8>(x, rot_norm, j);
+            }
+            if (w == 0 && lam) {  // K's per-channel scale, after the rotation
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * lm[e];
+            }
+            float a = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
+            a = group_max<4>(a);        // exact in any order
+            const float sc = a / qmax;  // correctly rounded IEEE division
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                float r = rintf(x[e] / sc);  // IEEE division, then half to even
+                r = fminf(fmaxf(r, qmin), qmax);
+                ccs[w][u][8 * j + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
+            }
+            if ((j & 3) == 0) (w ? vs : ks)[(head * cap + t0 + u) * NG + j / 4] = sc;
+        }
+    }
+    __syncthreads();
+    // the new tokens' K rows, word by word (word q: bits [32 q, 32 q + 32))
+    for (int W = tid; W < kTile * RW; W += 256) {
+        const int u = W / RW, q = W % RW;
+        if (!fresh(u)) continue;
+        uint32_t word = 0;
+        const int i0 = (32 * q) / BITS, i1 = min((32 * q + 31) / BITS, D - 1);
+        for (int i = i0; i <= i1; ++i) {
+            const uint32_t c = (uint32_t)ccs[0][u][i] & ((1u << BITS) - 1u);
+            const int off = i * BITS - 32 * q;  // negative for a code that starts in the word before
+            word |= off >= 0 ? c << off : c >> -off;
+        }
+        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(kc + (head * cap + t0 + u) * RB) + q);
+    }
+    // the tile's V words: the new tokens' fields
+    uint32_t* vt = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + tile) * (size_t)(kTile * RB));
+    for (int W = tid; W < VT::WORDS; W += 256) {
+        uint32_t val = 0, mask = 0;
+        vtile_fields<D, BITS>(W, [&](int u, int c, int bpos, int width, int shift) {
+            if (fresh(u)) {
+                const uint32_t fm = (1u << width) - 1u;
+                val |= (((uint32_t)(int)ccs[1][u][c] >> shift) & fm) << bpos;
                 mask |= fm << bpos;
             }
         });
@@ -377,10 +516,16 @@ hipError_t launch_q(const void* k, const void* v, int dtype, int n_new, int B, i
 {
     // an unaligned range of n_new tokens touches at most n_new / 32 + 2 tiles
     dim3 grid(n_new / kTile + 2, H, B), block(256);
-    quantize_bits_kernel<D, BITS><<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k),
-                                                          static_cast<const uint16_t*>(v), dtype, n_new,
-                                                          H, cap, kc, ks, vc, vs, pos, r.signs,
-                                                          r.rot_norm, r.rot_kind, r.lam, r.vsigns, err);
+    if (n_new < kBitsSmallAppend) {
+        quantize_bits_small_kernel<D, BITS><<<grid, block, 0, s>>>(
+            static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), dtype, n_new, H, cap, kc, ks, vc, vs,
+            pos, r.signs, r.rot_norm, r.rot_kind, r.lam, r.vsigns, err);
+        return hipGetLastError();
+    }
+    auto kern = (r.signs || r.vsigns) && r.rot_kind ? quantize_bits_kernel<D, BITS, true>
+                                                    : quantize_bits_kernel<D, BITS, false>;
+    kern<<<grid, block, 0, s>>>(static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), dtype, n_new, H,
+                                cap, kc, ks, vc, vs, pos, r.signs, r.rot_norm, r.lam, r.vsigns, err);
     return hipGetLastError();
 }
 

@@ -264,3 +264,30 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     ma, rel = errors(out.cpu().numpy(), ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
     assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("bits", [2, 3])
+@pytest.mark.parametrize("D", [64, 128, 256])
+@pytest.mark.parametrize("p0,n", [(37, 100), (5, 8), (64, 64), (90, 7)])
+def test_bits_append_inside_a_filled_cache(bits, D, p0, n):
+    """A cache filled with one set of tokens, then n other tokens appended at
+    p0 (tile-aligned or not, bulk and short appends): the new tokens' codes
+    and scales are the oracle's, every other token keeps its bytes (its V
+    fields share tile words with the new ones)."""
+    B, H, cap = 2, 2, 192
+    say(f"bits overwrite b={bits} D={D} p0={p0} n={n}")
+    k, v = _kv(B, H, cap, D, torch.bfloat16, seed=bits * 7 + D + p0)
+    k2, v2 = _kv(B, H, n, D, torch.bfloat16, seed=bits * 11 + D + n)
+    cache = _build(k, v, cap, bits, cap)
+    pos = torch.full((B,), p0, dtype=torch.int32, device=DEV)
+    cache.append(k2.to(DEV).contiguous(), v2.to(DEV).contiguous(), pos)
+    torch.cuda.synchronize()
+    km, vm = k.clone(), v.clone()
+    km[:, :, p0:p0 + n] = k2
+    vm[:, :, p0:p0 + n] = v2
+    kc, ks = oracle.quantize(to_bits(km), "bf16", code_bits=bits)
+    vc, vs = oracle.quantize(to_bits(vm), "bf16", code_bits=bits)
+    assert np.array_equal(cache.k_codes.cpu().numpy(), kc)
+    assert np.array_equal(cache.k_scales.cpu().numpy().view(np.uint32), ks.view(np.uint32))
+    assert np.array_equal(_vplain(cache), vc)
+    assert np.array_equal(cache.v_scales.cpu().numpy().view(np.uint32), vs.view(np.uint32))

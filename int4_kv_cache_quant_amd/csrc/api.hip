@@ -200,8 +200,12 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         // with two waves per SIMD: on the 70B layer at 128K (2-bit codes),
         // 32.8 us at chunk 2048 against 37.3 us at 1024
         const bool bits_mfma = code_bits(c) != 4 && variant == OTQ_VARIANT_MFMA;
+        // so is the int4 pass at head_dim 256 (one KV head per wave): on the
+        // Gemma-shaped layer (16 KV heads, 64K tokens) 63.1 us at chunk 2048
+        // against 63.9-64.6 us at 4096
+        const bool wide_mfma = code_bits(c) == 4 && variant == OTQ_VARIANT_MFMA && D == 256;
         const long long target = (ordered_batch(c->batch) || bits_vec) ? kTargetWaves * kOrderedWaveFactor
-                                 : bits_mfma                           ? kTargetWaves * 2
+                                 : (bits_mfma || wide_mfma)            ? kTargetWaves * 2
                                                                        : kTargetWaves;
         const long long groups = target / waves;
         long long want = ((long long)max_len * units + groups - 1) / groups;

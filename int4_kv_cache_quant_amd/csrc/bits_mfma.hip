@@ -36,18 +36,22 @@
 // A b-bit cache with a rotated or channel-scaled K takes the vector split
 // pass (its q is not exact in fp16); a rotated V is undone by the combine.
 //
-// Block = 4 waves, one (split, KV head, sequence); wave w takes the tiles w,
-// w + 4, ... of the split (32 tokens each).  Each tile (K rows, the V tile,
-// K and V scales: (8 b + 8) D bytes) is loaded into registers two tiles
-// ahead (one at head_dim 256), written to the wave's LDS stage when its turn
-// comes, and read back in the operand layouts below.  Lane l = 16 r + n:
-//  scores  A = K codes (row = token 16 s + n, k = channels 32 g + 8 r + the
-//          slot order), B = q of query head n (columns >= G are zero);
-//          C = S[token 16 s + 4 r + i][head n]
+// Block = 4 waves, one (split, P KV heads, sequence): P = 2 when 4 <= G <= 8
+// (the two heads' query heads fill the 16 MFMA columns), else 1; wave w takes
+// the tiles w, w + 4, ... of the split (32 tokens each).  Each tile (per
+// head: K rows, the V tile, K and V scales: (8 b + 8) D bytes) is loaded
+// into registers ahead (two tiles; one at head_dim 256 and for two heads per
+// wave), written to the wave's LDS stage when its turn comes, and read back
+// in the operand layouts below.  Lane l = 16 r + n:
+//  scores  A = K codes of head j (row = token 16 s + n, k = channels
+//          32 g + 8 r + the slot order), B = q of query head n masked to
+//          head j's columns (columns >= P G are zero); the P products
+//          accumulate into C = S[token 16 s + 4 r + i][head n]
 //  values  A = x (row = head n, k slots (2m, 2m + 1) = tokens 4 r + m and
 //          16 + 4 r + m: the tokens whose scores this lane holds), B = V codes
-//          (column = channel 16 cb + n, the same tokens), C = O[head 4 r + i]
-//          [channel 16 cb + n].
+//          (column = channel 16 cb + n, the same tokens), one accumulator set
+//          per KV head, C_j = O[head 4 r + i][channel 16 cb + n], of which
+//          the rows of head j are kept.
 #include "bits_layout.hpp"
 #include "common.hpp"
 #include "kernels.hpp"
@@ -67,7 +71,8 @@ template <int D, int P>
 constexpr int kB2Ahead = (D == 256 || P == 2) ? 1 : 2;
 // Where the score accumulator starts at the offset correction (a register
 // quad per group, live through the loop) rather than taking it after the
-// MFMA: everywhere but head_dim 256, whose registers are full.
+// MFMA: everywhere but head_dim 256 and two heads per wave, whose registers
+// are full.
 template <int D, int P>
 constexpr bool kB2QinitInAcc = D != 256 && P == 1;
 

@@ -303,11 +303,7 @@ def bench_workload(wnum, args, primary):
     extra_rot = primary and (args.srft or args.srht)
     chan = primary and args.chan_scale
     vrot = primary and args.v_rotate
-    if bits != 4 and (extra_rot or chan or vrot or w.rotate):
-        if primary:
-            sys.exit("bench.py: 2- and 3-bit caches take no rotation or channel scale")
-        log(f"bench: workload {wnum} rotates K: timed with 4-bit codes")
-    wbits = 4 if (bits != 4 and w.rotate) else bits
+    wbits = bits  # b-bit caches take the rotations and the channel scale too
     if args.srft and args.srht:
         sys.exit("bench.py: --srft and --srht name two different K rotations")
     t_setup = time.time()

@@ -134,8 +134,7 @@ int rot_kind(const otq_cache* c)
 bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
 // The b-bit MFMA split pass: 2- or 3-bit codes, power-of-two head_dim,
-// G <= 16, a K that is neither rotated nor channel-scaled (q must be exact
-// in fp16).
+// G <= 16; a rotated or channel-scaled K (hi + lo query) up to head_dim 128.
 bool bits_mfma_ok(const otq_cache* c, int G)
 {
     return otq::split_bits_mfma_supports(c->head_dim, G, code_bits(c), c->k_rot_signs || c->k_chan_scale);
@@ -190,7 +189,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
             waves = otq::split_mfma_block_waves(D);
             align = waves * OTQ_TILE;  // one tile per wave and round
         } else if (variant == OTQ_VARIANT_MFMA) {
-            units /= otq::split_bits_mfma_heads_per_wave(D, G, c->num_kv_heads);
+            units /= otq::split_bits_mfma_heads_per_wave(D, G, c->num_kv_heads, c->k_rot_signs || c->k_chan_scale);
         }
         // a batch takes its items longest first, which balances unequal
         // lengths better the more (smaller) items there are
@@ -429,7 +428,7 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
         const int G = num_q_heads / a.H;
         const int groups = chk.variant != OTQ_VARIANT_MFMA ? a.H
                            : code_bits(cache) == 4     ? a.H / otq::split_mfma_heads_per_wave(D, G, a.H)
-                                                       : a.H / otq::split_bits_mfma_heads_per_wave(D, G, a.H);
+                                                       : a.H / otq::split_bits_mfma_heads_per_wave(D, G, a.H, a.signs || a.lam);
         int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
                                               order_offset(cache, num_q_heads, chk));
         if (otq::launch_split_order(lens, lens_offset, max_len, chk.chunk, chk.num_splits, groups, a.B,

@@ -33,8 +33,10 @@
 //    exactly), undone in the softmax scale;
 //  * x = p * s_v * 2^E is split into fp16 hi + lo operands; E follows the
 //    largest V scale seen, as in the int4 pass.
-// A b-bit cache with a rotated or channel-scaled K takes the vector split
-// pass (its q is not exact in fp16); a rotated V is undone by the combine.
+// A rotated or channel-scaled K (head_dim up to 128) takes q rotated as K
+// was and divided by the channel scale, as fp16 hi + lo operands (two score
+// products per group, one KV head per wave); at head_dim 256 such caches take
+// the vector split pass.  A rotated V is undone by the combine.
 //
 // Block = 4 waves, one (split, P KV heads, sequence): P = 2 when 4 <= G <= 8
 // (the two heads' query heads fill the 16 MFMA columns), else 1; wave w takes
@@ -73,8 +75,8 @@ constexpr int kB2Ahead = (D == 256 || P == 2) ? 1 : 2;
 // quad per group, live through the loop) rather than taking it after the
 // MFMA: everywhere but head_dim 256 and two heads per wave, whose registers
 // are full.
-template <int D, int P>
-constexpr bool kB2QinitInAcc = D != 256 && P == 1;
+template <int D, int P, bool HILO>
+constexpr bool kB2QinitInAcc = D != 256 && P == 1 && !HILO;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -194,7 +196,7 @@ __device__ __forceinline__ half8_t unpack_v3(uint32_t x)
 template <int BITS>
 constexpr int kVExp[4] = {0, BITS == 2 ? 2 : 3, BITS == 2 ? 4 : 6, BITS == 2 ? 6 : 0};
 
-template <int D, int BITS, int P>
+template <int D, int BITS, int P, bool HILO>
 __global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 4 : 2)))
 void split_bits_mfma_kernel(SplitArgs a)
 {
@@ -289,6 +291,26 @@ void split_bits_mfma_kernel(SplitArgs a)
                 qx[g][e] = col_valid ? widen((uint16_t)(w4[e / 2] >> (16 * (e % 2))), a.dtype) : 0.0f;
         }
     }
+    // HILO (K rotated or channel-scaled): q rotated as K was (its signs, then
+    // the cache's transform; rot_norm goes into qmul), then divided by K's
+    // channel scale; such a q is not exact in fp16 and enters as hi + lo
+    const bool rot = HILO && a.signs != nullptr;
+    if constexpr (HILO) {
+        if (rot) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qx[g][e] *= a.signs[32 * g + 8 * r + e];
+            if (a.rot_kind) srft_query<NG>(qx, r);
+            else fwht_query<NG>(qx, r);
+        }
+        if (a.lam) {
+#pragma unroll
+            for (int g = 0; g < NG; ++g)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) qx[g][e] = qx[g][e] / a.lam[32 * g + 8 * r + e];
+        }
+    }
     int qk = 0;
     {
         float qa = 0.0f;
@@ -304,8 +326,8 @@ void split_bits_mfma_kernel(SplitArgs a)
     // kK3Exp at 3); the accumulator starts at -2^(b-1) * 2^-24 * sum(q over
     // the group).  With two KV heads per wave, head j's products take q
     // masked to its columns (qbj[j]), so both accumulate into one C.
-    half8_t qb[NG];
-    floatx4_t qinit4[kB2QinitInAcc<D, P> ? NG : 1];
+    half8_t qb[NG], qbl[HILO ? NG : 1];
+    floatx4_t qinit4[kB2QinitInAcc<D, P, HILO> ? NG : 1];
     float qinit1[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) {
@@ -314,13 +336,19 @@ void split_bits_mfma_kernel(SplitArgs a)
         for (int k = 0; k < 4; ++k)
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const _Float16 v = (_Float16)__builtin_ldexpf(qx[g][k + 4 * h], qk);
+                const float xs = __builtin_ldexpf(qx[g][k + 4 * h], qk);
+                const _Float16 v = (_Float16)xs;
                 const int pe = BITS == 2 ? 2 * k : kK3Exp[k];
                 qb[g][2 * k + h] = (_Float16)((float)v * __builtin_ldexpf(1.0f, -pe));
                 tq += (float)v;
+                if constexpr (HILO) {
+                    const _Float16 lo = (_Float16)(xs - (float)v);
+                    qbl[g][2 * k + h] = (_Float16)((float)lo * __builtin_ldexpf(1.0f, -pe));
+                    tq += (float)lo;
+                }
             }
         const float qi = -(float)(1 << (BITS - 1)) * 0x1p-24f * sum_xor32(sum_xor16(tq));
-        if constexpr (kB2QinitInAcc<D, P>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
+        if constexpr (kB2QinitInAcc<D, P, HILO>) qinit4[g] = floatx4_t{qi, qi, qi, qi};
         qinit1[g] = qi;
     }
     half8_t qbj[P][NG];
@@ -331,7 +359,7 @@ void split_bits_mfma_kernel(SplitArgs a)
             const half8_t zero = {};
             qbj[j][g] = (P == 1 || jl == j) ? qb[g] : zero;
         }
-    const float qmul = __builtin_ldexpf(a.qscale * 0x1p24f, -qk);
+    const float qmul = __builtin_ldexpf((rot ? a.qscale * a.rot_norm : a.qscale) * 0x1p24f, -qk);
     // 2 bits: the lane's K field is half r & 1 of word 2 g + r / 2 of a row;
     // 3 bits: it starts at bit 24 r of the group's three words
     const uint32_t ksel = (r & 1) ? 0x0C030C02u : 0x0C010C00u;
@@ -391,7 +419,7 @@ void split_bits_mfma_kernel(SplitArgs a)
             floatx4_t tot = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int g = 0; g < NG; ++g) {
-                floatx4_t d = kB2QinitInAcc<D, P> ? qinit4[kB2QinitInAcc<D, P> ? g : 0]
+                floatx4_t d = kB2QinitInAcc<D, P, HILO> ? qinit4[kB2QinitInAcc<D, P, HILO> ? g : 0]
                                                   : floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
                 for (int j = 0; j < P; ++j) {
@@ -406,10 +434,11 @@ void split_bits_mfma_kernel(SplitArgs a)
                         A = unpack_k3(__builtin_amdgcn_alignbit(kw[1], kw[0], k3s));
                     }
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qbj[j][g], d, 0, 0, 0);
+                    if constexpr (HILO) d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qbl[g], d, 0, 0, 0);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float di = kB2QinitInAcc<D, P> ? d[i] : d[i] + qinit1[g];
+                    const float di = kB2QinitInAcc<D, P, HILO> ? d[i] : d[i] + qinit1[g];
                     const float term = ksc[tok_of(s, i) * NG + g] * di;
                     tot[i] = (g == 0) ? term : tot[i] + term;
                 }
@@ -607,29 +636,32 @@ void split_bits_mfma_kernel(SplitArgs a)
 
 // KV heads per wave: two (filling 16 MFMA columns at G = 8) when 4 <= G <= 8,
 // the head count is even and the registers suffice (head_dim < 256), else one.
-int split_bits_mfma_heads_per_wave(int D, int G, int H)
+int split_bits_mfma_heads_per_wave(int D, int G, int H, bool hilo)
 {
+    if (hilo) return 1;  // the hi + lo query takes the registers of a second head
     return (D != 256 && G >= 4 && G <= 8 && H % 2 == 0) ? 2 : 1;
 }
 
 bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
 {
+    // a rotated or channel-scaled K (hi + lo query) up to head_dim 128, whose
+    // registers leave room for it
     return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (bits == 2 || bits == 3) &&
-           !rotated_or_scaled_k;
+           !(rotated_or_scaled_k && D == 256);
 }
 
 namespace {
 
-template <int D, int BITS, int P>
+template <int D, int BITS, int P, bool HILO>
 hipError_t launch_bp(const SplitArgs& a, hipStream_t stream)
 {
     const size_t lds = (size_t)kB2Waves * BStage<D, BITS, P>::BYTES;
     static const hipError_t attr = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&split_bits_mfma_kernel<D, BITS, P>),
+        reinterpret_cast<const void*>(&split_bits_mfma_kernel<D, BITS, P, HILO>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (attr != hipSuccess) return attr;
     dim3 grid(a.num_splits, a.H / P, a.B), block(64 * kB2Waves);
-    split_bits_mfma_kernel<D, BITS, P><<<grid, block, lds, stream>>>(a);
+    split_bits_mfma_kernel<D, BITS, P, HILO><<<grid, block, lds, stream>>>(a);
     return hipGetLastError();
 }
 
@@ -637,16 +669,18 @@ template <int D, int BITS>
 hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 {
     if constexpr (D != 256) {
-        if (split_bits_mfma_heads_per_wave(D, a.Hq / a.H, a.H) == 2) return launch_bp<D, BITS, 2>(a, stream);
+        if (a.signs || a.lam) return launch_bp<D, BITS, 1, true>(a, stream);
+        if (split_bits_mfma_heads_per_wave(D, a.Hq / a.H, a.H, false) == 2)
+            return launch_bp<D, BITS, 2, false>(a, stream);
     }
-    return launch_bp<D, BITS, 1>(a, stream);
+    return launch_bp<D, BITS, 1, false>(a, stream);
 }
 
 }  // namespace
 
 hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream)
 {
-    if (a.signs || a.lam || a.Hq / a.H > 16) return hipErrorInvalidValue;
+    if (((a.signs || a.lam) && a.D == 256) || a.Hq / a.H > 16) return hipErrorInvalidValue;
     switch (a.D * 10 + bits) {
     case 642: return launch_b<64, 2>(a, stream);
     case 643: return launch_b<64, 3>(a, stream);

@@ -1,9 +1,11 @@
 // mfma_common.hpp - pieces shared by the MFMA split passes (the int4 one and
-// the 2-bit one): operand types, the softmax-reference and value-exponent
-// constants, the hi/lo split of the value operand, and DPP lane moves.
+// the b-bit one): operand types, the softmax-reference and value-exponent
+// constants, the hi/lo split of the value operand, DPP lane moves, and the
+// rotations of the query in the passes' register layout.
 #pragma once
 
 #include "common.hpp"
+#include "srft.hpp"
 
 namespace otq {
 namespace mfma {
@@ -73,6 +75,121 @@ __device__ __forceinline__ float row_quad_gather(float v, int r)
     const float v0 = row_bcast<I>(v), v1 = row_bcast<4 + I>(v);
     const float v2 = row_bcast<8 + I>(v), v3 = row_bcast<12 + I>(v);
     return r == 0 ? v0 : r == 1 ? v1 : r == 2 ? v2 : v3;
+}
+
+// Butterfly across lane bit 4 (XOR16) or bit 5 (XOR32 = false): the lane with
+// that bit clear gets lo + hi, its partner lo - hi.  first_lo says whether the
+// swap's first register holds the value of the lane with the bit clear (told
+// by swapping the lane's own row index once).
+template <bool XOR16>
+__device__ __forceinline__ float butterfly_lanes(float v, bool first_lo, bool upper)
+{
+    float x, y;
+    pair_values<XOR16>(v, x, y);
+    const float lo = first_lo ? x : y, hi = first_lo ? y : x;
+    return upper ? lo - hi : lo + hi;
+}
+
+// The query's FFT rotation (without rot_norm, which the score multiplier
+// carries) in the split kernel's query layout: lane (n16, r) holds channels
+// 32 g + 8 r + e in qx[g][e], i.e. complex number j = 16 g + 4 r + e / 2,
+// component e % 2.  Decimation-in-frequency stages of half-size h: h >= 16
+// pair g with g + h / 16 in the lane, h = 8 and 4 pair lanes 32 and 16
+// apart, h = 2 and 1 pair complex numbers inside an 8-channel run.
+template <int NG>
+__device__ __forceinline__ void srft_query(float (&qx)[NG][8], int r)
+{
+    constexpr int N = 16 * NG;
+    auto bfly = [](float& ar, float& ai, float& br, float& bi, int u) {
+        const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+        const float dr = ar - br, di = ai - bi;
+        ar = ar + br;
+        ai = ai + bi;
+        br = dr * wr - di * wi;
+        bi = dr * wi + di * wr;
+    };
+#pragma unroll
+    for (int h = N / 2; h >= 16; h >>= 1) {
+        const int gm = h / 16;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            if ((g & gm) == 0)
+#pragma unroll
+                for (int cp = 0; cp < 4; ++cp)
+                    bfly(qx[g][2 * cp], qx[g][2 * cp + 1], qx[g + gm][2 * cp], qx[g + gm][2 * cp + 1],
+                         (16 * (g % gm) + 4 * r + cp) * (64 / h));
+    }
+#pragma unroll
+    for (int h = 8; h >= 4; h >>= 1) {  // lanes 32 (r bit 1) and 16 (r bit 0) apart
+        const int m = h == 8 ? 32 : 16;
+        const bool upper = (r & (h / 4)) != 0;
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+#pragma unroll
+            for (int cp = 0; cp < 4; ++cp) {
+                const float ore = shfl_xor(qx[g][2 * cp], m), oim = shfl_xor(qx[g][2 * cp + 1], m);
+                const int u = ((4 * r + cp) & (h - 1)) * (64 / h);
+                const float wr = srft_detail::kTw.re[u], wi = srft_detail::kTw.im[u];
+                const float dr = ore - qx[g][2 * cp], di = oim - qx[g][2 * cp + 1];
+                const float ur = dr * wr - di * wi, ui = dr * wi + di * wr;
+                qx[g][2 * cp] = upper ? ur : qx[g][2 * cp] + ore;
+                qx[g][2 * cp + 1] = upper ? ui : qx[g][2 * cp + 1] + oim;
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+        // h = 2: complex 0 with 2, 1 with 3; h = 1: 0 with 1, 2 with 3
+        bfly(qx[g][0], qx[g][1], qx[g][4], qx[g][5], 0);
+        bfly(qx[g][2], qx[g][3], qx[g][6], qx[g][7], 32);
+        bfly(qx[g][0], qx[g][1], qx[g][2], qx[g][3], 0);
+        bfly(qx[g][4], qx[g][5], qx[g][6], qx[g][7], 0);
+    }
+}
+
+// The query's Walsh-Hadamard rotation (without rot_norm, which the score
+// multiplier carries) in the split kernels' query layout: lane (n16, r)
+// holds channels 32 g + 8 r + e in qx[g][e].  The butterflies over channel
+// bits 0-2 stay in the lane, bits 3 and 4 pair lanes 16 and 32 apart, bits
+// 5.. pair the lane's groups (the stages of the transform commute).
+template <int NG>
+__device__ __forceinline__ void fwht_query(float (&qx)[NG][8], int r)
+{
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if ((e & h) == 0) {
+                    const float lo = qx[g][e], hi = qx[g][e + h];
+                    qx[g][e] = lo + hi;
+                    qx[g][e + h] = lo - hi;
+                }
+    unsigned ra = (unsigned)r, rb = ra;
+    swap_rows16(ra, rb);
+    const bool lo16 = (ra & 1u) == 0;
+    ra = (unsigned)r; rb = ra;
+    swap_rows32(ra, rb);
+    const bool lo32 = (ra & 2u) == 0;
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            qx[g][e] = butterfly_lanes<true>(qx[g][e], lo16, (r & 1) != 0);
+            qx[g][e] = butterfly_lanes<false>(qx[g][e], lo32, (r & 2) != 0);
+        }
+#pragma unroll
+    for (int h = 1; h < NG; h <<= 1)
+#pragma unroll
+        for (int g = 0; g < NG; ++g)
+            if ((g & h) == 0)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float lo = qx[g][e], hi = qx[g + h][e];
+                    qx[g][e] = lo + hi;
+                    qx[g + h][e] = lo - hi;
+                }
 }
 
 }  // namespace mfma

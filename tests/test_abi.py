@@ -406,9 +406,9 @@ def test_plan_interleaved_pieces():
 
 
 def test_plan_variants_of_b_bit_caches():
-    """b-bit caches take the MFMA split pass by default unless K is rotated
-    or channel-scaled; forcing MFMA where it does not apply is
-    OTQ_EUNSUPPORTED."""
+    """b-bit caches take the MFMA split pass by default, with a rotated or
+    channel-scaled K up to D = 128 too; at D = 256 such a K takes the vector
+    pass, and forcing MFMA there is OTQ_EUNSUPPORTED."""
     lib = otq.lib()
     plain2 = _desc(B=1, H=8, D=128, cap=4096)
     plain2.code_bits = 2
@@ -416,12 +416,16 @@ def test_plan_variants_of_b_bit_caches():
     assert otq.otq_sdpa_plan(64, plain2, 4096, variant=otq.OTQ_VARIANT_VECTOR).variant == otq.OTQ_VARIANT_VECTOR
     rot2 = _desc(B=1, H=8, D=128, cap=4096, signs=FAKE)
     rot2.code_bits = 2
-    assert otq.otq_sdpa_plan(64, rot2, 4096).variant == otq.OTQ_VARIANT_VECTOR
-    assert otq.otq_sdpa_plan(64, rot2, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == otq.OTQ_EUNSUPPORTED
+    assert otq.otq_sdpa_plan(64, rot2, 4096).variant == otq.OTQ_VARIANT_MFMA
     lam2 = _desc(B=1, H=8, D=128, cap=4096)
     lam2.code_bits = 2
     lam2.k_chan_scale = FAKE
-    assert otq.otq_sdpa_plan(64, lam2, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(64, lam2, 4096).variant == otq.OTQ_VARIANT_MFMA
+    rot256 = _desc(B=1, H=8, D=256, cap=4096, signs=FAKE)
+    rot256.code_bits = 2
+    assert otq.otq_sdpa_plan(64, rot256, 4096).variant == otq.OTQ_VARIANT_VECTOR
+    assert otq.otq_sdpa_plan(64, rot256, 4096, variant=otq.OTQ_VARIANT_MFMA, check=False)[0] == \
+        otq.OTQ_EUNSUPPORTED
     three = _desc(B=1, H=8, D=128, cap=4096)
     three.code_bits = 3
     assert otq.otq_sdpa_plan(64, three, 4096).variant == otq.OTQ_VARIANT_MFMA

@@ -207,7 +207,8 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     rows and merges it.  The token's slot holds junk before the call (code
     bytes and Inf/NaN scales); afterwards the whole cache equals the oracle's
     quantisation bit for bit and the outputs match the fp64 oracle.  Caches
-    with a plain K take the MFMA split pass, the others the vector one."""
+    take the MFMA split pass (a rotated or channel-scaled K with a hi + lo
+    query, up to D = 128), the others the vector one."""
     B, Hkv, cap = 3, 2, 320
     lens = [301, 96, 1]  # a token inside a tile, one opening a tile, one alone
     kind = "srft" if "srft" in opts else "srht"
@@ -242,7 +243,7 @@ def test_bits_fused_decode_step(bits, opts, G, D):
     scale = 1.0 / math.sqrt(D)
     plan = cache.plan(G * Hkv, max(lens), chunk=128)
     plain_k = sk is None and lam is None
-    want = otq.OTQ_VARIANT_MFMA if plain_k else otq.OTQ_VARIANT_VECTOR
+    want = otq.OTQ_VARIANT_MFMA if (plain_k or D <= 128) else otq.OTQ_VARIANT_VECTOR
     assert plan.variant == want
     otq.otq_last_device_error()
     out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max(lens), scale, plan=plan)

@@ -134,10 +134,19 @@ int rot_kind(const otq_cache* c)
 bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
 // The b-bit MFMA split pass: 2- or 3-bit codes, power-of-two head_dim,
-// G <= 16; a rotated or channel-scaled K (hi + lo query) up to head_dim 128.
+// G <= 16; a rotated or channel-scaled K (hi + lo query) up to head_dim 128;
+// and int4 codes at head_dim 192 with a K that is not rotated.
 bool bits_mfma_ok(const otq_cache* c, int G)
 {
-    return otq::split_bits_mfma_supports(c->head_dim, G, code_bits(c), c->k_rot_signs || c->k_chan_scale);
+    return otq::split_bits_mfma_supports(c->head_dim, G, code_bits(c), c->k_rot_signs != nullptr,
+                                         c->k_chan_scale != nullptr);
+}
+
+// The split pass is the b-bit matrix-core kernel: b-bit codes, or int4 at
+// the wide widths.
+bool takes_bits_mfma(const otq_cache* c, int variant)
+{
+    return variant == OTQ_VARIANT_MFMA && (code_bits(c) != 4 || !pow2_dim(c->head_dim));
 }
 
 int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
@@ -152,9 +161,11 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     if (G > 16) return OTQ_EUNSUPPORTED;
 
     int variant = variant_ov;
-    if (!pow2_dim(D)) {  // the wide split pass is vector arithmetic, any G <= 16
-        if (variant == OTQ_VARIANT_AUTO) variant = OTQ_VARIANT_VECTOR;
-        if (variant == OTQ_VARIANT_MFMA) return OTQ_EUNSUPPORTED;
+    if (!pow2_dim(D)) {
+        // the wide widths: the matrix-core pass for a K that is not rotated,
+        // the vector pass (any G <= 16) for every cache
+        if (variant == OTQ_VARIANT_AUTO) variant = bits_mfma_ok(c, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
+        if (variant == OTQ_VARIANT_MFMA && !bits_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_AUTO) {
         // the MFMA variant is the faster one at every measured G (1, 2, 4, 8)
         // (2- and 3-bit codes too, on a K that is neither rotated nor channel-scaled)
@@ -163,7 +174,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
                                      : OTQ_VARIANT_VECTOR;
     }
     if (!pow2_dim(D)) {
-        if (variant != OTQ_VARIANT_VECTOR) return OTQ_EINVAL;
+        if (variant != OTQ_VARIANT_VECTOR && variant != OTQ_VARIANT_MFMA) return OTQ_EINVAL;
     } else if (code_bits(c) != 4) {  // the b-bit split passes: vector (any), MFMA (plain K)
         if (variant == OTQ_VARIANT_MFMA) {
             if (!bits_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
@@ -184,7 +195,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
     if (chunk == 0) {
         long long units = (long long)c->batch * c->num_kv_heads;
         int waves = 4, align = kChunkAlign;
-        if (variant == OTQ_VARIANT_MFMA && code_bits(c) == 4) {
+        if (variant == OTQ_VARIANT_MFMA && !takes_bits_mfma(c, variant)) {
             units /= otq::split_mfma_heads_per_wave(D, G, c->num_kv_heads);
             waves = otq::split_mfma_block_waves(D);
             align = waves * OTQ_TILE;  // one tile per wave and round
@@ -198,7 +209,7 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
         // the b-bit MFMA pass (one KV head per block) is measured fastest
         // with two waves per SIMD: on the 70B layer at 128K (2-bit codes),
         // 32.8 us at chunk 2048 against 37.3 us at 1024
-        const bool bits_mfma = code_bits(c) != 4 && variant == OTQ_VARIANT_MFMA;
+        const bool bits_mfma = takes_bits_mfma(c, variant);
         // so is the int4 pass at head_dim 256 (one KV head per wave): on the
         // Gemma-shaped layer (16 KV heads, 64K tokens) 63.1 us at chunk 2048
         // against 63.9-64.6 us at 4096
@@ -427,8 +438,9 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
     if (ordered_batch(a.B)) {
         const int G = num_q_heads / a.H;
         const int groups = chk.variant != OTQ_VARIANT_MFMA ? a.H
-                           : code_bits(cache) == 4     ? a.H / otq::split_mfma_heads_per_wave(D, G, a.H)
-                                                       : a.H / otq::split_bits_mfma_heads_per_wave(D, G, a.H, a.signs || a.lam);
+                           : !takes_bits_mfma(cache, chk.variant)
+                               ? a.H / otq::split_mfma_heads_per_wave(D, G, a.H)
+                               : a.H / otq::split_bits_mfma_heads_per_wave(D, G, a.H, a.signs || a.lam);
         int2* items = reinterpret_cast<int2*>(static_cast<char*>(workspace) +
                                               order_offset(cache, num_q_heads, chk));
         if (otq::launch_split_order(lens, lens_offset, max_len, chk.chunk, chk.num_splits, groups, a.B,
@@ -436,7 +448,8 @@ int run_split(const void* q, int32_t dtype, int32_t num_q_heads, const otq_cache
             return OTQ_EDEVICE;
         a.items = items;
     }
-    const hipError_t e = !pow2_dim(D)            ? otq::launch_split_wide(a, s)
+    const hipError_t e = takes_bits_mfma(cache, chk.variant) ? otq::launch_split_bits_mfma(a, code_bits(cache), s)
+                         : !pow2_dim(D)                      ? otq::launch_split_wide(a, s)
                          : code_bits(cache) != 4 ? (chk.variant == OTQ_VARIANT_MFMA
                                                         ? otq::launch_split_bits_mfma(a, code_bits(cache), s)
                                                         : otq::launch_split_bits(a, code_bits(cache), s))

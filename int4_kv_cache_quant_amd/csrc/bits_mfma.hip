@@ -67,16 +67,16 @@ using namespace mfma;
 
 constexpr int kB2Waves = 4;  // waves per block
 // Tiles each wave holds in registers ahead of the one it computes (one at
-// head_dim 256 and for two KV heads per wave, whose tiles take twice the
-// registers).
-template <int D, int P>
-constexpr int kB2Ahead = (D == 256 || P == 2) ? 1 : 2;
+// head_dim 256, for two KV heads per wave, whose tiles take twice the
+// registers, and for the hi + lo query at head_dim 192).
+template <int D, int P, bool HILO>
+constexpr int kB2Ahead = (D == 256 || P == 2 || (D == 192 && HILO)) ? 1 : 2;
 // Where the score accumulator starts at the offset correction (a register
 // quad per group, live through the loop) rather than taking it after the
 // MFMA: everywhere but head_dim 256 and two heads per wave, whose registers
 // are full.
 template <int D, int P, bool HILO>
-constexpr bool kB2QinitInAcc = D != 256 && P == 1 && !HILO;
+constexpr bool kB2QinitInAcc = D != 256 && D != 192 && P == 1 && !HILO;
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
@@ -194,16 +194,17 @@ __device__ __forceinline__ half8_t unpack_v3(uint32_t x)
 
 // The power of two (log2) that slot pair m of an unpacked V word carries.
 template <int BITS>
-constexpr int kVExp[4] = {0, BITS == 2 ? 2 : 3, BITS == 2 ? 4 : 6, BITS == 2 ? 6 : 0};
+constexpr int kVExp[4] = {0, BITS == 2 ? 2 : BITS == 3 ? 3 : 4, BITS == 2 ? 4 : BITS == 3 ? 6 : 0,
+                          BITS == 2 ? 6 : BITS == 3 ? 0 : 4};
 
 template <int D, int BITS, int P, bool HILO>
 __global__ __launch_bounds__(64 * kB2Waves) __attribute__((amdgpu_waves_per_eu(2, D == 64 ? 4 : 2)))
 void split_bits_mfma_kernel(SplitArgs a)
 {
-    static_assert(BITS == 2 || BITS == 3, "2- or 3-bit codes");
+    static_assert(BITS == 2 || BITS == 3 || (BITS == 4 && D == 192), "2- or 3-bit codes, or int4 at 192");
     using T = BTile<D, BITS>;
     using SG = BStage<D, BITS, P>;
-    using VT = VBitsTile<D, BITS>;
+    using VT = VBitsTile<D, BITS == 4 ? 2 : BITS>;  // (b-bit V tiles only)
     constexpr int NG = T::NG, NCB = D / 16, RB = T::RB, W = kB2Waves;
     extern __shared__ __align__(16) char lds[];  // W stages of SG::BYTES
 
@@ -262,7 +263,7 @@ void split_bits_mfma_kernel(SplitArgs a)
             src_stride[k] = NG * 4;
         }
     }
-    constexpr int AH = kB2Ahead<D, P>;
+    constexpr int AH = kB2Ahead<D, P, HILO>;
     u32x4_t pf[AH][SG::LOADS];
     auto load_tile = [&](u32x4_t (&dst)[SG::LOADS], int it) {
         const int tok0 = start + it * kTile;
@@ -296,13 +297,15 @@ void split_bits_mfma_kernel(SplitArgs a)
     // channel scale; such a q is not exact in fp16 and enters as hi + lo
     const bool rot = HILO && a.signs != nullptr;
     if constexpr (HILO) {
-        if (rot) {
+        if (D != 192 && rot) {  // (a rotated K at head_dim 192 takes the vector pass)
 #pragma unroll
             for (int g = 0; g < NG; ++g)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qx[g][e] *= a.signs[32 * g + 8 * r + e];
-            if (a.rot_kind) srft_query<NG>(qx, r);
-            else fwht_query<NG>(qx, r);
+            if constexpr (D != 192) {
+                if (a.rot_kind) srft_query<NG>(qx, r);
+                else fwht_query<NG>(qx, r);
+            }
         }
         if (a.lam) {
 #pragma unroll
@@ -338,7 +341,7 @@ void split_bits_mfma_kernel(SplitArgs a)
             for (int h = 0; h < 2; ++h) {
                 const float xs = __builtin_ldexpf(qx[g][k + 4 * h], qk);
                 const _Float16 v = (_Float16)xs;
-                const int pe = BITS == 2 ? 2 * k : kK3Exp[k];
+                const int pe = BITS == 2 ? 2 * k : BITS == 3 ? kK3Exp[k] : 4 * (k & 1);
                 qb[g][2 * k + h] = (_Float16)((float)v * __builtin_ldexpf(1.0f, -pe));
                 tq += (float)v;
                 if constexpr (HILO) {
@@ -425,7 +428,9 @@ void split_bits_mfma_kernel(SplitArgs a)
                 for (int j = 0; j < P; ++j) {
                     const char* krow = stage + j * T::BYTES + T::KOFF + (16 * s + n16) * RB;
                     half8_t A;
-                    if constexpr (BITS == 2) {
+                    if constexpr (BITS == 4) {  // quarter-interleaved int4 row: word r NG + g
+                        A = unpack_codes_sub(*reinterpret_cast<const uint32_t*>(krow + 4 * (r * NG + g)));
+                    } else if constexpr (BITS == 2) {
                         A = unpack_k2(*reinterpret_cast<const uint32_t*>(krow + 4 * (2 * g + (r >> 1))), ksel);
                     } else {
                         // the word after the field's first lies inside the stage
@@ -510,11 +515,19 @@ void split_bits_mfma_kernel(SplitArgs a)
 
         // ---- values: the lane's words of the V tile (channel column n16 of
         //      every block, tokens 4 r + m and 16 + 4 r + m in the two halves)
-        uint32_t vw[P][VT::WPL];
+        constexpr int VW = BITS == 4 ? NCB : VT::WPL;  // words per lane and head
+        uint32_t vw[P][VW];
 #pragma unroll
         for (int j = 0; j < P; ++j) {
             const char* src = stage + j * T::BYTES + T::VOFF + lane * 4 * VT::WPL;
-            if constexpr (VT::WPL % 4 == 0) {
+            if constexpr (BITS == 4) {  // int4 V tile: block cb = 4 a + b in word ((4 a + r) 16 + n) 4 + b
+#pragma unroll
+                for (int a4 = 0; a4 < NCB / 4; ++a4) {
+                    const u32x4_t w = *reinterpret_cast<const u32x4_t*>(stage + j * T::BYTES + T::VOFF +
+                                                                         16 * ((a4 * 4 + r) * 16 + n16));
+                    vw[j][4 * a4] = w.x; vw[j][4 * a4 + 1] = w.y; vw[j][4 * a4 + 2] = w.z; vw[j][4 * a4 + 3] = w.w;
+                }
+            } else if constexpr (VT::WPL % 4 == 0) {
 #pragma unroll
                 for (int k = 0; k < VT::WPL; k += 4) {
                     const u32x4_t w = *reinterpret_cast<const u32x4_t*>(src + 4 * k);
@@ -550,7 +563,9 @@ void split_bits_mfma_kernel(SplitArgs a)
                 static_for<2>([&](auto hI) {
                     constexpr int cb = 2 * g + decltype(hI)::value;
                     half8_t B;
-                    if constexpr (BITS == 2) {
+                    if constexpr (BITS == 4) {
+                        B = unpack_codes_signed(vw[j][cb]);
+                    } else if constexpr (BITS == 2) {
                         B = unpack_v2((cb & 1) ? (vw[j][cb >> 1] >> 8) : vw[j][cb >> 1]);
                     } else {
                         constexpr int qd = cb >> 2, t = cb & 3;
@@ -639,15 +654,18 @@ void split_bits_mfma_kernel(SplitArgs a)
 int split_bits_mfma_heads_per_wave(int D, int G, int H, bool hilo)
 {
     if (hilo) return 1;  // the hi + lo query takes the registers of a second head
-    return (D != 256 && G >= 4 && G <= 8 && H % 2 == 0) ? 2 : 1;
+    return (D != 256 && D != 192 && G >= 4 && G <= 8 && H % 2 == 0) ? 2 : 1;
 }
 
-bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k)
+bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_k, bool scaled_k)
 {
+    if (G < 1 || G > 16) return false;
+    // int4 codes at head_dim 192: a plain or channel-scaled K (the FFT
+    // rotation of that width is not among the query transforms here)
+    if (D == 192) return bits == 4 && !rotated_k;
     // a rotated or channel-scaled K (hi + lo query) up to head_dim 128, whose
     // registers leave room for it
-    return (D == 64 || D == 128 || D == 256) && G >= 1 && G <= 16 && (bits == 2 || bits == 3) &&
-           !(rotated_or_scaled_k && D == 256);
+    return (D == 64 || D == 128 || D == 256) && (bits == 2 || bits == 3) && !((rotated_k || scaled_k) && D == 256);
 }
 
 namespace {
@@ -670,6 +688,8 @@ hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 {
     if constexpr (D != 256) {
         if (a.signs || a.lam) return launch_bp<D, BITS, 1, true>(a, stream);
+    }
+    if constexpr (D != 256 && D != 192) {
         if (split_bits_mfma_heads_per_wave(D, a.Hq / a.H, a.H, false) == 2)
             return launch_bp<D, BITS, 2, false>(a, stream);
     }
@@ -680,7 +700,9 @@ hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 
 hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream)
 {
-    if (((a.signs || a.lam) && a.D == 256) || a.Hq / a.H > 16) return hipErrorInvalidValue;
+    if (((a.signs || a.lam) && a.D == 256) || (a.signs && a.D == 192) || a.Hq / a.H > 16 ||
+        (a.D == 192) != (bits == 4))
+        return hipErrorInvalidValue;
     switch (a.D * 10 + bits) {
     case 642: return launch_b<64, 2>(a, stream);
     case 643: return launch_b<64, 3>(a, stream);
@@ -688,6 +710,7 @@ hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stre
     case 1283: return launch_b<128, 3>(a, stream);
     case 2562: return launch_b<256, 2>(a, stream);
     case 2563: return launch_b<256, 3>(a, stream);
+    case 1924: return launch_b<192, 4>(a, stream);  // int4 codes at head_dim 192
     default: return hipErrorInvalidValue;
     }
 }

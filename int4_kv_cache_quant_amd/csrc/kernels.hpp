@@ -69,8 +69,9 @@ hipError_t launch_quantize_bits(const void* k, const void* v, int dtype, int n_n
                                 const int32_t* pos, const BitsRot& rot, unsigned* err, hipStream_t stream);
 hipError_t launch_split_bits(const SplitArgs& a, int bits, hipStream_t stream);
 // 2- and 3-bit codes on the matrix cores (head_dim 64, 128, 256; G <= 16; a
-// rotated or channel-scaled K up to head_dim 128).
-bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_or_scaled_k);
+// rotated or channel-scaled K up to head_dim 128), and int4 codes at head_dim
+// 192 (K plain or channel-scaled).
+bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_k, bool scaled_k);
 int split_bits_mfma_heads_per_wave(int D, int G, int H, bool hilo);
 hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream);
 

@@ -78,57 +78,6 @@ namespace {
 
 using namespace mfma;
 
-// MFMA k-slot e of an unpacked word holds element kSlot[e] (0..7) of the
-// word, scaled by 2^kShift[e] (times 2^-24 for the subnormal form):
-// registers are (0,4), (1,5), (2,6), (3,7), each one mask of the word or of
-// the word shifted by 8 bits.
-constexpr int kSlot[8] = {0, 4, 1, 5, 2, 6, 3, 7};
-constexpr int kShift[8] = {0, 0, 4, 4, 0, 0, 4, 4};
-
-// 8 signed nibbles -> 8 fp16 subnormals (c + 8) * 2^(kShift[e] - 24) (the K
-// operand of the score products).
-__device__ __forceinline__ half8_t unpack_codes_sub(uint32_t w)
-{
-    const uint32_t w8 = w >> 8;
-    uint32_t r[4];
-    r[0] = (w ^ 0x88888888u) & 0x000F000Fu;
-    r[1] = (w ^ 0x88888888u) & 0x00F000F0u;
-    r[2] = (w8 ^ 0x00888888u) & 0x000F000Fu;
-    r[3] = (w8 ^ 0x00888888u) & 0x00F000F0u;
-    half8_t out;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        const half2_t p = __builtin_bit_cast(half2_t, r[m]);
-        out[2 * m] = p[0];
-        out[2 * m + 1] = p[1];
-    }
-    return out;
-}
-
-// 8 signed nibbles -> 8 normal fp16 values c * 2^kShift[e] (exact): the
-// offset-binary value n = c + 8 of a nibble goes into the mantissa of 1024.0
-// (0x6400, ulp 1), at bit 0 (1024 + n) or bit 4 (1024 + 16 n); one packed
-// subtraction of 1032 or 1152 then leaves c or 16 c.  One and-xor per
-// register, as for the subnormal form, plus one packed fp16 subtraction.
-__device__ __forceinline__ half8_t unpack_codes_signed(uint32_t w)
-{
-    const uint32_t w8 = w >> 8;
-    const half2_t b0 = half2_t{(_Float16)1032.0f, (_Float16)1032.0f};
-    const half2_t b4 = half2_t{(_Float16)1152.0f, (_Float16)1152.0f};
-    half2_t h[4];
-    h[0] = __builtin_bit_cast(half2_t, (w & 0x000F000Fu) ^ 0x64086408u) - b0;   // elements 0, 4
-    h[1] = __builtin_bit_cast(half2_t, (w & 0x00F000F0u) ^ 0x64806480u) - b4;   // elements 1, 5
-    h[2] = __builtin_bit_cast(half2_t, (w8 & 0x000F000Fu) ^ 0x64086408u) - b0;  // elements 2, 6
-    h[3] = __builtin_bit_cast(half2_t, (w8 & 0x00F000F0u) ^ 0x64806480u) - b4;  // elements 3, 7
-    half8_t out;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-        out[2 * m] = h[m][0];
-        out[2 * m + 1] = h[m][1];
-    }
-    return out;
-}
-
 // s_waitcnt lgkmcnt(0) with the vector-memory and export counters left
 // unconstrained (gfx9 encoding: vmcnt [3:0] + [15:14], expcnt [6:4],
 // lgkmcnt [11:8]).

@@ -6,7 +6,9 @@ Codes and scales must equal the oracle's bit for bit (plain, K rotated by
 the mixed-radix SRFT, with K's channel scale), appended one token at a time
 at odd and even positions and in chunks; outputs must be within max-abs 2e-3
 and relative L2 1e-3 of the fp64 oracle for every G <= 16, ragged batches
-(longest-first order) and the two-phase calls."""
+(longest-first order) and the two-phase calls, on both split passes: the
+matrix-core one (the default for a K that is not rotated) and the vector one
+(any cache; the default for a rotated K)."""
 import math
 
 import numpy as np
@@ -85,13 +87,15 @@ def test_wide_single_tokens_scattered_keep_neighbours():
 
 
 def _sdpa(B, G, Hkv, cap, lens, rotate=False, scaled=False, seed=0, chunk=0, dtype=torch.bfloat16,
-          two_phase=False):
+          two_phase=False, variant=otq.OTQ_VARIANT_AUTO):
     T = max(lens)
     k, v, q = _inputs(B, Hkv, cap, G, seed=seed, dtype=dtype)
     cache, signs, lam = _cache(B, Hkv, cap, rotate, scaled, seed=seed + 50)
     _fill(cache, k, v, T, 1000)
     lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
-    plan = cache.plan(G * Hkv, T, chunk=chunk)
+    plan = cache.plan(G * Hkv, T, chunk=chunk, variant=variant)
+    assert plan.variant == (variant if variant != otq.OTQ_VARIANT_AUTO
+                            else otq.OTQ_VARIANT_VECTOR if rotate else otq.OTQ_VARIANT_MFMA)
     say(f"wide sdpa B={B} G={G} Hkv={Hkv} lens={lens[:6]} rotate={rotate} scaled={scaled} "
         f"chunk={plan.chunk} splits={plan.num_splits} variant={plan.variant}")
     scale = 1.0 / math.sqrt(D)
@@ -120,32 +124,47 @@ def _sdpa(B, G, Hkv, cap, lens, rotate=False, scaled=False, seed=0, chunk=0, dty
     return plan
 
 
+VEC, MF = otq.OTQ_VARIANT_VECTOR, otq.OTQ_VARIANT_MFMA
+
+
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8, 16])
-@pytest.mark.parametrize("rotate,scaled", [(False, False), (True, False), (True, True)])
-def test_wide_sdpa_parity(G, rotate, scaled):
+@pytest.mark.parametrize("rotate,scaled,variant", [(False, False, 0), (False, False, VEC), (True, False, 0),
+                                                   (True, True, 0), (False, True, 0), (False, True, VEC)])
+def test_wide_sdpa_parity(G, rotate, scaled, variant):
     plan = _sdpa(2, G, 2, 640, [600, 131], rotate=rotate, scaled=scaled, seed=G + 10 * rotate + scaled,
-                 chunk=128)
-    assert plan.variant == otq.OTQ_VARIANT_VECTOR and plan.num_splits == 5
+                 chunk=128, variant=variant)
+    assert plan.num_splits == 5
 
 
 @pytest.mark.parametrize("lens", [[0, 1], [31, 32], [33, 256], [257, 0]])
-def test_wide_sdpa_edge_lengths(lens):
-    _sdpa(2, 4, 2, 320, lens, rotate=True, seed=sum(lens), chunk=128)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_wide_sdpa_edge_lengths(lens, rotate):
+    _sdpa(2, 4, 2, 320, lens, rotate=rotate, seed=sum(lens), chunk=128)
 
 
-def test_wide_sdpa_fp16_and_default_plan():
-    _sdpa(1, 8, 2, 2048, [2000], rotate=True, seed=77, dtype=torch.float16)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_wide_sdpa_fp16_and_default_plan(rotate):
+    _sdpa(1, 8, 2, 2048, [2000], rotate=rotate, seed=77, dtype=torch.float16)
 
 
-def test_wide_sdpa_ragged_batch_in_longest_first_order():
+@pytest.mark.parametrize("rotate", [True, False])
+def test_wide_sdpa_ragged_batch_in_longest_first_order(rotate):
     lens = [0, 1, 128, 129, 383, 256, 32, 300, 127, 384, 255, 2]
-    _sdpa(len(lens), 4, 2, 384, lens, rotate=True, seed=21, chunk=128)
+    _sdpa(len(lens), 4, 2, 384, lens, rotate=rotate, seed=21, chunk=128)
 
 
-def test_wide_two_phase_calls():
-    _sdpa(3, 8, 2, 512, [500, 77, 256], rotate=True, scaled=True, seed=33, chunk=128, two_phase=True)
+@pytest.mark.parametrize("rotate,scaled", [(True, True), (False, True)])
+def test_wide_two_phase_calls(rotate, scaled):
+    _sdpa(3, 8, 2, 512, [500, 77, 256], rotate=rotate, scaled=scaled, seed=33, chunk=128, two_phase=True)
 
 
-def test_wide_long_context():
-    """One sequence of 16384 tokens, K rotated, default plan (many splits)."""
-    _sdpa(1, 8, 2, 16384, [16384], rotate=True, seed=91)
+@pytest.mark.parametrize("rotate", [True, False])
+def test_wide_long_context(rotate):
+    """One sequence of 16384 tokens, default plan (many splits)."""
+    _sdpa(1, 8, 2, 16384, [16384], rotate=rotate, seed=91)
+
+
+def test_wide_mfma_rejects_a_rotated_k():
+    cache, _, _ = _cache(1, 2, 64, True, False, seed=1)
+    with pytest.raises(otq.OtqError):
+        cache.plan(8, 64, variant=MF)

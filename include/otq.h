@@ -53,7 +53,7 @@ typedef enum otq_status {
     OTQ_OK = 0,
     OTQ_EINVAL = -1,       /* null pointer, bad count, Hq % Hkv != 0, ...      */
     OTQ_ECAPACITY = -2,    /* max_len or n_new larger than the cache capacity */
-    OTQ_EUNSUPPORTED = -3, /* head_dim not in {64,128,256}, bad dtype, G > 16  */
+    OTQ_EUNSUPPORTED = -3, /* head_dim not in {64,128,192,256}, bad dtype, G>16 */
     OTQ_EWORKSPACE = -4,   /* workspace null or smaller than required          */
     OTQ_EDEVICE = -5       /* a HIP launch failed                              */
 } otq_status;
@@ -91,6 +91,15 @@ typedef enum otq_rot_kind {
  * step is one fp32 operation, the complex product (dr wr - di wi, dr wi +
  * di wr) with products rounded before the sum, and the twiddles (wr, wi)
  * are the correctly rounded fp32 cos and -sin of 2 pi t / N.
+ * head_dim 192 (N = 96 = 3 * 32; int4 codes only, K rotated by the FFT kind
+ * only, V not rotated, no fused append) takes the mixed-radix form of the
+ * same FFT ("SRFT + int4 KV-cache" page, core method: mixed radix for widths
+ * that are not powers of two): first a radix-3 stage, output position
+ * 32 m + j (m = 0, 1, 2; j < 32) from a_i = z_j+32i with u = a_0 - 0.5 (a_1 +
+ * a_2) and t = fp32(sqrt(3)/2) (a_1 - a_2): a_0 + a_1 + a_2, (u - i t) W^j
+ * and (u + i t) W^2j; then, inside each block of 32, the radix-2 stages of
+ * half-size h = 16, ..., 1 as above with t = (j mod h) 96 / (2h); W =
+ * exp(-2 pi i / 96); rot_norm = fp32(1/sqrt(96)).
  * The query is rotated the same way inside otq_sdpa_int4_decode, so scores
  * are unchanged by the rotation.
  * K only, when k_chan_scale != NULL (a per-coordinate scale lambda applied
@@ -153,7 +162,7 @@ typedef enum otq_rot_kind {
 typedef struct otq_cache {
     int32_t batch;
     int32_t num_kv_heads;
-    int32_t head_dim;      /* 64, 128 or 256 */
+    int32_t head_dim;      /* 64, 128, 256, or 192 (int4 codes, see above) */
     int32_t capacity;      /* tokens per sequence, multiple of OTQ_TILE, >= 32 */
     uint8_t *k_codes;
     float *k_scales;

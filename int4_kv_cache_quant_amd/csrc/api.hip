@@ -135,7 +135,7 @@ bool ordered_batch(int32_t B) { return B > 1 && B <= otq::kOrderMaxBatch; }
 
 // The b-bit MFMA split pass: 2- or 3-bit codes, power-of-two head_dim,
 // G <= 16; a rotated or channel-scaled K (hi + lo query) up to head_dim 128;
-// and int4 codes at head_dim 192 with a K that is not rotated.
+// and int4 codes at head_dim 192 (any K the cache takes there).
 bool bits_mfma_ok(const otq_cache* c, int G)
 {
     return otq::split_bits_mfma_supports(c->head_dim, G, code_bits(c), c->k_rot_signs != nullptr,
@@ -162,8 +162,8 @@ int make_plan(int32_t Hq, const otq_cache* c, int32_t max_len, int32_t chunk_ov,
 
     int variant = variant_ov;
     if (!pow2_dim(D)) {
-        // the wide widths: the matrix-core pass for a K that is not rotated,
-        // the vector pass (any G <= 16) for every cache
+        // the wide widths: the matrix-core pass by default, the vector pass
+        // (any G <= 16) when asked for
         if (variant == OTQ_VARIANT_AUTO) variant = bits_mfma_ok(c, G) ? OTQ_VARIANT_MFMA : OTQ_VARIANT_VECTOR;
         if (variant == OTQ_VARIANT_MFMA && !bits_mfma_ok(c, G)) return OTQ_EUNSUPPORTED;
     } else if (variant == OTQ_VARIANT_AUTO) {

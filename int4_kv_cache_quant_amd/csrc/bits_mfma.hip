@@ -33,10 +33,18 @@
 //    exactly), undone in the softmax scale;
 //  * x = p * s_v * 2^E is split into fp16 hi + lo operands; E follows the
 //    largest V scale seen, as in the int4 pass.
-// A rotated or channel-scaled K (head_dim up to 128) takes q rotated as K
+// A rotated or channel-scaled K (head_dim up to 192) takes q rotated as K
 // was and divided by the channel scale, as fp16 hi + lo operands (two score
 // products per group, one KV head per wave); at head_dim 256 such caches take
 // the vector split pass.  A rotated V is undone by the combine.
+//
+// Int4 caches at head_dim 192 (six groups, twelve channel blocks; the FFT
+// rotation of that width is mixed radix) take this kernel as well: K words
+// are the int4 rows' words (word 6 r + g holds channels 32 g + 8 r + 0..7),
+// unpacked to subnormals as in the int4 pass,
+// and V words the int4 tile words (tokens 4 r + m and 16 + 4 r + m in
+// nibbles m and 4 + m), with 2^(4 (k & 1)) as the k-slot powers; one KV head
+// per wave.
 //
 // Block = 4 waves, one (split, P KV heads, sequence): P = 2 when 4 <= G <= 8
 // (the two heads' query heads fill the 16 MFMA columns), else 1; wave w takes
@@ -297,12 +305,14 @@ void split_bits_mfma_kernel(SplitArgs a)
     // channel scale; such a q is not exact in fp16 and enters as hi + lo
     const bool rot = HILO && a.signs != nullptr;
     if constexpr (HILO) {
-        if (D != 192 && rot) {  // (a rotated K at head_dim 192 takes the vector pass)
+        if (rot) {
 #pragma unroll
             for (int g = 0; g < NG; ++g)
 #pragma unroll
                 for (int e = 0; e < 8; ++e) qx[g][e] *= a.signs[32 * g + 8 * r + e];
-            if constexpr (D != 192) {
+            if constexpr (D == 192) {
+                srft_query192(qx, r);  // the FFT kind only at this width
+            } else {
                 if (a.rot_kind) srft_query<NG>(qx, r);
                 else fwht_query<NG>(qx, r);
             }
@@ -660,9 +670,8 @@ int split_bits_mfma_heads_per_wave(int D, int G, int H, bool hilo)
 bool split_bits_mfma_supports(int D, int G, int bits, bool rotated_k, bool scaled_k)
 {
     if (G < 1 || G > 16) return false;
-    // int4 codes at head_dim 192: a plain or channel-scaled K (the FFT
-    // rotation of that width is not among the query transforms here)
-    if (D == 192) return bits == 4 && !rotated_k;
+    // int4 codes at head_dim 192 (a rotated K there is FFT-rotated)
+    if (D == 192) return bits == 4;
     // a rotated or channel-scaled K (hi + lo query) up to head_dim 128, whose
     // registers leave room for it
     return (D == 64 || D == 128 || D == 256) && (bits == 2 || bits == 3) && !((rotated_k || scaled_k) && D == 256);
@@ -700,7 +709,7 @@ hipError_t launch_b(const SplitArgs& a, hipStream_t stream)
 
 hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stream)
 {
-    if (((a.signs || a.lam) && a.D == 256) || (a.signs && a.D == 192) || a.Hq / a.H > 16 ||
+    if (((a.signs || a.lam) && a.D == 256) || (a.signs && a.D == 192 && a.rot_kind != 1) || a.Hq / a.H > 16 ||
         (a.D == 192) != (bits == 4))
         return hipErrorInvalidValue;
     switch (a.D * 10 + bits) {

@@ -146,6 +146,86 @@ __device__ __forceinline__ void srft_query(float (&qx)[NG][8], int r)
     }
 }
 
+// The query's mixed-radix FFT at head_dim 192 (N = 96 = 3 * 32 complex
+// numbers; without rot_norm) in the same layout, complex j = 16 g + 4 r +
+// e / 2 in qx[g][e], g < 6.  The radix-3 stage combines j, j + 32, j + 64:
+// groups g, g + 2, g + 4 of the lane, its outputs m = 0, 1, 2 going to
+// groups g + 2 m.  Inside each block of 32 (groups 2 m, 2 m + 1) the radix-2
+// stages of half-size 16 pair the block's two groups, 8 and 4 pair lanes 32
+// and 16 apart, 2 and 1 stay in the 8-channel run; twiddle index (j mod h)
+// 96 / (2 h).
+__device__ __forceinline__ void srft_query192(float (&qx)[6][8], int r)
+{
+    using srft_detail::kC3;
+    using srft_detail::kTw96;
+    auto cmul = [](float& xr, float& xi, int u) {
+        const float wr = kTw96.re[u], wi = kTw96.im[u];
+        const float pr = xr * wr - xi * wi, pi = xr * wi + xi * wr;
+        xr = pr;
+        xi = pi;
+    };
+    auto bfly = [&](float& ar, float& ai, float& br, float& bi, int u) {
+        float dr = ar - br, di = ai - bi;
+        ar = ar + br;
+        ai = ai + bi;
+        cmul(dr, di, u);
+        br = dr;
+        bi = di;
+    };
+#pragma unroll
+    for (int g0 = 0; g0 < 2; ++g0)
+#pragma unroll
+        for (int cp = 0; cp < 4; ++cp) {
+            const int j = 16 * g0 + 4 * r + cp;
+            float& a0r = qx[g0][2 * cp];
+            float& a0i = qx[g0][2 * cp + 1];
+            float& a1r = qx[g0 + 2][2 * cp];
+            float& a1i = qx[g0 + 2][2 * cp + 1];
+            float& a2r = qx[g0 + 4][2 * cp];
+            float& a2i = qx[g0 + 4][2 * cp + 1];
+            const float sr = a1r + a2r, si = a1i + a2i, dr = a1r - a2r, di = a1i - a2i;
+            const float mr = a0r - 0.5f * sr, mi = a0i - 0.5f * si;
+            const float tr = kC3 * dr, ti = kC3 * di;
+            a0r = a0r + sr;
+            a0i = a0i + si;
+            a1r = mr + ti;  // (m - i t) W^j
+            a1i = mi - tr;
+            cmul(a1r, a1i, j);
+            a2r = mr - ti;  // (m + i t) W^2j
+            a2i = mi + tr;
+            cmul(a2r, a2i, 2 * j);
+        }
+#pragma unroll
+    for (int m = 0; m < 3; ++m)
+#pragma unroll
+        for (int cp = 0; cp < 4; ++cp)  // h = 16: block position 4 r + cp with 16 + 4 r + cp
+            bfly(qx[2 * m][2 * cp], qx[2 * m][2 * cp + 1], qx[2 * m + 1][2 * cp], qx[2 * m + 1][2 * cp + 1],
+                 3 * (4 * r + cp));
+#pragma unroll
+    for (int h = 8; h >= 4; h >>= 1) {  // lanes 32 (r bit 1) and 16 (r bit 0) apart
+        const int lm = h == 8 ? 32 : 16;
+        const bool upper = (r & (h / 4)) != 0;
+#pragma unroll
+        for (int g = 0; g < 6; ++g)
+#pragma unroll
+            for (int cp = 0; cp < 4; ++cp) {
+                const float ore = shfl_xor(qx[g][2 * cp], lm), oim = shfl_xor(qx[g][2 * cp + 1], lm);
+                float dr = ore - qx[g][2 * cp], di = oim - qx[g][2 * cp + 1];
+                cmul(dr, di, ((4 * r + cp) & (h - 1)) * (96 / (2 * h)));
+                qx[g][2 * cp] = upper ? dr : qx[g][2 * cp] + ore;
+                qx[g][2 * cp + 1] = upper ? di : qx[g][2 * cp + 1] + oim;
+            }
+    }
+#pragma unroll
+    for (int g = 0; g < 6; ++g) {
+        // h = 2: complex 0 with 2, 1 with 3 (W^24 for the odd pair); h = 1
+        bfly(qx[g][0], qx[g][1], qx[g][4], qx[g][5], 0);
+        bfly(qx[g][2], qx[g][3], qx[g][6], qx[g][7], 24);
+        bfly(qx[g][0], qx[g][1], qx[g][2], qx[g][3], 0);
+        bfly(qx[g][4], qx[g][5], qx[g][6], qx[g][7], 0);
+    }
+}
+
 // The query's Walsh-Hadamard rotation (without rot_norm, which the score
 // multiplier carries) in the split kernels' query layout: lane (n16, r)
 // holds channels 32 g + 8 r + e in qx[g][e].  The butterflies over channel

@@ -36,42 +36,8 @@ namespace otq {
 namespace {
 
 constexpr float kNegInfW = -__builtin_huge_valf();
-constexpr float kC3 = 0x1.bb67aep-1f;  // fp32(sqrt(3) / 2), correctly rounded
-
-// W_96^t = (cos, -sin)(2 pi t / 96) for t < 96, rounded once from a double
-// Taylor series of the angle reduced to the first octant (quarter turns
-// exact).
-struct Twiddles96 {
-    float re[96];
-    float im[96];
-};
-
-constexpr Twiddles96 make_twiddles96()
-{
-    Twiddles96 t{};
-    for (int u = 0; u < 96; ++u) {
-        const int oct = u / 12, rem = u % 12;       // angle (pi/4) (oct + rem / 12)
-        const int m = (oct & 1) ? 12 - rem : rem;   // odd octants: the complement
-        double c1 = 1.0, s1 = 0.0;
-        if (m != 0) srft_detail::cos_sin(srft_detail::kPi / 4.0 * m / 12.0, c1, s1);
-        double c = 0.0, s = 0.0;
-        switch (oct) {
-        case 0: c = c1; s = s1; break;       // a
-        case 1: c = s1; s = c1; break;       // pi/2 - b
-        case 2: c = -s1; s = c1; break;      // pi/2 + a
-        case 3: c = -c1; s = s1; break;      // pi - b
-        case 4: c = -c1; s = -s1; break;     // pi + a
-        case 5: c = -s1; s = -c1; break;     // 3 pi/2 - b
-        case 6: c = s1; s = -c1; break;      // 3 pi/2 + a
-        default: c = c1; s = -s1; break;     // 2 pi - b
-        }
-        t.re[u] = static_cast<float>(c) + 0.0f;  // zeros are +0
-        t.im[u] = static_cast<float>(-s) + 0.0f;
-    }
-    return t;
-}
-
-static __constant__ Twiddles96 kTw96 = make_twiddles96();
+using srft_detail::kC3;
+using srft_detail::kTw96;
 
 // The complex product (dr wr - di wi, dr wi + di wr), products rounded
 // before the sum; the real part when part == 0, else the imaginary part.

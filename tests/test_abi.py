@@ -335,9 +335,8 @@ def test_noalloc_scratch_limit_on_host():
 def test_head_dim_192_host_checks():
     """head_dim 192 (D/2 = 3 * 32): int4 only, K rotated by the FFT kind only
     (the Hadamard form needs a power of two), V unrotated; the matrix-core
-    split pass for a plain or channel-scaled K, the vector one for every K
-    (the default for a rotated K); no fused append; sizes by the int4 closed
-    form."""
+    split pass by default, the vector one when asked for; no fused append;
+    sizes by the int4 closed form."""
     lib = otq.lib()
     P = ctypes.c_void_p
     cb, sb = otq.otq_cache_array_bytes(2, 3, 192, 64, 4)
@@ -356,8 +355,9 @@ def test_head_dim_192_host_checks():
     r = _desc(D=192, signs=FAKE)
     r.rot_kind = otq.OTQ_ROT_SRFT
     rc, p = plan(r)
+    assert rc == otq.OTQ_OK and p.variant == otq.OTQ_VARIANT_MFMA
+    rc, p = plan(r, otq.OTQ_VARIANT_VECTOR)
     assert rc == otq.OTQ_OK and p.variant == otq.OTQ_VARIANT_VECTOR
-    assert plan(r, otq.OTQ_VARIANT_MFMA)[0] == otq.OTQ_EUNSUPPORTED
     rc, p = otq.otq_sdpa_plan(32, d, 64, variant=otq.OTQ_VARIANT_MFMA, check=False)  # G = 16
     assert rc == otq.OTQ_OK and p.variant == otq.OTQ_VARIANT_MFMA
     r.rot_kind = otq.OTQ_ROT_SRHT

@@ -79,6 +79,13 @@ hipError_t launch_split_bits_mfma(const SplitArgs& a, int bits, hipStream_t stre
 // append (K optionally rotated by the mixed-radix FFT, V optionally too) and
 // the split pass (any G <= 16) for the int4 layouts.
 bool wide_supported_dim(int D);
+// The bulk append kernel at head_dim 192 (8 or more tokens; K plain,
+// channel-scaled or FFT-rotated, V not rotated).
+bool quantize_tile_wide_supports(int D, int n_new, bool v_rotated);
+hipError_t launch_quantize_tile_wide(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
+                                     int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
+                                     const float* signs, float rot_norm, const float* lam, const int32_t* pos,
+                                     unsigned* err, hipStream_t stream);
 hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
                                 int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs, const float* signs,
                                 float rot_norm, const float* lam, const float* vsigns, const int32_t* pos,

@@ -158,6 +158,87 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
     }
 }
 
+// The mixed-radix FFT of one K vector at head_dim 192 (N = 96 = 3 * 32
+// complex numbers), in the bulk kernel's layout: lane j (0..23) of the
+// token holds reals 8 j .. 8 j + 7, complex numbers 4 j + c (c < 4), and zr
+// is the token's row (after the signs) in LDS.  The radix-3 stage (output
+// 32 m + q from complex q, q + 32, q + 64, m = j / 8) reads the row; the
+// radix-2 stages of half-size 16, 8 and 4 inside each block of 32 pair lanes
+// 4, 2 and 1 apart (an aligned group of 8 lanes, never split by a wave),
+// those of 2 and 1 stay in the lane.  The fp32 operations and their order
+// are those of the per-token form in wide.hip, so the codes are the same.
+__device__ __forceinline__ void srft192_lane(float (&x)[8], const float* zr, int j)
+{
+#pragma clang fp contract(off)
+    using srft_detail::kC3;
+    using srft_detail::kTw96;
+    auto cmul = [](float& re, float& im, int u) {
+        const float wr = kTw96.re[u], wi = kTw96.im[u];
+        const float p1 = re * wr, p2 = im * wi, p3 = re * wi, p4 = im * wr;
+        re = p1 - p2;
+        im = p3 + p4;
+    };
+    const int jm = j & 7, m = j >> 3;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+        const int q = 4 * jm + c;
+        const float a0r = zr[2 * q], a0i = zr[2 * q + 1];
+        const float a1r = zr[2 * (q + 32)], a1i = zr[2 * (q + 32) + 1];
+        const float a2r = zr[2 * (q + 64)], a2i = zr[2 * (q + 64) + 1];
+        const float sr = a1r + a2r, si = a1i + a2i;
+        const float dr = a1r - a2r, di = a1i - a2i;
+        const float hr = 0.5f * sr, hi = 0.5f * si;
+        const float mr = a0r - hr, mi = a0i - hi;
+        const float tr = kC3 * dr, ti = kC3 * di;
+        float yr, yi;
+        if (m == 0) {
+            yr = a0r + sr;
+            yi = a0i + si;
+        } else if (m == 1) {  // (m - i t) W^q
+            yr = mr + ti;
+            yi = mi - tr;
+            cmul(yr, yi, q);
+        } else {  // (m + i t) W^2q
+            yr = mr - ti;
+            yi = mi + tr;
+            cmul(yr, yi, 2 * q);
+        }
+        x[2 * c] = yr;
+        x[2 * c + 1] = yi;
+    }
+#pragma unroll
+    for (int h = 16; h >= 4; h >>= 1) {
+        const int lm = h / 4;  // lane distance
+        const bool upper = (jm & lm) != 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const float ore = shfl_xor(x[2 * c], lm), oim = shfl_xor(x[2 * c + 1], lm);
+            if (upper) {
+                float dr = ore - x[2 * c], di = oim - x[2 * c + 1];
+                cmul(dr, di, (((4 * jm + c) & (2 * h - 1)) - h) * (96 / (2 * h)));
+                x[2 * c] = dr;
+                x[2 * c + 1] = di;
+            } else {
+                x[2 * c] = x[2 * c] + ore;
+                x[2 * c + 1] = x[2 * c + 1] + oim;
+            }
+        }
+    }
+#pragma unroll
+    for (int h = 2; h >= 1; h >>= 1)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if ((c & h) == 0) {
+                const float lr = x[2 * c], li = x[2 * c + 1], ur = x[2 * (c + h)], ui = x[2 * (c + h) + 1];
+                float dr = lr - ur, di = li - ui;
+                cmul(dr, di, (((c + h) & (2 * h - 1)) - h) * (96 / (2 * h)));
+                x[2 * c] = lr + ur;
+                x[2 * c + 1] = li + ui;
+                x[2 * (c + h)] = dr;
+                x[2 * (c + h) + 1] = di;
+            }
+}
+
 // One block per 32-token V tile of one head, so that every byte of the tile,
 // of its 32 K rows and of their scales is written from one CU (one L2) as
 // whole words.
@@ -190,11 +271,16 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
                                               uint8_t* __restrict__ vc, float* __restrict__ vs,
                                               const float* __restrict__ signs, float rot_norm,
                                               const float* __restrict__ lam,
-                                              const float* __restrict__ vsigns)
+                                              const float* __restrict__ vsigns, uint32_t* vstage, float* krot)
 {
     constexpr int NG = D / kGroup;
     constexpr int LT = D / 8;  // K lanes per token
     constexpr int U = D / 64;  // K units and V units per thread
+    // at head_dim 192 (24 lanes per token, which may straddle two waves) K's
+    // FFT rotation goes through LDS (srft192_lane) and V is not rotated
+    constexpr bool kRotates = (D & (D - 1)) == 0;
+    constexpr bool kSrft192 = D == 192 && SRFT;
+    static_assert(kRotates || (!VROT && (!SRFT || D == 192)), "head_dim 192: K's FFT rotation only");
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     auto fresh_at = [&](int t) { return FULL || (t >= p0 && t < t_end && t >= 0); };
     auto widen8 = [&](const uint4& q, float (&x)[8]) {
@@ -215,23 +301,29 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
     };
 
     // issue every load first; the K signs and channel scales of a lane are
-    // the same in every unit
-    float sg[8], lm[8], vsg[VROT ? 8 : 1];
+    // the same in every unit when a token's lanes divide the block (LT | 256),
+    // else (head_dim 192) the channel scales are loaded per unit
+    constexpr bool kSameJ = 256 % LT == 0;
+    float sg[kSameJ ? 1 : U][8], lm[kSameJ ? 1 : U][8], vsg[VROT ? 8 : 1];
     if (signs) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sg[e] = signs[8 * (tid % LT) + e];
+        for (int i = 0; i < (kSameJ ? 1 : U); ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sg[i][e] = signs[8 * ((i * 256 + tid) % LT) + e];
     }
     // the FFT rotation's twiddles: the lane's position in its token, hence
     // its twiddles, is the same in every unit
-    [[maybe_unused]] SrftLaneTw<D, 8> stw;
-    if constexpr (SRFT) stw.load(tid % LT);
+    [[maybe_unused]] SrftLaneTw<kRotates ? D : 64, 8> stw;
+    if constexpr (SRFT && kRotates) stw.load(tid % LT);
     if constexpr (VROT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) vsg[e] = vsigns[8 * (tid % LT) + e];
     }
     if (lam) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) lm[e] = lam[8 * (tid % LT) + e];
+        for (int i = 0; i < (kSameJ ? 1 : U); ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) lm[i][e] = lam[8 * ((i * 256 + tid) % LT) + e];
     }
     uint4 kraw[U], vraw[U];
 #pragma unroll
@@ -265,23 +357,44 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
         }
     }
 
+    // head_dim 192, K FFT-rotated: the tile's K rows, signs applied, in LDS
+    // (krot, kTile x D floats) for the radix-3 stage, which reads lanes of
+    // other waves
+    if constexpr (kSrft192) {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int L = i * 256 + tid;
+            float x[8];
+            widen8(kraw[i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) krot[(L / LT) * D + 8 * (L % LT) + e] = x[e] * sg[i][e];
+        }
+        __syncthreads();
+    }
+
     // K: widen, rotate, quantise; one code word and (per group) one scale
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         const int L = i * 256 + tid, t = t_tile + L / LT, j = L % LT;
         float x[8];
         widen8(kraw[i], x);
-        if (signs) {
+        if constexpr (kSrft192) {  // the row staged in LDS (signs applied) above
+            srft192_lane(x, krot + (L / LT) * D, j);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[e];
-            if constexpr (SRFT)
-                srft_signed<D, 8>(x, rot_norm, j, stw);
-            else
-                rotate_signed<D, 8>(x, rot_norm, j);
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * rot_norm;
+        } else if constexpr (kRotates) {
+            if (signs) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = x[e] * sg[0][e];
+                if constexpr (SRFT)
+                    srft_signed<D, 8>(x, rot_norm, j, stw);
+                else
+                    rotate_signed<D, 8>(x, rot_norm, j);
+            }
         }
         if (lam) {  // K's per-channel scale, after the rotation
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = x[e] * lm[e];
+            for (int e = 0; e < 8; ++e) x[e] = x[e] * lm[kSameJ ? 0 : i][e];
         }
         float sk;
         const uint32_t word = quantize_word8(x, sk);
@@ -293,8 +406,8 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
     }
 
     // V rotated: widen, rotate, quantise and store the scales in the K
-    // layout, then stage the code words in LDS (token u, channel block j)
-    __shared__ uint32_t vstage[VROT ? kTile * LT : 1];
+    // layout, then stage the code words in LDS (vstage, kTile x LT words:
+    // token u, channel block j)
     if constexpr (VROT) {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
@@ -365,15 +478,41 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const int t_end = min(p0 + n_new, cap);
     if (t_tile >= t_end) return;  // block-uniform
     const size_t head = (size_t)b * H + h;
+    // LDS of the rotated forms (one array for both instances below)
+    constexpr bool kSrft192 = D == 192 && SRFT;
+    __shared__ uint32_t vstage[VROT ? kTile * (D / 8) : 1];
+    __shared__ float krot[kSrft192 ? kTile * D : 1];
     if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
         quantize_tile<D, DTYPE, true, VROT, SRFT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
-                                            signs, rot_norm, lam, vsigns);
+                                            signs, rot_norm, lam, vsigns, vstage, krot);
     else
         quantize_tile<D, DTYPE, false, VROT, SRFT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
-                                             signs, rot_norm, lam, vsigns);
+                                             signs, rot_norm, lam, vsigns, vstage, krot);
 }
 
 }  // namespace
+
+bool quantize_tile_wide_supports(int D, int n_new, bool v_rotated)
+{
+    return D == 192 && n_new >= kPairKernelMaxTokens && !v_rotated;
+}
+
+hipError_t launch_quantize_tile_wide(const void* k, const void* v, int dtype, int n_new, int B, int H, int D,
+                                     int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,
+                                     const float* signs, float rot_norm, const float* lam, const int32_t* pos,
+                                     unsigned* err, hipStream_t stream)
+{
+    if (!quantize_tile_wide_supports(D, n_new, false)) return hipErrorInvalidValue;
+    const int tiles = (n_new + 2 * kTile - 2) / kTile;  // the range may start inside a tile
+    dim3 grid(tiles, H, B), block(256);
+    const auto* kk = static_cast<const uint16_t*>(k);
+    const auto* vv = static_cast<const uint16_t*>(v);
+    // a K rotation at this width is the FFT kind
+    auto kern = signs ? (dtype == 0 ? quantize_tile_kernel<192, 0, false, true> : quantize_tile_kernel<192, 1, false, true>)
+                      : (dtype == 0 ? quantize_tile_kernel<192, 0, false, false> : quantize_tile_kernel<192, 1, false, false>);
+    kern<<<grid, block, 0, stream>>>(kk, vv, n_new, H, cap, kc, ks, vc, vs, signs, rot_norm, lam, nullptr, pos, err);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_append(const void* k, const void* v, int dtype, int n_new, int B, int H,
                                   int D, int cap, uint8_t* kc, float* ks, uint8_t* vc, float* vs,

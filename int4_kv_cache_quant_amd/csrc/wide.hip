@@ -410,6 +410,9 @@ hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_n
                                 unsigned* err, hipStream_t stream)
 {
     if (D != 192) return hipErrorInvalidValue;
+    if (quantize_tile_wide_supports(D, n_new, vsigns != nullptr))  // one block per tile
+        return launch_quantize_tile_wide(k, v, dtype, n_new, B, H, D, cap, kc, ks, vc, vs, signs, rot_norm, lam, pos,
+                                         err, stream);
     dim3 grid(n_new, H, B), block(192);
     quantize_wide_kernel<192><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(k),
                                                            static_cast<const uint16_t*>(v), dtype, n_new, H,

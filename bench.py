@@ -33,10 +33,10 @@ HBM_PEAK_GBPS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 CSRC = "int4_kv_cache_quant_amd/csrc/"
 KERNEL_SOURCES = {  # the sources a split kernel's traffic summary is tagged with
-    "split_mfma": [CSRC + "sdpa_mfma.hip", CSRC + "mfma_common.hpp", CSRC + "common.hpp"],
+    "split_mfma": [CSRC + "sdpa_mfma.hip", CSRC + "mfma_common.hpp", CSRC + "srft.hpp", CSRC + "common.hpp"],
     "split_vec": [CSRC + "sdpa_vec.hip", CSRC + "common.hpp"],
     "split_bits_mfma": [CSRC + "bits_mfma.hip", CSRC + "bits_layout.hpp", CSRC + "mfma_common.hpp",
-                        CSRC + "common.hpp"],
+                        CSRC + "srft.hpp", CSRC + "common.hpp"],
     "split_bits": [CSRC + "bits.hip", CSRC + "bits_layout.hpp", CSRC + "common.hpp"],
 }
 

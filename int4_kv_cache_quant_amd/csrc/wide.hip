@@ -118,15 +118,19 @@ __global__ __launch_bounds__(D) void quantize_wide_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
     const float* __restrict__ signs, float rot_norm, const float* __restrict__ lam,
-    const float* __restrict__ vsigns, const int32_t* __restrict__ pos, unsigned* __restrict__ err)
+    const float* __restrict__ vsigns, const int32_t* __restrict__ pos, unsigned* __restrict__ err,
+    const int32_t* __restrict__ lens, int max_len)
 {
 #pragma clang fp contract(off)
     constexpr int NG = D / kGroup;
     __shared__ float xch[D];
     const int tok = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int ch = threadIdx.x, lane = ch & 63;
-    const int p0 = pos[b];
-    if (ch == 0 && tok == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new)) report_error(err, kErrPos);
+    // a decode step's token (lens given, n_new = 1) goes to position
+    // clamp(lens[b], 0, max_len) - 1, none when that is -1 (the split and
+    // combine passes report lens outside [0, max_len])
+    const int p0 = lens ? min(max(lens[b], 0), max_len) - 1 : pos[b];
+    if (!lens && ch == 0 && tok == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new)) report_error(err, kErrPos);
     const int t = p0 + tok;
     if (t < 0 || t >= cap) return;  // block-uniform: outside the cache
     const size_t head = (size_t)b * H + h;
@@ -417,7 +421,21 @@ hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_n
     quantize_wide_kernel<192><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(k),
                                                            static_cast<const uint16_t*>(v), dtype, n_new, H,
                                                            cap, kc, ks, vc, vs, signs, rot_norm, lam, vsigns,
-                                                           pos, err);
+                                                           pos, err, nullptr, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_step_wide(const void* k_new, const void* v_new, int dtype, int B, int H, int D, int cap,
+                                   uint8_t* kc, float* ks, uint8_t* vc, float* vs, const float* signs,
+                                   float rot_norm, const float* lam, const int32_t* lens, int max_len,
+                                   unsigned* err, hipStream_t stream)
+{
+    if (D != 192 || max_len < 1 || max_len > cap) return hipErrorInvalidValue;
+    dim3 grid(1, H, B), block(192);
+    quantize_wide_kernel<192><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(k_new),
+                                                           static_cast<const uint16_t*>(v_new), dtype, 1, H, cap,
+                                                           kc, ks, vc, vs, signs, rot_norm, lam, nullptr, nullptr,
+                                                           err, lens, max_len);
     return hipGetLastError();
 }
 

@@ -335,8 +335,9 @@ def test_noalloc_scratch_limit_on_host():
 def test_head_dim_192_host_checks():
     """head_dim 192 (D/2 = 3 * 32): int4 only, K rotated by the FFT kind only
     (the Hadamard form needs a power of two), V unrotated; the matrix-core
-    split pass by default, the vector one when asked for; no fused append;
-    sizes by the int4 closed form."""
+    split pass by default, the vector one when asked for; the decode step
+    passes the host checks (three launches at this width); sizes by the int4
+    closed form."""
     lib = otq.lib()
     P = ctypes.c_void_p
     cb, sb = otq.otq_cache_array_bytes(2, 3, 192, 64, 4)
@@ -370,9 +371,11 @@ def test_head_dim_192_host_checks():
     b3.code_bits = 3
     assert plan(b3)[0] == otq.OTQ_EUNSUPPORTED
     ws = lib.otq_sdpa_workspace_bytes(8, ctypes.byref(d), 64)
+    assert ws > 0
+    # accepted up to the workspace check (a byte short), which comes before any HIP call
     rc = lib.otq_sdpa_int4_decode_append(P(FAKE), P(FAKE), P(FAKE), 1, 8, ctypes.byref(d), P(FAKE), 64,
-                                         ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws), None, None)
-    assert rc == otq.OTQ_EUNSUPPORTED
+                                         ctypes.c_float(0.1), P(FAKE), P(FAKE), ctypes.c_size_t(ws - 1), None, None)
+    assert rc == otq.OTQ_EWORKSPACE
     for bad in (96, 160, 320):
         assert lib.otq_cache_bytes(1, 1, bad, 64, 4) == 0
 

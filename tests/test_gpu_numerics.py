@@ -150,6 +150,50 @@ def test_junk_scales_past_lens_fused(variant, G, rotate):
     assert ma <= MAX_ABS and rel <= REL_L2
 
 
+@pytest.mark.parametrize("variant,G", [(MF, 8), (MF, 1), (VEC, 4)])
+@pytest.mark.parametrize("rotate", [False, True])
+@pytest.mark.parametrize("fused", [False, True])
+def test_junk_scales_past_lens_head_dim_192(variant, G, rotate, fused):
+    """The same junk (Inf/NaN scales, arbitrary codes) at and past lens at
+    head_dim 192, K plain or SRFT-rotated, for the decode call and the decode
+    step (whose token takes its own append launch at this width)."""
+    B, Hkv, D, cap = 3, 2, 192, 320
+    Hq = G * Hkv
+    lens = [291, 78, 129]
+    k, v, q = _inputs(B, Hq, Hkv, D, cap, seed=5 * G + rotate + 2 * fused)
+    g = torch.Generator().manual_seed(97)
+    signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if rotate else None
+    cache = otq.Int4KVCache(B, Hkv, D, cap, device=DEV, rot_signs=None if signs is None else signs.to(DEV),
+                            rot_kind="srft")
+    _fill(cache, k, v, cap)
+    _poison_from(cache, [n - 1 for n in lens] if fused else lens)
+    lens_t = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    plan = cache.plan(Hq, max(lens), chunk=128, variant=variant)
+    say(f"junk past lens D=192: variant={variant} G={G} rotate={rotate} fused={fused} lens={lens}")
+    if fused:
+        idx = (lens_t.long() - 1).clamp(min=0)
+        ar = torch.arange(B, device=DEV)
+        kn = k.to(DEV)[ar, :, idx].contiguous()
+        vn = v.to(DEV)[ar, :, idx].contiguous()
+        out = cache.decode_append(q.to(DEV), kn, vn, lens_t, max(lens), 1.0 / math.sqrt(D), plan=plan)
+    else:
+        out = cache.decode(q.to(DEV), lens_t, max(lens), 1.0 / math.sqrt(D), plan=plan)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    ref, ref_cache = _oracle_out(q, k, v, lens, 1.0 / math.sqrt(D), "bf16",
+                                 None if signs is None else signs.numpy(), kind="srft")
+    if fused:
+        got_cache = host_cache(cache)
+        for b, n in enumerate(lens):
+            sub = tuple(x[b:b + 1, :, :n] for x in got_cache)
+            refb = tuple(x[b:b + 1, :, :n] for x in ref_cache)
+            assert compare_codes(sub, refb, n) == {"k_codes": 0, "k_scales": 0, "v_codes": 0, "v_scales": 0}
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
 def _query_rows(B, Hq, D, seed):
     """bf16 query rows of several magnitudes: ~1e5 (past fp16's range),
     ~1e-6 (subnormal in fp16), 1e5 and 1e-6 mixed in one row, and N(0, 1)."""
@@ -193,6 +237,41 @@ def test_query_magnitudes(variant, G, opt):
     ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale,
                       signs=None if signs is None else signs.numpy(), rot_norm=rn, threads=8,
                       chan_scale=None if lam is None else lam.numpy())
+    got = out.cpu().numpy()
+    ma, rel = errors(got, ref)
+    say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")
+    assert np.all(np.isfinite(got))
+    assert ma <= MAX_ABS and rel <= REL_L2
+
+
+@pytest.mark.parametrize("G", [8, 2])
+@pytest.mark.parametrize("opt", ["plain", "rotated", "scaled"])
+def test_query_magnitudes_head_dim_192(G, opt):
+    """The query magnitudes above on the matrix-core pass at head_dim 192
+    (K plain, SRFT-rotated or channel-scaled)."""
+    B, Hkv, D, cap = 2, 2, 192, 256
+    Hq = G * Hkv
+    lens = [250, 97]
+    k, v, _ = _inputs(B, Hq, Hkv, D, cap, seed=11 + G)
+    q = _query_rows(B, Hq, D, seed=16 + G)
+    g = torch.Generator().manual_seed(96)
+    signs = torch.where(torch.rand(D, generator=g) < 0.5, -1.0, 1.0) if opt == "rotated" else None
+    lam = torch.exp2(torch.rand(D, generator=g) * 4 - 2) if opt == "scaled" else None
+    cache = otq.Int4KVCache(B, Hkv, D, cap, device=DEV, rot_signs=None if signs is None else signs.to(DEV),
+                            chan_scale=None if lam is None else lam.to(DEV), rot_kind="srft")
+    _fill(cache, k, v, cap)
+    plan = cache.plan(Hq, max(lens), chunk=128, variant=MF)
+    scale = 1.0 / math.sqrt(D)
+    say(f"query magnitudes D=192: G={G} opt={opt}")
+    out = cache.decode(q.to(DEV), torch.tensor(lens, dtype=torch.int32, device=DEV), max(lens), scale,
+                       plan=plan)
+    torch.cuda.synchronize()
+    rn = rot_norm32(D, "srft")
+    kc, ks, vc, vs = oracle_cache(k, v, "bf16", None if signs is None else signs.numpy(), rn,
+                                  chan_scale=None if lam is None else lam.numpy(), rot_kind="srft")
+    ref = oracle.sdpa(to_bits(q), "bf16", kc, ks, vc, vs, np.array(lens, np.int32), scale,
+                      signs=None if signs is None else signs.numpy(), rot_norm=rn, threads=8,
+                      chan_scale=None if lam is None else lam.numpy(), rot_kind="srft")
     got = out.cpu().numpy()
     ma, rel = errors(got, ref)
     say(f"  max_abs={ma:.3e} rel_l2={rel:.3e}")

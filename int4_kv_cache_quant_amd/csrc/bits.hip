@@ -165,7 +165,9 @@ __global__ __launch_bounds__(256) void quantize_bits_small_kernel(
 // before any arithmetic.  Each vector is widened, rotated (its own signs, in
 // the same order of operations as the other append kernels), K scaled by its
 // channel scale, and quantised: s = abs-max / (2^(b-1) - 1) and c =
-// clamp(rint(x / s)) by IEEE division.  The codes pass through LDS; then the
+// clamp(rint(x / s)), the quotients correctly rounded (by reciprocal and
+// Markstein corrections for group maxima in [2^-80, 2^100], else by IEEE
+// division).  The codes pass through LDS; then the
 // block writes the tile's K rows and V words whole, merging V words with
 // their old contents under a mask where only part of the tile is new (only
 // this block writes the tile in this launch).
@@ -252,11 +254,28 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
             for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
             a = group_max<4>(a);        // exact in any order
             const float sc = a / qmax;  // correctly rounded IEEE division
+            if (a >= 0x1p-80f && a <= 0x1p100f) {
+                // RN(x / sc) from one correctly rounded reciprocal and two
+                // Markstein corrections: the int4 quantiser's argument
+                // (quant_lane.hpp) holds for any qmax <= 7, since |x / sc| <=
+                // qmax (1 + 2^-23) and sc >= a / 7; the same quotients as the
+                // division, hence the same codes
+                const float y = 1.0f / sc;  // correctly rounded IEEE division
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                float r = rintf(x[e] / sc);  // IEEE division, then half to even
-                r = fminf(fmaxf(r, qmin), qmax);
-                ccs[w][u][8 * j + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
+                for (int e = 0; e < 8; ++e) {
+                    float q = x[e] * y;
+                    q = __builtin_fmaf(__builtin_fmaf(-q, sc, x[e]), y, q);
+                    q = __builtin_fmaf(__builtin_fmaf(-q, sc, x[e]), y, q);  // RN(x / sc)
+                    const float r = fminf(fmaxf(rintf(q), qmin), qmax);
+                    ccs[w][u][8 * j + e] = (int8_t)(int)r;
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    float r = rintf(x[e] / sc);  // IEEE division, then half to even
+                    r = fminf(fmaxf(r, qmin), qmax);
+                    ccs[w][u][8 * j + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
+                }
             }
             if ((j & 3) == 0) (w ? vs : ks)[(head * cap + t0 + u) * NG + j / 4] = sc;
         }

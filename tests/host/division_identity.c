@@ -6,6 +6,8 @@
  *                                    [2^-80, 2^100] and for 2^100
  *   ./division_identity random N     N draws of (x, s = RN(a / 7)): x / s and
  *                                    the 8-code word
+ *   ./division_identity bits N       N draws each for qmax = 1 and 3 (the 2-
+ *                                    and 3-bit quantiser): x / s and the codes
  *
  * Built with -ffp-contract=off; fmaf is the C library's correctly rounded
  * fused multiply-add.  Exit status 0 when no draw differs. */
@@ -114,6 +116,53 @@ int main(int argc, char** argv)
                (unsigned long long)badq, (unsigned long long)badc);
         return badq != 0 || badc != 0;
     }
-    fprintf(stderr, "usage: %s exhaustive | random N\n", argv[0]);
+    if (argc >= 3 && strcmp(argv[1], "bits") == 0) {
+        /* the 2- and 3-bit quantiser: s = RN(a / qmax) by IEEE division for
+         * qmax = 1 and 3, quotients as above, codes clamp(rint(q), -qmax - 1,
+         * qmax) against those of the IEEE quotient, for every draw */
+        const long n = atol(argv[2]);
+        uint64_t badq = 0, badc = 0;
+        for (int qm = 1; qm <= 3; qm += 2) {
+            const float qmax = (float)qm, qmin = -(float)(qm + 1);
+            for (long i = 0; i < n; ++i) {
+                const uint64_t r = next(), r2 = next();
+                const int ea = (int)(r % 181) - 80;
+                float a = ldexpf(1.0f + (float)((r >> 8) & 0x7fffff) * 0x1p-23f, ea);
+                if (a > 0x1p100f) a = 0x1p100f;
+                const float s = a / qmax, y = 1.0f / s;
+                for (int e = 0; e < 8; ++e) {
+                    const uint64_t rr = next();
+                    float x;
+                    switch ((r2 >> (2 * e)) & 3) {
+                    case 0:
+                        x = a * ((float)(rr & 0xffffff) * 0x1p-23f - 1.0f);
+                        break;
+                    case 1: { /* a few ulps around (k + 1/2) s, k in [-qmax - 1, qmax] */
+                        const float t = ((float)((int)(rr % (2 * qm + 2)) - qm - 1) + 0.5f) * s;
+                        x = fu(uf(t) + (uint32_t)((int)((rr >> 8) % 9) - 4));
+                        break;
+                    }
+                    case 2:
+                        x = fu(uf(a * (float)((rr & 0xffff) + 1) * 0x1p-16f) & 0xffff0000u);
+                        if (rr & 0x10000) x = -x;
+                        break;
+                    default:
+                        x = (rr & 1) ? -a : a;
+                    }
+                    if (!(fabsf(x) <= a)) x = a;
+                    const float ref = x / s;
+                    const float q = quot(x, s, y);
+                    if (fabsf(ref) >= 0x1p-13f && uf(q) != uf(ref)) ++badq;
+                    const float c_ref = fminf(fmaxf(rintf(ref), qmin), qmax);
+                    const float c = fminf(fmaxf(rintf(q), qmin), qmax);
+                    if (c != c_ref) ++badc;
+                }
+            }
+        }
+        printf("b-bit x/s: 2 x %ld groups of 8, %llu quotients differ (|q| >= 2^-13), %llu codes differ\n", n,
+               (unsigned long long)badq, (unsigned long long)badc);
+        return badq != 0 || badc != 0;
+    }
+    fprintf(stderr, "usage: %s exhaustive | random N | bits N\n", argv[0]);
     return 2;
 }

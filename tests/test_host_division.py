@@ -3,7 +3,8 @@ division (Markstein-corrected quotients from one correctly rounded reciprocal,
 codes packed through a rounding constant): tests/host/division_identity.c,
 built with gcc, compares it with IEEE fp32 division + rint + clamp over
 complete binades of a / 7 and over random draws of x / s, including a few
-ulps around every half-integer quotient and bf16 inputs."""
+ulps around every half-integer quotient and bf16 inputs; the same for the
+2- and 3-bit quantiser's divisors a / 1 and a / 3."""
 import os
 import shutil
 import subprocess
@@ -35,3 +36,11 @@ def test_quotients_and_code_words_random(checker):
     r = subprocess.run([checker, "random", "4000000"], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "0 quotients differ" in r.stdout and "0 words differ" in r.stdout
+
+
+def test_bits_quotients_and_codes_random(checker):
+    """The 2- and 3-bit bulk append's quotients (s = a / 1 and a / 3) and
+    codes equal those of IEEE division."""
+    r = subprocess.run([checker, "bits", "2000000"], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "0 quotients differ" in r.stdout and "0 codes differ" in r.stdout

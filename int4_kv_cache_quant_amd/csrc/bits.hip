@@ -167,10 +167,11 @@ __global__ __launch_bounds__(256) void quantize_bits_small_kernel(
 // channel scale, and quantised: s = abs-max / (2^(b-1) - 1) and c =
 // clamp(rint(x / s)), the quotients correctly rounded (by reciprocal and
 // Markstein corrections for group maxima in [2^-80, 2^100], else by IEEE
-// division).  The codes pass through LDS; then the
-// block writes the tile's K rows and V words whole, merging V words with
-// their old contents under a mask where only part of the tile is new (only
-// this block writes the tile in this launch).
+// division).  K rows are written whole from registers (a lane's 8 fields
+// with its neighbours' make whole words); V codes pass through LDS, then the
+// block writes the tile's V words whole, merging them with their old
+// contents under a mask where only part of the tile is new (only this block
+// writes the tile in this launch).
 template <int D, int BITS, bool SRFT>
 __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
@@ -179,13 +180,13 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     const float* __restrict__ lam, const float* __restrict__ vsigns, unsigned* __restrict__ err)
 {
 #pragma clang fp contract(off)
-    constexpr int NG = D / kGroup, RB = D * BITS / 8, RW = RB / 4;
+    constexpr int NG = D / kGroup, RB = D * BITS / 8;
     constexpr int LT = D / 8;           // threads per token
     constexpr int U = kTile * LT / 256;  // units (16-byte pieces) per thread, of K and of V
     constexpr float qmax = (float)((1 << (BITS - 1)) - 1), qmin = -(float)(1 << (BITS - 1));
     using VT = VBitsTile<D, BITS>;
     static_assert(RB % 4 == 0, "whole words per row");
-    __shared__ int8_t ccs[2][kTile][D];  // the tile's K and V codes
+    __shared__ int8_t ccs[kTile][D];  // the tile's V codes
     const int tid = threadIdx.x, j = tid % LT;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
@@ -254,6 +255,7 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
             for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
             a = group_max<4>(a);        // exact in any order
             const float sc = a / qmax;  // correctly rounded IEEE division
+            int cd[8];
             if (a >= 0x1p-80f && a <= 0x1p100f) {
                 // RN(x / sc) from one correctly rounded reciprocal and two
                 // Markstein corrections: the int4 quantiser's argument
@@ -267,33 +269,42 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
                     q = __builtin_fmaf(__builtin_fmaf(-q, sc, x[e]), y, q);
                     q = __builtin_fmaf(__builtin_fmaf(-q, sc, x[e]), y, q);  // RN(x / sc)
                     const float r = fminf(fmaxf(rintf(q), qmin), qmax);
-                    ccs[w][u][8 * j + e] = (int8_t)(int)r;
+                    cd[e] = (int)r;
                 }
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     float r = rintf(x[e] / sc);  // IEEE division, then half to even
                     r = fminf(fmaxf(r, qmin), qmax);
-                    ccs[w][u][8 * j + e] = (int8_t)(sc != 0.0f ? (int)r : 0);
+                    cd[e] = sc != 0.0f ? (int)r : 0;
                 }
+            }
+            if (w == 0) {
+                // K: the lane's 8 fields are bits [8 b j, 8 b j + 8 b) of the
+                // row; whole words from the token's neighbouring lanes (a
+                // pair at 2 bits, the group's quad at 3)
+                uint32_t f = 0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f |= ((uint32_t)cd[e] & ((1u << BITS) - 1u)) << (BITS * e);
+                uint32_t* krow = reinterpret_cast<uint32_t*>(kc + (head * cap + t0 + u) * RB);
+                if constexpr (BITS == 2) {
+                    const uint32_t other = (uint32_t)__shfl_xor((int)f, 1, 64);
+                    if ((j & 1) == 0) __builtin_nontemporal_store(f | (other << 16), krow + j / 2);
+                } else {
+                    const int jj = j & 3;
+                    const uint32_t nx = (uint32_t)__shfl_down((int)f, 1, 4);  // lane j + 1 of the quad
+                    const uint32_t word = jj == 0 ? (f | (nx << 24)) : jj == 1 ? ((f >> 8) | (nx << 16))
+                                                                               : ((f >> 16) | (nx << 8));
+                    if (jj < 3) __builtin_nontemporal_store(word, krow + 3 * (j >> 2) + jj);
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ccs[u][8 * j + e] = (int8_t)cd[e];
             }
             if ((j & 3) == 0) (w ? vs : ks)[(head * cap + t0 + u) * NG + j / 4] = sc;
         }
     }
     __syncthreads();
-    // the new tokens' K rows, word by word (word q: bits [32 q, 32 q + 32))
-    for (int W = tid; W < kTile * RW; W += 256) {
-        const int u = W / RW, q = W % RW;
-        if (!fresh(u)) continue;
-        uint32_t word = 0;
-        const int i0 = (32 * q) / BITS, i1 = min((32 * q + 31) / BITS, D - 1);
-        for (int i = i0; i <= i1; ++i) {
-            const uint32_t c = (uint32_t)ccs[0][u][i] & ((1u << BITS) - 1u);
-            const int off = i * BITS - 32 * q;  // negative for a code that starts in the word before
-            word |= off >= 0 ? c << off : c >> -off;
-        }
-        __builtin_nontemporal_store(word, reinterpret_cast<uint32_t*>(kc + (head * cap + t0 + u) * RB) + q);
-    }
     // the tile's V words: the new tokens' fields
     uint32_t* vt = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + tile) * (size_t)(kTile * RB));
     for (int W = tid; W < VT::WORDS; W += 256) {
@@ -301,7 +312,7 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
         vtile_fields<D, BITS>(W, [&](int u, int c, int bpos, int width, int shift) {
             if (fresh(u)) {
                 const uint32_t fm = (1u << width) - 1u;
-                val |= (((uint32_t)(int)ccs[1][u][c] >> shift) & fm) << bpos;
+                val |= (((uint32_t)(int)ccs[u][c] >> shift) & fm) << bpos;
                 mask |= fm << bpos;
             }
         });

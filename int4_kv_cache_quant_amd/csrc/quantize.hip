@@ -167,13 +167,14 @@ __global__ __launch_bounds__(256) void quantize_pair_kernel(
 // 4, 2 and 1 apart (an aligned group of 8 lanes, never split by a wave),
 // those of 2 and 1 stay in the lane.  The fp32 operations and their order
 // are those of the per-token form in wide.hip, so the codes are the same.
-__device__ __forceinline__ void srft192_lane(float (&x)[8], const float* zr, int j)
+// tw is the 96-point twiddle table in LDS (re[96], then im[96]): the indices
+// differ from lane to lane.
+__device__ __forceinline__ void srft192_lane(float (&x)[8], const float* zr, int j, const float* tw)
 {
 #pragma clang fp contract(off)
     using srft_detail::kC3;
-    using srft_detail::kTw96;
-    auto cmul = [](float& re, float& im, int u) {
-        const float wr = kTw96.re[u], wi = kTw96.im[u];
+    auto cmul = [tw](float& re, float& im, int u) {
+        const float wr = tw[u], wi = tw[96 + u];
         const float p1 = re * wr, p2 = im * wi, p3 = re * wi, p4 = im * wr;
         re = p1 - p2;
         im = p3 + p4;
@@ -359,8 +360,9 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
 
     // head_dim 192, K FFT-rotated: the tile's K rows, signs applied, in LDS
     // (krot, kTile x D floats) for the radix-3 stage, which reads lanes of
-    // other waves
+    // other waves, followed by the 96-point twiddles (re, then im)
     if constexpr (kSrft192) {
+        if (tid < 192) krot[kTile * D + tid] = tid < 96 ? srft_detail::kTw96.re[tid] : srft_detail::kTw96.im[tid - 96];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
             const int L = i * 256 + tid;
@@ -379,7 +381,7 @@ __device__ __forceinline__ void quantize_tile(const uint16_t* __restrict__ k, co
         float x[8];
         widen8(kraw[i], x);
         if constexpr (kSrft192) {  // the row staged in LDS (signs applied) above
-            srft192_lane(x, krot + (L / LT) * D, j);
+            srft192_lane(x, krot + (L / LT) * D, j, krot + kTile * D);
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = x[e] * rot_norm;
         } else if constexpr (kRotates) {
@@ -481,7 +483,7 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     // LDS of the rotated forms (one array for both instances below)
     constexpr bool kSrft192 = D == 192 && SRFT;
     __shared__ uint32_t vstage[VROT ? kTile * (D / 8) : 1];
-    __shared__ float krot[kSrft192 ? kTile * D : 1];
+    __shared__ float krot[kSrft192 ? kTile * D + 192 : 1];
     if (t_tile >= 0 && t_tile >= p0 && t_tile + kTile <= t_end)
         quantize_tile<D, DTYPE, true, VROT, SRFT>(k, v, n_new, cap, head, p0, t_tile, t_end, kc, ks, vc, vs,
                                             signs, rot_norm, lam, vsigns, vstage, krot);

@@ -41,17 +41,17 @@
 // Int4 caches at head_dim 192 (six groups, twelve channel blocks; the FFT
 // rotation of that width is mixed radix) take this kernel as well: K words
 // are the int4 rows' words (word 6 r + g holds channels 32 g + 8 r + 0..7),
-// unpacked to subnormals as in the int4 pass,
-// and V words the int4 tile words (tokens 4 r + m and 16 + 4 r + m in
-// nibbles m and 4 + m), with 2^(4 (k & 1)) as the k-slot powers; one KV head
-// per wave.
+// unpacked to subnormals as in the int4 pass, and V words the int4 tile
+// words (tokens 4 r + m and 16 + 4 r + m in nibbles m and 4 + m), with
+// 2^(4 (k & 1)) as the k-slot powers; one KV head per wave.
 //
 // Block = 4 waves, one (split, P KV heads, sequence): P = 2 when 4 <= G <= 8
-// (the two heads' query heads fill the 16 MFMA columns), else 1; wave w takes
-// the tiles w, w + 4, ... of the split (32 tokens each).  Each tile (per
-// head: K rows, the V tile, K and V scales: (8 b + 8) D bytes) is loaded
-// into registers ahead (two tiles; one at head_dim 256 and for two heads per
-// wave), written to the wave's LDS stage when its turn comes, and read back
+// and head_dim is 64 or 128 (the two heads' query heads fill the 16 MFMA
+// columns), else 1; wave w takes the tiles w, w + 4, ... of the split (32
+// tokens each).  Each tile (per head: K rows, the V tile, K and V scales:
+// (8 b + 8) D bytes) is loaded into registers ahead (two tiles; one at head_dim
+// 256, for two heads per wave and for the hi + lo query at 192), written to
+// the wave's LDS stage when its turn comes, and read back
 // in the operand layouts below.  Lane l = 16 r + n:
 //  scores  A = K codes of head j (row = token 16 s + n, k = channels
 //          32 g + 8 r + the slot order), B = q of query head n masked to
@@ -660,7 +660,8 @@ void split_bits_mfma_kernel(SplitArgs a)
 }  // namespace
 
 // KV heads per wave: two (filling 16 MFMA columns at G = 8) when 4 <= G <= 8,
-// the head count is even and the registers suffice (head_dim < 256), else one.
+// the head count is even and the registers suffice (head_dim 64 or 128),
+// else one.
 int split_bits_mfma_heads_per_wave(int D, int G, int H, bool hilo)
 {
     if (hilo) return 1;  // the hi + lo query takes the registers of a second head

@@ -186,7 +186,11 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     constexpr float qmax = (float)((1 << (BITS - 1)) - 1), qmin = -(float)(1 << (BITS - 1));
     using VT = VBitsTile<D, BITS>;
     static_assert(RB % 4 == 0, "whole words per row");
-    __shared__ int8_t ccs[kTile][D];  // the tile's V codes
+    // the tile's V codes, channel-major (a channel's 32 tokens in a row of
+    // TS bytes: four tokens of a quarter are one aligned word, and the
+    // padding spreads the rows over the banks)
+    constexpr int TS = kTile + 4;
+    __shared__ __align__(4) int8_t ccs[D * TS];
     const int tid = threadIdx.x, j = tid % LT;
     const int h = blockIdx.y, b = blockIdx.z;
     const int p0 = pos[b];
@@ -299,7 +303,7 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
                 }
             } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) ccs[u][8 * j + e] = (int8_t)cd[e];
+                for (int e = 0; e < 8; ++e) ccs[(8 * j + e) * TS + u] = (int8_t)cd[e];
             }
             if ((j & 3) == 0) (w ? vs : ks)[(head * cap + t0 + u) * NG + j / 4] = sc;
         }
@@ -307,12 +311,41 @@ __global__ __launch_bounds__(256) void quantize_bits_kernel(
     __syncthreads();
     // the tile's V words: the new tokens' fields
     uint32_t* vt = reinterpret_cast<uint32_t*>(vc + (head * (cap / kTile) + tile) * (size_t)(kTile * RB));
+    if (nt == kTile) {  // block-uniform: every token of the tile is new
+        // the b-bit fields of the four tokens 4 r + m (m = 0..3) of channel
+        // c, quarter r, half h: one LDS word of four codes, packed at b m
+        auto quad = [&](int c, int h, int r) {
+            const uint32_t v = *reinterpret_cast<const uint32_t*>(&ccs[c * TS + 16 * h + 4 * r]);
+            constexpr uint32_t m = (1u << BITS) - 1u;
+            return (v & m) | ((v >> (8 - BITS)) & (m << BITS)) | ((v >> (16 - 2 * BITS)) & (m << (2 * BITS))) |
+                   ((v >> (24 - 3 * BITS)) & (m << (3 * BITS)));
+        };
+        for (int W = tid; W < VT::WORDS; W += 256) {
+            const int l = W / VT::WPL, k = W % VT::WPL, r = l >> 4, n = l & 15;
+            uint32_t val = 0;
+            if constexpr (BITS == 2) {  // blocks 2 k + t at bit 16 h + 8 t
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) val |= quad(16 * (2 * k + t) + n, h, r) << (16 * h + 8 * t);
+            } else {  // block 4 qd + w at bit 16 h, and bits 4 w .. 4 w + 3 of block 4 qd + 3 at 16 h + 12
+                const int qd = k / 3, w = k % 3;
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    val |= (quad(16 * (4 * qd + w) + n, h, r) | (((quad(16 * (4 * qd + 3) + n, h, r) >> (4 * w)) & 0xFu)
+                                                                << 12))
+                           << (16 * h);
+            }
+            vt[W] = val;
+        }
+        return;
+    }
     for (int W = tid; W < VT::WORDS; W += 256) {
         uint32_t val = 0, mask = 0;
         vtile_fields<D, BITS>(W, [&](int u, int c, int bpos, int width, int shift) {
             if (fresh(u)) {
                 const uint32_t fm = (1u << width) - 1u;
-                val |= (((uint32_t)(int)ccs[u][c] >> shift) & fm) << bpos;
+                val |= (((uint32_t)(int)ccs[c * TS + u] >> shift) & fm) << bpos;
                 mask |= fm << bpos;
             }
         });

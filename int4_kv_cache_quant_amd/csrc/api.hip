@@ -587,20 +587,6 @@ int otq_sdpa_int4_decode_append(const void* q, const void* k_new, const void* v_
     if (rc != OTQ_OK) return rc;
     if ((rc = check_workspace(workspace, workspace_bytes, chk)) != OTQ_OK) return rc;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    if (!pow2_dim(cache->head_dim)) {
-        // head_dim 192 (the combine's token forms are power-of-two ones): the
-        // token's own append launch, then the split and combine over [0, lens)
-        unsigned* err = error_word();
-        if (!err) return OTQ_EDEVICE;
-        if (otq::launch_append_step_wide(k_new, v_new, dtype, cache->batch, cache->num_kv_heads, cache->head_dim,
-                                         cache->capacity, cache->k_codes, cache->k_scales, cache->v_codes,
-                                         cache->v_scales, cache->k_rot_signs, cache->rot_norm,
-                                         cache->k_chan_scale, lens, max_len, err, s) != hipSuccess)
-            return OTQ_EDEVICE;
-        rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s);
-        if (rc != OTQ_OK) return rc;
-        return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s);
-    }
     rc = run_split(q, dtype, num_q_heads, cache, lens, max_len, scale, workspace, chk, s, 1);
     if (rc != OTQ_OK) return rc;
     return run_combine(num_q_heads, cache, lens, max_len, workspace, chk, out, s, q, k_new, v_new,

@@ -138,8 +138,11 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
     [[maybe_unused]] float sg = 1.0f, lm = 1.0f, vsg = 1.0f;
     [[maybe_unused]] int kvh = 0, pos = 0, ch = 0;
     [[maybe_unused]] bool writer = false;
-    [[maybe_unused]] SrftThreadTw<(DA > 0 ? DA : 64)> stw;  // the FFT rotation's twiddles
-    if constexpr (ROT || VROT) {
+    // the FFT rotation's twiddles (radix 2; head_dim 192 takes the
+    // mixed-radix stages through LDS, srft_mixed_block, in their place)
+    constexpr bool kMixed = DA == 192;
+    [[maybe_unused]] SrftThreadTw<(DA > 0 && !kMixed ? DA : 64)> stw;
+    if constexpr ((ROT || VROT) && !kMixed) {
         if (a.rot_kind) stw.load(tid);
     }
     if constexpr (APPEND) {
@@ -228,7 +231,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float x = widen(kx, a.dtype);
         if (ROT) {
             x = x * sg;
-            x = a.rot_kind ? srft_thread<DA>(x, xch, stw) : fwht_thread<DA>(x, xch);
+            if constexpr (kMixed) x = srft_mixed_block<DA>(x, xch);  // the FFT kind only at 192
+            else x = a.rot_kind ? srft_thread<DA>(x, xch, stw) : fwht_thread<DA>(x, xch);
             x = x * a.rot_norm;
         }
         if (LAM) x = x * lm;  // after the rotation
@@ -239,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         const int bits = a.bits;  // block-uniform: 4, or 2 / 3
         const float sk = bits == 4 ? quantize_lane<64>(xk, ck, lane) : quantize_lane_bits(xk[0], ck[0], bits);
         float xv[1] = {widen(vx, a.dtype)};
-        if (VROT) {  // V rotated as K is, with its own signs
+        if constexpr (VROT) {  // V rotated as K is, with its own signs
             xv[0] = xv[0] * vsg;
             xv[0] = a.rot_kind ? srft_thread<DA>(xv[0], xch, stw) : fwht_thread<DA>(xv[0], xch);
             xv[0] = xv[0] * a.rot_norm;
@@ -298,7 +302,8 @@ __global__ __launch_bounds__(kThreads) void lse_combine_kernel(CombineArgs a)
         float y = widen(qx, a.dtype);
         if (ROT) {
             y = y * sg;
-            y = a.rot_kind ? srft_thread<DA>(y, xch, stw) : fwht_thread<DA>(y, xch);
+            if constexpr (kMixed) y = srft_mixed_block<DA>(y, xch);
+            else y = a.rot_kind ? srft_thread<DA>(y, xch, stw) : fwht_thread<DA>(y, xch);
             y = y * a.rot_norm;
         }
         if (LAM) y = y / lm;
@@ -373,10 +378,13 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
                vrot = a.vsigns != nullptr;
     // whole rows for a rotated V, for the append with a rotated K, and for a
     // plain combine whose slices would take more than one round of resident
-    // blocks (2048)
+    // blocks (2048); at head_dim 192 (no whole-row form: its split groups
+    // would not divide the block) the slices, each block transforming the
+    // new token's K itself when it is rotated
     const bool pow2 = a.D == 64 || a.D == 128 || a.D == 256;  // the whole-row forms' widths
     const bool big = !append && pow2 && (long)a.B * a.Hq * (a.D / kCh) > 2048;
-    const bool rows = vrot || (append && rot) || big;
+    const bool rows = pow2 && (vrot || (append && rot) || big);
+    if (!pow2 && (a.D != 192 || vrot)) return hipErrorInvalidValue;
     dim3 grid(a.B * a.Hq, rows ? 1 : a.D / kCh), block(kThreads);
     if (!append && !rows) {
         lse_combine_kernel<0, false, false, false, false, false><<<grid, block, 0, stream>>>(a);
@@ -402,6 +410,14 @@ hipError_t launch_lse_combine(const CombineArgs& a, hipStream_t stream)
     };
     K kern = nullptr;
     switch (a.D) {
+    case 192:  // the slice form with the token (rotation and scale as compile-time choices)
+        switch ((rot ? 1 : 0) + (lam ? 2 : 0)) {
+        case 0: kern = lse_combine_kernel<192, true, false, false, false, false>; break;
+        case 1: kern = lse_combine_kernel<192, true, false, true, false, false>; break;
+        case 2: kern = lse_combine_kernel<192, true, false, false, true, false>; break;
+        default: kern = lse_combine_kernel<192, true, false, true, true, false>; break;
+        }
+        break;
     case 64: kern = pick(std::integral_constant<int, 64>{}); break;
     case 128: kern = pick(std::integral_constant<int, 128>{}); break;
     case 256: kern = pick(std::integral_constant<int, 256>{}); break;

@@ -91,13 +91,6 @@ hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_n
                                 float rot_norm, const float* lam, const float* vsigns, const int32_t* pos,
                                 unsigned* err, hipStream_t stream);
 hipError_t launch_split_wide(const SplitArgs& a, hipStream_t stream);
-// A decode step's new token at head_dim 192 (k_new, v_new [B][H][D]) into
-// position clamp(lens[b], 0, max_len) - 1 of each sequence (none at -1).
-hipError_t launch_append_step_wide(const void* k_new, const void* v_new, int dtype, int B, int H, int D, int cap,
-                                   uint8_t* kc, float* ks, uint8_t* vc, float* vs, const float* signs,
-                                   float rot_norm, const float* lam, const int32_t* lens, int max_len,
-                                   unsigned* err, hipStream_t stream);
-
 // Returns hipErrorInvalidValue for (D, G) pairs the variant does not build.
 hipError_t launch_split_vector(const SplitArgs& a, hipStream_t stream);
 // Largest batch whose split blocks are ordered longest first.

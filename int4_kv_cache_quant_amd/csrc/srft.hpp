@@ -327,4 +327,72 @@ __device__ __forceinline__ float isrft_thread(float y, float* xch, const SrftThr
     return y;
 }
 
+// The complex product (dr wr - di wi, dr wi + di wr), products rounded
+// before the sum; the real part when part == 0, else the imaginary part.
+__device__ __forceinline__ float cmul_part(float dr, float di, float wr, float wi, int part)
+{
+#pragma clang fp contract(off)
+    if (part == 0) {
+        const float p1 = dr * wr, p2 = di * wi;
+        return p1 - p2;
+    }
+    const float p3 = dr * wi, p4 = di * wr;
+    return p3 + p4;
+}
+
+// The transform (without rot_norm) of a vector of D reals held one per
+// thread (thread i < D holds real i, i.e. part i % 2 of complex i / 2),
+// through LDS xch[D]; returns thread i's real of the result.  Threads past D
+// take part in the barriers only.
+template <int D>
+__device__ __forceinline__ float srft_mixed_block(float y, float* xch)
+{
+#pragma clang fp contract(off)
+    constexpr int N = D / 2, M = N / 3;
+    static_assert(N % 3 == 0 && (M & (M - 1)) == 0, "N = 3 * 2^k");
+    const int i = threadIdx.x, P = i >> 1, part = i & 1;
+    const bool mine = i < D;
+    __syncthreads();
+    if (mine) xch[i] = y;
+    __syncthreads();
+    if (mine) {  // the radix-3 stage: output position P = m M + j
+        const int m = P / M, j = P % M;
+        const float a0r = xch[2 * j], a0i = xch[2 * j + 1];
+        const float a1r = xch[2 * (j + M)], a1i = xch[2 * (j + M) + 1];
+        const float a2r = xch[2 * (j + 2 * M)], a2i = xch[2 * (j + 2 * M) + 1];
+        const float sr = a1r + a2r, si = a1i + a2i;
+        const float dr = a1r - a2r, di = a1i - a2i;
+        const float hr = 0.5f * sr, hi = 0.5f * si;
+        const float mr = a0r - hr, mi = a0i - hi;
+        const float tr = srft_detail::kC3 * dr, ti = srft_detail::kC3 * di;
+        if (m == 0) {
+            y = part ? a0i + si : a0r + sr;
+        } else if (m == 1) {  // (m - i t) W^j
+            const float br = mr + ti, bi = mi - tr;
+            y = cmul_part(br, bi, srft_detail::kTw96.re[j], srft_detail::kTw96.im[j], part);
+        } else {  // (m + i t) W^2j
+            const float br = mr - ti, bi = mi + tr;
+            y = cmul_part(br, bi, srft_detail::kTw96.re[2 * j], srft_detail::kTw96.im[2 * j], part);
+        }
+    }
+#pragma unroll
+    for (int h = M / 2; h >= 1; h >>= 1) {  // radix-2 stages inside each block of M
+        __syncthreads();
+        if (mine) xch[i] = y;
+        __syncthreads();
+        if (mine) {
+            const int q = P % M, w = q & (2 * h - 1);  // position inside the 2h-block
+            if (w < h) {
+                y = xch[2 * P + part] + xch[2 * (P + h) + part];
+            } else {
+                const int lo = P - h;
+                const float dr = xch[2 * lo] - xch[2 * P], di = xch[2 * lo + 1] - xch[2 * P + 1];
+                const int t = (w - h) * (N / (2 * h));
+                y = cmul_part(dr, di, srft_detail::kTw96.re[t], srft_detail::kTw96.im[t], part);
+            }
+        }
+    }
+    return y;
+}
+
 }  // namespace otq

@@ -39,74 +39,6 @@ constexpr float kNegInfW = -__builtin_huge_valf();
 using srft_detail::kC3;
 using srft_detail::kTw96;
 
-// The complex product (dr wr - di wi, dr wi + di wr), products rounded
-// before the sum; the real part when part == 0, else the imaginary part.
-__device__ __forceinline__ float cmul_part(float dr, float di, float wr, float wi, int part)
-{
-#pragma clang fp contract(off)
-    if (part == 0) {
-        const float p1 = dr * wr, p2 = di * wi;
-        return p1 - p2;
-    }
-    const float p3 = dr * wi, p4 = di * wr;
-    return p3 + p4;
-}
-
-// The transform (without rot_norm) of a vector of D reals held one per
-// thread (thread i < D holds real i, i.e. part i % 2 of complex i / 2),
-// through LDS xch[D]; returns thread i's real of the result.  Threads past D
-// take part in the barriers only.
-template <int D>
-__device__ float srft_mixed_block(float y, float* xch)
-{
-#pragma clang fp contract(off)
-    constexpr int N = D / 2, M = N / 3;
-    static_assert(N % 3 == 0 && (M & (M - 1)) == 0, "N = 3 * 2^k");
-    const int i = threadIdx.x, P = i >> 1, part = i & 1;
-    const bool mine = i < D;
-    __syncthreads();
-    if (mine) xch[i] = y;
-    __syncthreads();
-    if (mine) {  // the radix-3 stage: output position P = m M + j
-        const int m = P / M, j = P % M;
-        const float a0r = xch[2 * j], a0i = xch[2 * j + 1];
-        const float a1r = xch[2 * (j + M)], a1i = xch[2 * (j + M) + 1];
-        const float a2r = xch[2 * (j + 2 * M)], a2i = xch[2 * (j + 2 * M) + 1];
-        const float sr = a1r + a2r, si = a1i + a2i;
-        const float dr = a1r - a2r, di = a1i - a2i;
-        const float hr = 0.5f * sr, hi = 0.5f * si;
-        const float mr = a0r - hr, mi = a0i - hi;
-        const float tr = kC3 * dr, ti = kC3 * di;
-        if (m == 0) {
-            y = part ? a0i + si : a0r + sr;
-        } else if (m == 1) {  // (m - i t) W^j
-            const float br = mr + ti, bi = mi - tr;
-            y = cmul_part(br, bi, kTw96.re[j], kTw96.im[j], part);
-        } else {  // (m + i t) W^2j
-            const float br = mr - ti, bi = mi + tr;
-            y = cmul_part(br, bi, kTw96.re[2 * j], kTw96.im[2 * j], part);
-        }
-    }
-#pragma unroll
-    for (int h = M / 2; h >= 1; h >>= 1) {  // radix-2 stages inside each block of M
-        __syncthreads();
-        if (mine) xch[i] = y;
-        __syncthreads();
-        if (mine) {
-            const int q = P % M, w = q & (2 * h - 1);  // position inside the 2h-block
-            if (w < h) {
-                y = xch[2 * P + part] + xch[2 * (P + h) + part];
-            } else {
-                const int lo = P - h;
-                const float dr = xch[2 * lo] - xch[2 * P], di = xch[2 * lo + 1] - xch[2 * P + 1];
-                const int t = (w - h) * (N / (2 * h));
-                y = cmul_part(dr, di, kTw96.re[t], kTw96.im[t], part);
-            }
-        }
-    }
-    return y;
-}
-
 // One block of D threads per (token, KV head, sequence): quantises the
 // token's K and V (each rotated when its signs are given; K scaled by its
 // channel scale after the rotation) with the per-lane quantiser of the
@@ -118,19 +50,15 @@ __global__ __launch_bounds__(D) void quantize_wide_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, int dtype, int n_new, int H, int cap,
     uint8_t* __restrict__ kc, float* __restrict__ ks, uint8_t* __restrict__ vc, float* __restrict__ vs,
     const float* __restrict__ signs, float rot_norm, const float* __restrict__ lam,
-    const float* __restrict__ vsigns, const int32_t* __restrict__ pos, unsigned* __restrict__ err,
-    const int32_t* __restrict__ lens, int max_len)
+    const float* __restrict__ vsigns, const int32_t* __restrict__ pos, unsigned* __restrict__ err)
 {
 #pragma clang fp contract(off)
     constexpr int NG = D / kGroup;
     __shared__ float xch[D];
     const int tok = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int ch = threadIdx.x, lane = ch & 63;
-    // a decode step's token (lens given, n_new = 1) goes to position
-    // clamp(lens[b], 0, max_len) - 1, none when that is -1 (the split and
-    // combine passes report lens outside [0, max_len])
-    const int p0 = lens ? min(max(lens[b], 0), max_len) - 1 : pos[b];
-    if (!lens && ch == 0 && tok == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new)) report_error(err, kErrPos);
+    const int p0 = pos[b];
+    if (ch == 0 && tok == 0 && h == 0 && (p0 < 0 || p0 > cap - n_new)) report_error(err, kErrPos);
     const int t = p0 + tok;
     if (t < 0 || t >= cap) return;  // block-uniform: outside the cache
     const size_t head = (size_t)b * H + h;
@@ -421,21 +349,7 @@ hipError_t launch_quantize_wide(const void* k, const void* v, int dtype, int n_n
     quantize_wide_kernel<192><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(k),
                                                            static_cast<const uint16_t*>(v), dtype, n_new, H,
                                                            cap, kc, ks, vc, vs, signs, rot_norm, lam, vsigns,
-                                                           pos, err, nullptr, 0);
-    return hipGetLastError();
-}
-
-hipError_t launch_append_step_wide(const void* k_new, const void* v_new, int dtype, int B, int H, int D, int cap,
-                                   uint8_t* kc, float* ks, uint8_t* vc, float* vs, const float* signs,
-                                   float rot_norm, const float* lam, const int32_t* lens, int max_len,
-                                   unsigned* err, hipStream_t stream)
-{
-    if (D != 192 || max_len < 1 || max_len > cap) return hipErrorInvalidValue;
-    dim3 grid(1, H, B), block(192);
-    quantize_wide_kernel<192><<<grid, block, 0, stream>>>(static_cast<const uint16_t*>(k_new),
-                                                           static_cast<const uint16_t*>(v_new), dtype, 1, H, cap,
-                                                           kc, ks, vc, vs, signs, rot_norm, lam, nullptr, nullptr,
-                                                           err, lens, max_len);
+                                                           pos, err);
     return hipGetLastError();
 }
 

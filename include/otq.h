@@ -350,9 +350,8 @@ int otq_sdpa_int4_decode_planned(const void *q, int32_t dtype, int32_t num_q_hea
  * call alike (so lens[b] > max_len appends at max_len - 1).  Other
  * arguments, contracts and errors as for otq_sdpa_int4_decode_planned; the
  * cache must hold tokens [0, lens[b] - 1) already.
- * At head_dim 192 the step is three launches on `stream`: the new token's
- * append (the same kernel and codes as otq_quantize_append), then the split
- * and combine passes over [0, lens[b]); results and errors are the same.
+ * At head_dim 192 the combine transforms the new token's rotated K with the
+ * mixed-radix FFT described above, in every channel slice of a row.
  */
 int otq_sdpa_int4_decode_append(const void *q, const void *k_new, const void *v_new,
                                 int32_t dtype, int32_t num_q_heads, const otq_cache *cache,

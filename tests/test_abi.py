@@ -336,8 +336,7 @@ def test_head_dim_192_host_checks():
     """head_dim 192 (D/2 = 3 * 32): int4 only, K rotated by the FFT kind only
     (the Hadamard form needs a power of two), V unrotated; the matrix-core
     split pass by default, the vector one when asked for; the decode step
-    passes the host checks (three launches at this width); sizes by the int4
-    closed form."""
+    passes the host checks; sizes by the int4 closed form."""
     lib = otq.lib()
     P = ctypes.c_void_p
     cb, sb = otq.otq_cache_array_bytes(2, 3, 192, 64, 4)

@@ -175,9 +175,9 @@ def test_fused_append_vector_variant(G, D, scaled):
 @pytest.mark.parametrize("G", [1, 4, 8, 16])
 @pytest.mark.parametrize("rotate,scaled", [(False, False), ("srft", False), ("srft", True), (False, True)])
 def test_fused_append_head_dim_192(G, rotate, scaled):
-    """head_dim 192: the step's token through its own append launch (the
-    mixed-radix FFT when K is rotated), then the split and combine over
-    [0, lens); two steps in a row, one sequence that has no token yet."""
+    """head_dim 192: the combine quantises the step's token (the mixed-radix
+    FFT in every channel slice when K is rotated), writes it and merges it;
+    two steps in a row, one sequence that has no token yet."""
     _run(3, G, 2, 192, 384, [351, 190, 0], rotate=rotate, chunk=128, seed=17 * G + scaled + 2 * bool(rotate),
          scaled=scaled, steps=2)
 

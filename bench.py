@@ -463,13 +463,20 @@ def bench_workload(wnum, args, primary):
         kname = "split_mfma" if plan.variant == 2 else "split_vec"
     if not primary:
         del caches, outs, ws, qs, k_new, v_new
-        return {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
-                "context": w.T, "layers": L, "code_bits": wbits, "chunk": plan.chunk,
-                "num_splits": plan.num_splits, "kernel": kname,
-                "us_layer_step": round(us_layer_step, 3), "split_us": round(split_us, 3),
-                "split_GBps": round(achieved, 1), "split_frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "step_GBps": round(step_gbps, 1), "step_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
-                "algorithmic_bytes_per_split_launch": int(split_bytes)}
+        torch.cuda.empty_cache()
+        rec = {"workload": w.name, "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv, "head_dim": w.D,
+               "context": w.T, "layers": L, "code_bits": wbits, "chunk": plan.chunk,
+               "num_splits": plan.num_splits, "kernel": kname,
+               "us_layer_step": round(us_layer_step, 3), "split_us": round(split_us, 3),
+               "split_GBps": round(achieved, 1), "split_frac": round(achieved / HBM_PEAK_GBPS, 4),
+               "step_GBps": round(step_gbps, 1), "step_frac": round(step_gbps / HBM_PEAK_GBPS, 4),
+               "algorithmic_bytes_per_split_launch": int(split_bytes)}
+        if not args.no_ceiling:  # the streaming rate at this workload's bytes per launch
+            c = stream_ceiling(torch, otq, dev, int(split_bytes), min(L, 16), max(4, args.steps // 2))
+            rec.update({"stream_ceiling_GBps": c["GBps"], "stream_ceiling_blocks": c["blocks"],
+                        "split_frac_of_ceiling": round(achieved / c["GBps"], 4),
+                        "step_frac_of_ceiling": round(step_gbps / c["GBps"], 4)})
+        return rec
 
     # ---------------------------------------------------------------- bulk append (cache build)
     # Chunks of the workload's K/V quantised into a scratch cache of the same

@@ -2,9 +2,13 @@
 // the decode kernels are measured against (not a step of the method).
 //
 // Every 16 bytes of the buffer are read once with non-temporal loads (as the
-// split pass reads the cache), four loads in flight per thread, over a grid
+// split pass reads the cache), one load in flight per thread, over a grid
 // that the dispatcher hands to whichever compute unit frees first; each
 // block folds what it read into one word so the loads are not removed.
+// One load per thread over 2048 blocks (8 MB in flight) read 160 MiB at 6.8
+// TB/s on MI355X, against 6.5-6.6 TB/s for four loads per thread at its best
+// block count (512); more bytes in flight than that lower the rate, so the
+// caller sweeps the block count.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,7 +19,7 @@ namespace {
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kProbeThreads = 256;
-constexpr int kProbeUnroll = 4;
+constexpr int kProbeUnroll = 1;
 
 __global__ __launch_bounds__(kProbeThreads) void stream_read_kernel(const u32x4_t* __restrict__ buf, size_t n16,
                                                                     uint32_t* __restrict__ sink)

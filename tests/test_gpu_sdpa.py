@@ -331,11 +331,11 @@ def _full(cfg, rows_per_seq=None, layer=0, options=False, srft=False):
 
 
 def test_full_workload_2_llama70b_32k():
-    _full(2, rows_per_seq=16)
+    _full(2)
 
 
 def test_full_workload_3_llama70b_128k():
-    _full(3, rows_per_seq=8)
+    _full(3)
 
 
 def test_full_workload_1_tiny():
@@ -343,22 +343,22 @@ def test_full_workload_1_tiny():
 
 
 def test_full_workload_4_gemma_scale1():
-    _full(4, rows_per_seq=8)
+    _full(4)
 
 
 def test_full_workload_5_ragged_rotated():
-    _full(5, rows_per_seq=2)
+    _full(5)
 
 
-@pytest.mark.parametrize("cfg,rows_per_seq", [(3, 8), (4, 8), (5, 2)])
-def test_full_workload_with_options(cfg, rows_per_seq):
+@pytest.mark.parametrize("cfg", [3, 4, 5])
+def test_full_workload_with_options(cfg):
     """The full workloads with K's per-channel scale and a rotated V."""
-    _full(cfg, rows_per_seq=rows_per_seq, options=True)
+    _full(cfg, options=True)
 
 
-@pytest.mark.parametrize("cfg,rows_per_seq,options", [(3, 8, False), (4, 8, True), (5, 2, False)])
-def test_full_workload_srft(cfg, rows_per_seq, options):
+@pytest.mark.parametrize("cfg,options", [(3, False), (4, True), (5, False)])
+def test_full_workload_srft(cfg, options):
     """The full workloads with K rotated by the sign-randomised FFT (workload
     5 switches from the Hadamard rotation to it); workload 4 with K's channel
     scale and V rotated by the same kind."""
-    _full(cfg, rows_per_seq=rows_per_seq, options=options, srft=True)
+    _full(cfg, options=options, srft=True)
